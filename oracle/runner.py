@@ -1,0 +1,85 @@
+"""Replay a request trace through the plain cache model.
+
+TEST INFRASTRUCTURE (oracle). Only tests/, the smoke check and the bench's CPU
+baseline leg may use this module.
+
+The request loop follows the pages: traverse (match) -> reuse -> compute the
+unmatched suffix only -> insert (hustzhy SGLang post, §2.3 (2); bowenzhou
+SGLang review, "Work loop"); a batch is formed after matching, evicting when
+memory is short, and the tree is updated after the batch runs (2312.07104_SGLang
+notes, App. A.2). The per-step order (extend, then decode, then finish) and the
+full-match cut are the trace's documented lifecycle.
+
+Outputs the event log both sides must agree on bit for bit:
+  ("match", rid, m, node)            m after the full-match cut
+  ("evict", rid, freed slots)        only when an allocation had to evict
+  ("alloc", rid, slots)
+  ("insert", rid, existing, node)    after extend (prompt) and at finish (prompt+output)
+plus each request's final slot row, the final tree dump and the counts.
+"""
+from __future__ import annotations
+
+from .radix_model import RadixCacheModel
+
+
+def _alloc(model, log, rid, n):
+    short = n - model.num_free()
+    if short > 0:
+        freed = model.evict(short)
+        log.append(("evict", rid, tuple(freed)))
+    slots = model.alloc(n)
+    log.append(("alloc", rid, tuple(slots)))
+    return slots
+
+
+def run_trace(job, steps=None):
+    """Run ``job.steps`` (or a prefix of them) through a fresh model. Returns a dict."""
+    model = RadixCacheModel(job.num_slots)
+    log = []
+    rows = {}
+    held = {}
+    prefix_len = {}
+    extend_step = {}
+    computed = 0
+    prompt_total = 0
+    matched_total = 0
+    steps = job.steps if steps is None else steps
+    for si, st in enumerate(steps):
+        for rid in st.extend:
+            r = job.requests[rid]
+            m, pslots, node = model.match(r.prompt)
+            if m == r.n:
+                m -= 1
+                pslots = pslots[:m]
+            log.append(("match", rid, m, node))
+            model.lock_ref(node, +1)
+            held[rid] = node
+            new = _alloc(model, log, rid, r.n - m)
+            rows[rid] = list(pslots) + list(new)
+            prefix_len[rid] = m
+            extend_step[rid] = si
+            computed += r.n - m
+            prompt_total += r.n
+            matched_total += m
+        for rid in st.extend:
+            r = job.requests[rid]
+            existing, node, tslots = model.insert(r.prompt, rows[rid][: r.n])
+            log.append(("insert", rid, existing, node))
+            rows[rid][: r.n] = tslots
+            model.lock_ref(node, +1)
+            model.lock_ref(held[rid], -1)
+            held[rid] = node
+        for rid in st.decode:
+            rows[rid].extend(_alloc(model, log, rid, 1))
+        for rid in st.finish:
+            r = job.requests[rid]
+            k = len(rows[rid]) - r.n
+            full = list(r.prompt) + list(r.output[:k])
+            existing, node, tslots = model.insert(full, rows[rid])
+            log.append(("insert", rid, existing, node))
+            rows[rid] = tslots
+            model.lock_ref(held[rid], -1)
+            del held[rid]
+    return dict(model=model, log=log, rows=rows, prefix_len=prefix_len, extend_step=extend_step,
+                computed=computed, prompt_total=prompt_total, matched_total=matched_total,
+                dump=model.dump(), stats=model.stats())
