@@ -1,0 +1,220 @@
+/*
+ * rax.h -- C ABI of librax, the MI355X (gfx950) implementation of RadixAttention's
+ * data-parallel hot path: attention over a token-granular KV pool whose prefix
+ * entries are reused through a radix tree.
+ *
+ * Sources for the operations (cited by page title and section):
+ *   [notes]  "2312.07104_SGLang: Efficient Execution of Structured Language Model
+ *            Programs" (paper notes), §3 RadixAttention, App. A.1-A.3, Figure 3.
+ *   [lqhl]   "SGLang: Efficient Execution of Structured Language Model Programs
+ *            (NeurIPS 2024)" review, "Core method".
+ *   [hustzhy] "SGLang: the structured-program revolution in LLM inference" post,
+ *            §2.2-2.5 (RadixAttention).
+ *   [bowen]  "SGLang: managing the KV cache as a cache for the first time" review,
+ *            "How RadixAttention works".
+ *
+ * Conventions for every entry point:
+ *   - Returns rax_status: RAX_OK (0) or a negative code. Nothing throws across the ABI.
+ *   - Arrays are caller-owned; capacities are explicit. The library keeps no pointer
+ *     to a caller array after the call returns (device calls: until the stream
+ *     reaches the launched work).
+ *   - Host tree calls are single-threaded: one rax_tree must not be used from two
+ *     threads at once. Different trees are independent.
+ *   - Device calls take device pointers (e.g. a torch tensor's data_ptr) and a
+ *     hipStream_t passed as void*; they only enqueue work and never synchronise.
+ *     Arguments are validated on the host before any launch (RAX_EINVAL, nothing
+ *     launched). A launch failure is RAX_EDEVICE. Kernels never dereference an
+ *     index outside the sizes given here: out-of-range slot ids, request rows or
+ *     positions are skipped and recorded in a device error word that
+ *     rax_device_errors() reads back.
+ *   - Layouts are row-major and dense. The KV pool is K and V arrays of shape
+ *     [num_slots, h_kv, d]: one slot holds one token's K (or V) for every KV head
+ *     (token-granular paging, [notes] §3: one page per token).
+ */
+#ifndef RAX_H
+#define RAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rax_status;
+#define RAX_OK 0
+#define RAX_EINVAL (-1)  /* bad argument; nothing changed, nothing launched */
+#define RAX_ENOMEM (-2)  /* not enough free slots (or host memory); nothing taken */
+#define RAX_ESTATE (-3)  /* unknown node, or a ref count would drop below zero */
+#define RAX_EDEVICE (-4) /* a HIP call or kernel launch failed */
+
+typedef enum { RAX_F32 = 0, RAX_BF16 = 1 } rax_dtype;
+
+/* Opaque host radix tree that also owns the slot free set of one KV pool. */
+typedef struct rax_tree rax_tree;
+/* Node handle. 0 is the root; every new node takes the next integer. A handle stays
+ * valid until its node is evicted; a node split keeps its handle on the lower part. */
+typedef int64_t rax_node;
+
+typedef struct {
+  int64_t num_slots;        /* pool size */
+  int64_t free_slots;       /* slots in the free set */
+  int64_t cached_tokens;    /* tokens held by tree nodes */
+  int64_t locked_tokens;    /* tokens in nodes with ref count > 0 */
+  int64_t evictable_tokens; /* cached_tokens - locked_tokens */
+  int64_t num_nodes;        /* excluding the root */
+  int64_t clock;            /* logical LRU clock (one tick per match or insert) */
+  int64_t matched_tokens;   /* cumulative over rax_match_prefix calls */
+  int64_t inserted_tokens;  /* cumulative new tokens adopted by rax_insert */
+  int64_t evicted_tokens;   /* cumulative */
+} rax_stats;
+
+const char* rax_status_str(rax_status s);
+int32_t rax_abi_version(void);
+
+/* ======================================================================== host: tree
+ * Semantics ([notes] §3; [bowen] "Work loop: insert, match, split, evict";
+ * [hustzhy] §2.3):
+ *  - match: longest cached prefix of the request ("traverse"); its KV is reused.
+ *  - a node shared only up to a divergence point splits in two (Figure 3 steps 4, 7).
+ *  - ref counts pin nodes that running requests depend on; only ref 0 may be freed.
+ *  - eviction is LRU over leaves; parents become candidates once they are leaves.
+ *  - cached and running KV share one pool of slots.
+ * Choices where the pages are silent (fixed so results are reproducible bit for bit):
+ *  - a match ending inside a node splits it immediately; the upper part is a new
+ *    node with the same ref count and tick; the lower part keeps its handle.
+ *  - one logical clock tick per match or insert call; every node on the matched /
+ *    inserted path takes it; ties between leaves break by the smaller handle.
+ *  - eviction removes whole leaves until at least the requested count is freed
+ *    (it may overshoot by part of one leaf) or nothing is evictable.
+ *  - the allocator hands out the lowest free slot ids, ascending.
+ */
+
+/* Create a tree over a pool of num_slots slots, all free. num_slots in [1, 2^31). */
+rax_status rax_tree_create(int64_t num_slots, rax_tree** out);
+void rax_tree_destroy(rax_tree* t);
+
+/* Longest cached prefix of tokens[0..n). Writes its slots to out_slots (capacity n,
+ * may be NULL when n == 0), the matched length to *out_len and the node where the
+ * match ends to *out_node (0 if nothing matched). Splits and ticks as above. */
+rax_status rax_match_prefix(rax_tree* t, const int32_t* tokens, int64_t n, int32_t* out_slots,
+                            int64_t* out_len, rax_node* out_node);
+
+/* Cache tokens[0..n) with the caller's slots[0..n) (request finished or prefilled;
+ * [bowen] "insert"). Positions already cached keep the tree's slot; a caller slot
+ * there that differs is returned to the free set. New positions adopt the caller's
+ * slots as one new leaf. out_slots (capacity n, or NULL) receives the slot the tree
+ * holds for every position afterwards; *out_existing the number of positions that
+ * were already cached; *out_node the node ending at position n. Slots must lie in
+ * [0, num_slots) and must not be free. */
+rax_status rax_insert(rax_tree* t, const int32_t* tokens, const int32_t* slots, int64_t n,
+                      int32_t* out_slots, int64_t* out_existing, rax_node* out_node);
+
+/* Add delta (+1 or -1) to the ref count of every node from `node` up to the root.
+ * RAX_ESTATE if the node is unknown or a count would go below zero (nothing changed). */
+rax_status rax_lock_ref(rax_tree* t, rax_node node, int32_t delta);
+
+/* Evict least-recently-used leaves with ref 0 until >= num_tokens slots are freed or
+ * nothing is evictable; freed slots go back to the free set. *out_num_freed is the
+ * total freed; the first min(cap, total) slot ids, leaf by leaf in eviction order and
+ * each leaf in token order, are written to out_freed (may be NULL when cap == 0). */
+rax_status rax_evict_lru(rax_tree* t, int64_t num_tokens, int32_t* out_freed, int64_t cap,
+                         int64_t* out_num_freed);
+
+/* Take the n lowest free slots (ascending) into out_slots. RAX_ENOMEM: nothing taken. */
+rax_status rax_alloc_slots(rax_tree* t, int64_t n, int32_t* out_slots);
+/* Allocation as a scheduler does it before running a batch ([notes] App. A.2: form the
+ * batch, evicting when memory is short): if fewer than n slots are free, first evict
+ * LRU leaves for the shortfall (as rax_evict_lru, reporting into out_freed / cap /
+ * *out_num_freed), then take the n lowest free slots. RAX_ENOMEM if still short
+ * (evicted slots stay free, nothing is taken). */
+rax_status rax_alloc_slots_evict(rax_tree* t, int64_t n, int32_t* out_slots, int32_t* out_freed,
+                                 int64_t cap, int64_t* out_num_freed);
+/* Number of free slots (O(1)). */
+rax_status rax_free_count(const rax_tree* t, int64_t* out);
+/* Return slots to the free set. RAX_EINVAL (nothing changed) if one is out of range,
+ * already free, or repeated. */
+rax_status rax_free_slots(rax_tree* t, const int32_t* slots, int64_t n);
+
+/* Token depth of the deepest common ancestor of nodes a and b (0 = root). Two running
+ * requests holding nodes a and b have identical slots on exactly these positions. */
+rax_status rax_lca_depth(const rax_tree* t, rax_node a, rax_node b, int64_t* out_depth);
+
+rax_status rax_tree_stats(const rax_tree* t, rax_stats* out);
+
+/* Serialise the tree in preorder (children by ascending first token), as int64 words:
+ * per node [handle, parent handle, length L, ref, tick, tokens[L], slots[L]]. With
+ * buf == NULL (or cap too small) *out_len receives the word count; too small a
+ * non-NULL buffer is RAX_EINVAL. */
+rax_status rax_tree_dump(const rax_tree* t, int64_t* buf, int64_t cap, int64_t* out_len);
+
+/* ====================================================================== device calls */
+
+/* KV write-back ([bowen] "insert": computed KV is kept for reuse; [notes] App. A.1):
+ *   k_pool[out_loc[i], h, :] = k_new[i, h, :] and v_pool[...] = v_new[...] for i < n_tok.
+ * k_new, v_new: [n_tok, h_kv, d] of dtype dt. out_loc: device int32 [n_tok].
+ * Rows whose slot is outside [0, num_slots) are skipped and flagged. */
+rax_status rax_kv_scatter(const void* k_new, const void* v_new, const int32_t* out_loc, int64_t n_tok,
+                          void* k_pool, void* v_pool, int64_t num_slots, int32_t h_kv, int32_t d,
+                          rax_dtype dt, void* stream);
+
+/* req_to_token row fill: for request r < batch and i < src_indptr[r+1] - src_indptr[r],
+ *   req_to_token[req_pool_idx[r] * rtt_stride + start[r] + i] = src_slots[src_indptr[r] + i].
+ * All pointers are device int32 arrays; total = src_indptr[batch] (host copy).
+ * Entries that would fall outside [0, rtt_rows) x [0, rtt_stride) are skipped and flagged. */
+rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                  const int32_t* req_pool_idx, const int32_t* start,
+                                  const int32_t* src_indptr, const int32_t* src_slots, int32_t batch,
+                                  int64_t total, void* stream);
+
+/* Extend (prefill) attention over radix-cached KV ([hustzhy] §2.3 (2): reuse the matched
+ * prefix's KV and compute only the unmatched suffix; [lqhl] "Core method").
+ * Request r (r < batch) has prefix_len[r] = m_r cached tokens and q_len_r =
+ * qo_indptr[r+1] - qo_indptr[r] new tokens. Query row t = qo_indptr[r] + i is the token
+ * at absolute position p = m_r + i; for query head h (KV head g = h / (h_q / h_kv)):
+ *   keys j <  m_r : K/V from the pool at slot req_to_token[req_pool_idx[r], j]
+ *   keys m_r <= j <= p : K/V rows qo_indptr[r] + (j - m_r) of k_ext / v_ext (causal)
+ *   o[t, h, :] = softmax_j(sm_scale * q[t,h,:] . k_j) V_j
+ * Shapes: q [total_q, h_q, d], k_ext/v_ext [total_q, h_kv, d], o [total_q, h_q, d];
+ * metadata arrays are device int32. shared_len (optional, may be NULL) is a hint:
+ * shared_len[r] (r >= 1) promises that requests r-1 and r have identical slots at
+ * positions [0, shared_len[r]) -- the kernel then loads those K/V tiles once for the
+ * query rows of both requests. d in {64, 128}; h_q % h_kv == 0; dt RAX_F32 or RAX_BF16
+ * (pools, q, k_ext, v_ext); o_dt RAX_F32 or RAX_BF16; fp32 accumulation throughout. */
+rax_status rax_extend_attention(const void* q, const void* k_ext, const void* v_ext,
+                                const void* k_pool, const void* v_pool, int64_t num_slots,
+                                const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                const int32_t* req_pool_idx, const int32_t* prefix_len,
+                                const int32_t* qo_indptr, const int32_t* shared_len, int32_t batch,
+                                int64_t total_q, int32_t h_q, int32_t h_kv, int32_t d, float sm_scale,
+                                rax_dtype dt, void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/* Batched decode attention ([notes] App. A.1: a decoding step attends over the KV of
+ * all previous tokens and itself). Request r's new token is already in the pool: its
+ * keys are positions 0..seq_len[r]-1, all read through req_to_token. q [batch, h_q, d],
+ * o [batch, h_q, d]. The key range is split (split-K) so that enough workgroups run;
+ * partial softmax states go to `workspace` (size from rax_attention_workspace_bytes)
+ * and are merged by log-sum-exp. shared_len as in rax_extend_attention. */
+rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                const int32_t* req_pool_idx, const int32_t* seq_len,
+                                const int32_t* shared_len, int32_t batch, int32_t max_seq_len,
+                                int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
+                                void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes that an extend (is_decode = 0, rows = total_q) or decode (is_decode =
+ * 1, rows = batch) call with these sizes may use. 0 means the call needs none. */
+size_t rax_attention_workspace_bytes(int32_t is_decode, int64_t rows, int32_t h_q, int32_t h_kv,
+                                     int32_t d, int32_t max_kv_len);
+
+/* Synchronise `stream`, return (and clear) the device error word: a bit mask of
+ * RAX_DEVERR_* for indices the kernels skipped since the last call. */
+#define RAX_DEVERR_SLOT 1   /* slot id outside [0, num_slots) */
+#define RAX_DEVERR_ROW 2    /* req_to_token row or column outside its bounds */
+rax_status rax_device_errors(void* stream, int32_t* out_mask);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RAX_H */

@@ -207,8 +207,10 @@ class RadixCacheModel:
         return m, node, out_slots
 
     def lock_ref(self, node: int, delta: int) -> None:
-        if node not in self.segs or delta not in (1, -1):
-            raise CacheError("EINVAL", f"bad lock {node} {delta}")
+        if delta not in (1, -1):
+            raise CacheError("EINVAL", f"bad delta {delta}")
+        if node not in self.segs:
+            raise CacheError("ESTATE", f"unknown node {node}")
         path = [p for p in self._path_segments(node) if p != 0]
         if delta < 0 and any(self.segs[p].ref + delta < 0 for p in path):
             raise CacheError("ESTATE", "unlock below zero")
@@ -234,6 +236,8 @@ class RadixCacheModel:
 
     def lca_depth(self, a: int, b: int) -> int:
         """Token depth of the deepest node that is an ancestor of (or equal to) both nodes."""
+        if a not in self.segs or b not in self.segs:
+            raise CacheError("ESTATE", "unknown node")
         pa = self._path_segments(a)
         pb = set(self._path_segments(b))
         for s in pa:

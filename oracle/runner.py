@@ -12,8 +12,8 @@ full-match cut are the trace's documented lifecycle.
 
 Outputs the event log both sides must agree on bit for bit:
   ("match", rid, m, node)            m after the full-match cut
-  ("evict", rid, freed slots)        only when an allocation had to evict
-  ("alloc", rid, slots)
+  ("evict", step, freed slots)       only when an allocation had to evict
+  ("alloc", step, slots)             one batch allocation per extend / decode call
   ("insert", rid, existing, node)    after extend (prompt) and at finish (prompt+output)
 plus each request's final slot row, the final tree dump and the counts.
 """
@@ -22,13 +22,13 @@ from __future__ import annotations
 from .radix_model import RadixCacheModel
 
 
-def _alloc(model, log, rid, n):
+def _alloc(model, log, si, n):
     short = n - model.num_free()
     if short > 0:
         freed = model.evict(short)
-        log.append(("evict", rid, tuple(freed)))
+        log.append(("evict", si, tuple(freed)))
     slots = model.alloc(n)
-    log.append(("alloc", rid, tuple(slots)))
+    log.append(("alloc", si, tuple(slots)))
     return slots
 
 
@@ -45,6 +45,7 @@ def run_trace(job, steps=None):
     matched_total = 0
     steps = job.steps if steps is None else steps
     for si, st in enumerate(steps):
+        pending = []
         for rid in st.extend:
             r = job.requests[rid]
             m, pslots, node = model.match(r.prompt)
@@ -54,13 +55,19 @@ def run_trace(job, steps=None):
             log.append(("match", rid, m, node))
             model.lock_ref(node, +1)
             held[rid] = node
-            new = _alloc(model, log, rid, r.n - m)
-            rows[rid] = list(pslots) + list(new)
-            prefix_len[rid] = m
-            extend_step[rid] = si
-            computed += r.n - m
-            prompt_total += r.n
-            matched_total += m
+            pending.append((rid, m, pslots))
+        if st.extend:
+            new = _alloc(model, log, si, sum(job.requests[rid].n - m for rid, m, _ in pending))
+            off = 0
+            for rid, m, pslots in pending:
+                r = job.requests[rid]
+                rows[rid] = list(pslots) + list(new[off: off + r.n - m])
+                off += r.n - m
+                prefix_len[rid] = m
+                extend_step[rid] = si
+                computed += r.n - m
+                prompt_total += r.n
+                matched_total += m
         for rid in st.extend:
             r = job.requests[rid]
             existing, node, tslots = model.insert(r.prompt, rows[rid][: r.n])
@@ -69,8 +76,10 @@ def run_trace(job, steps=None):
             model.lock_ref(node, +1)
             model.lock_ref(held[rid], -1)
             held[rid] = node
-        for rid in st.decode:
-            rows[rid].extend(_alloc(model, log, rid, 1))
+        if st.decode:
+            new = _alloc(model, log, si, len(st.decode))
+            for i, rid in enumerate(st.decode):
+                rows[rid].append(new[i])
         for rid in st.finish:
             r = job.requests[rid]
             k = len(rows[rid]) - r.n

@@ -1,0 +1,306 @@
+"""ctypes binding of librax (include/rax.h): argument marshalling only.
+
+Host tree calls take numpy int32 arrays; device calls take torch tensors that
+already live on the GPU and enqueue work on the current (or given) HIP stream.
+Every computation happens inside librax. There is no fallback: if the library
+is missing, importing anything that needs it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librax.so")
+
+OK, EINVAL, ENOMEM, ESTATE, EDEVICE = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+DEVERR_SLOT, DEVERR_ROW = 1, 2
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class RaxStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_slots", "free_slots", "cached_tokens", "locked_tokens", "evictable_tokens",
+        "num_nodes", "clock", "matched_tokens", "inserted_tokens", "evicted_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_SIGS = {
+    "rax_status_str": (ctypes.c_char_p, [_i32]),
+    "rax_abi_version": (_i32, []),
+    "rax_tree_create": (_i32, [_i64, ctypes.POINTER(_vp)]),
+    "rax_tree_destroy": (None, [_vp]),
+    "rax_match_prefix": (_i32, [_vp, _c_i32p, _i64, _c_i32p, _c_i64p, _c_i64p]),
+    "rax_insert": (_i32, [_vp, _c_i32p, _c_i32p, _i64, _c_i32p, _c_i64p, _c_i64p]),
+    "rax_lock_ref": (_i32, [_vp, _i64, _i32]),
+    "rax_evict_lru": (_i32, [_vp, _i64, _c_i32p, _i64, _c_i64p]),
+    "rax_alloc_slots": (_i32, [_vp, _i64, _c_i32p]),
+    "rax_alloc_slots_evict": (_i32, [_vp, _i64, _c_i32p, _c_i32p, _i64, _c_i64p]),
+    "rax_free_count": (_i32, [_vp, _c_i64p]),
+    "rax_free_slots": (_i32, [_vp, _c_i32p, _i64]),
+    "rax_lca_depth": (_i32, [_vp, _i64, _i64, _c_i64p]),
+    "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
+    "rax_tree_dump": (_i32, [_vp, _c_i64p, _i64, _c_i64p]),
+    "rax_kv_scatter": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "rax_req_to_token_write": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _vp]),
+    "rax_extend_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                    _i32, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "rax_decode_attention": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                    _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "rax_attention_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
+    "rax_device_errors": (_i32, [_vp, _c_i32p]),
+}
+
+EXPORTS = tuple(_SIGS)
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librax.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m prefix_shared_kv_extend_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class RaxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().rax_status_str(status).decode()
+        super().__init__(f"{what}: {msg} ({status})")
+        self.status = status
+
+
+def _check(st: int, what: str) -> None:
+    if st != OK:
+        raise RaxError(st, what)
+
+
+def _i32arr(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(_c_i32p)
+
+
+def status_str(st: int) -> str:
+    return lib().rax_status_str(st).decode()
+
+
+# --------------------------------------------------------------------- host tree
+class Tree:
+    """Owner of one rax_tree (radix tree + slot allocator of one KV pool)."""
+
+    def __init__(self, num_slots: int):
+        self._L = lib()
+        h = _vp()
+        _check(self._L.rax_tree_create(int(num_slots), ctypes.byref(h)), "rax_tree_create")
+        self._h = h
+        self.num_slots = int(num_slots)
+        self._freed = np.empty(self.num_slots, dtype=np.int32)  # eviction report buffer
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._L.rax_tree_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def match_prefix(self, tokens):
+        t = _i32arr(tokens)
+        out = np.empty(len(t), dtype=np.int32)
+        m, node = _i64(), _i64()
+        _check(self._L.rax_match_prefix(self._h, _p32(t), len(t), _p32(out), ctypes.byref(m),
+                                        ctypes.byref(node)), "rax_match_prefix")
+        return int(m.value), out[: m.value], int(node.value)
+
+    def insert(self, tokens, slots):
+        t, s = _i32arr(tokens), _i32arr(slots)
+        if len(t) != len(s):
+            raise ValueError("tokens and slots differ in length")
+        out = np.empty(len(t), dtype=np.int32)
+        ex, node = _i64(), _i64()
+        _check(self._L.rax_insert(self._h, _p32(t), _p32(s), len(t), _p32(out), ctypes.byref(ex),
+                                  ctypes.byref(node)), "rax_insert")
+        return int(ex.value), int(node.value), out
+
+    def lock_ref(self, node: int, delta: int) -> None:
+        _check(self._L.rax_lock_ref(self._h, int(node), int(delta)), "rax_lock_ref")
+
+    def evict_lru(self, num_tokens: int) -> np.ndarray:
+        n = _i64()
+        _check(self._L.rax_evict_lru(self._h, int(num_tokens), _p32(self._freed), self.num_slots,
+                                     ctypes.byref(n)), "rax_evict_lru")
+        return self._freed[: n.value].copy()
+
+    def alloc_slots(self, n: int) -> np.ndarray:
+        out = np.empty(int(n), dtype=np.int32)
+        _check(self._L.rax_alloc_slots(self._h, int(n), _p32(out)), "rax_alloc_slots")
+        return out
+
+    def alloc_slots_evict(self, n: int):
+        """(slots, freed) -- evicts LRU leaves first when the free set is short."""
+        out = np.empty(int(n), dtype=np.int32)
+        nf = _i64()
+        st = self._L.rax_alloc_slots_evict(self._h, int(n), _p32(out), _p32(self._freed), self.num_slots,
+                                           ctypes.byref(nf))
+        _check(st, "rax_alloc_slots_evict")
+        return out, self._freed[: nf.value].copy()
+
+    def free_count(self) -> int:
+        n = _i64()
+        _check(self._L.rax_free_count(self._h, ctypes.byref(n)), "rax_free_count")
+        return int(n.value)
+
+    def free_slots(self, slots) -> None:
+        s = _i32arr(slots)
+        _check(self._L.rax_free_slots(self._h, _p32(s), len(s)), "rax_free_slots")
+
+    def lca_depth(self, a: int, b: int) -> int:
+        d = _i64()
+        _check(self._L.rax_lca_depth(self._h, int(a), int(b), ctypes.byref(d)), "rax_lca_depth")
+        return int(d.value)
+
+    def stats(self) -> dict:
+        s = RaxStats()
+        _check(self._L.rax_tree_stats(self._h, ctypes.byref(s)), "rax_tree_stats")
+        return s.as_dict()
+
+    def dump(self) -> list:
+        """Preorder list of (id, parent, length, ref, tick, tokens, slots)."""
+        n = _i64()
+        _check(self._L.rax_tree_dump(self._h, None, 0, ctypes.byref(n)), "rax_tree_dump")
+        buf = np.empty(max(1, n.value), dtype=np.int64)
+        _check(self._L.rax_tree_dump(self._h, buf.ctypes.data_as(_c_i64p), len(buf), ctypes.byref(n)),
+               "rax_tree_dump")
+        out, i, words = [], 0, buf[: n.value].tolist()
+        while i < len(words):
+            nid, par, ln, ref, tick = words[i: i + 5]
+            toks = tuple(words[i + 5: i + 5 + ln])
+            sl = tuple(words[i + 5 + ln: i + 5 + 2 * ln])
+            out.append((nid, par, ln, ref, tick, toks, sl))
+            i += 5 + 2 * ln
+        return out
+
+
+# ----------------------------------------------------------------- device calls
+def _dev(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return _vp(getattr(stream, "cuda_stream", stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_i32(*ts):
+    import torch
+    for t in ts:
+        if t is not None:
+            _need(t.is_cuda and t.dtype == torch.int32 and t.is_contiguous(), "index arrays: contiguous cuda int32")
+
+
+def kv_scatter(k_new, v_new, out_loc, k_pool, v_pool, stream=None) -> None:
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new: [n_tok, h_kv, d]")
+    _need(k_pool.shape == v_pool.shape and k_pool.shape[1:] == k_new.shape[1:], "pool: [num_slots, h_kv, d]")
+    _need(k_new.dtype == k_pool.dtype == v_new.dtype == v_pool.dtype, "dtypes must agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (k_new, v_new, k_pool, v_pool)), "contiguous cuda tensors")
+    _cuda_i32(out_loc)
+    _need(out_loc.numel() == k_new.shape[0], "out_loc: [n_tok]")
+    _check(lib().rax_kv_scatter(_dev(k_new), _dev(v_new), _dev(out_loc), k_new.shape[0], _dev(k_pool),
+                                _dev(v_pool), k_pool.shape[0], k_pool.shape[1], k_pool.shape[2],
+                                _dtype_code(k_pool), _stream(stream)), "rax_kv_scatter")
+
+
+def req_to_token_write(req_to_token, req_pool_idx, start, src_indptr, src_slots, total: int, stream=None) -> None:
+    _cuda_i32(req_to_token, req_pool_idx, start, src_indptr, src_slots)
+    _need(req_to_token.dim() == 2, "req_to_token: [rows, stride]")
+    b = req_pool_idx.numel()
+    _need(start.numel() == b and src_indptr.numel() == b + 1 and src_slots.numel() >= total, "shapes")
+    _check(lib().rax_req_to_token_write(_dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
+                                        _dev(req_pool_idx), _dev(start), _dev(src_indptr), _dev(src_slots),
+                                        b, int(total), _stream(stream)), "rax_req_to_token_write")
+
+
+def attention_workspace_bytes(is_decode: bool, rows: int, h_q: int, h_kv: int, d: int, max_kv_len: int) -> int:
+    return int(lib().rax_attention_workspace_bytes(int(bool(is_decode)), int(rows), h_q, h_kv, d, int(max_kv_len)))
+
+
+def extend_attention(q, k_ext, v_ext, k_pool, v_pool, req_to_token, req_pool_idx, prefix_len, qo_indptr,
+                     o, shared_len=None, sm_scale=None, workspace=None, stream=None) -> None:
+    _need(q.dim() == 3 and k_ext.dim() == 3 and q.shape[0] == k_ext.shape[0], "q [T,h_q,d], k_ext [T,h_kv,d]")
+    _need(k_ext.shape == v_ext.shape and k_pool.shape == v_pool.shape, "k/v shapes")
+    _need(k_pool.shape[1:] == k_ext.shape[1:] and q.shape[2] == k_pool.shape[2], "head shapes")
+    _need(o.shape == q.shape and o.is_contiguous() and o.is_cuda, "o like q")
+    _need(q.dtype == k_ext.dtype == v_ext.dtype == k_pool.dtype == v_pool.dtype, "input dtypes agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (q, k_ext, v_ext, k_pool, v_pool)), "contiguous cuda")
+    _cuda_i32(req_to_token, req_pool_idx, prefix_len, qo_indptr, shared_len)
+    b = req_pool_idx.numel()
+    _need(prefix_len.numel() == b and qo_indptr.numel() == b + 1, "metadata shapes")
+    _need(shared_len is None or shared_len.numel() == b, "shared_len: [batch]")
+    d = q.shape[2]
+    scale = float(sm_scale if sm_scale is not None else d ** -0.5)
+    ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().rax_extend_attention(
+        _dev(q), _dev(k_ext), _dev(v_ext), _dev(k_pool), _dev(v_pool), k_pool.shape[0],
+        _dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0], _dev(req_pool_idx), _dev(prefix_len),
+        _dev(qo_indptr), _dev(shared_len), b, q.shape[0], q.shape[1], k_pool.shape[1], d, scale,
+        _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws, _stream(stream)), "rax_extend_attention")
+
+
+def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max_seq_len: int, o,
+                     workspace=None, shared_len=None, sm_scale=None, stream=None) -> None:
+    _need(q.dim() == 3 and q.shape[2] == k_pool.shape[2] and k_pool.shape == v_pool.shape, "shapes")
+    _need(o.shape == q.shape and o.is_contiguous() and o.is_cuda, "o like q")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "input dtypes agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (q, k_pool, v_pool)), "contiguous cuda")
+    _cuda_i32(req_to_token, req_pool_idx, seq_len, shared_len)
+    b = q.shape[0]
+    _need(req_pool_idx.numel() == b and seq_len.numel() == b, "metadata shapes")
+    d = q.shape[2]
+    scale = float(sm_scale if sm_scale is not None else d ** -0.5)
+    ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().rax_decode_attention(
+        _dev(q), _dev(k_pool), _dev(v_pool), k_pool.shape[0], _dev(req_to_token), req_to_token.shape[1],
+        req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
+        q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
+        _stream(stream)), "rax_decode_attention")
+
+
+def device_errors(stream=None) -> int:
+    m = _i32()
+    _check(lib().rax_device_errors(_stream(stream), ctypes.byref(m)), "rax_device_errors")
+    return int(m.value)

@@ -1,0 +1,115 @@
+// KV write-back into the token-granular pool, and req_to_token row fill.
+//
+// Write-back: the KV computed for new tokens is kept in the pool so that later
+// requests sharing the prefix reuse it (bowenzhou SGLang review, "Work loop":
+// insert; 2312.07104_SGLang notes, §3, one page per token). Each pool slot holds
+// one token's K (or V) for all KV heads: [num_slots, h_kv, d].
+//
+// Both kernels are pure data movement (HBM-bound): 16-byte vector loads and
+// stores, one token row of h_kv*d elements handled by consecutive lanes so reads
+// and writes are coalesced.
+#include "../../../include/rax.h"
+#include "rax_device.h"
+
+namespace raxk {
+
+__device__ int32_t g_rax_err = 0;
+
+// One thread moves one 16-byte chunk of one token row, for K and for V.
+__global__ void __launch_bounds__(256) kv_scatter_kernel(const uint4* __restrict__ k_new,
+                                                         const uint4* __restrict__ v_new,
+                                                         const int32_t* __restrict__ out_loc, int64_t n_tok,
+                                                         uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                         int64_t num_slots, int64_t chunks_per_row) {
+  const int64_t total = n_tok * chunks_per_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tok = i / chunks_per_row;
+    const int64_t c = i - tok * chunks_per_row;
+    const int32_t slot = out_loc[tok];
+    if (slot < 0 || slot >= num_slots) {
+      if (c == 0) flag_error(RAX_DEVERR_SLOT);
+      continue;
+    }
+    const int64_t dst = (int64_t)slot * chunks_per_row + c;
+    k_pool[dst] = k_new[i];
+    v_pool[dst] = v_new[i];
+  }
+}
+
+__global__ void __launch_bounds__(256) rtt_write_kernel(int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
+                                                        const int32_t* __restrict__ req_pool_idx,
+                                                        const int32_t* __restrict__ start,
+                                                        const int32_t* __restrict__ indptr,
+                                                        const int32_t* __restrict__ src, int32_t batch,
+                                                        int64_t total) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    // request owning entry e: last r with indptr[r] <= e
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (indptr[mid] <= e) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t row = req_pool_idx[lo];
+    const int64_t col = (int64_t)start[lo] + (e - indptr[lo]);
+    if (row < 0 || row >= rows || col < 0 || col >= stride) {
+      flag_error(RAX_DEVERR_ROW);
+      continue;
+    }
+    rtt[row * stride + col] = src[e];
+  }
+}
+
+static int grid_for(int64_t work, int64_t per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+}  // namespace raxk
+
+extern "C" rax_status rax_kv_scatter(const void* k_new, const void* v_new, const int32_t* out_loc,
+                                     int64_t n_tok, void* k_pool, void* v_pool, int64_t num_slots,
+                                     int32_t h_kv, int32_t d, rax_dtype dt, void* stream) {
+  if (n_tok < 0 || num_slots < 1 || h_kv < 1 || d < 1 || (dt != RAX_F32 && dt != RAX_BF16)) return RAX_EINVAL;
+  if (n_tok == 0) return RAX_OK;
+  if (!k_new || !v_new || !out_loc || !k_pool || !v_pool) return RAX_EINVAL;
+  const int64_t row_bytes = (int64_t)h_kv * d * (dt == RAX_F32 ? 4 : 2);
+  if (row_bytes % 16) return RAX_EINVAL;
+  const uintptr_t mis = (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool;
+  if (mis & 15) return RAX_EINVAL;
+  const int64_t cpr = row_bytes / 16;
+  hipLaunchKernelGGL(raxk::kv_scatter_kernel, dim3(raxk::grid_for(n_tok * cpr, 256)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4*)k_new, (const uint4*)v_new, out_loc, n_tok,
+                     (uint4*)k_pool, (uint4*)v_pool, num_slots, cpr);
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
+extern "C" rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                             const int32_t* req_pool_idx, const int32_t* start,
+                                             const int32_t* src_indptr, const int32_t* src_slots, int32_t batch,
+                                             int64_t total, void* stream) {
+  if (batch < 0 || total < 0 || rtt_stride < 1 || rtt_rows < 1) return RAX_EINVAL;
+  if (batch == 0 || total == 0) return RAX_OK;
+  if (!req_to_token || !req_pool_idx || !start || !src_indptr || !src_slots) return RAX_EINVAL;
+  hipLaunchKernelGGL(raxk::rtt_write_kernel, dim3(raxk::grid_for(total, 256)), dim3(256), 0,
+                     (hipStream_t)stream, req_to_token, rtt_stride, rtt_rows, req_pool_idx, start, src_indptr,
+                     src_slots, batch, total);
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
+extern "C" rax_status rax_device_errors(void* stream, int32_t* out_mask) {
+  if (!out_mask) return RAX_EINVAL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return RAX_EDEVICE;
+  int32_t v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(raxk::g_rax_err), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return RAX_EDEVICE;
+  const int32_t zero = 0;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(raxk::g_rax_err), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
+    return RAX_EDEVICE;
+  *out_mask = v;
+  return RAX_OK;
+}

@@ -1,0 +1,29 @@
+// Device-side helpers shared by librax's gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace raxk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Device error word: bits of RAX_DEVERR_* for indices a kernel skipped.
+extern __device__ int32_t g_rax_err;
+
+__device__ __forceinline__ void flag_error(int32_t bit) { atomicOr(&g_rax_err, bit); }
+
+// Workgroup ids are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Map the linear id so that ids landing on one XCD form contiguous runs of work items,
+// i.e. work items that share K/V tiles run under the same L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
+  constexpr int64_t kXcd = 8;
+  if (nblocks % kXcd != 0) return bid;
+  const int64_t per = nblocks / kXcd;
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+}  // namespace raxk

@@ -1,0 +1,274 @@
+// Host radix tree and slot allocator (see radix_tree.h for the cited semantics).
+#include "radix_tree.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace rax {
+
+// ------------------------------------------------------------------ allocator
+SlotAllocator::SlotAllocator(int64_t num_slots)
+    : num_slots_(num_slots), num_free_(num_slots), hint_(0), words_((num_slots + 63) / 64, ~0ull) {
+  const int64_t tail = num_slots & 63;
+  if (tail) words_.back() = (1ull << tail) - 1;
+}
+
+bool SlotAllocator::alloc(int64_t n, int32_t* out) {
+  if (n > num_free_) return false;
+  int64_t got = 0;
+  int64_t w = hint_;
+  const int64_t nw = static_cast<int64_t>(words_.size());
+  while (got < n && w < nw) {
+    uint64_t bits = words_[w];
+    while (bits && got < n) {
+      const int b = __builtin_ctzll(bits);
+      bits &= bits - 1;
+      out[got++] = static_cast<int32_t>(w * 64 + b);
+    }
+    words_[w] = bits;
+    if (bits == 0) ++w;
+  }
+  hint_ = w;
+  num_free_ -= n;
+  return true;
+}
+
+void SlotAllocator::release_one(int32_t s) {
+  words_[s >> 6] |= 1ull << (s & 63);
+  ++num_free_;
+  if ((s >> 6) < hint_) hint_ = s >> 6;
+}
+
+void SlotAllocator::release(const int32_t* slots, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) release_one(slots[i]);
+}
+
+// ----------------------------------------------------------------------- tree
+RadixTree::RadixTree(int64_t num_slots) : alloc_(num_slots) {
+  root_ = new Node();
+  root_->id = 0;
+  nodes_[0] = root_;
+}
+
+RadixTree::~RadixTree() {
+  for (auto& kv : nodes_) delete kv.second;
+}
+
+Node* RadixTree::new_node() {
+  Node* n = new Node();
+  n->id = next_id_++;
+  nodes_[n->id] = n;
+  return n;
+}
+
+const Node* RadixTree::find(int64_t id) const {
+  auto it = nodes_.find(id);
+  return it == nodes_.end() ? nullptr : it->second;
+}
+
+void RadixTree::lru_remove(Node* n) {
+  if (n->in_lru) {
+    lru_.erase({n->tick, n->id});
+    n->in_lru = false;
+  }
+}
+
+void RadixTree::lru_update(Node* n) {
+  const bool want = n != root_ && n->children.empty() && n->ref == 0;
+  if (want && !n->in_lru) {
+    lru_.insert({n->tick, n->id});
+    n->in_lru = true;
+  } else if (!want && n->in_lru) {
+    lru_remove(n);
+  }
+}
+
+Node* RadixTree::split(Node* child, int64_t k) {
+  Node* up = new_node();
+  Node* parent = child->parent;
+  up->parent = parent;
+  up->tokens.assign(child->tokens.begin(), child->tokens.begin() + k);
+  up->slots.assign(child->slots.begin(), child->slots.begin() + k);
+  up->ref = child->ref;
+  up->tick = child->tick;
+  up->depth_end = parent->depth_end + k;
+  child->tokens.erase(child->tokens.begin(), child->tokens.begin() + k);
+  child->slots.erase(child->slots.begin(), child->slots.begin() + k);
+  child->parent = up;
+  up->children[child->tokens[0]] = child;
+  parent->children[up->tokens[0]] = up;
+  return up;  // not a leaf; child keeps its LRU key (tick, id)
+}
+
+Node* RadixTree::walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out) {
+  Node* node = root_;
+  int64_t i = 0;
+  while (i < n) {
+    auto it = node->children.find(tokens[i]);
+    if (it == node->children.end()) break;
+    Node* c = it->second;
+    const int64_t len = static_cast<int64_t>(c->tokens.size());
+    const int64_t lim = std::min(len, n - i);
+    int64_t k = 1;  // first token matches by construction
+    while (k < lim && c->tokens[k] == tokens[i + k]) ++k;
+    if (out) std::memcpy(out + i, c->slots.data(), sizeof(int32_t) * k);
+    i += k;
+    if (k < len) {
+      node = split(c, k);
+      break;
+    }
+    node = c;
+  }
+  *matched = i;
+  return node;
+}
+
+void RadixTree::tick_path(Node* n) {
+  for (; n != root_; n = n->parent) {
+    if (n->in_lru) {
+      lru_.erase({n->tick, n->id});
+      n->tick = clock_;
+      lru_.insert({n->tick, n->id});
+    } else {
+      n->tick = clock_;
+    }
+  }
+}
+
+int64_t RadixTree::match(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_node) {
+  ++clock_;
+  int64_t m = 0;
+  Node* node = walk(tokens, n, &m, out_slots);
+  tick_path(node);
+  matched_total += m;
+  *out_node = node->id;
+  return m;
+}
+
+bool RadixTree::insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
+                       int64_t* out_existing, int64_t* out_node) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= alloc_.num_slots() || alloc_.is_free(slots[i])) return false;
+  }
+  ++clock_;
+  int64_t m = 0;
+  std::vector<int32_t> tree_slots(static_cast<size_t>(n));
+  Node* node = walk(tokens, n, &m, tree_slots.data());
+  for (int64_t i = 0; i < m; ++i) {
+    if (slots[i] != tree_slots[i]) alloc_.release_one(slots[i]);
+  }
+  if (m < n) {
+    Node* leaf = new_node();
+    leaf->parent = node;
+    leaf->tokens.assign(tokens + m, tokens + n);
+    leaf->slots.assign(slots + m, slots + n);
+    leaf->depth_end = node->depth_end + (n - m);
+    leaf->tick = clock_;
+    node->children[tokens[m]] = leaf;
+    lru_update(node);  // no longer a leaf
+    lru_update(leaf);
+    inserted_total += n - m;
+    std::memcpy(tree_slots.data() + m, slots + m, sizeof(int32_t) * (n - m));
+    node = leaf;
+  }
+  tick_path(node);
+  if (out_slots && n) std::memcpy(out_slots, tree_slots.data(), sizeof(int32_t) * n);
+  *out_existing = m;
+  *out_node = node->id;
+  return true;
+}
+
+int RadixTree::lock_ref(int64_t id, int32_t delta) {
+  auto it = nodes_.find(id);
+  if (it == nodes_.end()) return 1;
+  Node* start = it->second;
+  if (delta < 0) {
+    for (Node* n = start; n != root_; n = n->parent)
+      if (n->ref + delta < 0) return 2;
+  }
+  for (Node* n = start; n != root_; n = n->parent) {
+    n->ref += delta;
+    lru_update(n);
+  }
+  return 0;
+}
+
+int64_t RadixTree::evict(int64_t num_tokens, int32_t* out_freed, int64_t cap) {
+  int64_t freed = 0;
+  while (freed < num_tokens && !lru_.empty()) {
+    const int64_t id = lru_.begin()->second;
+    Node* n = nodes_[id];
+    lru_remove(n);
+    for (int32_t s : n->slots) {
+      if (out_freed && freed < cap) out_freed[freed] = s;
+      alloc_.release_one(s);
+      ++freed;
+    }
+    Node* p = n->parent;
+    p->children.erase(n->tokens[0]);
+    nodes_.erase(id);
+    delete n;
+    lru_update(p);
+  }
+  evicted_total += freed;
+  return freed;
+}
+
+bool RadixTree::lca_depth(int64_t a, int64_t b, int64_t* out) const {
+  const Node* na = find(a);
+  const Node* nb = find(b);
+  if (!na || !nb) return false;
+  // bring both to the same depth, then climb together
+  while (na->depth_end > nb->depth_end) na = na->parent;
+  while (nb->depth_end > na->depth_end) nb = nb->parent;
+  while (na != nb) {
+    if (na->depth_end >= nb->depth_end) na = na->parent;
+    else nb = nb->parent;
+  }
+  *out = na->depth_end;
+  return true;
+}
+
+void RadixTree::totals(int64_t* cached, int64_t* locked) const {
+  int64_t c = 0, l = 0;
+  for (auto& kv : nodes_) {
+    const int64_t len = static_cast<int64_t>(kv.second->tokens.size());
+    c += len;
+    if (kv.second->ref > 0) l += len;
+  }
+  *cached = c;
+  *locked = l;
+}
+
+int64_t RadixTree::dump(int64_t* buf, int64_t cap) const {
+  int64_t pos = 0;
+  std::vector<const Node*> stack;
+  auto push_children = [&](const Node* n) {
+    std::vector<const Node*> kids;
+    kids.reserve(n->children.size());
+    for (auto& kv : n->children) kids.push_back(kv.second);
+    std::sort(kids.begin(), kids.end(),
+              [](const Node* x, const Node* y) { return x->tokens[0] > y->tokens[0]; });
+    for (const Node* k : kids) stack.push_back(k);  // smallest first token popped first
+  };
+  auto put = [&](int64_t v) {
+    if (buf && pos < cap) buf[pos] = v;
+    ++pos;
+  };
+  push_children(root_);
+  while (!stack.empty()) {
+    const Node* n = stack.back();
+    stack.pop_back();
+    put(n->id);
+    put(n->parent->id);
+    put(static_cast<int64_t>(n->tokens.size()));
+    put(n->ref);
+    put(n->tick);
+    for (int32_t t : n->tokens) put(t);
+    for (int32_t s : n->slots) put(s);
+    push_children(n);
+  }
+  return pos;
+}
+
+}  // namespace rax

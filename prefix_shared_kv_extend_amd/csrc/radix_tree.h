@@ -1,0 +1,97 @@
+// Host radix tree over a token-granular KV pool, with the pool's slot allocator.
+//
+// Operations follow the pages: longest-prefix match ("traverse"), insert of a
+// finished or prefilled request as new edges / leaves, node split at a divergence
+// point, ref counts that pin nodes used by running requests, and LRU eviction of
+// leaves, with cached and running KV sharing one pool
+// (2312.07104_SGLang notes, §3 and Figure 3; bowenzhou SGLang review, "Work loop";
+// hustzhy SGLang post, §2.3). The reproducibility rules where the pages are silent
+// (split on match, one logical tick per call, whole-leaf eviction, lowest-slot-first
+// allocation, duplicate slots returned on insert) are stated in include/rax.h.
+#pragma once
+
+#include <cstdint>
+#include <set>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+namespace rax {
+
+// Free set of pool slots; hands out the lowest ids first.
+class SlotAllocator {
+ public:
+  explicit SlotAllocator(int64_t num_slots);
+  int64_t num_slots() const { return num_slots_; }
+  int64_t num_free() const { return num_free_; }
+  bool is_free(int32_t s) const { return (words_[s >> 6] >> (s & 63)) & 1ull; }
+  // Takes n lowest free slots into out (ascending). False (nothing taken) if short.
+  bool alloc(int64_t n, int32_t* out);
+  // Returns slots; the caller has checked they are in range and not free.
+  void release(const int32_t* slots, int64_t n);
+  void release_one(int32_t s);
+
+ private:
+  int64_t num_slots_;
+  int64_t num_free_;
+  int64_t hint_;                 // no free bit below word hint_
+  std::vector<uint64_t> words_;  // bit set = slot free
+};
+
+struct Node {
+  int64_t id = 0;
+  Node* parent = nullptr;
+  std::vector<int32_t> tokens;  // edge label
+  std::vector<int32_t> slots;   // one pool slot per label token
+  std::unordered_map<int32_t, Node*> children;  // keyed by the child's first token
+  int64_t depth_end = 0;        // tokens from the root to the end of this node
+  int32_t ref = 0;
+  int64_t tick = 0;
+  bool in_lru = false;
+};
+
+class RadixTree {
+ public:
+  explicit RadixTree(int64_t num_slots);
+  ~RadixTree();
+  RadixTree(const RadixTree&) = delete;
+  RadixTree& operator=(const RadixTree&) = delete;
+
+  SlotAllocator& alloc() { return alloc_; }
+  const SlotAllocator& alloc() const { return alloc_; }
+
+  int64_t match(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_node);
+  // Returns false (nothing changed) if a caller slot is out of range or free.
+  bool insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
+              int64_t* out_existing, int64_t* out_node);
+  // 0 ok, 1 unknown node, 2 would go below zero.
+  int lock_ref(int64_t node, int32_t delta);
+  int64_t evict(int64_t num_tokens, int32_t* out_freed, int64_t cap);
+  bool lca_depth(int64_t a, int64_t b, int64_t* out) const;
+  const Node* find(int64_t id) const;
+  int64_t dump(int64_t* buf, int64_t cap) const;  // returns words needed
+
+  int64_t num_nodes() const { return static_cast<int64_t>(nodes_.size()) - 1; }
+  int64_t clock() const { return clock_; }
+  void totals(int64_t* cached, int64_t* locked) const;
+  int64_t matched_total = 0, inserted_total = 0, evicted_total = 0;
+
+ private:
+  Node* new_node();
+  Node* split(Node* child, int64_t k);  // upper part gets the first k tokens
+  // Walks the longest cached prefix, splitting at its end. Returns the end node and
+  // the matched length; appends the slots if out != nullptr.
+  Node* walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out);
+  void tick_path(Node* n);
+  void lru_update(Node* n);  // re-evaluate leaf/ref-0 membership
+  void lru_remove(Node* n);
+
+  SlotAllocator alloc_;
+  Node* root_;
+  int64_t next_id_ = 1;
+  int64_t clock_ = 0;
+  std::unordered_map<int64_t, Node*> nodes_;
+  std::set<std::pair<int64_t, int64_t>> lru_;  // (tick, id) of leaves with ref 0
+};
+
+}  // namespace rax

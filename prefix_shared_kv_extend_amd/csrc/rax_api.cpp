@@ -1,0 +1,163 @@
+// C ABI: host radix-tree entry points of librax (declared in include/rax.h).
+#include <new>
+#include <vector>
+
+#include "../../include/rax.h"
+#include "radix_tree.h"
+
+struct rax_tree {
+  explicit rax_tree(int64_t n) : t(n) {}
+  rax::RadixTree t;
+};
+
+#define RAX_GUARD_BEGIN try {
+#define RAX_GUARD_END                 \
+  }                                   \
+  catch (const std::bad_alloc&) {     \
+    return RAX_ENOMEM;                \
+  }                                   \
+  catch (...) {                       \
+    return RAX_EINVAL;                \
+  }
+
+extern "C" {
+
+const char* rax_status_str(rax_status s) {
+  switch (s) {
+    case RAX_OK: return "ok";
+    case RAX_EINVAL: return "invalid argument";
+    case RAX_ENOMEM: return "not enough free slots or memory";
+    case RAX_ESTATE: return "unknown node or ref count below zero";
+    case RAX_EDEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+int32_t rax_abi_version(void) { return 1; }
+
+rax_status rax_tree_create(int64_t num_slots, rax_tree** out) {
+  if (!out || num_slots < 1 || num_slots >= (int64_t(1) << 31)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  *out = new rax_tree(num_slots);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+void rax_tree_destroy(rax_tree* t) { delete t; }
+
+rax_status rax_match_prefix(rax_tree* t, const int32_t* tokens, int64_t n, int32_t* out_slots,
+                            int64_t* out_len, rax_node* out_node) {
+  if (!t || n < 0 || !out_len || !out_node || (n > 0 && (!tokens || !out_slots))) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  *out_len = t->t.match(tokens, n, out_slots, out_node);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_insert(rax_tree* t, const int32_t* tokens, const int32_t* slots, int64_t n,
+                      int32_t* out_slots, int64_t* out_existing, rax_node* out_node) {
+  if (!t || n < 0 || !out_existing || !out_node || (n > 0 && (!tokens || !slots))) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  if (!t->t.insert(tokens, slots, n, out_slots, out_existing, out_node)) return RAX_EINVAL;
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_lock_ref(rax_tree* t, rax_node node, int32_t delta) {
+  if (!t || (delta != 1 && delta != -1)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  return t->t.lock_ref(node, delta) == 0 ? RAX_OK : RAX_ESTATE;
+  RAX_GUARD_END
+}
+
+rax_status rax_evict_lru(rax_tree* t, int64_t num_tokens, int32_t* out_freed, int64_t cap,
+                         int64_t* out_num_freed) {
+  if (!t || num_tokens < 0 || cap < 0 || !out_num_freed || (cap > 0 && !out_freed)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  *out_num_freed = t->t.evict(num_tokens, out_freed, cap);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_alloc_slots(rax_tree* t, int64_t n, int32_t* out_slots) {
+  if (!t || n < 0 || (n > 0 && !out_slots)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  return t->t.alloc().alloc(n, out_slots) ? RAX_OK : RAX_ENOMEM;
+  RAX_GUARD_END
+}
+
+rax_status rax_free_slots(rax_tree* t, const int32_t* slots, int64_t n) {
+  if (!t || n < 0 || (n > 0 && !slots)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  const rax::SlotAllocator& a = t->t.alloc();
+  std::vector<uint8_t> seen;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t s = slots[i];
+    if (s < 0 || s >= a.num_slots() || a.is_free(s)) return RAX_EINVAL;
+  }
+  if (n > 1) {
+    seen.assign(static_cast<size_t>(a.num_slots()), 0);
+    for (int64_t i = 0; i < n; ++i) {
+      if (seen[slots[i]]) return RAX_EINVAL;
+      seen[slots[i]] = 1;
+    }
+  }
+  t->t.alloc().release(slots, n);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_lca_depth(const rax_tree* t, rax_node a, rax_node b, int64_t* out_depth) {
+  if (!t || !out_depth) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  return t->t.lca_depth(a, b, out_depth) ? RAX_OK : RAX_ESTATE;
+  RAX_GUARD_END
+}
+
+rax_status rax_tree_stats(const rax_tree* t, rax_stats* out) {
+  if (!t || !out) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  const rax::RadixTree& r = t->t;
+  out->num_slots = r.alloc().num_slots();
+  out->free_slots = r.alloc().num_free();
+  r.totals(&out->cached_tokens, &out->locked_tokens);
+  out->evictable_tokens = out->cached_tokens - out->locked_tokens;
+  out->num_nodes = r.num_nodes();
+  out->clock = r.clock();
+  out->matched_tokens = r.matched_total;
+  out->inserted_tokens = r.inserted_total;
+  out->evicted_tokens = r.evicted_total;
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_tree_dump(const rax_tree* t, int64_t* buf, int64_t cap, int64_t* out_len) {
+  if (!t || !out_len || cap < 0) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  const int64_t need = t->t.dump(buf, buf ? cap : 0);
+  *out_len = need;
+  if (buf && need > cap) return RAX_EINVAL;
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_free_count(const rax_tree* t, int64_t* out) {
+  if (!t || !out) return RAX_EINVAL;
+  *out = t->t.alloc().num_free();
+  return RAX_OK;
+}
+
+rax_status rax_alloc_slots_evict(rax_tree* t, int64_t n, int32_t* out_slots, int32_t* out_freed,
+                                 int64_t cap, int64_t* out_num_freed) {
+  if (!t || n < 0 || cap < 0 || !out_num_freed || (n > 0 && !out_slots) || (cap > 0 && !out_freed))
+    return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  rax::RadixTree& r = t->t;
+  *out_num_freed = 0;
+  const int64_t short_by = n - r.alloc().num_free();
+  if (short_by > 0) *out_num_freed = r.evict(short_by, out_freed, cap);
+  return r.alloc().alloc(n, out_slots) ? RAX_OK : RAX_ENOMEM;
+  RAX_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+* kv_scatter and the req_to_token fill are checked bit for bit.
+* Whole traces run through RadixRuntime on the GPU; their host event logs
+  (matches, evictions, allocations, inserts), final slot rows and tree dumps
+  must equal the oracle's replay exactly, and attention outputs must agree with
+  fp64 attention recomputed from scratch over each full sequence within
+  max-abs 1e-5 (fp32 inputs) or 1e-2 (bf16 inputs, fp32 accumulation).
+* Small traces are checked at every output; the full-size configurations are
+  checked on sampled outputs (the oracle recomputes each sample from scratch).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import outputs_from_scratch
+from oracle.runner import run_trace
+from workloads import configs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from prefix_shared_kv_extend_amd import _lib
+    _lib.lib()          # fails loudly if librax.so is missing
+    yield
+
+
+def _collect(job, runner_kw=None, pick=None, progress=0):
+    """Run the job on the GPU; keep outputs chosen by pick(kind, step, rid, pos) -> bool."""
+    from prefix_shared_kv_extend_amd.driver import JobRunner
+    got = {}
+
+    def keep(kind, si, pairs, o):
+        idx = [i for i, (rid, p) in enumerate(pairs) if pick is None or pick(kind, si, rid, p)]
+        if idx:
+            sel = o[torch.tensor(idx, device=o.device)].float().cpu().numpy()
+            for j, i in enumerate(idx):
+                got[pairs[i]] = sel[j]
+
+    r = JobRunner(job, **(runner_kw or {}))
+    r.run(on_extend=lambda si, eb, pairs, o: keep("extend", si, pairs, o),
+          on_decode=lambda si, db, pairs, o: keep("decode", si, pairs, o), progress=progress)
+    torch.cuda.synchronize()
+    return r, got
+
+
+def _check_outputs(job, got, tol):
+    by_rid = {}
+    for (rid, p), o in got.items():
+        by_rid.setdefault(rid, []).append((p, o))
+    worst = 0.0
+    for rid, items in by_rid.items():
+        pos = [p for p, _ in items]
+        ref = outputs_from_scratch(job.full_tokens(rid), pos, job.h_q, job.h_kv, job.d, job.seed, job.dtype)
+        for i, (p, o) in enumerate(items):
+            err = float(np.abs(o.astype(np.float64) - ref[i]).max())
+            worst = max(worst, err)
+            assert err <= tol, f"rid {rid} pos {p}: max abs err {err:.3g} > {tol}"
+    return worst
+
+
+def _check_host(job, runner):
+    ref = run_trace(job)
+    assert len(runner.log) == len(ref["log"])
+    for a, b in zip(runner.log, ref["log"]):
+        assert a == b
+    assert runner.final_rows == ref["rows"]
+    assert runner.rt.tree.dump() == ref["dump"]
+    from prefix_shared_kv_extend_amd import _lib
+    assert _lib.device_errors() == 0
+
+
+# ------------------------------------------------------------------ data movement
+def test_kv_scatter_bit_exact():
+    from prefix_shared_kv_extend_amd import _lib
+    say("kv_scatter: bf16 [777, 8, 128] and fp32 [33, 4, 64] into shuffled slots")
+    g = torch.Generator().manual_seed(1)
+    for dt, (n, h, d), S in ((torch.bfloat16, (777, 8, 128), 5000), (torch.float32, (33, 4, 64), 100)):
+        k = torch.randn((n, h, d), generator=g).to(dt).cuda()
+        v = torch.randn((n, h, d), generator=g).to(dt).cuda()
+        loc = torch.randperm(S, generator=g)[:n].to(torch.int32)
+        kp = torch.zeros((S, h, d), dtype=dt, device="cuda")
+        vp = torch.zeros_like(kp)
+        _lib.kv_scatter(k, v, loc.cuda(), kp, vp)
+        torch.cuda.synchronize()
+        kp, vp, loc = kp.cpu(), vp.cpu(), loc.long()
+        assert torch.equal(kp[loc], k.cpu()) and torch.equal(vp[loc], v.cpu())
+        untouched = torch.ones(S, dtype=torch.bool)
+        untouched[loc] = False
+        assert int(kp[untouched].abs().sum()) == 0 and int(vp[untouched].abs().sum()) == 0
+    assert _lib.device_errors() == 0
+
+
+def test_kv_scatter_out_of_range_slot_is_skipped_and_flagged():
+    from prefix_shared_kv_extend_amd import _lib
+    say("kv_scatter: slot ids -1 and S are skipped by the kernel's own bounds check")
+    S, h, d = 16, 2, 64
+    k = torch.ones((3, h, d), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((S, h, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    _lib.kv_scatter(k, k, torch.tensor([-1, 5, S], dtype=torch.int32, device="cuda"), kp, vp)
+    assert _lib.device_errors() == _lib.DEVERR_SLOT
+    assert float(kp.sum()) == h * d and float(kp[5].sum()) == h * d
+    assert _lib.device_errors() == 0                  # cleared by the read
+
+
+def test_req_to_token_write_bit_exact():
+    from prefix_shared_kv_extend_amd import _lib
+    say("req_to_token_write: 5 requests, ragged spans")
+    rtt = torch.full((8, 50), -7, dtype=torch.int32, device="cuda")
+    rows = [3, 0, 7, 1, 5]
+    start = [0, 10, 49, 2, 0]
+    lens = [4, 0, 1, 9, 50]
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    src = np.arange(indptr[-1], dtype=np.int32) * 3 + 1
+    c = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device="cuda")
+    _lib.req_to_token_write(rtt, c(rows), c(start), c(indptr), c(src), int(indptr[-1]))
+    want = np.full((8, 50), -7, dtype=np.int32)
+    for r in range(5):
+        want[rows[r], start[r]: start[r] + lens[r]] = src[indptr[r]: indptr[r + 1]]
+    assert np.array_equal(rtt.cpu().numpy(), want)
+    assert _lib.device_errors() == 0
+
+
+# ------------------------------------------------------------- whole small traces
+SMALL = {
+    "tiny_fp32_d64": lambda: configs.tiny(),
+    "tiny_fp32_d128": lambda: configs.tiny(n_req=4, prefix=130, suffix=7, n_decode=5, h=4, d=128),
+    "fewshot_bf16_ragged": lambda: configs.fewshot(n_req=5, prefix=300, suffix=37, n_decode=3, h=4,
+                                                   num_slots=4096),
+    "fewshot_bf16_d64_many": lambda: configs.fewshot(n_req=70, prefix=65, suffix=3, n_decode=2, h=2, d=64,
+                                                     num_slots=8192),
+    "two_level_bf16": lambda: configs.two_level(system=100, n_blocks=3, block=70, n_q=4, q=9, n_decode=3,
+                                                h=4, num_slots=8192),
+    "self_consistency_gqa8": lambda: configs.self_consistency(prefix=200, n_branch=12, max_branch=90,
+                                                              n_decode=4, h_q=16, h_kv=2, num_slots=8192),
+    "self_consistency_gqa16_zero_branch": lambda: configs.self_consistency(prefix=70, n_branch=40,
+                                                                           max_branch=2, n_decode=2, h_q=16,
+                                                                           h_kv=1, num_slots=4096),
+    "multi_turn_evicting": lambda: configs.multi_turn(n_sessions=12, max_depth=3, median=40, lo=4, hi=150,
+                                                      system=30, h_q=8, h_kv=2, max_running=6,
+                                                      max_extend_tokens=400),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_trace_every_output(name):
+    job = SMALL[name]()
+    say(f"trace {name}: {job.dtype} h_q={job.h_q} h_kv={job.h_kv} d={job.d} "
+        f"requests={len(job.requests)} steps={len(job.steps)}")
+    runner, got = _collect(job)
+    _check_host(job, runner)
+    worst = _check_outputs(job, got, TOL[job.dtype])
+    say(f"  checked {len(got)} outputs, worst max-abs {worst:.3g}")
+    if name == "multi_turn_evicting":
+        assert any(e[0] == "evict" for e in runner.log)
+    if name == "self_consistency_gqa16_zero_branch":
+        assert 0 in job.notes["branch_lens"]
+
+
+def test_bf16_output_dtype():
+    job = configs.fewshot(n_req=3, prefix=100, suffix=20, n_decode=2, h=4, num_slots=2048)
+    say("fewshot with bf16 outputs")
+    runner, got = _collect(job, runner_kw=dict(out_dtype=torch.bfloat16))
+    _check_outputs(job, got, TOL["bf16"])
+
+
+# ------------------------------------------------------------- full-size configs
+def _pick_sampled(job, rng, per_step=3):
+    ext = {}
+    dec = {}
+    for si, st in enumerate(job.steps):
+        if st.extend:
+            ext[si] = set(rng.choice(st.extend, size=min(per_step, len(st.extend)), replace=False).tolist())
+            ext[si] |= {st.extend[0], st.extend[-1]}
+        if st.decode:
+            dec[si] = set(rng.choice(st.decode, size=min(per_step, len(st.decode)), replace=False).tolist())
+
+    def pick(kind, si, rid, p):
+        if kind == "extend":
+            r = job.requests[rid]
+            return rid in ext.get(si, ()) and (p == r.n - 1 or p % 97 == 0)
+        return rid in dec.get(si, ()) and (si % 8 == 0 or si == len(job.steps) - 1)
+    return pick
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_full_config_sampled(index):
+    job = configs.make(index)
+    say(f"config {index} ({job.name}) full size: requests={len(job.requests)} steps={len(job.steps)}")
+    rng = np.random.default_rng(index)
+    runner, got = _collect(job, pick=_pick_sampled(job, rng), progress=16)
+    _check_host(job, runner)
+    worst = _check_outputs(job, got, TOL[job.dtype])
+    say(f"  checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")
+
+
+def test_full_multi_turn_sampled():
+    job = configs.make(4)
+    say(f"config 4 (multi_turn) full size: requests={len(job.requests)} steps={len(job.steps)} "
+        f"pool={job.num_slots}")
+    rng = np.random.default_rng(4)
+    chosen = {}
+    for si in range(0, len(job.steps), 300):
+        st = job.steps[si]
+        c = []
+        if st.extend:
+            c.append(("extend", int(rng.choice(st.extend))))
+        if st.decode:
+            c.append(("decode", int(rng.choice(st.decode))))
+        chosen[si] = c
+
+    def pick(kind, si, rid, p):
+        if (kind, rid) not in chosen.get(si, ()):
+            return False
+        return kind == "decode" or p == job.requests[rid].n - 1 or p % 211 == 0
+
+    runner, got = _collect(job, pick=pick, progress=500)
+    say("  GPU run done; replaying the trace in the oracle")
+    _check_host(job, runner)
+    say("  host log identical; checking sampled outputs")
+    worst = _check_outputs(job, got, TOL[job.dtype])
+    say(f"  checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")

@@ -9,13 +9,15 @@ HellaSwag, self-consistency and multi-turn chat; 2312.07104_SGLang notes,
 App. A.1 Fig. 9) without using any benchmark item.
 
 Lifecycle that both the harness and the oracle apply to a trace, per step:
-  1. extend, in the listed order, per request: match the prompt, lock the
-     matched node, allocate slots for the unmatched suffix (evicting LRU leaves
-     if the pool is short); then run attention for the suffix queries; then
-     insert the prompt, lock the new node and unlock the old one.
-  2. decode, in the listed order: allocate one slot per request for the token
-     generated k-th (output[k], at position len(prompt) + k); then attention.
-  3. finish: insert prompt + output, unlock the held node.
+  1. extend: in the listed order, match each prompt and lock the matched node;
+     then allocate the slots of all unmatched suffixes at once (evicting LRU
+     leaves first if the pool is short) and hand them out in request order;
+     run attention for the suffix queries; then, in order, insert each prompt,
+     lock the new node and unlock the old one.
+  2. decode: allocate one slot per listed request at once (evicting if short),
+     in request order, for the token generated k-th (output[k], at position
+     len(prompt) + k); then attention.
+  3. finish: in order, insert prompt + output and unlock the held node.
 A match that covers the whole prompt is cut to len(prompt) - 1 so that the
 last prompt token is recomputed (the request needs one query to run).
 """

@@ -81,21 +81,20 @@ def prefix_hashes(tokens, seed: int, h0: int | None = None) -> np.ndarray:
 
 
 def prefix_hashes_batch(seqs: list, seed: int) -> list:
-    """prefix_hashes for many sequences, vectorised over sequences of equal length."""
-    out = [None] * len(seqs)
-    by_len: dict[int, list[int]] = {}
+    """prefix_hashes for many sequences at once (vectorised over sequences, padded)."""
+    if not seqs:
+        return []
+    lens = [len(s) for s in seqs]
+    lmax = max(lens)
+    toks = np.zeros((len(seqs), max(lmax, 1)), dtype=np.uint64)
     for i, s in enumerate(seqs):
-        by_len.setdefault(len(s), []).append(i)
-    for n, idx in by_len.items():
-        toks = np.stack([np.asarray(seqs[i], dtype=np.int64) for i in idx]).astype(np.uint64)
-        h = np.full(len(idx), splitmix64(seed & MASK64), dtype=np.uint64)
-        res = np.empty((len(idx), n), dtype=np.uint64)
-        for p in range(n):
-            h = _splitmix64_np(h ^ toks[:, p])
-            res[:, p] = h
-        for j, i in enumerate(idx):
-            out[i] = res[j]
-    return out
+        toks[i, : lens[i]] = np.asarray(s, dtype=np.int64).astype(np.uint64)
+    h = np.full(len(seqs), splitmix64(seed & MASK64), dtype=np.uint64)
+    res = np.empty((len(seqs), lmax), dtype=np.uint64)
+    for p in range(lmax):
+        h = _splitmix64_np(h ^ toks[:, p])
+        res[:, p] = h
+    return [res[i, : lens[i]].copy() for i in range(len(seqs))]
 
 
 # ----------------------------------------------------------- torch (any device)
