@@ -1,0 +1,245 @@
+"""Benchmark of the RadixAttention hot path on one MI355X.
+
+Workload (the few-shot configuration): one attention layer at Llama-2-7B attention
+shape (32 heads MHA, head_dim 128), bf16 inputs, fp32 accumulation, bf16 outputs;
+64 requests share a 2000-token prefix and each adds a distinct 50-token suffix;
+pool of 2^20 token slots; then 32 decode steps for all 64 requests.
+
+One timed step = the whole job from an empty cache, through the C ABI:
+  request 0 cold (match, lock, allocate, fill req_to_token, KV write-back, extend
+  attention over 2050 tokens, insert); the other 63 reuse its 2000-token prefix
+  (match splits its node) and extend only their 50 suffix tokens; 32 decode
+  steps (allocate, fill, write-back, decode attention); finish (insert prompt +
+  output, unlock); then evict the whole tree, so the next step starts empty.
+Q/K/V for every call are generated before timing and stay resident in HBM.
+
+value = attention tokens per second for the whole step (5200 extend queries +
+2048 decode queries, wall clock, host tree work included). The JSON line also
+carries per-phase kernel timings, the roofline of the dominant kernel (measured
+with HIP events on the stream the kernels run on) and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "attn tokens/s (extend, decode) + % MFMA/HBM peak on radix-cached KV"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain copy kernel of known size (for counter scaling) and exit")
+    return ap.parse_args()
+
+
+class Prepared:
+    """Pre-generated inputs for every attention call of one job, in call order."""
+
+    def __init__(self, runner, dev):
+        import torch
+        self.calls = []
+        job = runner.job
+        seen = {}
+
+        def grab(kind):
+            def cb(si, batch, pairs, o):
+                seen.setdefault(si, {})[kind] = list(pairs)
+            return cb
+
+        runner.run(on_extend=grab("extend"), on_decode=grab("decode"))
+        torch.cuda.synchronize()
+        for si in sorted(seen):
+            for kind in ("extend", "decode"):
+                if kind in seen[si]:
+                    q, k, v = runner.qkv(seen[si][kind])
+                    o = torch.empty((q.shape[0], job.h_q, job.d), dtype=torch.bfloat16, device=dev)
+                    self.calls.append((si, kind, seen[si][kind], q, k, v, o))
+
+
+def algorithmic(job, prep):
+    """Flops of each extend call and unique bytes of each decode call (per launch)."""
+    D, hq, hkv = job.d, job.h_q, job.h_kv
+    elt = 2
+    ext_flops, dec_bytes = [], []
+    for si, kind, pairs, q, k, v, o in prep.calls:
+        if kind == "extend":
+            ext_flops.append(sum(4.0 * D * hq * (p + 1) for _, p in pairs))
+        else:
+            # distinct slots read: the shared prefix once plus every request's own positions
+            lens = [p + 1 for _, p in pairs]
+            shared = 2000
+            distinct = shared + sum(n - shared for n in lens)
+            kv = distinct * 2 * hkv * D * elt
+            qo = len(pairs) * hq * D * elt * 2
+            idx = sum(lens) * 4
+            dec_bytes.append(kv + qo + idx)
+    return ext_flops, dec_bytes
+
+
+def run_step(runner, prep, timers=None):
+    rt = runner.rt
+    job = runner.job
+    rt.timers = timers
+    it = iter(prep.calls)
+    for si, st in enumerate(job.steps):
+        rt.step = si
+        if st.extend:
+            eb = rt.begin_extend([(rid, job.requests[rid].prompt) for rid in st.extend])
+            _, kind, pairs, q, k, v, o = next(it)
+            rt.run_extend(eb, q, k, v, o)
+            rt.end_extend(eb, {rid: job.requests[rid].prompt for rid in eb.rids})
+        if st.decode:
+            db = rt.begin_decode(st.decode)
+            _, kind, pairs, q, k, v, o = next(it)
+            rt.run_decode(db, q, k, v, o)
+        for rid in st.finish:
+            rt.finish(rid, runner.full[rid][: len(rt.reqs[rid].slots)])
+    rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next step starts empty
+    rt.timers = None
+
+
+def cpu_baseline(job, seconds):
+    """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
+    import torch
+    from oracle.attention import outputs_from_scratch
+    threads = len(os.sched_getaffinity(0))
+    torch.set_num_threads(threads)
+    rng = np.random.default_rng(0)
+    done = 0
+    t0 = time.perf_counter()
+    reqs = []
+    while time.perf_counter() - t0 < seconds:
+        rid = int(rng.integers(1, len(job.requests)))
+        r = job.requests[rid]
+        # all 50 suffix queries of one cached request plus its first decode query
+        pos = list(range(2000, r.n)) + [r.n]
+        outputs_from_scratch(job.full_tokens(rid), pos, job.h_q, job.h_kv, job.d, job.seed, job.dtype)
+        done += len(pos)
+        reqs.append(rid)
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "attn tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(reqs)} cached requests x (50 suffix queries + 1 decode query), each recomputed "
+                      f"from scratch over its 2051-token sequence in fp64 ({dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path would shard by KV heads or by requests, with no exchange inside attention)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from prefix_shared_kv_extend_amd import _lib
+    from prefix_shared_kv_extend_amd.driver import JobRunner
+    from workloads import configs
+
+    _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calib:
+        # plain copy through kv_scatter with identity slots: reads and writes 2 x 512 MiB
+        n = 1 << 15
+        k = torch.ones((n, 64, 128), dtype=torch.bfloat16, device=dev)
+        kp = torch.empty_like(k)
+        vp = torch.empty_like(k)
+        loc = torch.arange(n, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            _lib.kv_scatter(k, k, loc, kp, vp)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": 2 * k.numel() * 2 + n * 4, "copy_calib_bytes_written":
+                          2 * k.numel() * 2}))
+        return
+
+    job = configs.make(1)
+    runner = JobRunner(job, device="cuda:0", out_dtype=torch.bfloat16, record_log=False)
+    prep = Prepared(runner, dev)                       # one untimed pass to learn every call's positions
+    runner.rt.tree.evict_lru(runner.rt.num_slots)
+    ext_flops, dec_bytes = algorithmic(job, prep)
+    n_ext_tok = sum(len(c[2]) for c in prep.calls if c[1] == "extend")
+    n_dec_tok = sum(len(c[2]) for c in prep.calls if c[1] == "decode")
+
+    for _ in range(args.warmup):
+        run_step(runner, prep)
+    torch.cuda.synchronize()
+
+    timers = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(runner, prep, timers)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    ext_us = [a.elapsed_time(b) * 1e3 for a, b in timers.get("extend", [])]
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in timers.get("decode", [])]
+    per_step_ext = sum(ext_us) / args.steps
+    per_step_dec = sum(dec_us) / args.steps
+    ext_tflops = sum(ext_flops) * args.steps / (sum(ext_us) * 1e-6) / 1e12
+    dec_gbs = sum(dec_bytes) * args.steps / (sum(dec_us) * 1e-6) / 1e9
+    if per_step_ext >= per_step_dec:
+        roof = {"kernel": "extend attention (attn_kernel<bf16,128,extend>)", "bound": "mfma",
+                "achieved": ext_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ext_tflops / MFMA_BF16_PEAK_TFLOPS, "launches_per_step": len(ext_flops),
+                "avg_launch_us": sum(ext_us) / len(ext_us)}
+    else:
+        roof = {"kernel": "decode attention (attn_kernel<bf16,128,decode> + split-K merge)", "bound": "hbm",
+                "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                "launches_per_step": len(dec_bytes), "avg_launch_us": sum(dec_us) / len(dec_us)}
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            roof["traffic"] = json.load(f).get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": (n_ext_tok + n_dec_tok) * args.steps / (t1 - t0),
+        "unit": "attn tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded tokens; Q/K/V from a prefix-hash generator (N(0,1)), no model weights",
+        "config": {"workload": "fewshot: 64 requests x (2000 shared + 50 own) tokens, then 32 decode steps; "
+                               "1 layer, 32 heads MHA, head_dim 128, pool 2^20 slots",
+                   "extend_tokens_per_step": n_ext_tok, "decode_tokens_per_step": n_dec_tok,
+                   "prompt_tokens_per_step": sum(r.n for r in job.requests)},
+        "extend": {"kernel_us_per_step": per_step_ext, "tok_s_kernel": n_ext_tok / (per_step_ext * 1e-6),
+                   "tflops": ext_tflops, "frac_mfma_peak": ext_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "decode": {"kernel_us_per_step": per_step_dec, "tok_s_kernel": n_dec_tok / (per_step_dec * 1e-6),
+                   "gbs_unique": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS},
+        "hit_rate": 1.0 - n_ext_tok / sum(r.n for r in job.requests),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

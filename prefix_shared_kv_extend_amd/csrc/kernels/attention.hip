@@ -114,7 +114,7 @@ __device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int es
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + elem_off * esize);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kDecode>
 __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   using TL = Tile<T, D>;
   constexpr bool kBf16 = sizeof(T) == 2;
@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   // ---- block metadata (requests covered, shared length, tile list)
   if (tid == 0) {
     int r0, r1;
-    if (a.qo_indptr) {
+    if (!kDecode) {
       r0 = upper_req(a.qo_indptr, a.batch, qa);
       r1 = upper_req(a.qo_indptr, a.batch, qb - 1);
     } else {
@@ -170,9 +170,9 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
     }
     sm.req_row[i] = row;
     sm.req_m[i] = m;
-    sm.req_qo[i] = a.qo_indptr ? a.qo_indptr[r] : r;
+    sm.req_qo[i] = kDecode ? r : a.qo_indptr[r];
   }
-  if (tid == 0) sm.req_qo[nreq] = a.qo_indptr ? a.qo_indptr[r0 + nreq] : r0 + nreq;
+  if (tid == 0) sm.req_qo[nreq] = kDecode ? r0 + nreq : a.qo_indptr[r0 + nreq];
   __syncthreads();
   if (tid == 0) {
     int L;
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
     sm.own[nreq] = acc;
     const int n_sh = (L + BN - 1) / BN;
     int n_suf = 0;
-    if (a.k_ext) n_suf = (int)((qb - sm.req_qo[0] + BN - 1) / BN);
+    if (!kDecode) n_suf = (int)((qb - sm.req_qo[0] + BN - 1) / BN);
     const int total = n_sh + acc + n_suf;
     sm.hdr[2] = L;
     sm.hdr[3] = n_sh;
@@ -544,7 +544,10 @@ static size_t ws_bytes_for(int64_t items, int d) {
 template <typename T, int D>
 static rax_status launch(AttnArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-  hipLaunchKernelGGL((attn_kernel<T, D>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+  if (a.qo_indptr)
+    hipLaunchKernelGGL((attn_kernel<T, D, false>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, D, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
   if (a.nsplit > 1) {
     const int64_t rows = a.total_q * a.g;

@@ -75,6 +75,7 @@ class RadixRuntime:
         self.reqs: dict[int, ReqState] = {}
         self.log = log
         self.step = 0                 # label of the current step in the event log (set by the caller)
+        self.timers = None            # {"extend": [...], "decode": [...]} of (start, end) events, if set
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     # ------------------------------------------------------------------ helpers
@@ -106,6 +107,15 @@ class RadixRuntime:
         for i in range(1, len(rids)):
             out[i] = self.tree.lca_depth(self.reqs[rids[i - 1]].node, self.reqs[rids[i]].node)
         return out
+
+    def _event_pair(self, kind):
+        """When timing is on: record a start event now on the current stream, return (start, end)."""
+        if self.timers is None:
+            return None
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        pair[0].record()
+        self.timers.setdefault(kind, []).append(pair)
+        return pair
 
     def _log(self, *ev):
         if self.log is not None:
@@ -160,8 +170,11 @@ class RadixRuntime:
         if eb.total_q == 0:
             return
         L.kv_scatter(k_ext, v_ext, eb.dev["out_loc"], self.k_pool, self.v_pool)
+        ev = self._event_pair("extend")
         L.extend_attention(q, k_ext, v_ext, self.k_pool, self.v_pool, self.rtt, eb.dev["req_pool_idx"],
                            eb.dev["prefix_len"], eb.dev["qo_indptr"], o, shared_len=eb.dev["shared_len"])
+        if ev:
+            ev[1].record()
 
     def end_extend(self, eb: ExtendBatch, prompts: dict) -> None:
         """Insert every prompt; requests switch to the tree's copy of any duplicate slots."""
@@ -212,8 +225,11 @@ class RadixRuntime:
         L.kv_scatter(k_new, v_new, db.dev["out_loc"], self.k_pool, self.v_pool)
         ws = self._workspace(L.attention_workspace_bytes(True, len(db.rids), self.h_q, self.h_kv, self.d,
                                                          db.max_seq_len))
+        ev = self._event_pair("decode")
         L.decode_attention(q, self.k_pool, self.v_pool, self.rtt, db.dev["req_pool_idx"], db.dev["seq_len"],
                            db.max_seq_len, o, workspace=ws, shared_len=db.dev["shared_len"])
+        if ev:
+            ev[1].record()
 
     # ------------------------------------------------------------------- finish
     def finish(self, rid: int, tokens) -> list:
