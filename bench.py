@@ -111,8 +111,8 @@ def run_step(runner, prep, timers=None):
             db = rt.begin_decode(st.decode)
             _, kind, pairs, q, k, v, o = next(it)
             rt.run_decode(db, q, k, v, o)
-        for rid in st.finish:
-            rt.finish(rid, runner.full[rid][: len(rt.reqs[rid].slots)])
+        if st.finish:
+            rt.finish_batch([(rid, runner.full[rid][: rt.seq_len(rid)]) for rid in st.finish])
     rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next step starts empty
     rt.timers = None
 

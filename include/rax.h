@@ -140,6 +140,29 @@ rax_status rax_free_slots(rax_tree* t, const int32_t* slots, int64_t n);
  * requests holding nodes a and b have identical slots on exactly these positions. */
 rax_status rax_lca_depth(const rax_tree* t, rax_node a, rax_node b, int64_t* out_depth);
 
+/* Batched forms for a scheduler that handles a whole batch per call ([notes] App. A.2:
+ * match every waiting request, then form the batch). Request r's tokens are
+ * tokens[indptr[r] .. indptr[r+1]) (indptr: batch + 1 int64 entries, indptr[0] = 0).
+ *
+ * rax_match_prefix_batch: rax_match_prefix on each request in order; its slots go to
+ * out_slots[indptr[r] ..] (capacity indptr[batch]). cut_full != 0: a match covering a
+ * whole non-empty request is reported as n - 1 (the node stays the one covering all n).
+ * lock != 0: rax_lock_ref(node, +1) after each match. */
+rax_status rax_match_prefix_batch(rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                                  int32_t cut_full, int32_t lock, int32_t* out_slots, int64_t* out_len,
+                                  rax_node* out_node);
+/* rax_insert on each request in order, with slots[indptr[r] ..]; out_slots (nullable,
+ * capacity indptr[batch]) receives the tree's slots. On RAX_EINVAL (a bad slot) the
+ * requests before the failing one stay inserted; *out_done (nullable) counts them. */
+rax_status rax_insert_batch(rax_tree* t, const int32_t* tokens, const int32_t* slots, const int64_t* indptr,
+                            int32_t batch, int32_t* out_slots, int64_t* out_existing, rax_node* out_node,
+                            int32_t* out_done);
+/* rax_lock_ref on nodes[0..n) in order. All-or-nothing: RAX_ESTATE changes nothing. */
+rax_status rax_lock_ref_batch(rax_tree* t, const rax_node* nodes, int32_t n, int32_t delta);
+/* out[0] = 0 and out[i] = rax_lca_depth(nodes[i-1], nodes[i]) for 0 < i < n: the
+ * shared_len hint of consecutive requests for the attention kernels. */
+rax_status rax_lca_depths(const rax_tree* t, const rax_node* nodes, int32_t n, int32_t* out);
+
 rax_status rax_tree_stats(const rax_tree* t, rax_stats* out);
 
 /* Serialise the tree in preorder (children by ascending first token), as int64 words:

@@ -48,6 +48,10 @@ _SIGS = {
     "rax_free_count": (_i32, [_vp, _c_i64p]),
     "rax_free_slots": (_i32, [_vp, _c_i32p, _i64]),
     "rax_lca_depth": (_i32, [_vp, _i64, _i64, _c_i64p]),
+    "rax_match_prefix_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _i32, _i32, _c_i32p, _c_i64p, _c_i64p]),
+    "rax_insert_batch": (_i32, [_vp, _c_i32p, _c_i32p, _c_i64p, _i32, _c_i32p, _c_i64p, _c_i64p, _c_i32p]),
+    "rax_lock_ref_batch": (_i32, [_vp, _c_i64p, _i32, _i32]),
+    "rax_lca_depths": (_i32, [_vp, _c_i64p, _i32, _c_i32p]),
     "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
     "rax_tree_dump": (_i32, [_vp, _c_i64p, _i64, _c_i64p]),
     "rax_kv_scatter": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
@@ -172,6 +176,45 @@ class Tree:
     def free_slots(self, slots) -> None:
         s = _i32arr(slots)
         _check(self._L.rax_free_slots(self._h, _p32(s), len(s)), "rax_free_slots")
+
+    def match_prefix_batch(self, tokens_flat, indptr, cut_full=True, lock=True):
+        """Batched match (and lock) of requests tokens_flat[indptr[r]:indptr[r+1]].
+        Returns (slots_flat, m[batch], node[batch])."""
+        t = _i32arr(tokens_flat)
+        ip = np.ascontiguousarray(indptr, dtype=np.int64)
+        b = len(ip) - 1
+        out = np.empty(max(len(t), 1), dtype=np.int32)
+        m = np.empty(b, dtype=np.int64)
+        nodes = np.empty(b, dtype=np.int64)
+        _check(self._L.rax_match_prefix_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), b, int(cut_full),
+                                              int(lock), _p32(out), m.ctypes.data_as(_c_i64p),
+                                              nodes.ctypes.data_as(_c_i64p)), "rax_match_prefix_batch")
+        return out[: len(t)], m, nodes
+
+    def insert_batch(self, tokens_flat, slots_flat, indptr):
+        """Batched insert. Returns (tree_slots_flat, existing[batch], node[batch])."""
+        t, sl = _i32arr(tokens_flat), _i32arr(slots_flat)
+        ip = np.ascontiguousarray(indptr, dtype=np.int64)
+        b = len(ip) - 1
+        out = np.empty(max(len(t), 1), dtype=np.int32)
+        ex = np.empty(b, dtype=np.int64)
+        nodes = np.empty(b, dtype=np.int64)
+        done = ctypes.c_int32()
+        _check(self._L.rax_insert_batch(self._h, _p32(t), _p32(sl), ip.ctypes.data_as(_c_i64p), b, _p32(out),
+                                        ex.ctypes.data_as(_c_i64p), nodes.ctypes.data_as(_c_i64p),
+                                        ctypes.byref(done)), "rax_insert_batch")
+        return out[: len(t)], ex, nodes
+
+    def lock_ref_batch(self, nodes, delta: int) -> None:
+        nd = np.ascontiguousarray(nodes, dtype=np.int64)
+        _check(self._L.rax_lock_ref_batch(self._h, nd.ctypes.data_as(_c_i64p), len(nd), int(delta)),
+               "rax_lock_ref_batch")
+
+    def lca_depths(self, nodes) -> np.ndarray:
+        nd = np.ascontiguousarray(nodes, dtype=np.int64)
+        out = np.zeros(len(nd), dtype=np.int32)
+        _check(self._L.rax_lca_depths(self._h, nd.ctypes.data_as(_c_i64p), len(nd), _p32(out)), "rax_lca_depths")
+        return out
 
     def lca_depth(self, a: int, b: int) -> int:
         d = _i64()

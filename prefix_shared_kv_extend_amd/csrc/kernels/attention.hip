@@ -8,30 +8,37 @@
 // contiguous k_ext / v_ext rows under a causal mask. Decode is the same with one
 // query per request and every key read from the pool.
 //
-// Kernel design (one kernel for both; MI355X-specific choices):
-//  * A workgroup (4 waves of 64) owns a block of BM = 128 "MFMA rows". A row is a
-//    (query token, query head) pair; the h_q / h_kv query heads that share a KV head
-//    are packed into consecutive rows, so each K/V tile staged in LDS serves all of
-//    them (grouped-query attention). Rows of consecutive requests are packed into
-//    one block, so a block can span several requests.
+// Kernel design (one kernel template for both; MI355X-specific choices):
+//  * A workgroup of NW waves owns BM = NW * RT * 32 "MFMA rows"; each wave holds RT
+//    row tiles of 32. A row is a (query token, query head) pair; the h_q / h_kv query
+//    heads that share a KV head are packed into consecutive rows, so each K/V tile
+//    staged in LDS serves all of them (grouped-query attention). Rows of consecutive
+//    requests are packed into one block, so a block can span several requests.
+//    RT = 2 lets every K/V fragment read from LDS feed two MFMA row tiles, halving
+//    LDS traffic per flop.
 //  * The block's keys form a list of 64-key tiles: first the positions that all of
 //    its requests share (same slots; bounded by the shared_len hint), loaded once for
 //    every row; then each request's own remaining prefix positions (only the wave(s)
 //    holding that request's rows run the MFMAs); then, in extend, the suffix keys of
 //    the block's requests from k_ext under a block-diagonal causal mask.
-//  * Each tile is gathered slot by slot from HBM with 16-byte loads (16 lanes per
-//    token row: coalesced within the row) into LDS: K row-major with a 16-byte row
-//    pad, V transposed (d-major) with an 8-byte pad, so the MFMA operand reads are
-//    free of bank conflicts.
+//  * Software pipeline, one barrier per tile: while the waves run the MFMAs of tile
+//    t from one LDS buffer, every thread already has the 16-byte global loads of
+//    tile t+1 in flight (slot ids of tile t+2 too); after the MFMAs it writes them to
+//    the other LDS buffer. Gathers are slot by slot, 16 lanes per 256-byte token
+//    row (coalesced within the row). K is stored row-major with a 16-byte row pad,
+//    V transposed (d-major) with an 8-byte pad: MFMA operand reads are free of bank
+//    conflicts.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32: v_mfma_f32_32x32x2_f32): each lane
 //    owns one query row, so the softmax row max and sum are in-lane reductions plus
 //    one cross-half exchange. O^T = V^T P^T accumulates in fp32; P stays in
 //    registers (the contraction index is permuted consistently in both operands).
-//  * Online softmax in the log2 domain (scale * log2 e folded into the scores).
+//  * Online softmax in the log2 domain (scale * log2 e folded into the scores);
+//    full unmasked tiles skip the mask; the accumulator rescale is skipped when no
+//    row's running maximum grew (exactly the same result).
 //  * Split-K: the tile list is divided into nsplit ranges (decode needs it to fill
 //    256 CUs); partial (m, l, acc) go to a workspace and a merge kernel combines
 //    them by log-sum-exp. With nsplit == 1 the block writes O directly.
-//  * Workgroup ids are remapped so that all blocks of one KV head run on one XCD and
+//  * Workgroup ids are remapped so that the blocks of one KV head run on one XCD and
 //    share its L2 for the prefix tiles they all read.
 #include <math.h>
 
@@ -42,10 +49,7 @@
 
 namespace raxk {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int BM = 128;  // MFMA rows per workgroup (32 per wave)
-constexpr int BN = 64;   // keys per tile
+constexpr int BN = 64;  // keys per tile
 constexpr float kNegInf = -INFINITY;
 
 struct AttnArgs {
@@ -60,7 +64,7 @@ struct AttnArgs {
   int64_t rtt_rows;
   const int32_t* req_pool_idx;
   const int32_t* kv_len;      // keys read from the pool per request (prefix_len or seq_len)
-  const int32_t* qo_indptr;   // nullptr: request r owns query row r (decode)
+  const int32_t* qo_indptr;   // extend only: query rows of request r
   const int32_t* shared_len;  // nullptr: no sharing hint
   int32_t batch;
   int64_t total_q;
@@ -73,28 +77,49 @@ struct AttnArgs {
   float* ws;                  // split-K partials (nsplit > 1)
   int32_t nsplit;
   int32_t n_rb;               // row blocks per KV head
+  int32_t bm;                 // MFMA rows per block
+  // decode split into a shared part (this kernel) and an own part (own_kernel)
+  int32_t shared_only;        // 1: only the keys a block's requests share; always write partials
+  int32_t* ws_L;              // [n_rb] shared length of each row block (shared_only)
+  float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
+  int32_t n_chunk;            // most own-part key chunks per (request, KV head)
 };
 
-template <typename T, int D>
-struct Tile {
-  static constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  static constexpr int CHUNKS = D / EPC;           // chunks per token row
-  static constexpr int KPAD = EPC;                 // K row pad: 16 bytes
-  static constexpr int VPAD = sizeof(T) == 2 ? 4 : 1;  // V^T row pad: 8 (bf16) / 4 (fp32) bytes
-  static constexpr int KSTRIDE = D + KPAD;
-  static constexpr int VSTRIDE = BN + VPAD;
+template <typename T, int D, int NW, int RT>
+struct Cfg {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int BM = 32 * RT * NW;
+  static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
+  static constexpr int CHUNKS = D / EPC;                // chunks per token row
+  static constexpr int KSTRIDE = D + EPC;               // K row pad: 16 bytes
+  static constexpr int VSTRIDE = BN + (sizeof(T) == 2 ? 4 : 1);  // V^T row pad: 8 / 4 bytes
+  static constexpr int KPP = kThreads / CHUNKS;         // keys per load pass
+  static constexpr int KP = BN / KPP;                   // K load passes
+  static constexpr int VP = (BN / 2) / KPP;             // V load passes (key pairs)
+  static_assert(KPP > 0 && BN % KPP == 0 && (BN / 2) % KPP == 0, "tile load shape");
 };
 
-template <typename T, int D>
+template <typename T, int D, int NW, int RT>
 struct __align__(16) Smem {
-  T k[BN * Tile<T, D>::KSTRIDE];
-  T vt[D * Tile<T, D>::VSTRIDE];
-  int32_t slot[BN];
-  int32_t req_m[BM];
-  int32_t req_row[BM];
-  int32_t req_qo[BM + 1];
-  int32_t own[BM + 1];
+  using C = Cfg<T, D, NW, RT>;
+  T k[2][BN * C::KSTRIDE];
+  T vt[2][D * C::VSTRIDE];
+  int32_t slot[4][BN];
+  int32_t req_m[C::BM];
+  int32_t req_row[C::BM];
+  int32_t req_qo[C::BM + 1];
+  int32_t own[C::BM + 1];
+  int32_t req_sh[C::BM];
   int32_t hdr[8];
+};
+
+struct TileDesc {
+  int kind;  // 0 shared prefix, 1 one request's own prefix, 2 suffix (k_ext rows)
+  int cnt;   // valid keys in the tile
+  int pos0;  // first position (kinds 0, 1)
+  int kr0;   // first k_ext row (kind 2)
+  int req;   // local request index (kind 1)
+  int row;   // req_to_token row (kinds 0, 1)
 };
 
 __device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t) {
@@ -108,34 +133,101 @@ __device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t
   return lo;
 }
 
-// Load one 16-byte chunk (or zeros).
-__device__ __forceinline__ uint4 ld16(const void* base, int64_t elem_off, int esize, bool ok) {
-  if (!ok) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + elem_off * esize);
+template <typename SM>
+__device__ __forceinline__ TileDesc describe(int tau, const SM& sm, int L, int n_sh, int n_own, int suf0,
+                                             int64_t qb, int nreq) {
+  TileDesc d;
+  d.pos0 = 0;
+  d.kr0 = 0;
+  d.req = 0;
+  d.row = 0;
+  if (tau < n_sh) {
+    d.kind = 0;
+    d.pos0 = tau * BN;
+    d.cnt = min(BN, L - d.pos0);
+    d.row = sm.req_row[0];
+  } else if (tau < n_sh + n_own) {
+    d.kind = 1;
+    const int o = tau - n_sh;
+    int lo = 0, hi = nreq - 1;  // last i with own[i] <= o
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.own[mid] <= o) lo = mid;
+      else hi = mid - 1;
+    }
+    d.req = lo;
+    d.pos0 = L + (o - sm.own[lo]) * BN;
+    d.cnt = min(BN, sm.req_m[lo] - d.pos0);
+    d.row = sm.req_row[lo];
+  } else {
+    d.kind = 2;
+    d.kr0 = suf0 + (tau - n_sh - n_own) * BN;
+    d.cnt = (int)min((int64_t)BN, qb - d.kr0);
+  }
+  return d;
 }
 
-template <typename T, int D, bool kDecode>
-__global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
-  using TL = Tile<T, D>;
+// Slot ids of a tile are fetched in two halves so the load is unconditional (no branch
+// around a memory access, which lets the compiler keep several tiles' loads in flight):
+// slot_issue loads req_to_token at a valid index (index 0 for keys that have none) and
+// slot_finish turns the raw value into the slot id (pool), the k_ext row (suffix) or -1.
+__device__ __forceinline__ int slot_issue(const AttnArgs& a, const TileDesc& d, int i) {
+  const bool pool = d.kind != 2 && i < d.cnt;
+  const int64_t idx = pool ? (int64_t)d.row * a.rtt_stride + d.pos0 + i : 0;
+  return a.rtt[idx];
+}
+
+__device__ __forceinline__ int slot_finish(const AttnArgs& a, const TileDesc& d, int i, int raw) {
+  if (i >= d.cnt) return -1;
+  if (d.kind == 2) return d.kr0 + i;
+  if (raw < 0 || raw >= a.num_slots) {
+    flag_error(RAX_DEVERR_SLOT);
+    return -1;
+  }
+  return raw;
+}
+
+// 16-byte load that always reads valid memory: keys without a slot read row 0 and are
+// zeroed when the tile is written to LDS (the mask also removes them from the softmax).
+__device__ __forceinline__ u32x4 ld16(const char* base, int s, int64_t row_bytes) {
+  return *reinterpret_cast<const u32x4*>(base + (int64_t)(s < 0 ? 0 : s) * row_bytes);
+}
+
+__device__ __forceinline__ u32x4 keep_if(bool ok, u32x4 v) {
+  u32x4 r;
+  r.x = ok ? v.x : 0u;
+  r.y = ok ? v.y : 0u;
+  r.z = ok ? v.z : 0u;
+  r.w = ok ? v.w : 0u;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t word(u32x4 v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <typename T, int D, bool kDecode, int NW, int RT, int PD>
+__global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
+  using C = Cfg<T, D, NW, RT>;
+  constexpr int BM = C::BM;
   constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ Smem<T, D> sm;
+  __shared__ Smem<T, D, NW, RT> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int jrow = lane & 31;  // row within the wave's 32
+  const int jrow = lane & 31;  // row within a 32-row tile
   const int half = lane >> 5;  // which half of the key set this lane holds
 
   // ---- work item: (KV head, row block, split)
-  const int64_t nblocks = (int64_t)gridDim.x;
-  const int64_t item = xcd_remap(blockIdx.x, nblocks);
+  const int64_t item = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
   const int split = (int)(item % a.nsplit);
   const int64_t rb = (item / a.nsplit) % a.n_rb;
   const int h = (int)(item / ((int64_t)a.nsplit * a.n_rb));
 
-  const int64_t G0 = rb * BM;                 // first MFMA row
-  const int64_t qa = G0 / a.g;                // first query row (BM % g == 0)
-  int64_t qb = qa + BM / a.g;                 // one past the last query row
+  const int64_t G0 = rb * BM;   // first MFMA row
+  const int64_t qa = G0 / a.g;  // first query row (BM % g == 0)
+  int64_t qb = qa + BM / a.g;   // one past the last query row
   if (qb > a.total_q) qb = a.total_q;
 
   // ---- block metadata (requests covered, shared length, tile list)
@@ -159,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   __syncthreads();
   const int r0 = sm.hdr[0];
   const int nreq = sm.hdr[1];
-  for (int i = tid; i < nreq; i += kThreads) {
+  for (int i = tid; i < nreq; i += C::kThreads) {
     const int r = r0 + i;
     int row = a.req_pool_idx[r];
     int m = a.kv_len[r];
@@ -171,37 +263,47 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
     sm.req_row[i] = row;
     sm.req_m[i] = m;
     sm.req_qo[i] = kDecode ? r : a.qo_indptr[r];
+    sm.req_sh[i] = i == 0 ? (1 << 30) : (a.shared_len ? a.shared_len[r] : 0);
   }
   if (tid == 0) sm.req_qo[nreq] = kDecode ? r0 + nreq : a.qo_indptr[r0 + nreq];
   __syncthreads();
-  if (tid == 0) {
-    int L;
-    if (nreq == 1) {
-      L = sm.req_m[0];
-    } else {
-      L = sm.req_m[0];
-      for (int i = 1; i < nreq; ++i) {
-        const int sh = a.shared_len ? a.shared_len[r0 + i] : 0;
-        L = min(L, min(sm.req_m[i], sh));
+  if (wave == 0) {
+    // shared length L = min over the block's requests of their key counts and of the
+    // shared_len hints between neighbours; then an exclusive scan of own-tile counts
+    int Lw = 1 << 30;
+    for (int i = lane; i < nreq; i += 64) Lw = min(Lw, min(sm.req_m[i], sm.req_sh[i]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Lw = min(Lw, __shfl_xor(Lw, off));
+    const int L = max(Lw, 0);
+    int carry = 0;
+    for (int base = 0; base < (a.shared_only ? 0 : nreq); base += 64) {
+      const int i = base + lane;
+      const int rest = i < nreq ? sm.req_m[i] - L : 0;
+      const int cnt = rest > 0 ? (rest + BN - 1) / BN : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
       }
-      if (L < 0) L = 0;
+      if (i < nreq) sm.own[i] = carry + incl - cnt;
+      carry += __shfl(incl, 63);
     }
-    int acc = 0;
-    for (int i = 0; i < nreq; ++i) {
-      sm.own[i] = acc;
-      const int rest = sm.req_m[i] - L;
-      acc += rest > 0 ? (rest + BN - 1) / BN : 0;
+    if (a.shared_only) {
+      for (int i = lane; i < nreq; i += 64) sm.own[i] = 0;
+      if (lane == 0 && h == 0 && split == 0) a.ws_L[rb] = L;
     }
-    sm.own[nreq] = acc;
-    const int n_sh = (L + BN - 1) / BN;
-    int n_suf = 0;
-    if (!kDecode) n_suf = (int)((qb - sm.req_qo[0] + BN - 1) / BN);
-    const int total = n_sh + acc + n_suf;
-    sm.hdr[2] = L;
-    sm.hdr[3] = n_sh;
-    sm.hdr[4] = acc;
-    sm.hdr[5] = (int)(((int64_t)total * split) / a.nsplit);
-    sm.hdr[6] = (int)(((int64_t)total * (split + 1)) / a.nsplit);
+    if (lane == 0) {
+      sm.own[nreq] = carry;
+      const int n_sh = (L + BN - 1) / BN;
+      const int n_suf = kDecode ? 0 : (int)((qb - sm.req_qo[0] + BN - 1) / BN);
+      const int total = n_sh + carry + n_suf;
+      sm.hdr[2] = L;
+      sm.hdr[3] = n_sh;
+      sm.hdr[4] = carry;
+      sm.hdr[5] = (int)(((int64_t)total * split) / a.nsplit);
+      sm.hdr[6] = (int)(((int64_t)total * (split + 1)) / a.nsplit);
+    }
   }
   __syncthreads();
   const int L = sm.hdr[2];
@@ -211,280 +313,572 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(AttnArgs a) {
   const int t_end = sm.hdr[6];
   const int suf0 = sm.req_qo[0];
 
-  // ---- this lane's row
-  const int R = wave * 32 + jrow;
-  const int64_t Gr = G0 + R;
-  const int64_t t_row = Gr / a.g;
-  const bool row_ok = t_row < qb;
-  const int hq = h * a.g + (int)(Gr % a.g);
-  int my_req = 0;  // local request index
-  if (row_ok) {
-    int lo = 0, hi = nreq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.req_qo[mid] <= t_row) lo = mid;
-      else hi = mid - 1;
+  // ---- this lane's rows (RT row tiles)
+  bool row_ok[RT];
+  int64_t t_row[RT];
+  int hq[RT], my_req[RT], my_qo[RT];
+  int w_rlo = 1 << 30, w_rhi = -1, w_klo = 1 << 30, w_khi = -1, n_bad = 0;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int R = (wave * RT + rt) * 32 + jrow;
+    const int64_t Gr = G0 + R;
+    t_row[rt] = Gr / a.g;
+    row_ok[rt] = t_row[rt] < qb;
+    hq[rt] = h * a.g + (int)(Gr % a.g);
+    int req = 0;
+    if (row_ok[rt]) {
+      int lo = 0, hi = nreq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.req_qo[mid] <= t_row[rt]) lo = mid;
+        else hi = mid - 1;
+      }
+      req = lo;
+      w_rlo = min(w_rlo, req);
+      w_rhi = max(w_rhi, req);
+      w_klo = min(w_klo, sm.req_qo[req]);
+      w_khi = max(w_khi, (int)t_row[rt]);
+    } else {
+      ++n_bad;
     }
-    my_req = lo;
+    my_req[rt] = req;
+    my_qo[rt] = sm.req_qo[req];
   }
-  const int my_qo = sm.req_qo[my_req];
-  // wave's request range and suffix-key interest range (uniform across the wave)
-  int w_rlo = row_ok ? my_req : 1 << 30, w_rhi = row_ok ? my_req : -1;
-  int w_klo = row_ok ? my_qo : 1 << 30, w_khi = row_ok ? (int)t_row : -1;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     w_rlo = min(w_rlo, __shfl_xor(w_rlo, off));
     w_rhi = max(w_rhi, __shfl_xor(w_rhi, off));
     w_klo = min(w_klo, __shfl_xor(w_klo, off));
     w_khi = max(w_khi, __shfl_xor(w_khi, off));
+    n_bad += __shfl_xor(n_bad, off);
   }
   const bool wave_active = w_rhi >= 0;
+  const bool all_rows_ok = n_bad == 0;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row jrow, dims [ks*K + half*K/2, +K/2)
   constexpr int KSTEP = kBf16 ? 16 : 2;
   constexpr int NKS = D / KSTEP;
   typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
-  QFrag qf[NKS];
-  {
-    const T* qp = reinterpret_cast<const T*>(a.q) + (t_row * a.h_q + hq) * (int64_t)D;
+  QFrag qf[RT][NKS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (t_row[rt] * a.h_q + hq[rt]) * (int64_t)D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       if constexpr (kBf16) {
-        if (row_ok) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
-        else qf[ks] = bf16x8{};
+        if (row_ok[rt]) qf[rt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+        else qf[rt][ks] = bf16x8{};
       } else {
-        qf[ks] = row_ok ? qp[ks * 2 + half] : 0.f;
+        qf[rt][ks] = row_ok[rt] ? qp[ks * 2 + half] : 0.f;
       }
     }
   }
 
-  f32x16 acc[D / 32];
+  f32x16 acc[RT][D / 32];
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = kNegInf;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[rt][dt] = f32x16{};
+  }
 
-  const int64_t row_elems = (int64_t)a.h_kv * D;  // elements per pool slot / k_ext row
-  int own_i = 0;                                  // request of the current own tile
+  const int64_t row_bytes = (int64_t)a.h_kv * D * sizeof(T);  // bytes per pool slot / k_ext row
+  const int64_t head_off = (int64_t)h * D * sizeof(T);
+  const int c = tid % C::CHUNKS;
+  const int kk = tid / C::CHUNKS;
+  const int coff = c * 16;
 
-  for (int tau = t_begin; tau < t_end; ++tau) {
-    // -- decode tile
-    int kind, cnt, pos0 = 0, kr0 = 0, req_i = 0, row = 0;
-    if (tau < n_sh) {
-      kind = 0;
-      pos0 = tau * BN;
-      cnt = min(BN, L - pos0);
-      row = sm.req_row[0];
-    } else if (tau < n_sh + n_own) {
-      kind = 1;
-      const int o = tau - n_sh;
-      while (sm.own[own_i + 1] <= o) ++own_i;
-      req_i = own_i;
-      pos0 = L + (o - sm.own[own_i]) * BN;
-      cnt = min(BN, sm.req_m[own_i] - pos0);
-      row = sm.req_row[own_i];
-    } else {
-      kind = 2;
-      kr0 = suf0 + (tau - n_sh - n_own) * BN;
-      cnt = (int)min((int64_t)BN, qb - kr0);
+  // global -> registers for one tile (slot ids already in sm.slot[sb]); PD register sets
+  constexpr int NSB = PD + 2;  // slot-id buffers in LDS
+  u32x4 kreg[PD][C::KP];
+  u32x4 vreg[PD][C::VP][2];
+  // Always issues the same number of loads (live == false: row 0, results unused), so the
+  // compiler sees one load count on every path and waits only for the tile it consumes.
+  auto issue_loads = [&](const TileDesc& d, int sb, bool live, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+    const char* kb = reinterpret_cast<const char*>(d.kind == 2 ? a.k_ext : a.k_pool) + head_off + coff;
+    const char* vb = reinterpret_cast<const char*>(d.kind == 2 ? a.v_ext : a.v_pool) + head_off + coff;
+#pragma unroll
+    for (int p = 0; p < C::KP; ++p)
+      kreg[set][p] = ld16(kb, live ? sm.slot[sb][p * C::KPP + kk] : -1, row_bytes);
+#pragma unroll
+    for (int p = 0; p < C::VP; ++p) {
+      const int kp = p * C::KPP + kk;
+      vreg[set][p][0] = ld16(vb, live ? sm.slot[sb][2 * kp] : -1, row_bytes);
+      vreg[set][p][1] = ld16(vb, live ? sm.slot[sb][2 * kp + 1] : -1, row_bytes);
     }
-
-    // -- slot ids of the tile's keys
-    if (tid < BN) {
-      int s = -1;
-      if (kind != 2 && tid < cnt) {
-        s = a.rtt[(int64_t)row * a.rtt_stride + pos0 + tid];
-        if (s < 0 || s >= a.num_slots) {
-          flag_error(RAX_DEVERR_SLOT);
-          s = -1;
-        }
-      } else if (kind == 2 && tid < cnt) {
-        s = kr0 + tid;
-      }
-      sm.slot[tid] = s;
+  };
+  // registers -> LDS buffer b (K row-major, V transposed); keys without a slot become zeros
+  auto store_tile = [&](int b, int sb, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+#pragma unroll
+    for (int p = 0; p < C::KP; ++p) {
+      const int key = p * C::KPP + kk;
+      *reinterpret_cast<u32x4*>(&sm.k[b][key * C::KSTRIDE + c * C::EPC]) =
+          keep_if(sm.slot[sb][key] >= 0, kreg[set][p]);
     }
-    __syncthreads();
-
-    // -- gather K (row-major) and V (transposed) into LDS
-    {
-      const void* kb = kind == 2 ? a.k_ext : a.k_pool;
-      const void* vb = kind == 2 ? a.v_ext : a.v_pool;
-      constexpr int KPP = kThreads / TL::CHUNKS;  // keys per pass
-      const int c = tid % TL::CHUNKS;
-      const int kk = tid / TL::CHUNKS;
 #pragma unroll
-      for (int p = 0; p < BN / KPP; ++p) {
-        const int key = p * KPP + kk;
-        const int s = sm.slot[key];
-        const uint4 v = ld16(kb, ((int64_t)s * row_elems + (int64_t)h * D) + c * TL::EPC, sizeof(T), s >= 0);
-        *reinterpret_cast<uint4*>(&sm.k[key * TL::KSTRIDE + c * TL::EPC]) = v;
-      }
-      constexpr int PPP = kThreads / TL::CHUNKS;  // key pairs per pass
+    for (int p = 0; p < C::VP; ++p) {
+      const int kp = p * C::KPP + kk;
+      const u32x4 w0 = keep_if(sm.slot[sb][2 * kp] >= 0, vreg[set][p][0]);
+      const u32x4 w1 = keep_if(sm.slot[sb][2 * kp + 1] >= 0, vreg[set][p][1]);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[b][(c * C::EPC) * C::VSTRIDE + 2 * kp]);
+      constexpr int WSTRIDE = C::VSTRIDE * (int)sizeof(T) / 4;  // V^T row stride in 32-bit words
 #pragma unroll
-      for (int p = 0; p < (BN / 2) / PPP; ++p) {
-        const int kp = p * PPP + kk;
-        const int s0 = sm.slot[2 * kp], s1 = sm.slot[2 * kp + 1];
-        const uint4 v0 = ld16(vb, ((int64_t)s0 * row_elems + (int64_t)h * D) + c * TL::EPC, sizeof(T), s0 >= 0);
-        const uint4 v1 = ld16(vb, ((int64_t)s1 * row_elems + (int64_t)h * D) + c * TL::EPC, sizeof(T), s1 >= 0);
-        const T* e0 = reinterpret_cast<const T*>(&v0);
-        const T* e1 = reinterpret_cast<const T*>(&v1);
-#pragma unroll
-        for (int e = 0; e < TL::EPC; ++e) {
-          T* dst = &sm.vt[(c * TL::EPC + e) * TL::VSTRIDE + 2 * kp];
-          if constexpr (kBf16) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<bf16x2*>(dst) = bf16x2{e0[e], e1[e]};
-          } else {
-            dst[0] = e0[e];
-            dst[1] = e1[e];
-          }
+      for (int e = 0; e < C::EPC; ++e) {
+        if constexpr (kBf16) {
+          // element e of both keys -> one 32-bit word (key 2kp low half, key 2kp+1 high half)
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          dst[e * WSTRIDE] = __builtin_amdgcn_perm(word(w1, e >> 1), word(w0, e >> 1), sel);
+        } else {
+          float* df = reinterpret_cast<float*>(&sm.vt[b][(c * C::EPC + e) * C::VSTRIDE + 2 * kp]);
+          df[0] = __builtin_bit_cast(float, word(w0, e));
+          df[1] = __builtin_bit_cast(float, word(w1, e));
         }
       }
     }
-    __syncthreads();
+  };
+  auto desc = [&](int tau) { return describe(tau, sm, L, n_sh, n_own, suf0, qb, nreq); };
+
+  // ---- prologue: slot ids of tiles t_begin .. t_begin+PD, K/V loads of the first PD tiles
+  if (tid < BN) {
+#pragma unroll
+    for (int i = 0; i <= PD; ++i) {
+      if (t_begin + i < t_end) {
+        const TileDesc di = desc(t_begin + i);
+        sm.slot[(t_begin + i) % NSB][tid] = slot_finish(a, di, tid, slot_issue(a, di, tid));
+      }
+    }
+  }
+  __syncthreads();
+  if (t_begin < t_end) {
+    issue_loads(desc(t_begin), t_begin % NSB, true, std::integral_constant<int, 0>{});
+    if constexpr (PD > 1) {
+      const bool live = t_begin + 1 < t_end;
+      issue_loads(desc(live ? t_begin + 1 : t_begin), (t_begin + 1) % NSB, live, std::integral_constant<int, 1>{});
+    }
+    store_tile(0, t_begin % NSB, std::integral_constant<int, 0>{});
+  }
+  __syncthreads();
+
+  // one pipeline step; ph = (tau - t_begin) % PD selects the register sets at compile time
+  auto step = [&](int tau, auto ph_c) {
+    constexpr int ph = decltype(ph_c)::value;
+    const int buf = (tau - t_begin) & 1;
+    const TileDesc d = desc(tau);
+    // slot ids of tile tau+PD+1 first: vector loads retire in order, so waiting for this
+    // one (end of step) must not also wait for the K/V loads issued after it
+    const bool has_next = tau + PD + 1 < t_end;
+    const TileDesc dn = desc(has_next ? tau + PD + 1 : tau);
+    const int raw_slot = slot_issue(a, dn, tid < BN ? tid : 0);
+    const bool live = tau + PD < t_end;
+    issue_loads(desc(live ? tau + PD : tau), (tau + PD) % NSB, live, std::integral_constant<int, ph>{});
 
     // -- does this wave have rows that see any key of the tile?
     bool run = wave_active;
-    if (kind == 1) run = run && req_i >= w_rlo && req_i <= w_rhi;
-    if (kind == 2) run = run && kr0 <= w_khi && kr0 + cnt > w_klo;
+    if (d.kind == 1) run = run && d.req >= w_rlo && d.req <= w_rhi;
+    if (d.kind == 2) run = run && d.kr0 <= w_khi && d.kr0 + d.cnt > w_klo;
 
     if (run) {
-      f32x16 s[2];
+      const bool unmasked = d.kind == 0 && d.cnt == BN && all_rows_ok;
+      // two 32-key online-softmax steps per 64-key tile (keeps S and P small)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        f32x16 c16 = f32x16{};
-        const T* kr = &sm.k[(sub * 32 + jrow) * TL::KSTRIDE];
+        f32x16 s[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) s[rt] = f32x16{};
+        const T* kr = &sm.k[buf][(sub * 32 + jrow) * C::KSTRIDE];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           if constexpr (kBf16) {
             const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
-            c16 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], c16, 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[rt][ks], s[rt], 0, 0, 0);
           } else {
-            c16 = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[ks * 2 + half], qf[ks], c16, 0, 0, 0);
+            const float af = kr[ks * 2 + half];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              s[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, qf[rt][ks], s[rt], 0, 0, 0);
           }
         }
-        s[sub] = c16;
-      }
-      // scale + mask; key index of register r: sub*32 + 8*(r/4) + 4*half + r%4
-      float mx = kNegInf;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+        for (int rt = 0; rt < RT; ++rt) {
+          // scale + mask; key index of register r: sub*32 + 8*(r/4) + 4*half + r%4
+          float mx = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool ok = row_ok && key < cnt;
-          if (kind == 1) ok = ok && my_req == req_i;
-          if (kind == 2) {
-            const int kr = kr0 + key;
-            ok = ok && kr >= my_qo && kr <= t_row;
+          for (int r = 0; r < 16; ++r) {
+            float v = s[rt][r] * a.scale_log2;
+            if (!unmasked) {
+              const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              bool ok = row_ok[rt] && key < d.cnt;
+              if (d.kind == 1) ok = ok && my_req[rt] == d.req;
+              if (d.kind == 2) {
+                const int kr2 = d.kr0 + key;
+                ok = ok && kr2 >= my_qo[rt] && kr2 <= t_row[rt];
+              }
+              v = ok ? v : kNegInf;
+            }
+            s[rt][r] = v;
+            mx = fmaxf(mx, v);
           }
-          const float v = ok ? s[sub][r] * a.scale_log2 : kNegInf;
-          s[sub][r] = v;
-          mx = fmaxf(mx, v);
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run[rt], mx);
+          const float m_use = m_new == kNegInf ? 0.f : m_new;
+          if (__any(m_new > m_run[rt])) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+            l_run[rt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[rt][dt] *= alpha;
+          }
+          m_run[rt] = m_new;
+          float psum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(s[rt][r] - m_use);
+            s[rt][r] = p;
+            psum += p;
+          }
+          psum += __shfl_xor(psum, 32);
+          l_run[rt] += psum;
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[sub][r] - m_use);
-          s[sub][r] = p;
-          psum += p;
-        }
-      }
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
 
-      // O^T += V^T P^T
-      if constexpr (kBf16) {
-        bf16x8 pb[2][2];
+        // O^T += V^T P^T over this sub-step's 32 keys
+        if constexpr (kBf16) {
+          bf16x8 pb[RT][2];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[sub][kh][e] = (__bf16)s[sub][kh * 8 + e];
+              for (int e = 0; e < 8; ++e) pb[rt][kh][e] = (__bf16)s[rt][kh * 8 + e];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const T* vr = &sm.vt[(dt * 32 + jrow) * TL::VSTRIDE];
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
               const int kb0 = sub * 32 + kh * 16 + 4 * half;
               const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + kb0);
               const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + kb0 + 8);
               const bf16x8 af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[sub][kh], acc[dt], 0, 0, 0);
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[rt][kh], acc[rt][dt], 0, 0, 0);
             }
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const T* vr = &sm.vt[(dt * 32 + jrow) * TL::VSTRIDE];
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[key], s[sub][r], acc[dt], 0, 0, 0);
+              const float af = vr[key];
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, s[rt][r], acc[rt][dt], 0, 0, 0);
             }
           }
         }
       }
     }
+
+    if (tau + 1 < t_end) store_tile(buf ^ 1, (tau + 1) % NSB, std::integral_constant<int, (ph + 1) % PD>{});
+    if (has_next && tid < BN) sm.slot[(tau + PD + 1) % NSB][tid] = slot_finish(a, dn, tid, raw_slot);
     __syncthreads();
+  };
+
+  for (int tau = t_begin; tau < t_end; tau += PD) {
+    step(tau, std::integral_constant<int, 0>{});
+    if constexpr (PD > 1) {
+      if (tau + 1 < t_end) step(tau + 1, std::integral_constant<int, 1>{});
+    }
   }
 
-  // ---- epilogue: lane holds row jrow, dims dt*32 + 8*(r/4) + 4*half + r%4
-  if (!row_ok) return;
-  if (a.nsplit == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t obase = (t_row * a.h_q + hq) * (int64_t)D;
+  // ---- epilogue: lane holds row jrow of each row tile, dims dt*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+  for (int rt = 0; rt < RT; ++rt) {
+    if (!row_ok[rt]) continue;
+    const int R = (wave * RT + rt) * 32 + jrow;
+    const bool partial = a.nsplit > 1 || a.shared_only;
+    if (!partial) {
+      const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
+      const int64_t obase = (t_row[rt] * a.h_q + hq[rt]) * (int64_t)D;
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * half;
-        const float x0 = acc[dt][rg * 4 + 0] * inv, x1 = acc[dt][rg * 4 + 1] * inv;
-        const float x2 = acc[dt][rg * 4 + 2] * inv, x3 = acc[dt][rg * 4 + 3] * inv;
-        if (a.o_bf16) {
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
-              bf16x4{(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) = make_float4(x0, x1, x2, x3);
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = dt * 32 + 8 * rg + 4 * half;
+          const float x0 = acc[rt][dt][rg * 4 + 0] * inv, x1 = acc[rt][dt][rg * 4 + 1] * inv;
+          const float x2 = acc[rt][dt][rg * 4 + 2] * inv, x3 = acc[rt][dt][rg * 4 + 3] * inv;
+          if (a.o_bf16) {
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
+                bf16x4{(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) = make_float4(x0, x1, x2, x3);
+          }
+        }
+      }
+    } else if (l_run[rt] > 0.f) {
+      float* wacc = a.ws + (item * BM + R) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = dt * 32 + 8 * rg + 4 * half;
+          *reinterpret_cast<float4*>(wacc + d0) = make_float4(acc[rt][dt][rg * 4 + 0], acc[rt][dt][rg * 4 + 1],
+                                                              acc[rt][dt][rg * 4 + 2], acc[rt][dt][rg * 4 + 3]);
         }
       }
     }
-  } else {
-    float* wacc = a.ws + (item * BM + R) * (int64_t)D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * half;
-        *reinterpret_cast<float4*>(wacc + d0) =
-            make_float4(acc[dt][rg * 4 + 0], acc[dt][rg * 4 + 1], acc[dt][rg * 4 + 2], acc[dt][rg * 4 + 3]);
-      }
-    }
-    if (half == 0) {
+    if (partial && half == 0) {  // (m, l) of every row; l == 0 means "no keys here"
       const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
       float* wml = a.ws + n_items * BM * (int64_t)D + (item * BM + R) * 2;
-      wml[0] = m_run;
-      wml[1] = l_run;
+      wml[0] = m_run[rt];
+      wml[1] = l_run[rt];
     }
   }
 }
 
-// Log-sum-exp merge of split-K partials: one wave per (MFMA row, KV head).
+// ---- wavefront lane exchanges: value of lane (l ^ d)
+// d = 8, 2, 1 are DPP moves within a 16-lane row (row_ror:8, quad_perm [1,0,3,2] and
+// [2,3,0,1]); d = 32, 16, 4 go through ds_bpermute. (gfx950's v_permlane16/32_swap would
+// do 32 and 16 in the VALU, but the clang of this toolchain returns the swapped vdst for
+// both results of its builtin, dropping the swapped src0.)
+template <int d>
+__device__ __forceinline__ float xor_get(float x) {
+  if constexpr (d == 8 || d == 2 || d == 1) {
+    constexpr int ctrl = d == 8 ? 0x128 : d == 2 ? 0x4E : 0xB1;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+  } else {
+    return __shfl_xor(x, d);
+  }
+}
+
+// Sum over lanes that differ only in bit d.
+template <int d>
+__device__ __forceinline__ float xor_sum(float x) {
+  return x + xor_get<d>(x);
+}
+
+// One transposing butterfly step at distance d over the pair (x, y): lanes with bit d
+// clear return x + x(l ^ d), lanes with bit d set return y + y(l ^ d).
+template <int d>
+__device__ __forceinline__ float xor_pair(float x, float y, int lane) {
+  const bool up = lane & d;
+  return (up ? y : x) + xor_get<d>(up ? x : y);
+}
+
+// Wave reduction of P partial sums per lane: on return, v[0] of lane l is the sum over
+// all 64 lanes of v[l % P]. Distances >= P are plain sums (the lanes that differ there
+// hold the same pairs); below P each step halves the values a lane keeps.
+template <int P>
+__device__ __forceinline__ void wave_reduce_pairs(float (&v)[P], int lane) {
+#define RAX_SUM_STEP(dd)                                                   \
+  if constexpr (dd >= P) {                                                 \
+    _Pragma("unroll") for (int i = 0; i < P; ++i) v[i] = xor_sum<dd>(v[i]); \
+  } else {                                                                 \
+    _Pragma("unroll") for (int i = 0; i < dd; ++i) v[i] = xor_pair<dd>(v[i], v[i + dd], lane); \
+  }
+  RAX_SUM_STEP(32)
+  RAX_SUM_STEP(16)
+  RAX_SUM_STEP(8)
+  RAX_SUM_STEP(4)
+  RAX_SUM_STEP(2)
+  RAX_SUM_STEP(1)
+#undef RAX_SUM_STEP
+}
+
+template <int d>
+__device__ __forceinline__ float xor_max(float x) {
+  return fmaxf(x, xor_get<d>(x));
+}
+
+// Maximum over lanes that agree in the bits below g (g a power of two).
+__device__ __forceinline__ float group_max(float x, int g) {
+  x = xor_max<32>(x);
+  if (g <= 16) x = xor_max<16>(x);
+  if (g <= 8) x = xor_max<8>(x);
+  if (g <= 4) x = xor_max<4>(x);
+  if (g <= 2) x = xor_max<2>(x);
+  if (g <= 1) x = xor_max<1>(x);
+  return x;
+}
+
+__device__ __forceinline__ float group_sum(float x, int g) {
+  x = xor_sum<32>(x);
+  if (g <= 16) x = xor_sum<16>(x);
+  if (g <= 8) x = xor_sum<8>(x);
+  if (g <= 4) x = xor_sum<4>(x);
+  if (g <= 2) x = xor_sum<2>(x);
+  if (g <= 1) x = xor_sum<1>(x);
+  return x;
+}
+
+// Raw bits of E consecutive elements of a K/V row.
+template <typename T, int E>
+using piece_t = std::conditional_t<E * sizeof(T) == 2, uint16_t,
+                                   std::conditional_t<E * sizeof(T) == 4, uint32_t, uint64_t>>;
+
+template <typename T, int E>
+__device__ __forceinline__ float piece_elem(piece_t<T, E> r, int e) {
+  if constexpr (sizeof(T) == 2) return __builtin_bit_cast(float, (uint32_t)((r >> (16 * e)) & 0xffffu) << 16);
+  else return __builtin_bit_cast(float, (uint32_t)(r >> (32 * e)));
+}
+
+// Own keys of request r in split decode: positions [L, seq_len) with L the shared length of
+// the request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
+// at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets the
+// first own position and the chunk size.
+constexpr int kOwnMin = 64;
+__device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, int& per) {
+  const int L = a.ws_L[((int64_t)r * a.g) / a.bm];
+  const int end = a.kv_len[r];
+  const int row = a.req_pool_idx[r];
+  first = L;
+  per = 0;
+  if (row < 0 || row >= a.rtt_rows || end < 0 || end > a.rtt_stride) return 0;
+  const int n = end - L;
+  if (n <= 0) return 0;
+  const int n_act = min(a.n_chunk, (n + kOwnMin - 1) / kOwnMin);
+  per = (n + n_act - 1) / n_act;
+  return n_act;
+}
+
+// Own part of decode: the keys of one request that its row block does not share (see
+// own_chunks). One wave per (chunk, request, KV head), chunk index slowest so that chunks
+// past every request's own keys are whole workgroups that exit at once. No LDS, no
+// barriers: an HBM-bound gather with wavefront reductions. Lane l holds dims [l*E, l*E+E)
+// (E = D/64) of the G query heads of the KV head. A batch of KB keys: the slot ids are one
+// load per lane, then every K and V row piece of the batch is loaded at once (addresses of
+// keys without a slot are clamped to slot 0 and their values dropped), giving P = KB*G
+// (key, head) partial dot products per lane; wave_reduce_pairs leaves the score of pair l
+// in lane l. Softmax state per head is wave-uniform; P.V takes each key's probability
+// with v_readlane and accumulates in fp32.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
+  constexpr int E = D / 64;
+  constexpr int KB = (sizeof(T) == 4 ? 32 : 64) / G > 0 ? (sizeof(T) == 4 ? 32 : 64) / G : 1;
+  constexpr int P = KB * G;
+  using Raw = piece_t<T, E>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n_rh = (int64_t)a.batch * a.h_kv;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= n_rh * a.n_chunk) return;
+  const int c = (int)(w / n_rh);
+  const int64_t rh = w % n_rh;
+  const int r = (int)(rh / a.h_kv);
+  const int h = (int)(rh % a.h_kv);
+  int first, per;
+  const int n_act = own_chunks(a, r, first, per);
+  if (c >= n_act) return;  // the merge reads only chunks [0, n_act)
+  const int end = a.kv_len[r];
+  const int row = a.req_pool_idx[r];
+  const int start = first + c * per;
+  const int stop = min(start + per, end);
+  const int64_t item = rh * a.n_chunk + c;
+  float* out_acc = a.ws_own + item * G * (int64_t)D;
+  float* out_ml = a.ws_own + n_rh * a.n_chunk * G * (int64_t)D + item * G * 2;
+
+  float q[G][E], acc[G][E], m_run[G], l_run[G];
+  const T* qp = reinterpret_cast<const T*>(a.q) + ((int64_t)r * a.h_q + (int64_t)h * G) * D + lane * E;
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl) {
+    m_run[hl] = kNegInf;
+    l_run[hl] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      q[hl][e] = (float)qp[hl * D + e];
+      acc[hl][e] = 0.f;
+    }
+  }
+  const int64_t row_elems = (int64_t)a.h_kv * D;
+  const T* kb = reinterpret_cast<const T*>(a.k_pool) + (int64_t)h * D + lane * E;
+  const T* vb = reinterpret_cast<const T*>(a.v_pool) + (int64_t)h * D + lane * E;
+  const int32_t* rtt_row = a.rtt + (int64_t)row * a.rtt_stride;
+  const int my_key = (lane % P) / G;
+  const int my_hl = lane % G;
+
+  for (int j0 = start; j0 < stop; j0 += KB) {
+    const int nk = min(KB, stop - j0);
+    const int raw_slot = rtt_row[j0 + min(lane, nk - 1)];
+    int slot = -1;
+    if (lane < nk) {
+      if (raw_slot >= 0 && raw_slot < a.num_slots) slot = raw_slot;
+      else flag_error(RAX_DEVERR_SLOT);
+    }
+    const uint64_t valid = __ballot(slot >= 0);
+    Raw kr[KB], vr[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int s = __builtin_amdgcn_readlane(slot, kk);
+      const int64_t off = (int64_t)(s < 0 ? 0 : s) * row_elems;
+      kr[kk] = *reinterpret_cast<const Raw*>(kb + off);
+      vr[kk] = *reinterpret_cast<const Raw*>(vb + off);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) vr[kk] = ((valid >> kk) & 1) ? vr[kk] : (Raw)0;
+    float v[P];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int hl = 0; hl < G; ++hl) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x += q[hl][e] * piece_elem<T, E>(kr[kk], e);
+        v[kk * G + hl] = x;
+      }
+    wave_reduce_pairs<P>(v, lane);
+    const bool ok = lane < P && ((valid >> my_key) & 1);
+    const float sc = ok ? v[0] * a.scale_log2 : kNegInf;
+    const float mx = group_max(sc, G);  // lane hl < G holds head hl's batch maximum
+    float mu_lane = 0.f;
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) {
+      const float bmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hl));
+      const float m_new = fmaxf(m_run[hl], bmax);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[hl] - m_use);
+      l_run[hl] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[hl][e] *= alpha;
+      m_run[hl] = m_new;
+      if (my_hl == hl) mu_lane = m_use;
+    }
+    const float pr = __builtin_amdgcn_exp2f(sc - mu_lane);
+    const float ps = group_sum(pr, G);
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl)
+      l_run[hl] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps), hl));
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int hl = 0; hl < G; ++hl) {
+        const float pk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), kk * G + hl));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[hl][e] += pk * piece_elem<T, E>(vr[kk], e);
+      }
+  }
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) out_acc[(int64_t)hl * D + lane * E + e] = acc[hl][e];
+  }
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl)
+    if (lane == hl) {
+      out_ml[hl * 2] = m_run[hl];
+      out_ml[hl * 2 + 1] = l_run[hl];
+    }
+}
+
+// Log-sum-exp merge of partials: one wave per (MFMA row, KV head). Inputs are the split
+// partials of the row's block and, for split decode, the own-part chunks of the row's
+// request. Lane s fetches partial s's (m, l), so the wave reads every partial's state at
+// once; accumulator rows are then read eight partials at a time with unconditional loads
+// (rows of partials that saw no key are read and given weight 0).
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -492,28 +886,59 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int h = blockIdx.y;
   const int64_t t = G / a.g;
   if (t >= a.total_q) return;
-  const int hq = h * a.g + (int)(G % a.g);
-  const int64_t rb = G / BM;
-  const int R = (int)(G % BM);
+  const int hl = (int)(G % a.g);
+  const int hq = h * a.g + hl;
+  const int64_t rb = G / a.bm;
+  const int R = (int)(G % a.bm);
   const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
   const int64_t item0 = ((int64_t)h * a.n_rb + rb) * a.nsplit;
-  const float* ml = a.ws + n_items * BM * (int64_t)D;
-  float M = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[((item0 + s) * BM + R) * 2]);
+  const float* ml = a.ws + n_items * a.bm * (int64_t)D;
+  int n_own = 0, first = 0, per = 0;
+  if (a.shared_only) n_own = own_chunks(a, (int)t, first, per);
+  const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
+  const int64_t own0 = (t * a.h_kv + h) * a.n_chunk;  // own items of (request t, KV head h)
+  const float* oml = a.ws_own + own_items * a.g * (int64_t)D;
+  // partial s < nsplit: split s of the block; otherwise own chunk s - nsplit
+  auto acc_ptr = [&](int s) -> const float* {
+    if (s < a.nsplit) return a.ws + ((item0 + s) * a.bm + R) * (int64_t)D;
+    return a.ws_own + ((own0 + (s - a.nsplit)) * a.g + hl) * (int64_t)D;
+  };
+  const int n_part = a.nsplit + n_own;  // <= 64
+  float my_m = kNegInf, my_l = 0.f;
+  if (lane < n_part) {
+    const float* e = lane < a.nsplit ? ml + ((item0 + lane) * a.bm + R) * 2
+                                     : oml + ((own0 + (lane - a.nsplit)) * a.g + hl) * 2;
+    my_m = e[0];
+    my_l = e[1];
+  }
+  float M = my_l > 0.f ? my_m : kNegInf;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float Mu = M == kNegInf ? 0.f : M;
-  float lsum = 0.f;
+  const float my_w = my_l > 0.f ? exp2f(my_m - Mu) : 0.f;
+  float lsum = my_w * my_l;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
   constexpr int PER = D / 64;
+  constexpr int U = 8;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* e = ml + ((item0 + s) * BM + R) * 2;
-    const float w = exp2f(e[0] - Mu);
-    if (e[1] == 0.f) continue;
-    lsum += w * e[1];
-    const float* acc = a.ws + ((item0 + s) * BM + R) * (int64_t)D;
+  for (int s0 = 0; s0 < n_part; s0 += U) {
+    float x[U][PER], w[U];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += w * acc[lane + 64 * i];
+    for (int j = 0; j < U; ++j) {
+      const int s = s0 + j;
+      w[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), s & 63));
+      if (s >= n_part) w[j] = 0.f;
+      const float* p = acc_ptr(s < n_part ? s : 0);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[j][i] = p[lane + 64 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += w[j] != 0.f ? w[j] * x[j][i] : 0.f;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int64_t obase = (t * a.h_q + hq) * (int64_t)D;
@@ -525,11 +950,25 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ host side
+struct Shape {
+  int nw, rt, pd;
+  int bm() const { return 32 * nw * rt; }
+};
+
+// Work shape per call. Extend: 4 waves x two 32-row tiles (every LDS fragment feeds two
+// MFMAs), one tile of loads in flight. Decode: 2 waves x one 32-row tile with two tiles
+// of loads in flight, small enough that two workgroups share a CU (HBM-bound: what
+// matters is bytes in flight per CU).
+static Shape pick_shape(bool decode, rax_dtype dt) {
+  if (dt != RAX_BF16) return {4, 1, 1};
+  return decode ? Shape{2, 1, 2} : Shape{4, 2, 1};
+}
+
 static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
-  // enough workgroups for 256 CUs x 2 resident, but at least ~4 tiles per split
+  // enough workgroups for 256 CUs x 2 resident, at least one full request's tiles per split
   int64_t want = (512 + blocks - 1) / blocks;
   const int64_t tiles = (int64_t)(max_kv_len + BN - 1) / BN;
-  int64_t cap = tiles / 4;
+  int64_t cap = tiles;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 32) want = 32;
@@ -537,41 +976,107 @@ static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
   return (int)want;
 }
 
-static size_t ws_bytes_for(int64_t items, int d) {
-  return (size_t)items * BM * (size_t)(d + 2) * sizeof(float);
+static size_t ws_bytes_for(int64_t items, int bm, int d) {
+  return (size_t)items * bm * (size_t)(d + 2) * sizeof(float);
 }
 
-template <typename T, int D>
-static rax_status launch(AttnArgs& a, hipStream_t st) {
+template <typename T, int D, bool kDecode, int NW, int RT, int PD>
+static rax_status launch_one(AttnArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-  if (a.qo_indptr)
-    hipLaunchKernelGGL((attn_kernel<T, D, false>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<T, D, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
-  if (a.nsplit > 1) {
-    const int64_t rows = a.total_q * a.g;
-    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((rows + 3) / 4), (unsigned)a.h_kv), dim3(256), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+  hipLaunchKernelGGL((attn_kernel<T, D, kDecode, NW, RT, PD>), dim3((unsigned)items), dim3(64 * NW), 0, st, a);
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
+template <int D>
+static rax_status launch_merge(AttnArgs& a, hipStream_t st) {
+  const int64_t rows = a.total_q * a.g;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((rows + 3) / 4), (unsigned)a.h_kv), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
+template <typename T, int D, bool kDecode>
+static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
+  rax_status rc = RAX_EINVAL;
+  if constexpr (sizeof(T) == 2 && !kDecode) {
+    if (s.nw == 4 && s.rt == 2 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 2, 1>(a, st);
   }
+  if constexpr (sizeof(T) == 2 && kDecode) {
+    if (s.nw == 2 && s.rt == 1 && s.pd == 2) rc = launch_one<T, D, kDecode, 2, 1, 2>(a, st);
+  }
+  if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 1, 1>(a, st);
+  if (rc != RAX_OK) return rc;
+  if constexpr (kDecode) {
+    if (a.shared_only) {
+      const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
+      const unsigned blocks = (unsigned)((own_items + 3) / 4);
+      switch (a.g) {
+        case 1: hipLaunchKernelGGL((own_kernel<T, D, 1>), dim3(blocks), dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((own_kernel<T, D, 2>), dim3(blocks), dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((own_kernel<T, D, 4>), dim3(blocks), dim3(256), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((own_kernel<T, D, 8>), dim3(blocks), dim3(256), 0, st, a); break;
+        case 16: hipLaunchKernelGGL((own_kernel<T, D, 16>), dim3(blocks), dim3(256), 0, st, a); break;
+        default: return RAX_EINVAL;
+      }
+      if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+    }
+  }
+  if (a.nsplit > 1 || a.shared_only) return launch_merge<D>(a, st);
   return RAX_OK;
 }
 
-static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, hipStream_t st) {
+template <bool kDecode>
+static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_t st) {
   if (dt == RAX_BF16) {
-    if (d == 128) return launch<__bf16, 128>(a, st);
-    if (d == 64) return launch<__bf16, 64>(a, st);
+    if (d == 128) return launch_shape<__bf16, 128, kDecode>(a, s, st);
+    if (d == 64) return launch_shape<__bf16, 64, kDecode>(a, s, st);
   } else {
-    if (d == 128) return launch<float, 128>(a, st);
-    if (d == 64) return launch<float, 64>(a, st);
+    if (d == 128) return launch_shape<float, 128, kDecode>(a, s, st);
+    if (d == 64) return launch_shape<float, 64, kDecode>(a, s, st);
   }
   return RAX_EINVAL;
+}
+
+// Workspace of a decode call, in floats: shared-part partials (accumulators, then m/l),
+// the row blocks' shared lengths, own-part partials (accumulators, then m/l).
+struct DecodeLayout {
+  int64_t sh_acc, sh_ml, L, own_acc, own_ml, total;
+  int32_t nsplit, n_rb, n_chunk, bm;
+  bool split_decode;
+};
+
+static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
+                                  rax_dtype dt) {
+  DecodeLayout l{};
+  const int g = h_q / h_kv;
+  const Shape s = pick_shape(true, dt);
+  l.bm = s.bm();
+  l.n_rb = (int32_t)((batch * g + l.bm - 1) / l.bm);
+  l.nsplit = choose_nsplit((int64_t)l.n_rb * h_kv, max_seq_len);
+  l.split_decode = g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+  if (!l.split_decode) {
+    l.sh_acc = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * d : 0;
+    l.sh_ml = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * 2 : 0;
+    l.total = l.sh_acc + l.sh_ml;
+    return l;
+  }
+  // own part: up to one chunk per 256 keys of the longest sequence, at most 64 - nsplit
+  // partials per row (the kernel uses fewer when a request's own keys are fewer)
+  l.n_chunk = max(1, min(64 - l.nsplit, (max_seq_len + 255) / 256));
+  const int64_t sh_items = (int64_t)h_kv * l.n_rb * l.nsplit;
+  const int64_t own_rows = batch * h_kv * l.n_chunk * g;
+  l.sh_acc = sh_items * l.bm * d;
+  l.sh_ml = sh_items * l.bm * 2;
+  l.L = (l.n_rb + 63) / 64 * 64;
+  l.own_acc = own_rows * d;
+  l.own_ml = own_rows * 2;
+  l.total = l.sh_acc + l.sh_ml + l.L + l.own_acc + l.own_ml;
+  return l;
 }
 
 static bool common_ok(int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt, rax_dtype o_dt) {
   if (h_q < 1 || h_kv < 1 || h_q % h_kv) return false;
   const int g = h_q / h_kv;
-  if (g > BM || BM % g) return false;  // query-head groups tile a block exactly
+  if (g > 64 || 64 % g) return false;  // query-head groups tile every block shape exactly
   if (d != 64 && d != 128) return false;
   if ((dt != RAX_F32 && dt != RAX_BF16) || (o_dt != RAX_F32 && o_dt != RAX_BF16)) return false;
   return true;
@@ -583,11 +1088,14 @@ using namespace raxk;
 
 extern "C" size_t rax_attention_workspace_bytes(int32_t is_decode, int64_t rows, int32_t h_q, int32_t h_kv,
                                                 int32_t d, int32_t max_kv_len) {
-  if (rows <= 0 || h_kv < 1 || h_q < h_kv || h_q % h_kv || (d != 64 && d != 128)) return 0;
+  if (rows <= 0 || h_kv < 1 || h_q < h_kv || h_q % h_kv || (d != 64 && d != 128) || max_kv_len < 0) return 0;
   if (!is_decode) return 0;  // extend writes O directly
-  const int64_t n_rb = (rows * (h_q / h_kv) + BM - 1) / BM;
-  const int ns = choose_nsplit(n_rb * h_kv, max_kv_len);
-  return ns > 1 ? ws_bytes_for((int64_t)h_kv * n_rb * ns, d) : 0;
+  size_t need = 0;           // the larger need of the two input dtypes' block shapes
+  for (rax_dtype dt : {RAX_BF16, RAX_F32}) {
+    const DecodeLayout l = decode_layout(rows, h_q, h_kv, d, max_kv_len, dt);
+    need = max(need, (size_t)l.total * sizeof(float));
+  }
+  return need;
 }
 
 extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, const void* v_ext,
@@ -607,6 +1115,7 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   if (!q || !k_ext || !v_ext || !k_pool || !v_pool || !req_to_token || !req_pool_idx || !prefix_len ||
       !qo_indptr || !o)
     return RAX_EINVAL;
+  const Shape s = pick_shape(false, dt);
   AttnArgs a{};
   a.q = q;
   a.k_ext = k_ext;
@@ -631,8 +1140,9 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   a.o_bf16 = o_dt == RAX_BF16;
   a.ws = nullptr;
   a.nsplit = 1;
-  a.n_rb = (int32_t)((total_q * a.g + BM - 1) / BM);
-  return dispatch(a, dt, d, (hipStream_t)stream);
+  a.bm = s.bm();
+  a.n_rb = (int32_t)((total_q * a.g + a.bm - 1) / a.bm);
+  return dispatch<false>(a, dt, d, s, (hipStream_t)stream);
 }
 
 extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v_pool,
@@ -647,6 +1157,7 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
     return RAX_EINVAL;
   if (batch == 0) return RAX_OK;
   if (!q || !k_pool || !v_pool || !req_to_token || !req_pool_idx || !seq_len || !o) return RAX_EINVAL;
+  const Shape s = pick_shape(true, dt);
   AttnArgs a{};
   a.q = q;
   a.k_pool = k_pool;
@@ -667,12 +1178,20 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.o_bf16 = o_dt == RAX_BF16;
-  a.n_rb = (int32_t)(((int64_t)batch * a.g + BM - 1) / BM);
-  a.nsplit = choose_nsplit((int64_t)a.n_rb * h_kv, max_seq_len);
-  if (a.nsplit > 1) {
-    const size_t need = ws_bytes_for((int64_t)h_kv * a.n_rb * a.nsplit, d);
-    if (!workspace || ws_bytes < need) return RAX_EINVAL;
-    a.ws = reinterpret_cast<float*>(workspace);
+  const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt);
+  a.bm = l.bm;
+  a.n_rb = l.n_rb;
+  a.nsplit = l.nsplit;
+  if (l.total > 0) {
+    if (!workspace || ws_bytes < (size_t)l.total * sizeof(float)) return RAX_EINVAL;
+    float* w = reinterpret_cast<float*>(workspace);
+    a.ws = w;
+    if (l.split_decode) {
+      a.shared_only = 1;
+      a.ws_L = reinterpret_cast<int32_t*>(w + l.sh_acc + l.sh_ml);
+      a.ws_own = w + l.sh_acc + l.sh_ml + l.L;
+      a.n_chunk = l.n_chunk;
+    }
   }
-  return dispatch(a, dt, d, (hipStream_t)stream);
+  return dispatch<true>(a, dt, d, s, (hipStream_t)stream);
 }

@@ -141,6 +141,74 @@ rax_status rax_tree_dump(const rax_tree* t, int64_t* buf, int64_t cap, int64_t* 
   RAX_GUARD_END
 }
 
+rax_status rax_match_prefix_batch(rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                                  int32_t cut_full, int32_t lock, int32_t* out_slots, int64_t* out_len,
+                                  rax_node* out_node) {
+  if (!t || batch < 0 || (batch > 0 && (!indptr || !out_len || !out_node))) return RAX_EINVAL;
+  if (batch > 0 && indptr[0] != 0) return RAX_EINVAL;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr[r + 1] < indptr[r]) return RAX_EINVAL;
+  if (batch > 0 && indptr[batch] > 0 && (!tokens || !out_slots)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t n = indptr[r + 1] - indptr[r];
+    int64_t m = t->t.match(tokens + indptr[r], n, out_slots + indptr[r], &out_node[r]);
+    if (cut_full && n > 0 && m == n) --m;
+    out_len[r] = m;
+    if (lock) t->t.lock_ref(out_node[r], +1);
+  }
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_insert_batch(rax_tree* t, const int32_t* tokens, const int32_t* slots, const int64_t* indptr,
+                            int32_t batch, int32_t* out_slots, int64_t* out_existing, rax_node* out_node,
+                            int32_t* out_done) {
+  if (out_done) *out_done = 0;
+  if (!t || batch < 0 || (batch > 0 && (!indptr || !out_existing || !out_node))) return RAX_EINVAL;
+  if (batch > 0 && indptr[0] != 0) return RAX_EINVAL;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr[r + 1] < indptr[r]) return RAX_EINVAL;
+  if (batch > 0 && indptr[batch] > 0 && (!tokens || !slots)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t o = indptr[r], n = indptr[r + 1] - o;
+    if (!t->t.insert(tokens + o, slots + o, n, out_slots ? out_slots + o : nullptr, &out_existing[r],
+                     &out_node[r]))
+      return RAX_EINVAL;
+    if (out_done) *out_done = r + 1;
+  }
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_lock_ref_batch(rax_tree* t, const rax_node* nodes, int32_t n, int32_t delta) {
+  if (!t || n < 0 || (n > 0 && !nodes) || (delta != 1 && delta != -1)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = t->t.lock_ref(nodes[i], delta);
+    if (rc != 0) {  // undo the ones already applied
+      for (int32_t j = 0; j < i; ++j) t->t.lock_ref(nodes[j], -delta);
+      return RAX_ESTATE;
+    }
+  }
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_lca_depths(const rax_tree* t, const rax_node* nodes, int32_t n, int32_t* out) {
+  if (!t || n < 0 || (n > 0 && (!nodes || !out))) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  if (n > 0) out[0] = 0;
+  for (int32_t i = 1; i < n; ++i) {
+    int64_t d = 0;
+    if (!t->t.lca_depth(nodes[i - 1], nodes[i], &d)) return RAX_ESTATE;
+    out[i] = static_cast<int32_t>(d);
+  }
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
 rax_status rax_free_count(const rax_tree* t, int64_t* out) {
   if (!t || !out) return RAX_EINVAL;
   *out = t->t.alloc().num_free();

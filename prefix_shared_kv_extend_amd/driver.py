@@ -78,7 +78,9 @@ class JobRunner:
                 rt.run_decode(db, q, k, v, o)
                 if on_decode is not None:
                     on_decode(si, db, pairs, o)
-            for rid in st.finish:
-                n_done = len(rt.reqs[rid].slots)
-                self.final_rows[rid] = rt.finish(rid, self.full[rid][:n_done])
+            if st.finish:
+                rows = rt.finish_batch([(rid, self.full[rid][: rt.seq_len(rid)]) for rid in st.finish])
+                if self.log is not None:
+                    for rid, row in zip(st.finish, rows):
+                        self.final_rows[rid] = row.tolist()
         return self

@@ -4,24 +4,25 @@ Per batch (2312.07104_SGLang notes, App. A.2: match every request, form the batc
 evicting when memory is short, run it, update the tree; hustzhy SGLang post,
 §2.3 (2): traverse -> reuse -> compute -> insert):
 
-  extend   match each prompt in the tree (rax_match_prefix) and lock the matched
-           node; allocate slots for all unmatched suffixes at once
-           (rax_alloc_slots_evict); fill the requests' req_to_token rows on the
+  extend   match each prompt in the tree and lock the matched node
+           (rax_match_prefix_batch); allocate slots for all unmatched suffixes at
+           once (rax_alloc_slots_evict); fill the requests' req_to_token rows on the
            device; write the new tokens' K/V into the pool (rax_kv_scatter); run
-           extend attention over reused prefix + causal suffix; then insert each
-           prompt (rax_insert) and move the lock to the new node.
-  decode   allocate one slot per request, append it to the row, write the new
-           token's K/V, run decode attention over the whole row.
+           extend attention over reused prefix + causal suffix; then insert every
+           prompt (rax_insert_batch) and move the locks to the new nodes.
+  decode   allocate one slot per request, append it to the rows, write the new
+           tokens' K/V, run decode attention over the whole rows.
   finish   insert prompt + generated tokens, unlock.
 
 A match that covers the whole prompt is cut by one token so the request has a
 query to run. Consecutive requests' common slot prefix (the depth of the lowest
-common ancestor of their tree nodes, rax_lca_depth) is passed to the kernels as
+common ancestor of their tree nodes, rax_lca_depths) is passed to the kernels as
 `shared_len`, so K/V tiles they share are loaded once for all of them.
 
 All arithmetic runs in librax (host tree in C++, attention and data movement in
-HIP kernels). This module only sequences the calls and moves int32 metadata to
-the device in one pinned copy per call.
+HIP kernels). This module sequences the calls, keeps a host mirror of the
+req_to_token table, and moves each call's int32 metadata to the device in one
+pinned copy.
 """
 from __future__ import annotations
 
@@ -34,21 +35,14 @@ from . import _lib as L
 
 
 @dataclass
-class ReqState:
-    rid: int
-    row: int                      # req_to_token row
-    n_prompt: int
-    slots: list                   # host copy of the request's slot row
-    node: int                     # locked tree node
-
-
-@dataclass
 class ExtendBatch:
     rids: list
     prefix_len: np.ndarray        # m per request (after the full-match cut)
     q_len: np.ndarray
     qo_indptr: np.ndarray
     total_q: int
+    tokens: np.ndarray = None     # prompts, flat
+    tok_indptr: np.ndarray = None
     dev: dict = field(default_factory=dict)
 
 
@@ -70,13 +64,18 @@ class RadixRuntime:
         self.k_pool = torch.zeros((num_slots, h_kv, d), dtype=dtype, device=self.device)
         self.v_pool = torch.zeros((num_slots, h_kv, d), dtype=dtype, device=self.device)
         self.rtt = torch.zeros((max_reqs, max_ctx), dtype=torch.int32, device=self.device)
+        self.rows = np.zeros((max_reqs, max_ctx), dtype=np.int32)   # host mirror of rtt
         self.max_ctx = max_ctx
         self.free_rows = list(range(max_reqs - 1, -1, -1))
-        self.reqs: dict[int, ReqState] = {}
+        self.row_of: dict[int, int] = {}
+        self.len_of: dict[int, int] = {}     # current sequence length (slots in the row)
+        self.n_prompt: dict[int, int] = {}
+        self.node_of: dict[int, int] = {}    # locked tree node
         self.log = log
-        self.step = 0                 # label of the current step in the event log (set by the caller)
-        self.timers = None            # {"extend": [...], "decode": [...]} of (start, end) events, if set
+        self.step = 0                        # label of the current step in the event log (set by the caller)
+        self.timers = None                   # {"extend": [...], "decode": [...]} of (start, end) events, if set
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self._dec_cache = None               # (rids tuple, rows, device views) while the decode batch is unchanged
 
     # ------------------------------------------------------------------ helpers
     def _upload(self, parts: dict) -> dict:
@@ -102,12 +101,6 @@ class RadixRuntime:
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def _shared_len(self, rids) -> np.ndarray:
-        out = np.zeros(len(rids), dtype=np.int32)
-        for i in range(1, len(rids)):
-            out[i] = self.tree.lca_depth(self.reqs[rids[i - 1]].node, self.reqs[rids[i]].node)
-        return out
-
     def _event_pair(self, kind):
         """When timing is on: record a start event now on the current stream, return (start, end)."""
         if self.timers is None:
@@ -121,48 +114,62 @@ class RadixRuntime:
         if self.log is not None:
             self.log.append(ev)
 
+    def seq_len(self, rid: int) -> int:
+        """Current number of slots in the request's row."""
+        if self._dec_cache is not None and rid in self._dec_cache[0]:
+            return int(self._dec_cache[3][self._dec_cache[0].index(rid)])
+        return self.len_of[rid]
+
+    def slot_row(self, rid: int) -> np.ndarray:
+        return self.rows[self.row_of[rid], : self.seq_len(rid)].copy()
+
     # ------------------------------------------------------------------- extend
     def begin_extend(self, batch) -> ExtendBatch:
         """batch: list of (rid, prompt int32 array). Tree side + req_to_token fill."""
-        rids, m_list, pre = [], [], []
-        for rid, prompt in batch:
-            prompt = np.asarray(prompt, dtype=np.int32)
-            m, pslots, node = self.tree.match_prefix(prompt)
-            if m == len(prompt):
-                m -= 1
-                pslots = pslots[:m]
-            self._log("match", rid, m, node)
-            self.tree.lock_ref(node, +1)
-            if len(prompt) > self.max_ctx:
-                raise ValueError("prompt longer than the req_to_token rows")
-            self.reqs[rid] = ReqState(rid, self.free_rows.pop(), len(prompt), [], node)
-            rids.append(rid)
-            m_list.append(m)
-            pre.append(pslots)
-        n_list = [self.reqs[r].n_prompt for r in rids]
-        q_len = np.array([n - m for n, m in zip(n_list, m_list)], dtype=np.int32)
+        rids = [rid for rid, _ in batch]
+        prompts = [np.asarray(p, dtype=np.int32) for _, p in batch]
+        n = np.array([len(p) for p in prompts], dtype=np.int64)
+        if len(n) and int(n.max()) > self.max_ctx:
+            raise ValueError("prompt longer than the req_to_token rows")
+        ip = np.zeros(len(rids) + 1, dtype=np.int64)
+        ip[1:] = np.cumsum(n)
+        toks = np.concatenate(prompts) if prompts else np.zeros(0, np.int32)
+        pslots, m, nodes = self.tree.match_prefix_batch(toks, ip, cut_full=True, lock=True)
+        if self.log is not None:
+            for i, rid in enumerate(rids):
+                self._log("match", rid, int(m[i]), int(nodes[i]))
+        q_len = (n - m).astype(np.int32)
         new, freed = self.tree.alloc_slots_evict(int(q_len.sum()))
-        if len(freed):
-            self._log("evict", self.step, tuple(freed.tolist()))
-        self._log("alloc", self.step, tuple(new.tolist()))
-        rows_src, off = [], 0
+        if self.log is not None:
+            if len(freed):
+                self._log("evict", self.step, tuple(freed.tolist()))
+            self._log("alloc", self.step, tuple(new.tolist()))
+        src = np.empty(int(ip[-1]), dtype=np.int32)
+        off = 0
+        req_rows = np.empty(len(rids), dtype=np.int32)
         for i, rid in enumerate(rids):
-            st = self.reqs[rid]
-            own = new[off: off + q_len[i]]
-            off += q_len[i]
-            st.slots = pre[i].tolist() + own.tolist()
-            rows_src.append(np.concatenate([pre[i], own]))
+            row = self.free_rows.pop()
+            a, b, mi, qi = int(ip[i]), int(ip[i + 1]), int(m[i]), int(q_len[i])
+            src[a: a + mi] = pslots[a: a + mi]
+            src[a + mi: b] = new[off: off + qi]
+            off += qi
+            self.rows[row, : b - a] = src[a: b]
+            self.row_of[rid] = row
+            self.len_of[rid] = b - a
+            self.n_prompt[rid] = b - a
+            self.node_of[rid] = int(nodes[i])
+            req_rows[i] = row
         qo = np.zeros(len(rids) + 1, dtype=np.int32)
         qo[1:] = np.cumsum(q_len)
-        src_indptr = np.zeros(len(rids) + 1, dtype=np.int32)
-        src_indptr[1:] = np.cumsum(n_list)
-        eb = ExtendBatch(rids, np.array(m_list, dtype=np.int32), q_len, qo, int(qo[-1]))
+        eb = ExtendBatch(rids, m.astype(np.int32), q_len, qo, int(qo[-1]), toks, ip)
         eb.dev = self._upload(dict(
-            req_pool_idx=[self.reqs[r].row for r in rids], prefix_len=eb.prefix_len, qo_indptr=qo,
-            shared_len=self._shared_len(rids), out_loc=new, rtt_start=np.zeros(len(rids)),
-            rtt_indptr=src_indptr, rtt_src=np.concatenate(rows_src) if rows_src else np.zeros(0)))
+            req_pool_idx=req_rows, prefix_len=eb.prefix_len, qo_indptr=qo,
+            shared_len=self.tree.lca_depths(nodes), out_loc=new, rtt_start=np.zeros(len(rids)),
+            rtt_indptr=ip, rtt_src=src))
         L.req_to_token_write(self.rtt, eb.dev["req_pool_idx"], eb.dev["rtt_start"], eb.dev["rtt_indptr"],
-                             eb.dev["rtt_src"], int(src_indptr[-1]))
+                             eb.dev["rtt_src"], int(ip[-1]))
+        self._sync_decode_lengths()
+        self._dec_cache = None
         return eb
 
     def run_extend(self, eb: ExtendBatch, q, k_ext, v_ext, o) -> None:
@@ -176,47 +183,68 @@ class RadixRuntime:
         if ev:
             ev[1].record()
 
-    def end_extend(self, eb: ExtendBatch, prompts: dict) -> None:
+    def end_extend(self, eb: ExtendBatch, prompts=None) -> None:
         """Insert every prompt; requests switch to the tree's copy of any duplicate slots."""
-        fix_rows, fix_pos, fix_val = [], [], []
-        for rid in eb.rids:
-            st = self.reqs[rid]
-            prompt = np.asarray(prompts[rid], dtype=np.int32)
-            existing, node, tslots = self.tree.insert(prompt, np.asarray(st.slots[: st.n_prompt], np.int32))
-            self._log("insert", rid, existing, node)
-            ts = tslots.tolist()
-            if ts != st.slots[: st.n_prompt]:
-                for p in range(st.n_prompt):
-                    if ts[p] != st.slots[p]:
-                        fix_rows.append(st.row)
-                        fix_pos.append(p)
-                        fix_val.append(ts[p])
-                st.slots[: st.n_prompt] = ts
-            self.tree.lock_ref(node, +1)
-            self.tree.lock_ref(st.node, -1)
-            st.node = node
-        if fix_val:
-            k = len(fix_val)
-            dv = self._upload(dict(rows=fix_rows, start=fix_pos, indptr=np.arange(k + 1), src=fix_val))
+        rids, ip = eb.rids, eb.tok_indptr
+        rows = [self.row_of[r] for r in rids]
+        slots = np.concatenate([self.rows[row, : self.n_prompt[r]] for r, row in zip(rids, rows)]) \
+            if rids else np.zeros(0, np.int32)
+        tslots, existing, nodes = self.tree.insert_batch(eb.tokens, slots, ip)
+        if self.log is not None:
+            for i, rid in enumerate(rids):
+                self._log("insert", rid, int(existing[i]), int(nodes[i]))
+        diff = np.nonzero(tslots != slots)[0]
+        if len(diff):
+            req_i = np.searchsorted(ip, diff, side="right") - 1
+            pos = diff - ip[req_i]
+            fix_rows = np.array(rows, dtype=np.int32)[req_i]
+            self.rows[fix_rows, pos] = tslots[diff]
+            k = len(diff)
+            dv = self._upload(dict(rows=fix_rows, start=pos, indptr=np.arange(k + 1), src=tslots[diff]))
             L.req_to_token_write(self.rtt, dv["rows"], dv["start"], dv["indptr"], dv["src"], k)
+        old = [self.node_of[r] for r in rids]
+        self.tree.lock_ref_batch(nodes, +1)
+        self.tree.lock_ref_batch(old, -1)
+        for i, rid in enumerate(rids):
+            self.node_of[rid] = int(nodes[i])
+        self._sync_decode_lengths()
+        self._dec_cache = None
 
     # ------------------------------------------------------------------- decode
+    def _sync_decode_lengths(self):
+        """Write the decode batch's cached lengths back to the per-request table."""
+        if self._dec_cache is not None:
+            key, _, _, lens = self._dec_cache
+            for i, r in enumerate(key):
+                self.len_of[r] = int(lens[i])
+
     def begin_decode(self, rids) -> DecodeBatch:
+        key = tuple(rids)
+        if self._dec_cache is None or self._dec_cache[0] != key:
+            self._sync_decode_lengths()
+            req_rows = np.array([self.row_of[r] for r in rids], dtype=np.int32)
+            nodes = [self.node_of[r] for r in rids]
+            inv = self._upload(dict(req_pool_idx=req_rows, shared_len=self.tree.lca_depths(nodes),
+                                    rtt_indptr=np.arange(len(rids) + 1)))
+            lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
+            self._dec_cache = (key, req_rows, inv, lens)
+        _, req_rows, inv, lens = self._dec_cache
         new, freed = self.tree.alloc_slots_evict(len(rids))
-        if len(freed):
-            self._log("evict", self.step, tuple(freed.tolist()))
-        self._log("alloc", self.step, tuple(new.tolist()))
-        seq_len = np.empty(len(rids), dtype=np.int32)
-        for i, rid in enumerate(rids):
-            st = self.reqs[rid]
-            st.slots.append(int(new[i]))
-            seq_len[i] = len(st.slots)
-        if int(seq_len.max()) > self.max_ctx:
+        if self.log is not None:
+            if len(freed):
+                self._log("evict", self.step, tuple(freed.tolist()))
+            self._log("alloc", self.step, tuple(new.tolist()))
+        lens += 1                      # lengths live in the cache while the batch is unchanged
+        max_seq = int(lens.max())
+        if max_seq > self.max_ctx:
+            lens -= 1
             raise ValueError("sequence longer than the req_to_token rows")
-        db = DecodeBatch(list(rids), seq_len, int(seq_len.max()))
-        db.dev = self._upload(dict(
-            req_pool_idx=[self.reqs[r].row for r in rids], seq_len=seq_len, shared_len=self._shared_len(rids),
-            out_loc=new, rtt_start=seq_len - 1, rtt_indptr=np.arange(len(rids) + 1)))
+        self.rows[req_rows, lens - 1] = new
+        seq_len = lens.copy()
+        db = DecodeBatch(list(rids), seq_len, max_seq)
+        var = self._upload(dict(seq_len=seq_len, out_loc=new, rtt_start=seq_len - 1))
+        db.dev = dict(inv)
+        db.dev.update(var)
         L.req_to_token_write(self.rtt, db.dev["req_pool_idx"], db.dev["rtt_start"], db.dev["rtt_indptr"],
                              db.dev["out_loc"], len(rids))
         return db
@@ -232,17 +260,37 @@ class RadixRuntime:
             ev[1].record()
 
     # ------------------------------------------------------------------- finish
-    def finish(self, rid: int, tokens) -> list:
-        """Insert prompt + generated tokens, unlock; returns the tree's slots for them."""
-        st = self.reqs.pop(rid)
-        toks = np.asarray(tokens, dtype=np.int32)
-        if len(toks) != len(st.slots):
-            raise ValueError("finish: tokens and slot row differ in length")
-        existing, node, tslots = self.tree.insert(toks, np.asarray(st.slots, dtype=np.int32))
-        self._log("insert", rid, existing, node)
-        self.tree.lock_ref(st.node, -1)
-        self.free_rows.append(st.row)
-        return tslots.tolist()
+    def finish(self, rid: int, tokens) -> np.ndarray:
+        """Insert prompt + generated tokens of one request, unlock; returns the tree's slots."""
+        return self.finish_batch([(rid, tokens)])[0]
 
-    def slot_row(self, rid: int) -> list:
-        return list(self.reqs[rid].slots)
+    def finish_batch(self, items) -> list:
+        """items: list of (rid, tokens). Insert each, unlock each; returns the tree's slot rows."""
+        if not items:
+            return []
+        self._sync_decode_lengths()
+        rids = [rid for rid, _ in items]
+        toks = [np.asarray(t, dtype=np.int32) for _, t in items]
+        for rid, t in zip(rids, toks):
+            if len(t) != self.len_of[rid]:
+                raise ValueError("finish: tokens and slot row differ in length")
+        ip = np.zeros(len(rids) + 1, dtype=np.int64)
+        ip[1:] = np.cumsum([len(t) for t in toks])
+        slots = np.concatenate([self.rows[self.row_of[r], : self.len_of[r]] for r in rids])
+        tslots, existing, nodes = self.tree.insert_batch(np.concatenate(toks), slots, ip)
+        if self.log is not None:
+            for i, rid in enumerate(rids):
+                self._log("insert", rid, int(existing[i]), int(nodes[i]))
+        self.tree.lock_ref_batch([self.node_of[r] for r in rids], -1)
+        out = []
+        for i, rid in enumerate(rids):
+            self.free_rows.append(self.row_of.pop(rid))
+            del self.len_of[rid], self.n_prompt[rid], self.node_of[rid]
+            out.append(tslots[ip[i]: ip[i + 1]])
+        self._dec_cache = None
+        return out
+
+    @property
+    def reqs(self):
+        """Running request ids (those holding a req_to_token row)."""
+        return self.row_of
