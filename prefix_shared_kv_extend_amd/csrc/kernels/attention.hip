@@ -42,6 +42,8 @@
 //    share its L2 for the prefix tiles they all read.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "../../../include/rax.h"
@@ -732,7 +734,7 @@ __device__ __forceinline__ float piece_elem(piece_t<T, E> r, int e) {
 // the request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
 // at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets the
 // first own position and the chunk size.
-constexpr int kOwnMin = 64;
+constexpr int kOwnMin = 32;
 __device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, int& per) {
   const int L = a.ws_L[((int64_t)r * a.g) / a.bm];
   const int end = a.kv_len[r];
@@ -760,7 +762,7 @@ __device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
   constexpr int E = D / 64;
-  constexpr int KB = (sizeof(T) == 4 ? 32 : 64) / G > 0 ? (sizeof(T) == 4 ? 32 : 64) / G : 1;
+  constexpr int KB = 32 / G > 0 ? 32 / G : 1;  // 32 (key, head) pairs per batch
   constexpr int P = KB * G;
   using Raw = piece_t<T, E>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -876,9 +878,10 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
 
 // Log-sum-exp merge of partials: one wave per (MFMA row, KV head). Inputs are the split
 // partials of the row's block and, for split decode, the own-part chunks of the row's
-// request. Lane s fetches partial s's (m, l), so the wave reads every partial's state at
-// once; accumulator rows are then read eight partials at a time with unconditional loads
-// (rows of partials that saw no key are read and given weight 0).
+// request. Lane s fetches partial s's (m, l) for every partial that may exist, in the same
+// round trip as the request's own-chunk count; then only partials with nonzero weight are
+// visited, up to 32 per round trip, with unconditional loads (spare load slots read the
+// first such partial and get weight 0).
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -890,27 +893,28 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const int hq = h * a.g + hl;
   const int64_t rb = G / a.bm;
   const int R = (int)(G % a.bm);
-  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-  const int64_t item0 = ((int64_t)h * a.n_rb + rb) * a.nsplit;
-  const float* ml = a.ws + n_items * a.bm * (int64_t)D;
-  int n_own = 0, first = 0, per = 0;
-  if (a.shared_only) n_own = own_chunks(a, (int)t, first, per);
+  const int nsplit = a.nsplit;
+  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+  const int64_t item0 = ((int64_t)h * a.n_rb + rb) * nsplit;
   const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
   const int64_t own0 = (t * a.h_kv + h) * a.n_chunk;  // own items of (request t, KV head h)
-  const float* oml = a.ws_own + own_items * a.g * (int64_t)D;
   // partial s < nsplit: split s of the block; otherwise own chunk s - nsplit
-  auto acc_ptr = [&](int s) -> const float* {
-    if (s < a.nsplit) return a.ws + ((item0 + s) * a.bm + R) * (int64_t)D;
-    return a.ws_own + ((own0 + (s - a.nsplit)) * a.g + hl) * (int64_t)D;
-  };
-  const int n_part = a.nsplit + n_own;  // <= 64
-  float my_m = kNegInf, my_l = 0.f;
-  if (lane < n_part) {
-    const float* e = lane < a.nsplit ? ml + ((item0 + lane) * a.bm + R) * 2
-                                     : oml + ((own0 + (lane - a.nsplit)) * a.g + hl) * 2;
-    my_m = e[0];
-    my_l = e[1];
-  }
+  const float* sh_acc = a.ws + (item0 * a.bm + R) * (int64_t)D;
+  const int64_t sh_stride = (int64_t)a.bm * D;
+  const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + R) * 2;
+  const float* own_base = a.shared_only ? a.ws_own : a.ws;  // no own partials: never read
+  const float* own_acc = own_base + (own0 * a.g + hl) * (int64_t)D - (int64_t)nsplit * a.g * D;
+  const int64_t own_stride = (int64_t)a.g * D;
+  const float* own_ml = own_base + own_items * a.g * (int64_t)D + (own0 * a.g + hl) * 2 - (int64_t)nsplit * a.g * 2;
+  const int n_max = nsplit + (a.shared_only ? a.n_chunk : 0);  // <= 64
+  const int sl = lane < n_max ? lane : 0;
+  const float2 mlv = *reinterpret_cast<const float2*>(sl < nsplit ? sh_ml + (int64_t)sl * a.bm * 2
+                                                                  : own_ml + (int64_t)sl * a.g * 2);
+  const float my_m = mlv.x;
+  float my_l = lane < n_max ? mlv.y : 0.f;
+  int n_own = 0, first = 0, per = 0;
+  if (a.shared_only) n_own = own_chunks(a, (int)t, first, per);
+  if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -920,25 +924,28 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
   constexpr int PER = D / 64;
-  constexpr int U = 8;
+  constexpr int U = 32;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int s0 = 0; s0 < n_part; s0 += U) {
+  uint64_t nz = __ballot(my_w != 0.f);
+  const int s_first = nz ? __builtin_ctzll(nz) : 0;
+  while (nz) {
     float x[U][PER], w[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int s = s0 + j;
-      w[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), s & 63));
-      if (s >= n_part) w[j] = 0.f;
-      const float* p = acc_ptr(s < n_part ? s : 0);
+      const int s = nz ? __builtin_ctzll(nz) : s_first;
+      w[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), s));
+      if (!nz) w[j] = 0.f;
+      nz &= nz - 1;
+      const float* p = s < nsplit ? sh_acc + s * sh_stride : own_acc + s * own_stride;
 #pragma unroll
       for (int i = 0; i < PER; ++i) x[j][i] = p[lane + 64 * i];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += w[j] != 0.f ? w[j] * x[j][i] : 0.f;
+      for (int i = 0; i < PER; ++i) o[i] += w[j] * x[j][i];
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int64_t obase = (t * a.h_q + hq) * (int64_t)D;
@@ -1059,9 +1066,14 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
     l.total = l.sh_acc + l.sh_ml;
     return l;
   }
-  // own part: up to one chunk per 256 keys of the longest sequence, at most 64 - nsplit
-  // partials per row (the kernel uses fewer when a request's own keys are fewer)
-  l.n_chunk = max(1, min(64 - l.nsplit, (max_seq_len + 255) / 256));
+  // own part: chunks per (request, KV head) so that about kOwnWaves waves exist in total,
+  // at most one per kOwnMin keys of the longest sequence and at most 64 - nsplit partials
+  // per row; the kernel uses fewer when a request has fewer own keys. Waves past a
+  // request's chunks exit at once, but still hold a wave slot while they do.
+  constexpr int64_t kOwnWaves = 8192;
+  const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
+  l.n_chunk = (int32_t)std::max<int64_t>(
+      1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnMin - 1) / kOwnMin, (kOwnWaves + pairs - 1) / pairs}));
   const int64_t sh_items = (int64_t)h_kv * l.n_rb * l.nsplit;
   const int64_t own_rows = batch * h_kv * l.n_chunk * g;
   l.sh_acc = sh_items * l.bm * d;
