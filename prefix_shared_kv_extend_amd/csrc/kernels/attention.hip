@@ -53,6 +53,7 @@ namespace raxk {
 
 constexpr int BN = 64;  // keys per tile
 constexpr float kNegInf = -INFINITY;
+constexpr float kLazy = 8.f;  // log2 headroom of the lazy softmax rescale
 
 struct AttnArgs {
   const void* q;
@@ -135,6 +136,10 @@ __device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t
   return lo;
 }
 
+// Wave-uniform value (kept in an SGPR): block metadata read from LDS is the same in
+// every lane, and saying so keeps tile bookkeeping off the exec mask.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <typename SM>
 __device__ __forceinline__ TileDesc describe(int tau, const SM& sm, int L, int n_sh, int n_own, int suf0,
                                              int64_t qb, int nreq) {
@@ -147,20 +152,20 @@ __device__ __forceinline__ TileDesc describe(int tau, const SM& sm, int L, int n
     d.kind = 0;
     d.pos0 = tau * BN;
     d.cnt = min(BN, L - d.pos0);
-    d.row = sm.req_row[0];
+    d.row = uni(sm.req_row[0]);
   } else if (tau < n_sh + n_own) {
     d.kind = 1;
     const int o = tau - n_sh;
     int lo = 0, hi = nreq - 1;  // last i with own[i] <= o
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (sm.own[mid] <= o) lo = mid;
+      if (uni(sm.own[mid]) <= o) lo = mid;
       else hi = mid - 1;
     }
     d.req = lo;
-    d.pos0 = L + (o - sm.own[lo]) * BN;
-    d.cnt = min(BN, sm.req_m[lo] - d.pos0);
-    d.row = sm.req_row[lo];
+    d.pos0 = L + (o - uni(sm.own[lo])) * BN;
+    d.cnt = min(BN, uni(sm.req_m[lo]) - d.pos0);
+    d.row = uni(sm.req_row[lo]);
   } else {
     d.kind = 2;
     d.kr0 = suf0 + (tau - n_sh - n_own) * BN;
@@ -251,8 +256,8 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     sm.hdr[1] = nreq;
   }
   __syncthreads();
-  const int r0 = sm.hdr[0];
-  const int nreq = sm.hdr[1];
+  const int r0 = uni(sm.hdr[0]);
+  const int nreq = uni(sm.hdr[1]);
   for (int i = tid; i < nreq; i += C::kThreads) {
     const int r = r0 + i;
     int row = a.req_pool_idx[r];
@@ -308,12 +313,12 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-  const int L = sm.hdr[2];
-  const int n_sh = sm.hdr[3];
-  const int n_own = sm.hdr[4];
-  const int t_begin = sm.hdr[5];
-  const int t_end = sm.hdr[6];
-  const int suf0 = sm.req_qo[0];
+  const int L = uni(sm.hdr[2]);
+  const int n_sh = uni(sm.hdr[3]);
+  const int n_own = uni(sm.hdr[4]);
+  const int t_begin = uni(sm.hdr[5]);
+  const int t_end = uni(sm.hdr[6]);
+  const int suf0 = uni(sm.req_qo[0]);
 
   // ---- this lane's rows (RT row tiles)
   bool row_ok[RT];
@@ -354,8 +359,12 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     w_khi = max(w_khi, __shfl_xor(w_khi, off));
     n_bad += __shfl_xor(n_bad, off);
   }
+  w_rlo = uni(w_rlo);
+  w_rhi = uni(w_rhi);
+  w_klo = uni(w_klo);
+  w_khi = uni(w_khi);
   const bool wave_active = w_rhi >= 0;
-  const bool all_rows_ok = n_bad == 0;
+  const bool all_rows_ok = uni(n_bad) == 0;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row jrow, dims [ks*K + half*K/2, +K/2)
   constexpr int KSTEP = kBf16 ? 16 : 2;
@@ -402,14 +411,18 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     constexpr int set = decltype(set_c)::value;
     const char* kb = reinterpret_cast<const char*>(d.kind == 2 ? a.k_ext : a.k_pool) + head_off + coff;
     const char* vb = reinterpret_cast<const char*>(d.kind == 2 ? a.v_ext : a.v_pool) + head_off + coff;
+    // slot buffer sb may hold another tile's ids when !live: read it anyway, then drop
 #pragma unroll
-    for (int p = 0; p < C::KP; ++p)
-      kreg[set][p] = ld16(kb, live ? sm.slot[sb][p * C::KPP + kk] : -1, row_bytes);
+    for (int p = 0; p < C::KP; ++p) {
+      const int sv = sm.slot[sb][p * C::KPP + kk];
+      kreg[set][p] = ld16(kb, live ? sv : -1, row_bytes);
+    }
 #pragma unroll
     for (int p = 0; p < C::VP; ++p) {
       const int kp = p * C::KPP + kk;
-      vreg[set][p][0] = ld16(vb, live ? sm.slot[sb][2 * kp] : -1, row_bytes);
-      vreg[set][p][1] = ld16(vb, live ? sm.slot[sb][2 * kp + 1] : -1, row_bytes);
+      const int s0 = sm.slot[sb][2 * kp], s1 = sm.slot[sb][2 * kp + 1];
+      vreg[set][p][0] = ld16(vb, live ? s0 : -1, row_bytes);
+      vreg[set][p][1] = ld16(vb, live ? s1 : -1, row_bytes);
     }
   };
   // registers -> LDS buffer b (K row-major, V transposed); keys without a slot become zeros
@@ -508,11 +521,12 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          // scale + mask; key index of register r: sub*32 + 8*(r/4) + 4*half + r%4
+          // mask (raw scores; the scale is positive); key index of register r:
+          // sub*32 + 8*(r/4) + 4*half + r%4
           float mx = kNegInf;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float v = s[rt][r] * a.scale_log2;
+            float v = s[rt][r];
             if (!unmasked) {
               const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
               bool ok = row_ok[rt] && key < d.cnt;
@@ -526,20 +540,25 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
             s[rt][r] = v;
             mx = fmaxf(mx, v);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float m_new = fmaxf(m_run[rt], mx);
-          const float m_use = m_new == kNegInf ? 0.f : m_new;
-          if (__any(m_new > m_run[rt])) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+          // Lazy rescale: the reference maximum of a row moves only when some row of the
+          // wave sees a score more than 2^kLazy above its reference (also on the first
+          // keys, reference -inf). In between, probabilities are up to 2^kLazy; l, acc
+          // and the final division all use the same reference, so the result is the
+          // same softmax.
+          if (__any(mx > m_run[rt] + kLazy)) {
+            const float m_new = fmaxf(m_run[rt], mx);
+            const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
             l_run[rt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) acc[rt][dt] *= alpha;
+            m_run[rt] = m_new;
           }
-          m_run[rt] = m_new;
+          const float neg_m = m_run[rt] == kNegInf ? 0.f : -m_run[rt];
           float psum = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[rt][r] - m_use);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][r], a.scale_log2, neg_m));
             s[rt][r] = p;
             psum += p;
           }
