@@ -248,10 +248,13 @@ def _dev(t):
     return _vp(t.data_ptr()) if t is not None else _vp(0)
 
 
-def _stream(stream):
+def _stream(stream, like=None):
+    """hipStream_t of `stream`; None means the current stream of like's device (else of the
+    current device). torch.cuda.current_stream() costs ~10 us per call, the raw query ~1 us."""
     if stream is None:
         import torch
-        stream = torch.cuda.current_stream()
+        dev = like.get_device() if like is not None else torch._C._cuda_getDevice()
+        return _vp(torch._C._cuda_getCurrentRawStream(dev))
     return _vp(getattr(stream, "cuda_stream", stream))
 
 
@@ -285,7 +288,7 @@ def kv_scatter(k_new, v_new, out_loc, k_pool, v_pool, stream=None) -> None:
     _need(out_loc.numel() == k_new.shape[0], "out_loc: [n_tok]")
     _check(lib().rax_kv_scatter(_dev(k_new), _dev(v_new), _dev(out_loc), k_new.shape[0], _dev(k_pool),
                                 _dev(v_pool), k_pool.shape[0], k_pool.shape[1], k_pool.shape[2],
-                                _dtype_code(k_pool), _stream(stream)), "rax_kv_scatter")
+                                _dtype_code(k_pool), _stream(stream, k_pool)), "rax_kv_scatter")
 
 
 def req_to_token_write(req_to_token, req_pool_idx, start, src_indptr, src_slots, total: int, stream=None) -> None:
@@ -295,7 +298,7 @@ def req_to_token_write(req_to_token, req_pool_idx, start, src_indptr, src_slots,
     _need(start.numel() == b and src_indptr.numel() == b + 1 and src_slots.numel() >= total, "shapes")
     _check(lib().rax_req_to_token_write(_dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
                                         _dev(req_pool_idx), _dev(start), _dev(src_indptr), _dev(src_slots),
-                                        b, int(total), _stream(stream)), "rax_req_to_token_write")
+                                        b, int(total), _stream(stream, req_to_token)), "rax_req_to_token_write")
 
 
 def attention_workspace_bytes(is_decode: bool, rows: int, h_q: int, h_kv: int, d: int, max_kv_len: int) -> int:
@@ -321,7 +324,7 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, req_to_token, req_pool_idx
         _dev(q), _dev(k_ext), _dev(v_ext), _dev(k_pool), _dev(v_pool), k_pool.shape[0],
         _dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0], _dev(req_pool_idx), _dev(prefix_len),
         _dev(qo_indptr), _dev(shared_len), b, q.shape[0], q.shape[1], k_pool.shape[1], d, scale,
-        _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws, _stream(stream)), "rax_extend_attention")
+        _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws, _stream(stream, q)), "rax_extend_attention")
 
 
 def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max_seq_len: int, o,
@@ -340,7 +343,7 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max
         _dev(q), _dev(k_pool), _dev(v_pool), k_pool.shape[0], _dev(req_to_token), req_to_token.shape[1],
         req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
         q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
-        _stream(stream)), "rax_decode_attention")
+        _stream(stream, q)), "rax_decode_attention")
 
 
 def device_errors(stream=None) -> int:

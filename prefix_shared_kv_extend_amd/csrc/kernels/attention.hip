@@ -981,13 +981,16 @@ struct Shape {
   int bm() const { return 32 * nw * rt; }
 };
 
-// Work shape per call. Extend: 4 waves x two 32-row tiles (every LDS fragment feeds two
-// MFMAs), one tile of loads in flight. Decode: 2 waves x one 32-row tile with two tiles
-// of loads in flight, small enough that two workgroups share a CU (HBM-bound: what
-// matters is bytes in flight per CU).
-static Shape pick_shape(bool decode, rax_dtype dt) {
+// Work shape per call. Extend (bf16, D = 128): 8 waves x one 32-row tile; at under 256
+// VGPRs two such workgroups share a CU, so every SIMD has two waves and one wave's softmax
+// runs under the other's MFMAs. (4 waves x two row tiles reads half the LDS fragments per
+// flop but needs 350 VGPRs, one wave per SIMD, and measured 1.6x slower.) D = 64 has too
+// few 16-byte chunks per key row for 512 loaders and keeps 4 x 2. Decode: 2 waves x one
+// 32-row tile, one tile of loads in flight.
+static Shape pick_shape(bool decode, rax_dtype dt, int d) {
   if (dt != RAX_BF16) return {4, 1, 1};
-  return decode ? Shape{2, 1, 2} : Shape{4, 2, 1};
+  if (decode) return {2, 1, 1};
+  return d == 128 ? Shape{8, 1, 1} : Shape{4, 2, 1};
 }
 
 static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
@@ -1024,10 +1027,14 @@ template <typename T, int D, bool kDecode>
 static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
   rax_status rc = RAX_EINVAL;
   if constexpr (sizeof(T) == 2 && !kDecode) {
-    if (s.nw == 4 && s.rt == 2 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 2, 1>(a, st);
+    if constexpr (D == 128) {
+      if (s.nw == 8 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 8, 1, 1>(a, st);
+    } else {
+      if (s.nw == 4 && s.rt == 2 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 2, 1>(a, st);
+    }
   }
   if constexpr (sizeof(T) == 2 && kDecode) {
-    if (s.nw == 2 && s.rt == 1 && s.pd == 2) rc = launch_one<T, D, kDecode, 2, 1, 2>(a, st);
+    if (s.nw == 2 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 2, 1, 1>(a, st);
   }
   if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 1, 1>(a, st);
   if (rc != RAX_OK) return rc;
@@ -1074,7 +1081,7 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
                                   rax_dtype dt) {
   DecodeLayout l{};
   const int g = h_q / h_kv;
-  const Shape s = pick_shape(true, dt);
+  const Shape s = pick_shape(true, dt, d);
   l.bm = s.bm();
   l.n_rb = (int32_t)((batch * g + l.bm - 1) / l.bm);
   l.nsplit = choose_nsplit((int64_t)l.n_rb * h_kv, max_seq_len);
@@ -1146,7 +1153,7 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   if (!q || !k_ext || !v_ext || !k_pool || !v_pool || !req_to_token || !req_pool_idx || !prefix_len ||
       !qo_indptr || !o)
     return RAX_EINVAL;
-  const Shape s = pick_shape(false, dt);
+  const Shape s = pick_shape(false, dt, d);
   AttnArgs a{};
   a.q = q;
   a.k_ext = k_ext;
@@ -1188,7 +1195,7 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
     return RAX_EINVAL;
   if (batch == 0) return RAX_OK;
   if (!q || !k_pool || !v_pool || !req_to_token || !req_pool_idx || !seq_len || !o) return RAX_EINVAL;
-  const Shape s = pick_shape(true, dt);
+  const Shape s = pick_shape(true, dt, d);
   AttnArgs a{};
   a.q = q;
   a.k_pool = k_pool;
