@@ -86,12 +86,14 @@ struct AttnArgs {
   int32_t* ws_L;              // [n_rb] shared length of each row block (shared_only)
   float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
   int32_t n_chunk;            // most own-part key chunks per (request, KV head)
+  int32_t own_fused;          // own part merges in-workgroup and writes O (own_merge_kernel)
 };
 
-template <typename T, int D, int NW, int RT>
+template <typename T, int D, int NW, int RT, int KS>
 struct Cfg {
   static constexpr int kThreads = 64 * NW;
-  static constexpr int BM = 32 * RT * NW;
+  static constexpr int NWR = NW / KS;                   // waves along rows (KS along keys)
+  static constexpr int BM = 32 * RT * NWR;
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
   static constexpr int CHUNKS = D / EPC;                // chunks per token row
   static constexpr int KSTRIDE = D + EPC;               // K row pad: 16 bytes
@@ -102,9 +104,9 @@ struct Cfg {
   static_assert(KPP > 0 && BN % KPP == 0 && (BN / 2) % KPP == 0, "tile load shape");
 };
 
-template <typename T, int D, int NW, int RT>
+template <typename T, int D, int NW, int RT, int KS>
 struct __align__(16) Smem {
-  using C = Cfg<T, D, NW, RT>;
+  using C = Cfg<T, D, NW, RT, KS>;
   T k[2][BN * C::KSTRIDE];
   T vt[2][D * C::VSTRIDE];
   int32_t slot[4][BN];
@@ -213,15 +215,17 @@ __device__ __forceinline__ uint32_t word(u32x4 v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <typename T, int D, bool kDecode, int NW, int RT, int PD>
+template <typename T, int D, bool kDecode, int NW, int RT, int PD, int KS>
 __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
-  using C = Cfg<T, D, NW, RT>;
+  using C = Cfg<T, D, NW, RT, KS>;
   constexpr int BM = C::BM;
   constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ Smem<T, D, NW, RT> sm;
+  __shared__ Smem<T, D, NW, RT, KS> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int wrow = wave % C::NWR;  // which RT row tiles
+  const int wkey = wave / C::NWR;  // which 32-key half of every tile (KS == 2)
   const int lane = tid & 63;
   const int jrow = lane & 31;  // row within a 32-row tile
   const int half = lane >> 5;  // which half of the key set this lane holds
@@ -327,7 +331,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   int w_rlo = 1 << 30, w_rhi = -1, w_klo = 1 << 30, w_khi = -1, n_bad = 0;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int R = (wave * RT + rt) * 32 + jrow;
+    const int R = (wrow * RT + rt) * 32 + jrow;
     const int64_t Gr = G0 + R;
     t_row[rt] = Gr / a.g;
     row_ok[rt] = t_row[rt] < qb;
@@ -498,9 +502,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
 
     if (run) {
       const bool unmasked = d.kind == 0 && d.cnt == BN && all_rows_ok;
-      // two 32-key online-softmax steps per 64-key tile (keeps S and P small)
+      // two 32-key online-softmax steps per 64-key tile (keeps S and P small); with
+      // KS == 2 each wave takes one of them and the pair is combined at the end
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int si = 0; si < 2 / KS; ++si) {
+        const int sub = KS == 1 ? si : wkey;
         f32x16 s[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) s[rt] = f32x16{};
@@ -618,11 +624,51 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     }
   }
 
+  // ---- key-split pairs: the wave of the second key half hands its (m, l, acc) over LDS
+  // (the tile buffers are free after the loop's last barrier); the first combines them
+  if constexpr (KS == 2) {
+    constexpr int NV = (D / 32) * 16 + 2;
+    static_assert(C::NWR * RT * NV * 64 * sizeof(float) <= sizeof(sm.k), "key-split exchange area");
+    float* xs = reinterpret_cast<float*>(&sm.k[0][0]);
+    if (wkey == 1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int base = (wrow * RT + rt) * NV;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[(base + dt * 16 + r) * 64 + lane] = acc[rt][dt][r];
+        xs[(base + NV - 2) * 64 + lane] = m_run[rt];
+        xs[(base + NV - 1) * 64 + lane] = l_run[rt];
+      }
+    }
+    __syncthreads();
+    if (wkey == 1) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int base = (wrow * RT + rt) * NV;
+      const float m1 = xs[(base + NV - 2) * 64 + lane];
+      const float l1 = xs[(base + NV - 1) * 64 + lane];
+      const float m = fmaxf(m_run[rt], m1);
+      if (m != kNegInf) {
+        const float a0 = __builtin_amdgcn_exp2f(m_run[rt] - m);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+        l_run[rt] = l_run[rt] * a0 + l1 * a1;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[rt][dt][r] = acc[rt][dt][r] * a0 + xs[(base + dt * 16 + r) * 64 + lane] * a1;
+        m_run[rt] = m;
+      }
+    }
+  }
+
   // ---- epilogue: lane holds row jrow of each row tile, dims dt*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (!row_ok[rt]) continue;
-    const int R = (wave * RT + rt) * 32 + jrow;
+    const int R = (wrow * RT + rt) * 32 + jrow;
     const bool partial = a.nsplit > 1 || a.shared_only;
     if (!partial) {
       const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
@@ -769,41 +815,22 @@ __device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, 
 }
 
 // Own part of decode: the keys of one request that its row block does not share (see
-// own_chunks). One wave per (chunk, request, KV head), chunk index slowest so that chunks
-// past every request's own keys are whole workgroups that exit at once. No LDS, no
-// barriers: an HBM-bound gather with wavefront reductions. Lane l holds dims [l*E, l*E+E)
-// (E = D/64) of the G query heads of the KV head. A batch of KB keys: the slot ids are one
-// load per lane, then every K and V row piece of the batch is loaded at once (addresses of
-// keys without a slot are clamped to slot 0 and their values dropped), giving P = KB*G
-// (key, head) partial dot products per lane; wave_reduce_pairs leaves the score of pair l
-// in lane l. Softmax state per head is wave-uniform; P.V takes each key's probability
-// with v_readlane and accumulates in fp32.
+// own_chunks). No LDS in the key loop and no barriers: an HBM-bound gather with wavefront
+// reductions. Lane l holds dims [l*E, l*E+E) (E = D/64) of the G query heads of the KV
+// head. A batch of KB keys: the slot ids are one load per lane, then every K and V row
+// piece of the batch is loaded at once (addresses of keys without a slot are clamped to
+// slot 0 and their values dropped), giving P = KB*G (key, head) partial dot products per
+// lane; wave_reduce_pairs leaves the score of pair l in lane l. Softmax state per head is
+// wave-uniform; P.V takes each key's probability with v_readlane and accumulates in fp32.
+// own_chunk runs one wave over keys [start, stop) of request r, KV head h.
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
+__device__ __forceinline__ void own_chunk(const AttnArgs& a, int r, int h, int row, int start, int stop, int lane,
+                                          float (&acc)[G][D / 64], float (&m_run)[G], float (&l_run)[G]) {
   constexpr int E = D / 64;
   constexpr int KB = 32 / G > 0 ? 32 / G : 1;  // 32 (key, head) pairs per batch
   constexpr int P = KB * G;
   using Raw = piece_t<T, E>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n_rh = (int64_t)a.batch * a.h_kv;
-  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
-  if (w >= n_rh * a.n_chunk) return;
-  const int c = (int)(w / n_rh);
-  const int64_t rh = w % n_rh;
-  const int r = (int)(rh / a.h_kv);
-  const int h = (int)(rh % a.h_kv);
-  int first, per;
-  const int n_act = own_chunks(a, r, first, per);
-  if (c >= n_act) return;  // the merge reads only chunks [0, n_act)
-  const int end = a.kv_len[r];
-  const int row = a.req_pool_idx[r];
-  const int start = first + c * per;
-  const int stop = min(start + per, end);
-  const int64_t item = rh * a.n_chunk + c;
-  float* out_acc = a.ws_own + item * G * (int64_t)D;
-  float* out_ml = a.ws_own + n_rh * a.n_chunk * G * (int64_t)D + item * G * 2;
-
-  float q[G][E], acc[G][E], m_run[G], l_run[G];
+  float q[G][E];
   const T* qp = reinterpret_cast<const T*>(a.q) + ((int64_t)r * a.h_q + (int64_t)h * G) * D + lane * E;
 #pragma unroll
   for (int hl = 0; hl < G; ++hl) {
@@ -882,6 +909,32 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
         for (int e = 0; e < E; ++e) acc[hl][e] += pk * piece_elem<T, E>(vr[kk], e);
       }
   }
+}
+
+// Own part, general form: one wave per (chunk, request, KV head), chunk index slowest so
+// that chunks past every request's own keys are whole workgroups that exit at once;
+// partials go to the workspace and merge_kernel combines them with the shared part's.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
+  constexpr int E = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n_rh = (int64_t)a.batch * a.h_kv;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= n_rh * a.n_chunk) return;
+  const int c = (int)(w / n_rh);
+  const int64_t rh = w % n_rh;
+  const int r = (int)(rh / a.h_kv);
+  const int h = (int)(rh % a.h_kv);
+  int first, per;
+  const int n_act = own_chunks(a, r, first, per);
+  if (c >= n_act) return;  // the merge reads only chunks [0, n_act)
+  const int start = first + c * per;
+  const int stop = min(start + per, (int)a.kv_len[r]);
+  float acc[G][E], m_run[G], l_run[G];
+  own_chunk<T, D, G>(a, r, h, a.req_pool_idx[r], start, stop, lane, acc, m_run, l_run);
+  const int64_t item = rh * a.n_chunk + c;
+  float* out_acc = a.ws_own + item * G * (int64_t)D;
+  float* out_ml = a.ws_own + n_rh * a.n_chunk * G * (int64_t)D + item * G * 2;
 #pragma unroll
   for (int hl = 0; hl < G; ++hl) {
 #pragma unroll
@@ -893,6 +946,121 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
       out_ml[hl * 2] = m_run[hl];
       out_ml[hl * 2 + 1] = l_run[hl];
     }
+}
+
+// Own part with the merge folded in: one workgroup per (request, KV head), wave c runs own
+// chunk c (W = n_chunk waves). The chunk states meet in LDS; after one barrier, wave w
+// merges query heads w, w + W, ... : the shared part's split partials of the head's row
+// (written by the previous kernel) and the W chunk states, by log-sum-exp, then writes O.
+// Dynamic LDS: W*G*D floats of accumulators, then W*G (m, l) pairs.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
+  constexpr int E = D / 64;
+  constexpr int PER = D / 64;
+  extern __shared__ float own_lds[];
+  const int W = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rh = blockIdx.x;
+  const int r = (int)(rh / a.h_kv);
+  const int h = (int)(rh % a.h_kv);
+  float* s_acc = own_lds;
+  float* s_ml = own_lds + (int64_t)W * G * D;
+  {
+    int first, per;
+    const int n_act = own_chunks(a, r, first, per);
+    float acc[G][E], m_run[G], l_run[G];
+    if (wave < n_act) {
+      const int start = first + wave * per;
+      const int stop = min(start + per, (int)a.kv_len[r]);
+      own_chunk<T, D, G>(a, r, h, a.req_pool_idx[r], start, stop, lane, acc, m_run, l_run);
+    } else {
+#pragma unroll
+      for (int hl = 0; hl < G; ++hl) {
+        m_run[hl] = kNegInf;
+        l_run[hl] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[hl][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[(wave * G + hl) * D + lane * E + e] = acc[hl][e];
+      if (lane == 0) {
+        s_ml[(wave * G + hl) * 2] = m_run[hl];
+        s_ml[(wave * G + hl) * 2 + 1] = l_run[hl];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nsplit = a.nsplit;
+  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+  for (int hl = wave; hl < G; hl += W) {
+    const int64_t Grow = (int64_t)r * G + hl;  // MFMA row of (request r, query head h*G + hl)
+    const int64_t rb = Grow / a.bm;
+    const int R = (int)(Grow % a.bm);
+    const int64_t item0 = ((int64_t)h * a.n_rb + rb) * nsplit;
+    const float* sh_acc = a.ws + (item0 * a.bm + R) * (int64_t)D;
+    const int64_t sh_stride = (int64_t)a.bm * D;
+    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + R) * 2;
+    // lane s < nsplit: split partial s; nsplit <= s < nsplit + W: own chunk s - nsplit
+    const int sl = lane < nsplit ? lane : 0;
+    const float2 gml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sl * a.bm * 2);
+    const int oc = lane - nsplit;
+    const bool own_lane = oc >= 0 && oc < W;
+    const float om = own_lane ? s_ml[(oc * G + hl) * 2] : kNegInf;
+    const float ol = own_lane ? s_ml[(oc * G + hl) * 2 + 1] : 0.f;
+    const float my_m = lane < nsplit ? gml.x : om;
+    const float my_l = lane < nsplit ? gml.y : ol;
+    float M = my_l > 0.f ? my_m : kNegInf;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float Mu = M == kNegInf ? 0.f : M;
+    const float my_w = my_l > 0.f ? exp2f(my_m - Mu) : 0.f;
+    float lsum = my_w * my_l;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+    float o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    // split partials with nonzero weight, up to 32 per round trip
+    constexpr int U = 32;
+    uint64_t nz = __ballot(lane < nsplit && my_w != 0.f);
+    const int s_first = nz ? __builtin_ctzll(nz) : 0;
+    while (nz) {
+      float x[U][PER], wt[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int sp = nz ? __builtin_ctzll(nz) : s_first;
+        wt[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), sp));
+        if (!nz) wt[j] = 0.f;
+        nz &= nz - 1;
+        const float* pp = sh_acc + sp * sh_stride;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) x[j][i] = pp[lane + 64 * i];
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += wt[j] * x[j][i];
+    }
+    // own chunks (LDS)
+    for (int c = 0; c < W; ++c) {
+      const float wc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), nsplit + c));
+      if (wc != 0.f) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += wc * s_acc[(c * G + hl) * D + lane + 64 * i];
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t obase = ((int64_t)r * a.h_q + (int64_t)h * G + hl) * (int64_t)D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (a.o_bf16) reinterpret_cast<__bf16*>(a.o)[obase + lane + 64 * i] = (__bf16)(o[i] * inv);
+      else reinterpret_cast<float*>(a.o)[obase + lane + 64 * i] = o[i] * inv;
+    }
+  }
 }
 
 // Log-sum-exp merge of partials: one wave per (MFMA row, KV head). Inputs are the split
@@ -977,20 +1145,22 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ host side
 struct Shape {
-  int nw, rt, pd;
-  int bm() const { return 32 * nw * rt; }
+  int nw, rt, pd, ks;
+  int bm() const { return 32 * (nw / ks) * rt; }
 };
 
 // Work shape per call. Extend (bf16, D = 128): 8 waves x one 32-row tile; at under 256
 // VGPRs two such workgroups share a CU, so every SIMD has two waves and one wave's softmax
 // runs under the other's MFMAs. (4 waves x two row tiles reads half the LDS fragments per
 // flop but needs 350 VGPRs, one wave per SIMD, and measured 1.6x slower.) D = 64 has too
-// few 16-byte chunks per key row for 512 loaders and keeps 4 x 2. Decode: 2 waves x one
-// 32-row tile, one tile of loads in flight.
+// few 16-byte chunks per key row for 512 loaders and keeps 4 x 2. Decode: 4 waves as two
+// 32-row tiles x two 32-key halves of every tile (KS = 2), one tile of loads in flight:
+// the same 64 rows per block as 2 waves x 1 tile, half the MFMA chain per wave and twice
+// the waves per CU; the key halves combine their softmax states in LDS at the end.
 static Shape pick_shape(bool decode, rax_dtype dt, int d) {
-  if (dt != RAX_BF16) return {4, 1, 1};
-  if (decode) return {2, 1, 1};
-  return d == 128 ? Shape{8, 1, 1} : Shape{4, 2, 1};
+  if (dt != RAX_BF16) return {4, 1, 1, 1};
+  if (decode) return {4, 1, 1, 2};
+  return d == 128 ? Shape{8, 1, 1, 1} : Shape{4, 2, 1, 1};
 }
 
 static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
@@ -1009,10 +1179,10 @@ static size_t ws_bytes_for(int64_t items, int bm, int d) {
   return (size_t)items * bm * (size_t)(d + 2) * sizeof(float);
 }
 
-template <typename T, int D, bool kDecode, int NW, int RT, int PD>
+template <typename T, int D, bool kDecode, int NW, int RT, int PD, int KS>
 static rax_status launch_one(AttnArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-  hipLaunchKernelGGL((attn_kernel<T, D, kDecode, NW, RT, PD>), dim3((unsigned)items), dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<T, D, kDecode, NW, RT, PD, KS>), dim3((unsigned)items), dim3(64 * NW), 0, st, a);
   return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
 }
 
@@ -1023,22 +1193,44 @@ static rax_status launch_merge(AttnArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
 }
 
+constexpr int kOwnFusedMaxWaves = 8;
+constexpr size_t kOwnFusedMaxLds = 48 * 1024;
+static size_t own_fused_lds_bytes(int n_chunk, int g, int d) {
+  return (size_t)n_chunk * g * (d + 2) * sizeof(float);
+}
+
 template <typename T, int D, bool kDecode>
 static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
   rax_status rc = RAX_EINVAL;
   if constexpr (sizeof(T) == 2 && !kDecode) {
     if constexpr (D == 128) {
-      if (s.nw == 8 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 8, 1, 1>(a, st);
+      if (s.nw == 8 && s.rt == 1 && s.pd == 1 && s.ks == 1) rc = launch_one<T, D, kDecode, 8, 1, 1, 1>(a, st);
     } else {
-      if (s.nw == 4 && s.rt == 2 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 2, 1>(a, st);
+      if (s.nw == 4 && s.rt == 2 && s.pd == 1 && s.ks == 1) rc = launch_one<T, D, kDecode, 4, 2, 1, 1>(a, st);
     }
   }
   if constexpr (sizeof(T) == 2 && kDecode) {
-    if (s.nw == 2 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 2, 1, 1>(a, st);
+    if (s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 2) rc = launch_one<T, D, kDecode, 4, 1, 1, 2>(a, st);
   }
-  if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1) rc = launch_one<T, D, kDecode, 4, 1, 1>(a, st);
+  if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 1)
+    rc = launch_one<T, D, kDecode, 4, 1, 1, 1>(a, st);
   if (rc != RAX_OK) return rc;
   if constexpr (kDecode) {
+    if (a.shared_only && a.own_fused) {
+      // one workgroup per (request, KV head), n_chunk waves; writes O (no merge kernel)
+      const unsigned blocks = (unsigned)((int64_t)a.batch * a.h_kv);
+      const dim3 block((unsigned)(64 * a.n_chunk));
+      const size_t lds = own_fused_lds_bytes(a.n_chunk, a.g, D);
+      switch (a.g) {
+        case 1: hipLaunchKernelGGL((own_merge_kernel<T, D, 1>), dim3(blocks), block, lds, st, a); break;
+        case 2: hipLaunchKernelGGL((own_merge_kernel<T, D, 2>), dim3(blocks), block, lds, st, a); break;
+        case 4: hipLaunchKernelGGL((own_merge_kernel<T, D, 4>), dim3(blocks), block, lds, st, a); break;
+        case 8: hipLaunchKernelGGL((own_merge_kernel<T, D, 8>), dim3(blocks), block, lds, st, a); break;
+        case 16: hipLaunchKernelGGL((own_merge_kernel<T, D, 16>), dim3(blocks), block, lds, st, a); break;
+        default: return RAX_EINVAL;
+      }
+      return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+    }
     if (a.shared_only) {
       const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
       const unsigned blocks = (unsigned)((own_items + 3) / 4);
@@ -1074,7 +1266,7 @@ static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_
 struct DecodeLayout {
   int64_t sh_acc, sh_ml, L, own_acc, own_ml, total;
   int32_t nsplit, n_rb, n_chunk, bm;
-  bool split_decode;
+  bool split_decode, own_fused;
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
@@ -1100,8 +1292,10 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
   l.n_chunk = (int32_t)std::max<int64_t>(
       1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnMin - 1) / kOwnMin, (kOwnWaves + pairs - 1) / pairs}));
+  // the chunks of one (request, KV head) fit one workgroup: merge in LDS, no own partials
+  l.own_fused = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds;
   const int64_t sh_items = (int64_t)h_kv * l.n_rb * l.nsplit;
-  const int64_t own_rows = batch * h_kv * l.n_chunk * g;
+  const int64_t own_rows = l.own_fused ? 0 : batch * h_kv * l.n_chunk * g;
   l.sh_acc = sh_items * l.bm * d;
   l.sh_ml = sh_items * l.bm * 2;
   l.L = (l.n_rb + 63) / 64 * 64;
@@ -1229,6 +1423,7 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
       a.ws_L = reinterpret_cast<int32_t*>(w + l.sh_acc + l.sh_ml);
       a.ws_own = w + l.sh_acc + l.sh_ml + l.L;
       a.n_chunk = l.n_chunk;
+      a.own_fused = l.own_fused ? 1 : 0;
     }
   }
   return dispatch<true>(a, dt, d, s, (hipStream_t)stream);
