@@ -190,6 +190,29 @@ rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_stride, int
                                   const int32_t* src_indptr, const int32_t* src_slots, int32_t batch,
                                   int64_t total, void* stream);
 
+/* One decode step's bookkeeping and write-back for a batch of running requests, in one
+ * call: the work a scheduler does between two decode attention calls ([notes] App. A.2:
+ * take memory for the batch, evicting LRU leaves when short; [bowen] "insert": keep the
+ * new tokens' KV in the pool).
+ *  1. Host: one new slot per request, exactly as rax_alloc_slots_evict(t, batch, ...)
+ *     (eviction report into out_freed / cap / *out_num_freed); out_slots[i] receives
+ *     request i's slot and seq_len[i] is incremented.
+ *  2. Device, one kernel on `stream`: req_to_token[req_pool_idx[i], seq_len[i] - 1] =
+ *     out_slots[i], seq_len_dev[i] = seq_len[i], and the K/V rows k_new[i], v_new[i]
+ *     ([batch, h_kv, d] of dtype dt) go to the pools at out_slots[i].
+ * seq_len (in/out) and out_slots are host int32 [batch]; req_pool_idx and seq_len_dev are
+ * device int32 [batch]. Slots and lengths travel as kernel arguments, so the host arrays
+ * may be reused as soon as the call returns; device arrays must stay alive until the
+ * stream passes the call. RAX_EINVAL (nothing changed): bad argument, or a length that
+ * would exceed rtt_stride. RAX_ENOMEM: fewer than batch slots even after evicting (the
+ * evicted slots stay free, nothing else changes). A req_pool_idx outside [0, rtt_rows)
+ * is skipped on the device and flagged (RAX_DEVERR_ROW). */
+rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots,
+                             int32_t* out_freed, int64_t cap, int64_t* out_num_freed,
+                             const int32_t* req_pool_idx, int32_t* seq_len_dev, int32_t* req_to_token,
+                             int64_t rtt_stride, int64_t rtt_rows, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt, void* stream);
+
 /* Extend (prefill) attention over radix-cached KV ([hustzhy] §2.3 (2): reuse the matched
  * prefix's KV and compute only the unmatched suffix; [lqhl] "Core method").
  * Request r (r < batch) has prefix_len[r] = m_r cached tokens and q_len_r =

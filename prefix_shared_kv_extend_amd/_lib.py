@@ -55,6 +55,8 @@ _SIGS = {
     "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
     "rax_tree_dump": (_i32, [_vp, _c_i64p, _i64, _c_i64p]),
     "rax_kv_scatter": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "rax_decode_append": (_i32, [_vp, _i32, _c_i32p, _c_i32p, _c_i32p, _i64, _c_i64p, _vp, _vp, _vp, _i64, _i64,
+                                 _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "rax_req_to_token_write": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _vp]),
     "rax_extend_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
                                     _i32, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
@@ -166,6 +168,30 @@ class Tree:
         st = self._L.rax_alloc_slots_evict(self._h, int(n), _p32(out), _p32(self._freed), self.num_slots,
                                            ctypes.byref(nf))
         _check(st, "rax_alloc_slots_evict")
+        return out, self._freed[: nf.value].copy()
+
+    def decode_append(self, seq_len, req_to_token, req_pool_idx, seq_len_dev, k_new, v_new, k_pool, v_pool,
+                      stream=None):
+        """One decode step's slot allocation (evicting LRU leaves when short) and write-back
+        (rax_decode_append). seq_len: host int32 [batch], incremented in place; req_pool_idx,
+        seq_len_dev: device int32 [batch]. Returns (new slots, freed slots)."""
+        n = len(seq_len)
+        _need(isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32 and seq_len.flags.c_contiguous,
+              "seq_len: contiguous host int32 array")
+        _need(k_new.shape == v_new.shape and k_new.shape[0] == n and k_pool.shape == v_pool.shape
+              and k_pool.shape[1:] == k_new.shape[1:], "k_new/v_new [batch, h_kv, d], pools [slots, h_kv, d]")
+        _need(k_new.dtype == v_new.dtype == k_pool.dtype == v_pool.dtype, "dtypes must agree")
+        _need(all(t.is_contiguous() and t.is_cuda for t in (k_new, v_new, k_pool, v_pool)), "contiguous cuda")
+        _cuda_i32(req_to_token, req_pool_idx, seq_len_dev)
+        _need(req_pool_idx.numel() == n and seq_len_dev.numel() == n, "req_pool_idx, seq_len_dev: [batch]")
+        out = np.empty(n, dtype=np.int32)
+        nf = _i64()
+        st = self._L.rax_decode_append(
+            self._h, n, _p32(seq_len), _p32(out), _p32(self._freed), self.num_slots, ctypes.byref(nf),
+            _dev(req_pool_idx), _dev(seq_len_dev), _dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
+            _dev(k_new), _dev(v_new), _dev(k_pool), _dev(v_pool), k_pool.shape[1], k_pool.shape[2],
+            _dtype_code(k_pool), _stream(stream, k_pool))
+        _check(st, "rax_decode_append")
         return out, self._freed[: nf.value].copy()
 
     def free_count(self) -> int:

@@ -10,6 +10,7 @@
 // and writes are coalesced.
 #include "../../../include/rax.h"
 #include "rax_device.h"
+#include "../rax_internal.h"
 
 namespace raxk {
 
@@ -62,11 +63,62 @@ __global__ void __launch_bounds__(256) rtt_write_kernel(int32_t* __restrict__ rt
   }
 }
 
+// Decode step write-back: for request i of the batch, its new slot b.slot[i] goes to
+// req_to_token[req_pool_idx[i]][b.len[i] - 1], b.len[i] to seq_len_dev[i], and the K/V
+// rows of its new token to the pools at that slot. The slots and lengths arrive as kernel
+// arguments (host-computed, already validated).
+__global__ void __launch_bounds__(256) decode_append_kernel(AppendBatch b, const int32_t* __restrict__ req_pool_idx,
+                                                            int32_t* __restrict__ seq_len_dev,
+                                                            int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
+                                                            const uint4* __restrict__ k_new,
+                                                            const uint4* __restrict__ v_new,
+                                                            uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                            int64_t chunks_per_row) {
+  const int64_t total = (int64_t)b.n * chunks_per_row;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(e / chunks_per_row);
+    const int64_t c = e - (int64_t)i * chunks_per_row;
+    const int64_t slot = b.slot[i];
+    k_pool[slot * chunks_per_row + c] = k_new[e];
+    v_pool[slot * chunks_per_row + c] = v_new[e];
+    if (c == 0) {
+      const int64_t row = req_pool_idx[i];
+      const int32_t len = b.len[i];
+      seq_len_dev[i] = len;
+      if (row < 0 || row >= rows) flag_error(RAX_DEVERR_ROW);
+      else rtt[row * stride + len - 1] = (int32_t)slot;
+    }
+  }
+}
+
 static int grid_for(int64_t work, int64_t per_block) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
   if (g > 65536) g = 65536;
   return (int)g;
+}
+
+// Launch of decode_append_kernel in batches of kAppendMax requests (see rax_decode_append).
+rax_status launch_decode_append(int32_t batch, const int32_t* slots, const int32_t* lens,
+                                const int32_t* req_pool_idx, int32_t* seq_len_dev, int32_t* rtt, int64_t stride,
+                                int64_t rows, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                int64_t chunks_per_row, hipStream_t st) {
+  for (int32_t b0 = 0; b0 < batch; b0 += kAppendMax) {
+    AppendBatch b;
+    b.n = batch - b0 < kAppendMax ? batch - b0 : kAppendMax;
+    for (int i = 0; i < b.n; ++i) {
+      b.slot[i] = slots[b0 + i];
+      b.len[i] = lens[b0 + i];
+    }
+    const int64_t off = (int64_t)b0 * chunks_per_row;
+    hipLaunchKernelGGL(decode_append_kernel, dim3(grid_for(b.n * chunks_per_row, 256)), dim3(256), 0, st, b,
+                       req_pool_idx + b0, seq_len_dev + b0, rtt, stride, rows,
+                       reinterpret_cast<const uint4*>(k_new) + off, reinterpret_cast<const uint4*>(v_new) + off,
+                       reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool), chunks_per_row);
+    if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+  }
+  return RAX_OK;
 }
 
 }  // namespace raxk

@@ -4,6 +4,7 @@
 
 #include "../../include/rax.h"
 #include "radix_tree.h"
+#include "rax_internal.h"
 
 struct rax_tree {
   explicit rax_tree(int64_t n) : t(n) {}
@@ -225,6 +226,35 @@ rax_status rax_alloc_slots_evict(rax_tree* t, int64_t n, int32_t* out_slots, int
   const int64_t short_by = n - r.alloc().num_free();
   if (short_by > 0) *out_num_freed = r.evict(short_by, out_freed, cap);
   return r.alloc().alloc(n, out_slots) ? RAX_OK : RAX_ENOMEM;
+  RAX_GUARD_END
+}
+
+rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots, int32_t* out_freed,
+                             int64_t cap, int64_t* out_num_freed, const int32_t* req_pool_idx, int32_t* seq_len_dev,
+                             int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt,
+                             void* stream) {
+  if (!t || batch < 0 || cap < 0 || !out_num_freed || (cap > 0 && !out_freed) || rtt_stride < 1 || rtt_rows < 1 ||
+      h_kv < 1 || d < 1 || (dt != RAX_F32 && dt != RAX_BF16))
+    return RAX_EINVAL;
+  *out_num_freed = 0;
+  if (batch == 0) return RAX_OK;
+  if (!seq_len || !out_slots || !req_pool_idx || !seq_len_dev || !req_to_token || !k_new || !v_new || !k_pool ||
+      !v_pool)
+    return RAX_EINVAL;
+  const int64_t row_bytes = (int64_t)h_kv * d * (dt == RAX_F32 ? 4 : 2);
+  const uintptr_t mis = (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool;
+  if (row_bytes % 16 || (mis & 15)) return RAX_EINVAL;
+  for (int32_t i = 0; i < batch; ++i)
+    if (seq_len[i] < 0 || (int64_t)seq_len[i] + 1 > rtt_stride) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  rax::RadixTree& r = t->t;
+  const int64_t short_by = batch - r.alloc().num_free();
+  if (short_by > 0) *out_num_freed = r.evict(short_by, out_freed, cap);
+  if (!r.alloc().alloc(batch, out_slots)) return RAX_ENOMEM;
+  for (int32_t i = 0; i < batch; ++i) seq_len[i] += 1;
+  return raxk::launch_decode_append(batch, out_slots, seq_len, req_pool_idx, seq_len_dev, req_to_token, rtt_stride,
+                                    rtt_rows, k_new, v_new, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
   RAX_GUARD_END
 }
 

@@ -219,43 +219,45 @@ class RadixRuntime:
                 self.len_of[r] = int(lens[i])
 
     def begin_decode(self, rids) -> DecodeBatch:
+        """Describe the next decode step of `rids` (one new token each): db.seq_len holds the
+        lengths after the step, so token i of the batch sits at position db.seq_len[i] - 1.
+        Nothing changes until run_decode."""
         key = tuple(rids)
         if self._dec_cache is None or self._dec_cache[0] != key:
             self._sync_decode_lengths()
             req_rows = np.array([self.row_of[r] for r in rids], dtype=np.int32)
             nodes = [self.node_of[r] for r in rids]
             inv = self._upload(dict(req_pool_idx=req_rows, shared_len=self.tree.lca_depths(nodes),
-                                    rtt_indptr=np.arange(len(rids) + 1)))
+                                    seq_len=np.zeros(len(rids))))
             lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
             self._dec_cache = (key, req_rows, inv, lens)
         _, req_rows, inv, lens = self._dec_cache
-        new, freed = self.tree.alloc_slots_evict(len(rids))
+        seq_len = lens + 1
+        max_seq = int(seq_len.max()) if len(seq_len) else 0
+        if max_seq > self.max_ctx:
+            raise ValueError("sequence longer than the req_to_token rows")
+        db = DecodeBatch(list(rids), seq_len, max_seq)
+        db.dev = inv
+        return db
+
+    def run_decode(self, db: DecodeBatch, q, k_new, v_new, o) -> None:
+        """Allocate the new tokens' slots, append them to the rows, write their K/V into the
+        pools (one native call, one kernel), then run decode attention."""
+        key, req_rows, inv, lens = self._dec_cache
+        if key != tuple(db.rids):
+            raise ValueError("run_decode: batch differs from the last begin_decode")
+        new, freed = self.tree.decode_append(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], k_new, v_new,
+                                             self.k_pool, self.v_pool)
         if self.log is not None:
             if len(freed):
                 self._log("evict", self.step, tuple(freed.tolist()))
             self._log("alloc", self.step, tuple(new.tolist()))
-        lens += 1                      # lengths live in the cache while the batch is unchanged
-        max_seq = int(lens.max())
-        if max_seq > self.max_ctx:
-            lens -= 1
-            raise ValueError("sequence longer than the req_to_token rows")
         self.rows[req_rows, lens - 1] = new
-        seq_len = lens.copy()
-        db = DecodeBatch(list(rids), seq_len, max_seq)
-        var = self._upload(dict(seq_len=seq_len, out_loc=new, rtt_start=seq_len - 1))
-        db.dev = dict(inv)
-        db.dev.update(var)
-        L.req_to_token_write(self.rtt, db.dev["req_pool_idx"], db.dev["rtt_start"], db.dev["rtt_indptr"],
-                             db.dev["out_loc"], len(rids))
-        return db
-
-    def run_decode(self, db: DecodeBatch, q, k_new, v_new, o) -> None:
-        L.kv_scatter(k_new, v_new, db.dev["out_loc"], self.k_pool, self.v_pool)
         ws = self._workspace(L.attention_workspace_bytes(True, len(db.rids), self.h_q, self.h_kv, self.d,
                                                          db.max_seq_len))
         ev = self._event_pair("decode")
-        L.decode_attention(q, self.k_pool, self.v_pool, self.rtt, db.dev["req_pool_idx"], db.dev["seq_len"],
-                           db.max_seq_len, o, workspace=ws, shared_len=db.dev["shared_len"])
+        L.decode_attention(q, self.k_pool, self.v_pool, self.rtt, inv["req_pool_idx"], inv["seq_len"],
+                           db.max_seq_len, o, workspace=ws, shared_len=inv["shared_len"])
         if ev:
             ev[1].record()
 
