@@ -35,6 +35,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_READ_BYTES = 2 * (1 << 15) * 64 * 128 * 2 + (1 << 15) * 4   # --copy-calib: K, V and slot list read
+COPY_WRITE_BYTES = 2 * (1 << 15) * 64 * 128 * 2                    # K and V written
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "prefix_shared_kv_extend_amd", "csrc", "kernels", "attention.hip")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "attn tokens/s (extend, decode) + % MFMA/HBM peak on radix-cached KV"
 
@@ -46,7 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--traffic", default=TRAFFIC_JSON, help="counter summary with HBM bytes per launch")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="condense rocprofv3 counter runs in DIR into profiles/traffic.json and exit")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain copy kernel of known size (for counter scaling) and exit")
     return ap.parse_args()
@@ -145,6 +151,68 @@ def run_step(runner, prep, timers=None):
     rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next step starts empty
 
 
+def _sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _counter_means(csv_path, counter):
+    """Mean per dispatch of one counter, per kernel name, from a rocprofv3 counter CSV."""
+    import csv
+    acc = {}
+    with open(csv_path) as f:
+        for x in csv.DictReader(f):
+            if x["Counter_Name"] == counter:
+                acc.setdefault(x["Kernel_Name"], []).append(float(x["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+# kernels that make up one launch of each attention entry point (substrings of their names)
+ENTRY_KERNELS = {"decode": ("attn_kernelIDF16bLi128ELb1E", "own_merge_kernelIDF16bLi128E"),
+                 "extend": ("attn_kernelIDF16bLi128ELb0E",)}
+
+
+def write_traffic(run_dir):
+    """Condense rocprofv3 FETCH_SIZE / WRITE_SIZE runs (of this script, and of --copy-calib)
+    into profiles/traffic.json: HBM bytes per launch of each attention entry point, each
+    counter scaled by what it reads for the plain copy of known size."""
+    fetch = _counter_means(os.path.join(run_dir, "pmc_FETCH_SIZE", "bench_counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(run_dir, "pmc_WRITE_SIZE", "bench_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter_means(os.path.join(run_dir, "copy_FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter_means(os.path.join(run_dir, "copy_WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
+    copy_f = next(v for k, v in cf.items() if "kv_scatter_kernel" in k)
+    copy_w = next(v for k, v in cw.items() if "kv_scatter_kernel" in k)
+    f_scale = COPY_READ_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_WRITE_BYTES / (copy_w * 1024.0)
+    out = {"source_sha256": _sha256(KERNEL_SOURCE), "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "entries": {}}
+    for entry, keys in ENTRY_KERNELS.items():
+        per = {}
+        for key in keys:
+            kf = [v for k, v in fetch.items() if key in k]
+            kw = [v for k, v in write.items() if key in k]
+            if kf and kw:
+                per[key] = {"fetch_kib": kf[0], "write_kib": kw[0],
+                            "bytes": kf[0] * 1024 * f_scale + kw[0] * 1024 * w_scale}
+        out["entries"][entry] = {"kernels": per, "bytes_per_launch": sum(p["bytes"] for p in per.values())}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic(entry, path):
+    """HBM bytes per launch of `entry` from the committed counter summary, or None when there
+    is none or the kernel source changed since the counters were taken."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != _sha256(KERNEL_SOURCE):
+        return None
+    return t.get("entries", {}).get(entry, {}).get("bytes_per_launch")
+
+
 def cpu_baseline(job, seconds):
     """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
     import torch
@@ -171,6 +239,9 @@ def cpu_baseline(job, seconds):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the path would shard by KV heads or by requests, with no exchange inside attention)",
@@ -186,17 +257,18 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.copy_calib:
-        # plain copy through kv_scatter with identity slots: reads and writes 2 x 512 MiB
+        # plain copy through kv_scatter with identity slots: reads (distinct K and V) and
+        # writes 2 x 512 MiB, plus the 128 KiB slot list
         n = 1 << 15
         k = torch.ones((n, 64, 128), dtype=torch.bfloat16, device=dev)
+        v = torch.ones_like(k)
         kp = torch.empty_like(k)
         vp = torch.empty_like(k)
         loc = torch.arange(n, dtype=torch.int32, device=dev)
         for _ in range(3):
-            _lib.kv_scatter(k, k, loc, kp, vp)
+            _lib.kv_scatter(k, v, loc, kp, vp)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calib_bytes_read": 2 * k.numel() * 2 + n * 4, "copy_calib_bytes_written":
-                          2 * k.numel() * 2}))
+        print(json.dumps({"copy_calib_bytes_read": COPY_READ_BYTES, "copy_calib_bytes_written": COPY_WRITE_BYTES}))
         return
 
     job = configs.make(1)
@@ -243,10 +315,7 @@ def main():
         roof = {"kernel": "decode attention (shared-prefix attn_kernel + own_merge_kernel)", "bound": "hbm",
                 "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                 "launches_per_step": len(dec_bytes), "avg_launch_us": sum(dec_us) / len(dec_us)}
-    roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            roof["traffic"] = json.load(f).get("bytes_per_launch")
+    roof["traffic"] = load_traffic("extend" if roof["bound"] == "mfma" else "decode", args.traffic)
 
     out = {
         "metric": METRIC,

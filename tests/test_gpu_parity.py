@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the oracle.
 
-* kv_scatter and the req_to_token fill are checked bit for bit.
+* kv_scatter, the req_to_token fill and the decode append are checked bit for bit.
 * Whole traces run through RadixRuntime on the GPU; their host event logs
   (matches, evictions, allocations, inserts), final slot rows and tree dumps
   must equal the oracle's replay exactly, and attention outputs must agree with
@@ -134,6 +134,52 @@ def test_req_to_token_write_bit_exact():
         want[rows[r], start[r]: start[r] + lens[r]] = src[indptr[r]: indptr[r + 1]]
     assert np.array_equal(rtt.cpu().numpy(), want)
     assert _lib.device_errors() == 0
+
+
+def test_decode_append_bit_exact_and_errors():
+    """rax_decode_append: slots lowest-free-first, rows appended, lengths on both sides,
+    K/V rows in the pools; 300 requests (more than one kernel-argument batch of 256);
+    rejected calls change nothing."""
+    from prefix_shared_kv_extend_amd import _lib
+    say("decode_append: 300 requests into a 600-slot pool, then ENOMEM and EINVAL")
+    S, R, W, h, d, n = 600, 320, 40, 4, 64, 300
+    t = _lib.Tree(S)
+    t.alloc_slots(300)                                   # slots 0..299 taken: the new ones are 300..599
+    g = torch.Generator().manual_seed(7)
+    rows_np = torch.randperm(R, generator=g)[:n].numpy().astype(np.int32)
+    lens = torch.randint(0, W - 1, (n,), generator=g).numpy().astype(np.int32)
+    k = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    kp = torch.zeros((S, h, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    rtt = torch.full((R, W), -5, dtype=torch.int32, device="cuda")
+    rows = torch.tensor(rows_np, device="cuda")
+    sl_dev = torch.zeros(n, dtype=torch.int32, device="cuda")
+    seq = lens.copy()
+    new, freed = t.decode_append(seq, rtt, rows, sl_dev, k, v, kp, vp)
+    torch.cuda.synchronize()
+    assert np.array_equal(new, np.arange(300, 600, dtype=np.int32)) and len(freed) == 0
+    assert np.array_equal(seq, lens + 1) and np.array_equal(sl_dev.cpu().numpy(), lens + 1)
+    want = np.full((R, W), -5, dtype=np.int32)
+    want[rows_np, lens] = new
+    assert np.array_equal(rtt.cpu().numpy(), want)
+    kc, vc = kp.cpu(), vp.cpu()
+    assert torch.equal(kc[300:], k.cpu()) and torch.equal(vc[300:], v.cpu())
+    assert int(kc[:300].abs().sum()) == 0 and int(vc[:300].abs().sum()) == 0
+    assert _lib.device_errors() == 0
+    # no free slot and nothing evictable: ENOMEM, lengths untouched
+    before = seq.copy()
+    with pytest.raises(_lib.RaxError) as e:
+        t.decode_append(seq[:1].copy(), rtt, rows[:1], sl_dev[:1], k[:1], v[:1], kp, vp)
+    assert e.value.status == _lib.ENOMEM and np.array_equal(seq, before)
+    # a row already at full width: EINVAL before any slot is taken
+    t.free_slots([0])
+    full = np.array([W], dtype=np.int32)
+    with pytest.raises(_lib.RaxError) as e:
+        t.decode_append(full, rtt, rows[:1], sl_dev[:1], k[:1], v[:1], kp, vp)
+    assert e.value.status == _lib.EINVAL and full[0] == W and t.free_count() == 1
+    torch.cuda.synchronize()
+    assert np.array_equal(rtt.cpu().numpy(), want)
 
 
 # ------------------------------------------------------------- whole small traces
