@@ -163,6 +163,30 @@ rax_status rax_lock_ref_batch(rax_tree* t, const rax_node* nodes, int32_t n, int
  * shared_len hint of consecutive requests for the attention kernels. */
 rax_status rax_lca_depths(const rax_tree* t, const rax_node* nodes, int32_t n, int32_t* out);
 
+/* out_len[r] = length of the longest cached prefix of request r's tokens
+ * tokens[indptr[r] .. indptr[r+1]), for r < batch. Read-only: nothing splits, no clock
+ * tick (a scheduler's look at the cache, not a match). */
+rax_status rax_prefix_len_batch(const rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                                int64_t* out_len);
+
+/* Cache-aware scheduling ([notes] §3 and App. A.2; [lqhl] "Cache-aware scheduling"): the
+ * order in which waiting requests should be admitted. out_order receives a permutation of
+ * [0, batch) (request indices in arrival order); out_len the read-only prefix lengths as
+ * rax_prefix_len_batch. Policies:
+ *   RAX_SCHED_FCFS    arrival order;
+ *   RAX_SCHED_LPM     longest cached prefix first (ties: arrival order) -- the pages' policy;
+ *   RAX_SCHED_DFS     token sequences in lexicographic order (ties: arrival order): a
+ *                     depth-first order of the requests' own radix tree, the offline
+ *                     optimum of Theorem 3.1;
+ *   RAX_SCHED_RANDOM  a uniform shuffle (Fisher-Yates with SplitMix64 draws from `seed`:
+ *                     for i = batch-1 .. 1, j = next() % (i+1), swap). */
+#define RAX_SCHED_FCFS 0
+#define RAX_SCHED_LPM 1
+#define RAX_SCHED_DFS 2
+#define RAX_SCHED_RANDOM 3
+rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* tokens, const int64_t* indptr,
+                              int32_t batch, uint64_t seed, int32_t* out_order, int64_t* out_len);
+
 rax_status rax_tree_stats(const rax_tree* t, rax_stats* out);
 
 /* Serialise the tree in preorder (children by ascending first token), as int64 words:

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "librax.so")
 OK, EINVAL, ENOMEM, ESTATE, EDEVICE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 DEVERR_SLOT, DEVERR_ROW = 1, 2
+SCHED_FCFS, SCHED_LPM, SCHED_DFS, SCHED_RANDOM = 0, 1, 2, 3
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -52,6 +53,8 @@ _SIGS = {
     "rax_insert_batch": (_i32, [_vp, _c_i32p, _c_i32p, _c_i64p, _i32, _c_i32p, _c_i64p, _c_i64p, _c_i32p]),
     "rax_lock_ref_batch": (_i32, [_vp, _c_i64p, _i32, _i32]),
     "rax_lca_depths": (_i32, [_vp, _c_i64p, _i32, _c_i32p]),
+    "rax_prefix_len_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p]),
+    "rax_schedule_order": (_i32, [_vp, _i32, _c_i32p, _c_i64p, _i32, ctypes.c_uint64, _c_i32p, _c_i64p]),
     "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
     "rax_tree_dump": (_i32, [_vp, _c_i64p, _i64, _c_i64p]),
     "rax_kv_scatter": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
@@ -216,6 +219,28 @@ class Tree:
                                               int(lock), _p32(out), m.ctypes.data_as(_c_i64p),
                                               nodes.ctypes.data_as(_c_i64p)), "rax_match_prefix_batch")
         return out[: len(t)], m, nodes
+
+    def prefix_len_batch(self, tokens_flat, indptr) -> np.ndarray:
+        """Read-only longest cached prefix of each request (no split, no clock tick)."""
+        t = _i32arr(tokens_flat)
+        ip = np.ascontiguousarray(indptr, dtype=np.int64)
+        out = np.empty(len(ip) - 1, dtype=np.int64)
+        _check(self._L.rax_prefix_len_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), len(ip) - 1,
+                                            out.ctypes.data_as(_c_i64p)), "rax_prefix_len_batch")
+        return out
+
+    def schedule_order(self, policy: int, tokens_flat, indptr, seed: int = 0):
+        """Admission order of waiting requests under a SCHED_* policy (rax_schedule_order).
+        Returns (order[batch] of request indices, cached prefix length[batch])."""
+        t = _i32arr(tokens_flat)
+        ip = np.ascontiguousarray(indptr, dtype=np.int64)
+        b = len(ip) - 1
+        order = np.empty(b, dtype=np.int32)
+        m = np.empty(b, dtype=np.int64)
+        _check(self._L.rax_schedule_order(self._h, int(policy), _p32(t), ip.ctypes.data_as(_c_i64p), b,
+                                          int(seed) & (2 ** 64 - 1), _p32(order), m.ctypes.data_as(_c_i64p)),
+               "rax_schedule_order")
+        return order, m
 
     def insert_batch(self, tokens_flat, slots_flat, indptr):
         """Batched insert. Returns (tree_slots_flat, existing[batch], node[batch])."""

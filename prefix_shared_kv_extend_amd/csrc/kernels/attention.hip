@@ -83,7 +83,6 @@ struct AttnArgs {
   int32_t bm;                 // MFMA rows per block
   // decode split into a shared part (this kernel) and an own part (own_kernel)
   int32_t shared_only;        // 1: only the keys a block's requests share; always write partials
-  int32_t* ws_L;              // [n_rb] shared length of each row block (shared_only)
   float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
   int32_t n_chunk;            // most own-part key chunks per (request, KV head)
   int32_t own_fused;          // own part merges in-workgroup and writes O (own_merge_kernel)
@@ -241,27 +240,56 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   int64_t qb = qa + BM / a.g;   // one past the last query row
   if (qb > a.total_q) qb = a.total_q;
 
-  // ---- block metadata (requests covered, shared length, tile list)
-  if (tid == 0) {
-    int r0, r1;
-    if (!kDecode) {
-      r0 = upper_req(a.qo_indptr, a.batch, qa);
-      r1 = upper_req(a.qo_indptr, a.batch, qb - 1);
-    } else {
-      r0 = (int)qa;
-      r1 = (int)(qb - 1);
+  // ---- this lane's rows (RT row tiles) and their Q fragments (B operand of S^T = K Q^T:
+  // row jrow, dims [ks*K + half*K/2, +K/2)). They depend on the block index alone, so the
+  // Q loads go out first (rows past the block's end read row qa and are zeroed).
+  bool row_ok[RT];
+  int64_t t_row[RT];
+  int hq[RT];
+  constexpr int KSTEP = kBf16 ? 16 : 2;
+  constexpr int NKS = D / KSTEP;
+  typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
+  QFrag qf[RT][NKS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int R = (wrow * RT + rt) * 32 + jrow;
+    const int64_t Gr = G0 + R;
+    t_row[rt] = Gr / a.g;
+    row_ok[rt] = t_row[rt] < qb;
+    hq[rt] = h * a.g + (int)(Gr % a.g);
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((row_ok[rt] ? t_row[rt] : qa) * a.h_q + hq[rt]) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (kBf16) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+        qf[rt][ks] = row_ok[rt] ? v : bf16x8{};
+      } else {
+        const float v = qp[ks * 2 + half];
+        qf[rt][ks] = row_ok[rt] ? v : 0.f;
+      }
     }
-    int nreq = r1 - r0 + 1;
-    if (nreq > BM) {  // only possible with empty requests in between
-      flag_error(RAX_DEVERR_ROW);
-      nreq = BM;
-    }
-    sm.hdr[0] = r0;
-    sm.hdr[1] = nreq;
   }
-  __syncthreads();
-  const int r0 = uni(sm.hdr[0]);
-  const int nreq = uni(sm.hdr[1]);
+
+  // ---- block metadata (requests covered, shared length, tile list)
+  int r0, nreq;
+  if constexpr (kDecode) {  // one request per query row
+    r0 = (int)qa;
+    nreq = (int)(qb - qa);
+  } else {
+    if (tid == 0) {
+      const int ra = upper_req(a.qo_indptr, a.batch, qa);
+      int n = upper_req(a.qo_indptr, a.batch, qb - 1) - ra + 1;
+      if (n > BM) {  // only possible with empty requests in between
+        flag_error(RAX_DEVERR_ROW);
+        n = BM;
+      }
+      sm.hdr[0] = ra;
+      sm.hdr[1] = n;
+    }
+    __syncthreads();
+    r0 = uni(sm.hdr[0]);
+    nreq = uni(sm.hdr[1]);
+  }
   for (int i = tid; i < nreq; i += C::kThreads) {
     const int r = r0 + i;
     int row = a.req_pool_idx[r];
@@ -300,10 +328,8 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
       if (i < nreq) sm.own[i] = carry + incl - cnt;
       carry += __shfl(incl, 63);
     }
-    if (a.shared_only) {
+    if (a.shared_only)
       for (int i = lane; i < nreq; i += 64) sm.own[i] = 0;
-      if (lane == 0 && h == 0 && split == 0) a.ws_L[rb] = L;
-    }
     if (lane == 0) {
       sm.own[nreq] = carry;
       const int n_sh = (L + BN - 1) / BN;
@@ -324,18 +350,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   const int t_end = uni(sm.hdr[6]);
   const int suf0 = uni(sm.req_qo[0]);
 
-  // ---- this lane's rows (RT row tiles)
-  bool row_ok[RT];
-  int64_t t_row[RT];
-  int hq[RT], my_req[RT], my_qo[RT];
+  // ---- the request of each of this lane's rows
+  int my_req[RT], my_qo[RT];
   int w_rlo = 1 << 30, w_rhi = -1, w_klo = 1 << 30, w_khi = -1, n_bad = 0;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int R = (wrow * RT + rt) * 32 + jrow;
-    const int64_t Gr = G0 + R;
-    t_row[rt] = Gr / a.g;
-    row_ok[rt] = t_row[rt] < qb;
-    hq[rt] = h * a.g + (int)(Gr % a.g);
     int req = 0;
     if (row_ok[rt]) {
       int lo = 0, hi = nreq - 1;
@@ -369,25 +388,6 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   w_khi = uni(w_khi);
   const bool wave_active = w_rhi >= 0;
   const bool all_rows_ok = uni(n_bad) == 0;
-
-  // ---- Q fragments (B operand of S^T = K Q^T): row jrow, dims [ks*K + half*K/2, +K/2)
-  constexpr int KSTEP = kBf16 ? 16 : 2;
-  constexpr int NKS = D / KSTEP;
-  typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
-  QFrag qf[RT][NKS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const T* qp = reinterpret_cast<const T*>(a.q) + (t_row[rt] * a.h_q + hq[rt]) * (int64_t)D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (kBf16) {
-        if (row_ok[rt]) qf[rt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
-        else qf[rt][ks] = bf16x8{};
-      } else {
-        qf[rt][ks] = row_ok[rt] ? qp[ks * 2 + half] : 0.f;
-      }
-    }
-  }
 
   f32x16 acc[RT][D / 32];
   float m_run[RT], l_run[RT];
@@ -462,14 +462,17 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   auto desc = [&](int tau) { return describe(tau, sm, L, n_sh, n_own, suf0, qb, nreq); };
 
   // ---- prologue: slot ids of tiles t_begin .. t_begin+PD, K/V loads of the first PD tiles
-  if (tid < BN) {
+  if (tid < BN && t_begin < t_end) {  // all prologue slot loads in one round trip
+    TileDesc di[PD + 1];
+    int raw[PD + 1];
 #pragma unroll
     for (int i = 0; i <= PD; ++i) {
-      if (t_begin + i < t_end) {
-        const TileDesc di = desc(t_begin + i);
-        sm.slot[(t_begin + i) % NSB][tid] = slot_finish(a, di, tid, slot_issue(a, di, tid));
-      }
+      di[i] = desc(min(t_begin + i, t_end - 1));
+      raw[i] = slot_issue(a, di[i], tid);
     }
+#pragma unroll
+    for (int i = 0; i <= PD; ++i)
+      if (t_begin + i < t_end) sm.slot[(t_begin + i) % NSB][tid] = slot_finish(a, di[i], tid, raw[i]);
   }
   __syncthreads();
   if (t_begin < t_end) {
@@ -795,13 +798,34 @@ __device__ __forceinline__ float piece_elem(piece_t<T, E> r, int e) {
   else return __builtin_bit_cast(float, (uint32_t)(r >> (32 * e)));
 }
 
-// Own keys of request r in split decode: positions [L, seq_len) with L the shared length of
-// the request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
-// at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets the
-// first own position and the chunk size.
+// Shared length L of decode row block rb, by the rule the shared-part kernel applies: the
+// minimum over the block's requests of their key counts (0 for a request whose row or
+// length is invalid) and of the shared_len hints between neighbours (the block's first
+// request has none). One lane per request (a block holds at most 64); wave-uniform result.
+__device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, int lane) {
+  const int64_t qa = rb * a.bm / a.g;
+  int64_t qb = qa + a.bm / a.g;
+  if (qb > a.batch) qb = a.batch;
+  int v = 1 << 30;
+  const int64_t r = qa + lane;
+  if (r < qb) {
+    const int row = a.req_pool_idx[r];
+    int m = a.kv_len[r];
+    if (row < 0 || row >= a.rtt_rows || m < 0 || m > a.rtt_stride) m = 0;
+    const int sh = lane == 0 ? (1 << 30) : (a.shared_len ? a.shared_len[r] : 0);
+    v = min(m, sh);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  return uni(max(v, 0));
+}
+
+// Own keys of request r in split decode: positions [L, seq_len), L the shared length of the
+// request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
+// at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets
+// the first own position and the chunk size.
 constexpr int kOwnMin = 32;
-__device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, int& per) {
-  const int L = a.ws_L[((int64_t)r * a.g) / a.bm];
+__device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int L, int& first, int& per) {
   const int end = a.kv_len[r];
   const int row = a.req_pool_idx[r];
   first = L;
@@ -823,24 +847,31 @@ __device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int& first, 
 // lane; wave_reduce_pairs leaves the score of pair l in lane l. Softmax state per head is
 // wave-uniform; P.V takes each key's probability with v_readlane and accumulates in fp32.
 // own_chunk runs one wave over keys [start, stop) of request r, KV head h.
+// This lane's dims of the G query heads of (request r, KV head h), in fp32.
 template <typename T, int D, int G>
-__device__ __forceinline__ void own_chunk(const AttnArgs& a, int r, int h, int row, int start, int stop, int lane,
-                                          float (&acc)[G][D / 64], float (&m_run)[G], float (&l_run)[G]) {
+__device__ __forceinline__ void load_q_heads(const AttnArgs& a, int r, int h, int lane, float (&q)[G][D / 64]) {
+  constexpr int E = D / 64;
+  const T* qp = reinterpret_cast<const T*>(a.q) + ((int64_t)r * a.h_q + (int64_t)h * G) * D + lane * E;
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl)
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[hl][e] = (float)qp[hl * D + e];
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void own_chunk(const AttnArgs& a, int h, int row, int start, int stop, int lane,
+                                          const float (&q)[G][D / 64], float (&acc)[G][D / 64], float (&m_run)[G],
+                                          float (&l_run)[G]) {
   constexpr int E = D / 64;
   constexpr int KB = 32 / G > 0 ? 32 / G : 1;  // 32 (key, head) pairs per batch
   constexpr int P = KB * G;
   using Raw = piece_t<T, E>;
-  float q[G][E];
-  const T* qp = reinterpret_cast<const T*>(a.q) + ((int64_t)r * a.h_q + (int64_t)h * G) * D + lane * E;
 #pragma unroll
   for (int hl = 0; hl < G; ++hl) {
     m_run[hl] = kNegInf;
     l_run[hl] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      q[hl][e] = (float)qp[hl * D + e];
-      acc[hl][e] = 0.f;
-    }
+    for (int e = 0; e < E; ++e) acc[hl][e] = 0.f;
   }
   const int64_t row_elems = (int64_t)a.h_kv * D;
   const T* kb = reinterpret_cast<const T*>(a.k_pool) + (int64_t)h * D + lane * E;
@@ -925,13 +956,16 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
   const int64_t rh = w % n_rh;
   const int r = (int)(rh / a.h_kv);
   const int h = (int)(rh % a.h_kv);
+  float q[G][E];
+  load_q_heads<T, D, G>(a, r, h, lane, q);  // issued first: it depends on nothing else
   int first, per;
-  const int n_act = own_chunks(a, r, first, per);
+  const int L = block_shared_len(a, ((int64_t)r * G) / a.bm, lane);
+  const int n_act = own_chunks(a, r, L, first, per);
   if (c >= n_act) return;  // the merge reads only chunks [0, n_act)
   const int start = first + c * per;
   const int stop = min(start + per, (int)a.kv_len[r]);
   float acc[G][E], m_run[G], l_run[G];
-  own_chunk<T, D, G>(a, r, h, a.req_pool_idx[r], start, stop, lane, acc, m_run, l_run);
+  own_chunk<T, D, G>(a, h, a.req_pool_idx[r], start, stop, lane, q, acc, m_run, l_run);
   const int64_t item = rh * a.n_chunk + c;
   float* out_acc = a.ws_own + item * G * (int64_t)D;
   float* out_ml = a.ws_own + n_rh * a.n_chunk * G * (int64_t)D + item * G * 2;
@@ -965,14 +999,39 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
   const int h = (int)(rh % a.h_kv);
   float* s_acc = own_lds;
   float* s_ml = own_lds + (int64_t)W * G * D;
+  const int nsplit = a.nsplit;
+  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+  // the split partials' (m, l) of this wave's first merged head, fetched now so that the
+  // load overlaps the own-key work (they come from the previous kernel)
+  // the Q heads and, for this wave's first merged head, the split partials' (m, l) and the
+  // accumulator rows of the first kPre splits: all fetched now, so the loads overlap the
+  // own-key work (the partials come from the previous kernel)
+  constexpr int kPre = 8;
+  float q[G][E];
+  load_q_heads<T, D, G>(a, r, h, lane, q);
+  float2 pre_ml = make_float2(kNegInf, 0.f);
+  float pre_acc[kPre][PER];
+  if (wave < G) {
+    const int64_t Grow = (int64_t)r * G + wave;
+    const int64_t item0 = ((int64_t)h * a.n_rb + Grow / a.bm) * nsplit;
+    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Grow % a.bm) * 2;
+    pre_ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)(lane < nsplit ? lane : 0) * a.bm * 2);
+    const float* sh_acc = a.ws + (item0 * a.bm + Grow % a.bm) * (int64_t)D;
+#pragma unroll
+    for (int j = 0; j < kPre; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        pre_acc[j][i] = sh_acc[(int64_t)(j < nsplit ? j : 0) * a.bm * D + lane + 64 * i];
+  }
   {
     int first, per;
-    const int n_act = own_chunks(a, r, first, per);
+    const int L = block_shared_len(a, ((int64_t)r * G) / a.bm, lane);
+    const int n_act = own_chunks(a, r, L, first, per);
     float acc[G][E], m_run[G], l_run[G];
     if (wave < n_act) {
       const int start = first + wave * per;
       const int stop = min(start + per, (int)a.kv_len[r]);
-      own_chunk<T, D, G>(a, r, h, a.req_pool_idx[r], start, stop, lane, acc, m_run, l_run);
+      own_chunk<T, D, G>(a, h, a.req_pool_idx[r], start, stop, lane, q, acc, m_run, l_run);
     } else {
 #pragma unroll
       for (int hl = 0; hl < G; ++hl) {
@@ -994,8 +1053,6 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int nsplit = a.nsplit;
-  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
   for (int hl = wave; hl < G; hl += W) {
     const int64_t Grow = (int64_t)r * G + hl;  // MFMA row of (request r, query head h*G + hl)
     const int64_t rb = Grow / a.bm;
@@ -1006,7 +1063,7 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
     const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + R) * 2;
     // lane s < nsplit: split partial s; nsplit <= s < nsplit + W: own chunk s - nsplit
     const int sl = lane < nsplit ? lane : 0;
-    const float2 gml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sl * a.bm * 2);
+    const float2 gml = hl == wave ? pre_ml : *reinterpret_cast<const float2*>(sh_ml + (int64_t)sl * a.bm * 2);
     const int oc = lane - nsplit;
     const bool own_lane = oc >= 0 && oc < W;
     const float om = own_lane ? s_ml[(oc * G + hl) * 2] : kNegInf;
@@ -1024,9 +1081,21 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    // split partials with nonzero weight, up to 32 per round trip
-    constexpr int U = 32;
+    // split partials with nonzero weight: the prefetched ones (first head of this wave; a
+    // partial that saw no key may hold stale data, hence the select), then the rest up
+    // to 32 per round trip
     uint64_t nz = __ballot(lane < nsplit && my_w != 0.f);
+    if (hl == wave) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+        const bool use = j < nsplit && wj != 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] += use ? wj * pre_acc[j][i] : 0.f;
+      }
+      nz &= ~(uint64_t)((1u << kPre) - 1);
+    }
+    constexpr int U = 32;
     const int s_first = nz ? __builtin_ctzll(nz) : 0;
     while (nz) {
       float x[U][PER], wt[U];
@@ -1100,7 +1169,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const float my_m = mlv.x;
   float my_l = lane < n_max ? mlv.y : 0.f;
   int n_own = 0, first = 0, per = 0;
-  if (a.shared_only) n_own = own_chunks(a, (int)t, first, per);
+  if (a.shared_only) n_own = own_chunks(a, (int)t, block_shared_len(a, rb, lane), first, per);
   if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
 #pragma unroll
@@ -1164,8 +1233,9 @@ static Shape pick_shape(bool decode, rax_dtype dt, int d) {
 }
 
 static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
-  // enough workgroups for 256 CUs x 2 resident, at least one full request's tiles per split
-  int64_t want = (512 + blocks - 1) / blocks;
+  // about one workgroup per CU (256 CUs): measured as fast as two per CU for the shared
+  // prefix of decode, with half the split partials to write and merge
+  int64_t want = (256 + blocks - 1) / blocks;
   const int64_t tiles = (int64_t)(max_kv_len + BN - 1) / BN;
   int64_t cap = tiles;
   if (cap < 1) cap = 1;
@@ -1199,8 +1269,23 @@ static size_t own_fused_lds_bytes(int n_chunk, int g, int d) {
   return (size_t)n_chunk * g * (d + 2) * sizeof(float);
 }
 
+template <typename T, int D>
+static rax_status launch_own(AttnArgs& a, hipStream_t st) {
+  const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
+  const unsigned blocks = (unsigned)((own_items + 3) / 4);
+  switch (a.g) {
+    case 1: hipLaunchKernelGGL((own_kernel<T, D, 1>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((own_kernel<T, D, 2>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((own_kernel<T, D, 4>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((own_kernel<T, D, 8>), dim3(blocks), dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((own_kernel<T, D, 16>), dim3(blocks), dim3(256), 0, st, a); break;
+    default: return RAX_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
 template <typename T, int D, bool kDecode>
-static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
+static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st) {
   rax_status rc = RAX_EINVAL;
   if constexpr (sizeof(T) == 2 && !kDecode) {
     if constexpr (D == 128) {
@@ -1214,6 +1299,12 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
   }
   if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 1)
     rc = launch_one<T, D, kDecode, 4, 1, 1, 1>(a, st);
+  return rc;
+}
+
+template <typename T, int D, bool kDecode>
+static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
+  rax_status rc = launch_attn<T, D, kDecode>(a, s, st);
   if (rc != RAX_OK) return rc;
   if constexpr (kDecode) {
     if (a.shared_only && a.own_fused) {
@@ -1232,17 +1323,9 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
       return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
     }
     if (a.shared_only) {
-      const int64_t own_items = (int64_t)a.batch * a.h_kv * a.n_chunk;
-      const unsigned blocks = (unsigned)((own_items + 3) / 4);
-      switch (a.g) {
-        case 1: hipLaunchKernelGGL((own_kernel<T, D, 1>), dim3(blocks), dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((own_kernel<T, D, 2>), dim3(blocks), dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((own_kernel<T, D, 4>), dim3(blocks), dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((own_kernel<T, D, 8>), dim3(blocks), dim3(256), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((own_kernel<T, D, 16>), dim3(blocks), dim3(256), 0, st, a); break;
-        default: return RAX_EINVAL;
-      }
-      if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+      // more chunks per (request, KV head) than one workgroup takes: partials, then merge
+      rc = launch_own<T, D>(a, st);
+      if (rc != RAX_OK) return rc;
     }
   }
   if (a.nsplit > 1 || a.shared_only) return launch_merge<D>(a, st);
@@ -1264,7 +1347,7 @@ static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_
 // Workspace of a decode call, in floats: shared-part partials (accumulators, then m/l),
 // the row blocks' shared lengths, own-part partials (accumulators, then m/l).
 struct DecodeLayout {
-  int64_t sh_acc, sh_ml, L, own_acc, own_ml, total;
+  int64_t sh_acc, sh_ml, own_acc, own_ml, total;
   int32_t nsplit, n_rb, n_chunk, bm;
   bool split_decode, own_fused;
 };
@@ -1298,10 +1381,9 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   const int64_t own_rows = l.own_fused ? 0 : batch * h_kv * l.n_chunk * g;
   l.sh_acc = sh_items * l.bm * d;
   l.sh_ml = sh_items * l.bm * 2;
-  l.L = (l.n_rb + 63) / 64 * 64;
   l.own_acc = own_rows * d;
   l.own_ml = own_rows * 2;
-  l.total = l.sh_acc + l.sh_ml + l.L + l.own_acc + l.own_ml;
+  l.total = l.sh_acc + l.sh_ml + l.own_acc + l.own_ml;
   return l;
 }
 
@@ -1420,8 +1502,7 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
     a.ws = w;
     if (l.split_decode) {
       a.shared_only = 1;
-      a.ws_L = reinterpret_cast<int32_t*>(w + l.sh_acc + l.sh_ml);
-      a.ws_own = w + l.sh_acc + l.sh_ml + l.L;
+      a.ws_own = w + l.sh_acc + l.sh_ml;
       a.n_chunk = l.n_chunk;
       a.own_fused = l.own_fused ? 1 : 0;
     }

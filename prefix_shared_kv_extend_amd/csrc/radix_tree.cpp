@@ -135,6 +135,24 @@ void RadixTree::tick_path(Node* n) {
   }
 }
 
+int64_t RadixTree::prefix_len(const int32_t* tokens, int64_t n) const {
+  const Node* node = root_;
+  int64_t i = 0;
+  while (i < n) {
+    auto it = node->children.find(tokens[i]);
+    if (it == node->children.end()) break;
+    const Node* c = it->second;
+    const int64_t len = static_cast<int64_t>(c->tokens.size());
+    const int64_t lim = std::min(len, n - i);
+    int64_t k = 1;
+    while (k < lim && c->tokens[k] == tokens[i + k]) ++k;
+    i += k;
+    if (k < len) break;
+    node = c;
+  }
+  return i;
+}
+
 int64_t RadixTree::match(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_node) {
   ++clock_;
   int64_t m = 0;

@@ -61,6 +61,8 @@ class RadixTree {
   const SlotAllocator& alloc() const { return alloc_; }
 
   int64_t match(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_node);
+  // Length of the longest cached prefix of tokens, without splitting or ticking anything.
+  int64_t prefix_len(const int32_t* tokens, int64_t n) const;
   // Returns false (nothing changed) if a caller slot is out of range or free.
   bool insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
               int64_t* out_existing, int64_t* out_node);

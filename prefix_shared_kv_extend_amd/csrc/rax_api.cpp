@@ -1,5 +1,7 @@
 // C ABI: host radix-tree entry points of librax (declared in include/rax.h).
+#include <algorithm>
 #include <new>
+#include <numeric>
 #include <vector>
 
 #include "../../include/rax.h"
@@ -255,6 +257,54 @@ rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32
   for (int32_t i = 0; i < batch; ++i) seq_len[i] += 1;
   return raxk::launch_decode_append(batch, out_slots, seq_len, req_pool_idx, seq_len_dev, req_to_token, rtt_stride,
                                     rtt_rows, k_new, v_new, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
+  RAX_GUARD_END
+}
+
+rax_status rax_prefix_len_batch(const rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                                int64_t* out_len) {
+  if (!t || batch < 0 || (batch > 0 && (!indptr || !out_len))) return RAX_EINVAL;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr[r + 1] < indptr[r] || (indptr[r + 1] > indptr[r] && !tokens)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  for (int32_t r = 0; r < batch; ++r) out_len[r] = t->t.prefix_len(tokens + indptr[r], indptr[r + 1] - indptr[r]);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* tokens, const int64_t* indptr,
+                              int32_t batch, uint64_t seed, int32_t* out_order, int64_t* out_len) {
+  if (!t || batch < 0 || policy < RAX_SCHED_FCFS || policy > RAX_SCHED_RANDOM) return RAX_EINVAL;
+  if (batch == 0) return RAX_OK;
+  if (!out_order || !out_len) return RAX_EINVAL;
+  rax_status st = rax_prefix_len_batch(t, tokens, indptr, batch, out_len);
+  if (st != RAX_OK) return st;
+  RAX_GUARD_BEGIN
+  std::vector<int32_t> order(static_cast<size_t>(batch));
+  std::iota(order.begin(), order.end(), 0);
+  if (policy == RAX_SCHED_LPM) {
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return out_len[a] > out_len[b]; });
+  } else if (policy == RAX_SCHED_DFS) {
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return std::lexicographical_compare(tokens + indptr[a], tokens + indptr[a + 1], tokens + indptr[b],
+                                          tokens + indptr[b + 1]);
+    });
+  } else if (policy == RAX_SCHED_RANDOM) {
+    // Fisher-Yates, draws from SplitMix64 (Steele, Lea, Flood 2014) started at seed
+    uint64_t state = seed;
+    auto next = [&state]() {
+      state += 0x9E3779B97F4A7C15ull;
+      uint64_t z = state;
+      z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+      z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+      return z ^ (z >> 31);
+    };
+    for (int32_t i = batch - 1; i > 0; --i) {
+      const int32_t j = static_cast<int32_t>(next() % static_cast<uint64_t>(i + 1));
+      std::swap(order[i], order[j]);
+    }
+  }
+  std::copy(order.begin(), order.end(), out_order);
+  return RAX_OK;
   RAX_GUARD_END
 }
 
