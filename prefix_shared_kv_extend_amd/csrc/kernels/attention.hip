@@ -506,13 +506,17 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     if (run) {
       const bool unmasked = d.kind == 0 && d.cnt == BN && all_rows_ok;
       // two 32-key online-softmax steps per 64-key tile (keeps S and P small); with
-      // KS == 2 each wave takes one of them and the pair is combined at the end
+      // KS == 2 each wave takes one of them and the pair is combined at the end. The S
+      // products of all of this wave's halves are issued first, so that the second
+      // half's MFMAs run in the matrix pipe while the first half's softmax runs on the VALU
+      // (and its P.V MFMAs under the second half's softmax).
+      constexpr int NSUB = 2 / KS;
+      f32x16 sall[NSUB][RT];
 #pragma unroll
-      for (int si = 0; si < 2 / KS; ++si) {
+      for (int si = 0; si < NSUB; ++si) {
         const int sub = KS == 1 ? si : wkey;
-        f32x16 s[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) s[rt] = f32x16{};
+        for (int rt = 0; rt < RT; ++rt) sall[si][rt] = f32x16{};
         const T* kr = &sm.k[buf][(sub * 32 + jrow) * C::KSTRIDE];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -520,14 +524,19 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
             const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[rt][ks], s[rt], 0, 0, 0);
+              sall[si][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[rt][ks], sall[si][rt], 0, 0, 0);
           } else {
             const float af = kr[ks * 2 + half];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              s[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, qf[rt][ks], s[rt], 0, 0, 0);
+              sall[si][rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, qf[rt][ks], sall[si][rt], 0, 0, 0);
           }
         }
+      }
+#pragma unroll
+      for (int si = 0; si < NSUB; ++si) {
+        const int sub = KS == 1 ? si : wkey;
+        f32x16(&s)[RT] = sall[si];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           // mask (raw scores; the scale is positive); key index of register r:
