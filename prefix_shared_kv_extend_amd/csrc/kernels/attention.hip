@@ -1378,9 +1378,11 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   }
   // own part: chunks per (request, KV head) so that about kOwnWaves waves exist in total,
   // at most one per kOwnMin keys of the longest sequence and at most 64 - nsplit partials
-  // per row; the kernel uses fewer when a request has fewer own keys. Waves past a
-  // request's chunks exit at once, but still hold a wave slot while they do.
-  constexpr int64_t kOwnWaves = 8192;
+  // per row; the kernel uses fewer when a request has fewer own keys. kOwnWaves is one
+  // round of residency (256 CUs x 4 SIMDs x 4 waves at ~120 VGPRs): with more waves the
+  // latency chain of each (slots, then K/V, then merge) runs twice; measured on the
+  // few-shot decode, 4096 waves 15.4 us, 8192 waves 20.2 us, 2048 waves 16.7 us.
+  constexpr int64_t kOwnWaves = 4096;
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
   l.n_chunk = (int32_t)std::max<int64_t>(
       1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnMin - 1) / kOwnMin, (kOwnWaves + pairs - 1) / pairs}));
