@@ -66,7 +66,13 @@ typedef struct {
   int64_t clock;            /* logical LRU clock (one tick per match or insert) */
   int64_t matched_tokens;   /* cumulative over rax_match_prefix calls */
   int64_t inserted_tokens;  /* cumulative new tokens adopted by rax_insert */
-  int64_t evicted_tokens;   /* cumulative */
+  int64_t evicted_tokens;   /* cumulative (device slots freed, demoted or dropped) */
+  int64_t host_slots;       /* host tier size (0 = no tier) */
+  int64_t host_free_slots;
+  int64_t host_tokens;      /* tokens whose KV sits in the host tier (not in cached_tokens) */
+  int64_t demoted_tokens;   /* cumulative device -> host */
+  int64_t promoted_tokens;  /* cumulative host -> device */
+  int64_t pending_moves;    /* moves recorded and not yet run or taken */
 } rax_stats;
 
 const char* rax_status_str(rax_status s);
@@ -111,13 +117,17 @@ rax_status rax_insert(rax_tree* t, const int32_t* tokens, const int32_t* slots, 
                       int32_t* out_slots, int64_t* out_existing, rax_node* out_node);
 
 /* Add delta (+1 or -1) to the ref count of every node from `node` up to the root.
- * RAX_ESTATE if the node is unknown or a count would go below zero (nothing changed). */
+ * RAX_ESTATE if the node is unknown, is in the host tier, or a count would go below
+ * zero (nothing changed). */
 rax_status rax_lock_ref(rax_tree* t, rax_node node, int32_t delta);
 
 /* Evict least-recently-used leaves with ref 0 until >= num_tokens slots are freed or
  * nothing is evictable; freed slots go back to the free set. *out_num_freed is the
  * total freed; the first min(cap, total) slot ids, leaf by leaf in eviction order and
- * each leaf in token order, are written to out_freed (may be NULL when cap == 0). */
+ * each leaf in token order, are written to out_freed (may be NULL when cap == 0).
+ * With a host tier (rax_set_host_tier) a "leaf" is a device node with ref 0 and no
+ * device child, and its KV is demoted to host slots instead of dropped, which records
+ * moves that must run (rax_run_moves) before the freed slots are written. */
 rax_status rax_evict_lru(rax_tree* t, int64_t num_tokens, int32_t* out_freed, int64_t cap,
                          int64_t* out_num_freed);
 
@@ -190,10 +200,62 @@ rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* 
 rax_status rax_tree_stats(const rax_tree* t, rax_stats* out);
 
 /* Serialise the tree in preorder (children by ascending first token), as int64 words:
- * per node [handle, parent handle, length L, ref, tick, tokens[L], slots[L]]. With
+ * per node [handle, parent handle, length L, ref, tick, tokens[L], slots[L]] (a host
+ * node's slots as -1 - host slot id). With
  * buf == NULL (or cap too small) *out_len receives the word count; too small a
  * non-NULL buffer is RAX_EINVAL. */
 rax_status rax_tree_dump(const rax_tree* t, int64_t* buf, int64_t cap, int64_t* out_len);
+
+/* ================================================================ host-memory KV tier
+ * A second level below the device pool ([hustzhy] §6.1, HiCache: GPU memory holds the
+ * hottest KV, host memory the next; the pages' third level, distributed storage, is not
+ * built). The tier is a pinned host buffer of host_slots token rows laid out like the
+ * pool ([host_slots, h_kv, d], K and V apart); kernels read and write it directly over
+ * the bus. Rules (choices where the pages are silent):
+ *  - eviction demotes: the LRU device leaf's KV moves to the lowest free host slots and
+ *    the node stays in the tree as a host node. If the tier is short, LRU host leaves
+ *    are dropped first; if it is still short the node and its host subtree are dropped.
+ *  - host nodes only ever have host descendants. Matching (and rax_prefix_len_batch,
+ *    the scheduler's ordering) stops at the first host node: reuse needs device KV.
+ *  - rax_promote_batch moves the host continuation of each request's cached device
+ *    prefix back to device slots (evicting, hence demoting, when short), node by node,
+ *    splitting where the request diverges inside a host node; it stops at the first
+ *    node that does not fit.
+ *  - rax_insert adopts host nodes on the inserted path: the caller's fresh device slots
+ *    become the node's slots and its host slots are released (nothing to move).
+ *  - every demotion and promotion appends a move (kind 0: device src -> host dst, 1:
+ *    host src -> device dst) to the tree's pending list, in decision order. Run in that
+ *    order the moves are correct even when a slot freed by one is taken by a later one;
+ *    they must run before the caller writes any slot the same calls handed out.
+ *  - rax_tree_dump writes a host node's slots as -1 - host slot id. */
+
+/* Enable the tier with host_slots rows (or 0 to disable), at most once while no node is
+ * on the host. k_host, v_host: pinned host memory (allocated pinned, e.g.
+ * hipHostMalloc), host_slots * h_kv * d elements each, 16-byte aligned, caller-owned and
+ * alive while the tree is; both NULL (host-only use: moves are collected with
+ * rax_take_moves) or both set. RAX_EINVAL: bad size or memory the device cannot reach;
+ * RAX_ESTATE: host nodes exist. */
+rax_status rax_set_host_tier(rax_tree* t, int64_t host_slots, void* k_host, void* v_host);
+
+/* For each request i (tokens[indptr[i] .. indptr[i+1]), host int32/int64 arrays), promote
+ * its host-resident continuation as described above; out_promoted[i] = tokens promoted.
+ * Device slots freed by evictions are reported as by rax_alloc_slots_evict (first cap into
+ * out_freed, *out_num_freed = total). Promotions record moves; run them before use. */
+rax_status rax_promote_batch(rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                             int64_t* out_promoted, int32_t* out_freed, int64_t cap, int64_t* out_num_freed);
+
+/* Copy the pending moves (host int32 arrays of cap entries) and clear the list; with
+ * kind == src == dst == NULL only *out_len = number pending. RAX_EINVAL if cap is short
+ * (nothing taken). */
+rax_status rax_take_moves(rax_tree* t, int32_t* kind, int32_t* src, int32_t* dst, int64_t cap, int64_t* out_len);
+
+/* Run the pending moves on `stream` between the device pools ([num_slots, h_kv, d],
+ * dtype dt) and the tier's buffers, then clear the list: one kernel launch per 256
+ * moves of a phase (a run of one kind), phases in order, a later move to the same
+ * destination within a phase superseding an earlier one. RAX_ESTATE if moves are pending
+ * and the tier has no buffers. Host arrays are consumed before the call returns. */
+rax_status rax_run_moves(rax_tree* t, void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt,
+                         void* stream);
 
 /* ====================================================================== device calls */
 
@@ -230,7 +292,9 @@ rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_stride, int
  * stream passes the call. RAX_EINVAL (nothing changed): bad argument, or a length that
  * would exceed rtt_stride. RAX_ENOMEM: fewer than batch slots even after evicting (the
  * evicted slots stay free, nothing else changes). A req_pool_idx outside [0, rtt_rows)
- * is skipped on the device and flagged (RAX_DEVERR_ROW). */
+ * is skipped on the device and flagged (RAX_DEVERR_ROW). With a host tier, moves that
+ * step 1's eviction records (and any still pending) run first, on the same stream;
+ * RAX_ESTATE up front if the tier has no buffers. */
 rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots,
                              int32_t* out_freed, int64_t cap, int64_t* out_num_freed,
                              const int32_t* req_pool_idx, int32_t* seq_len_dev, int32_t* req_to_token,

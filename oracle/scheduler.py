@@ -26,6 +26,9 @@ Readings where the pages are silent (the native scheduler follows the same rules
   S3  A batch runs like an extend batch (match and lock every request, one
       allocation with eviction, insert every prompt) and then unlocks: these
       requests only prefill.
+  S5  With a host tier, each batch first promotes its requests' host-resident
+      prefixes (model rule H3), in batch order; ordering and admission look at the
+      device-resident prefix only.
   S4  The random order is a Fisher-Yates shuffle whose k-th draw is SplitMix64
       output k of a stream started at seed + step (Steele, Lea, Flood 2014),
       j = draw mod (i + 1) for i = n-1 down to 1.
@@ -65,10 +68,10 @@ def order(model, prompts, waiting, policy: str, seed: int) -> list:
 
 
 def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: int = 1 << 30,
-                max_batch: int = 1 << 30, seed: int = 0):
+                max_batch: int = 1 << 30, seed: int = 0, host_slots: int = 0):
     """Schedule and run every prompt (all waiting, list order = arrival). Returns
     (batches, computed tokens, event log)."""
-    model = RadixCacheModel(num_slots)
+    model = RadixCacheModel(num_slots, host_slots)
     waiting = list(range(len(prompts)))
     batches, log, computed, step = [], [], 0, 0
     while waiting:
@@ -84,6 +87,13 @@ def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: 
             tot += n
             new += need
         batches.append(batch)
+        if host_slots:                                # S5
+            done, freed = [], []
+            for r in batch:
+                d, f = model.promote(prompts[r])
+                done.append(d)
+                freed += f
+            log.append(("promote", step, tuple(done), tuple(freed)))
         # S3: the batch as an extend batch
         held, pending = {}, []
         for r in batch:
@@ -113,6 +123,7 @@ def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: 
             log.append(("insert", r, existing, node))
         for r in batch:
             model.lock_ref(held[r], -1)
+        model.take_moves()
         chosen = set(batch)
         waiting = [r for r in waiting if r not in chosen]
         step += 1

@@ -29,7 +29,8 @@ _i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c
 class RaxStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_slots", "free_slots", "cached_tokens", "locked_tokens", "evictable_tokens",
-        "num_nodes", "clock", "matched_tokens", "inserted_tokens", "evicted_tokens")]
+        "num_nodes", "clock", "matched_tokens", "inserted_tokens", "evicted_tokens",
+        "host_slots", "host_free_slots", "host_tokens", "demoted_tokens", "promoted_tokens", "pending_moves")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -56,6 +57,10 @@ _SIGS = {
     "rax_prefix_len_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p]),
     "rax_schedule_order": (_i32, [_vp, _i32, _c_i32p, _c_i64p, _i32, ctypes.c_uint64, _c_i32p, _c_i64p]),
     "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
+    "rax_set_host_tier": (_i32, [_vp, _i64, _vp, _vp]),
+    "rax_promote_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p, _c_i32p, _i64, _c_i64p]),
+    "rax_take_moves": (_i32, [_vp, _c_i32p, _c_i32p, _c_i32p, _i64, _c_i64p]),
+    "rax_run_moves": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "rax_tree_dump": (_i32, [_vp, _c_i64p, _i64, _c_i64p]),
     "rax_kv_scatter": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "rax_decode_append": (_i32, [_vp, _i32, _c_i32p, _c_i32p, _c_i32p, _i64, _c_i64p, _vp, _vp, _vp, _i64, _i64,
@@ -196,6 +201,49 @@ class Tree:
             _dtype_code(k_pool), _stream(stream, k_pool))
         _check(st, "rax_decode_append")
         return out, self._freed[: nf.value].copy()
+
+    # ------------------------------------------------------------ host tier
+    def set_host_tier(self, host_slots: int, k_host=None, v_host=None) -> None:
+        """Enable the host tier (rax_set_host_tier): host_slots token rows; k_host, v_host pinned
+        CPU tensors [host_slots, h_kv, d] (or None for host-only use, moves taken by take_moves)."""
+        if k_host is not None:
+            _need(k_host.shape == v_host.shape and k_host.shape[0] == host_slots and k_host.dtype == v_host.dtype
+                  and k_host.is_pinned() and v_host.is_pinned() and k_host.is_contiguous() and v_host.is_contiguous(),
+                  "k_host/v_host: pinned contiguous [host_slots, h_kv, d]")
+        _check(self._L.rax_set_host_tier(self._h, int(host_slots), _dev(k_host), _dev(v_host)), "rax_set_host_tier")
+
+    def promote_batch(self, tokens, indptr):
+        """Promote each request's host-resident continuation (rax_promote_batch).
+        Returns (promoted tokens per request, device slots freed by evictions)."""
+        t = _i32arr(tokens)
+        ip = np.ascontiguousarray(np.asarray(indptr, dtype=np.int64))
+        b = len(ip) - 1
+        out = np.zeros(max(b, 0), dtype=np.int64)
+        cap = 2 * self.num_slots + len(t)
+        freed = np.empty(cap, dtype=np.int32)
+        nf = _i64()
+        _check(self._L.rax_promote_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), b,
+                                         out.ctypes.data_as(_c_i64p), _p32(freed), cap, ctypes.byref(nf)),
+               "rax_promote_batch")
+        if nf.value > cap:
+            raise RuntimeError("rax_promote_batch: eviction report truncated")
+        return out, freed[: nf.value].copy()
+
+    def take_moves(self):
+        """Pending moves as (kind, src, dst) int32 arrays; clears the list (rax_take_moves)."""
+        n = _i64()
+        _check(self._L.rax_take_moves(self._h, None, None, None, 0, ctypes.byref(n)), "rax_take_moves")
+        k, s, d = (np.empty(max(n.value, 1), dtype=np.int32) for _ in range(3))
+        _check(self._L.rax_take_moves(self._h, _p32(k), _p32(s), _p32(d), len(k), ctypes.byref(n)),
+               "rax_take_moves")
+        return k[: n.value].copy(), s[: n.value].copy(), d[: n.value].copy()
+
+    def run_moves(self, k_pool, v_pool, stream=None) -> None:
+        """Launch the pending moves between the pools and the host tier (rax_run_moves)."""
+        _need(k_pool.shape == v_pool.shape and k_pool.is_cuda and k_pool.is_contiguous() and v_pool.is_contiguous(),
+              "pools: contiguous cuda [slots, h_kv, d]")
+        _check(self._L.rax_run_moves(self._h, _dev(k_pool), _dev(v_pool), k_pool.shape[1], k_pool.shape[2],
+                                     _dtype_code(k_pool), _stream(stream, k_pool)), "rax_run_moves")
 
     def free_count(self) -> int:
         n = _i64()

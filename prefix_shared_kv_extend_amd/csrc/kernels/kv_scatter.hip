@@ -10,6 +10,9 @@
 // and writes are coalesced.
 #include "../../../include/rax.h"
 #include "rax_device.h"
+#include <unordered_set>
+#include <vector>
+
 #include "../rax_internal.h"
 
 namespace raxk {
@@ -117,6 +120,71 @@ rax_status launch_decode_append(int32_t batch, const int32_t* slots, const int32
                        reinterpret_cast<const uint4*>(k_new) + off, reinterpret_cast<const uint4*>(v_new) + off,
                        reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool), chunks_per_row);
     if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+  }
+  return RAX_OK;
+}
+
+// KV moves between the device pool and the host tier (pinned host memory that the
+// kernel reads and writes directly over the bus): block (i, kv) copies row src[i] of
+// the source into row dst[i] of the destination, 16 bytes per lane.
+__global__ void __launch_bounds__(256) kv_move_kernel(MoveBatch b, const uint4* __restrict__ k_src,
+                                                      const uint4* __restrict__ v_src, uint4* __restrict__ k_dst,
+                                                      uint4* __restrict__ v_dst, int64_t chunks_per_row) {
+  const int i = blockIdx.x;
+  const uint4* src = blockIdx.y ? v_src : k_src;
+  uint4* dst = blockIdx.y ? v_dst : k_dst;
+  const int64_t s = (int64_t)b.src[i] * chunks_per_row;
+  const int64_t d = (int64_t)b.dst[i] * chunks_per_row;
+  for (int64_t c = threadIdx.x; c < chunks_per_row; c += blockDim.x) dst[d + c] = src[s + c];
+}
+
+bool host_device_ptr(const void* host, void** dev) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer) return false;
+  *dev = a.devicePointer;
+  return true;
+}
+
+rax_status launch_kv_moves(const int32_t* kind, const int32_t* src, const int32_t* dst, int64_t n, void* k_pool,
+                           void* v_pool, void* k_host_dev, void* v_host_dev, int64_t chunks_per_row,
+                           hipStream_t st) {
+  std::vector<int32_t> ps, pd;
+  std::unordered_set<int32_t> seen;
+  for (int64_t a = 0; a < n;) {
+    int64_t e = a;
+    while (e < n && kind[e] == kind[a]) ++e;
+    // the phase [a, e): keep the last move to each destination, in order
+    ps.clear();
+    pd.clear();
+    seen.clear();
+    for (int64_t j = e - 1; j >= a; --j) {
+      if (seen.insert(dst[j]).second) {
+        ps.push_back(src[j]);
+        pd.push_back(dst[j]);
+      }
+    }
+    const bool demote = kind[a] == 0;
+    const uint4* ks = reinterpret_cast<const uint4*>(demote ? k_pool : k_host_dev);
+    const uint4* vs = reinterpret_cast<const uint4*>(demote ? v_pool : v_host_dev);
+    uint4* kd = reinterpret_cast<uint4*>(demote ? k_host_dev : k_pool);
+    uint4* vd = reinterpret_cast<uint4*>(demote ? v_host_dev : v_pool);
+    const int64_t m = static_cast<int64_t>(ps.size());
+    for (int64_t b0 = 0; b0 < m; b0 += kMoveMax) {
+      MoveBatch b;
+      b.n = static_cast<int32_t>(m - b0 < kMoveMax ? m - b0 : kMoveMax);
+      for (int i = 0; i < b.n; ++i) {
+        b.src[i] = ps[m - 1 - (b0 + i)];  // collected backwards
+        b.dst[i] = pd[m - 1 - (b0 + i)];
+      }
+      hipLaunchKernelGGL(kv_move_kernel, dim3(b.n, 2), dim3(chunks_per_row < 256 ? 128 : 256), 0, st, b, ks, vs,
+                         kd, vd, chunks_per_row);
+      if (hipGetLastError() != hipSuccess) return RAX_EDEVICE;
+    }
+    a = e;
   }
   return RAX_OK;
 }

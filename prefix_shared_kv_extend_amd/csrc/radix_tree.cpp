@@ -74,13 +74,48 @@ void RadixTree::lru_remove(Node* n) {
 }
 
 void RadixTree::lru_update(Node* n) {
-  const bool want = n != root_ && n->children.empty() && n->ref == 0;
+  const bool want = n != root_ && !n->host && n->ndev == 0 && n->ref == 0;
   if (want && !n->in_lru) {
     lru_.insert({n->tick, n->id});
     n->in_lru = true;
   } else if (!want && n->in_lru) {
     lru_remove(n);
   }
+}
+
+void RadixTree::hlru_remove(Node* n) {
+  if (n->in_hlru) {
+    hlru_.erase({n->tick, n->id});
+    n->in_hlru = false;
+  }
+}
+
+void RadixTree::hlru_update(Node* n) {
+  const bool want = n->host && n->children.empty() && n->ref == 0;
+  if (want && !n->in_hlru) {
+    hlru_.insert({n->tick, n->id});
+    n->in_hlru = true;
+  } else if (!want && n->in_hlru) {
+    hlru_remove(n);
+  }
+}
+
+bool RadixTree::set_host_tier(int64_t host_slots) {
+  if (host_slots < 0 || host_tokens > 0) return false;
+  host_alloc_ = SlotAllocator(host_slots);
+  return true;
+}
+
+void RadixTree::erase_node(Node* n) {
+  lru_remove(n);
+  hlru_remove(n);
+  Node* p = n->parent;
+  p->children.erase(n->tokens[0]);
+  if (!n->host) --p->ndev;
+  nodes_.erase(n->id);
+  delete n;
+  lru_update(p);
+  hlru_update(p);
 }
 
 Node* RadixTree::split(Node* child, int64_t k) {
@@ -91,6 +126,8 @@ Node* RadixTree::split(Node* child, int64_t k) {
   up->slots.assign(child->slots.begin(), child->slots.begin() + k);
   up->ref = child->ref;
   up->tick = child->tick;
+  up->host = child->host;
+  up->ndev = child->host ? 0 : 1;
   up->depth_end = parent->depth_end + k;
   child->tokens.erase(child->tokens.begin(), child->tokens.begin() + k);
   child->slots.erase(child->slots.begin(), child->slots.begin() + k);
@@ -105,7 +142,7 @@ Node* RadixTree::walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_
   int64_t i = 0;
   while (i < n) {
     auto it = node->children.find(tokens[i]);
-    if (it == node->children.end()) break;
+    if (it == node->children.end() || it->second->host) break;  // the device part only
     Node* c = it->second;
     const int64_t len = static_cast<int64_t>(c->tokens.size());
     const int64_t lim = std::min(len, n - i);
@@ -140,7 +177,7 @@ int64_t RadixTree::prefix_len(const int32_t* tokens, int64_t n) const {
   int64_t i = 0;
   while (i < n) {
     auto it = node->children.find(tokens[i]);
-    if (it == node->children.end()) break;
+    if (it == node->children.end() || it->second->host) break;
     const Node* c = it->second;
     const int64_t len = static_cast<int64_t>(c->tokens.size());
     const int64_t lim = std::min(len, n - i);
@@ -175,6 +212,30 @@ bool RadixTree::insert(const int32_t* tokens, const int32_t* slots, int64_t n, i
   for (int64_t i = 0; i < m; ++i) {
     if (slots[i] != tree_slots[i]) alloc_.release_one(slots[i]);
   }
+  const int64_t m_dev = m;
+  // host nodes on the path take the caller's (device) slots: the KV is fresh on the device
+  while (m < n) {
+    auto it = node->children.find(tokens[m]);
+    if (it == node->children.end()) break;
+    Node* c = it->second;  // a host node (the device walk stopped at it)
+    const int64_t len = static_cast<int64_t>(c->tokens.size());
+    const int64_t lim = std::min(len, n - m);
+    int64_t k = 1;
+    while (k < lim && c->tokens[k] == tokens[m + k]) ++k;
+    Node* u = k < len ? split(c, k) : c;
+    hlru_remove(u);
+    host_alloc_.release(u->slots.data(), static_cast<int64_t>(u->slots.size()));
+    host_tokens -= k;
+    u->slots.assign(slots + m, slots + m + k);
+    u->host = false;
+    ++node->ndev;
+    std::memcpy(tree_slots.data() + m, slots + m, sizeof(int32_t) * k);
+    lru_update(node);
+    lru_update(u);
+    m += k;
+    node = u;
+    if (k < len) break;
+  }
   if (m < n) {
     Node* leaf = new_node();
     leaf->parent = node;
@@ -183,15 +244,16 @@ bool RadixTree::insert(const int32_t* tokens, const int32_t* slots, int64_t n, i
     leaf->depth_end = node->depth_end + (n - m);
     leaf->tick = clock_;
     node->children[tokens[m]] = leaf;
+    ++node->ndev;
     lru_update(node);  // no longer a leaf
     lru_update(leaf);
-    inserted_total += n - m;
     std::memcpy(tree_slots.data() + m, slots + m, sizeof(int32_t) * (n - m));
     node = leaf;
   }
+  inserted_total += n - m_dev;
   tick_path(node);
   if (out_slots && n) std::memcpy(out_slots, tree_slots.data(), sizeof(int32_t) * n);
-  *out_existing = m;
+  *out_existing = m_dev;
   *out_node = node->id;
   return true;
 }
@@ -200,6 +262,7 @@ int RadixTree::lock_ref(int64_t id, int32_t delta) {
   auto it = nodes_.find(id);
   if (it == nodes_.end()) return 1;
   Node* start = it->second;
+  if (start->host) return 3;  // only device KV can be pinned for a running request
   if (delta < 0) {
     for (Node* n = start; n != root_; n = n->parent)
       if (n->ref + delta < 0) return 2;
@@ -211,25 +274,123 @@ int RadixTree::lock_ref(int64_t id, int32_t delta) {
   return 0;
 }
 
+void RadixTree::drop_host_leaves(int64_t need) {
+  while (host_alloc_.num_free() < need && !hlru_.empty()) {
+    Node* h = nodes_[hlru_.begin()->second];
+    host_alloc_.release(h->slots.data(), static_cast<int64_t>(h->slots.size()));
+    host_tokens -= static_cast<int64_t>(h->slots.size());
+    erase_node(h);
+  }
+}
+
+void RadixTree::drop_subtree(Node* n, int32_t* out_freed, int64_t cap, int64_t* freed) {
+  while (!n->children.empty()) drop_subtree(n->children.begin()->second, out_freed, cap, freed);
+  if (n->host) {
+    host_alloc_.release(n->slots.data(), static_cast<int64_t>(n->slots.size()));
+    host_tokens -= static_cast<int64_t>(n->slots.size());
+  } else {
+    for (int32_t s : n->slots) {
+      if (out_freed && *freed < cap) out_freed[*freed] = s;
+      alloc_.release_one(s);
+      ++*freed;
+    }
+  }
+  erase_node(n);
+}
+
 int64_t RadixTree::evict(int64_t num_tokens, int32_t* out_freed, int64_t cap) {
   int64_t freed = 0;
   while (freed < num_tokens && !lru_.empty()) {
-    const int64_t id = lru_.begin()->second;
-    Node* n = nodes_[id];
+    Node* n = nodes_[lru_.begin()->second];
     lru_remove(n);
-    for (int32_t s : n->slots) {
-      if (out_freed && freed < cap) out_freed[freed] = s;
-      alloc_.release_one(s);
-      ++freed;
+    const int64_t len = static_cast<int64_t>(n->slots.size());
+    if (host_alloc_.num_slots() > 0) drop_host_leaves(len);
+    std::vector<int32_t> hs(static_cast<size_t>(len));
+    if (host_alloc_.num_slots() > 0 && host_alloc_.alloc(len, hs.data())) {
+      // demote: the KV moves to the host tier, the node stays in the tree
+      for (int64_t i = 0; i < len; ++i) {
+        const int32_t s = n->slots[i];
+        pending_.push(0, s, hs[i]);
+        if (out_freed && freed < cap) out_freed[freed] = s;
+        alloc_.release_one(s);
+        ++freed;
+      }
+      n->slots = hs;
+      n->host = true;
+      host_tokens += len;
+      demoted_total += len;
+      --n->parent->ndev;
+      lru_update(n);  // drop_host_leaves may have made it a candidate again
+      lru_update(n->parent);
+      hlru_update(n);
+    } else {
+      drop_subtree(n, out_freed, cap, &freed);
     }
-    Node* p = n->parent;
-    p->children.erase(n->tokens[0]);
-    nodes_.erase(id);
-    delete n;
-    lru_update(p);
   }
   evicted_total += freed;
   return freed;
+}
+
+int64_t RadixTree::promote(const int32_t* tokens, int64_t n, std::vector<int32_t>* freed) {
+  // device part (read only, no split), then the host continuation node by node
+  Node* node = root_;
+  int64_t i = 0;
+  while (i < n) {
+    auto it = node->children.find(tokens[i]);
+    if (it == node->children.end() || it->second->host) break;
+    Node* c = it->second;
+    const int64_t len = static_cast<int64_t>(c->tokens.size());
+    if (n - i < len) return 0;
+    for (int64_t k = 1; k < len; ++k)
+      if (c->tokens[k] != tokens[i + k]) return 0;  // diverges inside a device node
+    i += len;
+    node = c;
+  }
+  int64_t done = 0;
+  Node* locked = node == root_ ? nullptr : node;
+  if (locked) lock_ref(locked->id, +1);  // keep the device path while allocating
+  while (i < n) {
+    auto it = node->children.find(tokens[i]);
+    if (it == node->children.end()) break;
+    Node* c = it->second;  // host
+    const int64_t len = static_cast<int64_t>(c->tokens.size());
+    const int64_t lim = std::min(len, n - i);
+    int64_t k = 1;
+    while (k < lim && c->tokens[k] == tokens[i + k]) ++k;
+    Node* u = k < len ? split(c, k) : c;
+    ++u->ref;  // not droppable while its device slots are taken
+    hlru_remove(u);
+    std::vector<int32_t> ds(static_cast<size_t>(k));
+    const int64_t short_by = k - alloc_.num_free();
+    if (short_by > 0) {
+      std::vector<int32_t> f(static_cast<size_t>(alloc_.num_slots()));
+      const int64_t got = evict(short_by, f.data(), static_cast<int64_t>(f.size()));
+      freed->insert(freed->end(), f.begin(), f.begin() + got);
+    }
+    --u->ref;
+    if (!alloc_.alloc(k, ds.data())) {
+      hlru_update(u);
+      break;
+    }
+    for (int64_t j = 0; j < k; ++j) pending_.push(1, u->slots[j], ds[j]);
+    host_alloc_.release(u->slots.data(), k);
+    u->slots = ds;
+    u->host = false;
+    host_tokens -= k;
+    promoted_total += k;
+    ++node->ndev;
+    lru_update(node);
+    lru_update(u);
+    lock_ref(u->id, +1);
+    if (locked) lock_ref(locked->id, -1);
+    locked = u;
+    done += k;
+    i += k;
+    node = u;
+    if (k < len) break;
+  }
+  if (locked) lock_ref(locked->id, -1);
+  return done;
 }
 
 bool RadixTree::lca_depth(int64_t a, int64_t b, int64_t* out) const {
@@ -250,6 +411,7 @@ bool RadixTree::lca_depth(int64_t a, int64_t b, int64_t* out) const {
 void RadixTree::totals(int64_t* cached, int64_t* locked) const {
   int64_t c = 0, l = 0;
   for (auto& kv : nodes_) {
+    if (kv.second->host) continue;  // counted in host_tokens
     const int64_t len = static_cast<int64_t>(kv.second->tokens.size());
     c += len;
     if (kv.second->ref > 0) l += len;
@@ -283,7 +445,7 @@ int64_t RadixTree::dump(int64_t* buf, int64_t cap) const {
     put(n->ref);
     put(n->tick);
     for (int32_t t : n->tokens) put(t);
-    for (int32_t s : n->slots) put(s);
+    for (int32_t s : n->slots) put(n->host ? -1 - int64_t(s) : s);  // host slots as -1 - id
     push_children(n);
   }
   return pos;

@@ -48,6 +48,21 @@ struct Node {
   int32_t ref = 0;
   int64_t tick = 0;
   bool in_lru = false;
+  // host tier: the node's KV lives in host slots (slots holds host slot ids); host nodes
+  // only ever have host descendants
+  bool host = false;
+  bool in_hlru = false;
+  int32_t ndev = 0;             // children that are device nodes
+};
+
+// KV moves between the device pool and the host tier, in the order the tree decided
+// them: kind 0 = demotion (device slot src -> host slot dst), 1 = promotion (host slot
+// src -> device slot dst). Run in this order they are correct even when a slot freed by
+// one move is taken by a later one.
+struct Moves {
+  std::vector<int32_t> kind, src, dst;
+  void push(int32_t k, int32_t s, int32_t d) { kind.push_back(k); src.push_back(s); dst.push_back(d); }
+  void clear() { kind.clear(); src.clear(); dst.clear(); }
 };
 
 class RadixTree {
@@ -59,6 +74,18 @@ class RadixTree {
 
   SlotAllocator& alloc() { return alloc_; }
   const SlotAllocator& alloc() const { return alloc_; }
+  SlotAllocator& host_alloc() { return host_alloc_; }
+  const SlotAllocator& host_alloc() const { return host_alloc_; }
+  // Host tier of host_slots token slots (0 = none). Only while no node is on the host.
+  bool set_host_tier(int64_t host_slots);
+  // Moves recorded by evictions and promotions since the last take (see Moves).
+  Moves& pending() { return pending_; }
+  const Moves& pending() const { return pending_; }
+  // Promote the host-resident continuation of tokens' cached device prefix to the device,
+  // node by node: device slots for it (evicting, hence demoting, when short); stops at
+  // the first node that does not fit. Returns the tokens promoted; freed device slots
+  // append to freed.
+  int64_t promote(const int32_t* tokens, int64_t n, std::vector<int32_t>* freed);
 
   int64_t match(const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* out_node);
   // Length of the longest cached prefix of tokens, without splitting or ticking anything.
@@ -66,7 +93,7 @@ class RadixTree {
   // Returns false (nothing changed) if a caller slot is out of range or free.
   bool insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
               int64_t* out_existing, int64_t* out_node);
-  // 0 ok, 1 unknown node, 2 would go below zero.
+  // 0 ok, 1 unknown node, 2 would go below zero, 3 host node.
   int lock_ref(int64_t node, int32_t delta);
   int64_t evict(int64_t num_tokens, int32_t* out_freed, int64_t cap);
   bool lca_depth(int64_t a, int64_t b, int64_t* out) const;
@@ -77,6 +104,7 @@ class RadixTree {
   int64_t clock() const { return clock_; }
   void totals(int64_t* cached, int64_t* locked) const;
   int64_t matched_total = 0, inserted_total = 0, evicted_total = 0;
+  int64_t demoted_total = 0, promoted_total = 0, host_tokens = 0;
 
  private:
   Node* new_node();
@@ -85,15 +113,23 @@ class RadixTree {
   // the matched length; appends the slots if out != nullptr.
   Node* walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out);
   void tick_path(Node* n);
-  void lru_update(Node* n);  // re-evaluate leaf/ref-0 membership
+  void lru_update(Node* n);  // re-evaluate device-candidate membership
   void lru_remove(Node* n);
+  void hlru_update(Node* n);  // re-evaluate host-leaf membership
+  void hlru_remove(Node* n);
+  void erase_node(Node* n);   // unlink a node with no children
+  void drop_host_leaves(int64_t need);
+  void drop_subtree(Node* n, int32_t* out_freed, int64_t cap, int64_t* freed);
 
   SlotAllocator alloc_;
   Node* root_;
   int64_t next_id_ = 1;
   int64_t clock_ = 0;
   std::unordered_map<int64_t, Node*> nodes_;
-  std::set<std::pair<int64_t, int64_t>> lru_;  // (tick, id) of leaves with ref 0
+  std::set<std::pair<int64_t, int64_t>> lru_;  // (tick, id): device nodes, ref 0, no device child
+  std::set<std::pair<int64_t, int64_t>> hlru_;  // (tick, id): host nodes, no children, ref 0
+  SlotAllocator host_alloc_{0};
+  Moves pending_;
 };
 
 }  // namespace rax

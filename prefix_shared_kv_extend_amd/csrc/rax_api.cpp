@@ -11,7 +11,21 @@
 struct rax_tree {
   explicit rax_tree(int64_t n) : t(n) {}
   rax::RadixTree t;
+  void* k_host = nullptr;  // device-visible addresses of the host tier's K and V rows
+  void* v_host = nullptr;
 };
+
+// Launches and drains the tree's pending moves (no-op when none).
+static rax_status run_pending(rax_tree* t, void* k_pool, void* v_pool, int64_t chunks_per_row, hipStream_t st) {
+  rax::Moves& mv = t->t.pending();
+  if (mv.kind.empty()) return RAX_OK;
+  if (!t->k_host || !t->v_host) return RAX_ESTATE;
+  const rax_status s = raxk::launch_kv_moves(mv.kind.data(), mv.src.data(), mv.dst.data(),
+                                             static_cast<int64_t>(mv.kind.size()), k_pool, v_pool, t->k_host,
+                                             t->v_host, chunks_per_row, st);
+  mv.clear();
+  return s;
+}
 
 #define RAX_GUARD_BEGIN try {
 #define RAX_GUARD_END                 \
@@ -36,7 +50,7 @@ const char* rax_status_str(rax_status s) {
   }
 }
 
-int32_t rax_abi_version(void) { return 1; }
+int32_t rax_abi_version(void) { return 2; }
 
 rax_status rax_tree_create(int64_t num_slots, rax_tree** out) {
   if (!out || num_slots < 1 || num_slots >= (int64_t(1) << 31)) return RAX_EINVAL;
@@ -130,6 +144,12 @@ rax_status rax_tree_stats(const rax_tree* t, rax_stats* out) {
   out->matched_tokens = r.matched_total;
   out->inserted_tokens = r.inserted_total;
   out->evicted_tokens = r.evicted_total;
+  out->host_slots = r.host_alloc().num_slots();
+  out->host_free_slots = r.host_alloc().num_free();
+  out->host_tokens = r.host_tokens;
+  out->demoted_tokens = r.demoted_total;
+  out->promoted_tokens = r.promoted_total;
+  out->pending_moves = static_cast<int64_t>(r.pending().kind.size());
   return RAX_OK;
   RAX_GUARD_END
 }
@@ -249,12 +269,17 @@ rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32
   if (row_bytes % 16 || (mis & 15)) return RAX_EINVAL;
   for (int32_t i = 0; i < batch; ++i)
     if (seq_len[i] < 0 || (int64_t)seq_len[i] + 1 > rtt_stride) return RAX_EINVAL;
+  if (t->t.host_alloc().num_slots() > 0 && !t->k_host) return RAX_ESTATE;  // demotions would have nowhere to run
   RAX_GUARD_BEGIN
   rax::RadixTree& r = t->t;
   const int64_t short_by = batch - r.alloc().num_free();
   if (short_by > 0) *out_num_freed = r.evict(short_by, out_freed, cap);
   if (!r.alloc().alloc(batch, out_slots)) return RAX_ENOMEM;
   for (int32_t i = 0; i < batch; ++i) seq_len[i] += 1;
+  // moves (demotions of this call's evictions, and any left pending) read their slots
+  // before the append kernel writes the new tokens into them
+  const rax_status ms = run_pending(t, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
+  if (ms != RAX_OK) return ms;
   return raxk::launch_decode_append(batch, out_slots, seq_len, req_pool_idx, seq_len_dev, req_to_token, rtt_stride,
                                     rtt_rows, k_new, v_new, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
   RAX_GUARD_END
@@ -305,6 +330,70 @@ rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* 
   }
   std::copy(order.begin(), order.end(), out_order);
   return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_set_host_tier(rax_tree* t, int64_t host_slots, void* k_host, void* v_host) {
+  if (!t || host_slots < 0 || host_slots >= (int64_t(1) << 31) || (k_host == nullptr) != (v_host == nullptr) ||
+      (host_slots == 0 && k_host))
+    return RAX_EINVAL;
+  void* kd = nullptr;
+  void* vd = nullptr;
+  if (k_host && (!raxk::host_device_ptr(k_host, &kd) || !raxk::host_device_ptr(v_host, &vd) ||
+                 (((uintptr_t)kd | (uintptr_t)vd) & 15)))
+    return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  if (!t->t.set_host_tier(host_slots)) return RAX_ESTATE;
+  t->k_host = kd;
+  t->v_host = vd;
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_promote_batch(rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
+                             int64_t* out_promoted, int32_t* out_freed, int64_t cap, int64_t* out_num_freed) {
+  if (!t || batch < 0 || cap < 0 || !out_num_freed || (cap > 0 && !out_freed) ||
+      (batch > 0 && (!indptr || !out_promoted)))
+    return RAX_EINVAL;
+  for (int32_t i = 0; i < batch; ++i)
+    if (indptr[i + 1] < indptr[i] || indptr[0] != 0) return RAX_EINVAL;
+  if (batch > 0 && indptr[batch] > 0 && !tokens) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  rax::RadixTree& r = t->t;
+  std::vector<int32_t> freed;
+  for (int32_t i = 0; i < batch; ++i)
+    out_promoted[i] = r.promote(tokens + indptr[i], indptr[i + 1] - indptr[i], &freed);
+  *out_num_freed = static_cast<int64_t>(freed.size());
+  const int64_t k = std::min<int64_t>(cap, *out_num_freed);
+  if (k > 0) std::copy(freed.begin(), freed.begin() + k, out_freed);
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_take_moves(rax_tree* t, int32_t* kind, int32_t* src, int32_t* dst, int64_t cap, int64_t* out_len) {
+  if (!t || !out_len || cap < 0 || (kind == nullptr) != (src == nullptr) || (kind == nullptr) != (dst == nullptr))
+    return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  rax::Moves& mv = t->t.pending();
+  const int64_t n = static_cast<int64_t>(mv.kind.size());
+  *out_len = n;
+  if (!kind) return RAX_OK;  // count only
+  if (n > cap) return RAX_EINVAL;
+  std::copy(mv.kind.begin(), mv.kind.end(), kind);
+  std::copy(mv.src.begin(), mv.src.end(), src);
+  std::copy(mv.dst.begin(), mv.dst.end(), dst);
+  mv.clear();
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_run_moves(rax_tree* t, void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt,
+                         void* stream) {
+  if (!t || !k_pool || !v_pool || h_kv < 1 || d < 1 || (dt != RAX_F32 && dt != RAX_BF16)) return RAX_EINVAL;
+  const int64_t row_bytes = (int64_t)h_kv * d * (dt == RAX_F32 ? 4 : 2);
+  if (row_bytes % 16 || (((uintptr_t)k_pool | (uintptr_t)v_pool) & 15)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  return run_pending(t, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
   RAX_GUARD_END
 }
 

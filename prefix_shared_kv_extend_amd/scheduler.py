@@ -49,7 +49,8 @@ def _flat(prompts, ids):
 
 
 def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: int = 1 << 30,
-                max_batch: int = 1 << 30, seed: int = 0, record_log: bool = False) -> PrefillResult:
+                max_batch: int = 1 << 30, seed: int = 0, record_log: bool = False,
+                host_slots: int = 0) -> PrefillResult:
     """Admit and run every prompt (all waiting from the start, in list order = arrival).
 
     Each scheduling step orders the waiting queue under `policy` and admits requests in
@@ -57,12 +58,16 @@ def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: 
     new tokens always fit), its new tokens fit `max_batch_tokens` and it has at most
     `max_batch` requests; the first request of a step is always admitted. A prompt fully
     in the cache still computes its last token (the match is cut to n - 1). The random
-    policy draws with seed + step index."""
+    policy draws with seed + step index. With host_slots > 0 the tree has a host tier of that
+    many token rows: eviction demotes, and each batch first promotes its requests'
+    host-resident prefixes (ordering looks at the device-resident prefix only)."""
     if policy not in POLICIES:
         raise ValueError(f"policy must be one of {sorted(POLICIES)}")
     if any(len(p) > num_slots for p in prompts):
         raise ValueError("a prompt is longer than the pool")
     tree = L.Tree(num_slots)
+    if host_slots:
+        tree.set_host_tier(host_slots)
     waiting = list(range(len(prompts)))
     res = PrefillResult([], 0, sum(len(p) for p in prompts))
     log = res.log if record_log else None
@@ -83,15 +88,19 @@ def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: 
             tot += n
             new += need
         res.batches.append(batch)
-        _run_batch(tree, prompts, batch, res, log, step)
+        _run_batch(tree, prompts, batch, res, log, step, host_slots > 0)
         chosen = set(batch)
         waiting = [r for r in waiting if r not in chosen]
         step += 1
     return res
 
 
-def _run_batch(tree, prompts, batch, res, log, step):
+def _run_batch(tree, prompts, batch, res, log, step, tier):
     toks, ip = _flat(prompts, batch)
+    if tier:
+        done, freed = tree.promote_batch(toks, ip)
+        if log is not None:
+            log.append(("promote", step, tuple(done.tolist()), tuple(freed.tolist())))
     pslots, m, nodes = tree.match_prefix_batch(toks, ip, cut_full=True, lock=True)
     if log is not None:
         for i, rid in enumerate(batch):
@@ -113,3 +122,5 @@ def _run_batch(tree, prompts, batch, res, log, step):
         for i, rid in enumerate(batch):
             log.append(("insert", rid, int(existing[i]), int(ins_nodes[i])))
     tree.lock_ref_batch(nodes, -1)     # prefill-only requests finish with their batch
+    if tier:
+        tree.take_moves()              # no device data here: the moves are only counted

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
     assert set(L.EXPORTS) <= names            # the binding declares nothing that the header lacks
-    assert lib.rax_abi_version() == 1
+    assert lib.rax_abi_version() == 2
 
 
 def test_error_codes(L):
