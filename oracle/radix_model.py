@@ -267,7 +267,10 @@ class RadixCacheModel:
             self.segs[p].ref += delta
 
     def _children(self, sid: int) -> list:
-        return [c for c in self.segs.values() if c.parent == sid]
+        """Child segments: those whose first vertex hangs below this segment's last one."""
+        s = self.segs[sid]
+        below = self.root_v if s.top is None else s.bottom
+        return [self.segs[c.seg] for c in below.children.values()]
 
     def _remove_subtree(self, s: _Segment) -> None:
         """Unlink segment s and everything below it; host slots go back to the tier."""
