@@ -11,6 +11,8 @@ notes, App. A.2). The per-step order (extend, then decode, then finish) and the
 full-match cut are the trace's documented lifecycle.
 
 Outputs the event log both sides must agree on bit for bit:
+  ("promote", step, promoted, freed) with a host tier: per extend request, tokens
+                                     promoted (model rule H3), and the device slots freed
   ("match", rid, m, node)            m after the full-match cut
   ("evict", step, freed slots)       only when an allocation had to evict
   ("alloc", step, slots)             one batch allocation per extend / decode call
@@ -32,9 +34,10 @@ def _alloc(model, log, si, n):
     return slots
 
 
-def run_trace(job, steps=None):
-    """Run ``job.steps`` (or a prefix of them) through a fresh model. Returns a dict."""
-    model = RadixCacheModel(job.num_slots)
+def run_trace(job, steps=None, host_slots: int = 0):
+    """Run ``job.steps`` (or a prefix of them) through a fresh model (with a host tier of
+    host_slots rows if > 0: promotion before each extend batch's match). Returns a dict."""
+    model = RadixCacheModel(job.num_slots, host_slots)
     log = []
     rows = {}
     held = {}
@@ -46,6 +49,13 @@ def run_trace(job, steps=None):
     steps = job.steps if steps is None else steps
     for si, st in enumerate(steps):
         pending = []
+        if host_slots and st.extend:
+            done, freed = [], []
+            for rid in st.extend:
+                d, f = model.promote(job.requests[rid].prompt)
+                done.append(d)
+                freed += f
+            log.append(("promote", si, tuple(done), tuple(freed)))
         for rid in st.extend:
             r = job.requests[rid]
             m, pslots, node = model.match(r.prompt)

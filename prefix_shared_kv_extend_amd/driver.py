@@ -22,7 +22,7 @@ def torch_dtype(name: str) -> torch.dtype:
 
 class JobRunner:
     def __init__(self, job, device: str = "cuda", out_dtype: torch.dtype = torch.float32,
-                 max_reqs: int | None = None, record_log: bool = True):
+                 max_reqs: int | None = None, record_log: bool = True, host_slots: int = 0):
         self.job = job
         self.device = torch.device(device)
         self.dtype = torch_dtype(job.dtype)
@@ -35,7 +35,7 @@ class JobRunner:
             max_reqs = min(max_reqs, len(job.requests))
         self.log = [] if record_log else None
         self.rt = RadixRuntime(job.num_slots, job.h_q, job.h_kv, job.d, self.dtype, max_reqs, max_ctx,
-                               device=device, log=self.log)
+                               device=device, log=self.log, host_slots=host_slots)
         self.final_rows = {}
 
     # ------------------------------------------------------------------ inputs

@@ -14,6 +14,13 @@ evicting when memory is short, run it, update the tree; hustzhy SGLang post,
            tokens' K/V, run decode attention over the whole rows.
   finish   insert prompt + generated tokens, unlock.
 
+With a host tier (host_slots > 0; hustzhy SGLang post, §6.1, HiCache's host-memory
+level) eviction demotes KV to a pinned host buffer instead of dropping it; an extend
+batch first promotes its requests' host-resident prefixes back to the pool
+(rax_promote_batch), and every demotion and promotion runs as a copy kernel on the
+stream before the pool slots they free are written (rax_run_moves; the decode append
+runs its own).
+
 A match that covers the whole prompt is cut by one token so the request has a
 query to run. Consecutive requests' common slot prefix (the depth of the lowest
 common ancestor of their tree nodes, rax_lca_depths) is passed to the kernels as
@@ -56,13 +63,20 @@ class DecodeBatch:
 
 class RadixRuntime:
     def __init__(self, num_slots: int, h_q: int, h_kv: int, d: int, dtype: torch.dtype,
-                 max_reqs: int, max_ctx: int, device: str = "cuda", log: list | None = None):
+                 max_reqs: int, max_ctx: int, device: str = "cuda", log: list | None = None,
+                 host_slots: int = 0):
         self.tree = L.Tree(num_slots)
         self.num_slots = num_slots
         self.h_q, self.h_kv, self.d, self.dtype = h_q, h_kv, d, dtype
         self.device = torch.device(device)
         self.k_pool = torch.zeros((num_slots, h_kv, d), dtype=dtype, device=self.device)
         self.v_pool = torch.zeros((num_slots, h_kv, d), dtype=dtype, device=self.device)
+        self.host_slots = int(host_slots)
+        self.k_host = self.v_host = None
+        if self.host_slots:
+            self.k_host = torch.zeros((self.host_slots, h_kv, d), dtype=dtype, pin_memory=True)
+            self.v_host = torch.zeros((self.host_slots, h_kv, d), dtype=dtype, pin_memory=True)
+            self.tree.set_host_tier(self.host_slots, self.k_host, self.v_host)
         self.rtt = torch.zeros((max_reqs, max_ctx), dtype=torch.int32, device=self.device)
         self.rows = np.zeros((max_reqs, max_ctx), dtype=np.int32)   # host mirror of rtt
         self.max_ctx = max_ctx
@@ -134,6 +148,9 @@ class RadixRuntime:
         ip = np.zeros(len(rids) + 1, dtype=np.int64)
         ip[1:] = np.cumsum(n)
         toks = np.concatenate(prompts) if prompts else np.zeros(0, np.int32)
+        if self.host_slots:
+            done, pfreed = self.tree.promote_batch(toks, ip)
+            self._log("promote", self.step, tuple(done.tolist()), tuple(pfreed.tolist()))
         pslots, m, nodes = self.tree.match_prefix_batch(toks, ip, cut_full=True, lock=True)
         if self.log is not None:
             for i, rid in enumerate(rids):
@@ -168,6 +185,8 @@ class RadixRuntime:
             rtt_indptr=ip, rtt_src=src))
         L.req_to_token_write(self.rtt, eb.dev["req_pool_idx"], eb.dev["rtt_start"], eb.dev["rtt_indptr"],
                              eb.dev["rtt_src"], int(ip[-1]))
+        if self.host_slots:
+            self.tree.run_moves(self.k_pool, self.v_pool)   # before the scatter writes the freed slots
         self._sync_decode_lengths()
         self._dec_cache = None
         return eb

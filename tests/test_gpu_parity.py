@@ -73,8 +73,8 @@ def _check_outputs(job, got, tol):
     return worst
 
 
-def _check_host(job, runner):
-    ref = run_trace(job)
+def _check_host(job, runner, host_slots=0):
+    ref = run_trace(job, host_slots=host_slots)
     assert len(runner.log) == len(ref["log"])
     for a, b in zip(runner.log, ref["log"]):
         assert a == b
@@ -216,6 +216,70 @@ def test_small_trace_every_output(name):
         assert any(e[0] == "evict" for e in runner.log)
     if name == "self_consistency_gqa16_zero_branch":
         assert 0 in job.notes["branch_lens"]
+
+
+@pytest.mark.parametrize("host_slots", [300, 20000])
+def test_small_trace_host_tier_every_output(host_slots):
+    """Evicting multi-turn trace with a host tier: events and dumps equal the oracle's replay
+    (rules H1-H5), and every output, including those over promoted prefixes, matches
+    attention recomputed from scratch."""
+    job = SMALL["multi_turn_evicting"]()
+    say(f"trace multi_turn_evicting with a host tier of {host_slots} rows")
+    runner, got = _collect(job, runner_kw=dict(host_slots=host_slots))
+    _check_host(job, runner, host_slots)
+    worst = _check_outputs(job, got, TOL[job.dtype])
+    st = runner.rt.tree.stats()
+    say(f"  checked {len(got)} outputs, worst max-abs {worst:.3g}; demoted {st['demoted_tokens']} "
+        f"promoted {st['promoted_tokens']}")
+    assert st["demoted_tokens"] > 0 and st["promoted_tokens"] > 0 and st["pending_moves"] == 0
+    plain = run_trace(job)
+    assert run_trace(job, host_slots=host_slots)["computed"] < plain["computed"]
+
+
+def test_kv_moves_bit_exact():
+    """Demotion copies pool rows to the pinned host tier and promotion copies them back,
+    bit for bit, in the tree's order (bf16 [*, 8, 128] and fp32 [*, 4, 64])."""
+    from prefix_shared_kv_extend_amd import _lib
+    g = torch.Generator().manual_seed(3)
+    for dt, h, d in ((torch.bfloat16, 8, 128), (torch.float32, 4, 64)):
+        say(f"kv moves: {dt} rows [{h}, {d}]")
+        S, H = 600, 700
+        kp = torch.randn((S, h, d), generator=g).to(dt).cuda()
+        vp = torch.randn((S, h, d), generator=g).to(dt).cuda()
+        kh = torch.zeros((H, h, d), dtype=dt, pin_memory=True)
+        vh = torch.zeros((H, h, d), dtype=dt, pin_memory=True)
+        t = _lib.Tree(S)
+        t.set_host_tier(H, kh, vh)
+        seqs = [list(range(i * 1000, i * 1000 + 150)) for i in range(4)]
+        slots = [t.alloc_slots(150) for _ in seqs]
+        for q, sl in zip(seqs, slots):
+            t.insert(q, sl)
+        want_k = {i: kp[torch.from_numpy(sl).long().cuda()].cpu() for i, sl in enumerate(slots)}
+        want_v = {i: vp[torch.from_numpy(sl).long().cuda()].cpu() for i, sl in enumerate(slots)}
+        freed = t.evict_lru(450)                       # three sequences go to the host
+        assert len(freed) == 450 and t.stats()["host_tokens"] == 450
+        t.run_moves(kp, vp)
+        torch.cuda.synchronize()
+        dump = {d_[5][0]: d_ for d_ in t.dump()}
+        for i, q in enumerate(seqs):
+            sl = np.array(dump[q[0]][6])
+            if sl[0] < 0:
+                idx = torch.from_numpy(-1 - sl).long()
+                assert torch.equal(kh[idx], want_k[i]) and torch.equal(vh[idx], want_v[i])
+        kp[torch.from_numpy(freed).long().cuda()] = 0     # the freed rows get reused
+        vp[torch.from_numpy(freed).long().cuda()] = 0
+        ip = np.cumsum([0] + [150] * 4)
+        done, fr = t.promote_batch(np.concatenate([np.asarray(q, np.int32) for q in seqs]), ip)
+        assert int(done.sum()) == 450
+        t.run_moves(kp, vp)
+        torch.cuda.synchronize()
+        for i, q in enumerate(seqs):
+            m, sl, _ = t.match_prefix(q)
+            if m == 150:
+                idx = torch.from_numpy(sl).long().cuda()
+                assert torch.equal(kp[idx].cpu(), want_k[i]) and torch.equal(vp[idx].cpu(), want_v[i])
+        assert t.stats()["host_tokens"] + t.stats()["cached_tokens"] == 600
+    assert _lib.device_errors() == 0
 
 
 def test_bf16_output_dtype():
