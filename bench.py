@@ -244,6 +244,62 @@ def scheduler_ablation():
     return out
 
 
+def host_tier_measure(dev):
+    """Host-memory KV tier. Hit rate: the multi-turn trace (512 sessions, GQA 32/8) with the
+    device pool cut to 30% of its distinct tokens, replayed on the tree alone (the runtime's
+    sequence of tree calls) without a tier and with tiers of 25% and 50% of the distinct
+    tokens. Bandwidth: 65536 tokens of 32 x 128 bf16 K and V (1 GiB each way) demoted to the
+    pinned tier and promoted back by the move kernels, HIP events on the current stream."""
+    import torch
+    from prefix_shared_kv_extend_amd import _lib
+    from prefix_shared_kv_extend_amd.driver import tree_replay
+    from workloads import configs
+    job = configs.multi_turn(pool_frac=0.3)
+    uniq = job.notes["total_unique"]
+    prompt = sum(r.n for r in job.requests)
+    out = {"workload": f"multi_turn: 512 sessions, pool {job.num_slots} slots = 30% of {uniq} distinct tokens",
+           "prompt_tokens": prompt}
+    for name, frac in (("no_tier", 0.0), ("tier_25pct", 0.25), ("tier_50pct", 0.5)):
+        hs = int(frac * uniq)
+        _, _, tree, computed = tree_replay(job, hs)
+        st = tree.stats()
+        out[name] = {"host_slots": hs, "computed": computed, "hit_rate": 1 - computed / prompt,
+                     "demoted": st["demoted_tokens"], "promoted": st["promoted_tokens"]}
+    n, h, d = 65536, 32, 128
+    g = torch.Generator(device=dev).manual_seed(5)
+    kp = torch.randn((n, h, d), generator=g, device=dev).to(torch.bfloat16)
+    vp = torch.randn((n, h, d), generator=g, device=dev).to(torch.bfloat16)
+    kh = torch.empty((n, h, d), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty_like(kh, pin_memory=True)
+    t = _lib.Tree(n)
+    t.set_host_tier(n, kh, vh)
+    seq = 1024
+    toks = np.arange(n, dtype=np.int32)
+    for i in range(n // seq):
+        t.insert(toks[i * seq: (i + 1) * seq], t.alloc_slots(seq))
+    ip = np.arange(0, n + 1, seq, dtype=np.int64)
+    times = {"demote": [], "promote": []}
+    for rep_i in range(3):
+        for kind in ("demote", "promote"):
+            if kind == "demote":
+                t.evict_lru(n)
+            else:
+                t.promote_batch(toks, ip)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            t.run_moves(kp, vp)
+            b.record()
+            torch.cuda.synchronize()
+            if rep_i:
+                times[kind].append(a.elapsed_time(b) * 1e-3)
+    nbytes = n * 2 * h * d * 2
+    for kind, v in times.items():
+        out[f"{kind}_gbs"] = nbytes / (sum(v) / len(v)) / 1e9
+    out["moved_bytes"] = nbytes
+    assert _lib.device_errors() == 0
+    return out
+
+
 def cpu_baseline(job, seconds):
     """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
     import torch
@@ -373,6 +429,7 @@ def main():
         "roofline": roof,
     }
     out["scheduler"] = scheduler_ablation()
+    out["host_tier"] = host_tier_measure(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)

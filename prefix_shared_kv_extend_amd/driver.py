@@ -84,3 +84,70 @@ class JobRunner:
                     for rid, row in zip(st.finish, rows):
                         self.final_rows[rid] = row.tolist()
         return self
+
+
+def tree_replay(job, host_slots: int = 0):
+    """The runtime's tree-side sequence for a whole trace, without device work: per step,
+    promote (with a host tier), match and lock the extend batch, one allocation with
+    eviction, insert and move the locks; one decode allocation per step; insert and unlock
+    at finish. Moves are taken and dropped. Returns (event log, final slot rows, tree,
+    computed prompt tokens), the log in the runtime's format."""
+    from . import _lib as L
+    tree = L.Tree(job.num_slots)
+    if host_slots:
+        tree.set_host_tier(host_slots)
+    log, rows, held, computed = [], {}, {}, 0
+    for si, st in enumerate(job.steps):
+        if st.extend:
+            prompts = [job.requests[rid].prompt for rid in st.extend]
+            ip = np.zeros(len(prompts) + 1, dtype=np.int64)
+            ip[1:] = np.cumsum([len(p) for p in prompts])
+            toks = np.concatenate(prompts)
+            if host_slots:
+                done, pfreed = tree.promote_batch(toks, ip)
+                log.append(("promote", si, tuple(done.tolist()), tuple(pfreed.tolist())))
+            pslots, m, nodes = tree.match_prefix_batch(toks, ip, cut_full=True, lock=True)
+            for i, rid in enumerate(st.extend):
+                log.append(("match", rid, int(m[i]), int(nodes[i])))
+            n = np.diff(ip)
+            new, freed = tree.alloc_slots_evict(int((n - m).sum()))
+            if len(freed):
+                log.append(("evict", si, tuple(freed.tolist())))
+            log.append(("alloc", si, tuple(new.tolist())))
+            off, flat = 0, []
+            for i, rid in enumerate(st.extend):
+                mi, qi = int(m[i]), int(n[i] - m[i])
+                rows[rid] = pslots[ip[i]: ip[i] + mi].tolist() + new[off: off + qi].tolist()
+                flat.append(np.asarray(rows[rid], dtype=np.int32))
+                off += qi
+                computed += qi
+            tslots, existing, inodes = tree.insert_batch(toks, np.concatenate(flat), ip)
+            for i, rid in enumerate(st.extend):
+                log.append(("insert", rid, int(existing[i]), int(inodes[i])))
+                rows[rid] = tslots[ip[i]: ip[i + 1]].tolist()
+            tree.lock_ref_batch(inodes, +1)
+            tree.lock_ref_batch(nodes, -1)
+            for i, rid in enumerate(st.extend):
+                held[rid] = int(inodes[i])
+        if st.decode:
+            new, freed = tree.alloc_slots_evict(len(st.decode))
+            if len(freed):
+                log.append(("evict", si, tuple(freed.tolist())))
+            log.append(("alloc", si, tuple(new.tolist())))
+            for i, rid in enumerate(st.decode):
+                rows[rid].append(int(new[i]))
+        if st.finish:
+            full = [np.concatenate([job.requests[rid].prompt,
+                                    job.requests[rid].output[: len(rows[rid]) - job.requests[rid].n]])
+                    for rid in st.finish]
+            ip = np.zeros(len(full) + 1, dtype=np.int64)
+            ip[1:] = np.cumsum([len(f) for f in full])
+            tslots, existing, inodes = tree.insert_batch(
+                np.concatenate(full), np.concatenate([np.asarray(rows[r], np.int32) for r in st.finish]), ip)
+            for i, rid in enumerate(st.finish):
+                log.append(("insert", rid, int(existing[i]), int(inodes[i])))
+                rows[rid] = tslots[ip[i]: ip[i + 1]].tolist()
+            tree.lock_ref_batch([held.pop(rid) for rid in st.finish], -1)
+        if host_slots:
+            tree.take_moves()
+    return log, rows, tree, computed

@@ -263,74 +263,19 @@ def test_host_tier_errors(L):
     assert lib.rax_set_host_tier(t._h, 4, ctypes.c_void_p(12345), None) == L.EINVAL
 
 
-def _lifecycle_with_tier(L, job, host_slots):
-    """The runtime's trace lifecycle on the C++ tree alone (promote, match, allocate, insert,
-    decode allocation, finish), moves taken and dropped: no device data here."""
-    tree = L.Tree(job.num_slots)
-    tree.set_host_tier(host_slots)
-    log, rows, held = [], {}, {}
-    for si, st in enumerate(job.steps):
-        pend = []
-        if st.extend:
-            toks = [job.requests[rid].prompt for rid in st.extend]
-            ip = np.cumsum([0] + [len(t) for t in toks])
-            done, fr = tree.promote_batch(np.concatenate(toks), ip)
-            log.append(("promote", si, tuple(done.tolist()), tuple(fr.tolist())))
-        for rid in st.extend:
-            r = job.requests[rid]
-            m, ps, node = tree.match_prefix(r.prompt)
-            if m == r.n:
-                m -= 1
-                ps = ps[:m]
-            log.append(("match", rid, m, node))
-            tree.lock_ref(node, +1)
-            held[rid] = node
-            pend.append((rid, m, ps.tolist()))
-        if st.extend:
-            new, freed = tree.alloc_slots_evict(sum(job.requests[rid].n - m for rid, m, _ in pend))
-            if len(freed):
-                log.append(("evict", si, tuple(freed.tolist())))
-            log.append(("alloc", si, tuple(new.tolist())))
-            off = 0
-            for rid, m, ps in pend:
-                k = job.requests[rid].n - m
-                rows[rid] = ps + new[off: off + k].tolist()
-                off += k
-        for rid in st.extend:
-            r = job.requests[rid]
-            ex, node, ts = tree.insert(r.prompt, rows[rid][: r.n])
-            log.append(("insert", rid, ex, node))
-            rows[rid][: r.n] = ts.tolist()
-            tree.lock_ref(node, +1)
-            tree.lock_ref(held[rid], -1)
-            held[rid] = node
-        if st.decode:
-            new, freed = tree.alloc_slots_evict(len(st.decode))
-            if len(freed):
-                log.append(("evict", si, tuple(freed.tolist())))
-            log.append(("alloc", si, tuple(new.tolist())))
-            for i, rid in enumerate(st.decode):
-                rows[rid].append(int(new[i]))
-        for rid in st.finish:
-            r = job.requests[rid]
-            k = len(rows[rid]) - r.n
-            ex, node, ts = tree.insert(np.concatenate([r.prompt, r.output[:k]]), rows[rid])
-            log.append(("insert", rid, ex, node))
-            rows[rid] = ts.tolist()
-            tree.lock_ref(held.pop(rid), -1)
-        tree.take_moves()
-    return log, rows, tree
-
-
-@pytest.mark.parametrize("host_slots", [300, 20000])
+@pytest.mark.parametrize("host_slots", [0, 300, 20000])
 def test_trace_lifecycle_with_tier_matches_oracle(L, host_slots):
+    """The runtime's tree-side sequence (driver.tree_replay) equals the oracle's replay."""
     from oracle.runner import run_trace
     from workloads import configs
     job = configs.multi_turn(n_sessions=12, max_depth=3, median=40, lo=4, hi=150, system=30, h_q=8, h_kv=2,
                              max_running=6, max_extend_tokens=400)
+    from prefix_shared_kv_extend_amd.driver import tree_replay
     ref = run_trace(job, host_slots=host_slots)
-    log, rows, tree = _lifecycle_with_tier(L, job, host_slots)
+    log, rows, tree, computed = tree_replay(job, host_slots)
     assert log == ref["log"] and rows == ref["rows"] and tree.dump() == ref["dump"]
-    st = tree.stats()
-    assert st["demoted_tokens"] > 0 and st["promoted_tokens"] > 0
-    assert ref["computed"] < run_trace(job)["computed"]       # the tier saves prefill work
+    assert computed == ref["computed"]
+    if host_slots:
+        st = tree.stats()
+        assert st["demoted_tokens"] > 0 and st["promoted_tokens"] > 0
+        assert ref["computed"] < run_trace(job)["computed"]   # the tier saves prefill work
