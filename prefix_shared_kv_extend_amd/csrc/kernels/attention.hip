@@ -85,7 +85,7 @@ struct AttnArgs {
   int32_t shared_only;        // 1: only the keys a block's requests share; always write partials
   float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
   int32_t n_chunk;            // most own-part key chunks per (request, KV head)
-  int32_t own_fused;          // own part merges in-workgroup and writes O (own_merge_kernel)
+  int32_t own_fused;          // 0: own_kernel + merge_kernel; 1: own_merge_kernel writes O
 };
 
 template <typename T, int D, int NW, int RT, int KS>
@@ -811,19 +811,21 @@ __device__ __forceinline__ float piece_elem(piece_t<T, E> r, int e) {
 // minimum over the block's requests of their key counts (0 for a request whose row or
 // length is invalid) and of the shared_len hints between neighbours (the block's first
 // request has none). One lane per request (a block holds at most 64); wave-uniform result.
-__device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, int lane) {
+__device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, int lane, int* row0 = nullptr) {
   const int64_t qa = rb * a.bm / a.g;
   int64_t qb = qa + a.bm / a.g;
   if (qb > a.batch) qb = a.batch;
   int v = 1 << 30;
+  int row = 0;
   const int64_t r = qa + lane;
   if (r < qb) {
-    const int row = a.req_pool_idx[r];
+    row = a.req_pool_idx[r];
     int m = a.kv_len[r];
     if (row < 0 || row >= a.rtt_rows || m < 0 || m > a.rtt_stride) m = 0;
     const int sh = lane == 0 ? (1 << 30) : (a.shared_len ? a.shared_len[r] : 0);
     v = min(m, sh);
   }
+  if (row0) *row0 = uni(row);  // the block's first request's req_to_token row (lane 0)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
   return uni(max(v, 0));
@@ -1221,6 +1223,275 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   }
 }
 
+// Shared-prefix part of split decode, bf16 with D = 128: the keys every request of a
+// 64-row block shares (positions [0, L) of the block's first request's slot row), cut
+// into nsplit ranges of whole tiles; partials in attn_kernel's layout. attn_kernel
+// stages one tile at a time through registers, so each tile costs a full memory round
+// trip, and with one workgroup per CU nothing hides it. Here a workgroup issues the K
+// and V rows of up to kShTiles tiles at once straight into LDS (16-byte global-to-LDS
+// loads that hold no registers), then computes the first two tiles while the last two
+// may still be arriving. Eight waves: two 32-row tiles x four key groups; the 32-key
+// halves of a round's tiles go round-robin to the key groups, whose softmax states
+// combine in LDS at the end. (Running the requests' own keys in the same workgroups,
+// while the tiles arrive, measured slower: with eight waves per CU each own-key stream
+// is a chain of round trips that the separate own-part kernel's 16 waves per CU hide.)
+// LDS layout: row-major [key][D] per tile, the 16-byte chunks of row r XOR-swizzled by
+// 2 (r % 8), so that K fragment reads (32 rows x 2 chunks) and transposing V reads
+// (8 rows x 4 chunks) spread evenly over the banks; a lane's global address selects the
+// chunk that belongs at its fixed LDS position. The V^T fragments of O^T = V^T P^T come
+// from ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of
+// the 8-byte pieces addressed by lanes i / 4 + 4e (e = 0..3). Lane p therefore
+// addresses key kb + p / 4, dims d0 + 4 (p % 4), and lane i ends up with dim d0 + i of
+// keys kb .. kb + 3.
+constexpr int kShTiles = 4;
+__device__ __forceinline__ int sh_swz(int r) { return 2 * (r & 7); }
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
+// Written as asm so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not wait for every one in flight before each later LDS read: the kernel
+// waits for them itself (s_waitcnt vmcnt, in issue order).
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+template <int D>
+__global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
+  static_assert(D == 128, "the swizzle assumes 16 chunks per row");
+  constexpr int NW = 8, NKG = 4;       // waves; key groups
+  constexpr int BM = 64;
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RB = D * 2;            // bytes per row
+  constexpr int TB = BN * RB;          // bytes per K (or V) tile
+  constexpr int RPI = 1024 / RB;       // rows per 1 KB global-to-LDS instruction
+  constexpr int NI = BN / RPI;         // instructions per tile
+  constexpr int NKS = D / 16;
+  __shared__ __align__(16) char kv[2 * kShTiles * TB];  // K tiles, then V tiles
+  __shared__ int32_t slot[kShTiles * BN];
+  const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)kv;  // LDS byte address
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wrow = wave & 1, wkey = wave >> 1;  // 32-row tile, key group
+  const int jrow = lane & 31, half = lane >> 5;
+  const int64_t item = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  const int split = (int)(item % a.nsplit);
+  const int64_t rb = (item / a.nsplit) % a.n_rb;
+  const int h = (int)(item / ((int64_t)a.nsplit * a.n_rb));
+  const int64_t G0 = rb * BM;
+  const int64_t qa = G0 / a.g;
+  int64_t qb = qa + BM / a.g;
+  if (qb > a.batch) qb = a.batch;
+
+  // Q fragments of this lane's row (B operand of S^T = K Q^T), issued first
+  const int R = wrow * 32 + jrow;
+  const int64_t Gr = G0 + R;
+  const int64_t t_row = Gr / a.g;
+  const bool row_ok = t_row < qb;
+  const int hq = h * a.g + (int)(Gr % a.g);
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((row_ok ? t_row : qa) * a.h_q + hq) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
+  const bool all_rows_ok = __all(row_ok);
+
+  int row0;
+  const int L = block_shared_len(a, rb, lane, &row0);  // 0 if the first request's row is invalid
+  const int n_sh = (L + BN - 1) / BN;
+  const int t_begin = (int)(((int64_t)n_sh * split) / a.nsplit);
+  const int t_end = (int)(((int64_t)n_sh * (split + 1)) / a.nsplit);
+  const int64_t row_bytes = (int64_t)a.h_kv * RB;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
+
+  // slot ids, then every K and V row of the round's tiles into LDS
+  auto issue = [&](int tb, int nt) {
+    for (int i = tid; i < nt * BN; i += 64 * NW) {
+      const int pos = tb * BN + i;
+      const bool in = pos < L;
+      int sv = a.rtt[in ? (int64_t)row0 * a.rtt_stride + pos : 0];
+      if (in && (sv < 0 || sv >= a.num_slots)) {
+        flag_error(RAX_DEVERR_SLOT);
+        sv = -1;
+      }
+      slot[i] = in ? sv : -1;
+    }
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+#pragma unroll
+      for (int q = wave; q < NI; q += NW) {
+        const int r = q * RPI + lane / CH;
+        const int sv = slot[t * BN + r];
+        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes + (((lane % CH) ^ sh_swz(r)) * 16);
+        lds_load16(kbase + off, uni(kv_lds + t * TB + q * 1024));
+        lds_load16(vbase + off, uni(kv_lds + (kShTiles + t) * TB + q * 1024));
+      }
+    }
+  };
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  for (int tb = t_begin; tb < t_end; tb += kShTiles) {
+    const int nt = min(kShTiles, t_end - tb);
+    issue(tb, nt);
+    // each wave issued 2 * NI / NW loads per tile, in tile order, and they retire in order
+    static_assert(2 * NI / NW == 4 && kShTiles == 4, "wait counts below");
+    const int last_cnt = min(BN, L - (tb + nt - 1) * BN);
+    for (int part = 0; part < 2; ++part) {
+      const int t0 = part * 2, t1 = min(nt, t0 + 2);  // tiles of this part
+      if (t0 >= nt) break;
+      if (part == 0 && nt == 4) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8): tiles 2, 3 may fly
+      else if (part == 0 && nt == 3) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0);
+      // a plain barrier: __syncthreads' release fence would wait for every load in flight
+      asm volatile("s_barrier" ::: "memory");
+      // rows past L read slot 0: zero them (their scores are masked; zeros keep P.V finite)
+      if (last_cnt < BN && nt - 1 < t1) {
+        for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
+          const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
+          *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kv + kShTiles * TB + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+      }
+      // 32-key halves 2 t0 .. 2 t1 - 1 of the round, round-robin over the key groups
+      for (int j = 2 * t0 + wkey; j < 2 * t1; j += NKG) {
+      const int t = j >> 1, sub = j & 1;
+      const int cnt = min(BN, L - (tb + t) * BN);
+      const char* kt = kv + t * TB;
+      const char* vt = kv + (kShTiles + t) * TB;
+      // S^T over this wave's 32 keys: row kr of the tile, dims ks*16 + half*8
+      f32x16 sc = f32x16{};
+      const int kr = sub * 32 + jrow;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(kt + kr * RB + (((2 * ks + half) ^ sh_swz(kr)) * 16));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sc, 0, 0, 0);
+      }
+      // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
+      const bool unmasked = cnt == BN && all_rows_ok;
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = sc[r];
+        if (!unmasked) {
+          const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          v = row_ok && key < cnt ? v : kNegInf;
+        }
+        sc[r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      // lazy rescale, as in attn_kernel: the reference moves only when a row's maximum
+      // exceeds it by more than 2^kLazy
+      if (__any(mx > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
+        sc[r] = p;
+        psum += p;
+      }
+      psum += __shfl_xor(psum, 32);
+      l_run += psum;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+      // O^T += V^T P^T; transposing reads give lane l dim dt*32 + l%32 of 4 keys each
+      const int pl = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int d0 = dt * 32 + dsub * 16 + 4 * (pl & 3);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int key = sub * 32 + kh * 16 + 4 * half + (pl >> 2);
+          const char* p0 = vt + key * RB + (((d0 >> 3) ^ sh_swz(key)) * 16) + (d0 & 7) * 2;
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * RB));
+          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kh], acc[dt], 0, 0, 0);
+        }
+      }
+      }
+    }
+    __syncthreads();  // the next round overwrites the tiles
+  }
+
+  // key groups 1..3 hand (m, l, acc) to group 0 over LDS
+  constexpr int NV = (D / 32) * 16 + 2;
+  static_assert((NKG - 1) * 2 * NV * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
+  float* xs = reinterpret_cast<float*>(kv);
+  if (wkey > 0) {
+    const int base = ((wkey - 1) * 2 + wrow) * NV;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[(base + dt * 16 + r) * 64 + lane] = acc[dt][r];
+    xs[(base + NV - 2) * 64 + lane] = m_run;
+    xs[(base + NV - 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (wkey > 0) return;
+  {
+    float m = m_run;
+#pragma unroll
+    for (int k = 1; k < NKG; ++k) m = fmaxf(m, xs[(((k - 1) * 2 + wrow) * NV + NV - 2) * 64 + lane]);
+    if (m != kNegInf) {
+      const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+      l_run *= a0;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= a0;
+#pragma unroll
+      for (int k = 1; k < NKG; ++k) {
+        const int base = ((k - 1) * 2 + wrow) * NV;
+        const float mk = xs[(base + NV - 2) * 64 + lane];
+        const float ak = mk == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk - m);
+        l_run += xs[(base + NV - 1) * 64 + lane] * ak;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] += xs[(base + dt * 16 + r) * 64 + lane] * ak;
+      }
+      m_run = m;
+    }
+  }
+  if (!row_ok) return;
+  if (l_run > 0.f) {
+    float* wacc = a.ws + (item * BM + R) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * half;
+        *reinterpret_cast<float4*>(wacc + d0) =
+            make_float4(acc[dt][rg * 4 + 0], acc[dt][rg * 4 + 1], acc[dt][rg * 4 + 2], acc[dt][rg * 4 + 3]);
+      }
+  }
+  if (half == 0) {  // (m, l) of the row; l == 0 means "no keys here"
+    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
+    float* wml = a.ws + n_items * BM * (int64_t)D + (item * BM + R) * 2;
+    wml[0] = m_run;
+    wml[1] = l_run;
+  }
+}
+
 // ------------------------------------------------------------------ host side
 struct Shape {
   int nw, rt, pd, ks;
@@ -1304,6 +1575,13 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st) {
     }
   }
   if constexpr (sizeof(T) == 2 && kDecode) {
+    if constexpr (D == 128) {
+      if (a.shared_only) {  // shared part of split decode
+        const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
+        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a);
+        return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+      }
+    }
     if (s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 2) rc = launch_one<T, D, kDecode, 4, 1, 1, 2>(a, st);
   }
   if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 1)
@@ -1316,7 +1594,7 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
   rax_status rc = launch_attn<T, D, kDecode>(a, s, st);
   if (rc != RAX_OK) return rc;
   if constexpr (kDecode) {
-    if (a.shared_only && a.own_fused) {
+    if (a.shared_only && a.own_fused == 1) {
       // one workgroup per (request, KV head), n_chunk waves; writes O (no merge kernel)
       const unsigned blocks = (unsigned)((int64_t)a.batch * a.h_kv);
       const dim3 block((unsigned)(64 * a.n_chunk));
@@ -1331,7 +1609,7 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
       }
       return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
     }
-    if (a.shared_only) {
+    if (a.shared_only && a.own_fused == 0) {
       // more chunks per (request, KV head) than one workgroup takes: partials, then merge
       rc = launch_own<T, D>(a, st);
       if (rc != RAX_OK) return rc;
@@ -1358,7 +1636,8 @@ static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_
 struct DecodeLayout {
   int64_t sh_acc, sh_ml, own_acc, own_ml, total;
   int32_t nsplit, n_rb, n_chunk, bm;
-  bool split_decode, own_fused;
+  bool split_decode;
+  int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
@@ -1384,12 +1663,12 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   // few-shot decode, 4096 waves 15.4 us, 8192 waves 20.2 us, 2048 waves 16.7 us.
   constexpr int64_t kOwnWaves = 4096;
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
-  l.n_chunk = (int32_t)std::max<int64_t>(
-      1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnMin - 1) / kOwnMin, (kOwnWaves + pairs - 1) / pairs}));
+  const int64_t by_len = (max_seq_len + kOwnMin - 1) / kOwnMin;
+  l.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>({64 - l.nsplit, by_len, (kOwnWaves + pairs - 1) / pairs}));
   // the chunks of one (request, KV head) fit one workgroup: merge in LDS, no own partials
-  l.own_fused = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds;
+  l.own_mode = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds ? 1 : 0;
   const int64_t sh_items = (int64_t)h_kv * l.n_rb * l.nsplit;
-  const int64_t own_rows = l.own_fused ? 0 : batch * h_kv * l.n_chunk * g;
+  const int64_t own_rows = l.own_mode == 1 ? 0 : batch * h_kv * l.n_chunk * g;
   l.sh_acc = sh_items * l.bm * d;
   l.sh_ml = sh_items * l.bm * 2;
   l.own_acc = own_rows * d;
@@ -1515,7 +1794,7 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
       a.shared_only = 1;
       a.ws_own = w + l.sh_acc + l.sh_ml;
       a.n_chunk = l.n_chunk;
-      a.own_fused = l.own_fused ? 1 : 0;
+      a.own_fused = l.own_mode;
     }
   }
   return dispatch<true>(a, dt, d, s, (hipStream_t)stream);
