@@ -337,6 +337,48 @@ rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v
                                 int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
                                 void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream);
 
+/* One whole decode step in one call: rax_decode_append (slots, row append, K/V
+ * write-back, with any host-tier moves) followed by rax_decode_attention over the rows
+ * as they are after the append, on the same stream; max_seq_len is taken from the host
+ * lengths. Meant for serving loops, where the per-call argument marshalling of two
+ * entry points costs as much host time as the GPU spends on the step: the caller keeps
+ * one argument block per decode batch and updates only what changes (q, k_new, v_new, o,
+ * stream). Fields are as in the two calls; the pool holds the tree's num_slots rows.
+ * Outputs: seq_len (host, incremented), out_slots, out_freed / num_freed, and ws_needed,
+ * the workspace bytes the attention needs. If ws_bytes is smaller, nothing is done and
+ * RAX_EINVAL is returned with ws_needed set (grow the workspace and call again). Other
+ * errors are those of the two calls; an attention error after a successful append leaves
+ * the append done. */
+typedef struct {
+  int32_t batch;
+  int32_t* seq_len;           /* host [batch], in/out */
+  int32_t* out_slots;         /* host [batch] */
+  int32_t* out_freed;         /* host [cap] */
+  int64_t cap;
+  int64_t num_freed;          /* out */
+  size_t ws_needed;           /* out */
+  const int32_t* req_pool_idx; /* device [batch] */
+  int32_t* seq_len_dev;       /* device [batch] */
+  const int32_t* shared_len;  /* device [batch] or NULL */
+  int32_t* req_to_token;      /* device [rtt_rows, rtt_stride] */
+  int64_t rtt_stride;
+  int64_t rtt_rows;
+  const void* q;              /* device [batch, h_q, d] */
+  const void* k_new;          /* device [batch, h_kv, d] */
+  const void* v_new;
+  void* k_pool;               /* device [num_slots, h_kv, d] */
+  void* v_pool;
+  int32_t h_q, h_kv, d;
+  float sm_scale;
+  rax_dtype dt;
+  rax_dtype o_dt;
+  void* o;                    /* device [batch, h_q, d] */
+  void* workspace;
+  size_t ws_bytes;
+  void* stream;
+} rax_decode_step_args;
+rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* args);
+
 /* Workspace bytes that an extend (is_decode = 0, rows = total_q) or decode (is_decode =
  * 1, rows = batch) call with these sizes may use. 0 means the call needs none. */
 size_t rax_attention_workspace_bytes(int32_t is_decode, int64_t rows, int32_t h_q, int32_t h_kv,

@@ -36,6 +36,17 @@ class RaxStats(ctypes.Structure):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
+class DecodeStepArgs(ctypes.Structure):
+    """rax_decode_step_args (include/rax.h)."""
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", _c_i32p), ("out_slots", _c_i32p), ("out_freed", _c_i32p),
+                ("cap", ctypes.c_int64), ("num_freed", ctypes.c_int64), ("ws_needed", ctypes.c_size_t),
+                ("req_pool_idx", _vp), ("seq_len_dev", _vp), ("shared_len", _vp), ("req_to_token", _vp),
+                ("rtt_stride", ctypes.c_int64), ("rtt_rows", ctypes.c_int64), ("q", _vp), ("k_new", _vp),
+                ("v_new", _vp), ("k_pool", _vp), ("v_pool", _vp), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("dt", ctypes.c_int32), ("o_dt", ctypes.c_int32),
+                ("o", _vp), ("workspace", _vp), ("ws_bytes", ctypes.c_size_t), ("stream", _vp)]
+
+
 _SIGS = {
     "rax_status_str": (ctypes.c_char_p, [_i32]),
     "rax_abi_version": (_i32, []),
@@ -57,6 +68,7 @@ _SIGS = {
     "rax_prefix_len_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p]),
     "rax_schedule_order": (_i32, [_vp, _i32, _c_i32p, _c_i64p, _i32, ctypes.c_uint64, _c_i32p, _c_i64p]),
     "rax_tree_stats": (_i32, [_vp, ctypes.POINTER(RaxStats)]),
+    "rax_decode_step": (_i32, [_vp, ctypes.POINTER(DecodeStepArgs)]),
     "rax_set_host_tier": (_i32, [_vp, _i64, _vp, _vp]),
     "rax_promote_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p, _c_i32p, _i64, _c_i64p]),
     "rax_take_moves": (_i32, [_vp, _c_i32p, _c_i32p, _c_i32p, _i64, _c_i64p]),
@@ -201,6 +213,60 @@ class Tree:
             _dtype_code(k_pool), _stream(stream, k_pool))
         _check(st, "rax_decode_append")
         return out, self._freed[: nf.value].copy()
+
+    def decode_step_prepare(self, seq_len, req_to_token, req_pool_idx, seq_len_dev, k_pool, v_pool, h_q,
+                            shared_len=None, sm_scale=None, o_dtype=None):
+        """Argument block of rax_decode_step for one decode batch: everything except the
+        per-step tensors, checked once. seq_len: host int32 [batch] (kept and updated in place)."""
+        import torch
+        n = len(seq_len)
+        _need(isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32 and seq_len.flags.c_contiguous,
+              "seq_len: contiguous host int32 array")
+        _need(k_pool.shape == v_pool.shape and k_pool.dtype == v_pool.dtype and k_pool.is_cuda
+              and k_pool.is_contiguous() and v_pool.is_contiguous() and k_pool.shape[0] == self.num_slots,
+              "pools: contiguous cuda [num_slots, h_kv, d]")
+        _cuda_i32(req_to_token, req_pool_idx, seq_len_dev)
+        _need(req_pool_idx.numel() == n and seq_len_dev.numel() == n, "req_pool_idx, seq_len_dev: [batch]")
+        if shared_len is not None:
+            _cuda_i32(shared_len)
+            _need(shared_len.numel() == n, "shared_len: [batch]")
+        h_kv, d = k_pool.shape[1], k_pool.shape[2]
+        a = DecodeStepArgs()
+        keep = {"seq_len": seq_len, "out": np.empty(max(n, 1), dtype=np.int32),
+                "freed": np.empty(self.num_slots, dtype=np.int32)}
+        a.batch = n
+        a.seq_len = _p32(seq_len)
+        a.out_slots = _p32(keep["out"])
+        a.out_freed = _p32(keep["freed"])
+        a.cap = self.num_slots
+        a.req_pool_idx, a.seq_len_dev = req_pool_idx.data_ptr(), seq_len_dev.data_ptr()
+        a.shared_len = shared_len.data_ptr() if shared_len is not None else None
+        a.req_to_token = req_to_token.data_ptr()
+        a.rtt_stride, a.rtt_rows = req_to_token.shape[1], req_to_token.shape[0]
+        a.k_pool, a.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+        a.h_q, a.h_kv, a.d = int(h_q), int(h_kv), int(d)
+        a.sm_scale = float(sm_scale) if sm_scale is not None else 1.0 / float(d) ** 0.5
+        a.dt = _dtype_code(k_pool)
+        a.o_dt = F32 if o_dtype == torch.float32 else BF16 if o_dtype == torch.bfloat16 else a.dt
+        return a, keep, (n, int(h_q), d), (n, h_kv, d), k_pool.dtype, k_pool.get_device()
+
+    def decode_step(self, prep, q, k_new, v_new, o, workspace, stream=None):
+        """rax_decode_step with a block from decode_step_prepare; sets the per-step tensors.
+        Returns (new slots, freed slots, the workspace bytes the call needed)."""
+        a, keep, qshape, kshape, dtype, dev = prep
+        _need(tuple(q.shape) == qshape and tuple(k_new.shape) == kshape and tuple(v_new.shape) == kshape
+              and tuple(o.shape) == qshape and q.dtype == dtype and k_new.dtype == dtype and v_new.dtype == dtype,
+              "q, o: [batch, h_q, d]; k_new, v_new: [batch, h_kv, d], the pool dtype")
+        a.q, a.k_new, a.v_new, a.o = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), o.data_ptr()
+        a.o_dt = _dtype_code(o)
+        a.workspace = workspace.data_ptr() if workspace is not None else None
+        a.ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        a.stream = _stream(stream, q).value
+        st = self._L.rax_decode_step(self._h, ctypes.byref(a))
+        if st == EINVAL and a.ws_needed > a.ws_bytes:
+            return None, None, int(a.ws_needed)
+        _check(st, "rax_decode_step")
+        return keep["out"][: a.batch], keep["freed"][: a.num_freed], int(a.ws_needed)
 
     # ------------------------------------------------------------ host tier
     def set_host_tier(self, host_slots: int, k_host=None, v_host=None) -> None:

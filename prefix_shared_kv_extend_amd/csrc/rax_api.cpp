@@ -333,6 +333,31 @@ rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* 
   RAX_GUARD_END
 }
 
+rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
+  if (!t || !a || a->batch < 0) return RAX_EINVAL;
+  a->num_freed = 0;
+  a->ws_needed = 0;
+  if (a->batch == 0) return RAX_OK;
+  if (!a->seq_len) return RAX_EINVAL;
+  int32_t max_len = 0;
+  for (int32_t i = 0; i < a->batch; ++i) max_len = std::max(max_len, a->seq_len[i] + 1);
+  a->ws_needed = rax_attention_workspace_bytes(1, a->batch, a->h_q, a->h_kv, a->d, max_len);
+  if (a->ws_needed > a->ws_bytes) return RAX_EINVAL;  // nothing done yet
+  // the attention's argument checks first (a zero-row call checks shapes and types only)
+  if (!a->q || !a->o ||
+      rax_decode_attention(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token, a->rtt_stride,
+                           a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len, 0, max_len, a->h_q, a->h_kv,
+                           a->d, a->sm_scale, a->dt, a->o, a->o_dt, a->workspace, a->ws_bytes, a->stream) != RAX_OK)
+    return RAX_EINVAL;
+  const rax_status s = rax_decode_append(t, a->batch, a->seq_len, a->out_slots, a->out_freed, a->cap, &a->num_freed,
+                                         a->req_pool_idx, a->seq_len_dev, a->req_to_token, a->rtt_stride, a->rtt_rows,
+                                         a->k_new, a->v_new, a->k_pool, a->v_pool, a->h_kv, a->d, a->dt, a->stream);
+  if (s != RAX_OK) return s;
+  return rax_decode_attention(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token, a->rtt_stride,
+                              a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len, a->batch, max_len, a->h_q,
+                              a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt, a->workspace, a->ws_bytes, a->stream);
+}
+
 rax_status rax_set_host_tier(rax_tree* t, int64_t host_slots, void* k_host, void* v_host) {
   if (!t || host_slots < 0 || host_slots >= (int64_t(1) << 31) || (k_host == nullptr) != (v_host == nullptr) ||
       (host_slots == 0 && k_host))

@@ -11,7 +11,8 @@ evicting when memory is short, run it, update the tree; hustzhy SGLang post,
            extend attention over reused prefix + causal suffix; then insert every
            prompt (rax_insert_batch) and move the locks to the new nodes.
   decode   allocate one slot per request, append it to the rows, write the new
-           tokens' K/V, run decode attention over the whole rows.
+           tokens' K/V, run decode attention over the whole rows: one native call
+           (rax_decode_step) whose argument block is built once per decode batch.
   finish   insert prompt + generated tokens, unlock.
 
 With a host tier (host_slots > 0; hustzhy SGLang post, §6.1, HiCache's host-memory
@@ -59,6 +60,17 @@ class DecodeBatch:
     seq_len: np.ndarray
     max_seq_len: int
     dev: dict = field(default_factory=dict)
+    key: tuple = None
+
+
+@dataclass
+class _DecodeState:
+    """The running decode batch while its composition is unchanged."""
+    key: tuple                    # request ids, in batch order
+    req_rows: np.ndarray          # their req_to_token rows
+    inv: dict                     # device int32 views: req_pool_idx, shared_len, seq_len
+    lens: np.ndarray              # host lengths (slots in each row), updated by every step
+    prep: tuple                   # rax_decode_step argument block (Tree.decode_step_prepare)
 
 
 class RadixRuntime:
@@ -89,7 +101,7 @@ class RadixRuntime:
         self.step = 0                        # label of the current step in the event log (set by the caller)
         self.timers = None                   # {"extend": [...], "decode": [...]} of (start, end) events, if set
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
-        self._dec_cache = None               # (rids tuple, rows, device views) while the decode batch is unchanged
+        self._dec_cache = None               # _DecodeState while the decode batch is unchanged
 
     # ------------------------------------------------------------------ helpers
     def _upload(self, parts: dict) -> dict:
@@ -130,8 +142,8 @@ class RadixRuntime:
 
     def seq_len(self, rid: int) -> int:
         """Current number of slots in the request's row."""
-        if self._dec_cache is not None and rid in self._dec_cache[0]:
-            return int(self._dec_cache[3][self._dec_cache[0].index(rid)])
+        if self._dec_cache is not None and rid in self._dec_cache.key:
+            return int(self._dec_cache.lens[self._dec_cache.key.index(rid)])
         return self.len_of[rid]
 
     def slot_row(self, rid: int) -> np.ndarray:
@@ -233,52 +245,49 @@ class RadixRuntime:
     def _sync_decode_lengths(self):
         """Write the decode batch's cached lengths back to the per-request table."""
         if self._dec_cache is not None:
-            key, _, _, lens = self._dec_cache
-            for i, r in enumerate(key):
-                self.len_of[r] = int(lens[i])
+            for r, n in zip(self._dec_cache.key, self._dec_cache.lens.tolist()):
+                self.len_of[r] = n
 
     def begin_decode(self, rids) -> DecodeBatch:
         """Describe the next decode step of `rids` (one new token each): db.seq_len holds the
         lengths after the step, so token i of the batch sits at position db.seq_len[i] - 1.
         Nothing changes until run_decode."""
         key = tuple(rids)
-        if self._dec_cache is None or self._dec_cache[0] != key:
+        ds = self._dec_cache
+        if ds is None or ds.key != key:
             self._sync_decode_lengths()
             req_rows = np.array([self.row_of[r] for r in rids], dtype=np.int32)
             nodes = [self.node_of[r] for r in rids]
             inv = self._upload(dict(req_pool_idx=req_rows, shared_len=self.tree.lca_depths(nodes),
                                     seq_len=np.zeros(len(rids))))
             lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
-            self._dec_cache = (key, req_rows, inv, lens)
-        _, req_rows, inv, lens = self._dec_cache
-        seq_len = lens + 1
+            prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
+                                                 self.v_pool, self.h_q, shared_len=inv["shared_len"])
+            ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep)
+        seq_len = ds.lens + 1
         max_seq = int(seq_len.max()) if len(seq_len) else 0
         if max_seq > self.max_ctx:
             raise ValueError("sequence longer than the req_to_token rows")
-        db = DecodeBatch(list(rids), seq_len, max_seq)
-        db.dev = inv
+        db = DecodeBatch(list(rids), seq_len, max_seq, ds.inv, ds.key)
         return db
 
     def run_decode(self, db: DecodeBatch, q, k_new, v_new, o) -> None:
-        """Allocate the new tokens' slots, append them to the rows, write their K/V into the
-        pools (one native call, one kernel), then run decode attention."""
-        key, req_rows, inv, lens = self._dec_cache
-        if key != tuple(db.rids):
+        """One decode step in one native call (rax_decode_step): allocate the new tokens'
+        slots, append them to the rows, write their K/V into the pools, run decode attention."""
+        ds = self._dec_cache
+        if ds is None or db.key is not ds.key:
             raise ValueError("run_decode: batch differs from the last begin_decode")
-        new, freed = self.tree.decode_append(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], k_new, v_new,
-                                             self.k_pool, self.v_pool)
+        ev = self._event_pair("decode")
+        new, freed, need = self.tree.decode_step(ds.prep, q, k_new, v_new, o, self._ws)
+        if new is None:                      # workspace too small: nothing was done
+            new, freed, need = self.tree.decode_step(ds.prep, q, k_new, v_new, o, self._workspace(need))
+        if ev:
+            ev[1].record()
         if self.log is not None:
             if len(freed):
                 self._log("evict", self.step, tuple(freed.tolist()))
             self._log("alloc", self.step, tuple(new.tolist()))
-        self.rows[req_rows, lens - 1] = new
-        ws = self._workspace(L.attention_workspace_bytes(True, len(db.rids), self.h_q, self.h_kv, self.d,
-                                                         db.max_seq_len))
-        ev = self._event_pair("decode")
-        L.decode_attention(q, self.k_pool, self.v_pool, self.rtt, inv["req_pool_idx"], inv["seq_len"],
-                           db.max_seq_len, o, workspace=ws, shared_len=inv["shared_len"])
-        if ev:
-            ev[1].record()
+        self.rows[ds.req_rows, ds.lens - 1] = new
 
     # ------------------------------------------------------------------- finish
     def finish(self, rid: int, tokens) -> np.ndarray:

@@ -219,3 +219,25 @@ def test_trace_host_lifecycle_matches_oracle(L, index):
     assert tree.dump() == ref["dump"]
     if index == 4:
         assert any(e[0] == "evict" for e in log)     # the 60% pool really forces eviction
+
+
+def test_decode_step_workspace_check_changes_nothing(L):
+    """rax_decode_step checks the workspace before doing anything: too small -> EINVAL with
+    ws_needed set, and the tree, the host lengths and the slots stay as they were."""
+    import ctypes
+    t = L.Tree(64)
+    seq = np.array([5, 9], dtype=np.int32)
+    a = L.DecodeStepArgs()
+    out = np.zeros(2, np.int32)
+    fr = np.zeros(64, np.int32)
+    a.batch, a.seq_len, a.out_slots, a.out_freed, a.cap = 2, L._p32(seq), L._p32(out), L._p32(fr), 64
+    a.h_q, a.h_kv, a.d, a.dt, a.o_dt, a.sm_scale = 8, 2, 128, L.BF16, L.BF16, 0.1
+    a.rtt_stride, a.rtt_rows = 16, 2
+    for name in ("req_pool_idx", "seq_len_dev", "req_to_token", "q", "k_new", "v_new", "k_pool", "v_pool", "o"):
+        setattr(a, name, 4096)                      # never dereferenced: the call stops first
+    a.workspace, a.ws_bytes = 4096, 16
+    free0 = t.free_count()
+    st = L.lib().rax_decode_step(t._h, ctypes.byref(a))
+    need = L.lib().rax_attention_workspace_bytes(1, 2, 8, 2, 128, 10)
+    assert st == L.EINVAL and a.ws_needed == need > 16
+    assert seq.tolist() == [5, 9] and t.free_count() == free0 and a.num_freed == 0
