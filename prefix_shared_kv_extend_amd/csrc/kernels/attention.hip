@@ -117,6 +117,22 @@ struct __align__(16) Smem {
   int32_t hdr[8];
 };
 
+// Same, for tiles loaded straight into LDS (bf16, D = 128): unpadded, swizzled rows.
+template <typename T, int D, int NW, int RT, int KS>
+struct __align__(16) SmemDma {
+  using C = Cfg<T, D, NW, RT, KS>;
+  T k[2][BN * D];
+  T v[2][BN * D];
+  int32_t slot[4][BN];
+  int32_t bad[4];  // per slot buffer: some key of the tile has no slot
+  int32_t req_m[C::BM];
+  int32_t req_row[C::BM];
+  int32_t req_qo[C::BM + 1];
+  int32_t own[C::BM + 1];
+  int32_t req_sh[C::BM];
+  int32_t hdr[8];
+};
+
 struct TileDesc {
   int kind;  // 0 shared prefix, 1 one request's own prefix, 2 suffix (k_ext rows)
   int cnt;   // valid keys in the tile
@@ -125,6 +141,50 @@ struct TileDesc {
   int req;   // local request index (kind 1)
   int row;   // req_to_token row (kinds 0, 1)
 };
+
+// ---- tiles loaded straight into LDS (bf16, D = 128)
+// A tile is row-major [key][D] in LDS, 256 bytes per key, filled by 16-byte global-to-LDS
+// loads: one instruction moves 64 x 16 bytes (4 keys) to consecutive LDS bytes, so no
+// row padding is possible; instead the 16-byte chunks of row r are XOR-swizzled by
+// 2 (r % 8) (a lane's global address picks the chunk that belongs at its fixed LDS
+// position). K fragment reads (32 rows x 2 chunks) and the transposing V reads (8 rows x
+// 4 chunks) then spread evenly over the banks. The V^T fragments of O^T = V^T P^T come
+// from ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of
+// the 8-byte pieces addressed by lanes i / 4 + 4e (e = 0..3). Lane p therefore addresses
+// key kb + p / 4, dims d0 + 4 (p % 4), and lane i ends up with dim d0 + i of keys
+// kb .. kb + 3. Nothing is written to LDS by the threads, so no transposing stores.
+__device__ __forceinline__ int sh_swz(int r) { return 2 * (r & 7); }
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
+// Written as asm so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not wait for every one in flight before each later LDS read: the kernel
+// waits for them itself (s_waitcnt vmcnt, in issue order).
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// A operand (K rows kr = 32 keys, dims ks*16 + half*8 .. +8) of S^T = K Q^T.
+__device__ __forceinline__ bf16x8 k_frag(const char* kt, int kr, int ks, int half) {
+  return *reinterpret_cast<const bf16x8*>(kt + kr * 256 + (((2 * ks + half) ^ sh_swz(kr)) * 16));
+}
+
+// A operand of O^T = V^T P^T for 32 dims (dt) x 16 keys (kh) of a 32-key half (sub):
+// lane l holds dim dt*32 + l%32 of keys sub*32 + kh*16 + 4*(l/32) + {0..3} and the same
+// + 8, the key order of the P fragments.
+__device__ __forceinline__ bf16x8 vt_frag(const char* vt, int sub, int dt, int kh, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int pl = lane & 15, dsub = (lane >> 4) & 1, half = lane >> 5;
+  const int d0 = dt * 32 + dsub * 16 + 4 * (pl & 3);
+  const int key = sub * 32 + kh * 16 + 4 * half + (pl >> 2);
+  const char* p0 = vt + key * 256 + (((d0 >> 3) ^ sh_swz(key)) * 16) + (d0 & 7) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * 256));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 __device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t) {
   // last r in [0, batch) with qo[r] <= t
@@ -219,7 +279,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   using C = Cfg<T, D, NW, RT, KS>;
   constexpr int BM = C::BM;
   constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ Smem<T, D, NW, RT, KS> sm;
+  // extend, bf16, D = 128: tiles go straight into LDS (see "tiles loaded straight into
+  // LDS"); otherwise they are staged through registers and stored padded / transposed
+  constexpr bool kDma = kBf16 && D == 128 && !kDecode && KS == 1 && RT == 1 && PD == 1;
+  using SM = std::conditional_t<kDma, SmemDma<T, D, NW, RT, KS>, Smem<T, D, NW, RT, KS>>;
+  __shared__ SM sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -432,6 +496,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   // registers -> LDS buffer b (K row-major, V transposed); keys without a slot become zeros
   auto store_tile = [&](int b, int sb, auto set_c) {
     constexpr int set = decltype(set_c)::value;
+    if constexpr (!kDma) {
 #pragma unroll
     for (int p = 0; p < C::KP; ++p) {
       const int key = p * C::KPP + kk;
@@ -458,8 +523,55 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         }
       }
     }
+    }
   };
   auto desc = [&](int tau) { return describe(tau, sm, L, n_sh, n_own, suf0, qb, nreq); };
+
+  // kDma: K and V rows of tile d (slot ids in sm.slot[sb]) straight into LDS buffer b;
+  // keys without a slot read row 0. Each lane's 16 bytes land at LDS row 4q + lane/16,
+  // chunk lane%16.
+  constexpr int kDmaRpi = 4, kDmaNi = BN / kDmaRpi;  // rows per 1 KB instruction, instructions per tile
+  auto dma_tile = [&](const TileDesc& d, int sb, int b, auto) {
+    if constexpr (kDma) {
+    const char* kb = reinterpret_cast<const char*>(d.kind == 2 ? a.k_ext : a.k_pool) + head_off;
+    const char* vb = reinterpret_cast<const char*>(d.kind == 2 ? a.v_ext : a.v_pool) + head_off;
+    const uint32_t kl = lds_addr(&sm.k[b][0]), vl = lds_addr(&sm.v[b][0]);
+#pragma unroll
+    for (int q = wave; q < kDmaNi; q += NW) {
+      const int r = q * kDmaRpi + (lane >> 4);
+      const int sv = sm.slot[sb][r];
+      const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes + (((lane & 15) ^ sh_swz(r)) * 16);
+      lds_load16(kb + off, uni(kl + q * 1024));
+      lds_load16(vb + off, uni(vl + q * 1024));
+    }
+    }
+  };
+  // kDma: wait for this wave's loads, then zero the K and V rows of keys without a slot
+  // (each lane the positions it loaded, so no other wave's load can land after)
+  auto dma_finish = [&](int sb, int b, auto) {
+    if constexpr (kDma) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (uni(sm.bad[sb])) {
+#pragma unroll
+      for (int q = wave; q < kDmaNi; q += NW) {
+        const int r = q * kDmaRpi + (lane >> 4);
+        if (sm.slot[sb][r] < 0) {
+          const int off = r * D * (int)sizeof(T) + (lane & 15) * 16;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(&sm.k[b][0]) + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(&sm.v[b][0]) + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    }
+  };
+  // slot ids of one tile written by the first BN threads (wave 0), with the tile's flag
+  auto put_slot = [&](int sb, int v) {
+    sm.slot[sb][tid] = v;
+    if constexpr (kDma) {
+      const uint64_t bad = __ballot(v < 0);
+      if (tid == 0) sm.bad[sb] = bad != 0;
+    }
+  };
 
   // ---- prologue: slot ids of tiles t_begin .. t_begin+PD, K/V loads of the first PD tiles
   if (tid < BN && t_begin < t_end) {  // all prologue slot loads in one round trip
@@ -472,16 +584,21 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i <= PD; ++i)
-      if (t_begin + i < t_end) sm.slot[(t_begin + i) % NSB][tid] = slot_finish(a, di[i], tid, raw[i]);
+      if (t_begin + i < t_end) put_slot((t_begin + i) % NSB, slot_finish(a, di[i], tid, raw[i]));
   }
   __syncthreads();
   if (t_begin < t_end) {
-    issue_loads(desc(t_begin), t_begin % NSB, true, std::integral_constant<int, 0>{});
-    if constexpr (PD > 1) {
-      const bool live = t_begin + 1 < t_end;
-      issue_loads(desc(live ? t_begin + 1 : t_begin), (t_begin + 1) % NSB, live, std::integral_constant<int, 1>{});
+    if constexpr (kDma) {
+      dma_tile(desc(t_begin), t_begin % NSB, 0, 0);
+      dma_finish(t_begin % NSB, 0, 0);
+    } else {
+      issue_loads(desc(t_begin), t_begin % NSB, true, std::integral_constant<int, 0>{});
+      if constexpr (PD > 1) {
+        const bool live = t_begin + 1 < t_end;
+        issue_loads(desc(live ? t_begin + 1 : t_begin), (t_begin + 1) % NSB, live, std::integral_constant<int, 1>{});
+      }
+      store_tile(0, t_begin % NSB, std::integral_constant<int, 0>{});
     }
-    store_tile(0, t_begin % NSB, std::integral_constant<int, 0>{});
   }
   __syncthreads();
 
@@ -496,7 +613,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     const TileDesc dn = desc(has_next ? tau + PD + 1 : tau);
     const int raw_slot = slot_issue(a, dn, tid < BN ? tid : 0);
     const bool live = tau + PD < t_end;
-    issue_loads(desc(live ? tau + PD : tau), (tau + PD) % NSB, live, std::integral_constant<int, ph>{});
+    if constexpr (kDma) {
+      if (live) dma_tile(desc(tau + 1), (tau + 1) % NSB, buf ^ 1, 0);
+    } else {
+      issue_loads(desc(live ? tau + PD : tau), (tau + PD) % NSB, live, std::integral_constant<int, ph>{});
+    }
 
     // -- does this wave have rows that see any key of the tile?
     bool run = wave_active;
@@ -517,11 +638,13 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         const int sub = KS == 1 ? si : wkey;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sall[si][rt] = f32x16{};
-        const T* kr = &sm.k[buf][(sub * 32 + jrow) * C::KSTRIDE];
+        const T* kr = &sm.k[buf][(sub * 32 + jrow) * (kDma ? D : C::KSTRIDE)];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           if constexpr (kBf16) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
+            bf16x8 af;
+            if constexpr (kDma) af = k_frag(reinterpret_cast<const char*>(&sm.k[buf][0]), sub * 32 + jrow, ks, half);
+            else af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               sall[si][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[rt][ks], sall[si][rt], 0, 0, 0);
@@ -595,13 +718,18 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
               for (int e = 0; e < 8; ++e) pb[rt][kh][e] = (__bf16)s[rt][kh * 8 + e];
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-              const int kb0 = sub * 32 + kh * 16 + 4 * half;
-              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + kb0);
-              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + kb0 + 8);
-              const bf16x8 af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              bf16x8 af;
+              if constexpr (kDma) {
+                af = vt_frag(reinterpret_cast<const char*>(&sm.v[buf][0]), sub, dt, kh, lane);
+              } else {
+                const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
+                const int kb0 = sub * 32 + kh * 16 + 4 * half;
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + kb0);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + kb0 + 8);
+                af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              }
 #pragma unroll
               for (int rt = 0; rt < RT; ++rt)
                 acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[rt][kh], acc[rt][dt], 0, 0, 0);
@@ -624,8 +752,12 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
       }
     }
 
-    if (tau + 1 < t_end) store_tile(buf ^ 1, (tau + 1) % NSB, std::integral_constant<int, (ph + 1) % PD>{});
-    if (has_next && tid < BN) sm.slot[(tau + PD + 1) % NSB][tid] = slot_finish(a, dn, tid, raw_slot);
+    if constexpr (kDma) {
+      if (tau + 1 < t_end) dma_finish((tau + 1) % NSB, buf ^ 1, 0);
+    } else {
+      if (tau + 1 < t_end) store_tile(buf ^ 1, (tau + 1) % NSB, std::integral_constant<int, (ph + 1) % PD>{});
+    }
+    if (has_next && tid < BN) put_slot((tau + PD + 1) % NSB, slot_finish(a, dn, tid, raw_slot));
     __syncthreads();
   };
 
@@ -807,28 +939,46 @@ __device__ __forceinline__ float piece_elem(piece_t<T, E> r, int e) {
   else return __builtin_bit_cast(float, (uint32_t)(r >> (32 * e)));
 }
 
-// Shared length L of decode row block rb, by the rule the shared-part kernel applies: the
-// minimum over the block's requests of their key counts (0 for a request whose row or
-// length is invalid) and of the shared_len hints between neighbours (the block's first
-// request has none). One lane per request (a block holds at most 64); wave-uniform result.
-__device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, int lane, int* row0 = nullptr) {
+// Decode row-block metadata from one round of loads, one lane per request of the block
+// (a block holds at most 64): the request's req_to_token row and key count, raw, and its
+// shared_len hint to the previous request. Issued first and reduced later, so that other
+// loads can be in flight in between.
+struct BlockMeta {
+  int row, len, sh;
+  bool in;  // the lane holds a request of the block
+};
+__device__ __forceinline__ BlockMeta block_meta_load(const AttnArgs& a, int64_t rb, int lane) {
   const int64_t qa = rb * a.bm / a.g;
   int64_t qb = qa + a.bm / a.g;
   if (qb > a.batch) qb = a.batch;
-  int v = 1 << 30;
-  int row = 0;
   const int64_t r = qa + lane;
-  if (r < qb) {
-    row = a.req_pool_idx[r];
-    int m = a.kv_len[r];
-    if (row < 0 || row >= a.rtt_rows || m < 0 || m > a.rtt_stride) m = 0;
-    const int sh = lane == 0 ? (1 << 30) : (a.shared_len ? a.shared_len[r] : 0);
-    v = min(m, sh);
+  const bool in = r < qb;
+  const int64_t rr = in ? r : qa;  // unconditional loads
+  BlockMeta m;
+  m.row = a.req_pool_idx[rr];
+  m.len = a.kv_len[rr];
+  m.sh = a.shared_len ? a.shared_len[rr] : 0;
+  m.in = in;
+  return m;
+}
+
+// Shared length L of the block, by the rule every decode kernel applies: the minimum over
+// its requests of their key counts (0 for a request whose row or length is invalid) and
+// of the shared_len hints between neighbours (the block's first request has none).
+// Wave-uniform.
+__device__ __forceinline__ int block_shared_len(const AttnArgs& a, const BlockMeta& m, int lane) {
+  int v = 1 << 30;
+  if (m.in) {
+    const bool ok = m.row >= 0 && m.row < a.rtt_rows && m.len >= 0 && m.len <= a.rtt_stride;
+    v = min(ok ? m.len : 0, lane == 0 ? (1 << 30) : m.sh);
   }
-  if (row0) *row0 = uni(row);  // the block's first request's req_to_token row (lane 0)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
   return uni(max(v, 0));
+}
+
+__device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, int lane) {
+  return block_shared_len(a, block_meta_load(a, rb, lane), lane);
 }
 
 // Own keys of request r in split decode: positions [L, seq_len), L the shared length of the
@@ -836,9 +986,7 @@ __device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, i
 // at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets
 // the first own position and the chunk size.
 constexpr int kOwnMin = 32;
-__device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int L, int& first, int& per) {
-  const int end = a.kv_len[r];
-  const int row = a.req_pool_idx[r];
+__device__ __forceinline__ int own_chunks(const AttnArgs& a, int row, int end, int L, int& first, int& per) {
   first = L;
   per = 0;
   if (row < 0 || row >= a.rtt_rows || end < 0 || end > a.rtt_stride) return 0;
@@ -847,6 +995,9 @@ __device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int L, int& 
   const int n_act = min(a.n_chunk, (n + kOwnMin - 1) / kOwnMin);
   per = (n + n_act - 1) / n_act;
   return n_act;
+}
+__device__ __forceinline__ int own_chunks(const AttnArgs& a, int r, int L, int& first, int& per) {
+  return own_chunks(a, a.req_pool_idx[r], a.kv_len[r], L, first, per);
 }
 
 // Own part of decode: the keys of one request that its row block does not share (see
@@ -1035,14 +1186,20 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
         pre_acc[j][i] = sh_acc[(int64_t)(j < nsplit ? j : 0) * a.bm * D + lane + 64 * i];
   }
   {
+    // row and key count of request r from the block metadata's lanes (one round of loads)
+    const int64_t rb0 = ((int64_t)r * G) / a.bm;
+    const BlockMeta bm = block_meta_load(a, rb0, lane);
+    const int L = block_shared_len(a, bm, lane);
+    const int rl = (int)(r - rb0 * a.bm / G);
+    const int row = __builtin_amdgcn_readlane(bm.row, rl);
+    const int end = __builtin_amdgcn_readlane(bm.len, rl);
     int first, per;
-    const int L = block_shared_len(a, ((int64_t)r * G) / a.bm, lane);
-    const int n_act = own_chunks(a, r, L, first, per);
+    const int n_act = own_chunks(a, row, end, L, first, per);
     float acc[G][E], m_run[G], l_run[G];
     if (wave < n_act) {
       const int start = first + wave * per;
-      const int stop = min(start + per, (int)a.kv_len[r]);
-      own_chunk<T, D, G>(a, h, a.req_pool_idx[r], start, stop, lane, q, acc, m_run, l_run);
+      const int stop = min(start + per, end);
+      own_chunk<T, D, G>(a, h, row, start, stop, lane, q, acc, m_run, l_run);
     } else {
 #pragma unroll
       for (int hl = 0; hl < G; ++hl) {
@@ -1235,24 +1392,8 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 // combine in LDS at the end. (Running the requests' own keys in the same workgroups,
 // while the tiles arrive, measured slower: with eight waves per CU each own-key stream
 // is a chain of round trips that the separate own-part kernel's 16 waves per CU hide.)
-// LDS layout: row-major [key][D] per tile, the 16-byte chunks of row r XOR-swizzled by
-// 2 (r % 8), so that K fragment reads (32 rows x 2 chunks) and transposing V reads
-// (8 rows x 4 chunks) spread evenly over the banks; a lane's global address selects the
-// chunk that belongs at its fixed LDS position. The V^T fragments of O^T = V^T P^T come
-// from ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of
-// the 8-byte pieces addressed by lanes i / 4 + 4e (e = 0..3). Lane p therefore
-// addresses key kb + p / 4, dims d0 + 4 (p % 4), and lane i ends up with dim d0 + i of
-// keys kb .. kb + 3.
+// LDS layout and fragment reads: see "tiles loaded straight into LDS" above.
 constexpr int kShTiles = 4;
-__device__ __forceinline__ int sh_swz(int r) { return 2 * (r & 7); }
-
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
-// Written as asm so that the compiler, which cannot tell which LDS bytes such a load
-// writes, does not wait for every one in flight before each later LDS read: the kernel
-// waits for them itself (s_waitcnt vmcnt, in issue order).
-__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
 
 template <int D>
 __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
@@ -1267,7 +1408,7 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
   constexpr int NKS = D / 16;
   __shared__ __align__(16) char kv[2 * kShTiles * TB];  // K tiles, then V tiles
   __shared__ int32_t slot[kShTiles * BN];
-  const uint32_t kv_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)kv;  // LDS byte address
+  const uint32_t kv_lds = lds_addr(kv);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wrow = wave & 1, wkey = wave >> 1;  // 32-row tile, key group
@@ -1281,7 +1422,9 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
   int64_t qb = qa + BM / a.g;
   if (qb > a.batch) qb = a.batch;
 
-  // Q fragments of this lane's row (B operand of S^T = K Q^T), issued first
+  // block metadata, then Q fragments of this lane's row (B operand of S^T = K Q^T): the
+  // shared length is reduced only after both are in flight
+  const BlockMeta bmeta = block_meta_load(a, rb, lane);
   const int R = wrow * 32 + jrow;
   const int64_t Gr = G0 + R;
   const int64_t t_row = Gr / a.g;
@@ -1298,8 +1441,8 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
   }
   const bool all_rows_ok = __all(row_ok);
 
-  int row0;
-  const int L = block_shared_len(a, rb, lane, &row0);  // 0 if the first request's row is invalid
+  const int L = block_shared_len(a, bmeta, lane);  // 0 if the first request's row is invalid
+  const int row0 = __builtin_amdgcn_readfirstlane(bmeta.row);
   const int n_sh = (L + BN - 1) / BN;
   const int t_begin = (int)(((int64_t)n_sh * split) / a.nsplit);
   const int t_end = (int)(((int64_t)n_sh * (split + 1)) / a.nsplit);
@@ -1370,8 +1513,7 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
       const int kr = sub * 32 + jrow;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(kt + kr * RB + (((2 * ks + half) ^ sh_swz(kr)) * 16));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
       }
       // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
       const bool unmasked = cnt == BN && all_rows_ok;
@@ -1412,23 +1554,12 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
-      // O^T += V^T P^T; transposing reads give lane l dim dt*32 + l%32 of 4 keys each
-      const int pl = lane & 15, dsub = (lane >> 4) & 1;
+      // O^T += V^T P^T (V^T fragments by transposing LDS reads)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d0 = dt * 32 + dsub * 16 + 4 * (pl & 3);
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const int key = sub * 32 + kh * 16 + 4 * half + (pl >> 2);
-          const char* p0 = vt + key * RB + (((d0 >> 3) ^ sh_swz(key)) * 16) + (d0 & 7) * 2;
-          typedef short s16x4 __attribute__((ext_vector_type(4)));
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * RB));
-          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kh], acc[dt], 0, 0, 0);
-        }
-      }
+        for (int kh = 0; kh < 2; ++kh)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
       }
     }
     __syncthreads();  // the next round overwrites the tiles
