@@ -145,15 +145,20 @@ struct TileDesc {
 // ---- tiles loaded straight into LDS (bf16, D = 128)
 // A tile is row-major [key][D] in LDS, 256 bytes per key, filled by 16-byte global-to-LDS
 // loads: one instruction moves 64 x 16 bytes (4 keys) to consecutive LDS bytes, so no
-// row padding is possible; instead the 16-byte chunks of row r are XOR-swizzled by
-// 2 (r % 8) (a lane's global address picks the chunk that belongs at its fixed LDS
-// position). K fragment reads (32 rows x 2 chunks) and the transposing V reads (8 rows x
-// 4 chunks) then spread evenly over the banks. The V^T fragments of O^T = V^T P^T come
+// row padding is possible; instead the 16-byte chunk positions of row r are XORed with a
+// swizzle (a lane's global address picks the chunk that belongs at its fixed LDS
+// position). K fragment reads take one chunk of 16 consecutive rows per 256 bytes: K
+// rows use r % 16, so those rows hit 16 different chunk positions. A transposing V read
+// takes two adjacent chunks of 4 consecutive rows per 128 bytes and four of them per 256
+// bytes: V rows use 4 (r % 4) + 2 ((r / 2) % 2), which gives those rows different
+// 4-chunk blocks and different chunk pairs modulo 8 (no conflict with 128 or 256 bytes
+// of banks). The V^T fragments of O^T = V^T P^T come
 // from ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of
 // the 8-byte pieces addressed by lanes i / 4 + 4e (e = 0..3). Lane p therefore addresses
 // key kb + p / 4, dims d0 + 4 (p % 4), and lane i ends up with dim d0 + i of keys
 // kb .. kb + 3. Nothing is written to LDS by the threads, so no transposing stores.
-__device__ __forceinline__ int sh_swz(int r) { return 2 * (r & 7); }
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
 
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
 // Written as asm so that the compiler, which cannot tell which LDS bytes such a load
@@ -169,7 +174,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // A operand (K rows kr = 32 keys, dims ks*16 + half*8 .. +8) of S^T = K Q^T.
 __device__ __forceinline__ bf16x8 k_frag(const char* kt, int kr, int ks, int half) {
-  return *reinterpret_cast<const bf16x8*>(kt + kr * 256 + (((2 * ks + half) ^ sh_swz(kr)) * 16));
+  return *reinterpret_cast<const bf16x8*>(kt + kr * 256 + (((2 * ks + half) ^ swz_k(kr)) * 16));
 }
 
 // A operand of O^T = V^T P^T for 32 dims (dt) x 16 keys (kh) of a 32-key half (sub):
@@ -180,7 +185,7 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* vt, int sub, int dt, int k
   const int pl = lane & 15, dsub = (lane >> 4) & 1, half = lane >> 5;
   const int d0 = dt * 32 + dsub * 16 + 4 * (pl & 3);
   const int key = sub * 32 + kh * 16 + 4 * half + (pl >> 2);
-  const char* p0 = vt + key * 256 + (((d0 >> 3) ^ sh_swz(key)) * 16) + (d0 & 7) * 2;
+  const char* p0 = vt + key * 256 + (((d0 >> 3) ^ swz_v(key)) * 16) + (d0 & 7) * 2;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * 256));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -540,9 +545,9 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     for (int q = wave; q < kDmaNi; q += NW) {
       const int r = q * kDmaRpi + (lane >> 4);
       const int sv = sm.slot[sb][r];
-      const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes + (((lane & 15) ^ sh_swz(r)) * 16);
-      lds_load16(kb + off, uni(kl + q * 1024));
-      lds_load16(vb + off, uni(vl + q * 1024));
+      const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
+      lds_load16(kb + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
+      lds_load16(vb + off + (((lane & 15) ^ swz_v(r)) * 16), uni(vl + q * 1024));
     }
     }
   };
@@ -1468,9 +1473,9 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
       for (int q = wave; q < NI; q += NW) {
         const int r = q * RPI + lane / CH;
         const int sv = slot[t * BN + r];
-        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes + (((lane % CH) ^ sh_swz(r)) * 16);
-        lds_load16(kbase + off, uni(kv_lds + t * TB + q * 1024));
-        lds_load16(vbase + off, uni(kv_lds + (kShTiles + t) * TB + q * 1024));
+        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
+        lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + t * TB + q * 1024));
+        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (kShTiles + t) * TB + q * 1024));
       }
     }
   };
