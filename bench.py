@@ -169,7 +169,7 @@ def _counter_means(csv_path, counter):
 
 
 # kernels that make up one launch of each attention entry point (substrings of their names)
-ENTRY_KERNELS = {"decode": ("attn_kernelIDF16bLi128ELb1E", "own_merge_kernelIDF16bLi128E"),
+ENTRY_KERNELS = {"decode": ("shared_kernel<128>", "own_merge_kernelIDF16bLi128E"),
                  "extend": ("attn_kernelIDF16bLi128ELb0E",)}
 
 
@@ -401,7 +401,7 @@ def main():
                 "frac": ext_tflops / MFMA_BF16_PEAK_TFLOPS, "launches_per_step": len(ext_flops),
                 "avg_launch_us": sum(ext_us) / len(ext_us)}
     else:
-        roof = {"kernel": "decode attention (shared-prefix attn_kernel + own_merge_kernel)", "bound": "hbm",
+        roof = {"kernel": "decode attention (shared_kernel + own_merge_kernel)", "bound": "hbm",
                 "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                 "launches_per_step": len(dec_bytes), "avg_launch_us": sum(dec_us) / len(dec_us)}
     roof["traffic"] = load_traffic("extend" if roof["bound"] == "mfma" else "decode", args.traffic)
