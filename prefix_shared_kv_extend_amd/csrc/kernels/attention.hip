@@ -160,18 +160,6 @@ struct TileDesc {
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
 
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
-// Written as asm so that the compiler, which cannot tell which LDS bytes such a load
-// writes, does not wait for every one in flight before each later LDS read: the kernel
-// waits for them itself (s_waitcnt vmcnt, in issue order).
-__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-
 // A operand (K rows kr = 32 keys, dims ks*16 + half*8 .. +8) of S^T = K Q^T.
 __device__ __forceinline__ bf16x8 k_frag(const char* kt, int kr, int ks, int half) {
   return *reinterpret_cast<const bf16x8*>(kt + kr * 256 + (((2 * ks + half) ^ swz_k(kr)) * 16));

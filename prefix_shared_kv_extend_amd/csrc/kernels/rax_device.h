@@ -27,4 +27,17 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   return (bid % kXcd) * per + bid / kXcd;
 }
 
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform).
+// Written as asm so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not wait for every one in flight before each later LDS read: the kernel
+// waits for them itself (s_waitcnt vmcnt, in issue order).
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Byte address in LDS of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 }  // namespace raxk

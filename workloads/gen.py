@@ -159,3 +159,13 @@ def qkv_values(hashes, kind: int, n_heads: int, head_dim: int, seed: int,
 def tokens(rng: np.random.Generator, n: int, vocab: int = VOCAB) -> np.ndarray:
     """Uniform token ids in [0, vocab) as int32."""
     return rng.integers(0, vocab, size=int(n), dtype=np.int64).astype(np.int32)
+
+
+def projection_inputs(seed: int, t: int, hidden: int, n_out: int):
+    """Hidden states x [t, hidden] ~ N(0, 1) and projection weights w [n_out, hidden] ~
+    N(0, 1/hidden), both rounded to bf16 (returned as float32 CPU tensors holding bf16
+    values), so that projected values are O(1)."""
+    g = torch.Generator().manual_seed(int(seed) & 0x7FFFFFFF)
+    x = torch.randn((t, hidden), generator=g).to(torch.bfloat16).float()
+    w = (torch.randn((n_out, hidden), generator=g) / hidden ** 0.5).to(torch.bfloat16).float()
+    return x, w
