@@ -300,6 +300,49 @@ def host_tier_measure(dev):
     return out
 
 
+def projection_measure(dev):
+    """QKV projection fused with the KV write-back, on the cached few-shot extend batch:
+    3150 new tokens, hidden 4096, 32 heads x 128 (MHA), so W is [12288, 4096]. Fused: one
+    kernel writes Q, the contiguous K/V and the pool rows. Unfused: the same GEMM without
+    pool writes, then rax_kv_scatter from the contiguous K/V. HIP events around 20 calls of
+    each on the current stream."""
+    import torch
+    from prefix_shared_kv_extend_amd import _lib
+    from workloads.gen import projection_inputs
+    t, hidden, h, d = 3150, 4096, 32, 128
+    x, w = projection_inputs(5, t, hidden, 3 * h * d)
+    x, w = x.to(torch.bfloat16).to(dev), w.to(torch.bfloat16).to(dev)
+    loc = (torch.randperm(1 << 16, generator=torch.Generator().manual_seed(1))[:t]).to(torch.int32).to(dev)
+    kp = torch.zeros((1 << 16, h, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    q, k, v = _lib.qkv_project(x, w, h, h)
+
+    def fused():
+        _lib.qkv_project(x, w, h, h, out_loc=loc, k_pool=kp, v_pool=vp, q_out=q, k_ext=k, v_ext=v)
+
+    def unfused():
+        _lib.qkv_project(x, w, h, h, q_out=q, k_ext=k, v_ext=v)
+        _lib.kv_scatter(k, v, loc, kp, vp)
+
+    out = {"workload": "cached few-shot extend batch: 3150 tokens, hidden 4096, 32 heads x 128 (W 12288 x 4096)"}
+    flops = 2.0 * t * hidden * 3 * h * d
+    for name, fn in (("fused", fused), ("gemm_then_scatter", unfused)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / 20
+        out[name] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                     "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    out["saved_us"] = out["gemm_then_scatter"]["us"] - out["fused"]["us"]
+    assert _lib.device_errors() == 0
+    return out
+
+
 def cpu_baseline(job, seconds):
     """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
     import torch
@@ -438,6 +481,7 @@ def main():
     }
     out["scheduler"] = scheduler_ablation()
     out["host_tier"] = host_tier_measure(dev)
+    out["qkv_projection"] = projection_measure(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -384,6 +384,20 @@ rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* args);
 size_t rax_attention_workspace_bytes(int32_t is_decode, int64_t rows, int32_t h_q, int32_t h_kv,
                                      int32_t d, int32_t max_kv_len);
 
+/* QKV projection of new tokens, fused with their KV write-back (the step before the
+ * path; [hustzhy] §2.3 (2): the suffix is computed; [notes] App. A.1: its KV is kept).
+ * y = x W^T for x [n_tok, hidden] and W [(h_q + 2 h_kv) d, hidden] (device, row-major,
+ * dtype dt = RAX_BF16 only, 16-byte aligned), fp32 sums rounded once to bf16. Output
+ * features: Q (first h_q d) -> q_out [n_tok, h_q, d]; K (next h_kv d) -> k_ext
+ * [n_tok, h_kv, d]; V (last h_kv d) -> v_ext. With out_loc (device int32 [n_tok]) K and V
+ * also go to k_pool / v_pool [num_slots, h_kv, d] at slot out_loc[t] (the write-back of
+ * rax_kv_scatter, done by the same kernel); slots outside [0, num_slots) are skipped and
+ * flagged. RAX_EINVAL: bad sizes (hidden % 64, (h_q + 2 h_kv) d % 128 and d % 8 must be
+ * 0), pointers (all 16-byte aligned) or dtype. Asynchronous on `stream`. */
+rax_status rax_qkv_project(const void* x, const void* w, int64_t n_tok, int32_t hidden, int32_t h_q,
+                           int32_t h_kv, int32_t d, rax_dtype dt, void* q_out, void* k_ext, void* v_ext,
+                           const int32_t* out_loc, void* k_pool, void* v_pool, int64_t num_slots, void* stream);
+
 /* Synchronise `stream`, return (and clear) the device error word: a bit mask of
  * RAX_DEVERR_* for indices the kernels skipped since the last call. */
 #define RAX_DEVERR_SLOT 1   /* slot id outside [0, num_slots) */

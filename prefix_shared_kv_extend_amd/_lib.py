@@ -84,6 +84,7 @@ _SIGS = {
                                     _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_attention_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "rax_device_errors": (_i32, [_vp, _c_i32p]),
+    "rax_qkv_project": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -515,3 +516,38 @@ def device_errors(stream=None) -> int:
     m = _i32()
     _check(lib().rax_device_errors(_stream(stream), ctypes.byref(m)), "rax_device_errors")
     return int(m.value)
+
+
+def qkv_project(x, w, h_q: int, h_kv: int, out_loc=None, k_pool=None, v_pool=None, q_out=None, k_ext=None,
+                v_ext=None, stream=None):
+    """rax_qkv_project: x [T, hidden] bf16, w [(h_q + 2 h_kv) d, hidden] bf16 (cuda,
+    contiguous). Returns (q [T, h_q, d], k_ext [T, h_kv, d], v_ext [T, h_kv, d]); with
+    out_loc (cuda int32 [T]) K and V also go to the pools at those slots."""
+    import torch
+    _need(x.dim() == 2 and w.dim() == 2 and x.shape[1] == w.shape[1], "x [T, hidden], w [n_out, hidden]")
+    _need(x.is_cuda and w.is_cuda and x.is_contiguous() and w.is_contiguous()
+          and x.dtype == w.dtype == torch.bfloat16, "x, w: contiguous cuda bf16")
+    t, n_out = x.shape[0], w.shape[0]
+    _need(n_out % (h_q + 2 * h_kv) == 0, "w rows: (h_q + 2 h_kv) * d")
+    d = n_out // (h_q + 2 * h_kv)
+    if q_out is None:
+        q_out = torch.empty((t, h_q, d), dtype=x.dtype, device=x.device)
+    if k_ext is None:
+        k_ext = torch.empty((t, h_kv, d), dtype=x.dtype, device=x.device)
+    if v_ext is None:
+        v_ext = torch.empty((t, h_kv, d), dtype=x.dtype, device=x.device)
+    for o, h in ((q_out, h_q), (k_ext, h_kv), (v_ext, h_kv)):
+        _need(tuple(o.shape) == (t, h, d) and o.dtype == x.dtype and o.is_cuda and o.is_contiguous(),
+              "outputs: contiguous cuda [T, heads, d] of x's dtype")
+    slots = 0
+    if out_loc is not None:
+        _cuda_i32(out_loc)
+        _need(out_loc.numel() == t and k_pool is not None and v_pool is not None
+              and k_pool.shape == v_pool.shape and tuple(k_pool.shape[1:]) == (h_kv, d)
+              and k_pool.dtype == x.dtype and k_pool.is_contiguous() and v_pool.is_contiguous(),
+              "out_loc [T]; pools [slots, h_kv, d] of x's dtype")
+        slots = k_pool.shape[0]
+    _check(lib().rax_qkv_project(_dev(x), _dev(w), t, x.shape[1], h_q, h_kv, d, BF16, _dev(q_out), _dev(k_ext),
+                                 _dev(v_ext), _dev(out_loc), _dev(k_pool), _dev(v_pool), slots,
+                                 _stream(stream, x)), "rax_qkv_project")
+    return q_out, k_ext, v_ext

@@ -2,3 +2,4 @@
 // live in one code object (no relocatable device code needed).
 #include "kv_scatter.hip"
 #include "attention.hip"
+#include "projection.hip"

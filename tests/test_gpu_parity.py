@@ -345,3 +345,77 @@ def test_full_multi_turn_sampled():
     say("  host log identical; checking sampled outputs")
     worst = _check_outputs(job, got, TOL[job.dtype])
     say(f"  checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")
+
+
+# ------------------------------------------------------------- QKV projection (fused write-back)
+@pytest.mark.parametrize("t,hidden,h_q,h_kv,d", [(300, 256, 4, 2, 128), (77, 512, 8, 2, 64), (1, 128, 1, 1, 128)])
+def test_qkv_project_small(t, hidden, h_q, h_kv, d):
+    """Every output of the fused projection against the fp64 oracle (bf16 rounding of fp32
+    sums: max-abs 2e-2 at values of order 1), and the pool rows bit for bit equal to the
+    contiguous K/V outputs; untouched pool rows stay zero."""
+    from oracle.projection import qkv_project
+    from prefix_shared_kv_extend_amd import _lib
+    from workloads.gen import projection_inputs
+    say(f"qkv projection: T={t} hidden={hidden} h_q={h_q} h_kv={h_kv} d={d}")
+    n_out = (h_q + 2 * h_kv) * d
+    x, w = projection_inputs(11, t, hidden, n_out)
+    S = 3 * t + 5
+    loc = torch.randperm(S, generator=torch.Generator().manual_seed(2))[:t].to(torch.int32)
+    kp = torch.zeros((S, h_kv, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    q, k, v = _lib.qkv_project(x.to(torch.bfloat16).cuda(), w.to(torch.bfloat16).cuda(), h_q, h_kv,
+                               out_loc=loc.cuda(), k_pool=kp, v_pool=vp)
+    torch.cuda.synchronize()
+    rq, rk, rv = qkv_project(x.numpy(), w.numpy(), h_q, h_kv, d)
+    for got, ref in ((q, rq), (k, rk), (v, rv)):
+        err = float(np.abs(got.float().cpu().numpy() - ref).max())
+        assert err <= 2e-2, err
+    kp, vp, loc = kp.cpu(), vp.cpu(), loc.long()
+    assert torch.equal(kp[loc], k.cpu()) and torch.equal(vp[loc], v.cpu())
+    rest = torch.ones(S, dtype=torch.bool)
+    rest[loc] = False
+    assert int(kp[rest].abs().sum()) == 0 and int(vp[rest].abs().sum()) == 0
+    assert _lib.device_errors() == 0
+
+
+def test_qkv_project_full_size_sampled():
+    """The cached few-shot extend batch's projection (3150 tokens, hidden 4096, 32 heads x
+    128): sampled token rows against the oracle; the pool copy bit-exact."""
+    from oracle.projection import qkv_project_rows
+    from prefix_shared_kv_extend_amd import _lib
+    from workloads.gen import projection_inputs
+    t, hidden, h, d = 3150, 4096, 32, 128
+    say(f"qkv projection full size: T={t} hidden={hidden} heads={h} d={d}")
+    x, w = projection_inputs(12, t, hidden, 3 * h * d)
+    loc = torch.arange(t, dtype=torch.int32) * 3 + 1
+    kp = torch.zeros((3 * t + 2, h, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    q, k, v = _lib.qkv_project(x.to(torch.bfloat16).cuda(), w.to(torch.bfloat16).cuda(), h, h,
+                               out_loc=loc.cuda(), k_pool=kp, v_pool=vp)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 1000, 2047, 3071, 3072, 3149]
+    rq, rk, rv = qkv_project_rows(x.numpy(), w.numpy(), rows, h, h, d)
+    for got, ref in ((q, rq), (k, rk), (v, rv)):
+        err = float(np.abs(got[rows].float().cpu().numpy() - ref).max())
+        assert err <= 2e-2, err
+    assert torch.equal(kp[loc.long().cuda()], k) and torch.equal(vp[loc.long().cuda()], v)
+    assert _lib.device_errors() == 0
+
+
+def test_qkv_project_errors_and_flagged_slots():
+    from prefix_shared_kv_extend_amd import _lib
+    say("qkv projection: argument errors, out-of-range slot flagged and skipped")
+    x = torch.ones((4, 96), dtype=torch.bfloat16, device="cuda")          # hidden % 64 != 0
+    w = torch.ones((384, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(_lib.RaxError) as e:
+        _lib.qkv_project(x, w, 1, 1)
+    assert e.value.status == _lib.EINVAL
+    x = torch.ones((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((384, 64), dtype=torch.bfloat16, device="cuda") / 64
+    kp = torch.zeros((8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    q, k, v = _lib.qkv_project(x, w, 1, 1, out_loc=torch.tensor([0, 8, -1, 3], dtype=torch.int32, device="cuda"),
+                               k_pool=kp, v_pool=vp)
+    assert _lib.device_errors() == _lib.DEVERR_SLOT
+    assert float(kp[0].float().sum()) == 128 and float(kp[3].float().sum()) == 128
+    assert float(kp.float().sum()) == 256 and float(q.float().sum()) == 4 * 128
