@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "../../../include/rax.h"
+#include "../rax_internal.h"
 #include "rax_device.h"
 
 namespace raxk {
@@ -364,10 +365,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   if (tid == 0) sm.req_qo[nreq] = kDecode ? r0 + nreq : a.qo_indptr[r0 + nreq];
   __syncthreads();
   if (wave == 0) {
-    // shared length L = min over the block's requests of their key counts and of the
-    // shared_len hints between neighbours; then an exclusive scan of own-tile counts
+    // shared length L = min over the block's requests of their key counts (decode: minus
+    // one, so the newest key is always the request's own) and of the shared_len hints
+    // between neighbours; then an exclusive scan of own-tile counts
     int Lw = 1 << 30;
-    for (int i = lane; i < nreq; i += 64) Lw = min(Lw, min(sm.req_m[i], sm.req_sh[i]));
+    for (int i = lane; i < nreq; i += 64) Lw = min(Lw, min(sm.req_m[i] - (kDecode ? 1 : 0), sm.req_sh[i]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) Lw = min(Lw, __shfl_xor(Lw, off));
     const int L = max(Lw, 0);
@@ -940,7 +942,7 @@ struct BlockMeta {
   int row, len, sh;
   bool in;  // the lane holds a request of the block
 };
-__device__ __forceinline__ BlockMeta block_meta_load(const AttnArgs& a, int64_t rb, int lane) {
+__device__ __forceinline__ BlockMeta block_meta_load(const AttnArgs& a, int64_t rb, int lane, bool load_len = true) {
   const int64_t qa = rb * a.bm / a.g;
   int64_t qb = qa + a.bm / a.g;
   if (qb > a.batch) qb = a.batch;
@@ -949,21 +951,23 @@ __device__ __forceinline__ BlockMeta block_meta_load(const AttnArgs& a, int64_t 
   const int64_t rr = in ? r : qa;  // unconditional loads
   BlockMeta m;
   m.row = a.req_pool_idx[rr];
-  m.len = a.kv_len[rr];
+  m.len = load_len ? a.kv_len[rr] : 0;
   m.sh = a.shared_len ? a.shared_len[rr] : 0;
   m.in = in;
   return m;
 }
 
 // Shared length L of the block, by the rule every decode kernel applies: the minimum over
-// its requests of their key counts (0 for a request whose row or length is invalid) and
-// of the shared_len hints between neighbours (the block's first request has none).
-// Wave-uniform.
+// its requests of their key counts minus one (0 for a request whose row or length is
+// invalid) and of the shared_len hints between neighbours (the block's first request has
+// none). The minus one keeps every request's newest key in its own part, so the shared
+// part never reads a key that this step's append writes (rax_decode_step folds the
+// append into the shared-part kernel). Wave-uniform.
 __device__ __forceinline__ int block_shared_len(const AttnArgs& a, const BlockMeta& m, int lane) {
   int v = 1 << 30;
   if (m.in) {
     const bool ok = m.row >= 0 && m.row < a.rtt_rows && m.len >= 0 && m.len <= a.rtt_stride;
-    v = min(ok ? m.len : 0, lane == 0 ? (1 << 30) : m.sh);
+    v = min(ok ? m.len - 1 : 0, lane == 0 ? (1 << 30) : m.sh);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
@@ -1389,7 +1393,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 constexpr int kShTiles = 4;
 
 template <int D>
-__global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
   constexpr int NW = 8, NKG = 4;       // waves; key groups
   constexpr int BM = 64;
@@ -1415,9 +1419,37 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a) {
   int64_t qb = qa + BM / a.g;
   if (qb > a.batch) qb = a.batch;
 
+  // a decode step's append carried by this launch (rax_decode_step): token i's K/V row to
+  // its slot, the slot into its row at len - 1, len to seq_len_dev (what
+  // decode_append_kernel does). This kernel reads none of it: its keys end before every
+  // request's newest position, and it takes the lengths from the job.
+  for (int i = blockIdx.x; i < ap.n; i += gridDim.x) {
+    const int64_t slot = ap.slot[i];
+    const int64_t cpr = ap.chunks_per_row;
+    const u32x4* kn = reinterpret_cast<const u32x4*>(ap.k_new) + (int64_t)i * cpr;
+    const u32x4* vn = reinterpret_cast<const u32x4*>(ap.v_new) + (int64_t)i * cpr;
+    u32x4* kp = reinterpret_cast<u32x4*>(const_cast<void*>(a.k_pool)) + slot * cpr;
+    u32x4* vp = reinterpret_cast<u32x4*>(const_cast<void*>(a.v_pool)) + slot * cpr;
+    for (int64_t c = tid; c < cpr; c += 64 * NW) {
+      kp[c] = kn[c];
+      vp[c] = vn[c];
+    }
+    if (tid == 0) {
+      const int64_t row = a.req_pool_idx[i];
+      const int32_t len = ap.len[i];
+      ap.seq_len_dev[i] = len;
+      if (row < 0 || row >= a.rtt_rows) flag_error(RAX_DEVERR_ROW);
+      else const_cast<int32_t*>(a.rtt)[row * a.rtt_stride + len - 1] = (int32_t)slot;
+    }
+  }
+
   // block metadata, then Q fragments of this lane's row (B operand of S^T = K Q^T): the
   // shared length is reduced only after both are in flight
-  const BlockMeta bmeta = block_meta_load(a, rb, lane);
+  BlockMeta bmeta = block_meta_load(a, rb, lane, ap.n == 0);
+  if (ap.n > 0) {  // lengths after this step's append: from the job, not memory
+    const int64_t r = qa + lane;
+    bmeta.len = ap.len[r < ap.n ? r : qa];
+  }
   const int R = wrow * 32 + jrow;
   const int64_t Gr = G0 + R;
   const int64_t t_row = Gr / a.g;
@@ -1689,7 +1721,7 @@ static rax_status launch_own(AttnArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D, bool kDecode>
-static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st) {
+static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const AppendJob* ap) {
   rax_status rc = RAX_EINVAL;
   if constexpr (sizeof(T) == 2 && !kDecode) {
     if constexpr (D == 128) {
@@ -1702,7 +1734,9 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st) {
     if constexpr (D == 128) {
       if (a.shared_only) {  // shared part of split decode
         const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a);
+        AppendJob none;
+        none.n = 0;
+        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a, ap ? *ap : none);
         return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
       }
     }
@@ -1714,8 +1748,8 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st) {
 }
 
 template <typename T, int D, bool kDecode>
-static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
-  rax_status rc = launch_attn<T, D, kDecode>(a, s, st);
+static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const AppendJob* ap) {
+  rax_status rc = launch_attn<T, D, kDecode>(a, s, st, ap);
   if (rc != RAX_OK) return rc;
   if constexpr (kDecode) {
     if (a.shared_only && a.own_fused == 1) {
@@ -1744,13 +1778,14 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st) {
 }
 
 template <bool kDecode>
-static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_t st) {
+static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_t st,
+                           const AppendJob* ap = nullptr) {
   if (dt == RAX_BF16) {
-    if (d == 128) return launch_shape<__bf16, 128, kDecode>(a, s, st);
-    if (d == 64) return launch_shape<__bf16, 64, kDecode>(a, s, st);
+    if (d == 128) return launch_shape<__bf16, 128, kDecode>(a, s, st, ap);
+    if (d == 64) return launch_shape<__bf16, 64, kDecode>(a, s, st, ap);
   } else {
-    if (d == 128) return launch_shape<float, 128, kDecode>(a, s, st);
-    if (d == 64) return launch_shape<float, 64, kDecode>(a, s, st);
+    if (d == 128) return launch_shape<float, 128, kDecode>(a, s, st, ap);
+    if (d == 64) return launch_shape<float, 64, kDecode>(a, s, st, ap);
   }
   return RAX_EINVAL;
 }
@@ -1873,6 +1908,12 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   return dispatch<false>(a, dt, d, s, (hipStream_t)stream);
 }
 
+bool raxk::decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt) {
+  if (dt != RAX_BF16 || d != 128 || batch < 1 || batch > kAppendMax || h_kv < 1 || h_q % h_kv) return false;
+  const int g = h_q / h_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;  // split decode: shared_kernel runs first
+}
+
 extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                                            int64_t num_slots, const int32_t* req_to_token, int64_t rtt_stride,
                                            int64_t rtt_rows, const int32_t* req_pool_idx, const int32_t* seq_len,
@@ -1880,6 +1921,18 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
                                            int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
                                            void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes,
                                            void* stream) {
+  return raxk::decode_attention_impl(q, k_pool, v_pool, num_slots, req_to_token, rtt_stride, rtt_rows, req_pool_idx,
+                                     seq_len, shared_len, batch, max_seq_len, h_q, h_kv, d, sm_scale, dt, o, o_dt,
+                                     workspace, ws_bytes, stream, nullptr);
+}
+
+rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                       const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                       const int32_t* req_pool_idx, const int32_t* seq_len,
+                                       const int32_t* shared_len, int32_t batch, int32_t max_seq_len, int32_t h_q,
+                                       int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt, void* o,
+                                       rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream,
+                                       const AppendJob* ap) {
   if (!common_ok(h_q, h_kv, d, dt, o_dt) || batch < 0 || max_seq_len < 0 || num_slots < 1 || rtt_stride < 1 ||
       rtt_rows < 1 || rtt_stride > INT32_MAX)
     return RAX_EINVAL;
@@ -1921,5 +1974,6 @@ extern "C" rax_status rax_decode_attention(const void* q, const void* k_pool, co
       a.own_fused = l.own_mode;
     }
   }
-  return dispatch<true>(a, dt, d, s, (hipStream_t)stream);
+  if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
+  return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap);
 }

@@ -251,11 +251,14 @@ rax_status rax_alloc_slots_evict(rax_tree* t, int64_t n, int32_t* out_slots, int
   RAX_GUARD_END
 }
 
-rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots, int32_t* out_freed,
-                             int64_t cap, int64_t* out_num_freed, const int32_t* req_pool_idx, int32_t* seq_len_dev,
-                             int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows, const void* k_new,
-                             const void* v_new, void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt,
-                             void* stream) {
+// The host part of a decode append: checks, one slot per request (evicting when short),
+// lengths + 1, and pending host-tier moves launched on the stream, which read their slots
+// before anything writes the new tokens. *cpr = 16-byte chunks per K row.
+static rax_status append_host(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots, int32_t* out_freed,
+                              int64_t cap, int64_t* out_num_freed, const int32_t* req_pool_idx,
+                              int32_t* seq_len_dev, int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                              const void* k_new, const void* v_new, void* k_pool, void* v_pool, int32_t h_kv,
+                              int32_t d, rax_dtype dt, void* stream, int64_t* cpr) {
   if (!t || batch < 0 || cap < 0 || !out_num_freed || (cap > 0 && !out_freed) || rtt_stride < 1 || rtt_rows < 1 ||
       h_kv < 1 || d < 1 || (dt != RAX_F32 && dt != RAX_BF16))
     return RAX_EINVAL;
@@ -276,13 +279,23 @@ rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32
   if (short_by > 0) *out_num_freed = r.evict(short_by, out_freed, cap);
   if (!r.alloc().alloc(batch, out_slots)) return RAX_ENOMEM;
   for (int32_t i = 0; i < batch; ++i) seq_len[i] += 1;
-  // moves (demotions of this call's evictions, and any left pending) read their slots
-  // before the append kernel writes the new tokens into them
-  const rax_status ms = run_pending(t, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
-  if (ms != RAX_OK) return ms;
-  return raxk::launch_decode_append(batch, out_slots, seq_len, req_pool_idx, seq_len_dev, req_to_token, rtt_stride,
-                                    rtt_rows, k_new, v_new, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
+  *cpr = row_bytes / 16;
+  return run_pending(t, k_pool, v_pool, row_bytes / 16, (hipStream_t)stream);
   RAX_GUARD_END
+}
+
+rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32_t* out_slots, int32_t* out_freed,
+                             int64_t cap, int64_t* out_num_freed, const int32_t* req_pool_idx, int32_t* seq_len_dev,
+                             int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, int32_t h_kv, int32_t d, rax_dtype dt,
+                             void* stream) {
+  int64_t cpr = 0;
+  const rax_status s = append_host(t, batch, seq_len, out_slots, out_freed, cap, out_num_freed, req_pool_idx,
+                                   seq_len_dev, req_to_token, rtt_stride, rtt_rows, k_new, v_new, k_pool, v_pool, h_kv,
+                                   d, dt, stream, &cpr);
+  if (s != RAX_OK || batch == 0) return s;
+  return raxk::launch_decode_append(batch, out_slots, seq_len, req_pool_idx, seq_len_dev, req_to_token, rtt_stride,
+                                    rtt_rows, k_new, v_new, k_pool, v_pool, cpr, (hipStream_t)stream);
 }
 
 rax_status rax_prefix_len_batch(const rax_tree* t, const int32_t* tokens, const int64_t* indptr, int32_t batch,
@@ -349,13 +362,36 @@ rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
                            a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len, 0, max_len, a->h_q, a->h_kv,
                            a->d, a->sm_scale, a->dt, a->o, a->o_dt, a->workspace, a->ws_bytes, a->stream) != RAX_OK)
     return RAX_EINVAL;
-  const rax_status s = rax_decode_append(t, a->batch, a->seq_len, a->out_slots, a->out_freed, a->cap, &a->num_freed,
-                                         a->req_pool_idx, a->seq_len_dev, a->req_to_token, a->rtt_stride, a->rtt_rows,
-                                         a->k_new, a->v_new, a->k_pool, a->v_pool, a->h_kv, a->d, a->dt, a->stream);
+  if (!raxk::decode_folds_append(a->batch, a->h_q, a->h_kv, a->d, a->dt)) {
+    const rax_status s = rax_decode_append(t, a->batch, a->seq_len, a->out_slots, a->out_freed, a->cap, &a->num_freed,
+                                           a->req_pool_idx, a->seq_len_dev, a->req_to_token, a->rtt_stride,
+                                           a->rtt_rows, a->k_new, a->v_new, a->k_pool, a->v_pool, a->h_kv, a->d, a->dt,
+                                           a->stream);
+    if (s != RAX_OK) return s;
+    return rax_decode_attention(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token,
+                                a->rtt_stride, a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len, a->batch,
+                                max_len, a->h_q, a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt, a->workspace,
+                                a->ws_bytes, a->stream);
+  }
+  // the append rides in the first attention kernel's launch (one launch less per step)
+  raxk::AppendJob job;
+  const rax_status s = append_host(t, a->batch, a->seq_len, a->out_slots, a->out_freed, a->cap, &a->num_freed,
+                                   a->req_pool_idx, a->seq_len_dev, a->req_to_token, a->rtt_stride, a->rtt_rows,
+                                   a->k_new, a->v_new, a->k_pool, a->v_pool, a->h_kv, a->d, a->dt, a->stream,
+                                   &job.chunks_per_row);
   if (s != RAX_OK) return s;
-  return rax_decode_attention(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token, a->rtt_stride,
-                              a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len, a->batch, max_len, a->h_q,
-                              a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt, a->workspace, a->ws_bytes, a->stream);
+  job.k_new = a->k_new;
+  job.v_new = a->v_new;
+  job.seq_len_dev = a->seq_len_dev;
+  job.n = a->batch;
+  for (int32_t i = 0; i < a->batch; ++i) {
+    job.slot[i] = a->out_slots[i];
+    job.len[i] = a->seq_len[i];
+  }
+  return raxk::decode_attention_impl(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token,
+                                     a->rtt_stride, a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len,
+                                     a->batch, max_len, a->h_q, a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt,
+                                     a->workspace, a->ws_bytes, a->stream, &job);
 }
 
 rax_status rax_set_host_tier(rax_tree* t, int64_t host_slots, void* k_host, void* v_host) {

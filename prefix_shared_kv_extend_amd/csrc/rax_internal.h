@@ -16,6 +16,32 @@ struct AppendBatch {
   int32_t len[kAppendMax];
 };
 
+// A decode step's write-back carried by the first decode-attention kernel (see
+// rax_decode_step), passed by value: each new token's K/V row goes to its slot, the slot
+// to its req_to_token row at position len - 1, and len to seq_len_dev.
+struct AppendJob {
+  const void* k_new;
+  const void* v_new;
+  int32_t* seq_len_dev;
+  int64_t chunks_per_row;  // 16-byte chunks per K (or V) row
+  int32_t n;               // tokens (0: no append)
+  int32_t slot[kAppendMax];
+  int32_t len[kAppendMax];  // lengths after the step
+};
+
+// Whether decode attention with these sizes starts with the kernel that can carry an
+// AppendJob (bf16, D = 128, split decode, batch <= kAppendMax).
+bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt);
+
+// rax_decode_attention, with an optional append carried by its first kernel (seq_len is
+// then read from the job, not from memory, by that kernel).
+rax_status decode_attention_impl(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                 const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                 const int32_t* req_pool_idx, const int32_t* seq_len, const int32_t* shared_len,
+                                 int32_t batch, int32_t max_seq_len, int32_t h_q, int32_t h_kv, int32_t d,
+                                 float sm_scale, rax_dtype dt, void* o, rax_dtype o_dt, void* workspace,
+                                 size_t ws_bytes, void* stream, const AppendJob* ap);
+
 // One launch of the move kernel: n (src, dst) slot pairs, each dst written once.
 constexpr int kMoveMax = 256;
 struct MoveBatch {

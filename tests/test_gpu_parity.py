@@ -419,3 +419,55 @@ def test_qkv_project_errors_and_flagged_slots():
     assert _lib.device_errors() == _lib.DEVERR_SLOT
     assert float(kp[0].float().sum()) == 128 and float(kp[3].float().sum()) == 128
     assert float(kp.float().sum()) == 256 and float(q.float().sum()) == 4 * 128
+
+
+def test_decode_step_folded_append_equals_separate_calls():
+    """rax_decode_step carries the append in the first attention kernel (bf16, D = 128): the
+    slots, rows, lengths, pools and outputs equal those of rax_decode_append followed by
+    rax_decode_attention on an identical runtime, bit for bit, over several steps (70
+    requests, GQA 16/4, five row blocks)."""
+    from prefix_shared_kv_extend_amd import _lib
+    from prefix_shared_kv_extend_amd.runtime import RadixRuntime
+    say("decode step with the append folded in vs separate append + attention (bf16, g = 4)")
+    h_q, h_kv, d, B = 16, 4, 128, 70
+    rng = np.random.default_rng(5)
+    pre = rng.integers(0, 50, 120)
+    prompts = [np.concatenate([pre, rng.integers(0, 50, int(rng.integers(1, 30)))]).astype(np.int32)
+               for _ in range(B)]
+    gen = torch.Generator().manual_seed(9)
+
+    def rnd(*shape):
+        return torch.randn(shape, generator=gen).to(torch.bfloat16).cuda()
+
+    rts = []
+    for _ in range(2):
+        rt = RadixRuntime(16384, h_q, h_kv, d, torch.bfloat16, B, 400)
+        rts.append((rt, rt.begin_extend(list(enumerate(prompts)))))
+    t = rts[0][1].total_q
+    q, k, v = rnd(t, h_q, d), rnd(t, h_kv, d), rnd(t, h_kv, d)
+    for rt, eb in rts:
+        rt.run_extend(eb, q, k, v, torch.empty((t, h_q, d), dtype=torch.bfloat16, device="cuda"))
+        rt.end_extend(eb)
+    (ra, _), (rb, _) = rts
+    rids = list(range(B))
+    for step in range(3):
+        qd, kd, vd = rnd(B, h_q, d), rnd(B, h_kv, d), rnd(B, h_kv, d)
+        oa = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
+        ra.run_decode(ra.begin_decode(rids), qd, kd, vd, oa)
+        rb.begin_decode(rids)
+        ds = rb._dec_cache
+        new, _ = rb.tree.decode_append(ds.lens, rb.rtt, ds.inv["req_pool_idx"], ds.inv["seq_len"], kd, vd,
+                                       rb.k_pool, rb.v_pool)
+        rb.rows[ds.req_rows, ds.lens - 1] = new
+        mx = int(ds.lens.max())
+        ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, mx), dtype=torch.uint8, device="cuda")
+        ob = torch.empty_like(oa)
+        _lib.decode_attention(qd, rb.k_pool, rb.v_pool, rb.rtt, ds.inv["req_pool_idx"], ds.inv["seq_len"], mx, ob,
+                              workspace=ws, shared_len=ds.inv["shared_len"])
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {step}"
+        assert np.array_equal(ra._dec_cache.lens, ds.lens)
+        assert torch.equal(ra._dec_cache.inv["seq_len"], ds.inv["seq_len"])
+    assert torch.equal(ra.rtt, rb.rtt) and np.array_equal(ra.rows, rb.rows)
+    assert torch.equal(ra.k_pool, rb.k_pool) and torch.equal(ra.v_pool, rb.v_pool)
+    assert _lib.device_errors() == 0
