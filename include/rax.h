@@ -340,7 +340,9 @@ rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v
 /* One whole decode step in one call: rax_decode_append (slots, row append, K/V
  * write-back, with any host-tier moves) followed by rax_decode_attention over the rows
  * as they are after the append, on the same stream; max_seq_len is taken from the host
- * lengths. Meant for serving loops, where the per-call argument marshalling of two
+ * lengths. For dt = RAX_BF16, d = 128, h_q / h_kv in {1, 2, 4, 8, 16} and batch <= 256
+ * the append is done by the attention's first kernel (one launch less); the results are
+ * the same bit for bit. Meant for serving loops, where the per-call argument marshalling of two
  * entry points costs as much host time as the GPU spends on the step: the caller keeps
  * one argument block per decode batch and updates only what changes (q, k_new, v_new, o,
  * stream). Fields are as in the two calls; the pool holds the tree's num_slots rows.
