@@ -1590,61 +1590,68 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
     __syncthreads();  // the next round overwrites the tiles
   }
 
-  // key groups 1..3 hand (m, l, acc) to group 0 over LDS
-  constexpr int NV = (D / 32) * 16 + 2;
-  static_assert((NKG - 1) * 2 * NV * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
-  float* xs = reinterpret_cast<float*>(kv);
-  if (wkey > 0) {
-    const int base = ((wkey - 1) * 2 + wrow) * NV;
+  // The four key groups combine their states over LDS, the work split by dims: every wave
+  // hands the other groups its accumulator slices dt != wkey and its (m, l); then wave
+  // (wrow, wkey) merges slice dt = wkey from all four groups and writes it. (Merging
+  // everything in one wave per row tile made that wave read three whole states and
+  // write every dim alone.)
+  constexpr int NDT = D / 32;
+  static_assert(NDT == NKG, "one 32-dim slice per key group");
+  constexpr int NX = 2 * NDT * (NKG - 1) * 16;  // floats per lane handed over
+  static_assert((NX + 2 * NKG * 2) * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
+  float* xs = reinterpret_cast<float*>(kv);       // [wrow][dt][group other than dt][16][64]
+  float* xml = xs + NX * 64;                      // [wrow][group][m, l][64]
+  auto xacc = [&](int row_tile, int dt, int grp, int r) -> float& {
+    const int g3 = grp < dt ? grp : grp - 1;
+    return xs[(((row_tile * NDT + dt) * (NKG - 1) + g3) * 16 + r) * 64 + lane];
+  };
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt == wkey) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xs[(base + dt * 16 + r) * 64 + lane] = acc[dt][r];
-    xs[(base + NV - 2) * 64 + lane] = m_run;
-    xs[(base + NV - 1) * 64 + lane] = l_run;
+    for (int r = 0; r < 16; ++r) xacc(wrow, dt, wkey, r) = acc[dt][r];
   }
+  xml[((wrow * NKG + wkey) * 2 + 0) * 64 + lane] = m_run;
+  xml[((wrow * NKG + wkey) * 2 + 1) * 64 + lane] = l_run;
   __syncthreads();
-  if (wkey > 0) return;
-  {
-    float m = m_run;
+  float mk[NKG], lk[NKG];
+  float m = kNegInf;
 #pragma unroll
-    for (int k = 1; k < NKG; ++k) m = fmaxf(m, xs[(((k - 1) * 2 + wrow) * NV + NV - 2) * 64 + lane]);
+  for (int k = 0; k < NKG; ++k) {
+    mk[k] = xml[((wrow * NKG + k) * 2 + 0) * 64 + lane];
+    lk[k] = xml[((wrow * NKG + k) * 2 + 1) * 64 + lane];
+    m = fmaxf(m, mk[k]);
+  }
+  float l = 0.f;
+  f32x16 o = f32x16{};
+  // slice dt = wkey: group k's part is this wave's registers for k == wkey, else LDS
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt != wkey) continue;
     if (m != kNegInf) {
-      const float a0 = __builtin_amdgcn_exp2f(m_run - m);
-      l_run *= a0;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= a0;
+      for (int k = 0; k < NKG; ++k) {
+        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
+        l += lk[k] * ak;
 #pragma unroll
-      for (int k = 1; k < NKG; ++k) {
-        const int base = ((k - 1) * 2 + wrow) * NV;
-        const float mk = xs[(base + NV - 2) * 64 + lane];
-        const float ak = mk == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk - m);
-        l_run += xs[(base + NV - 1) * 64 + lane] * ak;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] += xs[(base + dt * 16 + r) * 64 + lane] * ak;
+        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(wrow, dt, k, r)) * ak;
       }
-      m_run = m;
     }
   }
   if (!row_ok) return;
-  if (l_run > 0.f) {
+  if (l > 0.f) {
     float* wacc = a.ws + (item * BM + R) * (int64_t)D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * half;
-        *reinterpret_cast<float4*>(wacc + d0) =
-            make_float4(acc[dt][rg * 4 + 0], acc[dt][rg * 4 + 1], acc[dt][rg * 4 + 2], acc[dt][rg * 4 + 3]);
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+      *reinterpret_cast<float4*>(wacc + d0) = make_float4(o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]);
+    }
   }
-  if (half == 0) {  // (m, l) of the row; l == 0 means "no keys here"
+  if (wkey == 0 && half == 0) {  // (m, l) of the row; l == 0 means "no keys here"
     const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
     float* wml = a.ws + n_items * BM * (int64_t)D + (item * BM + R) * 2;
-    wml[0] = m_run;
-    wml[1] = l_run;
+    wml[0] = m;
+    wml[1] = l;
   }
 }
 
