@@ -38,6 +38,7 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-mllvm", "-amdgpu-mfma-vgpr-form",
+           "-mllvm", "-amdgpu-kernarg-preload-count=14",
            "-Wall", "-Wno-unused-function",
            *SOURCES, "-o", tmp]
     if verbose:

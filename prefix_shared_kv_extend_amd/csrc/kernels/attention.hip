@@ -943,12 +943,12 @@ struct BlockMeta {
   bool in;  // the lane holds a request of the block
 };
 __device__ __forceinline__ BlockMeta block_meta_load(const AttnArgs& a, int64_t rb, int lane, bool load_len = true) {
-  const int64_t qa = rb * a.bm / a.g;
-  int64_t qb = qa + a.bm / a.g;
-  if (qb > a.batch) qb = a.batch;
-  const int64_t r = qa + lane;
+  // 32-bit index math (rows < 2^31): 64-bit divisions cost hundreds of instructions here
+  const int qa = (int)rb * a.bm / a.g;
+  const int qb = min(qa + a.bm / a.g, a.batch);
+  const int r = qa + lane;
   const bool in = r < qb;
-  const int64_t rr = in ? r : qa;  // unconditional loads
+  const int rr = in ? r : qa;  // unconditional loads
   BlockMeta m;
   m.row = a.req_pool_idx[rr];
   m.len = load_len ? a.kv_len[rr] : 0;
@@ -1146,16 +1146,31 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
 // merges query heads w, w + W, ... : the shared part's split partials of the head's row
 // (written by the previous kernel) and the W chunk states, by log-sum-exp, then writes O.
 // Dynamic LDS: W*G*D floats of accumulators, then W*G (m, l) pairs.
+// Leading scalar arguments: preloaded copies of fields of `a` (see shared_kernel).
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(512) own_merge_kernel(const void* p_q, float* p_ws, const int32_t* p_rpi,
+                                                        const int32_t* p_len, const int32_t* p_sh, int32_t h_kv,
+                                                        int32_t bm, int32_t batch, int32_t split_rb, AttnArgs a) {
+  a.q = p_q;
+  a.ws = p_ws;
+  a.req_pool_idx = p_rpi;
+  a.kv_len = p_len;
+  a.shared_len = p_sh;
+  a.h_kv = h_kv;
+  a.h_q = h_kv * G;
+  a.g = G;
+  a.bm = bm;
+  a.batch = batch;
+  a.nsplit = split_rb & 255;  // nsplit <= 32, n_rb < 2^23 (checked on the host)
+  a.n_rb = split_rb >> 8;
   constexpr int E = D / 64;
   constexpr int PER = D / 64;
   extern __shared__ float own_lds[];
   const int W = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rh = blockIdx.x;
-  const int r = (int)(rh / a.h_kv);
-  const int h = (int)(rh % a.h_kv);
+  const int rh = blockIdx.x;
+  const int r = rh / a.h_kv;
+  const int h = rh - r * a.h_kv;
   float* s_acc = own_lds;
   float* s_ml = own_lds + (int64_t)W * G * D;
   const int nsplit = a.nsplit;
@@ -1166,16 +1181,20 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
   // accumulator rows of the first kPre splits: all fetched now, so the loads overlap the
   // own-key work (the partials come from the previous kernel)
   constexpr int kPre = 8;
+  // block metadata first: the own-key work waits for it, and loads complete in order
+  const int rb0 = r * G / a.bm;
+  const BlockMeta meta = block_meta_load(a, rb0, lane);
   float q[G][E];
   load_q_heads<T, D, G>(a, r, h, lane, q);
   float2 pre_ml = make_float2(kNegInf, 0.f);
   float pre_acc[kPre][PER];
   if (wave < G) {
-    const int64_t Grow = (int64_t)r * G + wave;
-    const int64_t item0 = ((int64_t)h * a.n_rb + Grow / a.bm) * nsplit;
-    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Grow % a.bm) * 2;
+    const int Grow = r * G + wave;
+    const int rbw = Grow / a.bm, Rw = Grow - rbw * a.bm;
+    const int64_t item0 = ((int64_t)h * a.n_rb + rbw) * nsplit;
+    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rw) * 2;
     pre_ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)(lane < nsplit ? lane : 0) * a.bm * 2);
-    const float* sh_acc = a.ws + (item0 * a.bm + Grow % a.bm) * (int64_t)D;
+    const float* sh_acc = a.ws + (item0 * a.bm + Rw) * (int64_t)D;
 #pragma unroll
     for (int j = 0; j < kPre; ++j)
 #pragma unroll
@@ -1183,13 +1202,11 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
         pre_acc[j][i] = sh_acc[(int64_t)(j < nsplit ? j : 0) * a.bm * D + lane + 64 * i];
   }
   {
-    // row and key count of request r from the block metadata's lanes (one round of loads)
-    const int64_t rb0 = ((int64_t)r * G) / a.bm;
-    const BlockMeta bm = block_meta_load(a, rb0, lane);
-    const int L = block_shared_len(a, bm, lane);
-    const int rl = (int)(r - rb0 * a.bm / G);
-    const int row = __builtin_amdgcn_readlane(bm.row, rl);
-    const int end = __builtin_amdgcn_readlane(bm.len, rl);
+    // row and key count of request r from the block metadata's lanes
+    const int L = block_shared_len(a, meta, lane);
+    const int rl = r - rb0 * a.bm / G;
+    const int row = __builtin_amdgcn_readlane(meta.row, rl);
+    const int end = __builtin_amdgcn_readlane(meta.len, rl);
     int first, per;
     const int n_act = own_chunks(a, row, end, L, first, per);
     float acc[G][E], m_run[G], l_run[G];
@@ -1219,9 +1236,9 @@ __global__ void __launch_bounds__(512) own_merge_kernel(AttnArgs a) {
   __syncthreads();
 
   for (int hl = wave; hl < G; hl += W) {
-    const int64_t Grow = (int64_t)r * G + hl;  // MFMA row of (request r, query head h*G + hl)
-    const int64_t rb = Grow / a.bm;
-    const int R = (int)(Grow % a.bm);
+    const int Grow = r * G + hl;  // MFMA row of (request r, query head h*G + hl)
+    const int rb = Grow / a.bm;
+    const int R = Grow - rb * a.bm;
     const int64_t item0 = ((int64_t)h * a.n_rb + rb) * nsplit;
     const float* sh_acc = a.ws + (item0 * a.bm + R) * (int64_t)D;
     const int64_t sh_stride = (int64_t)a.bm * D;
@@ -1392,9 +1409,23 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 // LDS layout and fragment reads: see "tiles loaded straight into LDS" above.
 constexpr int kShTiles = 4;
 
+// The leading scalar arguments repeat fields of `a`: the compiler preloads the first 14
+// argument dwords into SGPRs at wave launch (kernel-argument preloading), so the loads
+// of the block metadata and Q are issued without first waiting for an argument fetch.
 template <int D>
-__global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
+__global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
+                                                     const void* p_q, int32_t n_items, int32_t nsplit, int32_t n_rb,
+                                                     int32_t g, int32_t batch, int32_t h_q, AttnArgs a, AppendJob ap) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
+  a.req_pool_idx = p_rpi;
+  a.kv_len = p_len;
+  a.shared_len = p_sh;
+  a.q = p_q;
+  a.nsplit = nsplit;
+  a.n_rb = n_rb;
+  a.g = g;
+  a.batch = batch;
+  a.h_q = h_q;
   constexpr int NW = 8, NKG = 4;       // waves; key groups
   constexpr int BM = 64;
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -1410,20 +1441,43 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wrow = wave & 1, wkey = wave >> 1;  // 32-row tile, key group
   const int jrow = lane & 31, half = lane >> 5;
-  const int64_t item = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
-  const int split = (int)(item % a.nsplit);
-  const int64_t rb = (item / a.nsplit) % a.n_rb;
-  const int h = (int)(item / ((int64_t)a.nsplit * a.n_rb));
-  const int64_t G0 = rb * BM;
-  const int64_t qa = G0 / a.g;
-  int64_t qb = qa + BM / a.g;
-  if (qb > a.batch) qb = a.batch;
+  // 32-bit index math (grid and rows < 2^31): 64-bit divisions cost hundreds of
+  // instructions before the first load could issue
+  const int item = (int)xcd_remap(blockIdx.x, n_items);
+  const int isp = item / nsplit;
+  const int split = item - isp * nsplit;
+  const int h = isp / n_rb;
+  const int rb = isp - h * n_rb;
+  const int G0 = rb * BM;
+  const int qa = G0 / g;
+  const int qb = min(qa + BM / g, batch);
+
+  // block metadata and Q fragments of this lane's row (B operand of S^T = K Q^T) first:
+  // their addresses need only the preloaded arguments. Lengths are loaded from memory
+  // even when the job carries them (the value is then replaced below: this launch's
+  // append may be rewriting it).
+  a.bm = BM;
+  BlockMeta bmeta = block_meta_load(a, rb, lane, true);
+  const int R = wrow * 32 + jrow;
+  const int Gr = G0 + R;
+  const int t_row = Gr / g;
+  const bool row_ok = t_row < qb;
+  const int hq = h * g + (Gr - t_row * g);
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)(row_ok ? t_row : qa) * a.h_q + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
 
   // a decode step's append carried by this launch (rax_decode_step): token i's K/V row to
   // its slot, the slot into its row at len - 1, len to seq_len_dev (what
   // decode_append_kernel does). This kernel reads none of it: its keys end before every
   // request's newest position, and it takes the lengths from the job.
-  for (int i = blockIdx.x; i < ap.n; i += gridDim.x) {
+  for (int i = blockIdx.x; i < ap.n; i += n_items) {
     const int64_t slot = ap.slot[i];
     const int64_t cpr = ap.chunks_per_row;
     const u32x4* kn = reinterpret_cast<const u32x4*>(ap.k_new) + (int64_t)i * cpr;
@@ -1442,27 +1496,9 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
       else const_cast<int32_t*>(a.rtt)[row * a.rtt_stride + len - 1] = (int32_t)slot;
     }
   }
-
-  // block metadata, then Q fragments of this lane's row (B operand of S^T = K Q^T): the
-  // shared length is reduced only after both are in flight
-  BlockMeta bmeta = block_meta_load(a, rb, lane, ap.n == 0);
   if (ap.n > 0) {  // lengths after this step's append: from the job, not memory
-    const int64_t r = qa + lane;
+    const int r = qa + lane;
     bmeta.len = ap.len[r < ap.n ? r : qa];
-  }
-  const int R = wrow * 32 + jrow;
-  const int64_t Gr = G0 + R;
-  const int64_t t_row = Gr / a.g;
-  const bool row_ok = t_row < qb;
-  const int hq = h * a.g + (int)(Gr % a.g);
-  bf16x8 qf[NKS];
-  {
-    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((row_ok ? t_row : qa) * a.h_q + hq) * (int64_t)D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
-      qf[ks] = row_ok ? v : bf16x8{};
-    }
   }
   const bool all_rows_ok = __all(row_ok);
 
@@ -1644,7 +1680,7 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
   // measured 0.5-0.8 µs longer per decode call. (Non-temporal stores of O in extend or
   // of the appended rows measured slower.)
   if (l > 0.f) {
-    float* wacc = a.ws + (item * BM + R) * (int64_t)D;
+    float* wacc = a.ws + ((int64_t)item * BM + R) * D;
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = wkey * 32 + 8 * rg + 4 * half;
@@ -1653,8 +1689,7 @@ __global__ void __launch_bounds__(512) shared_kernel(AttnArgs a, AppendJob ap) {
     }
   }
   if (wkey == 0 && half == 0) {  // (m, l) of the row; l == 0 means "no keys here"
-    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-    float* wml = a.ws + n_items * BM * (int64_t)D + (item * BM + R) * 2;
+    float* wml = a.ws + (int64_t)n_items * BM * D + ((int64_t)item * BM + R) * 2;
     __builtin_nontemporal_store(m, wml);
     __builtin_nontemporal_store(l, wml + 1);
   }
@@ -1748,7 +1783,9 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const Append
         const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
         AppendJob none;
         none.n = 0;
-        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a, ap ? *ap : none);
+        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a.req_pool_idx, a.kv_len,
+                           a.shared_len, a.q, (int32_t)items, a.nsplit, a.n_rb, a.g, a.batch, a.h_q, a,
+                           ap ? *ap : none);
         return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
       }
     }
@@ -1766,17 +1803,20 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
   if constexpr (kDecode) {
     if (a.shared_only && a.own_fused == 1) {
       // one workgroup per (request, KV head), n_chunk waves; writes O (no merge kernel)
+      if (a.nsplit > 255 || a.n_rb >= (1 << 23)) return RAX_EINVAL;  // packed in one argument
       const unsigned blocks = (unsigned)((int64_t)a.batch * a.h_kv);
       const dim3 block((unsigned)(64 * a.n_chunk));
       const size_t lds = own_fused_lds_bytes(a.n_chunk, a.g, D);
+#define OWN_ARGS a.q, a.ws, a.req_pool_idx, a.kv_len, a.shared_len, a.h_kv, a.bm, a.batch, a.nsplit | a.n_rb << 8, a
       switch (a.g) {
-        case 1: hipLaunchKernelGGL((own_merge_kernel<T, D, 1>), dim3(blocks), block, lds, st, a); break;
-        case 2: hipLaunchKernelGGL((own_merge_kernel<T, D, 2>), dim3(blocks), block, lds, st, a); break;
-        case 4: hipLaunchKernelGGL((own_merge_kernel<T, D, 4>), dim3(blocks), block, lds, st, a); break;
-        case 8: hipLaunchKernelGGL((own_merge_kernel<T, D, 8>), dim3(blocks), block, lds, st, a); break;
-        case 16: hipLaunchKernelGGL((own_merge_kernel<T, D, 16>), dim3(blocks), block, lds, st, a); break;
+        case 1: hipLaunchKernelGGL((own_merge_kernel<T, D, 1>), dim3(blocks), block, lds, st, OWN_ARGS); break;
+        case 2: hipLaunchKernelGGL((own_merge_kernel<T, D, 2>), dim3(blocks), block, lds, st, OWN_ARGS); break;
+        case 4: hipLaunchKernelGGL((own_merge_kernel<T, D, 4>), dim3(blocks), block, lds, st, OWN_ARGS); break;
+        case 8: hipLaunchKernelGGL((own_merge_kernel<T, D, 8>), dim3(blocks), block, lds, st, OWN_ARGS); break;
+        case 16: hipLaunchKernelGGL((own_merge_kernel<T, D, 16>), dim3(blocks), block, lds, st, OWN_ARGS); break;
         default: return RAX_EINVAL;
       }
+#undef OWN_ARGS
       return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
     }
     if (a.shared_only && a.own_fused == 0) {
