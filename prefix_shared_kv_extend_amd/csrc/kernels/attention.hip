@@ -1473,27 +1473,25 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
     }
   }
 
-  // a decode step's append carried by this launch (rax_decode_step): token i's K/V row to
+  // A decode step's append carried by this launch (rax_decode_step): token i's K/V row to
   // its slot, the slot into its row at len - 1, len to seq_len_dev (what
   // decode_append_kernel does). This kernel reads none of it: its keys end before every
-  // request's newest position, and it takes the lengths from the job.
-  for (int i = blockIdx.x; i < ap.n; i += n_items) {
-    const int64_t slot = ap.slot[i];
-    const int64_t cpr = ap.chunks_per_row;
-    const u32x4* kn = reinterpret_cast<const u32x4*>(ap.k_new) + (int64_t)i * cpr;
-    const u32x4* vn = reinterpret_cast<const u32x4*>(ap.v_new) + (int64_t)i * cpr;
-    u32x4* kp = reinterpret_cast<u32x4*>(const_cast<void*>(a.k_pool)) + slot * cpr;
-    u32x4* vp = reinterpret_cast<u32x4*>(const_cast<void*>(a.v_pool)) + slot * cpr;
-    for (int64_t c = tid; c < cpr; c += 64 * NW) {
-      kp[c] = kn[c];
-      vp[c] = vn[c];
-    }
-    if (tid == 0) {
-      const int64_t row = a.req_pool_idx[i];
-      const int32_t len = ap.len[i];
-      ap.seq_len_dev[i] = len;
-      if (row < 0 || row >= a.rtt_rows) flag_error(RAX_DEVERR_ROW);
-      else const_cast<int32_t*>(a.rtt)[row * a.rtt_stride + len - 1] = (int32_t)slot;
+  // request's newest position, and it takes the lengths from the job. The workgroup's
+  // first token is loaded into registers now and stored after the tiles are computed, so
+  // that no wait for it sits on the path to the tile loads; further tokens (more tokens
+  // than workgroups) and row chunks past kApR per thread are copied at the end.
+  constexpr int kApR = 2;
+  const bool ap_mine = (int)blockIdx.x < ap.n;
+  const int64_t ap_cpr = ap.chunks_per_row;
+  u32x4 ap_k[kApR], ap_v[kApR];
+  if (ap_mine) {
+    const u32x4* kn = reinterpret_cast<const u32x4*>(ap.k_new) + (int64_t)blockIdx.x * ap_cpr;
+    const u32x4* vn = reinterpret_cast<const u32x4*>(ap.v_new) + (int64_t)blockIdx.x * ap_cpr;
+#pragma unroll
+    for (int j = 0; j < kApR; ++j) {
+      const int64_t c = tid + (int64_t)j * 64 * NW;
+      ap_k[j] = c < ap_cpr ? kn[c] : u32x4{};
+      ap_v[j] = c < ap_cpr ? vn[c] : u32x4{};
     }
   }
   if (ap.n > 0) {  // lengths after this step's append: from the job, not memory
@@ -1624,6 +1622,43 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
       }
     }
     __syncthreads();  // the next round overwrites the tiles
+  }
+
+  // the carried append (see above): this workgroup's first token from registers, then the
+  // rest
+  auto append_token = [&](int i, bool from_regs) {
+    const int64_t slot = ap.slot[i];
+    const u32x4* kn = reinterpret_cast<const u32x4*>(ap.k_new) + (int64_t)i * ap_cpr;
+    const u32x4* vn = reinterpret_cast<const u32x4*>(ap.v_new) + (int64_t)i * ap_cpr;
+    u32x4* kp = reinterpret_cast<u32x4*>(const_cast<void*>(a.k_pool)) + slot * ap_cpr;
+    u32x4* vp = reinterpret_cast<u32x4*>(const_cast<void*>(a.v_pool)) + slot * ap_cpr;
+    int64_t c0 = tid;
+    if (from_regs) {
+#pragma unroll
+      for (int j = 0; j < kApR; ++j) {
+        const int64_t c = tid + (int64_t)j * 64 * NW;
+        if (c < ap_cpr) {
+          kp[c] = ap_k[j];
+          vp[c] = ap_v[j];
+        }
+      }
+      c0 = tid + (int64_t)kApR * 64 * NW;
+    }
+    for (int64_t c = c0; c < ap_cpr; c += 64 * NW) {
+      kp[c] = kn[c];
+      vp[c] = vn[c];
+    }
+    if (tid == 0) {
+      const int64_t row = a.req_pool_idx[i];
+      const int32_t len = ap.len[i];
+      ap.seq_len_dev[i] = len;
+      if (row < 0 || row >= a.rtt_rows) flag_error(RAX_DEVERR_ROW);
+      else const_cast<int32_t*>(a.rtt)[row * a.rtt_stride + len - 1] = (int32_t)slot;
+    }
+  };
+  if (ap_mine) {
+    append_token(blockIdx.x, true);
+    for (int i = blockIdx.x + n_items; i < ap.n; i += n_items) append_token(i, false);
   }
 
   // The four key groups combine their states over LDS, the work split by dims: every wave
