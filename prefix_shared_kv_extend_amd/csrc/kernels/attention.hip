@@ -290,8 +290,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   // ---- work item: (KV head, row block, split)
   const int64_t item = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
   const int split = (int)(item % a.nsplit);
-  const int64_t rb = (item / a.nsplit) % a.n_rb;
+  int64_t rb = (item / a.nsplit) % a.n_rb;
   const int h = (int)(item / ((int64_t)a.nsplit * a.n_rb));
+  // extend: a KV head's row blocks from the last to the first, so that under causal
+  // masking the longest blocks are dispatched first and the short ones fill in behind
+  if (!kDecode) rb = a.n_rb - 1 - rb;
 
   const int64_t G0 = rb * BM;   // first MFMA row
   const int64_t qa = G0 / a.g;  // first query row (BM % g == 0)
