@@ -343,6 +343,56 @@ def projection_measure(dev):
     return out
 
 
+def decode_gqa_measure(n_steps=8):
+    """Decode attention on the decode-heavy workload: self-consistency, 256 branches of
+    U{0..1024} tokens off one 4096-token prefix, GQA 64/8 heads x 128, bf16. The two extend
+    steps run untimed; then each of the first n_steps decode calls (rax_decode_step, as
+    the runtime runs it) is replayed REPLAYS times through rax_decode_attention between
+    one HIP event pair. Algorithmic bytes per call: distinct K/V rows (the prefix once,
+    every branch's own rows), Q and O, 4 B per req_to_token entry."""
+    import torch
+    from prefix_shared_kv_extend_amd import _lib as L
+    from prefix_shared_kv_extend_amd.driver import JobRunner
+    from workloads import configs
+    job = configs.make(3)
+    runner = JobRunner(job, out_dtype=torch.bfloat16, record_log=False)
+    rt = runner.rt
+    first = next(i for i, st in enumerate(job.steps) if st.decode)
+    runner.run(steps=range(first))
+    prefix = len(job.requests[0].prompt)
+    elt = 2
+    us, nbytes = [], []
+
+    def on_decode(si, db, pairs, o):
+        q = torch.randn((len(db.rids), job.h_q, job.d), device=o.device).to(torch.bfloat16)
+        ws = rt._workspace(L.attention_workspace_bytes(True, len(db.rids), job.h_q, job.h_kv, job.d,
+                                                       db.max_seq_len))
+
+        def call():
+            L.decode_attention(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"], db.dev["seq_len"],
+                               db.max_seq_len, o, workspace=ws, shared_len=db.dev["shared_len"])
+        call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(REPLAYS):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / REPLAYS)
+        lens = db.seq_len.astype(np.int64)
+        distinct = prefix + int((lens - prefix).sum())
+        nbytes.append(distinct * 2 * job.h_kv * job.d * elt + 2 * len(lens) * job.h_q * job.d * elt
+                      + int(lens.sum()) * 4)
+
+    runner.run(steps=range(first, first + n_steps), on_decode=on_decode)
+    assert L.device_errors() == 0
+    gbs = sum(nbytes) / (sum(us) * 1e-6) / 1e9
+    return {"workload": "self-consistency: 256 branches of U{0..1024} tokens off a 4096-token prefix, "
+                        "GQA 64/8 x 128, bf16; first %d decode steps" % n_steps,
+            "us_per_call": sum(us) / len(us), "mb_per_call": sum(nbytes) / len(nbytes) / 1e6,
+            "gbs_unique": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
 def cpu_baseline(job, seconds):
     """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
     import torch
@@ -482,6 +532,7 @@ def main():
     out["scheduler"] = scheduler_ablation()
     out["host_tier"] = host_tier_measure(dev)
     out["qkv_projection"] = projection_measure(dev)
+    out["decode_gqa"] = decode_gqa_measure()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)

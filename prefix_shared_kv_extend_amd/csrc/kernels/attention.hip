@@ -86,7 +86,9 @@ struct AttnArgs {
   int32_t shared_only;        // 1: only the keys a block's requests share; always write partials
   float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
   int32_t n_chunk;            // most own-part key chunks per (request, KV head)
-  int32_t own_fused;          // 0: own_kernel + merge_kernel; 1: own_merge_kernel writes O
+  int32_t own_fused;          // 0: own_kernel + merge_kernel; 1: own_merge_kernel writes O;
+                              // 2: own_tile_kernel + merge_kernel
+  int32_t own_min;            // fewest own keys per chunk (own_chunks)
 };
 
 template <typename T, int D, int NW, int RT, int KS>
@@ -983,16 +985,18 @@ __device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, i
 
 // Own keys of request r in split decode: positions [L, seq_len), L the shared length of the
 // request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
-// at least kOwnMin keys. Returns n_act (0: nothing of its own, or an invalid row) and sets
-// the first own position and the chunk size.
-constexpr int kOwnMin = 32;
+// at least a.own_min keys. Returns n_act (0: nothing of its own, or an invalid row) and
+// sets the first own position and the chunk size.
+constexpr int kOwnMin = 32;       // own_kernel / own_merge_kernel
+constexpr int kOwnTileMin = 128;  // own_tile_kernel
+constexpr int kOwnTileChunks = 4;
 __device__ __forceinline__ int own_chunks(const AttnArgs& a, int row, int end, int L, int& first, int& per) {
   first = L;
   per = 0;
   if (row < 0 || row >= a.rtt_rows || end < 0 || end > a.rtt_stride) return 0;
   const int n = end - L;
   if (n <= 0) return 0;
-  const int n_act = min(a.n_chunk, (n + kOwnMin - 1) / kOwnMin);
+  const int n_act = min(a.n_chunk, (n + a.own_min - 1) / a.own_min);
   per = (n + n_act - 1) / n_act;
   return n_act;
 }
@@ -1042,25 +1046,36 @@ __device__ __forceinline__ void own_chunk(const AttnArgs& a, int h, int row, int
   const int my_key = (lane % P) / G;
   const int my_hl = lane % G;
 
-  for (int j0 = start; j0 < stop; j0 += KB) {
-    const int nk = min(KB, stop - j0);
+  // Load rounds of KL keys: one slot-id load, then every K and V piece of the round in
+  // flight at once; the round's keys are then scored in batches of KB keys (P pairs). With
+  // query-head groups (G > 1) a batch has fewer keys, but a round still fetches 32, so the
+  // number of dependent round trips does not grow with G.
+  constexpr int KL = sizeof(Raw) <= 4 && KB < 32 ? 32 : KB;
+  constexpr int NSUB = KL / KB;
+  static_assert(KL % KB == 0 && KL <= 64, "load round");
+  for (int j0 = start; j0 < stop; j0 += KL) {
+    const int nk = min(KL, stop - j0);
     const int raw_slot = rtt_row[j0 + min(lane, nk - 1)];
     int slot = -1;
     if (lane < nk) {
       if (raw_slot >= 0 && raw_slot < a.num_slots) slot = raw_slot;
       else flag_error(RAX_DEVERR_SLOT);
     }
-    const uint64_t valid = __ballot(slot >= 0);
-    Raw kr[KB], vr[KB];
+    const uint64_t valid_all = __ballot(slot >= 0);
+    Raw kr[KL], vr[KL];
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
+    for (int kk = 0; kk < KL; ++kk) {
       const int s = __builtin_amdgcn_readlane(slot, kk);
       const int64_t off = (int64_t)(s < 0 ? 0 : s) * row_elems;
       kr[kk] = *reinterpret_cast<const Raw*>(kb + off);
       vr[kk] = *reinterpret_cast<const Raw*>(vb + off);
     }
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) vr[kk] = ((valid >> kk) & 1) ? vr[kk] : (Raw)0;
+    for (int kk = 0; kk < KL; ++kk) vr[kk] = ((valid_all >> kk) & 1) ? vr[kk] : (Raw)0;
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+    if (sb * KB >= nk) break;  // no keys left in this round
+    const uint64_t valid = valid_all >> (sb * KB);
     float v[P];
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
@@ -1068,7 +1083,7 @@ __device__ __forceinline__ void own_chunk(const AttnArgs& a, int h, int row, int
       for (int hl = 0; hl < G; ++hl) {
         float x = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) x += q[hl][e] * piece_elem<T, E>(kr[kk], e);
+        for (int e = 0; e < E; ++e) x += q[hl][e] * piece_elem<T, E>(kr[sb * KB + kk], e);
         v[kk * G + hl] = x;
       }
     wave_reduce_pairs<P>(v, lane);
@@ -1099,8 +1114,9 @@ __device__ __forceinline__ void own_chunk(const AttnArgs& a, int h, int row, int
       for (int hl = 0; hl < G; ++hl) {
         const float pk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), kk * G + hl));
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[hl][e] += pk * piece_elem<T, E>(vr[kk], e);
+        for (int e = 0; e < E; ++e) acc[hl][e] += pk * piece_elem<T, E>(vr[sb * KB + kk], e);
       }
+    }
   }
 }
 
@@ -1733,6 +1749,236 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
   }
 }
 
+// Own part of split decode on MFMA for query-head groups (g = 2..16), bf16, D = 128.
+// own_chunk scores 32 / g keys per batch, each batch a chain of cross-lane reductions and
+// broadcasts, so for g > 1 that work bounds it rather than memory (self-consistency
+// decode, GQA 64/8: 0.56 ms per call for 0.59 GB). Here a workgroup takes one own chunk
+// of (request t, KV head h): the chunk's keys go straight into LDS in rounds of up to
+// kShTiles 64-key tiles, as in shared_kernel, and the g query heads of (t, h) are the
+// rows of one 32-row MFMA tile (rows past g are padding). Four waves are four key groups
+// taking the 32-key halves round-robin; they combine split by dims, and the chunk's
+// partial goes to the workspace in own_kernel's layout, for merge_kernel.
+template <int D>
+__global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
+  static_assert(D == 128, "the swizzle assumes 16 chunks per row");
+  constexpr int NW = 4, NKG = 4;
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RB = D * 2;            // bytes per row
+  constexpr int TB = BN * RB;          // bytes per K (or V) tile
+  constexpr int RPI = 1024 / RB;       // rows per 1 KB global-to-LDS instruction
+  constexpr int NI = BN / RPI;         // instructions per tile
+  constexpr int NKS = D / 16;
+  __shared__ __align__(16) char kv[2 * kShTiles * TB];  // K tiles, then V tiles
+  __shared__ int32_t slot[kShTiles * BN];
+  const uint32_t kv_lds = lds_addr(kv);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wkey = wave;  // key group
+  const int jrow = lane & 31, half = lane >> 5;
+  const int G = a.g;
+  const int n_rh = a.batch * a.h_kv;
+  const int c = blockIdx.x / n_rh;  // chunk slowest: chunks past every request's keys exit together
+  const int rh = blockIdx.x - c * n_rh;
+  const int t = rh / a.h_kv;
+  const int h = rh - t * a.h_kv;
+
+  // metadata of the request's row block, then Q of this lane's row (query head h*G + jrow
+  // of request t; the B operand of S^T = K Q^T)
+  const int rb0 = t * G / a.bm;
+  const BlockMeta meta = block_meta_load(a, rb0, lane);
+  const bool row_ok = jrow < G;
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp =
+        reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? jrow : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
+  const int L = block_shared_len(a, meta, lane);
+  const int rl = t - rb0 * a.bm / G;
+  const int row_t = __builtin_amdgcn_readlane(meta.row, rl);
+  const int end = __builtin_amdgcn_readlane(meta.len, rl);
+  int first, per;
+  const int n_act = own_chunks(a, row_t, end, L, first, per);
+  if (c >= n_act) return;  // the same for the whole workgroup
+  const int start = first + c * per;
+  const int stop = min(start + per, end);
+  const int n_tiles = (stop - start + BN - 1) / BN;
+  const int64_t row_bytes = (int64_t)a.h_kv * RB;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
+  const int32_t* rtt_row = a.rtt + (int64_t)row_t * a.rtt_stride;  // row_t valid: n_act > 0
+
+  // slot ids of the round's positions, then every K and V row of its tiles into LDS
+  auto issue = [&](int tb, int nt) {
+    for (int i = tid; i < nt * BN; i += 64 * NW) {
+      const int pos = start + tb * BN + i;
+      const bool in = pos < stop;
+      int sv = rtt_row[in ? pos : start];
+      if (in && (sv < 0 || sv >= a.num_slots)) {
+        flag_error(RAX_DEVERR_SLOT);
+        sv = -1;
+      }
+      slot[i] = in ? sv : -1;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+#pragma unroll
+      for (int q = wave; q < NI; q += NW) {
+        const int r = q * RPI + lane / CH;
+        const int sv = slot[tt * BN + r];
+        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
+        lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + tt * TB + q * 1024));
+        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (kShTiles + tt) * TB + q * 1024));
+      }
+    }
+  };
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  for (int tb = 0; tb < n_tiles; tb += kShTiles) {
+    const int nt = min(kShTiles, n_tiles - tb);
+    issue(tb, nt);
+    // each wave issued 2 * NI / NW loads per tile, in tile order, and they retire in order
+    static_assert(2 * NI / NW == 8 && kShTiles == 4, "wait counts below");
+    const int last_cnt = min(BN, stop - (start + (tb + nt - 1) * BN));
+    for (int part = 0; part < 2; ++part) {
+      const int t0 = part * 2, t1 = min(nt, t0 + 2);  // tiles of this part
+      if (t0 >= nt) break;
+      // vmcnt is split in the immediate: bits [3:0] and [15:14]
+      if (part == 0 && nt == 4) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16): tiles 2, 3 may fly
+      else if (part == 0 && nt == 3) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+      else __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("s_barrier" ::: "memory");
+      // rows past the chunk read slot 0: zero them (their scores are masked; zeros keep P.V finite)
+      if (last_cnt < BN && nt - 1 < t1) {
+        for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
+          const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
+          *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kv + kShTiles * TB + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+      }
+      for (int j = 2 * t0 + wkey; j < 2 * t1; j += NKG) {
+        const int tt = j >> 1, sub = j & 1;
+        const int cnt = min(BN, stop - (start + (tb + tt) * BN));
+        const char* kt = kv + tt * TB;
+        const char* vt = kv + (kShTiles + tt) * TB;
+        f32x16 sc = f32x16{};
+        const int kr = sub * 32 + jrow;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
+        // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float v = row_ok && key < cnt ? sc[r] : kNegInf;
+          sc[r] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        if (__any(mx > m_run + kLazy)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+          m_run = m_new;
+        }
+        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
+          sc[r] = pv;
+          psum += pv;
+        }
+        psum += __shfl_xor(psum, 32);
+        l_run += psum;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the next round overwrites the tiles
+  }
+
+  // the four key groups combine split by dims (as in shared_kernel, one row tile)
+  constexpr int NDT = D / 32;
+  static_assert(NDT == NKG, "one 32-dim slice per key group");
+  constexpr int NX = NDT * (NKG - 1) * 16;  // floats per lane handed over
+  static_assert((NX + NKG * 2) * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
+  float* xs = reinterpret_cast<float*>(kv);  // [dt][group other than dt][16][64]
+  float* xml = xs + NX * 64;                 // [group][m, l][64]
+  auto xacc = [&](int dt, int grp, int r) -> float& {
+    const int g3 = grp < dt ? grp : grp - 1;
+    return xs[((dt * (NKG - 1) + g3) * 16 + r) * 64 + lane];
+  };
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt == wkey) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xacc(dt, wkey, r) = acc[dt][r];
+  }
+  xml[(wkey * 2 + 0) * 64 + lane] = m_run;
+  xml[(wkey * 2 + 1) * 64 + lane] = l_run;
+  __syncthreads();
+  float mk[NKG], lk[NKG];
+  float m = kNegInf;
+#pragma unroll
+  for (int k = 0; k < NKG; ++k) {
+    mk[k] = xml[(k * 2 + 0) * 64 + lane];
+    lk[k] = xml[(k * 2 + 1) * 64 + lane];
+    m = fmaxf(m, mk[k]);
+  }
+  float l = 0.f;
+  f32x16 o = f32x16{};
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt != wkey) continue;
+    if (m != kNegInf) {
+#pragma unroll
+      for (int k = 0; k < NKG; ++k) {
+        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
+        l += lk[k] * ak;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(dt, k, r)) * ak;
+      }
+    }
+  }
+  if (!row_ok) return;
+  // partial of (request t, KV head h, chunk c), query head jrow, in own_kernel's layout
+  const int64_t item = (int64_t)rh * a.n_chunk + c;
+  if (l > 0.f) {
+    float* wacc = a.ws_own + (item * G + jrow) * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+      __builtin_nontemporal_store(f32x4{o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]},
+                                  reinterpret_cast<f32x4*>(wacc + d0));
+    }
+  }
+  if (wkey == 0 && half == 0) {
+    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + jrow) * 2;
+    __builtin_nontemporal_store(m, wml);
+    __builtin_nontemporal_store(l, wml + 1);
+  }
+}
+
 // ------------------------------------------------------------------ host side
 struct Shape {
   int nw, rt, pd, ks;
@@ -1862,6 +2108,17 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
       rc = launch_own<T, D>(a, st);
       if (rc != RAX_OK) return rc;
     }
+    if (a.shared_only && a.own_fused == 2) {
+      if constexpr (sizeof(T) == 2 && D == 128) {
+        const int64_t items = (int64_t)a.batch * a.h_kv * a.n_chunk;
+        if (items > INT32_MAX) return RAX_EINVAL;
+        hipLaunchKernelGGL((own_tile_kernel<D>), dim3((unsigned)items), dim3(256), 0, st, a);
+        rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+        if (rc != RAX_OK) return rc;
+      } else {
+        return RAX_EINVAL;
+      }
+    }
   }
   if (a.nsplit > 1 || a.shared_only) return launch_merge<D>(a, st);
   return RAX_OK;
@@ -1886,7 +2143,8 @@ struct DecodeLayout {
   int64_t sh_acc, sh_ml, own_acc, own_ml, total;
   int32_t nsplit, n_rb, n_chunk, bm;
   bool split_decode;
-  int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel
+  int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_tile_kernel + merge_kernel
+  int32_t own_min;   // fewest keys per own chunk
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
@@ -1912,10 +2170,21 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   // few-shot decode, 4096 waves 15.4 us, 8192 waves 20.2 us, 2048 waves 16.7 us.
   constexpr int64_t kOwnWaves = 4096;
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
-  const int64_t by_len = (max_seq_len + kOwnMin - 1) / kOwnMin;
-  l.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>({64 - l.nsplit, by_len, (kOwnWaves + pairs - 1) / pairs}));
-  // the chunks of one (request, KV head) fit one workgroup: merge in LDS, no own partials
-  l.own_mode = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds ? 1 : 0;
+  if (dt == RAX_BF16 && d == 128 && g >= 2) {
+    // query-head groups: own keys on MFMA (own_tile_kernel), chunks of at least
+    // kOwnTileMin keys, at most kOwnTileChunks per (request, KV head); longer chunks take
+    // several rounds of tiles
+    l.own_min = kOwnTileMin;
+    l.n_chunk = (int32_t)std::max<int64_t>(
+        1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnTileMin - 1) / kOwnTileMin, kOwnTileChunks}));
+    l.own_mode = 2;
+  } else {
+    l.own_min = kOwnMin;
+    const int64_t by_len = (max_seq_len + kOwnMin - 1) / kOwnMin;
+    l.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>({64 - l.nsplit, by_len, (kOwnWaves + pairs - 1) / pairs}));
+    // the chunks of one (request, KV head) fit one workgroup: merge in LDS, no own partials
+    l.own_mode = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds ? 1 : 0;
+  }
   const int64_t sh_items = (int64_t)h_kv * l.n_rb * l.nsplit;
   const int64_t own_rows = l.own_mode == 1 ? 0 : batch * h_kv * l.n_chunk * g;
   l.sh_acc = sh_items * l.bm * d;
@@ -2062,6 +2331,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
       a.ws_own = w + l.sh_acc + l.sh_ml;
       a.n_chunk = l.n_chunk;
       a.own_fused = l.own_mode;
+      a.own_min = l.own_min;
     }
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
