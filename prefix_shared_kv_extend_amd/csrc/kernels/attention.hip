@@ -989,7 +989,8 @@ __device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, i
 // sets the first own position and the chunk size.
 constexpr int kOwnMin = 32;       // own_kernel / own_merge_kernel
 constexpr int kOwnTileMin = 128;  // own_tile_kernel
-constexpr int kOwnTileChunks = 4;
+constexpr int kOwnTileChunks = 8;
+constexpr int kOwnTiles = 2;       // own_tile_kernel: 64-key tiles per round
 __device__ __forceinline__ int own_chunks(const AttnArgs& a, int row, int end, int L, int& first, int& per) {
   first = L;
   per = 0;
@@ -1754,12 +1755,13 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
 // broadcasts, so for g > 1 that work bounds it rather than memory (self-consistency
 // decode, GQA 64/8: 0.56 ms per call for 0.59 GB). Here a workgroup takes one own chunk
 // of (request t, KV head h): the chunk's keys go straight into LDS in rounds of up to
-// kShTiles 64-key tiles, as in shared_kernel, and the g query heads of (t, h) are the
+// kOwnTiles 64-key tiles, as in shared_kernel (64 KB of LDS: two workgroups per CU, whose
+// round trips overlap), and the g query heads of (t, h) are the
 // rows of one 32-row MFMA tile (rows past g are padding). Four waves are four key groups
 // taking the 32-key halves round-robin; they combine split by dims, and the chunk's
 // partial goes to the workspace in own_kernel's layout, for merge_kernel.
 template <int D>
-__global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) own_tile_kernel(AttnArgs a) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
   constexpr int NW = 4, NKG = 4;
   constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -1768,8 +1770,9 @@ __global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
   constexpr int RPI = 1024 / RB;       // rows per 1 KB global-to-LDS instruction
   constexpr int NI = BN / RPI;         // instructions per tile
   constexpr int NKS = D / 16;
-  __shared__ __align__(16) char kv[2 * kShTiles * TB];  // K tiles, then V tiles
-  __shared__ int32_t slot[kShTiles * BN];
+  constexpr int OT = kOwnTiles;                           // tiles per round
+  __shared__ __align__(16) char kv[2 * OT * TB];          // K tiles, then V tiles
+  __shared__ int32_t slot[OT * BN];
   const uint32_t kv_lds = lds_addr(kv);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1832,7 +1835,7 @@ __global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
         const int sv = slot[tt * BN + r];
         const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
         lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + tt * TB + q * 1024));
-        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (kShTiles + tt) * TB + q * 1024));
+        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (OT + tt) * TB + q * 1024));
       }
     }
   };
@@ -1841,18 +1844,17 @@ __global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int tb = 0; tb < n_tiles; tb += kShTiles) {
-    const int nt = min(kShTiles, n_tiles - tb);
+  for (int tb = 0; tb < n_tiles; tb += OT) {
+    const int nt = min(OT, n_tiles - tb);
     issue(tb, nt);
-    // each wave issued 2 * NI / NW loads per tile, in tile order, and they retire in order
-    static_assert(2 * NI / NW == 8 && kShTiles == 4, "wait counts below");
+    // each wave issued 2 * NI / NW = 8 loads per tile, in tile order, and they retire in
+    // order: with two tiles, the first is computed while the second may still arrive
+    static_assert(2 * NI / NW == 8 && OT == 2, "wait counts below");
     const int last_cnt = min(BN, stop - (start + (tb + nt - 1) * BN));
     for (int part = 0; part < 2; ++part) {
-      const int t0 = part * 2, t1 = min(nt, t0 + 2);  // tiles of this part
+      const int t0 = part, t1 = min(nt, t0 + 1);  // tile of this part
       if (t0 >= nt) break;
-      // vmcnt is split in the immediate: bits [3:0] and [15:14]
-      if (part == 0 && nt == 4) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16): tiles 2, 3 may fly
-      else if (part == 0 && nt == 3) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+      if (part == 0 && nt == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 1 may fly
       else __builtin_amdgcn_s_waitcnt(0);
       asm volatile("s_barrier" ::: "memory");
       // rows past the chunk read slot 0: zero them (their scores are masked; zeros keep P.V finite)
@@ -1860,7 +1862,7 @@ __global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
         for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
           const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
           *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(kv + kShTiles * TB + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kv + OT * TB + off) = u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
       }
@@ -1868,7 +1870,7 @@ __global__ void __launch_bounds__(256) own_tile_kernel(AttnArgs a) {
         const int tt = j >> 1, sub = j & 1;
         const int cnt = min(BN, stop - (start + (tb + tt) * BN));
         const char* kt = kv + tt * TB;
-        const char* vt = kv + (kShTiles + tt) * TB;
+        const char* vt = kv + (OT + tt) * TB;
         f32x16 sc = f32x16{};
         const int kr = sub * 32 + jrow;
 #pragma unroll
