@@ -471,3 +471,55 @@ def test_decode_step_folded_append_equals_separate_calls():
     assert torch.equal(ra.rtt, rb.rtt) and np.array_equal(ra.rows, rb.rows)
     assert torch.equal(ra.k_pool, rb.k_pool) and torch.equal(ra.v_pool, rb.v_pool)
     assert _lib.device_errors() == 0
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(4, 2), (32, 4), (64, 4)])
+def test_decode_query_head_groups_direct(h_q, h_kv):
+    """Decode attention with query-head groups (own keys on MFMA tiles) on hand-built rows:
+    a 150-key prefix shared by all requests (hinted), then own ranges of 0..2600 keys, so
+    that chunks are empty, shorter than a tile, exactly one or two tiles, ragged, several
+    per (request, KV head), and longer than one round of tiles. Every output against fp64
+    attention over the request's keys (oracle.attention.attend)."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    say(f"decode, query-head groups {h_q}/{h_kv}: own ranges 0..2600 keys past a 150-key shared prefix")
+    d, S, P = 128, 16384, 150
+    own = [0, 1, 63, 64, 65, 127, 128, 129, 300, 1100, 2600, 7]
+    B = len(own)
+    W = P + max(own) + 2
+    gen = torch.Generator().manual_seed(23 + h_q)
+    k_pool = torch.randn((S, h_kv, d), generator=gen).to(torch.bfloat16)
+    v_pool = torch.randn((S, h_kv, d), generator=gen).to(torch.bfloat16)
+    q = torch.randn((B, h_q, d), generator=gen).to(torch.bfloat16)
+    perm = torch.randperm(S, generator=gen).numpy().astype(np.int32)
+    rtt = np.full((B + 3, W), -1, dtype=np.int32)
+    rows = np.arange(B, dtype=np.int32) + 2                 # rows 0, 1 stay unused
+    prefix_slots = perm[:P]
+    used = P
+    lens = []
+    for i, n in enumerate(own):
+        ln = P + n + 1                                      # the newest key is always in the own part
+        rtt[rows[i], :P] = prefix_slots
+        rtt[rows[i], P:ln] = perm[used: used + ln - P]
+        used += ln - P
+        lens.append(ln)
+    lens = np.array(lens, dtype=np.int32)
+    hints = np.full(B, P, dtype=np.int32)
+    dev = lambda x: torch.as_tensor(x).cuda()
+    ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, int(lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    ob = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
+    _lib.decode_attention(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(lens), int(lens.max()), ob,
+                          workspace=ws, shared_len=dev(hints))
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    got = ob.float().cpu().numpy()
+    kf, vf, qf = k_pool.float().numpy(), v_pool.float().numpy(), q.float().numpy()
+    worst = 0.0
+    for i in range(B):
+        sl = rtt[rows[i], : lens[i]]
+        ref = attend(qf[i], kf[sl], vf[sl])
+        err = float(np.abs(got[i] - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], f"request {i} (own {own[i]}): max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g}")
