@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the sections beside the headline (scheduler, host tier, projection, GQA decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", default=TRAFFIC_JSON, help="counter summary with HBM bytes per launch")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
@@ -529,10 +531,11 @@ def main():
                     "attention_kernel_ms_per_step": (per_step_ext + per_step_dec) * 1e-3,
                     "host_bound": host_ms > 0.97 * ms},
     }
-    out["scheduler"] = scheduler_ablation()
-    out["host_tier"] = host_tier_measure(dev)
-    out["qkv_projection"] = projection_measure(dev)
-    out["decode_gqa"] = decode_gqa_measure()
+    if not args.no_side:
+        out["scheduler"] = scheduler_ablation()
+        out["host_tier"] = host_tier_measure(dev)
+        out["qkv_projection"] = projection_measure(dev)
+        out["decode_gqa"] = decode_gqa_measure()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)
