@@ -89,6 +89,7 @@ struct AttnArgs {
   int32_t own_fused;          // 0: own_kernel + merge_kernel; 1: own_merge_kernel writes O;
                               // 2: own_tile_kernel + merge_kernel
   int32_t own_min;            // fewest own keys per chunk (own_chunks)
+  int32_t sh_small;           // 1: shared part with 4-wave workgroups, 2 tiles per round
 };
 
 template <typename T, int D, int NW, int RT, int KS>
@@ -1432,8 +1433,9 @@ constexpr int kShTiles = 4;
 // The leading scalar arguments repeat fields of `a`: the compiler preloads the first 14
 // argument dwords into SGPRs at wave launch (kernel-argument preloading), so the loads
 // of the block metadata and Q are issued without first waiting for an argument fetch.
-template <int D>
-__global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
+template <int D, int NKG, int ST>
+__global__ void __launch_bounds__(128 * NKG) __attribute__((amdgpu_waves_per_eu(NKG == 2 ? 2 : 1)))
+shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
                                                      const void* p_q, int32_t n_items, int32_t nsplit, int32_t n_rb,
                                                      int32_t g, int32_t batch, int32_t h_q, AttnArgs a, AppendJob ap) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
@@ -1446,7 +1448,7 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
   a.g = g;
   a.batch = batch;
   a.h_q = h_q;
-  constexpr int NW = 8, NKG = 4;       // waves; key groups
+  constexpr int NW = 2 * NKG;          // waves: two row tiles x NKG key groups
   constexpr int BM = 64;
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int RB = D * 2;            // bytes per row
@@ -1454,8 +1456,8 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
   constexpr int RPI = 1024 / RB;       // rows per 1 KB global-to-LDS instruction
   constexpr int NI = BN / RPI;         // instructions per tile
   constexpr int NKS = D / 16;
-  __shared__ __align__(16) char kv[2 * kShTiles * TB];  // K tiles, then V tiles
-  __shared__ int32_t slot[kShTiles * BN];
+  __shared__ __align__(16) char kv[2 * ST * TB];  // ST K tiles, then ST V tiles
+  __shared__ int32_t slot[ST * BN];
   const uint32_t kv_lds = lds_addr(kv);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1549,7 +1551,7 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
         const int sv = slot[t * BN + r];
         const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
         lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + t * TB + q * 1024));
-        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (kShTiles + t) * TB + q * 1024));
+        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (ST + t) * TB + q * 1024));
       }
     }
   };
@@ -1558,17 +1560,21 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int tb = t_begin; tb < t_end; tb += kShTiles) {
-    const int nt = min(kShTiles, t_end - tb);
+  for (int tb = t_begin; tb < t_end; tb += ST) {
+    const int nt = min(ST, t_end - tb);
     issue(tb, nt);
-    // each wave issued 2 * NI / NW loads per tile, in tile order, and they retire in order
-    static_assert(2 * NI / NW == 4 && kShTiles == 4, "wait counts below");
+    // each wave issued LPT = 2 * NI / NW loads per tile, in tile order, and they retire in
+    // order; the round is computed in two parts of ST / 2 tiles, the second part's loads
+    // may still fly during the first
+    constexpr int PT = ST / 2, LPT = 2 * NI / NW;
+    static_assert(ST % 2 == 0 && PT * LPT <= 15, "vmcnt immediates below (bits [3:0])");
     const int last_cnt = min(BN, L - (tb + nt - 1) * BN);
     for (int part = 0; part < 2; ++part) {
-      const int t0 = part * 2, t1 = min(nt, t0 + 2);  // tiles of this part
+      const int t0 = part * PT, t1 = min(nt, t0 + PT);  // tiles of this part
       if (t0 >= nt) break;
-      if (part == 0 && nt == 4) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8): tiles 2, 3 may fly
-      else if (part == 0 && nt == 3) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      const int fly = part == 0 ? (nt - t1) * LPT : 0;  // loads of later tiles that may fly
+      if (fly == 8) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+      else if (fly == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
       else __builtin_amdgcn_s_waitcnt(0);
       // a plain barrier: __syncthreads' release fence would wait for every load in flight
       asm volatile("s_barrier" ::: "memory");
@@ -1577,7 +1583,7 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
         for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
           const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
           *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(kv + kShTiles * TB + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kv + ST * TB + off) = u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
       }
@@ -1586,7 +1592,7 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
       const int t = j >> 1, sub = j & 1;
       const int cnt = min(BN, L - (tb + t) * BN);
       const char* kt = kv + t * TB;
-      const char* vt = kv + (kShTiles + t) * TB;
+      const char* vt = kv + (ST + t) * TB;
       // S^T over this wave's 32 keys: row kr of the tile, dims ks*16 + half*8
       f32x16 sc = f32x16{};
       const int kr = sub * 32 + jrow;
@@ -1681,52 +1687,58 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
     for (int i = blockIdx.x + n_items; i < ap.n; i += n_items) append_token(i, false);
   }
 
-  // The four key groups combine their states over LDS, the work split by dims: every wave
-  // hands the other groups its accumulator slices dt != wkey and its (m, l); then wave
-  // (wrow, wkey) merges slice dt = wkey from all four groups and writes it. (Merging
-  // everything in one wave per row tile made that wave read three whole states and
-  // write every dim alone.)
+  // The key groups combine their states over LDS, the work split by dims: slice dt (32
+  // dims) belongs to group dt % NKG. Every wave hands the owners of the other slices its
+  // parts of them and its (m, l); then each wave merges its own slices from all groups and
+  // writes them. (Merging everything in one wave per row tile made that wave read every
+  // other state and write every dim alone.)
   constexpr int NDT = D / 32;
-  static_assert(NDT == NKG, "one 32-dim slice per key group");
+  static_assert(NDT % NKG == 0, "whole 32-dim slices per key group");
+  constexpr int SPG = NDT / NKG;                // slices per group
   constexpr int NX = 2 * NDT * (NKG - 1) * 16;  // floats per lane handed over
   static_assert((NX + 2 * NKG * 2) * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
-  float* xs = reinterpret_cast<float*>(kv);       // [wrow][dt][group other than dt][16][64]
+  float* xs = reinterpret_cast<float*>(kv);       // [wrow][dt][group other than dt's owner][16][64]
   float* xml = xs + NX * 64;                      // [wrow][group][m, l][64]
   auto xacc = [&](int row_tile, int dt, int grp, int r) -> float& {
-    const int g3 = grp < dt ? grp : grp - 1;
+    const int own = dt % NKG;
+    const int g3 = grp < own ? grp : grp - 1;
     return xs[(((row_tile * NDT + dt) * (NKG - 1) + g3) * 16 + r) * 64 + lane];
   };
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    if (dt == wkey) continue;
+    if (dt % NKG == wkey) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) xacc(wrow, dt, wkey, r) = acc[dt][r];
   }
   xml[((wrow * NKG + wkey) * 2 + 0) * 64 + lane] = m_run;
   xml[((wrow * NKG + wkey) * 2 + 1) * 64 + lane] = l_run;
   __syncthreads();
-  float mk[NKG], lk[NKG];
+  float mk[NKG], ak[NKG];
   float m = kNegInf;
 #pragma unroll
-  for (int k = 0; k < NKG; ++k) {
-    mk[k] = xml[((wrow * NKG + k) * 2 + 0) * 64 + lane];
-    lk[k] = xml[((wrow * NKG + k) * 2 + 1) * 64 + lane];
-    m = fmaxf(m, mk[k]);
+  for (int kg = 0; kg < NKG; ++kg) {
+    mk[kg] = xml[((wrow * NKG + kg) * 2 + 0) * 64 + lane];
+    m = fmaxf(m, mk[kg]);
   }
   float l = 0.f;
-  f32x16 o = f32x16{};
-  // slice dt = wkey: group k's part is this wave's registers for k == wkey, else LDS
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    if (dt != wkey) continue;
-    if (m != kNegInf) {
+  for (int kg = 0; kg < NKG; ++kg) {
+    ak[kg] = m == kNegInf || mk[kg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[kg] - m);
+    l += xml[((wrow * NKG + kg) * 2 + 1) * 64 + lane] * ak[kg];
+  }
+  // slices dt = wkey + sp * NKG: group kg's part is this wave's registers for kg == wkey,
+  // else LDS
+  f32x16 o[SPG];
 #pragma unroll
-      for (int k = 0; k < NKG; ++k) {
-        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
-        l += lk[k] * ak;
+  for (int sp = 0; sp < SPG; ++sp) {
+    o[sp] = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(wrow, dt, k, r)) * ak;
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (dt != wkey + sp * NKG) continue;
+#pragma unroll
+      for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[sp][r] += (kg == wkey ? acc[dt][r] : xacc(wrow, dt, kg, r)) * ak[kg];
     }
   }
   if (!row_ok) return;
@@ -1737,11 +1749,13 @@ __global__ void __launch_bounds__(512) shared_kernel(const int32_t* p_rpi, const
   if (l > 0.f) {
     float* wacc = a.ws + ((int64_t)item * BM + R) * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = wkey * 32 + 8 * rg + 4 * half;
-      __builtin_nontemporal_store(f32x4{o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]},
-                                  reinterpret_cast<f32x4*>(wacc + d0));
-    }
+    for (int sp = 0; sp < SPG; ++sp)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = (wkey + sp * NKG) * 32 + 8 * rg + 4 * half;
+        __builtin_nontemporal_store(f32x4{o[sp][rg * 4 + 0], o[sp][rg * 4 + 1], o[sp][rg * 4 + 2], o[sp][rg * 4 + 3]},
+                                    reinterpret_cast<f32x4*>(wacc + d0));
+      }
   }
   if (wkey == 0 && half == 0) {  // (m, l) of the row; l == 0 means "no keys here"
     float* wml = a.ws + (int64_t)n_items * BM * D + ((int64_t)item * BM + R) * 2;
@@ -2069,9 +2083,14 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const Append
         const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
         AppendJob none;
         none.n = 0;
-        hipLaunchKernelGGL((shared_kernel<D>), dim3((unsigned)items), dim3(512), 0, st, a.req_pool_idx, a.kv_len,
-                           a.shared_len, a.q, (int32_t)items, a.nsplit, a.n_rb, a.g, a.batch, a.h_q, a,
-                           ap ? *ap : none);
+        if (a.sh_small)
+          hipLaunchKernelGGL((shared_kernel<D, 2, 2>), dim3((unsigned)items), dim3(256), 0, st, a.req_pool_idx,
+                             a.kv_len, a.shared_len, a.q, (int32_t)items, a.nsplit, a.n_rb, a.g, a.batch, a.h_q, a,
+                             ap ? *ap : none);
+        else
+          hipLaunchKernelGGL((shared_kernel<D, 4, kShTiles>), dim3((unsigned)items), dim3(512), 0, st,
+                             a.req_pool_idx, a.kv_len, a.shared_len, a.q, (int32_t)items, a.nsplit, a.n_rb, a.g,
+                             a.batch, a.h_q, a, ap ? *ap : none);
         return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
       }
     }
@@ -2147,6 +2166,7 @@ struct DecodeLayout {
   bool split_decode;
   int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_tile_kernel + merge_kernel
   int32_t own_min;   // fewest keys per own chunk
+  int32_t sh_small;  // shared part: 4-wave workgroups, 2 tiles per round (two per CU)
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
@@ -2158,6 +2178,17 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   l.n_rb = (int32_t)((batch * g + l.bm - 1) / l.bm);
   l.nsplit = choose_nsplit((int64_t)l.n_rb * h_kv, max_seq_len);
   l.split_decode = g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+  // Many prefix tiles per workgroup (many row blocks, long prefixes): the shared part runs
+  // in 4-wave workgroups with 2 tiles per round, two per CU, over twice the workgroups, so
+  // that two chains of rounds overlap on each CU.
+  {
+    const int64_t blocks = (int64_t)l.n_rb * h_kv;
+    const int64_t tiles = std::max<int64_t>(1, (max_seq_len + BN - 1) / BN);
+    if (l.split_decode && dt == RAX_BF16 && d == 128 && tiles > 8 * (int64_t)l.nsplit) {
+      l.sh_small = 1;
+      l.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(512 + blocks - 1) / blocks, tiles, 32}));
+    }
+  }
   if (!l.split_decode) {
     l.sh_acc = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * d : 0;
     l.sh_ml = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * 2 : 0;
@@ -2334,6 +2365,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
       a.n_chunk = l.n_chunk;
       a.own_fused = l.own_mode;
       a.own_min = l.own_min;
+      a.sh_small = l.sh_small;
     }
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
