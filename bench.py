@@ -171,7 +171,7 @@ def _counter_means(csv_path, counter):
 
 
 # kernels that make up one launch of each attention entry point (substrings of their names)
-ENTRY_KERNELS = {"decode": ("shared_kernel<128>", "own_merge_kernelIDF16bLi128E"),
+ENTRY_KERNELS = {"decode": ("shared_kernel<128, 4, 4>", "own_merge_kernelIDF16bLi128E"),
                  "extend": ("attn_kernelIDF16bLi128ELb0E",)}
 
 
