@@ -1377,6 +1377,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   float my_l = lane < n_max ? mlv.y : 0.f;
   int n_own = 0, first = 0, per = 0;
   if (a.shared_only) n_own = own_chunks(a, (int)t, block_shared_len(a, rb, lane), first, per);
+  if (a.own_fused == 2 && n_own == 1) return;  // own_tile_kernel merged this row and wrote O
   if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
 #pragma unroll
@@ -1424,14 +1425,17 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 // into nsplit ranges of whole tiles; partials in attn_kernel's layout. attn_kernel
 // stages one tile at a time through registers, so each tile costs a full memory round
 // trip, and with one workgroup per CU nothing hides it. Here a workgroup issues the K
-// and V rows of up to kShTiles tiles at once straight into LDS (16-byte global-to-LDS
-// loads that hold no registers), then computes the first two tiles while the last two
-// may still be arriving. Eight waves: two 32-row tiles x four key groups; the 32-key
-// halves of a round's tiles go round-robin to the key groups, whose softmax states
-// combine in LDS at the end. (Running the requests' own keys in the same workgroups,
-// while the tiles arrive, measured slower: with eight waves per CU each own-key stream
-// is a chain of round trips that the separate own-part kernel's 16 waves per CU hide.)
-// LDS layout and fragment reads: see "tiles loaded straight into LDS" above.
+// and V rows of a round of ST tiles at once straight into LDS (16-byte global-to-LDS
+// loads that hold no registers), then computes the first half of the round while the
+// second half may still be arriving. 2 x NKG waves: two 32-row tiles x NKG key groups;
+// the 32-key halves of a round's tiles go round-robin to the key groups, whose softmax
+// states combine in LDS at the end. Two forms: NKG = 4, ST = kShTiles (8 waves, 128 KB of
+// LDS, one workgroup per CU), and, when a split holds many tiles, NKG = 2, ST = 2 (4
+// waves, 64 KB, two workgroups per CU whose rounds overlap). (Running the requests' own
+// keys in the same workgroups, while the tiles arrive, measured slower: with eight waves
+// per CU each own-key stream is a chain of round trips that the separate own-part
+// kernel's 16 waves per CU hide.) LDS layout and fragment reads: see "tiles loaded
+// straight into LDS" above.
 constexpr int kShTiles = 4;
 
 // The leading scalar arguments repeat fields of `a`: the compiler preloads the first 14
@@ -1981,6 +1985,56 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) o
     }
   }
   if (!row_ok) return;
+  if (n_act == 1) {
+    // the request's only own chunk: merge here with the shared part's split partials of
+    // this row (written by the previous kernel) by log-sum-exp and write this wave's
+    // dims of O; merge_kernel skips such rows. A split that saw no key (l == 0) may hold
+    // stale data, hence the selects.
+    const int Grow = t * G + jrow;
+    const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
+    const int nsplit = a.nsplit;
+    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+    const int64_t item0 = ((int64_t)h * a.n_rb + rbr) * nsplit;
+    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
+    const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D;
+    float M = l > 0.f ? m : kNegInf;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
+      if (ml.y > 0.f) M = fmaxf(M, ml.x);
+    }
+    const float Mu = M == kNegInf ? 0.f : M;
+    const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
+    float lsum = w_own * l;
+    f32x16 fin;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fin[r] = w_own != 0.f ? w_own * o[r] : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
+      const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - Mu) : 0.f;
+      lsum += w * ml.y;
+      const float* pa = sh_acc + (int64_t)sp * a.bm * D;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 8 * rg + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin[rg * 4 + e] += w != 0.f ? w * x[e] : 0.f;
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t obase = ((int64_t)t * a.h_q + h * G + jrow) * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+      if (a.o_bf16)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
+            bf16x4{(__bf16)(fin[rg * 4 + 0] * inv), (__bf16)(fin[rg * 4 + 1] * inv), (__bf16)(fin[rg * 4 + 2] * inv),
+                   (__bf16)(fin[rg * 4 + 3] * inv)};
+      else
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) =
+            make_float4(fin[rg * 4 + 0] * inv, fin[rg * 4 + 1] * inv, fin[rg * 4 + 2] * inv, fin[rg * 4 + 3] * inv);
+    }
+    return;
+  }
   // partial of (request t, KV head h, chunk c), query head jrow, in own_kernel's layout
   const int64_t item = (int64_t)rh * a.n_chunk + c;
   if (l > 0.f) {
