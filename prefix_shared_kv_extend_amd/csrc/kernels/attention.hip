@@ -1837,18 +1837,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) o
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
   const int32_t* rtt_row = a.rtt + (int64_t)row_t * a.rtt_stride;  // row_t valid: n_act > 0
 
-  // slot ids of the round's positions, then every K and V row of its tiles into LDS
+  // Slot ids: thread i < OT * BN holds position start + tb * BN + i of a round. Each round's
+  // ids are fetched during the previous round (the first before the loop), so a round
+  // starts with its tile loads instead of a slot-id round trip.
+  static_assert(OT * BN <= 64 * NW, "one slot id per thread and round");
+  auto slot_at = [&](int tb) {
+    const int pos = start + tb * BN + tid;
+    return rtt_row[pos < stop ? pos : start];
+  };
+  int sv_cur = tid < OT * BN ? slot_at(0) : 0;
+  // this round's slot ids into LDS, the next round's fetched, then every K and V row of the
+  // round's tiles into LDS
   auto issue = [&](int tb, int nt) {
-    for (int i = tid; i < nt * BN; i += 64 * NW) {
-      const int pos = start + tb * BN + i;
+    if (tid < nt * BN) {
+      const int pos = start + tb * BN + tid;
       const bool in = pos < stop;
-      int sv = rtt_row[in ? pos : start];
+      int sv = sv_cur;
       if (in && (sv < 0 || sv >= a.num_slots)) {
         flag_error(RAX_DEVERR_SLOT);
         sv = -1;
       }
-      slot[i] = in ? sv : -1;
+      slot[tid] = in ? sv : -1;
     }
+    // issued before the tile loads: the waits below (in issue order) cover it
+    if (tb + OT < n_tiles && tid < OT * BN) sv_cur = slot_at(tb + OT);
     __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
 #pragma unroll
