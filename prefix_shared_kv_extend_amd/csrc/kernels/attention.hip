@@ -90,6 +90,8 @@ struct AttnArgs {
                               // 2: own_tile_kernel + merge_kernel
   int32_t own_min;            // fewest own keys per chunk (own_chunks)
   int32_t sh_small;           // 1: shared part with 4-wave workgroups, 2 tiles per round
+  int32_t run_cap;            // split decode: most extra shared-part tiles per row block taken
+                              // for deeper runs (block_runs); 0: none
 };
 
 template <typename T, int D, int NW, int RT, int KS>
@@ -984,6 +986,76 @@ __device__ __forceinline__ int block_shared_len(const AttnArgs& a, int64_t rb, i
   return block_shared_len(a, block_meta_load(a, rb, lane), lane);
 }
 
+// Deeper runs inside a row block. A request whose shared_len hint to its predecessor
+// exceeds the block's shared length L0 joins the predecessor's run: the runs are the
+// subtrees of the radix tree below the block's common prefix, contiguous when a batch is
+// in tree order (a system prompt branching into few-shot blocks puts a whole block of
+// questions in one run). A run of two or more requests shares keys [L0, L1) of its first
+// request's slot row, L1 by block_shared_len's rule over the run alone (so the newest key
+// of each request stays its own). Runs are taken in request order while their extra
+// 64-key tiles add up to at most a.run_cap: the shared-part kernel computes a taken run's
+// tiles once for the run's rows, and the own parts of its requests start at L1. Every
+// decode kernel derives the same runs from the same block metadata. Wave-uniform except
+// where noted.
+struct BlockRuns {
+  int L0;          // shared length of the whole block
+  int l1;          // per lane: where the lane's request's own keys start (L0, or its run's L1)
+  int end;         // per lane: one past the last request of the lane's run (block-relative)
+  int excl;        // per lane: extra tiles of the taken runs before the lane's run
+  uint64_t heads;  // lanes whose request is the first of a taken run
+  int tiles;       // extra tiles of all taken runs
+};
+__device__ __forceinline__ BlockRuns block_runs(const AttnArgs& a, const BlockMeta& m, int lane) {
+  BlockRuns b;
+  b.L0 = block_shared_len(a, m, lane);
+  b.l1 = b.L0;
+  b.end = lane + 1;
+  b.excl = 0;
+  b.heads = 0;
+  b.tiles = 0;
+  if (a.run_cap <= 0) return b;
+  const bool join = m.in && lane > 0 && m.sh > b.L0;
+  if (!__ballot(join)) return b;  // no deeper run: the common case costs one ballot
+  const bool ok = m.in && m.row >= 0 && m.row < a.rtt_rows && m.len >= 0 && m.len <= a.rtt_stride;
+  const int own_v = ok ? m.len - 1 : 0;
+  const uint64_t starts = __ballot(m.in && !join);  // bit 0 set: a block holds request 0
+  const int nb = __popcll(__ballot(m.in));
+  const uint64_t upto = lane == 63 ? ~0ull : (2ull << lane) - 1;  // lanes 0 .. lane
+  const int head = 63 - __builtin_clzll((starts & upto) | 1ull);
+  const uint64_t later = starts & ~upto;
+  const int end = later ? __builtin_ctzll(later) : nb;
+  // segmented minimum over [head, lane] of the rule's terms, then the run's at its last lane
+  int w = m.in ? (lane == head ? own_v : min(own_v, m.sh)) : (1 << 30);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(w, off);
+    if (lane - off >= head) w = min(w, y);
+  }
+  const int l1 = __shfl(w, end > 0 ? end - 1 : 0);
+  const bool cand = m.in && lane == head && end - head >= 2 && l1 > b.L0;
+  const int nt = cand ? (l1 - b.L0 + BN - 1) / BN : 0;
+  int incl = nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const bool take = cand && incl <= a.run_cap;
+  b.heads = __ballot(take);
+  b.excl = incl - nt;
+  b.tiles = b.heads ? __builtin_amdgcn_readlane(incl, 63 - __builtin_clzll(b.heads)) : 0;
+  const bool run_taken = __shfl(take ? 1 : 0, head) != 0;
+  if (m.in && run_taken) b.l1 = l1;
+  b.end = end;
+  return b;
+}
+
+// Where the own keys of request rl of the block (block-relative, wave-uniform) start.
+__device__ __forceinline__ int row_shared_len(const AttnArgs& a, const BlockMeta& m, int lane, int rl) {
+  if (a.run_cap <= 0) return block_shared_len(a, m, lane);
+  return __builtin_amdgcn_readlane(block_runs(a, m, lane).l1, rl);
+}
+
 // Own keys of request r in split decode: positions [L, seq_len), L the shared length of the
 // request's row block. They are cut into n_act <= n_chunk chunks of about equal size, each
 // at least a.own_min keys. Returns n_act (0: nothing of its own, or an invalid row) and
@@ -1143,7 +1215,8 @@ __global__ void __launch_bounds__(256) own_kernel(AttnArgs a) {
   float q[G][E];
   load_q_heads<T, D, G>(a, r, h, lane, q);  // issued first: it depends on nothing else
   int first, per;
-  const int L = block_shared_len(a, ((int64_t)r * G) / a.bm, lane);
+  const int rbk = r * G / a.bm;
+  const int L = row_shared_len(a, block_meta_load(a, rbk, lane), lane, r - rbk * a.bm / G);
   const int n_act = own_chunks(a, r, L, first, per);
   if (c >= n_act) return;  // the merge reads only chunks [0, n_act)
   const int start = first + c * per;
@@ -1228,8 +1301,8 @@ __global__ void __launch_bounds__(512) own_merge_kernel(const void* p_q, float* 
   }
   {
     // row and key count of request r from the block metadata's lanes
-    const int L = block_shared_len(a, meta, lane);
     const int rl = r - rb0 * a.bm / G;
+    const int L = row_shared_len(a, meta, lane, rl);
     const int row = __builtin_amdgcn_readlane(meta.row, rl);
     const int end = __builtin_amdgcn_readlane(meta.len, rl);
     int first, per;
@@ -1376,7 +1449,10 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
   const float my_m = mlv.x;
   float my_l = lane < n_max ? mlv.y : 0.f;
   int n_own = 0, first = 0, per = 0;
-  if (a.shared_only) n_own = own_chunks(a, (int)t, block_shared_len(a, rb, lane), first, per);
+  if (a.shared_only) {
+    const int rl = (int)(t - rb * a.bm / a.g);  // request t's lane in its block's metadata
+    n_own = own_chunks(a, (int)t, row_shared_len(a, block_meta_load(a, rb, lane), lane, rl), first, per);
+  }
   if (a.own_fused == 2 && n_own == 1) return;  // own_tile_kernel merged this row and wrote O
   if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
@@ -1421,8 +1497,11 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 }
 
 // Shared-prefix part of split decode, bf16 with D = 128: the keys every request of a
-// 64-row block shares (positions [0, L) of the block's first request's slot row), cut
-// into nsplit ranges of whole tiles; partials in attn_kernel's layout. attn_kernel
+// 64-row block shares (positions [0, L) of the block's first request's slot row), then
+// the keys [L, L1) that each taken run of the block shares beyond them (block_runs: from
+// the run's first request's row, scores masked to the run's rows), all cut into nsplit
+// ranges of whole tiles; partials in attn_kernel's layout (a row that saw no key of a
+// split gets l = 0 there, which the merges skip). attn_kernel
 // stages one tile at a time through registers, so each tile costs a full memory round
 // trip, and with one workgroup per CU nothing hides it. Here a workgroup issues the K
 // and V rows of a round of ST tiles at once straight into LDS (16-byte global-to-LDS
@@ -1530,21 +1609,67 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
   }
   const bool all_rows_ok = __all(row_ok);
 
-  const int L = block_shared_len(a, bmeta, lane);  // 0 if the first request's row is invalid
+  const BlockRuns br = block_runs(a, bmeta, lane);
+  const int L = br.L0;  // 0 if the first request's row is invalid
   const int row0 = __builtin_amdgcn_readfirstlane(bmeta.row);
   const int n_sh = (L + BN - 1) / BN;
-  const int t_begin = (int)(((int64_t)n_sh * split) / a.nsplit);
-  const int t_end = (int)(((int64_t)n_sh * (split + 1)) / a.nsplit);
+  // the block's tiles: its shared keys [0, L), then each taken run's keys [L, L1)
+  // (block_runs), cut into nsplit ranges of whole tiles
+  const int n_vt = n_sh + br.tiles;
+  const int t_begin = (int)(((int64_t)n_vt * split) / a.nsplit);
+  const int t_end = (int)(((int64_t)n_vt * (split + 1)) / a.nsplit);
+  const int rq = t_row - qa;  // request of this lane's row, block-relative
   const int64_t row_bytes = (int64_t)a.h_kv * RB;
   const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
 
+  // Tile v of the block: positions [k0, k1) of slot row `row`, seen by the rows of the
+  // block's requests [ra, rb) (wave-uniform)
+  struct TileRef {
+    int k0, k1, row, ra, rb;
+  };
+  auto tile_ref = [&](int v) {
+    TileRef r;
+    if (v < n_sh) {
+      r.k0 = v * BN;
+      r.k1 = L;
+      r.row = row0;
+      r.ra = 0;
+      r.rb = 64;
+      return r;
+    }
+    const int u = v - n_sh;  // run tiles: the last taken run starting at or before u
+    const uint64_t at = __ballot(((br.heads >> lane) & 1ull) && br.excl <= u);
+    const int hd = 63 - __builtin_clzll(at | 1ull);
+    r.k0 = L + (u - __builtin_amdgcn_readlane(br.excl, hd)) * BN;
+    r.k1 = __builtin_amdgcn_readlane(br.l1, hd);
+    r.row = __builtin_amdgcn_readlane(bmeta.row, hd);
+    r.ra = hd;
+    r.rb = __builtin_amdgcn_readlane(br.end, hd);
+    return r;
+  };
+  // the round's tiles as named values, picked by selects (an array indexed by a
+  // variable tile number would live in scratch memory)
+  static_assert(ST == 2 || ST == 4, "tiles per round");
+  TileRef tr0, tr1, tr2, tr3;
+  auto tile_of = [&](int t) {
+    auto pick = [t](int x0, int x1, int x2, int x3) { return t == 0 ? x0 : t == 1 ? x1 : t == 2 ? x2 : x3; };
+    TileRef r;
+    r.k0 = pick(tr0.k0, tr1.k0, tr2.k0, tr3.k0);
+    r.k1 = pick(tr0.k1, tr1.k1, tr2.k1, tr3.k1);
+    r.row = pick(tr0.row, tr1.row, tr2.row, tr3.row);
+    r.ra = pick(tr0.ra, tr1.ra, tr2.ra, tr3.ra);
+    r.rb = pick(tr0.rb, tr1.rb, tr2.rb, tr3.rb);
+    return r;
+  };
+
   // slot ids, then every K and V row of the round's tiles into LDS
-  auto issue = [&](int tb, int nt) {
+  auto issue = [&](int nt, auto tile) {
     for (int i = tid; i < nt * BN; i += 64 * NW) {
-      const int pos = tb * BN + i;
-      const bool in = pos < L;
-      int sv = a.rtt[in ? (int64_t)row0 * a.rtt_stride + pos : 0];
+      const TileRef r = tile(i / BN);
+      const int pos = r.k0 + i % BN;
+      const bool in = pos < r.k1;
+      int sv = a.rtt[in ? (int64_t)r.row * a.rtt_stride + pos : 0];
       if (in && (sv < 0 || sv >= a.num_slots)) {
         flag_error(RAX_DEVERR_SLOT);
         sv = -1;
@@ -1568,15 +1693,41 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
+  // The tile loop in two forms: blocks with taken runs, and blocks without (every tile
+  // from the block's row for all rows, whose code stays that of the plain loop).
+  auto tile_loop = [&](auto with_runs) {
+  constexpr bool kRuns = decltype(with_runs)::value;
   for (int tb = t_begin; tb < t_end; tb += ST) {
     const int nt = min(ST, t_end - tb);
-    issue(tb, nt);
+    if constexpr (kRuns) {
+      tr0 = tile_ref(tb);
+      tr1 = tile_ref(min(tb + 1, t_end - 1));
+      if constexpr (ST == 4) {
+        tr2 = tile_ref(min(tb + 2, t_end - 1));
+        tr3 = tile_ref(min(tb + 3, t_end - 1));
+      } else {
+        tr2 = tr3 = tr1;
+      }
+    }
+    auto tile = [&](int t) {
+      if constexpr (kRuns) {
+        return tile_of(t);
+      } else {
+        TileRef r;
+        r.k0 = (tb + t) * BN;
+        r.k1 = L;
+        r.row = row0;
+        r.ra = 0;
+        r.rb = 64;
+        return r;
+      }
+    };
+    issue(nt, tile);
     // each wave issued LPT = 2 * NI / NW loads per tile, in tile order, and they retire in
     // order; the round is computed in two parts of ST / 2 tiles, the second part's loads
     // may still fly during the first
     constexpr int PT = ST / 2, LPT = 2 * NI / NW;
     static_assert(ST % 2 == 0 && PT * LPT <= 15, "vmcnt immediates below (bits [3:0])");
-    const int last_cnt = min(BN, L - (tb + nt - 1) * BN);
     for (int part = 0; part < 2; ++part) {
       const int t0 = part * PT, t1 = min(nt, t0 + PT);  // tiles of this part
       if (t0 >= nt) break;
@@ -1586,19 +1737,28 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
       else __builtin_amdgcn_s_waitcnt(0);
       // a plain barrier: __syncthreads' release fence would wait for every load in flight
       asm volatile("s_barrier" ::: "memory");
-      // rows past L read slot 0: zero them (their scores are masked; zeros keep P.V finite)
-      if (last_cnt < BN && nt - 1 < t1) {
-        for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
-          const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
-          *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(kv + ST * TB + off) = u32x4{0u, 0u, 0u, 0u};
+      // rows past a tile's last key read slot 0: zero them (their scores are masked; zeros
+      // keep P.V finite)
+      bool zeroed = false;
+      for (int t = t0; t < t1; ++t) {
+        const TileRef tz = tile(t);
+        const int cnt = tz.k1 - tz.k0;
+        if (cnt < BN) {
+          for (int i = tid; i < (BN - cnt) * CH; i += 64 * NW) {
+            const int off = t * TB + (cnt + i / CH) * RB + (i % CH) * 16;
+            *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(kv + ST * TB + off) = u32x4{0u, 0u, 0u, 0u};
+          }
+          zeroed = true;
         }
-        __syncthreads();
       }
+      if (zeroed) __syncthreads();
       // 32-key halves 2 t0 .. 2 t1 - 1 of the round, round-robin over the key groups
       for (int j = 2 * t0 + wkey; j < 2 * t1; j += NKG) {
       const int t = j >> 1, sub = j & 1;
-      const int cnt = min(BN, L - (tb + t) * BN);
+      const TileRef tt = tile(t);
+      const int cnt = min(BN, tt.k1 - tt.k0);
+      const bool rows_in = rq >= tt.ra && rq < tt.rb;  // run tiles: the run's rows only
       const char* kt = kv + t * TB;
       const char* vt = kv + (ST + t) * TB;
       // S^T over this wave's 32 keys: row kr of the tile, dims ks*16 + half*8
@@ -1609,14 +1769,14 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
       }
       // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
-      const bool unmasked = cnt == BN && all_rows_ok;
+      const bool unmasked = cnt == BN && all_rows_ok && tt.ra == 0 && tt.rb == 64;
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = sc[r];
         if (!unmasked) {
           const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          v = row_ok && key < cnt ? v : kNegInf;
+          v = row_ok && rows_in && key < cnt ? v : kNegInf;
         }
         sc[r] = v;
         mx = fmaxf(mx, v);
@@ -1657,6 +1817,9 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
     }
     __syncthreads();  // the next round overwrites the tiles
   }
+  };
+  if (br.tiles > 0) tile_loop(std::true_type{});
+  else tile_loop(std::false_type{});
 
   // the carried append (see above): this workgroup's first token from registers, then the
   // rest
@@ -1822,8 +1985,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) o
       qf[ks] = row_ok ? v : bf16x8{};
     }
   }
-  const int L = block_shared_len(a, meta, lane);
   const int rl = t - rb0 * a.bm / G;
+  const int L = row_shared_len(a, meta, lane, rl);
   const int row_t = __builtin_amdgcn_readlane(meta.row, rl);
   const int end = __builtin_amdgcn_readlane(meta.len, rl);
   int first, per;
@@ -2237,6 +2400,7 @@ struct DecodeLayout {
   int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_tile_kernel + merge_kernel
   int32_t own_min;   // fewest keys per own chunk
   int32_t sh_small;  // shared part: 4-wave workgroups, 2 tiles per round (two per CU)
+  int32_t run_cap;   // most extra shared-part tiles per row block for deeper runs
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
@@ -2259,6 +2423,11 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
       l.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(512 + blocks - 1) / blocks, tiles, 32}));
     }
   }
+  // Deeper runs (block_runs) where the shared part runs in shared_kernel: up to four
+  // times the longest sequence's tiles per row block, so that a block whose requests
+  // form many deep runs cannot make its shared part more than ~5x longer than the rest.
+  if (l.split_decode && dt == RAX_BF16 && d == 128)
+    l.run_cap = (int32_t)std::min<int64_t>(4 * (((int64_t)max_seq_len + BN - 1) / BN), 1 << 24);
   if (!l.split_decode) {
     l.sh_acc = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * d : 0;
     l.sh_ml = l.nsplit > 1 ? (int64_t)h_kv * l.n_rb * l.nsplit * l.bm * 2 : 0;
@@ -2436,6 +2605,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
       a.own_fused = l.own_mode;
       a.own_min = l.own_min;
       a.sh_small = l.sh_small;
+      a.run_cap = l.run_cap;
     }
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append

@@ -531,3 +531,80 @@ def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
         worst = max(worst, err)
         assert err <= TOL["bf16"], f"request {i} (own {own[i]}): max abs err {err:.3g}"
     say(f"  worst max-abs {worst:.3g} over {len(check)} requests")
+
+
+# (h_q, h_kv, groups): each group is (requests, extra shared keys past the block prefix).
+# Row blocks hold 64 / (h_q / h_kv) requests, so groups fall inside, across and exactly on
+# block boundaries.
+_RUN_CASES = [
+    # MHA, 150 requests (3 blocks): runs of 1..30 requests, extra prefixes short of a tile,
+    # exactly one, ragged, and several rounds of tiles; a group with no extra keys
+    (4, 4, [(1, 0), (2, 1), (3, 63), (16, 64), (17, 65), (5, 0), (30, 700), (2, 129), (40, 200),
+            (1, 500), (33, 1300)]),
+    # query-head groups (own keys on MFMA tiles): 8 and 16 requests per block
+    (64, 8, [(2, 100), (3, 64), (1, 0), (5, 900), (8, 1000), (4, 30), (2, 0), (7, 300)]),
+    (16, 4, [(3, 200), (13, 520), (4, 1), (1, 0), (6, 64)]),
+    # 64 requests in 32 pairs, each pair sharing 1000 keys past the block's: the extra
+    # tiles exceed the per-block cap, so only the first pairs are computed as runs
+    (4, 4, [(2, 1000)] * 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(_RUN_CASES)))
+def test_decode_deeper_runs_direct(case):
+    """Decode attention on hand-built two-level rows: a block prefix shared by every
+    request (hinted), then groups of consecutive requests sharing more keys (hinted to
+    their predecessor), then own keys. Groups of two or more requests become runs whose
+    extra keys the shared-part kernel computes once for the group's rows, up to a per-block
+    cap; their own parts start past the group's keys. Outputs against fp64 attention over
+    each request's keys (oracle.attention.attend), every request."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    h_q, h_kv, groups = _RUN_CASES[case]
+    say(f"decode, deeper runs, case {case}: {h_q}/{h_kv} heads, {sum(n for n, _ in groups)} requests in "
+        f"{len(groups)} groups")
+    d, S, P = 128, 1 << 16, 300
+    own_cycle = [0, 1, 5, 63, 64, 65, 130, 7, 260, 33]
+    gen = torch.Generator().manual_seed(101 + case)
+    perm = torch.randperm(S, generator=gen).numpy().astype(np.int32)
+    used = P
+    rows_keys, hints = [], []
+    for gi, (n, extra) in enumerate(groups):
+        ext = perm[used: used + extra]
+        used += extra
+        for j in range(n):
+            own = own_cycle[(gi * 3 + j) % len(own_cycle)]
+            mine = perm[used: used + own + 1]           # the newest key is always own
+            used += own + 1
+            rows_keys.append(np.concatenate([perm[:P], ext, mine]))
+            hints.append(P + extra if j > 0 else P)
+    assert used <= S
+    B = len(rows_keys)
+    lens = np.array([len(k) for k in rows_keys], dtype=np.int32)
+    W = int(lens.max()) + 3
+    rtt = np.full((B + 2, W), -1, dtype=np.int32)
+    rows = np.arange(B, dtype=np.int32)[::-1].copy() + 1   # rows in reverse, row 0 unused
+    for i, k in enumerate(rows_keys):
+        rtt[rows[i], : len(k)] = k
+    hints = np.array(hints, dtype=np.int32)
+    k_pool = torch.randn((S, h_kv, d), generator=gen).to(torch.bfloat16)
+    v_pool = torch.randn((S, h_kv, d), generator=gen).to(torch.bfloat16)
+    q = torch.randn((B, h_q, d), generator=gen).to(torch.bfloat16)
+    dev = lambda x: torch.as_tensor(x).cuda()
+    ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, int(lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    ob = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
+    _lib.decode_attention(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(lens), int(lens.max()), ob,
+                          workspace=ws, shared_len=dev(hints))
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    got = ob.float().cpu().numpy()
+    kf, vf, qf = k_pool.float().numpy(), v_pool.float().numpy(), q.float().numpy()
+    worst = 0.0
+    for i in range(B):
+        sl = rtt[rows[i], : lens[i]]
+        ref = attend(qf[i], kf[sl], vf[sl])
+        err = float(np.abs(got[i] - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], f"request {i}: max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {B} requests")
