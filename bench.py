@@ -345,23 +345,22 @@ def projection_measure(dev):
     return out
 
 
-def decode_gqa_measure(n_steps=8):
-    """Decode attention on the decode-heavy workload: self-consistency, 256 branches of
-    U{0..1024} tokens off one 4096-token prefix, GQA 64/8 heads x 128, bf16. The two extend
-    steps run untimed; then each of the first n_steps decode calls (rax_decode_step, as
-    the runtime runs it) is replayed REPLAYS times through rax_decode_attention between
-    one HIP event pair. Algorithmic bytes per call: distinct K/V rows (the prefix once,
-    every branch's own rows), Q and O, 4 B per req_to_token entry."""
+def decode_side_measure(index, workload, n_steps=8, first_decode=0):
+    """Decode attention on one of the decode-heavy workloads (configuration `index` of
+    workloads.configs). The steps before the chosen decode step run untimed; then each of
+    the next n_steps decode calls (rax_decode_step, as the runtime runs it) is replayed
+    REPLAYS times through rax_decode_attention between one HIP event pair. Algorithmic
+    bytes per call: the distinct K/V rows the batch reads (each slot id in the batch's
+    req_to_token rows once), Q and O, 4 B per req_to_token entry."""
     import torch
     from prefix_shared_kv_extend_amd import _lib as L
     from prefix_shared_kv_extend_amd.driver import JobRunner
     from workloads import configs
-    job = configs.make(3)
+    job = configs.make(index)
     runner = JobRunner(job, out_dtype=torch.bfloat16, record_log=False)
     rt = runner.rt
-    first = next(i for i, st in enumerate(job.steps) if st.decode)
+    first = [i for i, st in enumerate(job.steps) if st.decode][first_decode]
     runner.run(steps=range(first))
-    prefix = len(job.requests[0].prompt)
     elt = 2
     us, nbytes = [], []
 
@@ -382,17 +381,37 @@ def decode_gqa_measure(n_steps=8):
         torch.cuda.synchronize()
         us.append(a.elapsed_time(b) * 1e3 / REPLAYS)
         lens = db.seq_len.astype(np.int64)
-        distinct = prefix + int((lens - prefix).sum())
+        rows = db.dev["req_pool_idx"].long()
+        width = int(lens.max())
+        keys = rt.rtt[rows, :width]
+        inside = torch.arange(width, device=keys.device)[None, :] < torch.as_tensor(lens, device=keys.device)[:, None]
+        distinct = int(torch.unique(keys[inside]).numel())
         nbytes.append(distinct * 2 * job.h_kv * job.d * elt + 2 * len(lens) * job.h_q * job.d * elt
                       + int(lens.sum()) * 4)
 
     runner.run(steps=range(first, first + n_steps), on_decode=on_decode)
     assert L.device_errors() == 0
     gbs = sum(nbytes) / (sum(us) * 1e-6) / 1e9
-    return {"workload": "self-consistency: 256 branches of U{0..1024} tokens off a 4096-token prefix, "
-                        "GQA 64/8 x 128, bf16; first %d decode steps" % n_steps,
+    return {"workload": workload + "; %d decode steps" % n_steps,
             "us_per_call": sum(us) / len(us), "mb_per_call": sum(nbytes) / len(nbytes) / 1e6,
             "gbs_unique": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+def decode_gqa_measure(n_steps=8):
+    """Self-consistency decode: 256 branches of U{0..1024} tokens off one 4096-token
+    prefix, GQA 64/8 heads x 128, bf16; its first n_steps decode calls."""
+    return decode_side_measure(3, "self-consistency: 256 branches of U{0..1024} tokens off a 4096-token prefix, "
+                                  "GQA 64/8 x 128, bf16; from the first decode step", n_steps)
+
+
+def decode_two_level_measure(n_steps=8):
+    """Two-level decode: a 1024-token system prefix, 8 exemplar blocks of 512 tokens, 16
+    questions of 64 tokens under each (128 requests), MHA 32 x 128, bf16; its first
+    n_steps decode calls. A 64-request row block spans four exemplar blocks: their keys
+    are computed once per block as deeper runs."""
+    return decode_side_measure(2, "two-level: 1024-token system prefix, 8 x 512-token exemplar blocks, "
+                                  "16 x 64-token questions each (128 requests), MHA 32 x 128, bf16; "
+                                  "from the first decode step", n_steps)
 
 
 def cpu_baseline(job, seconds):
@@ -536,6 +555,7 @@ def main():
         out["host_tier"] = host_tier_measure(dev)
         out["qkv_projection"] = projection_measure(dev)
         out["decode_gqa"] = decode_gqa_measure()
+        out["decode_two_level"] = decode_two_level_measure()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)

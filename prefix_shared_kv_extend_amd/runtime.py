@@ -71,6 +71,7 @@ class _DecodeState:
     inv: dict                     # device int32 views: req_pool_idx, shared_len, seq_len
     lens: np.ndarray              # host lengths (slots in each row), updated by every step
     prep: tuple                   # rax_decode_step argument block (Tree.decode_step_prepare)
+    max_len: int = 0              # lens.max(), kept in step with lens
 
 
 class RadixRuntime:
@@ -173,21 +174,26 @@ class RadixRuntime:
             if len(freed):
                 self._log("evict", self.step, tuple(freed.tolist()))
             self._log("alloc", self.step, tuple(new.tolist()))
-        src = np.empty(int(ip[-1]), dtype=np.int32)
+        # slot of every prompt position: the tree's for the matched prefix (already in
+        # pslots), a new one after it; plain lists in the per-request loop (numpy scalar
+        # indexing costs more than the row copies)
+        src = pslots
         off = 0
-        req_rows = np.empty(len(rids), dtype=np.int32)
+        req_rows = [0] * len(rids)
+        ipl, ml, ql, nl = ip.tolist(), m.tolist(), q_len.tolist(), nodes.tolist()
         for i, rid in enumerate(rids):
             row = self.free_rows.pop()
-            a, b, mi, qi = int(ip[i]), int(ip[i + 1]), int(m[i]), int(q_len[i])
-            src[a: a + mi] = pslots[a: a + mi]
-            src[a + mi: b] = new[off: off + qi]
-            off += qi
+            a, b, mi, qi = ipl[i], ipl[i + 1], ml[i], ql[i]
+            if qi:
+                src[a + mi: b] = new[off: off + qi]
+                off += qi
             self.rows[row, : b - a] = src[a: b]
             self.row_of[rid] = row
             self.len_of[rid] = b - a
             self.n_prompt[rid] = b - a
-            self.node_of[rid] = int(nodes[i])
+            self.node_of[rid] = nl[i]
             req_rows[i] = row
+        req_rows = np.array(req_rows, dtype=np.int32)
         qo = np.zeros(len(rids) + 1, dtype=np.int32)
         qo[1:] = np.cumsum(q_len)
         eb = ExtendBatch(rids, m.astype(np.int32), q_len, qo, int(qo[-1]), toks, ip)
@@ -263,9 +269,9 @@ class RadixRuntime:
             lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
             prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
                                                  self.v_pool, self.h_q, shared_len=inv["shared_len"])
-            ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep)
+            ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0)
         seq_len = ds.lens + 1
-        max_seq = int(seq_len.max()) if len(seq_len) else 0
+        max_seq = ds.max_len + 1 if len(seq_len) else 0
         if max_seq > self.max_ctx:
             raise ValueError("sequence longer than the req_to_token rows")
         db = DecodeBatch(list(rids), seq_len, max_seq, ds.inv, ds.key)
@@ -287,6 +293,7 @@ class RadixRuntime:
             if len(freed):
                 self._log("evict", self.step, tuple(freed.tolist()))
             self._log("alloc", self.step, tuple(new.tolist()))
+        ds.max_len += 1                      # every request gained one token
         self.rows[ds.req_rows, ds.lens - 1] = new
 
     # ------------------------------------------------------------------- finish
