@@ -167,6 +167,21 @@ rax_status rax_match_prefix_batch(rax_tree* t, const int32_t* tokens, const int6
 rax_status rax_insert_batch(rax_tree* t, const int32_t* tokens, const int32_t* slots, const int64_t* indptr,
                             int32_t batch, int32_t* out_slots, int64_t* out_existing, rax_node* out_node,
                             int32_t* out_done);
+/* rax_insert_batch without walking and checking each request's cached prefix again
+ * ([hustzhy] §2.3 (3): the request's KV is inserted once computed; here from where its
+ * prefix matched). start[r] must be a device node whose root path spells the request's
+ * first tokens (the node rax_match_prefix(_batch) returned for them, locked since,
+ * qualifies: locking keeps it on the device, and splits leave its path and depth as they
+ * are), and the request's slots for positions [0, trusted[r]) must be the tree's. The
+ * walk starts at the deepest of start[r] and its ancestors that ends at or before
+ * trusted[r]; from there on everything is as in rax_insert_batch (same results, same
+ * returns). A start node that is unknown, a host node, deeper than the request or whose
+ * label differs from the request's tokens gives RAX_ESTATE; a bad slot past the walk's
+ * start gives RAX_EINVAL; in both cases the requests before the failing one stay
+ * inserted and *out_done (nullable) counts them. */
+rax_status rax_insert_batch_from(rax_tree* t, const rax_node* start, const int64_t* trusted, const int32_t* tokens,
+                                 const int32_t* slots, const int64_t* indptr, int32_t batch, int32_t* out_slots,
+                                 int64_t* out_existing, rax_node* out_node, int32_t* out_done);
 /* rax_lock_ref on nodes[0..n) in order. All-or-nothing: RAX_ESTATE changes nothing. */
 rax_status rax_lock_ref_batch(rax_tree* t, const rax_node* nodes, int32_t n, int32_t delta);
 /* out[0] = 0 and out[i] = rax_lca_depth(nodes[i-1], nodes[i]) for 0 < i < n: the

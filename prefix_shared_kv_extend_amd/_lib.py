@@ -63,6 +63,8 @@ _SIGS = {
     "rax_lca_depth": (_i32, [_vp, _i64, _i64, _c_i64p]),
     "rax_match_prefix_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _i32, _i32, _c_i32p, _c_i64p, _c_i64p]),
     "rax_insert_batch": (_i32, [_vp, _c_i32p, _c_i32p, _c_i64p, _i32, _c_i32p, _c_i64p, _c_i64p, _c_i32p]),
+    "rax_insert_batch_from": (_i32, [_vp, _c_i64p, _c_i64p, _c_i32p, _c_i32p, _c_i64p, _i32, _c_i32p, _c_i64p,
+                                     _c_i64p, _c_i32p]),
     "rax_lock_ref_batch": (_i32, [_vp, _c_i64p, _i32, _i32]),
     "rax_lca_depths": (_i32, [_vp, _c_i64p, _i32, _c_i32p]),
     "rax_prefix_len_batch": (_i32, [_vp, _c_i32p, _c_i64p, _i32, _c_i64p]),
@@ -369,6 +371,27 @@ class Tree:
         _check(self._L.rax_insert_batch(self._h, _p32(t), _p32(sl), ip.ctypes.data_as(_c_i64p), b, _p32(out),
                                         ex.ctypes.data_as(_c_i64p), nodes.ctypes.data_as(_c_i64p),
                                         ctypes.byref(done)), "rax_insert_batch")
+        return out[: len(t)], ex, nodes
+
+    def insert_batch_from(self, start_nodes, trusted, tokens_flat, slots_flat, indptr):
+        """insert_batch with each walk starting at start_nodes[r] (rax_insert_batch_from):
+        a node matched for the request's tokens and locked since; slots before trusted[r]
+        are the tree's. Same returns."""
+        t, sl = _i32arr(tokens_flat), _i32arr(slots_flat)
+        ip = np.ascontiguousarray(indptr, dtype=np.int64)
+        st = np.ascontiguousarray(start_nodes, dtype=np.int64)
+        tr = np.ascontiguousarray(trusted, dtype=np.int64)
+        b = len(ip) - 1
+        _need(len(st) == b and len(tr) == b, "start_nodes, trusted: one per request")
+        out = np.empty(max(len(t), 1), dtype=np.int32)
+        ex = np.empty(b, dtype=np.int64)
+        nodes = np.empty(b, dtype=np.int64)
+        done = ctypes.c_int32()
+        _check(self._L.rax_insert_batch_from(self._h, st.ctypes.data_as(_c_i64p), tr.ctypes.data_as(_c_i64p),
+                                             _p32(t), _p32(sl),
+                                             ip.ctypes.data_as(_c_i64p), b, _p32(out), ex.ctypes.data_as(_c_i64p),
+                                             nodes.ctypes.data_as(_c_i64p), ctypes.byref(done)),
+               "rax_insert_batch_from")
         return out[: len(t)], ex, nodes
 
     def lock_ref_batch(self, nodes, delta: int) -> None:

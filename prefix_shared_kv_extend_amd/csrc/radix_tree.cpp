@@ -138,8 +138,12 @@ Node* RadixTree::split(Node* child, int64_t k) {
 }
 
 Node* RadixTree::walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out) {
-  Node* node = root_;
-  int64_t i = 0;
+  return walk_from(root_, 0, tokens, n, matched, out);
+}
+
+Node* RadixTree::walk_from(Node* node, int64_t i0, const int32_t* tokens, int64_t n, int64_t* matched,
+                           int32_t* out) {
+  int64_t i = i0;
   while (i < n) {
     auto it = node->children.find(tokens[i]);
     if (it == node->children.end() || it->second->host) break;  // the device part only
@@ -202,14 +206,35 @@ int64_t RadixTree::match(const int32_t* tokens, int64_t n, int32_t* out_slots, i
 
 bool RadixTree::insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
                        int64_t* out_existing, int64_t* out_node) {
-  for (int64_t i = 0; i < n; ++i) {
+  return insert_at(root_, 0, tokens, slots, n, out_slots, out_existing, out_node);
+}
+
+int RadixTree::insert_from(int64_t start, int64_t trusted, const int32_t* tokens, const int32_t* slots, int64_t n,
+                           int32_t* out_slots, int64_t* out_existing, int64_t* out_node) {
+  auto it = nodes_.find(start);
+  if (it == nodes_.end() || trusted < 0) return 1;
+  Node* s = it->second;
+  if (s->host || s->depth_end > n) return 1;
+  while (s != root_ && s->depth_end > trusted) s = s->parent;
+  const int64_t d = s->depth_end;
+  // the start's own label must end the first d tokens (its ancestors are the caller's word)
+  const int64_t len = static_cast<int64_t>(s->tokens.size());
+  if (s != root_ && !std::equal(s->tokens.begin(), s->tokens.end(), tokens + d - len)) return 1;
+  return insert_at(s, d, tokens, slots, n, out_slots, out_existing, out_node) ? 0 : 2;
+}
+
+bool RadixTree::insert_at(Node* start, int64_t d, const int32_t* tokens, const int32_t* slots, int64_t n,
+                          int32_t* out_slots, int64_t* out_existing, int64_t* out_node) {
+  // positions before d hold the tree's own slots (insert_from's contract): checked from d
+  for (int64_t i = d; i < n; ++i) {
     if (slots[i] < 0 || slots[i] >= alloc_.num_slots() || alloc_.is_free(slots[i])) return false;
   }
   ++clock_;
-  int64_t m = 0;
+  int64_t m = d;
   std::vector<int32_t> tree_slots(static_cast<size_t>(n));
-  Node* node = walk(tokens, n, &m, tree_slots.data());
-  for (int64_t i = 0; i < m; ++i) {
+  if (d) std::memcpy(tree_slots.data(), slots, sizeof(int32_t) * d);
+  Node* node = walk_from(start, d, tokens, n, &m, tree_slots.data());
+  for (int64_t i = d; i < m; ++i) {
     if (slots[i] != tree_slots[i]) alloc_.release_one(slots[i]);
   }
   const int64_t m_dev = m;

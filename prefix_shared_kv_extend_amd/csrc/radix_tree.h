@@ -93,6 +93,14 @@ class RadixTree {
   // Returns false (nothing changed) if a caller slot is out of range or free.
   bool insert(const int32_t* tokens, const int32_t* slots, int64_t n, int32_t* out_slots,
               int64_t* out_existing, int64_t* out_node);
+  // The same insert, walking from a node on the sequence's path instead of the root:
+  // `start` must be a device node whose root path spells the first tokens of the
+  // sequence (a node matched for these tokens and still locked qualifies), and the
+  // caller's slots for positions [0, trusted) must be the tree's. The walk starts at the
+  // deepest of start and its ancestors that ends at or before `trusted`. Returns 1 for a
+  // bad start (nothing changed), 2 for a bad slot (nothing changed), 0 when done.
+  int insert_from(int64_t start, int64_t trusted, const int32_t* tokens, const int32_t* slots, int64_t n,
+                  int32_t* out_slots, int64_t* out_existing, int64_t* out_node);
   // 0 ok, 1 unknown node, 2 would go below zero, 3 host node.
   int lock_ref(int64_t node, int32_t delta);
   int64_t evict(int64_t num_tokens, int32_t* out_freed, int64_t cap);
@@ -112,6 +120,11 @@ class RadixTree {
   // Walks the longest cached prefix, splitting at its end. Returns the end node and
   // the matched length; appends the slots if out != nullptr.
   Node* walk(const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out);
+  // walk from `node`, tokens [i0, n) left to match (out indexed from position 0)
+  Node* walk_from(Node* node, int64_t i0, const int32_t* tokens, int64_t n, int64_t* matched, int32_t* out);
+  // insert with the walk starting at `start`, which ends at position d
+  bool insert_at(Node* start, int64_t d, const int32_t* tokens, const int32_t* slots, int64_t n,
+                 int32_t* out_slots, int64_t* out_existing, int64_t* out_node);
   void tick_path(Node* n);
   void lru_update(Node* n);  // re-evaluate device-candidate membership
   void lru_remove(Node* n);

@@ -50,7 +50,7 @@ const char* rax_status_str(rax_status s) {
   }
 }
 
-int32_t rax_abi_version(void) { return 2; }
+int32_t rax_abi_version(void) { return 3; }
 
 rax_status rax_tree_create(int64_t num_slots, rax_tree** out) {
   if (!out || num_slots < 1 || num_slots >= (int64_t(1) << 31)) return RAX_EINVAL;
@@ -199,6 +199,29 @@ rax_status rax_insert_batch(rax_tree* t, const int32_t* tokens, const int32_t* s
     if (!t->t.insert(tokens + o, slots + o, n, out_slots ? out_slots + o : nullptr, &out_existing[r],
                      &out_node[r]))
       return RAX_EINVAL;
+    if (out_done) *out_done = r + 1;
+  }
+  return RAX_OK;
+  RAX_GUARD_END
+}
+
+rax_status rax_insert_batch_from(rax_tree* t, const rax_node* start, const int64_t* trusted, const int32_t* tokens,
+                                 const int32_t* slots, const int64_t* indptr, int32_t batch, int32_t* out_slots,
+                                 int64_t* out_existing, rax_node* out_node, int32_t* out_done) {
+  if (out_done) *out_done = 0;
+  if (!t || batch < 0 || (batch > 0 && (!indptr || !start || !trusted || !out_existing || !out_node)))
+    return RAX_EINVAL;
+  if (batch > 0 && indptr[0] != 0) return RAX_EINVAL;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr[r + 1] < indptr[r]) return RAX_EINVAL;
+  if (batch > 0 && indptr[batch] > 0 && (!tokens || !slots)) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t o = indptr[r], n = indptr[r + 1] - o;
+    const int rc = t->t.insert_from(start[r], trusted[r], tokens + o, slots + o, n,
+                                    out_slots ? out_slots + o : nullptr, &out_existing[r], &out_node[r]);
+    if (rc == 1) return RAX_ESTATE;
+    if (rc == 2) return RAX_EINVAL;
     if (out_done) *out_done = r + 1;
   }
   return RAX_OK;

@@ -98,6 +98,7 @@ class RadixRuntime:
         self.len_of: dict[int, int] = {}     # current sequence length (slots in the row)
         self.n_prompt: dict[int, int] = {}
         self.node_of: dict[int, int] = {}    # locked tree node
+        self.trusted_of: dict[int, int] = {}  # row positions before it hold the tree's slots
         self.log = log
         self.step = 0                        # label of the current step in the event log (set by the caller)
         self.timers = None                   # {"extend": [...], "decode": [...]} of (start, end) events, if set
@@ -192,6 +193,7 @@ class RadixRuntime:
             self.len_of[rid] = b - a
             self.n_prompt[rid] = b - a
             self.node_of[rid] = nl[i]
+            self.trusted_of[rid] = mi
             req_rows[i] = row
         req_rows = np.array(req_rows, dtype=np.int32)
         qo = np.zeros(len(rids) + 1, dtype=np.int32)
@@ -226,7 +228,10 @@ class RadixRuntime:
         rows = [self.row_of[r] for r in rids]
         slots = np.concatenate([self.rows[row, : self.n_prompt[r]] for r, row in zip(rids, rows)]) \
             if rids else np.zeros(0, np.int32)
-        tslots, existing, nodes = self.tree.insert_batch(eb.tokens, slots, ip)
+        # each walk starts where the request's prefix matched (its locked node): the
+        # matched slots are the tree's already
+        tslots, existing, nodes = self.tree.insert_batch_from([self.node_of[r] for r in rids],
+                                                              [self.trusted_of[r] for r in rids], eb.tokens, slots, ip)
         if self.log is not None:
             for i, rid in enumerate(rids):
                 self._log("insert", rid, int(existing[i]), int(nodes[i]))
@@ -244,6 +249,7 @@ class RadixRuntime:
         self.tree.lock_ref_batch(old, -1)
         for i, rid in enumerate(rids):
             self.node_of[rid] = int(nodes[i])
+            self.trusted_of[rid] = self.n_prompt[rid]   # duplicates switched to the tree's above
         self._sync_decode_lengths()
         self._dec_cache = None
 
@@ -314,7 +320,11 @@ class RadixRuntime:
         ip = np.zeros(len(rids) + 1, dtype=np.int64)
         ip[1:] = np.cumsum([len(t) for t in toks])
         slots = np.concatenate([self.rows[self.row_of[r], : self.len_of[r]] for r in rids])
-        tslots, existing, nodes = self.tree.insert_batch(np.concatenate(toks), slots, ip)
+        # from each request's locked node (its prompt's; the row holds the tree's slots up
+        # to its trusted length)
+        tslots, existing, nodes = self.tree.insert_batch_from([self.node_of[r] for r in rids],
+                                                              [self.trusted_of[r] for r in rids],
+                                                              np.concatenate(toks), slots, ip)
         if self.log is not None:
             for i, rid in enumerate(rids):
                 self._log("insert", rid, int(existing[i]), int(nodes[i]))
@@ -322,7 +332,7 @@ class RadixRuntime:
         out = []
         for i, rid in enumerate(rids):
             self.free_rows.append(self.row_of.pop(rid))
-            del self.len_of[rid], self.n_prompt[rid], self.node_of[rid]
+            del self.len_of[rid], self.n_prompt[rid], self.node_of[rid], self.trusted_of[rid]
             out.append(tslots[ip[i]: ip[i + 1]])
         self._dec_cache = None
         return out

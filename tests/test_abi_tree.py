@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
     assert set(L.EXPORTS) <= names            # the binding declares nothing that the header lacks
-    assert lib.rax_abi_version() == 2
+    assert lib.rax_abi_version() == 3
 
 
 def test_error_codes(L):
@@ -156,10 +156,18 @@ def test_random_ops_match_oracle(L, seed):
             (ms["cached"], ms["locked"], ms["nodes"], ms["free"])
 
 
-def host_lifecycle(L, job):
-    """The trace lifecycle on the C++ tree alone (no kernels); same log format as the oracle."""
+def host_lifecycle(L, job, from_node=False):
+    """The trace lifecycle on the C++ tree alone (no kernels); same log format as the oracle.
+    from_node: inserts walk from each request's locked node (rax_insert_batch_from), with
+    the positions known to hold the tree's slots (the match length, then the prompt)."""
     tree = L.Tree(job.num_slots)
-    log, rows, held = [], {}, {}
+    log, rows, held, trusted = [], {}, {}, {}
+
+    def insert(rid, tokens, slots):
+        if not from_node:
+            return tree.insert(tokens, slots)
+        ts, ex, nodes = tree.insert_batch_from([held[rid]], [trusted[rid]], tokens, slots, [0, len(tokens)])
+        return int(ex[0]), int(nodes[0]), ts
     for si, st in enumerate(job.steps):
         pend = []
         for rid in st.extend:
@@ -171,6 +179,7 @@ def host_lifecycle(L, job):
             log.append(("match", rid, m, node))
             tree.lock_ref(node, +1)
             held[rid] = node
+            trusted[rid] = m
             pend.append((rid, m, ps.tolist()))
         if st.extend:
             new, freed = tree.alloc_slots_evict(sum(job.requests[rid].n - m for rid, m, _ in pend))
@@ -184,12 +193,13 @@ def host_lifecycle(L, job):
                 off += k
         for rid in st.extend:
             r = job.requests[rid]
-            ex, node, ts = tree.insert(r.prompt, rows[rid][: r.n])
+            ex, node, ts = insert(rid, r.prompt, np.array(rows[rid][: r.n], dtype=np.int32))
             log.append(("insert", rid, ex, node))
             rows[rid][: r.n] = ts.tolist()
             tree.lock_ref(node, +1)
             tree.lock_ref(held[rid], -1)
             held[rid] = node
+            trusted[rid] = r.n
         if st.decode:
             new, freed = tree.alloc_slots_evict(len(st.decode))
             if len(freed):
@@ -200,18 +210,20 @@ def host_lifecycle(L, job):
         for rid in st.finish:
             r = job.requests[rid]
             k = len(rows[rid]) - r.n
-            ex, node, ts = tree.insert(np.concatenate([r.prompt, r.output[:k]]), rows[rid])
+            ex, node, ts = insert(rid, np.concatenate([r.prompt, r.output[:k]]).astype(np.int32),
+                                  np.array(rows[rid], dtype=np.int32))
             log.append(("insert", rid, ex, node))
             rows[rid] = ts.tolist()
             tree.lock_ref(held.pop(rid), -1)
     return log, rows, tree
 
 
+@pytest.mark.parametrize("from_node", [False, True])
 @pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
-def test_trace_host_lifecycle_matches_oracle(L, index):
+def test_trace_host_lifecycle_matches_oracle(L, index, from_node):
     job = configs.make(index)
     ref = run_trace(job)
-    log, rows, tree = host_lifecycle(L, job)
+    log, rows, tree = host_lifecycle(L, job, from_node)
     assert len(log) == len(ref["log"])
     for a, b in zip(log, ref["log"]):
         assert a == b
@@ -241,3 +253,41 @@ def test_decode_step_workspace_check_changes_nothing(L):
     need = L.lib().rax_attention_workspace_bytes(1, 2, 8, 2, 128, 10)
     assert st == L.EINVAL and a.ws_needed == need > 16
     assert seq.tolist() == [5, 9] and t.free_count() == free0 and a.num_freed == 0
+
+
+def test_insert_from_node_errors(L):
+    """rax_insert_batch_from refuses a start node that is unknown, a host node, deeper than
+    the request or whose label differs from the request's tokens (RAX_ESTATE), and a bad
+    slot past the walk's start (RAX_EINVAL); the tree is unchanged by a refused request."""
+    tree = L.Tree(64)
+    a = np.arange(10, 20, dtype=np.int32)
+    sa, _ = tree.alloc_slots_evict(10)
+    ex, node, _ = tree.insert(a, sa)
+    tree.lock_ref(node, +1)
+    before = tree.dump()
+    b = np.concatenate([a, np.arange(50, 55, dtype=np.int32)])
+    sb = np.concatenate([sa, tree.alloc_slots_evict(5)[0]])
+    ip = [0, len(b)]
+    for start, trusted in ((10 ** 9, 10), (node, -1)):
+        with pytest.raises(RuntimeError, match="ESTATE|-3"):
+            tree.insert_batch_from([start], [trusted], b, sb, ip)
+    with pytest.raises(RuntimeError, match="ESTATE|-3"):   # deeper than the request
+        tree.insert_batch_from([node], [5], b[:5], sb[:5], [0, 5])
+    c = b.copy()
+    c[9] = 99                                               # the start's label differs
+    with pytest.raises(RuntimeError, match="ESTATE|-3"):
+        tree.insert_batch_from([node], [10], c, sb, ip)
+    bad = sb.copy()
+    bad[12] = 1000                                          # out of range past the start
+    with pytest.raises(RuntimeError, match="EINVAL|-1"):
+        tree.insert_batch_from([node], [10], b, bad, ip)
+    assert tree.dump() == before
+    ts, ex, nodes = tree.insert_batch_from([node], [10], b, sb, ip)
+    assert int(ex[0]) == 10 and np.array_equal(ts, sb)
+    # a start deeper than the trusted length walks from its ancestor instead
+    tree2 = L.Tree(64)
+    s2, _ = tree2.alloc_slots_evict(10)
+    _, n2, _ = tree2.insert(a, s2)
+    own = np.concatenate([s2[:9], tree2.alloc_slots_evict(1)[0]])   # position 9 not the tree's
+    ts2, ex2, _ = tree2.insert_batch_from([n2], [9], a, own, [0, 10])
+    assert int(ex2[0]) == 10 and np.array_equal(ts2, s2)
