@@ -72,6 +72,7 @@ class _DecodeState:
     lens: np.ndarray              # host lengths (slots in each row), updated by every step
     prep: tuple                   # rax_decode_step argument block (Tree.decode_step_prepare)
     max_len: int = 0              # lens.max(), kept in step with lens
+    pos: dict = None              # request id -> its index in the batch
 
 
 class RadixRuntime:
@@ -144,8 +145,11 @@ class RadixRuntime:
 
     def seq_len(self, rid: int) -> int:
         """Current number of slots in the request's row."""
-        if self._dec_cache is not None and rid in self._dec_cache.key:
-            return int(self._dec_cache.lens[self._dec_cache.key.index(rid)])
+        ds = self._dec_cache
+        if ds is not None:
+            i = ds.pos.get(rid)
+            if i is not None:
+                return int(ds.lens[i])
         return self.len_of[rid]
 
     def slot_row(self, rid: int) -> np.ndarray:
@@ -275,7 +279,8 @@ class RadixRuntime:
             lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
             prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
                                                  self.v_pool, self.h_q, shared_len=inv["shared_len"])
-            ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0)
+            ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0,
+                                                {r: i for i, r in enumerate(key)})
         seq_len = ds.lens + 1
         max_seq = ds.max_len + 1 if len(seq_len) else 0
         if max_seq > self.max_ctx:
