@@ -393,6 +393,9 @@ typedef struct {
   void* workspace;
   size_t ws_bytes;
   void* stream;
+  const int32_t* shared_len_host; /* NULL, or a host copy of shared_len [batch]: then the
+                                   * shared-prefix part's key splits are sized for the
+                                   * deeper runs the hints form (results unchanged) */
 } rax_decode_step_args;
 rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* args);
 

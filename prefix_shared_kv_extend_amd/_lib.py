@@ -44,7 +44,8 @@ class DecodeStepArgs(ctypes.Structure):
                 ("rtt_stride", ctypes.c_int64), ("rtt_rows", ctypes.c_int64), ("q", _vp), ("k_new", _vp),
                 ("v_new", _vp), ("k_pool", _vp), ("v_pool", _vp), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("dt", ctypes.c_int32), ("o_dt", ctypes.c_int32),
-                ("o", _vp), ("workspace", _vp), ("ws_bytes", ctypes.c_size_t), ("stream", _vp)]
+                ("o", _vp), ("workspace", _vp), ("ws_bytes", ctypes.c_size_t), ("stream", _vp),
+                ("shared_len_host", _c_i32p)]
 
 
 _SIGS = {
@@ -218,9 +219,10 @@ class Tree:
         return out, self._freed[: nf.value].copy()
 
     def decode_step_prepare(self, seq_len, req_to_token, req_pool_idx, seq_len_dev, k_pool, v_pool, h_q,
-                            shared_len=None, sm_scale=None, o_dtype=None):
+                            shared_len=None, sm_scale=None, o_dtype=None, shared_len_host=None):
         """Argument block of rax_decode_step for one decode batch: everything except the
-        per-step tensors, checked once. seq_len: host int32 [batch] (kept and updated in place)."""
+        per-step tensors, checked once. seq_len: host int32 [batch] (kept and updated in place);
+        shared_len_host: optional host copy of shared_len (sizes the shared part's splits)."""
         import torch
         n = len(seq_len)
         _need(isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32 and seq_len.flags.c_contiguous,
@@ -237,6 +239,9 @@ class Tree:
         a = DecodeStepArgs()
         keep = {"seq_len": seq_len, "out": np.empty(max(n, 1), dtype=np.int32),
                 "freed": np.empty(self.num_slots, dtype=np.int32)}
+        if shared_len_host is not None:
+            _need(shared_len is not None and len(shared_len_host) == n, "shared_len_host: [batch], with shared_len")
+            keep["sh_host"] = _i32arr(shared_len_host)
         a.batch = n
         a.seq_len = _p32(seq_len)
         a.out_slots = _p32(keep["out"])
@@ -244,6 +249,7 @@ class Tree:
         a.cap = self.num_slots
         a.req_pool_idx, a.seq_len_dev = req_pool_idx.data_ptr(), seq_len_dev.data_ptr()
         a.shared_len = shared_len.data_ptr() if shared_len is not None else None
+        a.shared_len_host = _p32(keep["sh_host"]) if "sh_host" in keep else None
         a.req_to_token = req_to_token.data_ptr()
         a.rtt_stride, a.rtt_rows = req_to_token.shape[1], req_to_token.shape[0]
         a.k_pool, a.v_pool = k_pool.data_ptr(), v_pool.data_ptr()

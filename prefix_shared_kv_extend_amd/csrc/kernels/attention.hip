@@ -2404,7 +2404,7 @@ struct DecodeLayout {
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
-                                  rax_dtype dt) {
+                                  rax_dtype dt, int32_t tiles_hint = 0) {
   DecodeLayout l{};
   const int g = h_q / h_kv;
   const Shape s = pick_shape(true, dt, d);
@@ -2417,7 +2417,9 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   // that two chains of rounds overlap on each CU.
   {
     const int64_t blocks = (int64_t)l.n_rb * h_kv;
-    const int64_t tiles = std::max<int64_t>(1, (max_seq_len + BN - 1) / BN);
+    // the most tiles a row block's shared part holds: known from the hints (deeper runs
+    // included), else bounded by the longest sequence
+    const int64_t tiles = std::max<int64_t>(1, tiles_hint > 0 ? tiles_hint : (max_seq_len + BN - 1) / BN);
     if (l.split_decode && dt == RAX_BF16 && d == 128 && tiles > 8 * (int64_t)l.nsplit) {
       l.sh_small = 1;
       l.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(512 + blocks - 1) / blocks, tiles, 32}));
@@ -2539,6 +2541,50 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   return dispatch<false>(a, dt, d, s, (hipStream_t)stream);
 }
 
+size_t raxk::decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
+                                    int32_t tiles_hint) {
+  if (batch <= 0 || h_kv < 1 || h_q < h_kv || h_q % h_kv || (d != 64 && d != 128) || max_seq_len < 0) return 0;
+  size_t need = 0;
+  for (rax_dtype dt : {RAX_BF16, RAX_F32}) {
+    const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, tiles_hint);
+    need = max(need, (size_t)l.total * sizeof(float));
+  }
+  return need;
+}
+
+int32_t raxk::shared_tiles_hint(const int32_t* len, const int32_t* shared_len, int32_t batch, int32_t h_q,
+                                int32_t h_kv, int32_t max_seq_len) {
+  if (!len || !shared_len || batch < 1 || h_kv < 1 || h_q % h_kv || 64 % (h_q / h_kv)) return 0;
+  const int32_t per_block = 64 / (h_q / h_kv);  // requests per 64-row block
+  const int64_t cap = 4 * (((int64_t)max_seq_len + BN - 1) / BN);  // as decode_layout's run_cap
+  int64_t most = 0;
+  for (int32_t b0 = 0; b0 < batch; b0 += per_block) {
+    const int32_t b1 = std::min(batch, b0 + per_block);
+    // the block rule: lengths after the append minus one (len here), hints to the predecessor
+    int64_t L0 = 1 << 30;
+    for (int32_t i = b0; i < b1; ++i) L0 = std::min<int64_t>(L0, i > b0 ? std::min(len[i], shared_len[i]) : len[i]);
+    L0 = std::max<int64_t>(L0, 0);
+    // deeper runs, taken in order while their tiles stay within the cap
+    int64_t extra = 0;
+    for (int32_t i = b0; i < b1;) {
+      int32_t j = i + 1;
+      int64_t L1 = len[i];
+      while (j < b1 && shared_len[j] > L0) {
+        L1 = std::min<int64_t>(L1, std::min(len[j], shared_len[j]));
+        ++j;
+      }
+      if (j - i >= 2 && L1 > L0) {
+        const int64_t nt = (L1 - L0 + BN - 1) / BN;
+        if (extra + nt > cap) break;
+        extra += nt;
+      }
+      i = j;
+    }
+    most = std::max(most, (L0 + BN - 1) / BN + extra);
+  }
+  return (int32_t)std::min<int64_t>(most, 1 << 24);
+}
+
 bool raxk::decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt) {
   if (dt != RAX_BF16 || d != 128 || batch < 1 || batch > kAppendMax || h_kv < 1 || h_q % h_kv) return false;
   const int g = h_q / h_kv;
@@ -2563,7 +2609,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
                                        const int32_t* shared_len, int32_t batch, int32_t max_seq_len, int32_t h_q,
                                        int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt, void* o,
                                        rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream,
-                                       const AppendJob* ap) {
+                                       const AppendJob* ap, int32_t tiles_hint) {
   if (!common_ok(h_q, h_kv, d, dt, o_dt) || batch < 0 || max_seq_len < 0 || num_slots < 1 || rtt_stride < 1 ||
       rtt_rows < 1 || rtt_stride > INT32_MAX)
     return RAX_EINVAL;
@@ -2590,7 +2636,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.o_bf16 = o_dt == RAX_BF16;
-  const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt);
+  const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, tiles_hint);
   a.bm = l.bm;
   a.n_rb = l.n_rb;
   a.nsplit = l.nsplit;

@@ -274,11 +274,12 @@ class RadixRuntime:
             self._sync_decode_lengths()
             req_rows = np.array([self.row_of[r] for r in rids], dtype=np.int32)
             nodes = [self.node_of[r] for r in rids]
-            inv = self._upload(dict(req_pool_idx=req_rows, shared_len=self.tree.lca_depths(nodes),
-                                    seq_len=np.zeros(len(rids))))
+            hints = self.tree.lca_depths(nodes)
+            inv = self._upload(dict(req_pool_idx=req_rows, shared_len=hints, seq_len=np.zeros(len(rids))))
             lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
             prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
-                                                 self.v_pool, self.h_q, shared_len=inv["shared_len"])
+                                                 self.v_pool, self.h_q, shared_len=inv["shared_len"],
+                                                 shared_len_host=hints)
             ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0,
                                                 {r: i for i, r in enumerate(key)})
         seq_len = ds.lens + 1
