@@ -291,3 +291,42 @@ def test_insert_from_node_errors(L):
     own = np.concatenate([s2[:9], tree2.alloc_slots_evict(1)[0]])   # position 9 not the tree's
     ts2, ex2, _ = tree2.insert_batch_from([n2], [9], a, own, [0, 10])
     assert int(ex2[0]) == 10 and np.array_equal(ts2, s2)
+
+
+def _decode_step_ws_needed(L, seq, hints):
+    """ws_needed that rax_decode_step reports for a bf16 MHA 32 x 128 batch (the call stops
+    at the workspace check, so no device pointer is dereferenced)."""
+    import ctypes
+    n = len(seq)
+    t = L.Tree(1 << 16)
+    seq = np.array(seq, dtype=np.int32)
+    a = L.DecodeStepArgs()
+    out = np.zeros(n, np.int32)
+    fr = np.zeros(64, np.int32)
+    a.batch, a.seq_len, a.out_slots, a.out_freed, a.cap = n, L._p32(seq), L._p32(out), L._p32(fr), 64
+    a.h_q, a.h_kv, a.d, a.dt, a.o_dt, a.sm_scale = 32, 32, 128, L.BF16, L.BF16, 0.1
+    a.rtt_stride, a.rtt_rows = 4096, n
+    for name in ("req_pool_idx", "seq_len_dev", "shared_len", "req_to_token", "q", "k_new", "v_new", "k_pool",
+                 "v_pool", "o"):
+        setattr(a, name, 4096)
+    h = np.array(hints, dtype=np.int32) if hints is not None else None
+    a.shared_len_host = L._p32(h) if h is not None else None
+    a.workspace, a.ws_bytes = 4096, 16
+    assert L.lib().rax_decode_step(t._h, ctypes.byref(a)) == L.EINVAL
+    assert seq.tolist() == [1600] * n and a.num_freed == 0    # nothing done
+    return a.ws_needed
+
+
+def test_decode_step_host_hints_keep_the_workspace_check(L):
+    """A host copy of the hints (which sizes the shared-prefix splits for deeper runs) is
+    read before anything is done: the workspace check still comes first and changes
+    nothing, and the workspace it asks for covers the hinted layout. Two-level batch (128
+    requests: a 1024-token prefix, groups of 16 sharing 512 more) and a few-shot batch
+    (one common prefix). (Which kernel form runs is seen in the GPU kernel traces.)"""
+    seq = [1600] * 128
+    plain = _decode_step_ws_needed(L, seq, None)
+    assert plain == L.lib().rax_attention_workspace_bytes(1, 128, 32, 32, 128, 1601)
+    two_level = [0 if i == 0 else (1536 if i % 16 else 1024) for i in range(128)]
+    few_shot = [0] + [1500] * 127
+    for hints in (two_level, few_shot):
+        assert _decode_step_ws_needed(L, seq, hints) >= plain
