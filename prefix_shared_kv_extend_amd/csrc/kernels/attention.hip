@@ -2404,7 +2404,7 @@ struct DecodeLayout {
 };
 
 static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
-                                  rax_dtype dt, int32_t tiles_hint = 0) {
+                                  rax_dtype dt, DecodeHint hint = {}) {
   DecodeLayout l{};
   const int g = h_q / h_kv;
   const Shape s = pick_shape(true, dt, d);
@@ -2419,7 +2419,7 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
     const int64_t blocks = (int64_t)l.n_rb * h_kv;
     // the most tiles a row block's shared part holds: known from the hints (deeper runs
     // included), else bounded by the longest sequence
-    const int64_t tiles = std::max<int64_t>(1, tiles_hint > 0 ? tiles_hint : (max_seq_len + BN - 1) / BN);
+    const int64_t tiles = std::max<int64_t>(1, hint.tiles > 0 ? hint.tiles : (max_seq_len + BN - 1) / BN);
     if (l.split_decode && dt == RAX_BF16 && d == 128 && tiles > 8 * (int64_t)l.nsplit) {
       l.sh_small = 1;
       l.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(512 + blocks - 1) / blocks, tiles, 32}));
@@ -2456,6 +2456,16 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
     l.own_min = kOwnMin;
     const int64_t by_len = (max_seq_len + kOwnMin - 1) / kOwnMin;
     l.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>({64 - l.nsplit, by_len, (kOwnWaves + pairs - 1) / pairs}));
+    // Knowing the most own keys: enough chunks that each takes one round of keys
+    // (kOwnMin), when that stays within 1.5x the wave budget. A chunk's second round costs
+    // a whole K/V round trip: few-shot steps with 65..83 own keys measured 36.9 -> 34.8 us
+    // at 3 chunks instead of 2, while at most 64 own keys 2 chunks stay faster.
+    if (hint.own > 0) {
+      const int64_t one_round = (hint.own + kOwnMin - 1) / kOwnMin;
+      const int64_t roomy = std::max<int64_t>((kOwnWaves + pairs - 1) / pairs, (3 * kOwnWaves / 2) / pairs);
+      l.n_chunk = (int32_t)std::max<int64_t>(
+          1, std::min<int64_t>({64 - l.nsplit, by_len, std::max<int64_t>(l.n_chunk, std::min(one_round, roomy))}));
+    }
     // the chunks of one (request, KV head) fit one workgroup: merge in LDS, no own partials
     l.own_mode = l.n_chunk <= kOwnFusedMaxWaves && own_fused_lds_bytes(l.n_chunk, g, d) <= kOwnFusedMaxLds ? 1 : 0;
   }
@@ -2542,22 +2552,23 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
 }
 
 size_t raxk::decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
-                                    int32_t tiles_hint) {
+                                    DecodeHint hint) {
   if (batch <= 0 || h_kv < 1 || h_q < h_kv || h_q % h_kv || (d != 64 && d != 128) || max_seq_len < 0) return 0;
   size_t need = 0;
   for (rax_dtype dt : {RAX_BF16, RAX_F32}) {
-    const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, tiles_hint);
+    const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, hint);
     need = max(need, (size_t)l.total * sizeof(float));
   }
   return need;
 }
 
-int32_t raxk::shared_tiles_hint(const int32_t* len, const int32_t* shared_len, int32_t batch, int32_t h_q,
-                                int32_t h_kv, int32_t max_seq_len) {
-  if (!len || !shared_len || batch < 1 || h_kv < 1 || h_q % h_kv || 64 % (h_q / h_kv)) return 0;
+DecodeHint raxk::decode_hint(const int32_t* len, const int32_t* shared_len, int32_t batch, int32_t h_q,
+                             int32_t h_kv, int32_t max_seq_len) {
+  DecodeHint hint;
+  if (!len || !shared_len || batch < 1 || h_kv < 1 || h_q % h_kv || 64 % (h_q / h_kv)) return hint;
   const int32_t per_block = 64 / (h_q / h_kv);  // requests per 64-row block
   const int64_t cap = 4 * (((int64_t)max_seq_len + BN - 1) / BN);  // as decode_layout's run_cap
-  int64_t most = 0;
+  int64_t most = 0, own = 0;
   for (int32_t b0 = 0; b0 < batch; b0 += per_block) {
     const int32_t b1 = std::min(batch, b0 + per_block);
     // the block rule: lengths after the append minus one (len here), hints to the predecessor
@@ -2566,6 +2577,7 @@ int32_t raxk::shared_tiles_hint(const int32_t* len, const int32_t* shared_len, i
     L0 = std::max<int64_t>(L0, 0);
     // deeper runs, taken in order while their tiles stay within the cap
     int64_t extra = 0;
+    bool full = false;
     for (int32_t i = b0; i < b1;) {
       int32_t j = i + 1;
       int64_t L1 = len[i];
@@ -2573,16 +2585,24 @@ int32_t raxk::shared_tiles_hint(const int32_t* len, const int32_t* shared_len, i
         L1 = std::min<int64_t>(L1, std::min(len[j], shared_len[j]));
         ++j;
       }
-      if (j - i >= 2 && L1 > L0) {
+      int64_t start = L0;  // where the run's own keys start
+      if (!full && j - i >= 2 && L1 > L0) {
         const int64_t nt = (L1 - L0 + BN - 1) / BN;
-        if (extra + nt > cap) break;
-        extra += nt;
+        if (extra + nt > cap) {
+          full = true;
+        } else {
+          extra += nt;
+          start = L1;
+        }
       }
+      for (int32_t r = i; r < j; ++r) own = std::max<int64_t>(own, (int64_t)len[r] + 1 - start);
       i = j;
     }
     most = std::max(most, (L0 + BN - 1) / BN + extra);
   }
-  return (int32_t)std::min<int64_t>(most, 1 << 24);
+  hint.tiles = (int32_t)std::min<int64_t>(most, 1 << 24);
+  hint.own = (int32_t)std::min<int64_t>(std::max<int64_t>(own, 0), 1 << 30);
+  return hint;
 }
 
 bool raxk::decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt) {
@@ -2609,7 +2629,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
                                        const int32_t* shared_len, int32_t batch, int32_t max_seq_len, int32_t h_q,
                                        int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt, void* o,
                                        rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream,
-                                       const AppendJob* ap, int32_t tiles_hint) {
+                                       const AppendJob* ap, DecodeHint hint) {
   if (!common_ok(h_q, h_kv, d, dt, o_dt) || batch < 0 || max_seq_len < 0 || num_slots < 1 || rtt_stride < 1 ||
       rtt_rows < 1 || rtt_stride > INT32_MAX)
     return RAX_EINVAL;
@@ -2636,7 +2656,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.o_bf16 = o_dt == RAX_BF16;
-  const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, tiles_hint);
+  const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, hint);
   a.bm = l.bm;
   a.n_rb = l.n_rb;
   a.nsplit = l.nsplit;

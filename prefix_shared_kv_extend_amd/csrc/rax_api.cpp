@@ -377,12 +377,13 @@ rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
   if (!a->seq_len) return RAX_EINVAL;
   int32_t max_len = 0;
   for (int32_t i = 0; i < a->batch; ++i) max_len = std::max(max_len, a->seq_len[i] + 1);
-  // with host hints, the shared part's key splits are sized for the tiles its row blocks hold
-  const int32_t tiles_hint =
-      a->shared_len_host ? raxk::shared_tiles_hint(a->seq_len, a->shared_len_host, a->batch, a->h_q, a->h_kv, max_len)
-                         : 0;
-  a->ws_needed = tiles_hint > 0 ? raxk::decode_workspace_bytes(a->batch, a->h_q, a->h_kv, a->d, max_len, tiles_hint)
-                                : rax_attention_workspace_bytes(1, a->batch, a->h_q, a->h_kv, a->d, max_len);
+  // with host hints, the launches are sized for the tiles the row blocks' shared parts
+  // hold and for the longest own part
+  const raxk::DecodeHint hint = a->shared_len_host ? raxk::decode_hint(a->seq_len, a->shared_len_host, a->batch,
+                                                                      a->h_q, a->h_kv, max_len)
+                                                   : raxk::DecodeHint{};
+  a->ws_needed = a->shared_len_host ? raxk::decode_workspace_bytes(a->batch, a->h_q, a->h_kv, a->d, max_len, hint)
+                                    : rax_attention_workspace_bytes(1, a->batch, a->h_q, a->h_kv, a->d, max_len);
   if (a->ws_needed > a->ws_bytes) return RAX_EINVAL;  // nothing done yet
   // the attention's argument checks first (a zero-row call checks shapes and types only)
   if (!a->q || !a->o ||
@@ -399,7 +400,7 @@ rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
     return raxk::decode_attention_impl(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token,
                                        a->rtt_stride, a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len,
                                        a->batch, max_len, a->h_q, a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt,
-                                       a->workspace, a->ws_bytes, a->stream, nullptr, tiles_hint);
+                                       a->workspace, a->ws_bytes, a->stream, nullptr, hint);
   }
   // the append rides in the first attention kernel's launch (one launch less per step)
   raxk::AppendJob job;
@@ -419,7 +420,7 @@ rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
   return raxk::decode_attention_impl(a->q, a->k_pool, a->v_pool, t->t.alloc().num_slots(), a->req_to_token,
                                      a->rtt_stride, a->rtt_rows, a->req_pool_idx, a->seq_len_dev, a->shared_len,
                                      a->batch, max_len, a->h_q, a->h_kv, a->d, a->sm_scale, a->dt, a->o, a->o_dt,
-                                     a->workspace, a->ws_bytes, a->stream, &job, tiles_hint);
+                                     a->workspace, a->ws_bytes, a->stream, &job, hint);
 }
 
 rax_status rax_set_host_tier(rax_tree* t, int64_t host_slots, void* k_host, void* v_host) {

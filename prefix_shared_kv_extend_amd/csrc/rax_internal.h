@@ -35,24 +35,32 @@ bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, ra
 
 // rax_decode_attention, with an optional append carried by its first kernel (seq_len is
 // then read from the job, not from memory, by that kernel).
-// tiles_hint > 0: the most 64-key tiles the shared-prefix part of any row block will
-// compute (shared_tiles_hint), which sizes its key splits; 0: the longest sequence's tiles.
+// What the host knows of a decode batch from host copies of its lengths and hints
+// (decode_hint); zeros: nothing, the layout follows the longest sequence.
+struct DecodeHint {
+  int32_t tiles = 0;  // the most 64-key tiles the shared-prefix part of any row block computes
+  int32_t own = 0;    // the most own keys of any request (past its block's or run's shared keys)
+};
+
+// rax_decode_attention, with an optional append carried by its first kernel (seq_len is
+// then read from the job, not from memory, by that kernel) and an optional hint that
+// sizes the launches (results unchanged).
 rax_status decode_attention_impl(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
                                  const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
                                  const int32_t* req_pool_idx, const int32_t* seq_len, const int32_t* shared_len,
                                  int32_t batch, int32_t max_seq_len, int32_t h_q, int32_t h_kv, int32_t d,
                                  float sm_scale, rax_dtype dt, void* o, rax_dtype o_dt, void* workspace,
-                                 size_t ws_bytes, void* stream, const AppendJob* ap, int32_t tiles_hint = 0);
+                                 size_t ws_bytes, void* stream, const AppendJob* ap, DecodeHint hint = {});
 
-// Workspace bytes of a decode call laid out with tiles_hint (as above).
+// Workspace bytes of a decode call laid out with the hint.
 size_t decode_workspace_bytes(int64_t batch, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_seq_len,
-                              int32_t tiles_hint);
+                              DecodeHint hint);
 
 // From host copies of the lengths before a decode step's append (len) and the shared_len
-// hints: the most shared-prefix tiles of any row block after the append, by the rule of
-// the decode kernels (block shared length, then deeper runs up to their per-block cap).
-int32_t shared_tiles_hint(const int32_t* len, const int32_t* shared_len, int32_t batch, int32_t h_q,
-                          int32_t h_kv, int32_t max_seq_len);
+// hints, by the rule of the decode kernels (block shared length, then deeper runs up to
+// their per-block cap), for the lengths after the append.
+DecodeHint decode_hint(const int32_t* len, const int32_t* shared_len, int32_t batch, int32_t h_q, int32_t h_kv,
+                       int32_t max_seq_len);
 
 // One launch of the move kernel: n (src, dst) slot pairs, each dst written once.
 constexpr int kMoveMax = 256;
