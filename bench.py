@@ -143,11 +143,14 @@ def run_step(runner, prep, timers=None):
             _, kind, pairs, q, k, v, o = next(it)
             rt.run_decode(db, q, k, v, o)
             if timers is not None:
-                ws = rt._workspace(L.attention_workspace_bytes(True, len(db.rids), job.h_q, job.h_kv, job.d,
-                                                               db.max_seq_len))
-                timed("decode", lambda: L.decode_attention(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"],
-                                                           db.dev["seq_len"], db.max_seq_len, o, workspace=ws,
-                                                           shared_len=db.dev["shared_len"]))
+                # replays in the layout the runtime's decode step chose (host hints)
+                def dec(ws):
+                    return L.decode_attention_hinted(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"],
+                                                     db.dev["seq_len"], db.max_seq_len, o, db.seq_len,
+                                                     db.shared_len_host, workspace=ws,
+                                                     shared_len=db.dev["shared_len"])
+                ws = rt._workspace(dec(None))
+                timed("decode", lambda: dec(ws))
         if st.finish:
             rt.finish_batch([(rid, runner.full[rid][: rt.seq_len(rid)]) for rid in st.finish])
     rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next step starts empty
@@ -349,7 +352,8 @@ def decode_side_measure(index, workload, n_steps=8, first_decode=0):
     """Decode attention on one of the decode-heavy workloads (configuration `index` of
     workloads.configs). The steps before the chosen decode step run untimed; then each of
     the next n_steps decode calls (rax_decode_step, as the runtime runs it) is replayed
-    REPLAYS times through rax_decode_attention between one HIP event pair. Algorithmic
+    REPLAYS times between one HIP event pair through rax_decode_attention_hinted, in the
+    layout the decode step chose from its host hints. Algorithmic
     bytes per call: the distinct K/V rows the batch reads (each slot id in the batch's
     req_to_token rows once), Q and O, 4 B per req_to_token entry."""
     import torch
@@ -369,14 +373,16 @@ def decode_side_measure(index, workload, n_steps=8, first_decode=0):
         ws = rt._workspace(L.attention_workspace_bytes(True, len(db.rids), job.h_q, job.h_kv, job.d,
                                                        db.max_seq_len))
 
-        def call():
-            L.decode_attention(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"], db.dev["seq_len"],
-                               db.max_seq_len, o, workspace=ws, shared_len=db.dev["shared_len"])
-        call()
+        def call(w):
+            return L.decode_attention_hinted(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"],
+                                             db.dev["seq_len"], db.max_seq_len, o, db.seq_len, db.shared_len_host,
+                                             workspace=w, shared_len=db.dev["shared_len"])
+        ws = rt._workspace(max(call(None), ws.numel()))
+        call(ws)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(REPLAYS):
-            call()
+            call(ws)
         b.record()
         torch.cuda.synchronize()
         us.append(a.elapsed_time(b) * 1e3 / REPLAYS)

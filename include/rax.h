@@ -352,6 +352,21 @@ rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v
                                 int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
                                 void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream);
 
+/* rax_decode_attention with host copies of seq_len and shared_len (seq_len_host,
+ * shared_len_host: [batch] each, as the device arrays): the launches are sized from them
+ * as rax_decode_step sizes its attention (the tiles each row block's shared part holds,
+ * deeper runs included, and the longest own part); results as rax_decode_attention's up
+ * to summation order. The workspace this layout needs goes to *out_ws_needed (nullable);
+ * if ws_bytes is smaller, nothing is launched and RAX_EINVAL is returned. */
+rax_status rax_decode_attention_hinted(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                       const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                       const int32_t* req_pool_idx, const int32_t* seq_len,
+                                       const int32_t* shared_len, int32_t batch, int32_t max_seq_len, int32_t h_q,
+                                       int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt, void* o,
+                                       rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream,
+                                       const int32_t* seq_len_host, const int32_t* shared_len_host,
+                                       size_t* out_ws_needed);
+
 /* One whole decode step in one call: rax_decode_append (slots, row append, K/V
  * write-back, with any host-tier moves) followed by rax_decode_attention over the rows
  * as they are after the append, on the same stream; max_seq_len is taken from the host

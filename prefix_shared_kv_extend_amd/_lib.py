@@ -85,6 +85,9 @@ _SIGS = {
                                     _i32, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_decode_attention": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "rax_decode_attention_hinted": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                           _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp, _c_i32p,
+                                           _c_i32p, ctypes.POINTER(_sz)]),
     "rax_attention_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "rax_device_errors": (_i32, [_vp, _c_i32p]),
     "rax_qkv_project": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
@@ -539,6 +542,36 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max
         req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
         q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
         _stream(stream, q)), "rax_decode_attention")
+
+
+def decode_attention_hinted(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max_seq_len: int, o,
+                            seq_len_host, shared_len_host, workspace=None, shared_len=None, sm_scale=None,
+                            stream=None) -> int:
+    """rax_decode_attention_hinted: decode_attention with host copies of seq_len and
+    shared_len sizing the launches. Returns the workspace bytes the layout needs; when
+    `workspace` is smaller nothing runs (grow it and call again)."""
+    _need(q.dim() == 3 and q.shape[2] == k_pool.shape[2] and k_pool.shape == v_pool.shape, "shapes")
+    _need(o.shape == q.shape and o.is_contiguous() and o.is_cuda, "o like q")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "input dtypes agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (q, k_pool, v_pool)), "contiguous cuda")
+    _cuda_i32(req_to_token, req_pool_idx, seq_len, shared_len)
+    b = q.shape[0]
+    _need(req_pool_idx.numel() == b and seq_len.numel() == b, "metadata shapes")
+    sl, sh = _i32arr(seq_len_host), _i32arr(shared_len_host)
+    _need(len(sl) == b and len(sh) == b, "host copies: [batch]")
+    d = q.shape[2]
+    scale = float(sm_scale if sm_scale is not None else d ** -0.5)
+    ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    need = _sz()
+    st = lib().rax_decode_attention_hinted(
+        _dev(q), _dev(k_pool), _dev(v_pool), k_pool.shape[0], _dev(req_to_token), req_to_token.shape[1],
+        req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
+        q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
+        _stream(stream, q), _p32(sl), _p32(sh), ctypes.byref(need))
+    if st == EINVAL and need.value > ws:
+        return int(need.value)
+    _check(st, "rax_decode_attention_hinted")
+    return int(need.value)
 
 
 def device_errors(stream=None) -> int:

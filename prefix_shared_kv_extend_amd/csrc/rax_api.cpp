@@ -369,6 +369,32 @@ rax_status rax_schedule_order(const rax_tree* t, int32_t policy, const int32_t* 
   RAX_GUARD_END
 }
 
+rax_status rax_decode_attention_hinted(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                       const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                       const int32_t* req_pool_idx, const int32_t* seq_len,
+                                       const int32_t* shared_len, int32_t batch, int32_t max_seq_len, int32_t h_q,
+                                       int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt, void* o,
+                                       rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream,
+                                       const int32_t* seq_len_host, const int32_t* shared_len_host,
+                                       size_t* out_ws_needed) {
+  if (out_ws_needed) *out_ws_needed = 0;
+  if (batch < 0 || (batch > 0 && (!seq_len_host || !shared_len_host))) return RAX_EINVAL;
+  RAX_GUARD_BEGIN
+  // the hint counts from the lengths before a step's append: one less than these
+  std::vector<int32_t> before(static_cast<size_t>(batch));
+  for (int32_t i = 0; i < batch; ++i) before[i] = std::max(seq_len_host[i] - 1, 0);
+  const raxk::DecodeHint hint =
+      batch > 0 ? raxk::decode_hint(before.data(), shared_len_host, batch, h_q, h_kv, max_seq_len)
+                : raxk::DecodeHint{};
+  const size_t need = batch > 0 ? raxk::decode_workspace_bytes(batch, h_q, h_kv, d, max_seq_len, hint) : 0;
+  if (out_ws_needed) *out_ws_needed = need;
+  if (need > ws_bytes) return RAX_EINVAL;
+  return raxk::decode_attention_impl(q, k_pool, v_pool, num_slots, req_to_token, rtt_stride, rtt_rows, req_pool_idx,
+                                     seq_len, shared_len, batch, max_seq_len, h_q, h_kv, d, sm_scale, dt, o, o_dt,
+                                     workspace, ws_bytes, stream, nullptr, hint);
+  RAX_GUARD_END
+}
+
 rax_status rax_decode_step(rax_tree* t, rax_decode_step_args* a) {
   if (!t || !a || a->batch < 0) return RAX_EINVAL;
   a->num_freed = 0;

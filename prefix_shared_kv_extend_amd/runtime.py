@@ -61,6 +61,7 @@ class DecodeBatch:
     max_seq_len: int
     dev: dict = field(default_factory=dict)
     key: tuple = None
+    shared_len_host: np.ndarray = None  # host copy of dev["shared_len"]
 
 
 @dataclass
@@ -73,6 +74,7 @@ class _DecodeState:
     prep: tuple                   # rax_decode_step argument block (Tree.decode_step_prepare)
     max_len: int = 0              # lens.max(), kept in step with lens
     pos: dict = None              # request id -> its index in the batch
+    hints: np.ndarray = None      # host copy of inv["shared_len"]
 
 
 class RadixRuntime:
@@ -281,12 +283,12 @@ class RadixRuntime:
                                                  self.v_pool, self.h_q, shared_len=inv["shared_len"],
                                                  shared_len_host=hints)
             ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0,
-                                                {r: i for i, r in enumerate(key)})
+                                                {r: i for i, r in enumerate(key)}, hints)
         seq_len = ds.lens + 1
         max_seq = ds.max_len + 1 if len(seq_len) else 0
         if max_seq > self.max_ctx:
             raise ValueError("sequence longer than the req_to_token rows")
-        db = DecodeBatch(list(rids), seq_len, max_seq, ds.inv, ds.key)
+        db = DecodeBatch(list(rids), seq_len, max_seq, ds.inv, ds.key, ds.hints)
         return db
 
     def run_decode(self, db: DecodeBatch, q, k_new, v_new, o) -> None:

@@ -599,12 +599,23 @@ def test_decode_deeper_runs_direct(case):
     torch.cuda.synchronize()
     assert _lib.device_errors() == 0
     got = ob.float().cpu().numpy()
+    # the same call laid out from host copies of the lengths and hints
+    oh = torch.empty_like(ob)
+    hinted = lambda w: _lib.decode_attention_hinted(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows),
+                                                    dev(lens), int(lens.max()), oh, lens, hints, workspace=w,
+                                                    shared_len=dev(hints))
+    need = hinted(None)
+    hinted(torch.empty(max(need, 1), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    got_h = oh.float().cpu().numpy()
     kf, vf, qf = k_pool.float().numpy(), v_pool.float().numpy(), q.float().numpy()
     worst = 0.0
     for i in range(B):
         sl = rtt[rows[i], : lens[i]]
         ref = attend(qf[i], kf[sl], vf[sl])
-        err = float(np.abs(got[i] - ref).max())
-        worst = max(worst, err)
-        assert err <= TOL["bf16"], f"request {i}: max abs err {err:.3g}"
-    say(f"  worst max-abs {worst:.3g} over {B} requests")
+        for out in (got, got_h):
+            err = float(np.abs(out[i] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], f"request {i}: max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {B} requests, plain and hinted layouts")
