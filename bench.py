@@ -225,17 +225,21 @@ def scheduler_ablation():
     policy, against Theorem 3.1's optimum (each edge of the requests' radix tree once):
       tight: a pool of exactly the longest prompt, one request per batch (the theorem's case);
       batched: a pool of 16384 slots, at most 4096 new tokens per batch."""
-    from oracle.trie import NaiveTrie
+    from prefix_shared_kv_extend_amd import _lib
     from prefix_shared_kv_extend_amd import scheduler as S
     from workloads import configs
     job = configs.make(2)
     rng = np.random.default_rng(7)
     prompts = [job.requests[i].prompt for i in rng.permutation(len(job.requests))]
-    trie = NaiveTrie()
-    for pr in prompts:
-        trie.insert(pr)
     total = sum(len(pr) for pr in prompts)
-    opt = trie.num_nodes()
+    # the optimum: every distinct token prefix computed once = the tokens a tree large
+    # enough for all prompts caches after inserting each of them
+    every = _lib.Tree(total)
+    for pr in prompts:
+        m, slots, _ = every.match_prefix(pr)
+        every.insert(pr, np.concatenate([slots[:m], every.alloc_slots(len(pr) - m)]))
+    opt = every.stats()["cached_tokens"]
+    every.close()
     out = {"workload": "two_level: 136 prompts (8 x 1536, 128 x 1600), shuffled arrival",
            "prompt_tokens": total, "optimal_computed": opt, "optimal_hit_rate": 1 - opt / total}
     for regime, kw in (("tight", dict(num_slots=max(len(pr) for pr in prompts), max_batch=1)),

@@ -57,14 +57,29 @@ def order(model, prompts, waiting, policy: str, seed: int) -> list:
     if policy == "dfs":
         return sorted(idx, key=lambda j: list(prompts[waiting[j]]))  # lexicographic, stable
     if policy == "random":
-        state = seed & MASK64
-        for i in range(len(idx) - 1, 0, -1):
-            draw = splitmix64(state)
-            state = (state + GOLDEN) & MASK64
-            j = draw % (i + 1)
-            idx[i], idx[j] = idx[j], idx[i]
-        return idx
+        return fisher_yates(len(idx), splitmix_draws(seed, max(len(idx) - 1, 0)))
     raise ValueError(policy)
+
+
+def splitmix_draws(seed: int, count: int) -> list:
+    """The first `count` outputs of a SplitMix64 stream whose state starts at `seed` (S4)."""
+    state = seed & MASK64
+    out = []
+    for _ in range(count):
+        out.append(splitmix64(state))
+        state = (state + GOLDEN) & MASK64
+    return out
+
+
+def fisher_yates(n: int, draws) -> list:
+    """Fisher-Yates shuffle of [0, n): for i = n-1 down to 1 the next draw picks
+    j = draw mod (i + 1) and positions i and j swap (S4)."""
+    idx = list(range(n))
+    it = iter(draws)
+    for i in range(n - 1, 0, -1):
+        j = next(it) % (i + 1)
+        idx[i], idx[j] = idx[j], idx[i]
+    return idx
 
 
 def run_prefill(prompts, num_slots: int, policy: str = "lpm", max_batch_tokens: int = 1 << 30,

@@ -269,6 +269,10 @@ class Tree:
         _need(tuple(q.shape) == qshape and tuple(k_new.shape) == kshape and tuple(v_new.shape) == kshape
               and tuple(o.shape) == qshape and q.dtype == dtype and k_new.dtype == dtype and v_new.dtype == dtype,
               "q, o: [batch, h_q, d]; k_new, v_new: [batch, h_kv, d], the pool dtype")
+        _need(all(t.is_contiguous() and t.is_cuda and t.get_device() == dev for t in (q, k_new, v_new, o)),
+              "q, k_new, v_new, o: contiguous tensors on the pools' device")
+        _need(workspace is None or (workspace.is_contiguous() and workspace.is_cuda and workspace.get_device() == dev),
+              "workspace: contiguous, on the pools' device")
         a.q, a.k_new, a.v_new, a.o = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), o.data_ptr()
         a.o_dt = _dtype_code(o)
         a.workspace = workspace.data_ptr() if workspace is not None else None

@@ -2242,9 +2242,11 @@ struct Shape {
 // 32-row tiles x two 32-key halves of every tile (KS = 2), one tile of loads in flight:
 // the same 64 rows per block as 2 waves x 1 tile, half the MFMA chain per wave and twice
 // the waves per CU; the key halves combine their softmax states in LDS at the end.
+// Every decode shape has 64 rows per block: the decode kernels read a block's requests
+// with one lane each (block_meta_load), so a block may hold at most 64 requests.
 static Shape pick_shape(bool decode, rax_dtype dt, int d) {
-  if (dt != RAX_BF16) return {4, 1, 1, 1};
   if (decode) return {4, 1, 1, 2};
+  if (dt != RAX_BF16) return {4, 1, 1, 1};
   return d == 128 ? Shape{8, 1, 1, 1} : Shape{4, 2, 1, 1};
 }
 
@@ -2327,10 +2329,14 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const Append
         return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
       }
     }
+  }
+  if constexpr (kDecode) {
     if (s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 2) rc = launch_one<T, D, kDecode, 4, 1, 1, 2>(a, st);
   }
-  if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 1)
-    rc = launch_one<T, D, kDecode, 4, 1, 1, 1>(a, st);
+  if constexpr (!kDecode) {
+    if (rc == RAX_EINVAL && s.nw == 4 && s.rt == 1 && s.pd == 1 && s.ks == 1)
+      rc = launch_one<T, D, kDecode, 4, 1, 1, 1>(a, st);
+  }
   return rc;
 }
 
@@ -2657,6 +2663,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   a.o = o;
   a.o_bf16 = o_dt == RAX_BF16;
   const DecodeLayout l = decode_layout(batch, h_q, h_kv, d, max_seq_len, dt, hint);
+  if (l.bm / a.g > 64) return RAX_EINVAL;  // one lane per request of a block (block_meta_load)
   a.bm = l.bm;
   a.n_rb = l.n_rb;
   a.nsplit = l.nsplit;

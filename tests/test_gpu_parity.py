@@ -533,6 +533,75 @@ def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
     say(f"  worst max-abs {worst:.3g} over {len(check)} requests")
 
 
+@pytest.mark.parametrize("d,B", [(64, 150), (128, 131)])
+def test_decode_fp32_mha_many_requests_direct(d, B):
+    """fp32 MHA decode with more than 128 requests, so row blocks are full and there are
+    several of them: a shared prefix (hinted for most neighbours, with some hints cut
+    short), own ranges of 0..300 keys. Every output against fp64 attention over the
+    request's keys (oracle.attention.attend) within 1e-5."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    h, S, P = 4, 1 << 15, 97
+    say(f"decode fp32 MHA, {B} requests, d={d}: {P}-key prefix, own ranges 0..300")
+    gen = torch.Generator().manual_seed(977 + d)
+    perm = torch.randperm(S, generator=gen).numpy().astype(np.int32)
+    own = [(i * 37) % 301 for i in range(B)]
+    lens = np.array([P + n + 1 for n in own], dtype=np.int32)
+    W = int(lens.max()) + 1
+    rtt = np.full((B + 1, W), -1, dtype=np.int32)
+    rows = (np.arange(B, dtype=np.int32) * 7) % (B + 1)      # shuffled, distinct rows
+    used = P
+    for i in range(B):
+        rtt[rows[i], :P] = perm[:P]
+        rtt[rows[i], P:lens[i]] = perm[used: used + lens[i] - P]
+        used += lens[i] - P
+    assert used <= S and len(set(rows.tolist())) == B
+    hints = np.array([P if i % 9 else P // 2 for i in range(B)], dtype=np.int32)
+    k_pool = torch.randn((S, h, d), generator=gen)
+    v_pool = torch.randn((S, h, d), generator=gen)
+    q = torch.randn((B, h, d), generator=gen)
+    dev = lambda x: torch.as_tensor(x).cuda()
+    ws = torch.empty(_lib.attention_workspace_bytes(True, B, h, h, d, int(lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, h, d), dtype=torch.float32, device="cuda")
+    _lib.decode_attention(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(lens), int(lens.max()), o,
+                          workspace=ws, shared_len=dev(hints))
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    got = o.cpu().numpy()
+    kf, vf, qf = k_pool.numpy(), v_pool.numpy(), q.numpy()
+    worst = 0.0
+    for i in range(B):
+        sl = rtt[rows[i], : lens[i]]
+        err = float(np.abs(got[i] - attend(qf[i], kf[sl], vf[sl])).max())
+        worst = max(worst, err)
+        assert err <= TOL["f32"], f"request {i} (own {own[i]}): max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {B} requests")
+
+
+def test_decode_step_rejects_strided_and_host_tensors():
+    """rax_decode_step's binding checks every per-step tensor before the native call."""
+    from prefix_shared_kv_extend_amd import _lib
+    say("decode_step binding: strided q and host k_new are refused")
+    h, d, B = 4, 128, 3
+    t = _lib.Tree(64)
+    kp = torch.zeros((64, h, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    rtt = torch.zeros((4, 16), dtype=torch.int32, device="cuda")
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    lens = np.zeros(B, dtype=np.int32)
+    prep = t.decode_step_prepare(lens, rtt, rows, torch.zeros(B, dtype=torch.int32, device="cuda"), kp, vp, h)
+    q = torch.zeros((B, h, d), dtype=torch.bfloat16, device="cuda")
+    kn = torch.zeros((B, h, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    wide = torch.zeros((B, h, 2 * d), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        t.decode_step(prep, wide[:, :, :d], kn, kn, o, None)
+    with pytest.raises(ValueError):
+        t.decode_step(prep, q, kn.cpu(), kn, o, None)
+    assert t.free_count() == 64                              # nothing was allocated
+
+
 # (h_q, h_kv, groups): each group is (requests, extra shared keys past the block prefix).
 # Row blocks hold 64 / (h_q / h_kv) requests, so groups fall inside, across and exactly on
 # block boundaries.
