@@ -1,24 +1,35 @@
 """Benchmark of the RadixAttention hot path on one MI355X.
 
-Workload (the few-shot configuration): one attention layer at Llama-2-7B attention
-shape (32 heads MHA, head_dim 128), bf16 inputs, fp32 accumulation, bf16 outputs;
-64 requests share a 2000-token prefix and each adds a distinct 50-token suffix;
-pool of 2^20 token slots; then 32 decode steps for all 64 requests.
+Headline workload (the multi-turn chat configuration, the largest one): one attention
+layer at Mixtral-8x7B attention shape (32 query heads, 8 KV heads, head_dim 128), bf16
+inputs, fp32 accumulation, bf16 outputs. 512 sessions of 1..8 turns whose user and
+assistant segments are lognormal (median 200 tokens) behind one 200-token system prompt;
+each turn's prompt is the session history plus the new user segment. The pool holds 60%
+of the distinct tokens (878,695 slots), so leaf-first LRU eviction runs throughout. The
+trace is 6040 mixed steps: a ragged extend batch (1474 calls, 737,768 suffix queries)
+and a decode batch of up to 256 requests (6038 calls, 732,323 decode queries).
 
-One timed step = the whole job from an empty cache, through the C ABI:
-  request 0 cold (match, lock, allocate, fill req_to_token, KV write-back, extend
-  attention over 2050 tokens, insert); the other 63 reuse its 2000-token prefix
-  (match splits its node) and extend only their 50 suffix tokens; 32 decode
-  steps (allocate, fill, write-back, decode attention); finish (insert prompt +
-  output, unlock); then evict the whole tree, so the next step starts empty.
-Q/K/V for every call are generated before timing and stay resident in HBM.
+One timed step = the whole job from an empty cache, through the C ABI: every trace step's
+extend (match, lock, allocate with eviction, fill req_to_token, KV write-back, extend
+attention, insert), decode (allocate with eviction, append, write-back, decode
+attention) and finish (insert prompt + output, unlock); then the whole tree is evicted so
+the next step starts empty. Q/K/V of every call are generated before timing and stay
+resident in HBM (about 18 GB).
 
-value = attention tokens per second for the whole step (5200 extend queries +
-2048 decode queries, wall clock, host tree work included), from a pass with no
-timing events. A second pass over the same steps records a HIP event pair around
-every attention call on the stream the kernels run on; it gives the per-phase
-kernel times and the roofline of the dominant kernel. The JSON line also carries
-the CPU oracle's rate on a bounded sample of the same workload.
+Passes over the same job (--passes):
+  wall     K timed jobs, each between two synchronisations: value (attention tokens per
+           second of wall clock, host tree work included), median/p10/p90 of the job time,
+           host time to issue a job;
+  cold     one job with a 512 MiB scratch write (untimed) before every attention call, so
+           L2 and the 256 MB MALL hold nothing of it, and a HIP event pair around the call
+           on the stream it runs on: per-call kernel times, the per-kind rates and the
+           roofline of the dominant kernel (the headline figures);
+  natural  one job with the event pairs and no scratch writes (calls as they run).
+Beside the headline, each of the other shared-prefix configurations (few-shot, two-level
+tree, self-consistency fork) runs its whole trace and times every attention call over
+--reps cold repetitions (scratch write before each) and --reps warm ones (back to back):
+medians, p10 and p90. The JSON line also carries the CPU oracle's rate on a bounded sample
+of the headline workload.
 """
 from __future__ import annotations
 
@@ -35,189 +46,380 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 COPY_READ_BYTES = 2 * (1 << 15) * 64 * 128 * 2 + (1 << 15) * 4   # --copy-calib: K, V and slot list read
 COPY_WRITE_BYTES = 2 * (1 << 15) * 64 * 128 * 2                    # K and V written
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "prefix_shared_kv_extend_amd", "csrc", "kernels", "attention.hip")
-MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "attn tokens/s (extend, decode) + % MFMA/HBM peak on radix-cached KV"
+HEADLINE = 4                  # workloads.configs index of the headline job (multi-turn)
+SIDE = {"fewshot": 1, "two_level": 2, "self_consistency": 3}
+DESCR = {
+    1: "fewshot: 64 requests x (2000 shared + 50 own) tokens, then 32 decode steps; 32 heads MHA x 128, bf16",
+    2: "two_level: 1024-token system prefix -> 8 x 512-token exemplar blocks -> 16 x 64-token questions "
+       "(128 leaves), leaf extend then 16 decode steps; 32 heads MHA x 128, bf16",
+    3: "self_consistency: 4096-token prefix, 256 branches of U{0..1024} tokens, 64 decode steps; "
+       "GQA 64/8 x 128, bf16",
+    4: "multi_turn: 512 sessions, 1-8 turns, lognormal(200, 1.0) segments in [16, 2048], 200-token system "
+       "prompt, pool = 60% of distinct tokens (878,695 slots, LRU eviction), 6040 mixed extend + decode "
+       "steps (<= 256 running); GQA 32/8 x 128, bf16",
+}
+# kernels of one launch of each attention entry point (substrings of their names) and the
+# kernel every launch runs exactly once (its dispatch count is the number of launches)
+ENTRY_KERNELS = {
+    "decode": {"kernels": ("shared_kernel", "own_merge_kernel", "own_tile_kernel", "own_kernel", "merge_kernel"),
+               "anchor": "shared_kernel"},
+    "extend": {"kernels": ("attn_kernelIDF16bLi128ELb0E",), "anchor": "attn_kernelIDF16bLi128ELb0E"},
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=5, help="timed jobs of the wall pass")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed jobs before the wall pass")
+    ap.add_argument("--reps", type=int, default=20, help="cold and warm repetitions per call (side sections)")
+    ap.add_argument("--passes", default="wall,cold,natural", help="comma list of wall, cold, natural")
+    ap.add_argument("--flush-mib", type=int, default=512, help="scratch written before each cold call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
-                    help="skip the sections beside the headline (scheduler, host tier, projection, GQA decode)")
+                    help="skip the sections beside the headline (other configurations, scheduler, host tier, "
+                         "projection)")
+    ap.add_argument("--only", default=None, choices=sorted(SIDE),
+                    help="run only this configuration's per-call section (cold and warm reps) and print it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", default=TRAFFIC_JSON, help="counter summary with HBM bytes per launch")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
                     help="condense rocprofv3 counter runs in DIR into profiles/traffic.json and exit")
+    ap.add_argument("--summarize-trace", default=None, metavar="CSV",
+                    help="print a markdown summary of a rocprofv3 kernel trace (per kernel; GPU idle between "
+                         "kernels over the window of the hot path's kernels) and exit")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain copy kernel of known size (for counter scaling) and exit")
     return ap.parse_args()
 
 
-class Prepared:
-    """Pre-generated inputs for every attention call of one job, in call order."""
+# ------------------------------------------------------------------ helpers
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if len(xs) else None
 
-    def __init__(self, runner, dev):
+
+def stats(xs):
+    return {"median": pct(xs, 50), "p10": pct(xs, 10), "p90": pct(xs, 90), "n": len(xs)}
+
+
+class Flusher:
+    """An untimed write of a scratch buffer larger than L2 (8 x 4 MB) and the 256 MB MALL, so
+    that the next call finds nothing of its inputs in either."""
+
+    def __init__(self, dev, mib):
         import torch
-        self.calls = []
-        job = runner.job
-        seen = {}
+        self.buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+        self.n = 0
 
-        def grab(kind):
-            def cb(si, batch, pairs, o):
-                seen.setdefault(si, {})[kind] = list(pairs)
-            return cb
-
-        runner.run(on_extend=grab("extend"), on_decode=grab("decode"))
-        torch.cuda.synchronize()
-        for si in sorted(seen):
-            for kind in ("extend", "decode"):
-                if kind in seen[si]:
-                    q, k, v = runner.qkv(seen[si][kind])
-                    o = torch.empty((q.shape[0], job.h_q, job.d), dtype=torch.bfloat16, device=dev)
-                    self.calls.append((si, kind, seen[si][kind], q, k, v, o))
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
 
 
-def algorithmic(job, prep):
-    """Flops of each extend call and unique bytes of each decode call (per launch)."""
-    D, hq, hkv = job.d, job.h_q, job.h_kv
-    elt = 2
-    ext_flops, dec_bytes = [], []
-    for si, kind, pairs, q, k, v, o in prep.calls:
-        if kind == "extend":
-            ext_flops.append(sum(4.0 * D * hq * (p + 1) for _, p in pairs))
-        else:
-            # distinct slots read: the shared prefix once plus every request's own positions
-            lens = [p + 1 for _, p in pairs]
-            shared = 2000
-            distinct = shared + sum(n - shared for n in lens)
-            kv = distinct * 2 * hkv * D * elt
-            qo = len(pairs) * hq * D * elt * 2
-            idx = sum(lens) * 4
-            dec_bytes.append(kv + qo + idx)
-    return ext_flops, dec_bytes
+def extend_flops(job, pairs):
+    """QK^T and PV over keys 0..p of every suffix query (causal): 4 D h_q (p + 1) each."""
+    p = np.fromiter((q for _, q in pairs), dtype=np.float64, count=len(pairs))
+    return float(4.0 * job.d * job.h_q * (p + 1).sum())
 
 
-REPLAYS = 4
+def decode_bytes(job, n_req, n_keys, distinct):
+    """Distinct K/V rows read (each slot once), Q in and O out, 4 B per req_to_token entry."""
+    return distinct * 2 * job.h_kv * job.d * 2 + 2 * n_req * job.h_q * job.d * 2 + n_keys * 4
 
 
-def run_step(runner, prep, timers=None):
-    """One job pass. With timers: after each attention call, the same call (identical inputs;
-    it only writes its output) is replayed REPLAYS times back to back between one HIP event
-    pair on the stream the kernels run on, so the measured time is kernel time, not time
-    the GPU spent waiting for the host to issue the next launch."""
+def distinct_slots(rt, db):
+    """Number of distinct slot ids in the batch's req_to_token rows (device sort, no sync):
+    the K/V rows the decode call must read at least once."""
     import torch
-    from prefix_shared_kv_extend_amd import _lib as L
-    rt = runner.rt
-    job = runner.job
-    it = iter(prep.calls)
+    dev = rt.rtt.device
+    width = int(db.max_seq_len)
+    lens = torch.from_numpy(db.seq_len.astype(np.int32)).to(dev, non_blocking=True)
+    keys = rt.rtt[db.dev["req_pool_idx"].long(), :width]
+    inside = torch.arange(width, device=dev)[None, :] < lens[:, None]
+    k = torch.where(inside, keys, torch.full_like(keys, -1)).flatten().sort().values
+    return ((k[1:] != k[:-1]) & (k[1:] >= 0)).sum() + (k[0] >= 0).to(torch.int64)
 
-    def timed(kind, fn):
-        if timers is None:
-            return
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(REPLAYS):
-            fn()
-        e1.record()
-        timers.setdefault(kind, []).append((e0, e1))
 
+# ------------------------------------------------------------------ the headline job
+def call_plan(job):
+    """Every attention call of one job from an empty cache, in order: (step, kind, pairs of
+    (request, position)). Match lengths come from the tree alone (the runtime's sequence of
+    tree calls, driver.tree_replay), so nothing runs on the GPU."""
+    from prefix_shared_kv_extend_amd.driver import tree_replay
+    log, _, tree, _ = tree_replay(job)
+    tree.close()
+    matches = iter([e for e in log if e[0] == "match"])
+    length, calls = {}, []
+    for si, st in enumerate(job.steps):
+        if st.extend:
+            pairs = []
+            for rid in st.extend:
+                ev = next(matches)
+                assert ev[1] == rid
+                n = job.requests[rid].n
+                pairs += [(rid, p) for p in range(ev[2], n)]
+                length[rid] = n
+            calls.append((si, "extend", pairs))
+        if st.decode:
+            pairs = []
+            for rid in st.decode:
+                pairs.append((rid, length[rid]))
+                length[rid] += 1
+            calls.append((si, "decode", pairs))
+    return calls
+
+
+class Inputs:
+    """Q/K/V of every attention call of the job, generated on the device before timing."""
+
+    def __init__(self, runner, calls):
+        import torch
+        job = runner.job
+        self.calls = calls
+        self.qkv = [runner.qkv(pairs) for _, _, pairs in calls]
+        most = max(len(p) for _, _, p in calls)
+        self.o = torch.empty((most, job.h_q, job.d), dtype=torch.bfloat16, device=runner.device)
+        self.flops = [extend_flops(job, p) if kind == "extend" else 0.0 for _, kind, p in calls]
+        torch.cuda.synchronize()
+
+
+def run_job(runner, inp, pre=None, timed=False, after_decode=None):
+    """One job pass through the runtime. pre: called right before each attention call is
+    issued; timed: a HIP event pair around every attention call (rt.timers)."""
+    rt, job = runner.rt, runner.job
+    rt.timers = {} if timed else None
+    rt.pre_attention = pre
+    i = 0
     for si, st in enumerate(job.steps):
         rt.step = si
         if st.extend:
             eb = rt.begin_extend([(rid, job.requests[rid].prompt) for rid in st.extend])
-            _, kind, pairs, q, k, v, o = next(it)
-            rt.run_extend(eb, q, k, v, o)
-            timed("extend", lambda: L.extend_attention(q, k, v, rt.k_pool, rt.v_pool, rt.rtt, eb.dev["req_pool_idx"],
-                                                       eb.dev["prefix_len"], eb.dev["qo_indptr"], o,
-                                                       shared_len=eb.dev["shared_len"]))
-            rt.end_extend(eb, {rid: job.requests[rid].prompt for rid in eb.rids})
+            q, k, v = inp.qkv[i]
+            rt.run_extend(eb, q, k, v, inp.o[: q.shape[0]])
+            rt.end_extend(eb)
+            i += 1
         if st.decode:
             db = rt.begin_decode(st.decode)
-            _, kind, pairs, q, k, v, o = next(it)
-            rt.run_decode(db, q, k, v, o)
-            if timers is not None:
-                # replays in the layout the runtime's decode step chose (host hints)
-                def dec(ws):
-                    return L.decode_attention_hinted(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"],
-                                                     db.dev["seq_len"], db.max_seq_len, o, db.seq_len,
-                                                     db.shared_len_host, workspace=ws,
-                                                     shared_len=db.dev["shared_len"])
-                ws = rt._workspace(dec(None))
-                timed("decode", lambda: dec(ws))
+            q, k, v = inp.qkv[i]
+            rt.run_decode(db, q, k, v, inp.o[: q.shape[0]])
+            if after_decode is not None:
+                after_decode(i, db)
+            i += 1
         if st.finish:
             rt.finish_batch([(rid, runner.full[rid][: rt.seq_len(rid)]) for rid in st.finish])
-    rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next step starts empty
+    rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next job starts empty
+    timers, rt.timers, rt.pre_attention = rt.timers, None, None
+    return timers
 
 
-def _sha256(path):
-    import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def per_kind(job, inp, timers, dec_bytes):
+    """Per-call times (us) and work of one timed pass, by kind."""
+    out = {}
+    for kind in ("extend", "decode"):
+        idx = [i for i, c in enumerate(inp.calls) if c[1] == kind]
+        us = [a.elapsed_time(b) * 1e3 for a, b in timers.get(kind, [])]
+        assert len(us) == len(idx), (kind, len(us), len(idx))
+        work = [inp.flops[i] for i in idx] if kind == "extend" else [dec_bytes[i] for i in idx]
+        out[kind] = (us, work)
+    return out
 
 
-def _counter_means(csv_path, counter):
-    """Mean per dispatch of one counter, per kernel name, from a rocprofv3 counter CSV."""
-    import csv
-    acc = {}
-    with open(csv_path) as f:
-        for x in csv.DictReader(f):
-            if x["Counter_Name"] == counter:
-                acc.setdefault(x["Kernel_Name"], []).append(float(x["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+def summarize_kind(kind, us, work, n_tok):
+    tot_us, tot_w = sum(us), sum(work)
+    if kind == "extend":
+        rate = tot_w / (tot_us * 1e-6) / 1e12
+        per_call = [w / (u * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS for u, w in zip(us, work)]
+        return {"us_per_step": tot_us, "calls": len(us), "tok_s_kernel": n_tok / (tot_us * 1e-6),
+                "tflops": rate, "frac_mfma_peak": rate / MFMA_BF16_PEAK_TFLOPS,
+                "per_call_frac": stats(per_call)}
+    rate = tot_w / (tot_us * 1e-6) / 1e9
+    per_call = [w / (u * 1e-6) / 1e9 / HBM_PEAK_GBS for u, w in zip(us, work)]
+    return {"us_per_step": tot_us, "calls": len(us), "tok_s_kernel": n_tok / (tot_us * 1e-6),
+            "gbs_unique": rate, "frac_hbm_peak": rate / HBM_PEAK_GBS, "mb_per_call": tot_w / len(us) / 1e6,
+            "per_call_frac": stats(per_call)}
 
 
-# kernels that make up one launch of each attention entry point (substrings of their names)
-ENTRY_KERNELS = {"decode": ("shared_kernel<128, 4, 4>", "own_merge_kernelIDF16bLi128E"),
-                 "extend": ("attn_kernelIDF16bLi128ELb0E",)}
+def headline(args, dev):
+    import torch
+    from prefix_shared_kv_extend_amd.driver import JobRunner
+    from workloads import configs
+    job = configs.make(HEADLINE)
+    calls = call_plan(job)
+    runner = JobRunner(job, device="cuda:0", out_dtype=torch.bfloat16, record_log=False)
+    inp = Inputs(runner, calls)
+    n_ext = sum(len(p) for _, k, p in calls if k == "extend")
+    n_dec = sum(len(p) for _, k, p in calls if k == "decode")
+    passes = set(args.passes.split(","))
+    out = {"config": {"workload": DESCR[HEADLINE], "extend_tokens_per_step": n_ext,
+                      "decode_tokens_per_step": n_dec, "prompt_tokens_per_step": sum(r.n for r in job.requests),
+                      "extend_calls_per_step": sum(1 for c in calls if c[1] == "extend"),
+                      "decode_calls_per_step": sum(1 for c in calls if c[1] == "decode"),
+                      "trace_steps": len(job.steps), "pool_slots": job.num_slots}}
+    out["hit_rate"] = 1.0 - n_ext / out["config"]["prompt_tokens_per_step"]
+
+    if "wall" in passes:
+        for _ in range(args.warmup):
+            run_job(runner, inp)
+        torch.cuda.synchronize()
+        walls, issue = [], []
+        for _ in range(args.steps):
+            t0 = time.perf_counter()
+            run_job(runner, inp)
+            t1 = time.perf_counter()          # the host never waits inside a job
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            walls.append(t2 - t0)
+            issue.append(t1 - t0)
+        out["wall"] = {"value": (n_ext + n_dec) * len(walls) / sum(walls), "ms_per_step": sum(walls) * 1e3 / len(walls),
+                       "ms_stats": stats([w * 1e3 for w in walls]), "host_issue_ms": sum(issue) * 1e3 / len(issue)}
+
+    # distinct K/V rows of every decode call, counted on the device after the call (outside
+    # its event pair) in the first timed pass
+    counts, dec_bytes = {}, {}
+
+    def count(i, db):
+        counts[i] = distinct_slots(runner.rt, db)
+
+    def finish_counts():
+        for i, c in enumerate(calls):
+            if c[1] == "decode" and i not in dec_bytes:
+                pairs = c[2]
+                dec_bytes[i] = decode_bytes(job, len(pairs), sum(p + 1 for _, p in pairs), int(counts[i]))
+
+    for name in ("cold", "natural"):
+        if name not in passes:
+            continue
+        flush = Flusher(dev, args.flush_mib) if name == "cold" else None
+        timers = run_job(runner, inp, pre=flush, timed=True, after_decode=None if dec_bytes else count)
+        torch.cuda.synchronize()
+        finish_counts()
+        res = per_kind(job, inp, timers, dec_bytes)
+        out[name] = {k: summarize_kind(k, *res[k], n_ext if k == "extend" else n_dec) for k in res}
+        del flush
+    from prefix_shared_kv_extend_amd import _lib
+    assert _lib.device_errors() == 0
+    out["_job"] = job
+    out["_inp"] = None
+    return out
 
 
-def write_traffic(run_dir):
-    """Condense rocprofv3 FETCH_SIZE / WRITE_SIZE runs (of this script, and of --copy-calib)
-    into profiles/traffic.json: HBM bytes per launch of each attention entry point, each
-    counter scaled by what it reads for the plain copy of known size."""
-    fetch = _counter_means(os.path.join(run_dir, "pmc_FETCH_SIZE", "bench_counter_collection.csv"), "FETCH_SIZE")
-    write = _counter_means(os.path.join(run_dir, "pmc_WRITE_SIZE", "bench_counter_collection.csv"), "WRITE_SIZE")
-    cf = _counter_means(os.path.join(run_dir, "copy_FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
-    cw = _counter_means(os.path.join(run_dir, "copy_WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
-    copy_f = next(v for k, v in cf.items() if "kv_scatter_kernel" in k)
-    copy_w = next(v for k, v in cw.items() if "kv_scatter_kernel" in k)
-    f_scale = COPY_READ_BYTES / (copy_f * 1024.0)
-    w_scale = COPY_WRITE_BYTES / (copy_w * 1024.0)
-    out = {"source_sha256": _sha256(KERNEL_SOURCE), "fetch_scale": f_scale, "write_scale": w_scale,
-           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "entries": {}}
-    for entry, keys in ENTRY_KERNELS.items():
-        per = {}
-        for key in keys:
-            kf = [v for k, v in fetch.items() if key in k]
-            kw = [v for k, v in write.items() if key in k]
-            if kf and kw:
-                per[key] = {"fetch_kib": kf[0], "write_kib": kw[0],
-                            "bytes": kf[0] * 1024 * f_scale + kw[0] * 1024 * w_scale}
-        out["entries"][entry] = {"kernels": per, "bytes_per_launch": sum(p["bytes"] for p in per.values())}
-    with open(TRAFFIC_JSON, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+def roofline_of(cold, traffic_path):
+    ext, dec = cold["extend"], cold["decode"]
+    if ext["us_per_step"] >= dec["us_per_step"]:
+        roof = {"kernel": "extend attention (attn_kernel, bf16, D=128)", "bound": "mfma",
+                "achieved": ext["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ext["frac_mfma_peak"], "launches_per_step": ext["calls"],
+                "avg_launch_us": ext["us_per_step"] / ext["calls"]}
+        entry = "extend"
+    else:
+        roof = {"kernel": "decode attention (shared_kernel + own part + merge_kernel)", "bound": "hbm",
+                "achieved": dec["gbs_unique"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec["frac_hbm_peak"],
+                "launches_per_step": dec["calls"], "avg_launch_us": dec["us_per_step"] / dec["calls"],
+                "algorithmic_bytes_per_launch": dec["mb_per_call"] * 1e6}
+        entry = "decode"
+    roof["traffic"] = load_traffic(entry, traffic_path)
+    roof["timing"] = "cold: 512 MiB scratch write before every call, HIP events on the call's stream"
+    return roof
 
 
-def load_traffic(entry, path):
-    """HBM bytes per launch of `entry` from the committed counter summary, or None when there
-    is none or the kernel source changed since the counters were taken."""
-    if not path or not os.path.exists(path):
-        return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("source_sha256") != _sha256(KERNEL_SOURCE):
-        return None
-    return t.get("entries", {}).get(entry, {}).get("bytes_per_launch")
+# ------------------------------------------------------------------ side configurations
+def side_config(index, reps, flush):
+    """Run configuration `index` through the runtime and time each attention call: after
+    the call runs in the job, 2 untimed repetitions, `reps` cold ones (a scratch write before
+    each, HIP events around the call) and `reps` warm ones (back to back). Decode calls are
+    replayed through rax_decode_attention_hinted in the layout the decode step chose; extend
+    calls through rax_extend_attention with the call's own inputs."""
+    import torch
+    from prefix_shared_kv_extend_amd import _lib as L
+    from prefix_shared_kv_extend_amd.driver import JobRunner
+    from workloads import configs
+    job = configs.make(index)
+    runner = JobRunner(job, out_dtype=torch.bfloat16, record_log=False)
+    rt = runner.rt
+    rec = {"extend": [], "decode": []}
+
+    def measure(fn):
+        fn()
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * reps)]
+        for a, b in ev[:reps]:
+            flush()
+            a.record()
+            fn()
+            b.record()
+        for a, b in ev[reps:]:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        return us[:reps], us[reps:]
+
+    def on_extend(si, eb, pairs, o):
+        q, k, v = runner.qkv(pairs)
+        ws = rt._workspace(L.attention_workspace_bytes(False, eb.total_q, job.h_q, job.h_kv, job.d, eb.max_kv_len))
+        fn = lambda: L.extend_attention(q, k, v, rt.k_pool, rt.v_pool, rt.rtt, eb.dev["req_pool_idx"],
+                                        eb.dev["prefix_len"], eb.dev["qo_indptr"], o, shared_len=eb.dev["shared_len"],
+                                        workspace=ws, max_kv_len=eb.max_kv_len)
+        cold, warm = measure(fn)
+        rec["extend"].append({"queries": len(pairs), "requests": len(eb.rids), "work": extend_flops(job, pairs),
+                              "cold": cold, "warm": warm})
+
+    def on_decode(si, db, pairs, o):
+        q = torch.randn((len(db.rids), job.h_q, job.d), device=o.device).to(torch.bfloat16)
+
+        def call(w):
+            return L.decode_attention_hinted(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"], db.dev["seq_len"],
+                                             db.max_seq_len, o, db.seq_len, db.shared_len_host, workspace=w,
+                                             shared_len=db.dev["shared_len"])
+        ws = rt._workspace(call(None))
+        cold, warm = measure(lambda: call(ws))
+        n_keys = int(db.seq_len.astype(np.int64).sum())
+        rec["decode"].append({"requests": len(db.rids), "work": decode_bytes(job, len(db.rids), n_keys,
+                                                                            int(distinct_slots(rt, db))),
+                              "cold": cold, "warm": warm})
+
+    runner.run(on_extend=on_extend, on_decode=on_decode)
+    assert L.device_errors() == 0
+
+    def agg(kind, items):
+        if not items:
+            return None
+        res = {"calls": len(items)}
+        for temp in ("cold", "warm"):
+            med = [pct(it[temp], 50) for it in items]
+            p10 = [pct(it[temp], 10) for it in items]
+            p90 = [pct(it[temp], 90) for it in items]
+            w = sum(it["work"] for it in items)
+            if kind == "extend":
+                rate = lambda us: w / (sum(us) * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+                key = "frac_mfma_peak"
+            else:
+                rate = lambda us: w / (sum(us) * 1e-6) / 1e9 / HBM_PEAK_GBS
+                key = "frac_hbm_peak"
+            res[temp] = {"us_per_call_median": sum(med) / len(med), key: rate(med),
+                         key + "_p10_time": rate(p90), key + "_p90_time": rate(p10)}
+        if kind == "extend":
+            res["per_call"] = [{"queries": it["queries"], "requests": it["requests"], "gflop": it["work"] / 1e9,
+                                "cold_us": stats(it["cold"]), "warm_us": stats(it["warm"]),
+                                "cold_frac_mfma_peak": it["work"] / (pct(it["cold"], 50) * 1e-6) / 1e12
+                                / MFMA_BF16_PEAK_TFLOPS} for it in items]
+        else:
+            res["mb_per_call"] = sum(it["work"] for it in items) / len(items) / 1e6
+            res["requests"] = items[0]["requests"]
+        return res
+
+    return {"workload": DESCR[index], "reps": reps, "extend": agg("extend", rec["extend"]),
+            "decode": agg("decode", rec["decode"])}
 
 
+# ------------------------------------------------------------------ other sections
 def scheduler_ablation():
     """Cache-aware scheduling on the host (no device work): the two-level workload's 136
     prompts (1024-token system prompt, 8 blocks of 512, 16 questions of 64 per block) in a
@@ -352,106 +554,152 @@ def projection_measure(dev):
     return out
 
 
-def decode_side_measure(index, workload, n_steps=8, first_decode=0):
-    """Decode attention on one of the decode-heavy workloads (configuration `index` of
-    workloads.configs). The steps before the chosen decode step run untimed; then each of
-    the next n_steps decode calls (rax_decode_step, as the runtime runs it) is replayed
-    REPLAYS times between one HIP event pair through rax_decode_attention_hinted, in the
-    layout the decode step chose from its host hints. Algorithmic
-    bytes per call: the distinct K/V rows the batch reads (each slot id in the batch's
-    req_to_token rows once), Q and O, 4 B per req_to_token entry."""
-    import torch
-    from prefix_shared_kv_extend_amd import _lib as L
-    from prefix_shared_kv_extend_amd.driver import JobRunner
-    from workloads import configs
-    job = configs.make(index)
-    runner = JobRunner(job, out_dtype=torch.bfloat16, record_log=False)
-    rt = runner.rt
-    first = [i for i, st in enumerate(job.steps) if st.decode][first_decode]
-    runner.run(steps=range(first))
-    elt = 2
-    us, nbytes = [], []
-
-    def on_decode(si, db, pairs, o):
-        q = torch.randn((len(db.rids), job.h_q, job.d), device=o.device).to(torch.bfloat16)
-        ws = rt._workspace(L.attention_workspace_bytes(True, len(db.rids), job.h_q, job.h_kv, job.d,
-                                                       db.max_seq_len))
-
-        def call(w):
-            return L.decode_attention_hinted(q, rt.k_pool, rt.v_pool, rt.rtt, db.dev["req_pool_idx"],
-                                             db.dev["seq_len"], db.max_seq_len, o, db.seq_len, db.shared_len_host,
-                                             workspace=w, shared_len=db.dev["shared_len"])
-        ws = rt._workspace(max(call(None), ws.numel()))
-        call(ws)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(REPLAYS):
-            call(ws)
-        b.record()
-        torch.cuda.synchronize()
-        us.append(a.elapsed_time(b) * 1e3 / REPLAYS)
-        lens = db.seq_len.astype(np.int64)
-        rows = db.dev["req_pool_idx"].long()
-        width = int(lens.max())
-        keys = rt.rtt[rows, :width]
-        inside = torch.arange(width, device=keys.device)[None, :] < torch.as_tensor(lens, device=keys.device)[:, None]
-        distinct = int(torch.unique(keys[inside]).numel())
-        nbytes.append(distinct * 2 * job.h_kv * job.d * elt + 2 * len(lens) * job.h_q * job.d * elt
-                      + int(lens.sum()) * 4)
-
-    runner.run(steps=range(first, first + n_steps), on_decode=on_decode)
-    assert L.device_errors() == 0
-    gbs = sum(nbytes) / (sum(us) * 1e-6) / 1e9
-    return {"workload": workload + "; %d decode steps" % n_steps,
-            "us_per_call": sum(us) / len(us), "mb_per_call": sum(nbytes) / len(nbytes) / 1e6,
-            "gbs_unique": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
-
-
-def decode_gqa_measure(n_steps=8):
-    """Self-consistency decode: 256 branches of U{0..1024} tokens off one 4096-token
-    prefix, GQA 64/8 heads x 128, bf16; its first n_steps decode calls."""
-    return decode_side_measure(3, "self-consistency: 256 branches of U{0..1024} tokens off a 4096-token prefix, "
-                                  "GQA 64/8 x 128, bf16; from the first decode step", n_steps)
-
-
-def decode_two_level_measure(n_steps=8):
-    """Two-level decode: a 1024-token system prefix, 8 exemplar blocks of 512 tokens, 16
-    questions of 64 tokens under each (128 requests), MHA 32 x 128, bf16; its first
-    n_steps decode calls. A 64-request row block spans four exemplar blocks: their keys
-    are computed once per block as deeper runs."""
-    return decode_side_measure(2, "two-level: 1024-token system prefix, 8 x 512-token exemplar blocks, "
-                                  "16 x 64-token questions each (128 requests), MHA 32 x 128, bf16; "
-                                  "from the first decode step", n_steps)
-
-
 def cpu_baseline(job, seconds):
-    """The oracle (fp64 recompute from scratch) on a bounded sample of the same workload."""
+    """The oracle (fp64 recompute from scratch) on a bounded sample of the headline job:
+    random requests, each with all of its attention queries (its extend suffix and every
+    decode position) recomputed from scratch over its full sequence."""
     import torch
     from oracle.attention import outputs_from_scratch
     threads = len(os.sched_getaffinity(0))
     torch.set_num_threads(threads)
+    first = {}
+    for _, kind, pairs in call_plan(job):
+        if kind == "extend":
+            for rid, p in pairs:
+                first.setdefault(rid, p)
     rng = np.random.default_rng(0)
-    done = 0
+    done, reqs, keys = 0, 0, 0
     t0 = time.perf_counter()
-    reqs = []
     while time.perf_counter() - t0 < seconds:
-        rid = int(rng.integers(1, len(job.requests)))
+        rid = int(rng.integers(0, len(job.requests)))
         r = job.requests[rid]
-        # all 50 suffix queries of one cached request plus its first decode query
-        pos = list(range(2000, r.n)) + [r.n]
+        pos = list(range(first[rid], r.n + len(r.output)))
         outputs_from_scratch(job.full_tokens(rid), pos, job.h_q, job.h_kv, job.d, job.seed, job.dtype)
         done += len(pos)
-        reqs.append(rid)
+        keys += sum(p + 1 for p in pos)
+        reqs += 1
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "attn tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(reqs)} cached requests x (50 suffix queries + 1 decode query), each recomputed "
-                      f"from scratch over its 2051-token sequence in fp64 ({dt:.1f} s)"}
+            "sample": f"{reqs} random multi-turn requests, each with all of its queries ({done} in total: the extend "
+                      f"suffix and every decode position, {keys / done:.0f} keys per query on average) recomputed "
+                      f"from scratch over its full sequence in fp64 ({dt:.1f} s)"}
 
 
+# ------------------------------------------------------------------ counter and trace summaries
+def _sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _counter_rows(csv_path, counter):
+    import csv
+    with open(csv_path) as f:
+        return [(x["Kernel_Name"], float(x["Counter_Value"])) for x in csv.DictReader(f)
+                if x["Counter_Name"] == counter]
+
+
+def write_traffic(run_dir):
+    """Condense rocprofv3 FETCH_SIZE / WRITE_SIZE runs (of this script with --passes cold, and
+    of --copy-calib) into profiles/traffic.json: HBM bytes per launch of each attention entry
+    point = the counters of all its kernels' dispatches / the number of launches (dispatches
+    of its anchor kernel), each counter scaled by what it reads for the plain copy of known
+    size."""
+    fetch = _counter_rows(os.path.join(run_dir, "pmc_FETCH_SIZE", "bench_counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_rows(os.path.join(run_dir, "pmc_WRITE_SIZE", "bench_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter_rows(os.path.join(run_dir, "copy_FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter_rows(os.path.join(run_dir, "copy_WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
+    copy_f = np.mean([v for k, v in cf if "kv_scatter_kernel" in k])
+    copy_w = np.mean([v for k, v in cw if "kv_scatter_kernel" in k])
+    f_scale = COPY_READ_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_WRITE_BYTES / (copy_w * 1024.0)
+    out = {"source_sha256": _sha256(KERNEL_SOURCE), "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "entries": {}}
+    for entry, spec in ENTRY_KERNELS.items():
+        n = sum(1 for k, _ in fetch if spec["anchor"] in k)
+        if not n:
+            continue
+        per = {}
+        for key in spec["kernels"]:
+            kf = [v for k, v in fetch if key in k and not any(o != key and o in k and len(o) > len(key)
+                                                             for o in spec["kernels"])]
+            kw = [v for k, v in write if key in k and not any(o != key and o in k and len(o) > len(key)
+                                                             for o in spec["kernels"])]
+            if kf:
+                per[key] = {"dispatches": len(kf), "fetch_kib_total": sum(kf), "write_kib_total": sum(kw),
+                            "bytes_per_launch": (sum(kf) * f_scale + sum(kw) * w_scale) * 1024 / n}
+        out["entries"][entry] = {"launches": n, "kernels": per,
+                                 "bytes_per_launch": sum(p["bytes_per_launch"] for p in per.values())}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic(entry, path):
+    """HBM bytes per launch of `entry` from the committed counter summary, or None when there
+    is none or the kernel source changed since the counters were taken."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != _sha256(KERNEL_SOURCE):
+        return None
+    return t.get("entries", {}).get(entry, {}).get("bytes_per_launch")
+
+
+HOT = ("shared_kernel", "own_", "merge_kernel", "attn_kernel", "kv_scatter_kernel", "rtt_write_kernel",
+       "decode_append_kernel", "kv_move_kernel")
+
+
+def summarize_trace(csv_path):
+    """Markdown summary of a rocprofv3 kernel trace: per kernel name, dispatches, mean and
+    total duration; and GPU idle over the window from the first to the last dispatch of the
+    hot path's kernels: the time no kernel runs (the union of dispatch intervals subtracted
+    from the window), in total and per trace step."""
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for x in csv.DictReader(f):
+            rows.append((int(x["Start_Timestamp"]), int(x["End_Timestamp"]), x["Kernel_Name"]))
+    rows.sort()
+    per = {}
+    for s, e, k in rows:
+        p = per.setdefault(k, [0, 0])
+        p[0] += 1
+        p[1] += e - s
+    print("| kernel | dispatches | mean us | total ms |\n|---|---|---|---|")
+    for k, (n, tot) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{k[:110]}` | {n} | {tot / n / 1e3:.2f} | {tot / 1e6:.3f} |")
+    hot = [r for r in rows if any(h in r[2] for h in HOT)]
+    if not hot:
+        return
+    w0, w1 = hot[0][0], max(e for _, e, _ in hot)
+    busy, cur_s, cur_e = 0, None, None
+    for s, e, _ in rows:
+        if e <= w0 or s >= w1:
+            continue
+        s, e = max(s, w0), min(e, w1)
+        if cur_e is None or s > cur_e:
+            if cur_e is not None:
+                busy += cur_e - cur_s
+            cur_s, cur_e = s, e
+        else:
+            cur_e = max(cur_e, e)
+    if cur_e is not None:
+        busy += cur_e - cur_s
+    win = w1 - w0
+    print(f"\nWindow of the hot path's kernels: {win / 1e6:.3f} ms; kernels busy {busy / 1e6:.3f} ms; "
+          f"GPU idle {(win - busy) / 1e6:.3f} ms ({(win - busy) / win:.1%}).")
+
+
+# ------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.write_traffic:
         write_traffic(args.write_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -460,8 +708,6 @@ def main():
         sys.exit(2)
     import torch
     from prefix_shared_kv_extend_amd import _lib
-    from prefix_shared_kv_extend_amd.driver import JobRunner
-    from workloads import configs
 
     _lib.lib()
     dev = torch.device("cuda:0")
@@ -482,90 +728,50 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": COPY_READ_BYTES, "copy_calib_bytes_written": COPY_WRITE_BYTES}))
         return
 
-    job = configs.make(1)
-    runner = JobRunner(job, device="cuda:0", out_dtype=torch.bfloat16, record_log=False)
-    prep = Prepared(runner, dev)                       # one untimed pass to learn every call's positions
-    runner.rt.tree.evict_lru(runner.rt.num_slots)
-    ext_flops, dec_bytes = algorithmic(job, prep)
-    n_ext_tok = sum(len(c[2]) for c in prep.calls if c[1] == "extend")
-    n_dec_tok = sum(len(c[2]) for c in prep.calls if c[1] == "decode")
+    if args.only:
+        print(json.dumps({args.only: side_config(SIDE[args.only], args.reps, Flusher(dev, args.flush_mib))}),
+              flush=True)
+        return
 
-    for _ in range(args.warmup):
-        run_step(runner, prep)
-    torch.cuda.synchronize()
-
-    # pass 1: the job as it runs (no timing events) -> value, ms_per_step
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step(runner, prep)
-    t_issued = time.perf_counter()                     # the host never waits inside the loop
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    host_ms = (t_issued - t0) * 1e3 / args.steps
-
-    # pass 2: the same steps, each attention call replayed back to back between a HIP event
-    # pair on the stream the kernels run on -> per-launch kernel times for the roofline
-    timers = {}
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        run_step(runner, prep, timers)
-    torch.cuda.synchronize()
-
-    ext_us = [a.elapsed_time(b) * 1e3 / REPLAYS for a, b in timers.get("extend", [])]
-    dec_us = [a.elapsed_time(b) * 1e3 / REPLAYS for a, b in timers.get("decode", [])]
-    per_step_ext = sum(ext_us) / args.steps
-    per_step_dec = sum(dec_us) / args.steps
-    ext_tflops = sum(ext_flops) * args.steps / (sum(ext_us) * 1e-6) / 1e12
-    dec_gbs = sum(dec_bytes) * args.steps / (sum(dec_us) * 1e-6) / 1e9
-    if per_step_ext >= per_step_dec:
-        roof = {"kernel": "extend attention (attn_kernel, bf16, D=128)", "bound": "mfma",
-                "achieved": ext_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ext_tflops / MFMA_BF16_PEAK_TFLOPS, "launches_per_step": len(ext_flops),
-                "avg_launch_us": sum(ext_us) / len(ext_us)}
+    h = headline(args, dev)
+    job = h.pop("_job")
+    h.pop("_inp")
+    out = {"metric": METRIC}
+    if "wall" in h:
+        out.update({"value": h["wall"]["value"], "unit": "attn tokens/s", "n_gpus": 1, "steps": args.steps,
+                    "warmup": args.warmup, "ms_per_step": h["wall"]["ms_per_step"]})
     else:
-        roof = {"kernel": "decode attention (shared_kernel + own_merge_kernel)", "bound": "hbm",
-                "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                "launches_per_step": len(dec_bytes), "avg_launch_us": sum(dec_us) / len(dec_us)}
-    roof["traffic"] = load_traffic("extend" if roof["bound"] == "mfma" else "decode", args.traffic)
-
-    out = {
-        "metric": METRIC,
-        "value": (n_ext_tok + n_dec_tok) * args.steps / (t1 - t0),
-        "unit": "attn tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded tokens; Q/K/V from a prefix-hash generator (N(0,1)), no model weights",
-        "config": {"workload": "fewshot: 64 requests x (2000 shared + 50 own) tokens, then 32 decode steps; "
-                               "1 layer, 32 heads MHA, head_dim 128, pool 2^20 slots",
-                   "extend_tokens_per_step": n_ext_tok, "decode_tokens_per_step": n_dec_tok,
-                   "prompt_tokens_per_step": sum(r.n for r in job.requests)},
-        "extend": {"kernel_us_per_step": per_step_ext, "tok_s_kernel": n_ext_tok / (per_step_ext * 1e-6),
-                   "tflops": ext_tflops, "frac_mfma_peak": ext_tflops / MFMA_BF16_PEAK_TFLOPS},
-        "decode": {"kernel_us_per_step": per_step_dec, "tok_s_kernel": n_dec_tok / (per_step_dec * 1e-6),
-                   "gbs_unique": dec_gbs, "frac_hbm_peak": dec_gbs / HBM_PEAK_GBS},
-        "hit_rate": 1.0 - n_ext_tok / sum(r.n for r in job.requests),
-        "roofline": roof,
-        # host/GPU overlap: the runtime never synchronises inside a step, so the tree work
-        # of one call overlaps the kernels of the previous ones; the GPU waits on the host
-        # only if issuing a step takes as long as the step itself
-        "overlap": {"host_issue_ms_per_step": host_ms, "wall_ms_per_step": ms,
-                    "attention_kernel_ms_per_step": (per_step_ext + per_step_dec) * 1e-3,
-                    "host_bound": host_ms > 0.97 * ms},
-    }
+        out.update({"value": None, "unit": "attn tokens/s", "n_gpus": 1, "steps": 0, "warmup": 0,
+                    "ms_per_step": None})
+    out.update({"higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic: seeded tokens; Q/K/V from a prefix-hash generator (N(0,1)), no model weights",
+                "config": h["config"], "hit_rate": h["hit_rate"]})
+    if "wall" in h:
+        out["ms_stats"] = h["wall"]["ms_stats"]
+    if "cold" in h:
+        out["extend"] = {"cold": h["cold"]["extend"]}
+        out["decode"] = {"cold": h["cold"]["decode"]}
+        if "natural" in h:
+            out["extend"]["natural"] = h["natural"]["extend"]
+            out["decode"]["natural"] = h["natural"]["decode"]
+        out["roofline"] = roofline_of(h["cold"], args.traffic)
+    if "wall" in h:
+        # the runtime never synchronises inside a job, so the tree work of one call overlaps
+        # the kernels of the previous ones; the GPU waits on the host when issuing a job takes
+        # about as long as the job
+        ov = {"host_issue_ms_per_step": h["wall"]["host_issue_ms"], "wall_ms_per_step": h["wall"]["ms_per_step"],
+              "host_bound": h["wall"]["host_issue_ms"] > 0.97 * h["wall"]["ms_per_step"]}
+        if "natural" in h:
+            ov["attention_kernel_ms_per_step"] = (h["natural"]["extend"]["us_per_step"]
+                                                  + h["natural"]["decode"]["us_per_step"]) * 1e-3
+        out["overlap"] = ov
     if not args.no_side:
+        flush = Flusher(dev, args.flush_mib)
+        for name, idx in SIDE.items():
+            out[name] = side_config(idx, args.reps, flush)
         out["scheduler"] = scheduler_ablation()
         out["host_tier"] = host_tier_measure(dev)
         out["qkv_projection"] = projection_measure(dev)
-        out["decode_gqa"] = decode_gqa_measure()
-        out["decode_two_level"] = decode_two_level_measure()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -329,15 +329,22 @@ rax_status rax_decode_append(rax_tree* t, int32_t batch, int32_t* seq_len, int32
  * shared_len[r] (r >= 1) promises that requests r-1 and r have identical slots at
  * positions [0, shared_len[r]) -- the kernel then loads those K/V tiles once for the
  * query rows of both requests. d in {64, 128}; h_q % h_kv == 0; dt RAX_F32 or RAX_BF16
- * (pools, q, k_ext, v_ext); o_dt RAX_F32 or RAX_BF16; fp32 accumulation throughout. */
+ * (pools, q, k_ext, v_ext); o_dt RAX_F32 or RAX_BF16; fp32 accumulation throughout.
+ * max_kv_len: the most keys any query row of the call sees (max over r of prefix_len[r] +
+ * q_len_r), or 0 if unknown. It only sizes the work: when the call has few row blocks
+ * (few long requests), each block's key range is split over several workgroups whose
+ * partial softmax states go to `workspace` and are merged by log-sum-exp (results equal
+ * up to summation order). The split uses at most what ws_bytes holds (size from
+ * rax_attention_workspace_bytes(0, total_q, ..., max_kv_len)); with no workspace or
+ * max_kv_len 0 there is no split. RAX_EINVAL: bad sizes, dtypes or null pointers. */
 rax_status rax_extend_attention(const void* q, const void* k_ext, const void* v_ext,
                                 const void* k_pool, const void* v_pool, int64_t num_slots,
                                 const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
                                 const int32_t* req_pool_idx, const int32_t* prefix_len,
                                 const int32_t* qo_indptr, const int32_t* shared_len, int32_t batch,
-                                int64_t total_q, int32_t h_q, int32_t h_kv, int32_t d, float sm_scale,
-                                rax_dtype dt, void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes,
-                                void* stream);
+                                int64_t total_q, int32_t max_kv_len, int32_t h_q, int32_t h_kv, int32_t d,
+                                float sm_scale, rax_dtype dt, void* o, rax_dtype o_dt, void* workspace,
+                                size_t ws_bytes, void* stream);
 
 /* Batched decode attention ([notes] App. A.1: a decoding step attends over the KV of
  * all previous tokens and itself). Request r's new token is already in the pool: its

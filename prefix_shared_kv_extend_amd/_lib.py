@@ -82,7 +82,7 @@ _SIGS = {
                                  _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "rax_req_to_token_write": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _vp]),
     "rax_extend_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
-                                    _i32, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
+                                    _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_decode_attention": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_decode_attention_hinted": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
@@ -508,7 +508,10 @@ def attention_workspace_bytes(is_decode: bool, rows: int, h_q: int, h_kv: int, d
 
 
 def extend_attention(q, k_ext, v_ext, k_pool, v_pool, req_to_token, req_pool_idx, prefix_len, qo_indptr,
-                     o, shared_len=None, sm_scale=None, workspace=None, stream=None) -> None:
+                     o, shared_len=None, sm_scale=None, workspace=None, stream=None, max_kv_len: int = 0) -> None:
+    """rax_extend_attention. max_kv_len (the most keys a query row sees, 0 = unknown) and a
+    workspace of rax_attention_workspace_bytes(False, total_q, ..., max_kv_len) bytes let a
+    call of few long requests split its key ranges over more workgroups."""
     _need(q.dim() == 3 and k_ext.dim() == 3 and q.shape[0] == k_ext.shape[0], "q [T,h_q,d], k_ext [T,h_kv,d]")
     _need(k_ext.shape == v_ext.shape and k_pool.shape == v_pool.shape, "k/v shapes")
     _need(k_pool.shape[1:] == k_ext.shape[1:] and q.shape[2] == k_pool.shape[2], "head shapes")
@@ -519,13 +522,14 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, req_to_token, req_pool_idx
     b = req_pool_idx.numel()
     _need(prefix_len.numel() == b and qo_indptr.numel() == b + 1, "metadata shapes")
     _need(shared_len is None or shared_len.numel() == b, "shared_len: [batch]")
+    _need(workspace is None or (workspace.is_cuda and workspace.is_contiguous()), "workspace: contiguous cuda")
     d = q.shape[2]
     scale = float(sm_scale if sm_scale is not None else d ** -0.5)
     ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().rax_extend_attention(
         _dev(q), _dev(k_ext), _dev(v_ext), _dev(k_pool), _dev(v_pool), k_pool.shape[0],
         _dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0], _dev(req_pool_idx), _dev(prefix_len),
-        _dev(qo_indptr), _dev(shared_len), b, q.shape[0], q.shape[1], k_pool.shape[1], d, scale,
+        _dev(qo_indptr), _dev(shared_len), b, q.shape[0], int(max_kv_len), q.shape[1], k_pool.shape[1], d, scale,
         _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws, _stream(stream, q)), "rax_extend_attention")
 
 

@@ -812,6 +812,8 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds row jrow of each row tile, dims dt*32 + 8*(r/4) + 4*half + r%4
+  // (split partials at the block's own place: extend takes row blocks in reverse order)
+  const int64_t item_w = ((int64_t)h * a.n_rb + rb) * a.nsplit + split;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (!row_ok[rt]) continue;
@@ -836,7 +838,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         }
       }
     } else if (l_run[rt] > 0.f) {
-      float* wacc = a.ws + (item * BM + R) * (int64_t)D;
+      float* wacc = a.ws + (item_w * BM + R) * (int64_t)D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -849,7 +851,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     }
     if (partial && half == 0) {  // (m, l) of every row; l == 0 means "no keys here"
       const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
-      float* wml = a.ws + n_items * BM * (int64_t)D + (item * BM + R) * 2;
+      float* wml = a.ws + n_items * BM * (int64_t)D + (item_w * BM + R) * 2;
       wml[0] = m_run[rt];
       wml[1] = l_run[rt];
     }
@@ -1935,6 +1937,128 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
   }
 }
 
+// End of an own-part workgroup with query-head groups (bf16, D = 128, 4 waves as four key
+// groups, the g query heads as rows of one 32-row tile): the groups' (m, l, acc) combine
+// split by dims through LDS (xbuf: at least 51,200 bytes, free when called), then either
+// the request's only own chunk is merged in place with the shared part's split partials and
+// O written, or the chunk's partial goes to the workspace in own_kernel's layout.
+template <int D>
+__device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbuf, const f32x16 (&acc)[D / 32],
+                                                    float m_run, float l_run, int wkey, int lane, int jrow, int half,
+                                                    bool row_ok, int t, int h, int rh, int c, int n_act, int n_rh) {
+  constexpr int NKG = 4;
+  const int G = a.g;
+  constexpr int NDT = D / 32;
+  static_assert(NDT == NKG, "one 32-dim slice per key group");
+  constexpr int NX = NDT * (NKG - 1) * 16;  // floats per lane handed over
+  static_assert((NX + NKG * 2) * 64 * sizeof(float) <= 51200, "key-split exchange area");
+  float* xs = reinterpret_cast<float*>(xbuf);  // [dt][group other than dt][16][64]
+  float* xml = xs + NX * 64;                 // [group][m, l][64]
+  auto xacc = [&](int dt, int grp, int r) -> float& {
+    const int g3 = grp < dt ? grp : grp - 1;
+    return xs[((dt * (NKG - 1) + g3) * 16 + r) * 64 + lane];
+  };
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt == wkey) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xacc(dt, wkey, r) = acc[dt][r];
+  }
+  xml[(wkey * 2 + 0) * 64 + lane] = m_run;
+  xml[(wkey * 2 + 1) * 64 + lane] = l_run;
+  __syncthreads();
+  float mk[NKG], lk[NKG];
+  float m = kNegInf;
+#pragma unroll
+  for (int k = 0; k < NKG; ++k) {
+    mk[k] = xml[(k * 2 + 0) * 64 + lane];
+    lk[k] = xml[(k * 2 + 1) * 64 + lane];
+    m = fmaxf(m, mk[k]);
+  }
+  float l = 0.f;
+  f32x16 o = f32x16{};
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    if (dt != wkey) continue;
+    if (m != kNegInf) {
+#pragma unroll
+      for (int k = 0; k < NKG; ++k) {
+        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
+        l += lk[k] * ak;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(dt, k, r)) * ak;
+      }
+    }
+  }
+  if (!row_ok) return;
+  if (n_act == 1) {
+    // the request's only own chunk: merge here with the shared part's split partials of
+    // this row (written by the previous kernel) by log-sum-exp and write this wave's
+    // dims of O; merge_kernel skips such rows. A split that saw no key (l == 0) may hold
+    // stale data, hence the selects.
+    const int Grow = t * G + jrow;
+    const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
+    const int nsplit = a.nsplit;
+    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+    const int64_t item0 = ((int64_t)h * a.n_rb + rbr) * nsplit;
+    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
+    const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D;
+    float M = l > 0.f ? m : kNegInf;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
+      if (ml.y > 0.f) M = fmaxf(M, ml.x);
+    }
+    const float Mu = M == kNegInf ? 0.f : M;
+    const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
+    float lsum = w_own * l;
+    f32x16 fin;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fin[r] = w_own != 0.f ? w_own * o[r] : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
+      const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - Mu) : 0.f;
+      lsum += w * ml.y;
+      const float* pa = sh_acc + (int64_t)sp * a.bm * D;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 8 * rg + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin[rg * 4 + e] += w != 0.f ? w * x[e] : 0.f;
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t obase = ((int64_t)t * a.h_q + h * G + jrow) * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+      if (a.o_bf16)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
+            bf16x4{(__bf16)(fin[rg * 4 + 0] * inv), (__bf16)(fin[rg * 4 + 1] * inv), (__bf16)(fin[rg * 4 + 2] * inv),
+                   (__bf16)(fin[rg * 4 + 3] * inv)};
+      else
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) =
+            make_float4(fin[rg * 4 + 0] * inv, fin[rg * 4 + 1] * inv, fin[rg * 4 + 2] * inv, fin[rg * 4 + 3] * inv);
+    }
+    return;
+  }
+  // partial of (request t, KV head h, chunk c), query head jrow, in own_kernel's layout
+  const int64_t item = (int64_t)rh * a.n_chunk + c;
+  if (l > 0.f) {
+    float* wacc = a.ws_own + (item * G + jrow) * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+      __builtin_nontemporal_store(f32x4{o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]},
+                                  reinterpret_cast<f32x4*>(wacc + d0));
+    }
+  }
+  if (wkey == 0 && half == 0) {
+    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + jrow) * 2;
+    __builtin_nontemporal_store(m, wml);
+    __builtin_nontemporal_store(l, wml + 1);
+  }
+}
+
 // Own part of split decode on MFMA for query-head groups (g = 2..16), bf16, D = 128.
 // own_chunk scores 32 / g keys per batch, each batch a chain of cross-lane reductions and
 // broadcasts, so for g > 1 that work bounds it rather than memory (self-consistency
@@ -2116,116 +2240,194 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) o
     __syncthreads();  // the next round overwrites the tiles
   }
 
-  // the four key groups combine split by dims (as in shared_kernel, one row tile)
-  constexpr int NDT = D / 32;
-  static_assert(NDT == NKG, "one 32-dim slice per key group");
-  constexpr int NX = NDT * (NKG - 1) * 16;  // floats per lane handed over
-  static_assert((NX + NKG * 2) * 64 * sizeof(float) <= sizeof(kv), "key-split exchange area");
-  float* xs = reinterpret_cast<float*>(kv);  // [dt][group other than dt][16][64]
-  float* xml = xs + NX * 64;                 // [group][m, l][64]
-  auto xacc = [&](int dt, int grp, int r) -> float& {
-    const int g3 = grp < dt ? grp : grp - 1;
-    return xs[((dt * (NKG - 1) + g3) * 16 + r) * 64 + lane];
-  };
+  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wkey, lane, jrow, half, row_ok, t, h, rh, c, n_act, n_rh);
+}
+
+// Own part of split decode with query-head groups (bf16, D = 128), as one continuous
+// stream per workgroup. A workgroup takes one own chunk of (request t, KV head h), at
+// most kStreamCap keys. Its slot ids go to LDS first (one round of loads); then the
+// chunk's keys stream through a ring of S stages of 32 keys (8 KB of K and 8 KB of V
+// each) filled straight from global memory: while stage i is computed, the loads of the
+// next S - 1 stages are in flight, so bytes stay in flight all the time instead of one
+// round of tiles at a time. One barrier per stage. The four waves are four key groups:
+// wave w computes stages i = w (mod 4) (S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMA,
+// the g query heads as rows of one 32-row tile, rows past g masked), and the groups
+// combine at the end as in own_tile_kernel. Keys past the chunk in its last stage read
+// the chunk's first slot (a key it attends, so finite) and are masked.
+constexpr int kStreamCap = 2048;  // most keys per own chunk of own_stream_kernel
+constexpr int kStreamTK = 32;     // keys per stage
+#ifndef RAX_STREAM_STAGES
+#define RAX_STREAM_STAGES 4
+#endif
+#ifndef RAX_STREAM_NT
+#define RAX_STREAM_NT 1
+#endif
+constexpr int kStreamStages = RAX_STREAM_STAGES;
+
+template <int D, int S>
+__global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
+  static_assert(D == 128, "the swizzle assumes 16 chunks per row");
+  static_assert(S >= 2 && 2 * (S - 2) < 64, "stages");
+  constexpr int NW = 4;
+  constexpr int TK = kStreamTK;
+  constexpr int RB = D * 2;              // bytes per row
+  constexpr int TB = TK * RB;            // bytes of K (or V) per stage
+  constexpr int RPI = 1024 / RB;         // rows per 1 KB global-to-LDS instruction
+  constexpr int NI = TK / RPI;           // instructions per K (or V) stage
+  constexpr int IPW = NI / NW;           // of them per wave
+  constexpr int NKS = D / 16;
+  constexpr int KV_BYTES = S * 2 * TB > 51200 ? S * 2 * TB : 51200;  // also the groups' exchange area
+  static_assert(NI % NW == 0, "loads per wave");
+  __shared__ __align__(16) char kv[KV_BYTES];
+  __shared__ int32_t slot[kStreamCap];
+  const uint32_t kv_lds = lds_addr(kv);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int jrow = lane & 31, half = lane >> 5;
+  const int G = a.g;
+  const int n_rh = a.batch * a.h_kv;
+  const int c = blockIdx.x / n_rh;  // chunk slowest: chunks past every request's keys exit together
+  const int rh = blockIdx.x - c * n_rh;
+  const int t = rh / a.h_kv;
+  const int h = rh - t * a.h_kv;
+
+  const int rb0 = t * G / a.bm;
+  const BlockMeta meta = block_meta_load(a, rb0, lane);
+  const bool row_ok = jrow < G;
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp =
+        reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? jrow : 0)) * D;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    if (dt == wkey) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xacc(dt, wkey, r) = acc[dt][r];
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
   }
-  xml[(wkey * 2 + 0) * 64 + lane] = m_run;
-  xml[(wkey * 2 + 1) * 64 + lane] = l_run;
+  const int rl = t - rb0 * a.bm / G;
+  const int L = row_shared_len(a, meta, lane, rl);
+  const int row_t = __builtin_amdgcn_readlane(meta.row, rl);
+  const int end = __builtin_amdgcn_readlane(meta.len, rl);
+  int first, per;
+  const int n_act = own_chunks(a, row_t, end, L, first, per);
+  if (c >= n_act) return;  // the same for the whole workgroup
+  const int start = first + c * per;
+  int stop = min(start + per, end);
+  if (stop - start > kStreamCap) {  // the layout bounds every chunk; never taken
+    flag_error(RAX_DEVERR_ROW);
+    stop = start + kStreamCap;
+  }
+  const int n = stop - start;
+  const int n_tiles = (n + TK - 1) / TK;
+  const int64_t row_bytes = (int64_t)a.h_kv * RB;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
+  const int32_t* rtt_row = a.rtt + (int64_t)row_t * a.rtt_stride;  // row_t valid: n_act > 0
+
+  // every slot id of the chunk into LDS in one round of loads (positions past the chunk
+  // take the chunk's first slot)
+  {
+    constexpr int PER_T = kStreamCap / (64 * NW);
+    int raw[PER_T];
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int i = tid + k * 64 * NW;
+      raw[k] = rtt_row[start + (i < n ? i : 0)];
+    }
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int i = tid + k * 64 * NW;
+      int sv = raw[k];
+      if (sv < 0 || sv >= a.num_slots) {
+        if (i < n) flag_error(RAX_DEVERR_SLOT);
+        sv = 0;
+      }
+      if (i < n_tiles * TK) slot[i] = sv;
+    }
+  }
   __syncthreads();
-  float mk[NKG], lk[NKG];
-  float m = kNegInf;
+
+  // the K and V rows of stage j's keys into ring slot j % S
+  auto issue = [&](int j) {
+    const uint32_t kl = kv_lds + (j % S) * 2 * TB;
 #pragma unroll
-  for (int k = 0; k < NKG; ++k) {
-    mk[k] = xml[(k * 2 + 0) * 64 + lane];
-    lk[k] = xml[(k * 2 + 1) * 64 + lane];
-    m = fmaxf(m, mk[k]);
-  }
-  float l = 0.f;
-  f32x16 o = f32x16{};
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    if (dt != wkey) continue;
-    if (m != kNegInf) {
-#pragma unroll
-      for (int k = 0; k < NKG; ++k) {
-        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
-        l += lk[k] * ak;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(dt, k, r)) * ak;
-      }
+    for (int u = 0; u < IPW; ++u) {
+      const int q = wave + u * NW;
+      const int r = q * RPI + (lane >> 4);
+      const int64_t off = (int64_t)slot[j * TK + r] * row_bytes;
+#if RAX_STREAM_NT
+      lds_load16_nt(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
+      lds_load16_nt(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + TB + q * 1024));
+#else
+      lds_load16(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
+      lds_load16(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + TB + q * 1024));
+#endif
     }
-  }
-  if (!row_ok) return;
-  if (n_act == 1) {
-    // the request's only own chunk: merge here with the shared part's split partials of
-    // this row (written by the previous kernel) by log-sum-exp and write this wave's
-    // dims of O; merge_kernel skips such rows. A split that saw no key (l == 0) may hold
-    // stale data, hence the selects.
-    const int Grow = t * G + jrow;
-    const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
-    const int nsplit = a.nsplit;
-    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
-    const int64_t item0 = ((int64_t)h * a.n_rb + rbr) * nsplit;
-    const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
-    const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D;
-    float M = l > 0.f ? m : kNegInf;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
-      if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  for (int j = 0; j < S - 1 && j < n_tiles; ++j) issue(j);
+  for (int i = 0; i < n_tiles; ++i) {
+    // this wave's loads of stage i are done when at most those of the stages issued after
+    // it (up to S - 2, each 2 * IPW loads) are in flight; the barrier makes every wave's
+    // loads of stage i visible and frees ring slot (i - 1) % S for stage i + S - 1
+    if (i + S - 2 < n_tiles) wait_vmcnt<2 * IPW * (S - 2)>();
+    else wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    if (i + S - 1 < n_tiles) issue(i + S - 1);
+    if ((i & (NW - 1)) != wave) continue;
+    const char* kt = kv + (i % S) * 2 * TB;
+    const char* vt = kt + TB;
+    const int cnt = min(TK, n - i * TK);
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, jrow, ks, half), qf[ks], sc, 0, 0, 0);
+    // register r holds key 8*(r/4) + 4*half + r%4 of the stage, for this lane's row
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+      const float v = row_ok && key < cnt ? sc[r] : kNegInf;
+      sc[r] = v;
+      mx = fmaxf(mx, v);
     }
-    const float Mu = M == kNegInf ? 0.f : M;
-    const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
-    float lsum = w_own * l;
-    f32x16 fin;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) fin[r] = w_own != 0.f ? w_own * o[r] : 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
-      const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - Mu) : 0.f;
-      lsum += w * ml.y;
-      const float* pa = sh_acc + (int64_t)sp * a.bm * D;
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 8 * rg + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fin[rg * 4 + e] += w != 0.f ? w * x[e] : 0.f;
-      }
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int64_t obase = ((int64_t)t * a.h_q + h * G + jrow) * D;
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    float psum = 0.f;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = wkey * 32 + 8 * rg + 4 * half;
-      if (a.o_bf16)
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
-            bf16x4{(__bf16)(fin[rg * 4 + 0] * inv), (__bf16)(fin[rg * 4 + 1] * inv), (__bf16)(fin[rg * 4 + 2] * inv),
-                   (__bf16)(fin[rg * 4 + 3] * inv)};
-      else
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) =
-            make_float4(fin[rg * 4 + 0] * inv, fin[rg * 4 + 1] * inv, fin[rg * 4 + 2] * inv, fin[rg * 4 + 3] * inv);
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
+      sc[r] = pv;
+      psum += pv;
     }
-    return;
-  }
-  // partial of (request t, KV head h, chunk c), query head jrow, in own_kernel's layout
-  const int64_t item = (int64_t)rh * a.n_chunk + c;
-  if (l > 0.f) {
-    float* wacc = a.ws_own + (item * G + jrow) * D;
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    bf16x8 pb[2];
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = wkey * 32 + 8 * rg + 4 * half;
-      __builtin_nontemporal_store(f32x4{o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]},
-                                  reinterpret_cast<f32x4*>(wacc + d0));
-    }
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, 0, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
   }
-  if (wkey == 0 && half == 0) {
-    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + jrow) * 2;
-    __builtin_nontemporal_store(m, wml);
-    __builtin_nontemporal_store(l, wml + 1);
-  }
+  __syncthreads();  // the exchange below overwrites the ring
+  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wave, lane, jrow, half, row_ok, t, h, rh, c, n_act, n_rh);
 }
 
 // ------------------------------------------------------------------ host side
@@ -2261,6 +2463,20 @@ static int choose_nsplit(int64_t blocks, int32_t max_kv_len) {
   if (want > 32) want = 32;
   if (want < 1) want = 1;
   return (int)want;
+}
+
+// Key splits of an extend call: up to one workgroup per CU (the extend shape runs one per
+// CU), never more, so the grid stays one round. A call of few long requests has few row
+// blocks (a multi-turn turn of 500 new tokens over a 2000-token history: 8 blocks per KV
+// head), so without splits most CUs would idle. Each split keeps at least 4 tiles of the
+// longest key range; 0 = unknown length, no split.
+constexpr int64_t kExtendWGs = 256;
+static int32_t extend_nsplit(int64_t blocks, int32_t max_kv_len) {
+  if (max_kv_len <= 0 || blocks <= 0) return 1;
+  const int64_t tiles = ((int64_t)max_kv_len + BN - 1) / BN;
+  int64_t want = kExtendWGs / blocks;
+  want = std::min<int64_t>({want, tiles / 4, 32});
+  return (int32_t)std::max<int64_t>(want, 1);
 }
 
 static size_t ws_bytes_for(int64_t items, int bm, int d) {
@@ -2372,7 +2588,7 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
       if constexpr (sizeof(T) == 2 && D == 128) {
         const int64_t items = (int64_t)a.batch * a.h_kv * a.n_chunk;
         if (items > INT32_MAX) return RAX_EINVAL;
-        hipLaunchKernelGGL((own_tile_kernel<D>), dim3((unsigned)items), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a);
         rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
         if (rc != RAX_OK) return rc;
       } else {
@@ -2450,13 +2666,15 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   // few-shot decode, 4096 waves 15.4 us, 8192 waves 20.2 us, 2048 waves 16.7 us.
   constexpr int64_t kOwnWaves = 4096;
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
-  if (dt == RAX_BF16 && d == 128 && g >= 2) {
-    // query-head groups: own keys on MFMA (own_tile_kernel), chunks of at least
-    // kOwnTileMin keys, at most kOwnTileChunks per (request, KV head); longer chunks take
-    // several rounds of tiles
+  // query-head groups: own keys on MFMA (own_stream_kernel), chunks of at least
+  // kOwnTileMin keys, at most kOwnTileChunks per (request, KV head) unless more are needed
+  // to keep every chunk within kStreamCap keys (the slot ids a workgroup holds in LDS)
+  const int64_t cap_chunks = ((int64_t)max_seq_len + kStreamCap - 1) / kStreamCap;
+  if (dt == RAX_BF16 && d == 128 && g >= 2 && cap_chunks <= 64 - l.nsplit) {
     l.own_min = kOwnTileMin;
     l.n_chunk = (int32_t)std::max<int64_t>(
-        1, std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnTileMin - 1) / kOwnTileMin, kOwnTileChunks}));
+        {1, cap_chunks,
+         std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnTileMin - 1) / kOwnTileMin, kOwnTileChunks})});
     l.own_mode = 2;
   } else {
     l.own_min = kOwnMin;
@@ -2501,8 +2719,16 @@ using namespace raxk;
 extern "C" size_t rax_attention_workspace_bytes(int32_t is_decode, int64_t rows, int32_t h_q, int32_t h_kv,
                                                 int32_t d, int32_t max_kv_len) {
   if (rows <= 0 || h_kv < 1 || h_q < h_kv || h_q % h_kv || (d != 64 && d != 128) || max_kv_len < 0) return 0;
-  if (!is_decode) return 0;  // extend writes O directly
-  size_t need = 0;           // the larger need of the two input dtypes' block shapes
+  size_t need = 0;  // the larger need of the two input dtypes' block shapes
+  if (!is_decode) {  // key-split partials of extend (none without splits)
+    for (rax_dtype dt : {RAX_BF16, RAX_F32}) {
+      const Shape s = pick_shape(false, dt, d);
+      const int64_t n_rb = (rows * (h_q / h_kv) + s.bm() - 1) / s.bm();
+      const int32_t nsplit = extend_nsplit(n_rb * h_kv, max_kv_len);
+      if (nsplit > 1) need = max(need, ws_bytes_for((int64_t)h_kv * n_rb * nsplit, s.bm(), d));
+    }
+    return need;
+  }
   for (rax_dtype dt : {RAX_BF16, RAX_F32}) {
     const DecodeLayout l = decode_layout(rows, h_q, h_kv, d, max_kv_len, dt);
     need = max(need, (size_t)l.total * sizeof(float));
@@ -2515,13 +2741,11 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
                                            const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
                                            const int32_t* req_pool_idx, const int32_t* prefix_len,
                                            const int32_t* qo_indptr, const int32_t* shared_len, int32_t batch,
-                                           int64_t total_q, int32_t h_q, int32_t h_kv, int32_t d,
-                                           float sm_scale, rax_dtype dt, void* o, rax_dtype o_dt,
+                                           int64_t total_q, int32_t max_kv_len, int32_t h_q, int32_t h_kv,
+                                           int32_t d, float sm_scale, rax_dtype dt, void* o, rax_dtype o_dt,
                                            void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!common_ok(h_q, h_kv, d, dt, o_dt) || batch < 0 || total_q < 0 || num_slots < 1 || rtt_stride < 1 ||
-      rtt_rows < 1 || rtt_stride > INT32_MAX)
+      rtt_rows < 1 || rtt_stride > INT32_MAX || max_kv_len < 0)
     return RAX_EINVAL;
   if (batch == 0 || total_q == 0) return RAX_OK;
   if (!q || !k_ext || !v_ext || !k_pool || !v_pool || !req_to_token || !req_pool_idx || !prefix_len ||
@@ -2551,9 +2775,13 @@ extern "C" rax_status rax_extend_attention(const void* q, const void* k_ext, con
   a.o = o;
   a.o_bf16 = o_dt == RAX_BF16;
   a.ws = nullptr;
-  a.nsplit = 1;
   a.bm = s.bm();
   a.n_rb = (int32_t)((total_q * a.g + a.bm - 1) / a.bm);
+  // key splits, as many as the workspace holds (none without one)
+  int32_t nsplit = extend_nsplit((int64_t)a.n_rb * h_kv, max_kv_len);
+  while (nsplit > 1 && (!workspace || ws_bytes < ws_bytes_for((int64_t)h_kv * a.n_rb * nsplit, a.bm, d))) --nsplit;
+  a.nsplit = nsplit;
+  if (nsplit > 1) a.ws = reinterpret_cast<float*>(workspace);
   return dispatch<false>(a, dt, d, s, (hipStream_t)stream);
 }
 

@@ -50,7 +50,7 @@ const char* rax_status_str(rax_status s) {
   }
 }
 
-int32_t rax_abi_version(void) { return 3; }
+int32_t rax_abi_version(void) { return 4; }
 
 rax_status rax_tree_create(int64_t num_slots, rax_tree** out) {
   if (!out || num_slots < 1 || num_slots >= (int64_t(1) << 31)) return RAX_EINVAL;

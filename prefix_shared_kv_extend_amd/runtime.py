@@ -51,6 +51,7 @@ class ExtendBatch:
     total_q: int
     tokens: np.ndarray = None     # prompts, flat
     tok_indptr: np.ndarray = None
+    max_kv_len: int = 0           # the most keys a query row sees (the longest prompt)
     dev: dict = field(default_factory=dict)
 
 
@@ -105,6 +106,7 @@ class RadixRuntime:
         self.log = log
         self.step = 0                        # label of the current step in the event log (set by the caller)
         self.timers = None                   # {"extend": [...], "decode": [...]} of (start, end) events, if set
+        self.pre_attention = None            # called right before each attention call is issued, if set
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
         self._dec_cache = None               # _DecodeState while the decode batch is unchanged
 
@@ -204,7 +206,8 @@ class RadixRuntime:
         req_rows = np.array(req_rows, dtype=np.int32)
         qo = np.zeros(len(rids) + 1, dtype=np.int32)
         qo[1:] = np.cumsum(q_len)
-        eb = ExtendBatch(rids, m.astype(np.int32), q_len, qo, int(qo[-1]), toks, ip)
+        eb = ExtendBatch(rids, m.astype(np.int32), q_len, qo, int(qo[-1]), toks, ip,
+                         max_kv_len=int(n.max()) if len(n) else 0)
         eb.dev = self._upload(dict(
             req_pool_idx=req_rows, prefix_len=eb.prefix_len, qo_indptr=qo,
             shared_len=self.tree.lca_depths(nodes), out_loc=new, rtt_start=np.zeros(len(rids)),
@@ -222,9 +225,14 @@ class RadixRuntime:
         if eb.total_q == 0:
             return
         L.kv_scatter(k_ext, v_ext, eb.dev["out_loc"], self.k_pool, self.v_pool)
+        if self.pre_attention is not None:
+            self.pre_attention()
+        ws = self._workspace(L.attention_workspace_bytes(False, eb.total_q, self.h_q, self.h_kv, self.d,
+                                                         eb.max_kv_len))
         ev = self._event_pair("extend")
         L.extend_attention(q, k_ext, v_ext, self.k_pool, self.v_pool, self.rtt, eb.dev["req_pool_idx"],
-                           eb.dev["prefix_len"], eb.dev["qo_indptr"], o, shared_len=eb.dev["shared_len"])
+                           eb.dev["prefix_len"], eb.dev["qo_indptr"], o, shared_len=eb.dev["shared_len"],
+                           workspace=ws, max_kv_len=eb.max_kv_len)
         if ev:
             ev[1].record()
 
@@ -297,6 +305,8 @@ class RadixRuntime:
         ds = self._dec_cache
         if ds is None or db.key is not ds.key:
             raise ValueError("run_decode: batch differs from the last begin_decode")
+        if self.pre_attention is not None:
+            self.pre_attention()
         ev = self._event_pair("decode")
         new, freed, need = self.tree.decode_step(ds.prep, q, k_new, v_new, o, self._ws)
         if new is None:                      # workspace too small: nothing was done

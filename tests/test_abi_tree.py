@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
     assert set(L.EXPORTS) <= names            # the binding declares nothing that the header lacks
-    assert lib.rax_abi_version() == 3
+    assert lib.rax_abi_version() == 4
 
 
 def test_error_codes(L):
@@ -78,7 +78,13 @@ def test_error_codes(L):
     assert lib.rax_decode_attention(None, None, None, 1, None, 1, 1, None, None, None, 1, 1,
                                     6, 4, 128, 1.0, 1, None, 0, None, 0, None) == L.EINVAL   # h_q % h_kv
     assert lib.rax_extend_attention(None, None, None, None, None, 1, None, 1, 1, None, None, None, None,
-                                    1, 1, 4, 4, 96, 1.0, 1, None, 0, None, 0, None) == L.EINVAL  # d = 96
+                                    1, 1, 0, 4, 4, 96, 1.0, 1, None, 0, None, 0, None) == L.EINVAL  # d = 96
+    assert lib.rax_extend_attention(None, None, None, None, None, 1, None, 1, 1, None, None, None, None,
+                                    1, 1, -1, 4, 4, 128, 1.0, 1, None, 0, None, 0, None) == L.EINVAL  # length
+    # extend workspace: none for many row blocks or unknown lengths, split partials for few
+    assert L.attention_workspace_bytes(False, 3150, 32, 32, 128, 2050) == 0
+    assert L.attention_workspace_bytes(False, 500, 32, 8, 128, 0) == 0
+    assert L.attention_workspace_bytes(False, 500, 32, 8, 128, 2500) > 0
 
 
 def _both(op, model, tree, *args):

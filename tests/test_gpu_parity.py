@@ -602,6 +602,72 @@ def test_decode_step_rejects_strided_and_host_tensors():
     assert t.free_count() == 64                              # nothing was allocated
 
 
+@pytest.mark.parametrize("dt,h_q,h_kv,d,reqs", [
+    ("bf16", 32, 8, 128, [(1800, 300)]),
+    ("bf16", 32, 8, 128, [(1500, 200), (0, 77), (1700, 64)]),
+    ("bf16", 4, 4, 128, [(2100, 130), (900, 1)]),
+    ("f32", 8, 2, 64, [(1300, 150), (640, 33)]),
+    ("f32", 4, 4, 128, [(1100, 90)]),
+])
+def test_extend_key_split_direct(dt, h_q, h_kv, d, reqs):
+    """Extend calls of few long requests, whose key ranges are split over several workgroups
+    (partials merged by log-sum-exp): hand-built prefixes in shuffled pool slots and
+    suffixes in k_ext/v_ext. Every output against fp64 attention over the request's keys
+    (oracle.attention.attend), with and without the workspace that enables the split."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    say(f"extend key split: {dt} {h_q}/{h_kv} d={d}, (prefix, suffix) = {reqs}")
+    S = 1 << 14
+    gen = torch.Generator().manual_seed(331 + h_q + d + len(reqs))
+    perm = torch.randperm(S, generator=gen).numpy().astype(np.int32)
+    B = len(reqs)
+    W = max(m + n for m, n in reqs) + 5
+    rtt = np.full((B + 2, W), -1, dtype=np.int32)
+    rows = np.arange(B, dtype=np.int32) + 1
+    used = 0
+    for i, (m, n) in enumerate(reqs):
+        rtt[rows[i], :m] = perm[used: used + m]
+        used += m
+    qo = np.zeros(B + 1, dtype=np.int32)
+    qo[1:] = np.cumsum([n for _, n in reqs])
+    T = int(qo[-1])
+    prefix = np.array([m for m, _ in reqs], dtype=np.int32)
+    max_kv = int(max(m + n for m, n in reqs))
+    k_pool = torch.randn((S, h_kv, d), generator=gen).to(tdt)
+    v_pool = torch.randn((S, h_kv, d), generator=gen).to(tdt)
+    q = torch.randn((T, h_q, d), generator=gen).to(tdt)
+    k_ext = torch.randn((T, h_kv, d), generator=gen).to(tdt)
+    v_ext = torch.randn((T, h_kv, d), generator=gen).to(tdt)
+    need = _lib.attention_workspace_bytes(False, T, h_q, h_kv, d, max_kv)
+    assert need > 0, "the case must take the split path"
+    dev = lambda x: torch.as_tensor(x).cuda()
+    args = [dev(q), dev(k_ext), dev(v_ext), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(prefix), dev(qo)]
+    outs = []
+    for ws in (torch.empty(need, dtype=torch.uint8, device="cuda"), None):
+        o = torch.empty((T, h_q, d), dtype=torch.float32, device="cuda")
+        _lib.extend_attention(*args, o, workspace=ws, max_kv_len=max_kv)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    kf, vf, qf = k_pool.double().numpy(), v_pool.double().numpy(), q.double().numpy()
+    kef, vef = k_ext.double().numpy(), v_ext.double().numpy()
+    got = [o.cpu().numpy() for o in outs]
+    worst = 0.0
+    for r, (m, n) in enumerate(reqs):
+        sl = rtt[rows[r], :m]
+        for i in range(n):
+            t = int(qo[r]) + i
+            K = np.concatenate([kf[sl], kef[qo[r]: t + 1]])
+            V = np.concatenate([vf[sl], vef[qo[r]: t + 1]])
+            ref = attend(qf[t], K, V)
+            for g in got:
+                err = float(np.abs(g[t] - ref).max())
+                worst = max(worst, err)
+                assert err <= TOL[dt], f"request {r} query {i}: max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {T} queries, split and unsplit")
+
+
 # (h_q, h_kv, groups): each group is (requests, extra shared keys past the block prefix).
 # Row blocks hold 64 / (h_q / h_kv) requests, so groups fall inside, across and exactly on
 # block boundaries.
