@@ -87,7 +87,7 @@ struct AttnArgs {
   float* ws_own;              // own-part partials: [batch * h_kv * n_chunk * g][D], then (m, l)
   int32_t n_chunk;            // most own-part key chunks per (request, KV head)
   int32_t own_fused;          // 0: own_kernel + merge_kernel; 1: own_merge_kernel writes O;
-                              // 2: own_tile_kernel + merge_kernel
+                              // 2: own_stream_kernel + merge_kernel
   int32_t own_min;            // fewest own keys per chunk (own_chunks)
   int32_t sh_small;           // 1: shared part with 4-wave workgroups, 2 tiles per round
   int32_t run_cap;            // split decode: most extra shared-part tiles per row block taken
@@ -1063,13 +1063,13 @@ __device__ __forceinline__ int row_shared_len(const AttnArgs& a, const BlockMeta
 // at least a.own_min keys. Returns n_act (0: nothing of its own, or an invalid row) and
 // sets the first own position and the chunk size.
 constexpr int kOwnMin = 32;       // own_kernel / own_merge_kernel
-// own_tile_kernel: chunks of at least 1024 keys, at most 4 per (request, KV head). Measured
+// own_stream_kernel: chunks of at least 1024 keys, at most 4 per (request, KV head) unless
+// more keep each within kStreamCap. Measured (with the tile-round form it replaced)
 // on GQA decode (self-consistency 64/8, multi-turn 32/8) from 128/8 to 1024/4: fewer,
 // longer chunks win (275 -> 225 us, 204 -> 159 us); idle workgroups (chunks past a
 // request's keys) and partials to merge cost more than the parallelism they add.
 constexpr int kOwnTileMin = 1024;
 constexpr int kOwnTileChunks = 4;
-constexpr int kOwnTiles = 2;       // own_tile_kernel: 64-key tiles per round
 __device__ __forceinline__ int own_chunks(const AttnArgs& a, int row, int end, int L, int& first, int& per) {
   first = L;
   per = 0;
@@ -1455,7 +1455,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
     const int rl = (int)(t - rb * a.bm / a.g);  // request t's lane in its block's metadata
     n_own = own_chunks(a, (int)t, row_shared_len(a, block_meta_load(a, rb, lane), lane, rl), first, per);
   }
-  if (a.own_fused == 2 && n_own == 1) return;  // own_tile_kernel merged this row and wrote O
+  if (a.own_fused == 2 && n_own == 1) return;  // own_stream_kernel merged this row and wrote O
   if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
 #pragma unroll
@@ -2059,192 +2059,10 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
   }
 }
 
-// Own part of split decode on MFMA for query-head groups (g = 2..16), bf16, D = 128.
-// own_chunk scores 32 / g keys per batch, each batch a chain of cross-lane reductions and
-// broadcasts, so for g > 1 that work bounds it rather than memory (self-consistency
-// decode, GQA 64/8: 0.56 ms per call for 0.59 GB). Here a workgroup takes one own chunk
-// of (request t, KV head h): the chunk's keys go straight into LDS in rounds of up to
-// kOwnTiles 64-key tiles, as in shared_kernel (64 KB of LDS: two workgroups per CU, whose
-// round trips overlap), and the g query heads of (t, h) are the
-// rows of one 32-row MFMA tile (rows past g are padding). Four waves are four key groups
-// taking the 32-key halves round-robin; they combine split by dims, and the chunk's
-// partial goes to the workspace in own_kernel's layout, for merge_kernel.
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) own_tile_kernel(AttnArgs a) {
-  static_assert(D == 128, "the swizzle assumes 16 chunks per row");
-  constexpr int NW = 4, NKG = 4;
-  constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int RB = D * 2;            // bytes per row
-  constexpr int TB = BN * RB;          // bytes per K (or V) tile
-  constexpr int RPI = 1024 / RB;       // rows per 1 KB global-to-LDS instruction
-  constexpr int NI = BN / RPI;         // instructions per tile
-  constexpr int NKS = D / 16;
-  constexpr int OT = kOwnTiles;                           // tiles per round
-  __shared__ __align__(16) char kv[2 * OT * TB];          // K tiles, then V tiles
-  __shared__ int32_t slot[OT * BN];
-  const uint32_t kv_lds = lds_addr(kv);
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wkey = wave;  // key group
-  const int jrow = lane & 31, half = lane >> 5;
-  const int G = a.g;
-  const int n_rh = a.batch * a.h_kv;
-  const int c = blockIdx.x / n_rh;  // chunk slowest: chunks past every request's keys exit together
-  const int rh = blockIdx.x - c * n_rh;
-  const int t = rh / a.h_kv;
-  const int h = rh - t * a.h_kv;
-
-  // metadata of the request's row block, then Q of this lane's row (query head h*G + jrow
-  // of request t; the B operand of S^T = K Q^T)
-  const int rb0 = t * G / a.bm;
-  const BlockMeta meta = block_meta_load(a, rb0, lane);
-  const bool row_ok = jrow < G;
-  bf16x8 qf[NKS];
-  {
-    const __bf16* qp =
-        reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? jrow : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
-      qf[ks] = row_ok ? v : bf16x8{};
-    }
-  }
-  const int rl = t - rb0 * a.bm / G;
-  const int L = row_shared_len(a, meta, lane, rl);
-  const int row_t = __builtin_amdgcn_readlane(meta.row, rl);
-  const int end = __builtin_amdgcn_readlane(meta.len, rl);
-  int first, per;
-  const int n_act = own_chunks(a, row_t, end, L, first, per);
-  if (c >= n_act) return;  // the same for the whole workgroup
-  const int start = first + c * per;
-  const int stop = min(start + per, end);
-  const int n_tiles = (stop - start + BN - 1) / BN;
-  const int64_t row_bytes = (int64_t)a.h_kv * RB;
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
-  const int32_t* rtt_row = a.rtt + (int64_t)row_t * a.rtt_stride;  // row_t valid: n_act > 0
-
-  // Slot ids: thread i < OT * BN holds position start + tb * BN + i of a round. Each round's
-  // ids are fetched during the previous round (the first before the loop), so a round
-  // starts with its tile loads instead of a slot-id round trip.
-  static_assert(OT * BN <= 64 * NW, "one slot id per thread and round");
-  auto slot_at = [&](int tb) {
-    const int pos = start + tb * BN + tid;
-    return rtt_row[pos < stop ? pos : start];
-  };
-  int sv_cur = tid < OT * BN ? slot_at(0) : 0;
-  // this round's slot ids into LDS, the next round's fetched, then every K and V row of the
-  // round's tiles into LDS
-  auto issue = [&](int tb, int nt) {
-    if (tid < nt * BN) {
-      const int pos = start + tb * BN + tid;
-      const bool in = pos < stop;
-      int sv = sv_cur;
-      if (in && (sv < 0 || sv >= a.num_slots)) {
-        flag_error(RAX_DEVERR_SLOT);
-        sv = -1;
-      }
-      slot[tid] = in ? sv : -1;
-    }
-    // issued before the tile loads: the waits below (in issue order) cover it
-    if (tb + OT < n_tiles && tid < OT * BN) sv_cur = slot_at(tb + OT);
-    __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-#pragma unroll
-      for (int q = wave; q < NI; q += NW) {
-        const int r = q * RPI + lane / CH;
-        const int sv = slot[tt * BN + r];
-        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
-        lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + tt * TB + q * 1024));
-        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (OT + tt) * TB + q * 1024));
-      }
-    }
-  };
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
-
-  for (int tb = 0; tb < n_tiles; tb += OT) {
-    const int nt = min(OT, n_tiles - tb);
-    issue(tb, nt);
-    // each wave issued 2 * NI / NW = 8 loads per tile, in tile order, and they retire in
-    // order: with two tiles, the first is computed while the second may still arrive
-    static_assert(2 * NI / NW == 8 && OT == 2, "wait counts below");
-    const int last_cnt = min(BN, stop - (start + (tb + nt - 1) * BN));
-    for (int part = 0; part < 2; ++part) {
-      const int t0 = part, t1 = min(nt, t0 + 1);  // tile of this part
-      if (t0 >= nt) break;
-      if (part == 0 && nt == 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 1 may fly
-      else __builtin_amdgcn_s_waitcnt(0);
-      asm volatile("s_barrier" ::: "memory");
-      // rows past the chunk read slot 0: zero them (their scores are masked; zeros keep P.V finite)
-      if (last_cnt < BN && nt - 1 < t1) {
-        for (int i = tid; i < (BN - last_cnt) * CH; i += 64 * NW) {
-          const int off = (nt - 1) * TB + (last_cnt + i / CH) * RB + (i % CH) * 16;
-          *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(kv + OT * TB + off) = u32x4{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
-      }
-      for (int j = 2 * t0 + wkey; j < 2 * t1; j += NKG) {
-        const int tt = j >> 1, sub = j & 1;
-        const int cnt = min(BN, stop - (start + (tb + tt) * BN));
-        const char* kt = kv + tt * TB;
-        const char* vt = kv + (OT + tt) * TB;
-        f32x16 sc = f32x16{};
-        const int kr = sub * 32 + jrow;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
-        // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float v = row_ok && key < cnt ? sc[r] : kNegInf;
-          sc[r] = v;
-          mx = fmaxf(mx, v);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-        if (__any(mx > m_run + kLazy)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-          m_run = m_new;
-        }
-        const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
-          sc[r] = pv;
-          psum += pv;
-        }
-        psum += __shfl_xor(psum, 32);
-        l_run += psum;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // the next round overwrites the tiles
-  }
-
-  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wkey, lane, jrow, half, row_ok, t, h, rh, c, n_act, n_rh);
-}
-
 // Own part of split decode with query-head groups (bf16, D = 128), as one continuous
-// stream per workgroup. A workgroup takes one own chunk of (request t, KV head h), at
+// stream per workgroup, on MFMA: the VALU own part (own_chunk) scores 32 / g keys per
+// batch through chains of cross-lane reductions, which for g > 1 bound it rather than
+// memory (0.56 ms per GQA 64/8 self-consistency call for 0.59 GB). A workgroup takes one own chunk of (request t, KV head h), at
 // most kStreamCap keys. Its slot ids go to LDS first (one round of loads); then the
 // chunk's keys stream through a ring of S stages of 32 keys (8 KB of K and 8 KB of V
 // each) filled straight from global memory: while stage i is computed, the loads of the
@@ -2252,17 +2070,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) o
 // round of tiles at a time. One barrier per stage. The four waves are four key groups:
 // wave w computes stages i = w (mod 4) (S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMA,
 // the g query heads as rows of one 32-row tile, rows past g masked), and the groups
-// combine at the end as in own_tile_kernel. Keys past the chunk in its last stage read
+// combine at the end (own_groups_epilogue). Keys past the chunk in its last stage read
 // the chunk's first slot (a key it attends, so finite) and are masked.
 constexpr int kStreamCap = 2048;  // most keys per own chunk of own_stream_kernel
 constexpr int kStreamTK = 32;     // keys per stage
-#ifndef RAX_STREAM_STAGES
-#define RAX_STREAM_STAGES 4
-#endif
-#ifndef RAX_STREAM_NT
-#define RAX_STREAM_NT 1
-#endif
-constexpr int kStreamStages = RAX_STREAM_STAGES;
+// Four stages (72 KB of LDS, two workgroups per CU) measured as fast as three and
+// faster than six or nine (one workgroup per CU: 360 against 241 us per multi-turn call).
+constexpr int kStreamStages = 4;
 
 template <int D, int S>
 __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
@@ -2355,13 +2169,9 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
       const int q = wave + u * NW;
       const int r = q * RPI + (lane >> 4);
       const int64_t off = (int64_t)slot[j * TK + r] * row_bytes;
-#if RAX_STREAM_NT
+      // read once per call: non-temporal (multi-turn decode 300 -> 241 us per call)
       lds_load16_nt(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
       lds_load16_nt(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + TB + q * 1024));
-#else
-      lds_load16(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
-      lds_load16(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + TB + q * 1024));
-#endif
     }
   };
 
@@ -2619,7 +2429,7 @@ struct DecodeLayout {
   int64_t sh_acc, sh_ml, own_acc, own_ml, total;
   int32_t nsplit, n_rb, n_chunk, bm;
   bool split_decode;
-  int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_tile_kernel + merge_kernel
+  int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_stream_kernel + merge_kernel
   int32_t own_min;   // fewest keys per own chunk
   int32_t sh_small;  // shared part: 4-wave workgroups, 2 tiles per round (two per CU)
   int32_t run_cap;   // most extra shared-part tiles per row block for deeper runs
@@ -2912,3 +2722,4 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
   return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap);
 }
+
