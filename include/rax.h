@@ -359,6 +359,23 @@ rax_status rax_decode_attention(const void* q, const void* k_pool, const void* v
                                 int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
                                 void* o, rax_dtype o_dt, void* workspace, size_t ws_bytes, void* stream);
 
+/* rax_decode_attention that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving loops). Its
+ * split-K partials live in a 64 MiB device array of the library (each GPU it runs on
+ * holds one until the process ends), whose device address is taken on the first call
+ * on each device: make the device of the pools and stream current before calling. Calls
+ * on one GPU share that array, so calls that overlap on one GPU (other streams, other
+ * host threads) race; calls on one stream do not. Results as rax_decode_attention's.
+ * RAX_EINVAL: bad sizes or pointers; RAX_ENOMEM: the call's layout needs more than
+ * 64 MiB (rax_attention_workspace_bytes(1, ...) > 64 MiB; nothing runs); RAX_EDEVICE:
+ * no device address for the array. */
+rax_status rax_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool, int64_t num_slots,
+                                        const int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                        const int32_t* req_pool_idx, const int32_t* seq_len,
+                                        const int32_t* shared_len, int32_t batch, int32_t max_seq_len,
+                                        int32_t h_q, int32_t h_kv, int32_t d, float sm_scale, rax_dtype dt,
+                                        void* o, rax_dtype o_dt, void* stream);
+
 /* rax_decode_attention with host copies of seq_len and shared_len (seq_len_host,
  * shared_len_host: [batch] each, as the device arrays): the launches are sized from them
  * as rax_decode_step sizes its attention (the tiles each row block's shared part holds,

@@ -85,6 +85,8 @@ _SIGS = {
                                     _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_decode_attention": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "rax_decode_attention_noalloc": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp]),
     "rax_decode_attention_hinted": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
                                            _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp, _c_i32p,
                                            _c_i32p, ctypes.POINTER(_sz)]),
@@ -550,6 +552,25 @@ def decode_attention(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max
         req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
         q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
         _stream(stream, q)), "rax_decode_attention")
+
+
+def decode_attention_noalloc(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max_seq_len: int, o,
+                             shared_len=None, sm_scale=None, stream=None) -> None:
+    """rax_decode_attention_noalloc: decode_attention with the library's static workspace."""
+    _need(q.dim() == 3 and q.shape[2] == k_pool.shape[2] and k_pool.shape == v_pool.shape, "shapes")
+    _need(o.shape == q.shape and o.is_contiguous() and o.is_cuda, "o like q")
+    _need(q.dtype == k_pool.dtype == v_pool.dtype, "input dtypes agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (q, k_pool, v_pool)), "contiguous cuda")
+    _cuda_i32(req_to_token, req_pool_idx, seq_len, shared_len)
+    b = q.shape[0]
+    _need(req_pool_idx.numel() == b and seq_len.numel() == b, "metadata shapes")
+    d = q.shape[2]
+    scale = float(sm_scale if sm_scale is not None else d ** -0.5)
+    _check(lib().rax_decode_attention_noalloc(
+        _dev(q), _dev(k_pool), _dev(v_pool), k_pool.shape[0], _dev(req_to_token), req_to_token.shape[1],
+        req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
+        q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _stream(stream, q)),
+        "rax_decode_attention_noalloc")
 
 
 def decode_attention_hinted(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_len, max_seq_len: int, o,

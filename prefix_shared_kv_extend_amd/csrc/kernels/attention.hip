@@ -43,6 +43,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include <type_traits>
 
@@ -2723,3 +2724,48 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap);
 }
 
+// ---- decode attention that allocates nothing: for callers that cannot allocate device
+// memory (code under graph capture, tight serving loops). Its workspace is this file-scope
+// device array, which every GPU the library runs on holds until the process ends; calls
+// on one GPU share it, so calls that overlap on one GPU race. Nothing in it has to start
+// at zero (every kernel writes its partials before the merge reads them).
+constexpr size_t kScratchBytes = 64ull << 20;  // covers 256 requests x 64 query heads
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, taken once per device with that device
+// current (the name itself is a host-side stand-in, never passed to a kernel).
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+static rax_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RAX_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RAX_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RAX_OK;
+}
+
+extern "C" rax_status rax_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                                   int64_t num_slots, const int32_t* req_to_token,
+                                                   int64_t rtt_stride, int64_t rtt_rows,
+                                                   const int32_t* req_pool_idx, const int32_t* seq_len,
+                                                   const int32_t* shared_len, int32_t batch, int32_t max_seq_len,
+                                                   int32_t h_q, int32_t h_kv, int32_t d, float sm_scale,
+                                                   rax_dtype dt, void* o, rax_dtype o_dt, void* stream) {
+  if (!common_ok(h_q, h_kv, d, dt, o_dt) || batch < 0 || max_seq_len < 0) return RAX_EINVAL;
+  if (batch == 0) return RAX_OK;
+  const size_t need = raxk::decode_workspace_bytes(batch, h_q, h_kv, d, max_seq_len, DecodeHint{});
+  if (need > kScratchBytes) return RAX_ENOMEM;  // beyond the static workspace
+  void* ws = nullptr;
+  if (need > 0) {
+    const rax_status rc = scratch_on_current_device(&ws);
+    if (rc != RAX_OK) return rc;
+  }
+  return raxk::decode_attention_impl(q, k_pool, v_pool, num_slots, req_to_token, rtt_stride, rtt_rows, req_pool_idx,
+                                     seq_len, shared_len, batch, max_seq_len, h_q, h_kv, d, sm_scale, dt, o, o_dt, ws,
+                                     need > 0 ? kScratchBytes : 0, stream, nullptr);
+}
