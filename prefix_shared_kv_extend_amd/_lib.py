@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librax.so")
+# RAX_LIB_PATH selects another build of the same library (the sanitized host build of
+# prefix_shared_kv_extend_amd.sanitize_check)
+LIB_PATH = os.environ.get("RAX_LIB_PATH") or os.path.join(_HERE, "librax.so")
 
 OK, EINVAL, ENOMEM, ESTATE, EDEVICE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1

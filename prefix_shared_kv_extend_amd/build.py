@@ -33,13 +33,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librax)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+SANITIZED_LIB = os.path.join(PKG, "librax_san.so")
+# host code only: AddressSanitizer and UndefinedBehaviorSanitizer on the tree, the API and
+# the launch code; the device code is built as usual
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = SANITIZED_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O1" if sanitize else "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-mllvm", "-amdgpu-kernarg-preload-count=14",
            "-Wall", "-Wno-unused-function",
+           *(SANITIZE_FLAGS if sanitize else []),
            *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,9 +59,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"librax build failed:\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

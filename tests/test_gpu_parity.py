@@ -291,20 +291,27 @@ def test_bf16_output_dtype():
 
 # ------------------------------------------------------------- full-size configs
 def _pick_sampled(job, rng, per_step=3):
+    """Extend: per_step random requests of every extend batch plus its first and last, at
+    their last position and every 97th. Decode: per_step random requests at every 8th
+    step and the last, and per_step fixed requests (the first decode batch's first, middle
+    and last) at every decode step."""
     ext = {}
     dec = {}
+    fixed = set()
     for si, st in enumerate(job.steps):
         if st.extend:
             ext[si] = set(rng.choice(st.extend, size=min(per_step, len(st.extend)), replace=False).tolist())
             ext[si] |= {st.extend[0], st.extend[-1]}
         if st.decode:
             dec[si] = set(rng.choice(st.decode, size=min(per_step, len(st.decode)), replace=False).tolist())
+            if not fixed:
+                fixed = {st.decode[0], st.decode[len(st.decode) // 2], st.decode[-1]}
 
     def pick(kind, si, rid, p):
         if kind == "extend":
             r = job.requests[rid]
             return rid in ext.get(si, ()) and (p == r.n - 1 or p % 97 == 0)
-        return rid in dec.get(si, ()) and (si % 8 == 0 or si == len(job.steps) - 1)
+        return rid in fixed or (rid in dec.get(si, ()) and (si % 8 == 0 or si == len(job.steps) - 1))
     return pick
 
 
@@ -319,13 +326,22 @@ def test_full_config_sampled(index):
     say(f"  checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")
 
 
-def test_full_multi_turn_sampled():
-    job = configs.make(4)
-    say(f"config 4 (multi_turn) full size: requests={len(job.requests)} steps={len(job.steps)} "
-        f"pool={job.num_slots}")
+_MT = {}
+
+
+def _multi_turn_plan(job):
+    """Sampled outputs of the full multi-turn trace: one extend and one decode request on
+    every 50th step and on every 50th step with an eviction, split in three parts; and
+    three fixed long-context requests (100..300 generated tokens each) at every decode
+    step and the last position of their extend."""
+    from prefix_shared_kv_extend_amd.driver import tree_replay
+    log, _, tree, _ = tree_replay(job)
+    tree.close()
+    ev_steps = sorted({e[1] for e in log if e[0] == "evict"})
+    steps = sorted(set(range(0, len(job.steps), 50)) | set(ev_steps[::50]))
     rng = np.random.default_rng(4)
     chosen = {}
-    for si in range(0, len(job.steps), 300):
+    for si in steps:
         st = job.steps[si]
         c = []
         if st.extend:
@@ -333,18 +349,71 @@ def test_full_multi_turn_sampled():
         if st.decode:
             c.append(("decode", int(rng.choice(st.decode))))
         chosen[si] = c
+    fixed = [r.rid for r in job.requests if 100 <= len(r.output) <= 300 and r.n >= 1000][:3]
+    return steps, chosen, fixed, ev_steps
+
+
+def _multi_turn_run():
+    """One GPU run of the full multi-turn trace, shared by the tests below (cached)."""
+    if "got" in _MT:
+        return _MT
+    job = configs.make(4)
+    steps, chosen, fixed, ev_steps = _multi_turn_plan(job)
+    say(f"config 4 (multi_turn) full size: requests={len(job.requests)} steps={len(job.steps)} "
+        f"pool={job.num_slots}; {len(steps)} sampled steps ({len(ev_steps)} steps evict), fixed requests {fixed}")
+    fixed_set = set(fixed)
 
     def pick(kind, si, rid, p):
+        if rid in fixed_set:
+            return kind == "decode" or p == job.requests[rid].n - 1
         if (kind, rid) not in chosen.get(si, ()):
             return False
         return kind == "decode" or p == job.requests[rid].n - 1 or p % 211 == 0
 
-    runner, got = _collect(job, pick=pick, progress=500)
+    from prefix_shared_kv_extend_amd import _lib
+    runner, got = _collect(job, pick=pick, progress=1000)
+    _MT.update(job=job, steps=steps, chosen=chosen, fixed=fixed, got=got, log=runner.log,
+               rows=runner.final_rows, dump=runner.rt.tree.dump(), errors=_lib.device_errors())
+    del runner
+    torch.cuda.empty_cache()
+    return _MT
+
+
+def test_full_multi_turn_host_log():
+    mt = _multi_turn_run()
     say("  GPU run done; replaying the trace in the oracle")
-    _check_host(job, runner)
-    say("  host log identical; checking sampled outputs")
+    ref = run_trace(mt["job"])
+    assert mt["errors"] == 0
+    assert len(mt["log"]) == len(ref["log"])
+    for a, b in zip(mt["log"], ref["log"]):
+        assert a == b
+    assert mt["rows"] == ref["rows"] and mt["dump"] == ref["dump"]
+    say(f"  host log identical ({len(ref['log'])} events, {sum(1 for e in ref['log'] if e[0] == 'evict')} evictions)")
+
+
+@pytest.mark.parametrize("part", range(3))
+def test_full_multi_turn_sampled(part):
+    mt = _multi_turn_run()
+    job = mt["job"]
+    mine = set(mt["steps"][part::3])
+    keep = {(k, r) for si in mine for k, r in mt["chosen"].get(si, ())}
+    # the outputs the run kept for the requests chosen at this part's steps
+    rids = {r for _, r in keep} - set(mt["fixed"])
+    got = {(rid, p): o for (rid, p), o in mt["got"].items() if rid in rids}
     worst = _check_outputs(job, got, TOL[job.dtype])
-    say(f"  checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")
+    say(f"  part {part}: {len(mine)} steps, checked {len(got)} sampled outputs, worst max-abs {worst:.3g}")
+    assert got
+
+
+def test_full_multi_turn_fixed_requests_every_step():
+    mt = _multi_turn_run()
+    job = mt["job"]
+    got = {(rid, p): o for (rid, p), o in mt["got"].items() if rid in mt["fixed"]}
+    for rid in mt["fixed"]:
+        r = job.requests[rid]
+        assert sum(1 for (x, p) in got if x == rid and p >= r.n) == len(r.output)
+    worst = _check_outputs(job, got, TOL[job.dtype])
+    say(f"  fixed requests {mt['fixed']}: {len(got)} outputs (every decode step), worst max-abs {worst:.3g}")
 
 
 # ------------------------------------------------------------- QKV projection (fused write-back)
