@@ -24,7 +24,9 @@ Passes over the same job (--passes):
            L2 and the 256 MB MALL hold nothing of it, and a HIP event pair around the call
            on the stream it runs on: per-call kernel times, the per-kind rates and the
            roofline of the dominant kernel (the headline figures);
-  natural  one job with the event pairs and no scratch writes (calls as they run).
+  natural  one job with the event pairs and no scratch writes (calls as they run);
+  host     one job synchronised after every trace step: the host time of each runtime
+           call with no launch waiting for the GPU (the host work alone, by phase).
 Beside the headline, each of the other shared-prefix configurations (few-shot, two-level
 tree, self-consistency fork) runs its whole trace and times every attention call over
 --reps cold repetitions (scratch write before each) and --reps warm ones (back to back):
@@ -79,7 +81,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5, help="timed jobs of the wall pass")
     ap.add_argument("--warmup", type=int, default=1, help="untimed jobs before the wall pass")
     ap.add_argument("--reps", type=int, default=20, help="cold and warm repetitions per call (side sections)")
-    ap.add_argument("--passes", default="wall,cold,natural", help="comma list of wall, cold, natural")
+    ap.add_argument("--passes", default="wall,cold,natural,host", help="comma list of wall, cold, natural, host")
     ap.add_argument("--flush-mib", type=int, default=512, help="scratch written before each cold call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
@@ -189,30 +191,53 @@ class Inputs:
         torch.cuda.synchronize()
 
 
-def run_job(runner, inp, pre=None, timed=False, after_decode=None):
+PHASES = ("begin_extend", "run_extend", "end_extend", "begin_decode", "run_decode", "finish")
+
+
+def run_job(runner, inp, pre=None, timed=False, after_decode=None, phases=None):
     """One job pass through the runtime. pre: called right before each attention call is
-    issued; timed: a HIP event pair around every attention call (rt.timers)."""
+    issued; timed: a HIP event pair around every attention call (rt.timers); phases: a dict
+    that accumulates the host time of each runtime call, with the device synchronised after
+    every trace step (so no launch waits for the GPU and the times are host work alone)."""
+    import torch
     rt, job = runner.rt, runner.job
     rt.timers = {} if timed else None
     rt.pre_attention = pre
+    clock = time.perf_counter
+
+    def tick(name, t0):
+        t1 = clock()
+        if phases is not None:
+            phases[name] = phases.get(name, 0.0) + (t1 - t0)
+        return t1
+
     i = 0
     for si, st in enumerate(job.steps):
         rt.step = si
+        t = clock()
         if st.extend:
             eb = rt.begin_extend([(rid, job.requests[rid].prompt) for rid in st.extend])
+            t = tick("begin_extend", t)
             q, k, v = inp.qkv[i]
             rt.run_extend(eb, q, k, v, inp.o[: q.shape[0]])
+            t = tick("run_extend", t)
             rt.end_extend(eb)
+            t = tick("end_extend", t)
             i += 1
         if st.decode:
             db = rt.begin_decode(st.decode)
+            t = tick("begin_decode", t)
             q, k, v = inp.qkv[i]
             rt.run_decode(db, q, k, v, inp.o[: q.shape[0]])
+            t = tick("run_decode", t)
             if after_decode is not None:
                 after_decode(i, db)
             i += 1
         if st.finish:
             rt.finish_batch([(rid, runner.full[rid][: rt.seq_len(rid)]) for rid in st.finish])
+            t = tick("finish", t)
+        if phases is not None:
+            torch.cuda.synchronize()
     rt.tree.evict_lru(rt.num_slots)             # the cache yields everything: next job starts empty
     timers, rt.timers, rt.pre_attention = rt.timers, None, None
     return timers
@@ -256,6 +281,9 @@ def headline(args, dev):
     n_ext = sum(len(p) for _, k, p in calls if k == "extend")
     n_dec = sum(len(p) for _, k, p in calls if k == "decode")
     passes = set(args.passes.split(","))
+    unknown = passes - {"wall", "cold", "natural", "host"}
+    if unknown:
+        raise SystemExit(f"bench.py: unknown passes {sorted(unknown)}")
     out = {"config": {"workload": DESCR[HEADLINE], "extend_tokens_per_step": n_ext,
                       "decode_tokens_per_step": n_dec, "prompt_tokens_per_step": sum(r.n for r in job.requests),
                       "extend_calls_per_step": sum(1 for c in calls if c[1] == "extend"),
@@ -302,6 +330,12 @@ def headline(args, dev):
         res = per_kind(job, inp, timers, dec_bytes)
         out[name] = {k: summarize_kind(k, *res[k], n_ext if k == "extend" else n_dec) for k in res}
         del flush
+    if "host" in passes:
+        # host work alone: every trace step synchronised, so no launch waits for the GPU
+        ph = {}
+        run_job(runner, inp, phases=ph)
+        torch.cuda.synchronize()
+        out["host"] = {"ms_per_step": sum(ph.values()) * 1e3, "phases_ms": {k: ph.get(k, 0.0) * 1e3 for k in PHASES}}
     from prefix_shared_kv_extend_amd import _lib
     assert _lib.device_errors() == 0
     out["_job"] = job
@@ -757,10 +791,14 @@ def main():
         out["roofline"] = roofline_of(h["cold"], args.traffic)
     if "wall" in h:
         # the runtime never synchronises inside a job, so the tree work of one call overlaps
-        # the kernels of the previous ones; the GPU waits on the host when issuing a job takes
-        # about as long as the job
-        ov = {"host_issue_ms_per_step": h["wall"]["host_issue_ms"], "wall_ms_per_step": h["wall"]["ms_per_step"],
-              "host_bound": h["wall"]["host_issue_ms"] > 0.97 * h["wall"]["ms_per_step"]}
+        # the kernels of the previous ones. host_issue_ms includes time a launch waits for a
+        # full GPU queue; the host pass gives the host work alone (each step synchronised).
+        # The job is host-bound when that host work takes about as long as the job.
+        ov = {"host_issue_ms_per_step": h["wall"]["host_issue_ms"], "wall_ms_per_step": h["wall"]["ms_per_step"]}
+        if "host" in h:
+            ov["host_work_ms_per_step"] = h["host"]["ms_per_step"]
+            ov["host_phases_ms"] = h["host"]["phases_ms"]
+            ov["host_bound"] = h["host"]["ms_per_step"] > 0.97 * h["wall"]["ms_per_step"]
         if "natural" in h:
             ov["attention_kernel_ms_per_step"] = (h["natural"]["extend"]["us_per_step"]
                                                   + h["natural"]["decode"]["us_per_step"]) * 1e-3

@@ -493,8 +493,9 @@ def test_qkv_project_errors_and_flagged_slots():
 def test_decode_step_folded_append_equals_separate_calls():
     """rax_decode_step carries the append in the first attention kernel (bf16, D = 128): the
     slots, rows, lengths, pools and outputs equal those of rax_decode_append followed by
-    rax_decode_attention on an identical runtime, bit for bit, over several steps (70
-    requests, GQA 16/4, five row blocks)."""
+    rax_decode_attention_hinted (the same layout) on an identical runtime, bit for bit, over
+    several steps (70 requests, GQA 16/4, five row blocks); plain rax_decode_attention, laid
+    out from the longest sequence, agrees within the bf16 tolerance."""
     from prefix_shared_kv_extend_amd import _lib
     from prefix_shared_kv_extend_amd.runtime import RadixRuntime
     say("decode step with the append folded in vs separate append + attention (bf16, g = 4)")
@@ -529,12 +530,21 @@ def test_decode_step_folded_append_equals_separate_calls():
                                        rb.k_pool, rb.v_pool)
         rb.rows[ds.req_rows, ds.lens - 1] = new
         mx = int(ds.lens.max())
-        ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, mx), dtype=torch.uint8, device="cuda")
         ob = torch.empty_like(oa)
-        _lib.decode_attention(qd, rb.k_pool, rb.v_pool, rb.rtt, ds.inv["req_pool_idx"], ds.inv["seq_len"], mx, ob,
-                              workspace=ws, shared_len=ds.inv["shared_len"])
+        # the same layout as the decode step: sized from host copies of the lengths and hints
+        hinted = lambda w: _lib.decode_attention_hinted(qd, rb.k_pool, rb.v_pool, rb.rtt, ds.inv["req_pool_idx"],
+                                                        ds.inv["seq_len"], mx, ob, ds.lens, ds.hints, workspace=w,
+                                                        shared_len=ds.inv["shared_len"])
+        hinted(torch.empty(hinted(None), dtype=torch.uint8, device="cuda"))
         torch.cuda.synchronize()
         assert torch.equal(oa, ob), f"step {step}"
+        # and the plain call (layout from the longest sequence) within the bf16 tolerance
+        oc = torch.empty_like(oa)
+        ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, mx), dtype=torch.uint8, device="cuda")
+        _lib.decode_attention(qd, rb.k_pool, rb.v_pool, rb.rtt, ds.inv["req_pool_idx"], ds.inv["seq_len"], mx, oc,
+                              workspace=ws, shared_len=ds.inv["shared_len"])
+        torch.cuda.synchronize()
+        assert float((oa.float() - oc.float()).abs().max()) <= TOL["bf16"], f"step {step}"
         assert np.array_equal(ra._dec_cache.lens, ds.lens)
         assert torch.equal(ra._dec_cache.inv["seq_len"], ds.inv["seq_len"])
     assert torch.equal(ra.rtt, rb.rtt) and np.array_equal(ra.rows, rb.rows)
@@ -587,19 +597,26 @@ def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
     ob = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
     _lib.decode_attention(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(lens), int(lens.max()), ob,
                           workspace=ws, shared_len=dev(hints))
+    # the same call laid out from host copies (the own part as a work queue of waves)
+    oh = torch.empty_like(ob)
+    hinted = lambda w: _lib.decode_attention_hinted(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows),
+                                                    dev(lens), int(lens.max()), oh, lens, hints, workspace=w,
+                                                    shared_len=dev(hints))
+    hinted(torch.empty(hinted(None), dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert _lib.device_errors() == 0
-    got = ob.float().cpu().numpy()
+    outs = (ob.float().cpu().numpy(), oh.float().cpu().numpy())
     kf, vf, qf = k_pool.float().numpy(), v_pool.float().numpy(), q.float().numpy()
     worst = 0.0
     check = range(B) if B <= 64 else sorted(set(np.linspace(0, B - 1, 64).astype(int).tolist()))
     for i in check:
         sl = rtt[rows[i], : lens[i]]
         ref = attend(qf[i], kf[sl], vf[sl])
-        err = float(np.abs(got[i] - ref).max())
-        worst = max(worst, err)
-        assert err <= TOL["bf16"], f"request {i} (own {own[i]}): max abs err {err:.3g}"
-    say(f"  worst max-abs {worst:.3g} over {len(check)} requests")
+        for got in outs:
+            err = float(np.abs(got[i] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], f"request {i} (own {own[i]}): max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {len(check)} requests, plain and hinted layouts")
 
 
 @pytest.mark.parametrize("d,B", [(64, 150), (128, 131)])
