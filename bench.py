@@ -66,13 +66,10 @@ DESCR = {
        "prompt, pool = 60% of distinct tokens (878,695 slots, LRU eviction), 6040 mixed extend + decode "
        "steps (<= 256 running); GQA 32/8 x 128, bf16",
 }
-# kernels of one launch of each attention entry point (substrings of their names) and the
-# kernel every launch runs exactly once (its dispatch count is the number of launches)
-ENTRY_KERNELS = {
-    "decode": {"kernels": ("shared_kernel", "own_merge_kernel", "own_tile_kernel", "own_kernel", "merge_kernel"),
-               "anchor": "shared_kernel"},
-    "extend": {"kernels": ("attn_kernelIDF16bLi128ELb0E",), "anchor": "attn_kernelIDF16bLi128ELb0E"},
-}
+# kernels that start a launch of each attention entry point (substrings of their names); the
+# kernels after one (own parts, merges) belong to it, up to the next launch's first kernel
+ENTRY_FIRST = {"decode": "shared_kernel", "extend": "attn_kernelIDF16bLi128ELb0E"}
+ENTRY_REST = ("own_", "merge_kernel")
 
 
 def parse():
@@ -96,6 +93,8 @@ def parse():
     ap.add_argument("--summarize-trace", default=None, metavar="CSV",
                     help="print a markdown summary of a rocprofv3 kernel trace (per kernel; GPU idle between "
                          "kernels over the window of the hot path's kernels) and exit")
+    ap.add_argument("--summarize-counters", default=None, nargs="+", metavar="DIR",
+                    help="print a markdown summary of rocprofv3 counter runs (one directory per pass) and exit")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain copy kernel of known size (for counter scaling) and exit")
     return ap.parse_args()
@@ -627,43 +626,63 @@ def _sha256(path):
 
 
 def _counter_rows(csv_path, counter):
+    """(dispatch id, kernel name, value) of one counter, in dispatch order."""
     import csv
+    out = []
     with open(csv_path) as f:
-        return [(x["Kernel_Name"], float(x["Counter_Value"])) for x in csv.DictReader(f)
-                if x["Counter_Name"] == counter]
+        for x in csv.DictReader(f):
+            if x["Counter_Name"] == counter:
+                did = int(x.get("Dispatch_Id") or x.get("Correlation_Id") or len(out))
+                out.append((did, x["Kernel_Name"], float(x["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def _per_launch(rows):
+    """Sum a counter over each attention launch: a launch is its entry point's first kernel
+    and the own-part and merge kernels that follow it. Returns {entry: [sums]} and, per
+    entry, {kernel: total}."""
+    sums, per_kernel, cur = {}, {}, None
+    for _, k, v in rows:
+        entry = next((e for e, first in ENTRY_FIRST.items() if first in k), None)
+        if entry is not None:
+            cur = entry
+            sums.setdefault(cur, []).append(0.0)
+        elif cur is None or not any(r in k for r in ENTRY_REST):
+            cur = None  # another kernel: the launch ended
+            continue
+        sums[cur][-1] += v
+        per_kernel.setdefault(cur, {})
+        per_kernel[cur][k] = per_kernel[cur].get(k, 0.0) + v
+    return sums, per_kernel
 
 
 def write_traffic(run_dir):
     """Condense rocprofv3 FETCH_SIZE / WRITE_SIZE runs (of this script with --passes cold, and
     of --copy-calib) into profiles/traffic.json: HBM bytes per launch of each attention entry
-    point = the counters of all its kernels' dispatches / the number of launches (dispatches
-    of its anchor kernel), each counter scaled by what it reads for the plain copy of known
-    size."""
+    point = its kernels' counters summed per launch (dispatch order), averaged over launches,
+    each counter scaled by what it reads for the plain copy of known size."""
     fetch = _counter_rows(os.path.join(run_dir, "pmc_FETCH_SIZE", "bench_counter_collection.csv"), "FETCH_SIZE")
     write = _counter_rows(os.path.join(run_dir, "pmc_WRITE_SIZE", "bench_counter_collection.csv"), "WRITE_SIZE")
     cf = _counter_rows(os.path.join(run_dir, "copy_FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
     cw = _counter_rows(os.path.join(run_dir, "copy_WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
-    copy_f = np.mean([v for k, v in cf if "kv_scatter_kernel" in k])
-    copy_w = np.mean([v for k, v in cw if "kv_scatter_kernel" in k])
+    copy_f = np.mean([v for _, k, v in cf if "kv_scatter_kernel" in k])
+    copy_w = np.mean([v for _, k, v in cw if "kv_scatter_kernel" in k])
     f_scale = COPY_READ_BYTES / (copy_f * 1024.0)
     w_scale = COPY_WRITE_BYTES / (copy_w * 1024.0)
+    fs, fk = _per_launch(fetch)
+    ws, wk = _per_launch(write)
     out = {"source_sha256": _sha256(KERNEL_SOURCE), "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "entries": {}}
-    for entry, spec in ENTRY_KERNELS.items():
-        n = sum(1 for k, _ in fetch if spec["anchor"] in k)
-        if not n:
+    for entry in ENTRY_FIRST:
+        if not fs.get(entry) or not ws.get(entry):
             continue
-        per = {}
-        for key in spec["kernels"]:
-            kf = [v for k, v in fetch if key in k and not any(o != key and o in k and len(o) > len(key)
-                                                             for o in spec["kernels"])]
-            kw = [v for k, v in write if key in k and not any(o != key and o in k and len(o) > len(key)
-                                                             for o in spec["kernels"])]
-            if kf:
-                per[key] = {"dispatches": len(kf), "fetch_kib_total": sum(kf), "write_kib_total": sum(kw),
-                            "bytes_per_launch": (sum(kf) * f_scale + sum(kw) * w_scale) * 1024 / n}
-        out["entries"][entry] = {"launches": n, "kernels": per,
-                                 "bytes_per_launch": sum(p["bytes_per_launch"] for p in per.values())}
+        n = len(fs[entry])
+        per = {k: {"fetch_kib_per_launch": fk[entry].get(k, 0.0) / n, "write_kib_per_launch": wk[entry].get(k, 0.0) / n}
+               for k in set(fk[entry]) | set(wk[entry].keys())}
+        out["entries"][entry] = {
+            "launches": n, "kernels": per,
+            "bytes_per_launch": (sum(fs[entry]) * f_scale + sum(ws[entry]) * w_scale) * 1024 / n}
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -679,6 +698,43 @@ def load_traffic(entry, path):
     if t.get("source_sha256") != _sha256(KERNEL_SOURCE):
         return None
     return t.get("entries", {}).get(entry, {}).get("bytes_per_launch")
+
+
+def summarize_counters(run_dirs):
+    """Markdown summary of rocprofv3 counter runs (one directory per pass): per kernel of the
+    hot path, dispatches and the mean per dispatch of every counter, plus the MFMA
+    utilisation (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs) and the
+    fraction of wave cycles spent waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) where the pass
+    holds those counters. MOPS_BF16 counts 512 flops per unit."""
+    import csv
+    import glob
+    acc = {}
+    for d in run_dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(f) as fh:
+                for x in csv.DictReader(fh):
+                    k = x["Kernel_Name"]
+                    if not any(h in k for h in HOT):
+                        continue
+                    per = acc.setdefault(k, {})
+                    per.setdefault(x["Counter_Name"], []).append(float(x["Counter_Value"]))
+    for k, per in sorted(acc.items()):
+        n = max(len(v) for v in per.values())
+        print(f"\n`{k[:120]}` ({n} dispatches)\n")
+        print("| counter | mean per dispatch |\n|---|---|")
+        mean = {c: sum(v) / len(v) for c, v in per.items()}
+        for c in sorted(mean):
+            print(f"| {c} | {mean[c]:.6g} |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; the busy cycles over all 1024 SIMDs
+            print(f"| MFMA utilisation (busy / (GUI_ACTIVE / 8 XCDs x 1024 SIMDs)) | "
+                  f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] / 8 * 1024):.3f} |")
+        if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+            print(f"| waves waiting (WAIT_INST_ANY / WAVE_CYCLES) | {mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:.3f} |")
+        if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean and mean["SQ_INSTS_MFMA"]:
+            print(f"| VALU instructions per MFMA | {mean['SQ_INSTS_VALU'] / mean['SQ_INSTS_MFMA']:.2f} |")
+        if "SQ_INSTS_SALU" in mean and "SQ_INSTS_MFMA" in mean and mean["SQ_INSTS_MFMA"]:
+            print(f"| SALU instructions per MFMA | {mean['SQ_INSTS_SALU'] / mean['SQ_INSTS_MFMA']:.2f} |")
 
 
 HOT = ("shared_kernel", "own_", "merge_kernel", "attn_kernel", "kv_scatter_kernel", "rtt_write_kernel",
@@ -734,6 +790,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

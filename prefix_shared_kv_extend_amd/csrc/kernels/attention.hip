@@ -859,6 +859,408 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   }
 }
 
+// ---- extend, bf16, D = 128: the block layout, tile list, masks and softmax of
+// attn_kernel's extend form (8 waves of one 32-row tile, 256 rows per block) with a lean
+// tile loop. Counters on the few-shot calls showed attn_kernel issuing 10.5 VALU and 8.6
+// SALU instructions per MFMA (tile descriptors found by binary search per tile, slot ids
+// fetched and checked per tile, mask code on every tile), so the MFMA pipe was busy 16% of
+// the time. Here, per segment of up to kExtSeg tiles, the block first builds a table of its
+// tiles (kind, key count, source) and stages the source row of every key (pool slot, or
+// k_ext row for suffix tiles; past a tile's keys, its first key's row) in LDS, in one
+// round of loads. The tile loop then only waits, issues the K/V rows of the tile kExtPD
+// ahead straight into LDS (swizzled as above), and computes; full shared-prefix tiles take
+// a path without masks. A slot id outside the pool is flagged and read as slot 0.
+constexpr int kExtSeg = 128;
+constexpr int kExtBuf = 3;  // K/V buffers: kExtBuf - 1 tiles in flight while one is computed
+
+__global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
+  constexpr int D = 128, NW = 8, BM = 256;
+  constexpr int RB = D * 2;              // bytes per row
+  constexpr int TB = BN * RB;            // bytes of K (or V) per tile
+  constexpr int NKS = D / 16;
+  constexpr int NBUF = kExtBuf, PF = NBUF - 1;
+  constexpr int IPW = (BN / 4) / NW;     // 1 KB loads per wave per K (or V) tile
+  static_assert(IPW == 2, "two K and two V loads per wave and tile");
+  struct __align__(16) Sm {
+    char k[NBUF][TB];
+    char v[NBUF][TB];
+    int32_t src[kExtSeg * BN];           // per key of the segment: pool slot or k_ext row
+    int32_t t_kind[kExtSeg];             // per tile of the segment: kind | request << 2
+    int32_t t_cnt[kExtSeg];              // keys
+    int32_t t_row[kExtSeg];              // req_to_token row (kinds 0, 1) or first k_ext row (kind 2)
+    int32_t t_pos[kExtSeg];              // first position (kinds 0, 1)
+    int32_t req_m[BM];
+    int32_t req_row[BM];
+    int32_t req_qo[BM + 1];
+    int32_t own[BM + 1];
+    int32_t req_sh[BM];
+    int32_t hdr[8];
+  };
+  __shared__ Sm sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int jrow = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item: (KV head, row block, split); a KV head's row blocks from the last to
+  // the first, so that under causal masking the longest blocks are dispatched first
+  const int64_t item = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  const int split = (int)(item % a.nsplit);
+  const int64_t rb = a.n_rb - 1 - (item / a.nsplit) % a.n_rb;
+  const int h = (int)(item / ((int64_t)a.nsplit * a.n_rb));
+  const int64_t G0 = rb * BM;
+  const int64_t qa = G0 / a.g;
+  int64_t qb = qa + BM / a.g;
+  if (qb > a.total_q) qb = a.total_q;
+
+  // ---- this lane's row and its Q fragments (B operand of S^T = K Q^T)
+  const int R = wave * 32 + jrow;
+  const int64_t t_row = (G0 + R) / a.g;
+  const bool row_ok = t_row < qb;
+  const int hq = h * a.g + (int)((G0 + R) % a.g);
+  bf16x8 qf[NKS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((row_ok ? t_row : qa) * a.h_q + hq) * (int64_t)D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      qf[ks] = row_ok ? v : bf16x8{};
+    }
+  }
+
+  // ---- block metadata (requests covered, shared length, tile list), as attn_kernel
+  if (tid == 0) {
+    const int ra = upper_req(a.qo_indptr, a.batch, qa);
+    int n = upper_req(a.qo_indptr, a.batch, qb - 1) - ra + 1;
+    if (n > BM) {  // only possible with empty requests in between
+      flag_error(RAX_DEVERR_ROW);
+      n = BM;
+    }
+    sm.hdr[0] = ra;
+    sm.hdr[1] = n;
+  }
+  __syncthreads();
+  const int r0 = uni(sm.hdr[0]);
+  const int nreq = uni(sm.hdr[1]);
+  for (int i = tid; i < nreq; i += 64 * NW) {
+    const int r = r0 + i;
+    int row = a.req_pool_idx[r];
+    int m = a.kv_len[r];
+    if (row < 0 || row >= a.rtt_rows || m < 0 || m > a.rtt_stride) {
+      flag_error(RAX_DEVERR_ROW);
+      row = 0;
+      m = 0;
+    }
+    sm.req_row[i] = row;
+    sm.req_m[i] = m;
+    sm.req_qo[i] = a.qo_indptr[r];
+    sm.req_sh[i] = i == 0 ? (1 << 30) : (a.shared_len ? a.shared_len[r] : 0);
+  }
+  if (tid == 0) sm.req_qo[nreq] = a.qo_indptr[r0 + nreq];
+  __syncthreads();
+  if (wave == 0) {
+    int Lw = 1 << 30;
+    for (int i = lane; i < nreq; i += 64) Lw = min(Lw, min(sm.req_m[i], sm.req_sh[i]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Lw = min(Lw, __shfl_xor(Lw, off));
+    const int L = max(Lw, 0);
+    int carry = 0;
+    for (int base = 0; base < nreq; base += 64) {
+      const int i = base + lane;
+      const int rest = i < nreq ? sm.req_m[i] - L : 0;
+      const int cnt = rest > 0 ? (rest + BN - 1) / BN : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (i < nreq) sm.own[i] = carry + incl - cnt;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      sm.own[nreq] = carry;
+      const int n_sh = (L + BN - 1) / BN;
+      const int n_suf = (int)((qb - sm.req_qo[0] + BN - 1) / BN);
+      const int total = n_sh + carry + n_suf;
+      sm.hdr[2] = L;
+      sm.hdr[3] = n_sh;
+      sm.hdr[4] = carry;
+      sm.hdr[5] = (int)(((int64_t)total * split) / a.nsplit);
+      sm.hdr[6] = (int)(((int64_t)total * (split + 1)) / a.nsplit);
+    }
+  }
+  __syncthreads();
+  const int L = uni(sm.hdr[2]);
+  const int n_sh = uni(sm.hdr[3]);
+  const int n_own = uni(sm.hdr[4]);
+  const int tb = uni(sm.hdr[5]);
+  const int te = uni(sm.hdr[6]);
+  const int suf0 = uni(sm.req_qo[0]);
+
+  // ---- the request of this lane's row; the wave's request and suffix-row ranges
+  int my_req = 0;
+  int w_rlo = 1 << 30, w_rhi = -1, w_klo = 1 << 30, w_khi = -1, n_bad = 0;
+  if (row_ok) {
+    int lo = 0, hi = nreq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.req_qo[mid] <= t_row) lo = mid;
+      else hi = mid - 1;
+    }
+    my_req = lo;
+    w_rlo = w_rhi = my_req;
+    w_klo = sm.req_qo[my_req];
+    w_khi = (int)t_row;
+  } else {
+    n_bad = 1;
+  }
+  const int my_qo = sm.req_qo[my_req];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    w_rlo = min(w_rlo, __shfl_xor(w_rlo, off));
+    w_rhi = max(w_rhi, __shfl_xor(w_rhi, off));
+    w_klo = min(w_klo, __shfl_xor(w_klo, off));
+    w_khi = max(w_khi, __shfl_xor(w_khi, off));
+    n_bad += __shfl_xor(n_bad, off);
+  }
+  w_rlo = uni(w_rlo);
+  w_rhi = uni(w_rhi);
+  w_klo = uni(w_klo);
+  w_khi = uni(w_khi);
+  const bool wave_active = w_rhi >= 0;
+  const bool all_rows_ok = uni(n_bad) == 0;
+
+  const int64_t row_bytes = (int64_t)a.h_kv * RB;
+  const int64_t head_off = (int64_t)h * RB;
+  const uint32_t k_lds = lds_addr(&sm.k[0][0]), v_lds = lds_addr(&sm.v[0][0]);
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool) + head_off;
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool) + head_off;
+  const char* kext = reinterpret_cast<const char*>(a.k_ext) + head_off;
+  const char* vext = reinterpret_cast<const char*>(a.v_ext) + head_off;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  // K and V rows of segment tile lt into buffer b (this wave's 2 + 2 loads)
+  auto issue = [&](int lt, int b) {
+    const bool ext = (uni(sm.t_kind[lt]) & 3) == 2;
+    const char* kb = ext ? kext : kpool;
+    const char* vb = ext ? vext : vpool;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int q = wave + u * NW;
+      const int r = q * 4 + (lane >> 4);
+      const int64_t off = (int64_t)sm.src[lt * BN + r] * row_bytes;
+      lds_load16(kb + off + (((lane & 15) ^ swz_k(r)) * 16), uni(k_lds + b * TB + q * 1024));
+      lds_load16(vb + off + (((lane & 15) ^ swz_v(r)) * 16), uni(v_lds + b * TB + q * 1024));
+    }
+  };
+
+  // the online softmax of one 32-key half (sub) of a tile's (masked) scores, then
+  // O^T += V^T P^T
+  auto half_step = [&](const char* vt, f32x16& sc, int sub) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
+      sc[r] = pv;
+      psum += pv;
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+  };
+
+  for (int seg0 = tb; seg0 < te; seg0 += kExtSeg) {
+    const int nt = min(te - seg0, kExtSeg);
+    // ---- table of the segment's tiles (one thread per tile, as describe() but per lane)
+    for (int i = tid; i < nt; i += 64 * NW) {
+      const int tau = seg0 + i;
+      int kind, cnt, row = 0, pos0 = 0, req = 0;
+      if (tau < n_sh) {
+        kind = 0;
+        pos0 = tau * BN;
+        cnt = min(BN, L - pos0);
+        row = sm.req_row[0];
+      } else if (tau < n_sh + n_own) {
+        kind = 1;
+        const int o = tau - n_sh;
+        int lo = 0, hi = nreq - 1;  // last request with own[] <= o
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.own[mid] <= o) lo = mid;
+          else hi = mid - 1;
+        }
+        req = lo;
+        pos0 = L + (o - sm.own[lo]) * BN;
+        cnt = min(BN, sm.req_m[lo] - pos0);
+        row = sm.req_row[lo];
+      } else {
+        kind = 2;
+        row = suf0 + (tau - n_sh - n_own) * BN;  // first k_ext row
+        cnt = (int)min((int64_t)BN, qb - row);
+      }
+      sm.t_kind[i] = kind | (req << 2);
+      sm.t_cnt[i] = cnt;
+      sm.t_row[i] = row;
+      sm.t_pos[i] = pos0;
+    }
+    __syncthreads();
+    // ---- every key's source row: the slot ids of a pool tile straight into LDS (one 4-byte
+    // load per lane, tiles dealt over the waves, all in flight at once), then the suffix
+    // tiles' k_ext rows, positions past a tile's keys and slot ids outside the pool fixed up
+    // (past the keys: the tile's first key's row, finite data that the masks drop)
+    for (int lt = wave; lt < nt; lt += NW) {
+      const int tk = uni(sm.t_kind[lt]);
+      const int cnt = uni(sm.t_cnt[lt]);
+      int64_t idx = 0;
+      if ((tk & 3) != 2) idx = (int64_t)uni(sm.t_row[lt]) * a.rtt_stride + uni(sm.t_pos[lt]) + (lane < cnt ? lane : 0);
+      lds_load4(a.rtt + idx, uni(lds_addr(&sm.src[lt * BN])));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int i = tid; i < nt * BN; i += 64 * NW) {
+      const int lt = i / BN, j = i % BN;
+      const int kind = sm.t_kind[lt] & 3;
+      const bool in = j < sm.t_cnt[lt];
+      int sv;
+      if (kind == 2) {
+        sv = sm.t_row[lt] + (in ? j : 0);
+      } else {
+        sv = sm.src[i];
+        if (sv < 0 || sv >= a.num_slots) {
+          if (in) flag_error(RAX_DEVERR_SLOT);
+          sv = 0;
+        }
+      }
+      sm.src[i] = sv;
+    }
+    __syncthreads();
+
+    // ---- the tile loop: PF tiles in flight while one is computed
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (j < nt) issue(j, j);
+    for (int i = 0; i < nt; ++i) {
+      // this wave's loads of tile i are done when at most those of the PF - 1 tiles issued
+      // after it are in flight
+      if (i + PF - 1 < nt) wait_vmcnt<4 * (PF - 1)>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // every wave's loads of tile i landed; buffer (i - 1) % NBUF is free
+      if (i + PF < nt) issue(i + PF, (i + PF) % NBUF);
+      const int tk = uni(sm.t_kind[i]);
+      const int kind = tk & 3, req = tk >> 2;
+      const int cnt = uni(sm.t_cnt[i]);
+      const int kr0 = uni(sm.t_row[i]);
+      bool run = wave_active;
+      if (kind == 1) run = run && req >= w_rlo && req <= w_rhi;
+      if (kind == 2) run = run && kr0 <= w_khi && kr0 + cnt > w_klo;
+      if (!run) continue;
+      const int b = i % NBUF;
+      const char* kt = &sm.k[b][0];
+      const char* vt = &sm.v[b][0];
+      f32x16 sall[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        sall[sub] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sall[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, sub * 32 + jrow, ks, half), qf[ks],
+                                                              sall[sub], 0, 0, 0);
+      }
+      if (!(kind == 0 && cnt == BN && all_rows_ok)) {  // masks: full shared tiles have none
+        // this lane's row sees keys [lo, hi) of the tile: all of its keys (shared prefix), those
+        // of its own request (own prefix), or the causal range of its request's suffix
+        int lo = 0, hi = row_ok ? cnt : 0;
+        if (kind == 1 && my_req != req) hi = 0;
+        if (kind == 2) {
+          lo = max(lo, my_qo - kr0);
+          hi = min(hi, (int)(t_row - kr0) + 1);
+        }
+        // key of register r: sub*32 + 8*(r/4) + 4*half + r%4; compare the constant part
+        lo -= 4 * half;
+        hi -= 4 * half;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = sub * 32 + 8 * (r >> 2) + (r & 3);
+            sall[sub][r] = c >= lo && c < hi ? sall[sub][r] : kNegInf;
+          }
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) half_step(vt, sall[sub], sub);
+    }
+    __syncthreads();  // the next segment rewrites the table, the rows and the buffers
+  }
+
+  // ---- epilogue: lane holds row jrow, dims dt*32 + 8*(r/4) + 4*half + r%4
+  if (!row_ok) return;
+  if (a.nsplit == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t obase = (t_row * a.h_q + hq) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = dt * 32 + 8 * rg + 4 * half;
+        const float x0 = acc[dt][rg * 4 + 0] * inv, x1 = acc[dt][rg * 4 + 1] * inv;
+        const float x2 = acc[dt][rg * 4 + 2] * inv, x3 = acc[dt][rg * 4 + 3] * inv;
+        if (a.o_bf16)
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
+              bf16x4{(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+        else
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) = make_float4(x0, x1, x2, x3);
+      }
+    }
+    return;
+  }
+  // split partials at the block's own place (merge_kernel's layout)
+  const int64_t item_w = ((int64_t)h * a.n_rb + rb) * a.nsplit + split;
+  if (l_run > 0.f) {
+    float* wacc = a.ws + (item_w * BM + R) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<float4*>(wacc + dt * 32 + 8 * rg + 4 * half) =
+            make_float4(acc[dt][rg * 4 + 0], acc[dt][rg * 4 + 1], acc[dt][rg * 4 + 2], acc[dt][rg * 4 + 3]);
+  }
+  if (half == 0) {
+    const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
+    float* wml = a.ws + n_items * BM * (int64_t)D + (item_w * BM + R) * 2;
+    wml[0] = m_run;
+    wml[1] = l_run;
+  }
+}
+
 // ---- wavefront lane exchanges: value of lane (l ^ d)
 // d = 8, 2, 1 are DPP moves within a 16-lane row (row_ror:8, quad_perm [1,0,3,2] and
 // [2,3,0,1]); d = 32, 16, 4 go through ds_bpermute. (gfx950's v_permlane16/32_swap would
@@ -2334,7 +2736,11 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const Append
   rax_status rc = RAX_EINVAL;
   if constexpr (sizeof(T) == 2 && !kDecode) {
     if constexpr (D == 128) {
-      if (s.nw == 8 && s.rt == 1 && s.pd == 1 && s.ks == 1) rc = launch_one<T, D, kDecode, 8, 1, 1, 1>(a, st);
+      if (s.nw == 8 && s.rt == 1 && s.pd == 1 && s.ks == 1) {
+        const int64_t items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
+        hipLaunchKernelGGL(extend_kernel, dim3((unsigned)items), dim3(512), 0, st, a);
+        rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+      }
     } else {
       if (s.nw == 4 && s.rt == 2 && s.pd == 1 && s.ks == 1) rc = launch_one<T, D, kDecode, 4, 2, 1, 1>(a, st);
     }

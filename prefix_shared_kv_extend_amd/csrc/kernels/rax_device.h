@@ -35,6 +35,11 @@ __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory into LDS at lds + 4 * lane (lds wave-uniform).
+__device__ __forceinline__ void lds_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
 // The same load with the non-temporal hint, for rows read once per call: measured on a
 // 4 GB streaming read, plain 16-byte loads reach ~5.8 TB/s and non-temporal ones ~7.2 TB/s
 // (the lines are not kept in the caches on the way).
