@@ -68,7 +68,7 @@ DESCR = {
 }
 # kernels that start a launch of each attention entry point (substrings of their names); the
 # kernels after one (own parts, merges) belong to it, up to the next launch's first kernel
-ENTRY_FIRST = {"decode": "shared_kernel", "extend": "attn_kernelIDF16bLi128ELb0E"}
+ENTRY_FIRST = {"decode": "shared_kernel", "extend": "extend_kernel"}
 ENTRY_REST = ("own_", "merge_kernel")
 
 
@@ -737,8 +737,8 @@ def summarize_counters(run_dirs):
             print(f"| SALU instructions per MFMA | {mean['SQ_INSTS_SALU'] / mean['SQ_INSTS_MFMA']:.2f} |")
 
 
-HOT = ("shared_kernel", "own_", "merge_kernel", "attn_kernel", "kv_scatter_kernel", "rtt_write_kernel",
-       "decode_append_kernel", "kv_move_kernel")
+HOT = ("shared_kernel", "own_", "merge_kernel", "attn_kernel", "extend_kernel", "kv_scatter_kernel",
+       "rtt_write_kernel", "decode_append_kernel", "kv_move_kernel")
 
 
 def summarize_trace(csv_path):

@@ -124,22 +124,6 @@ struct __align__(16) Smem {
   int32_t hdr[8];
 };
 
-// Same, for tiles loaded straight into LDS (bf16, D = 128): unpadded, swizzled rows.
-template <typename T, int D, int NW, int RT, int KS>
-struct __align__(16) SmemDma {
-  using C = Cfg<T, D, NW, RT, KS>;
-  T k[2][BN * D];
-  T v[2][BN * D];
-  int32_t slot[4][BN];
-  int32_t bad[4];  // per slot buffer: some key of the tile has no slot
-  int32_t req_m[C::BM];
-  int32_t req_row[C::BM];
-  int32_t req_qo[C::BM + 1];
-  int32_t own[C::BM + 1];
-  int32_t req_sh[C::BM];
-  int32_t hdr[8];
-};
-
 struct TileDesc {
   int kind;  // 0 shared prefix, 1 one request's own prefix, 2 suffix (k_ext rows)
   int cnt;   // valid keys in the tile
@@ -184,6 +168,29 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* vt, int sub, int dt, int k
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * 256));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Fragment reads through LDS-address-space pointers (the arithmetic stays in the LDS
+// address space, so constant parts fold into the instructions' offset fields): k_frag's
+// read, and vt_frag's transposing pair (the second 8 keys further)
+typedef __attribute__((address_space(3))) const char* lds_cp;
+__device__ __forceinline__ lds_cp lds_ptr(uint32_t addr) { return (lds_cp)(uintptr_t)addr; }
+__device__ __forceinline__ bf16x8 k_at(lds_cp p) {
+  return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 vt_at(lds_cp p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lp;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 8 * 256));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// An empty asm that the compiler must treat as changing x: a base formed from it is not
+// re-associated with the constant parts of later addresses, which then fold into the
+// reads' offset fields (one add per base and tile instead of two per read).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
 __device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t) {
@@ -279,10 +286,9 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   using C = Cfg<T, D, NW, RT, KS>;
   constexpr int BM = C::BM;
   constexpr bool kBf16 = sizeof(T) == 2;
-  // extend, bf16, D = 128: tiles go straight into LDS (see "tiles loaded straight into
-  // LDS"); otherwise they are staged through registers and stored padded / transposed
-  constexpr bool kDma = kBf16 && D == 128 && !kDecode && KS == 1 && RT == 1 && PD == 1;
-  using SM = std::conditional_t<kDma, SmemDma<T, D, NW, RT, KS>, Smem<T, D, NW, RT, KS>>;
+  // tiles are staged through registers and stored padded / transposed (bf16 extend with
+  // D = 128 runs in extend_kernel, which loads them straight into LDS)
+  using SM = Smem<T, D, NW, RT, KS>;
   __shared__ SM sm;
 
   const int tid = threadIdx.x;
@@ -500,7 +506,6 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   // registers -> LDS buffer b (K row-major, V transposed); keys without a slot become zeros
   auto store_tile = [&](int b, int sb, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    if constexpr (!kDma) {
 #pragma unroll
     for (int p = 0; p < C::KP; ++p) {
       const int key = p * C::KPP + kk;
@@ -527,55 +532,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         }
       }
     }
-    }
   };
   auto desc = [&](int tau) { return describe(tau, sm, L, n_sh, n_own, suf0, qb, nreq); };
 
-  // kDma: K and V rows of tile d (slot ids in sm.slot[sb]) straight into LDS buffer b;
-  // keys without a slot read row 0. Each lane's 16 bytes land at LDS row 4q + lane/16,
-  // chunk lane%16.
-  constexpr int kDmaRpi = 4, kDmaNi = BN / kDmaRpi;  // rows per 1 KB instruction, instructions per tile
-  auto dma_tile = [&](const TileDesc& d, int sb, int b, auto) {
-    if constexpr (kDma) {
-    const char* kb = reinterpret_cast<const char*>(d.kind == 2 ? a.k_ext : a.k_pool) + head_off;
-    const char* vb = reinterpret_cast<const char*>(d.kind == 2 ? a.v_ext : a.v_pool) + head_off;
-    const uint32_t kl = lds_addr(&sm.k[b][0]), vl = lds_addr(&sm.v[b][0]);
-#pragma unroll
-    for (int q = wave; q < kDmaNi; q += NW) {
-      const int r = q * kDmaRpi + (lane >> 4);
-      const int sv = sm.slot[sb][r];
-      const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
-      lds_load16(kb + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
-      lds_load16(vb + off + (((lane & 15) ^ swz_v(r)) * 16), uni(vl + q * 1024));
-    }
-    }
-  };
-  // kDma: wait for this wave's loads, then zero the K and V rows of keys without a slot
-  // (each lane the positions it loaded, so no other wave's load can land after)
-  auto dma_finish = [&](int sb, int b, auto) {
-    if constexpr (kDma) {
-    __builtin_amdgcn_s_waitcnt(0);
-    if (uni(sm.bad[sb])) {
-#pragma unroll
-      for (int q = wave; q < kDmaNi; q += NW) {
-        const int r = q * kDmaRpi + (lane >> 4);
-        if (sm.slot[sb][r] < 0) {
-          const int off = r * D * (int)sizeof(T) + (lane & 15) * 16;
-          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(&sm.k[b][0]) + off) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(&sm.v[b][0]) + off) = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    }
-  };
-  // slot ids of one tile written by the first BN threads (wave 0), with the tile's flag
-  auto put_slot = [&](int sb, int v) {
-    sm.slot[sb][tid] = v;
-    if constexpr (kDma) {
-      const uint64_t bad = __ballot(v < 0);
-      if (tid == 0) sm.bad[sb] = bad != 0;
-    }
-  };
+  // slot ids of one tile written by the first BN threads (wave 0)
+  auto put_slot = [&](int sb, int v) { sm.slot[sb][tid] = v; };
 
   // ---- prologue: slot ids of tiles t_begin .. t_begin+PD, K/V loads of the first PD tiles
   if (tid < BN && t_begin < t_end) {  // all prologue slot loads in one round trip
@@ -592,17 +553,12 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (t_begin < t_end) {
-    if constexpr (kDma) {
-      dma_tile(desc(t_begin), t_begin % NSB, 0, 0);
-      dma_finish(t_begin % NSB, 0, 0);
-    } else {
-      issue_loads(desc(t_begin), t_begin % NSB, true, std::integral_constant<int, 0>{});
-      if constexpr (PD > 1) {
-        const bool live = t_begin + 1 < t_end;
-        issue_loads(desc(live ? t_begin + 1 : t_begin), (t_begin + 1) % NSB, live, std::integral_constant<int, 1>{});
-      }
-      store_tile(0, t_begin % NSB, std::integral_constant<int, 0>{});
+    issue_loads(desc(t_begin), t_begin % NSB, true, std::integral_constant<int, 0>{});
+    if constexpr (PD > 1) {
+      const bool live = t_begin + 1 < t_end;
+      issue_loads(desc(live ? t_begin + 1 : t_begin), (t_begin + 1) % NSB, live, std::integral_constant<int, 1>{});
     }
+    store_tile(0, t_begin % NSB, std::integral_constant<int, 0>{});
   }
   __syncthreads();
 
@@ -617,11 +573,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     const TileDesc dn = desc(has_next ? tau + PD + 1 : tau);
     const int raw_slot = slot_issue(a, dn, tid < BN ? tid : 0);
     const bool live = tau + PD < t_end;
-    if constexpr (kDma) {
-      if (live) dma_tile(desc(tau + 1), (tau + 1) % NSB, buf ^ 1, 0);
-    } else {
-      issue_loads(desc(live ? tau + PD : tau), (tau + PD) % NSB, live, std::integral_constant<int, ph>{});
-    }
+    issue_loads(desc(live ? tau + PD : tau), (tau + PD) % NSB, live, std::integral_constant<int, ph>{});
 
     // -- does this wave have rows that see any key of the tile?
     bool run = wave_active;
@@ -642,13 +594,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
         const int sub = KS == 1 ? si : wkey;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sall[si][rt] = f32x16{};
-        const T* kr = &sm.k[buf][(sub * 32 + jrow) * (kDma ? D : C::KSTRIDE)];
+        const T* kr = &sm.k[buf][(sub * 32 + jrow) * C::KSTRIDE];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           if constexpr (kBf16) {
-            bf16x8 af;
-            if constexpr (kDma) af = k_frag(reinterpret_cast<const char*>(&sm.k[buf][0]), sub * 32 + jrow, ks, half);
-            else af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + ks * 16 + half * 8);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               sall[si][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[rt][ks], sall[si][rt], 0, 0, 0);
@@ -724,16 +674,11 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
           for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-              bf16x8 af;
-              if constexpr (kDma) {
-                af = vt_frag(reinterpret_cast<const char*>(&sm.v[buf][0]), sub, dt, kh, lane);
-              } else {
-                const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
-                const int kb0 = sub * 32 + kh * 16 + 4 * half;
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + kb0);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + kb0 + 8);
-                af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-              }
+              const T* vr = &sm.vt[buf][(dt * 32 + jrow) * C::VSTRIDE];
+              const int kb0 = sub * 32 + kh * 16 + 4 * half;
+              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + kb0);
+              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + kb0 + 8);
+              const bf16x8 af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
               for (int rt = 0; rt < RT; ++rt)
                 acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[rt][kh], acc[rt][dt], 0, 0, 0);
@@ -756,11 +701,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
       }
     }
 
-    if constexpr (kDma) {
-      if (tau + 1 < t_end) dma_finish((tau + 1) % NSB, buf ^ 1, 0);
-    } else {
-      if (tau + 1 < t_end) store_tile(buf ^ 1, (tau + 1) % NSB, std::integral_constant<int, (ph + 1) % PD>{});
-    }
+    if (tau + 1 < t_end) store_tile(buf ^ 1, (tau + 1) % NSB, std::integral_constant<int, (ph + 1) % PD>{});
     if (has_next && tid < BN) put_slot((tau + PD + 1) % NSB, slot_finish(a, dn, tid, raw_slot));
     __syncthreads();
   };
@@ -1046,6 +987,22 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
+  // LDS byte offsets of this lane's fragment reads within a tile buffer, by k-step (K) and
+  // by 32-dim slice (V): the swizzles XOR lane bits into them, so they are formed once here
+  // and a tile adds only its buffer's base (k_frag / vt_frag compute the same addresses)
+  uint32_t koff[NKS], voff[D / 32];
+  {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = jrow * 256 + (((2 * ks + half) ^ swz_k(jrow)) * 16);
+    const int pl = lane & 15, dsub = (lane >> 4) & 1;
+    const int kl = 4 * half + (pl >> 2);  // key within a 16-key group
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int d0 = dt * 32 + dsub * 16 + 4 * (pl & 3);
+      voff[dt] = kl * 256 + (((d0 >> 3) ^ swz_v(kl)) * 16) + (d0 & 7) * 2;
+    }
+  }
+
   // K and V rows of segment tile lt into buffer b (this wave's 2 + 2 loads)
   auto issue = [&](int lt, int b) {
     const bool ext = (uni(sm.t_kind[lt]) & 3) == 2;
@@ -1063,7 +1020,7 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
 
   // the online softmax of one 32-key half (sub) of a tile's (masked) scores, then
   // O^T += V^T P^T
-  auto half_step = [&](const char* vt, f32x16& sc, int sub) {
+  auto half_step = [&](const uint32_t (&va)[D / 32], f32x16& sc, int sub) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
@@ -1095,7 +1052,8 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_at(lds_ptr(va[dt]) + sub * 8192 + kh * 4096),
+                                                          pb[kh], acc[dt], 0, 0, 0);
   };
 
   for (int seg0 = tb; seg0 < te; seg0 += kExtSeg) {
@@ -1184,16 +1142,20 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
       if (kind == 2) run = run && kr0 <= w_khi && kr0 + cnt > w_klo;
       if (!run) continue;
       const int b = i % NBUF;
-      const char* kt = &sm.k[b][0];
-      const char* vt = &sm.v[b][0];
+      const uint32_t kb = uni(k_lds + b * TB), vb = uni(v_lds + b * TB);
+      uint32_t ka[NKS], va[D / 32];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) ka[ks] = opaque(kb + koff[ks]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) va[dt] = opaque(vb + voff[dt]);
       f32x16 sall[2];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         sall[sub] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          sall[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, sub * 32 + jrow, ks, half), qf[ks],
-                                                              sall[sub], 0, 0, 0);
+          sall[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_at(lds_ptr(ka[ks]) + sub * 8192), qf[ks], sall[sub],
+                                                              0, 0, 0);
       }
       if (!(kind == 0 && cnt == BN && all_rows_ok)) {  // masks: full shared tiles have none
         // this lane's row sees keys [lo, hi) of the tile: all of its keys (shared prefix), those
@@ -1204,19 +1166,23 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
           lo = max(lo, my_qo - kr0);
           hi = min(hi, (int)(t_row - kr0) + 1);
         }
-        // key of register r: sub*32 + 8*(r/4) + 4*half + r%4; compare the constant part
-        lo -= 4 * half;
-        hi -= 4 * half;
+        // nothing to mask when every row of the wave sees the whole tile (interior tiles
+        // of a row's own prefix or below its causal diagonal)
+        if (!__all(lo <= 0 && hi >= BN)) {
+          // key of register r: sub*32 + 8*(r/4) + 4*half + r%4; compare the constant part
+          lo -= 4 * half;
+          hi -= 4 * half;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+          for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = sub * 32 + 8 * (r >> 2) + (r & 3);
-            sall[sub][r] = c >= lo && c < hi ? sall[sub][r] : kNegInf;
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int c = sub * 32 + 8 * (r >> 2) + (r & 3);
+              sall[sub][r] = c >= lo && c < hi ? sall[sub][r] : kNegInf;
+            }
+        }
       }
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) half_step(vt, sall[sub], sub);
+      for (int sub = 0; sub < 2; ++sub) half_step(va, sall[sub], sub);
     }
     __syncthreads();  // the next segment rewrites the table, the rows and the buffers
   }
