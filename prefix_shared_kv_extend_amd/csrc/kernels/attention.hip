@@ -44,8 +44,9 @@
 
 #include <algorithm>
 #include <mutex>
-
+#include <numeric>
 #include <type_traits>
+#include <vector>
 
 #include "../../../include/rax.h"
 #include "../rax_internal.h"
@@ -2307,31 +2308,27 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
 }
 
 // End of an own-part workgroup with query-head groups (bf16, D = 128, 4 waves as four key
-// groups, the g query heads as rows of one 32-row tile): the groups' (m, l, acc) combine
-// split by dims through LDS (xbuf: at least 51,200 bytes, free when called), then either
+// groups, the g query heads as rows of one 16-row tile; lane l holds row l % 16, dims
+// dt*16 + 4*(l/16) + {0..3} of acc[dt]): the groups' (m, l, acc) combine through LDS (xbuf:
+// at least kOwnXBytes, free when called), wave w finishing dims [32w, 32w + 32); then either
 // the request's only own chunk is merged in place with the shared part's split partials and
 // O written, or the chunk's partial goes to the workspace in own_kernel's layout.
+constexpr int kOwnXBytes = (8 * 4 * 4 + 4 * 2) * 64 * (int)sizeof(float);
 template <int D>
-__device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbuf, const f32x16 (&acc)[D / 32],
-                                                    float m_run, float l_run, int wkey, int lane, int jrow, int half,
-                                                    bool row_ok, int t, int h, int rh, int c, int n_act, int n_rh) {
+__device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbuf, const f32x4 (&acc)[D / 16],
+                                                    float m_run, float l_run, int wkey, int lane, bool row_ok,
+                                                    int t, int h, int rh, int c, int n_act, int n_rh) {
   constexpr int NKG = 4;
+  static_assert(D == 128, "four 32-dim quarters, one per key group");
   const int G = a.g;
-  constexpr int NDT = D / 32;
-  static_assert(NDT == NKG, "one 32-dim slice per key group");
-  constexpr int NX = NDT * (NKG - 1) * 16;  // floats per lane handed over
-  static_assert((NX + NKG * 2) * 64 * sizeof(float) <= 51200, "key-split exchange area");
-  float* xs = reinterpret_cast<float*>(xbuf);  // [dt][group other than dt][16][64]
-  float* xml = xs + NX * 64;                 // [group][m, l][64]
-  auto xacc = [&](int dt, int grp, int r) -> float& {
-    const int g3 = grp < dt ? grp : grp - 1;
-    return xs[((dt * (NKG - 1) + g3) * 16 + r) * 64 + lane];
-  };
+  const int r16 = lane & 15, g4 = lane >> 4;
+  float* xs = reinterpret_cast<float*>(xbuf);  // [dt][group][4][64]
+  float* xml = xs + (D / 16) * NKG * 4 * 64;   // [group][m, l][64]
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    if (dt == wkey) continue;
+  for (int dt = 0; dt < D / 16; ++dt) {
+    if ((dt >> 1) == wkey) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xacc(dt, wkey, r) = acc[dt][r];
+    for (int e = 0; e < 4; ++e) xs[((dt * NKG + wkey) * 4 + e) * 64 + lane] = acc[dt][e];
   }
   xml[(wkey * 2 + 0) * 64 + lane] = m_run;
   xml[(wkey * 2 + 1) * 64 + lane] = l_run;
@@ -2345,17 +2342,24 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
     m = fmaxf(m, mk[k]);
   }
   float l = 0.f;
-  f32x16 o = f32x16{};
+  f32x4 o[2] = {f32x4{}, f32x4{}};
+  if (m != kNegInf) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    if (dt != wkey) continue;
-    if (m != kNegInf) {
+    for (int k = 0; k < NKG; ++k) {
+      const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
+      l += lk[k] * ak;
 #pragma unroll
-      for (int k = 0; k < NKG; ++k) {
-        const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
-        l += lk[k] * ak;
+      for (int j = 0; j < 2; ++j) {
+        const int dt = 2 * wkey + j;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] += (k == wkey ? acc[dt][r] : xacc(dt, k, r)) * ak;
+        for (int e = 0; e < 4; ++e) {
+          // acc[dt] with dt chosen at run time would go through scratch: select instead
+          float mine = 0.f;
+#pragma unroll
+          for (int q = 0; q < D / 16; ++q)
+            if (q == dt) mine = acc[q][e];
+          o[j][e] += (k == wkey ? mine : xs[((dt * NKG + k) * 4 + e) * 64 + lane]) * ak;
+        }
       }
     }
   }
@@ -2365,7 +2369,7 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
     // this row (written by the previous kernel) by log-sum-exp and write this wave's
     // dims of O; merge_kernel skips such rows. A split that saw no key (l == 0) may hold
     // stale data, hence the selects.
-    const int Grow = t * G + jrow;
+    const int Grow = t * G + r16;
     const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
     const int nsplit = a.nsplit;
     const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
@@ -2380,75 +2384,95 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
     const float Mu = M == kNegInf ? 0.f : M;
     const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
     float lsum = w_own * l;
-    f32x16 fin;
+    f32x4 fin[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) fin[r] = w_own != 0.f ? w_own * o[r] : 0.f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fin[j][e] = w_own != 0.f ? w_own * o[j][e] : 0.f;
     for (int sp = 0; sp < nsplit; ++sp) {
       const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
       const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - Mu) : 0.f;
       lsum += w * ml.y;
       const float* pa = sh_acc + (int64_t)sp * a.bm * D;
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 8 * rg + 4 * half);
+      for (int j = 0; j < 2; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 16 * j + 4 * g4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fin[rg * 4 + e] += w != 0.f ? w * x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) fin[j][e] += w != 0.f ? w * x[e] : 0.f;
       }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int64_t obase = ((int64_t)t * a.h_q + h * G + jrow) * D;
+    const int64_t obase = ((int64_t)t * a.h_q + h * G + r16) * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = wkey * 32 + 8 * rg + 4 * half;
+    for (int j = 0; j < 2; ++j) {
+      const int d0 = wkey * 32 + 16 * j + 4 * g4;
       if (a.o_bf16)
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
-            bf16x4{(__bf16)(fin[rg * 4 + 0] * inv), (__bf16)(fin[rg * 4 + 1] * inv), (__bf16)(fin[rg * 4 + 2] * inv),
-                   (__bf16)(fin[rg * 4 + 3] * inv)};
+            bf16x4{(__bf16)(fin[j][0] * inv), (__bf16)(fin[j][1] * inv), (__bf16)(fin[j][2] * inv),
+                   (__bf16)(fin[j][3] * inv)};
       else
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) =
-            make_float4(fin[rg * 4 + 0] * inv, fin[rg * 4 + 1] * inv, fin[rg * 4 + 2] * inv, fin[rg * 4 + 3] * inv);
+            make_float4(fin[j][0] * inv, fin[j][1] * inv, fin[j][2] * inv, fin[j][3] * inv);
     }
     return;
   }
-  // partial of (request t, KV head h, chunk c), query head jrow, in own_kernel's layout
+  // partial of (request t, KV head h, chunk c), query head r16, in own_kernel's layout
   const int64_t item = (int64_t)rh * a.n_chunk + c;
   if (l > 0.f) {
-    float* wacc = a.ws_own + (item * G + jrow) * D;
+    float* wacc = a.ws_own + (item * G + r16) * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = wkey * 32 + 8 * rg + 4 * half;
-      __builtin_nontemporal_store(f32x4{o[rg * 4 + 0], o[rg * 4 + 1], o[rg * 4 + 2], o[rg * 4 + 3]},
-                                  reinterpret_cast<f32x4*>(wacc + d0));
-    }
+    for (int j = 0; j < 2; ++j)
+      __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4*>(wacc + wkey * 32 + 16 * j + 4 * g4));
   }
-  if (wkey == 0 && half == 0) {
-    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + jrow) * 2;
+  if (wkey == 0 && g4 == 0) {
+    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + r16) * 2;
     __builtin_nontemporal_store(m, wml);
     __builtin_nontemporal_store(l, wml + 1);
   }
 }
 
+// 16x16x32 MFMA fragments of a stage (32 keys x 128 dims of K, and of V, swizzled as above).
+// A operand of S^T = K Q^T: key 16*kh + l%16, dims 32*ks + 8*(l/16) .. +8.
+__device__ __forceinline__ bf16x8 k_frag16(const char* kt, int kh, int ks, int lane) {
+  const int key = 16 * kh + (lane & 15);
+  return *reinterpret_cast<const bf16x8*>(kt + key * 256 + (((4 * ks + (lane >> 4)) ^ swz_k(key)) * 16));
+}
+// A operand of O^T = V^T P^T for dims 16*dt .. +16: lane l holds dim 16*dt + l%16 of keys
+// 4*(l/16) + {0..3} and 16 + 4*(l/16) + {0..3}, the key order of the P fragment (the two
+// 16-key score tiles of a lane, one after the other). Each transposing read takes 4 keys x
+// 16 dims over 16 lanes (lane i: key i/4, dims 4*(i%4) .. +4) and hands lane i dim i.
+__device__ __forceinline__ bf16x8 vt_frag16(const char* vt, int dt, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int i = lane & 15;
+  const int d0 = dt * 16 + 4 * (i & 3);
+  const int key = 4 * (lane >> 4) + (i >> 2);
+  const char* p0 = vt + key * 256 + (((d0 >> 3) ^ swz_v(key)) * 16) + (d0 & 7) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 16 * 256));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Own part of split decode with query-head groups (bf16, D = 128), as one continuous
 // stream per workgroup, on MFMA: the VALU own part (own_chunk) scores 32 / g keys per
 // batch through chains of cross-lane reductions, which for g > 1 bound it rather than
-// memory (0.56 ms per GQA 64/8 self-consistency call for 0.59 GB). A workgroup takes one own chunk of (request t, KV head h), at
-// most kStreamCap keys. Its slot ids go to LDS first (one round of loads); then the
-// chunk's keys stream through a ring of S stages of 32 keys (8 KB of K and 8 KB of V
-// each) filled straight from global memory: while stage i is computed, the loads of the
-// next S - 1 stages are in flight, so bytes stay in flight all the time instead of one
-// round of tiles at a time. One barrier per stage. The four waves are four key groups:
-// wave w computes stages i = w (mod 4) (S^T = K Q^T and O^T = V^T P^T on 32x32x16 MFMA,
-// the g query heads as rows of one 32-row tile, rows past g masked), and the groups
-// combine at the end (own_groups_epilogue). Keys past the chunk in its last stage read
-// the chunk's first slot (a key it attends, so finite) and are masked.
+// memory (0.56 ms per GQA 64/8 self-consistency call for 0.59 GB). A workgroup takes one
+// own chunk of (request t, KV head h), at most kStreamCap keys. Its slot ids go to LDS
+// first (one round of loads); then the chunk's keys stream through a ring of S stages of
+// 32 keys (8 KB of K and 8 KB of V each) filled straight from global memory: while stage i
+// is computed, the loads of the next S - 1 stages are in flight. One barrier per stage.
+// The four waves are four key groups: wave w computes stages i = w (mod 4) and the groups
+// combine at the end (own_groups_epilogue). A stage is S^T = K Q^T and O^T = V^T P^T on
+// 16x16x32 MFMA with the g <= 16 query heads as the columns of one 16-wide tile (columns
+// past g masked): the 16-row shape does half the matrix work of a 32-row one, so the one
+// wave that computes a stage holds the barrier half as long (per-workgroup timestamps of
+// the 32-row form: ~1 us per stage, about the stage's whole time). Keys past the chunk in
+// its last stage read the chunk's first slot (a key it attends, so finite) and are masked.
 constexpr int kStreamCap = 2048;  // most keys per own chunk of own_stream_kernel
 constexpr int kStreamTK = 32;     // keys per stage
-// Four stages (72 KB of LDS, two workgroups per CU) measured as fast as three and
-// faster than six or nine (one workgroup per CU: 360 against 241 us per multi-turn call).
 constexpr int kStreamStages = 4;
 
 template <int D, int S>
-__global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder ord) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
   static_assert(S >= 2 && 2 * (S - 2) < 64, "stages");
   constexpr int NW = 4;
@@ -2458,32 +2482,44 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
   constexpr int RPI = 1024 / RB;         // rows per 1 KB global-to-LDS instruction
   constexpr int NI = TK / RPI;           // instructions per K (or V) stage
   constexpr int IPW = NI / NW;           // of them per wave
-  constexpr int NKS = D / 16;
-  constexpr int KV_BYTES = S * 2 * TB > 51200 ? S * 2 * TB : 51200;  // also the groups' exchange area
+  constexpr int NKS = D / 32;
+  constexpr int KV_BYTES = S * 2 * TB > kOwnXBytes ? S * 2 * TB : kOwnXBytes;  // also the exchange area
   static_assert(NI % NW == 0, "loads per wave");
   __shared__ __align__(16) char kv[KV_BYTES];
   __shared__ int32_t slot[kStreamCap];
   const uint32_t kv_lds = lds_addr(kv);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int jrow = lane & 31, half = lane >> 5;
+  const int r16 = lane & 15, g4 = lane >> 4;
   const int G = a.g;
   const int n_rh = a.batch * a.h_kv;
-  const int c = blockIdx.x / n_rh;  // chunk slowest: chunks past every request's keys exit together
-  const int rh = blockIdx.x - c * n_rh;
-  const int t = rh / a.h_kv;
-  const int h = rh - t * a.h_kv;
+  // Workgroup order. The hardware hands out workgroups in id order, round-robin over the
+  // XCDs and their shader engines, and waits for room on the next one's engine: work items
+  // that exit at once must come in contiguous runs, not at a fixed stride (interleaving
+  // one live item with three exiting ones put every live one on one engine in four and
+  // measured 2x slower). Rows of n_rh ids, one chunk index per row, heads of a request
+  // together. With the host's order (requests by descending own keys): the last chunk
+  // index first, so that the rows whose live items are the long requests' chunks (a
+  // prefix of each row) start first and the last row ends with the shortest requests.
+  // Without it: chunk 0 first, in batch order.
+  const int row_i = blockIdx.x / n_rh;
+  const int in_row = blockIdx.x - row_i * n_rh;
+  const bool ordered = ord.n == a.batch;
+  const int c = ordered ? a.n_chunk - 1 - row_i : row_i;
+  const int rank = in_row / a.h_kv;
+  const int h = in_row - rank * a.h_kv;
+  const int t = ordered ? (int)ord.req[rank] : rank;
+  const int rh = t * a.h_kv + h;
 
   const int rb0 = t * G / a.bm;
   const BlockMeta meta = block_meta_load(a, rb0, lane);
-  const bool row_ok = jrow < G;
-  bf16x8 qf[NKS];
+  const bool row_ok = r16 < G;
+  bf16x8 qf[NKS];  // B operand: query head r16, dims 32*ks + 8*g4 .. +8
   {
-    const __bf16* qp =
-        reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? jrow : 0)) * D;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? r16 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + g4 * 8);
       qf[ks] = row_ok ? v : bf16x8{};
     }
   }
@@ -2544,9 +2580,9 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
     }
   };
 
-  f32x16 acc[D / 32];
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
 
   for (int j = 0; j < S - 1 && j < n_tiles; ++j) issue(j);
@@ -2562,51 +2598,55 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a) {
     const char* kt = kv + (i % S) * 2 * TB;
     const char* vt = kt + TB;
     const int cnt = min(TK, n - i * TK);
-    f32x16 sc = f32x16{};
+    f32x4 sc[2];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, jrow, ks, half), qf[ks], sc, 0, 0, 0);
-    // register r holds key 8*(r/4) + 4*half + r%4 of the stage, for this lane's row
+    for (int kh = 0; kh < 2; ++kh) {
+      sc[kh] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        sc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_frag16(kt, kh, ks, lane), qf[ks], sc[kh], 0, 0, 0);
+    }
+    // sc[kh][e] is the score of key 16*kh + 4*g4 + e of the stage for query head r16
     float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * half + (r & 3);
-      const float v = row_ok && key < cnt ? sc[r] : kNegInf;
-      sc[r] = v;
-      mx = fmaxf(mx, v);
-    }
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kh + 4 * g4 + e;
+        const float v = row_ok && key < cnt ? sc[kh][e] : kNegInf;
+        sc[kh][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
       m_run = m_new;
     }
     const float neg_m = m_run == kNegInf ? 0.f : -m_run;
     float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
-      sc[r] = pv;
-      psum += pv;
-    }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
-    bf16x8 pb[2];
+    bf16x8 pb;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+      for (int e = 0; e < 4; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][e], a.scale_log2, neg_m));
+        psum += pv;
+        pb[kh * 4 + e] = (__bf16)pv;
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, 0, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+    for (int dt = 0; dt < D / 16; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag16(vt, dt, lane), pb, acc[dt], 0, 0, 0);
   }
   __syncthreads();  // the exchange below overwrites the ring
-  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wave, lane, jrow, half, row_ok, t, h, rh, c, n_act, n_rh);
+  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wave, lane, row_ok, t, h, rh, c, n_act, n_rh);
 }
 
 // ------------------------------------------------------------------ host side
@@ -2740,7 +2780,7 @@ static rax_status launch_attn(AttnArgs& a, Shape s, hipStream_t st, const Append
 }
 
 template <typename T, int D, bool kDecode>
-static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const AppendJob* ap) {
+static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const AppendJob* ap, const OwnOrder* ord) {
   rax_status rc = launch_attn<T, D, kDecode>(a, s, st, ap);
   if (rc != RAX_OK) return rc;
   if constexpr (kDecode) {
@@ -2770,8 +2810,10 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
     if (a.shared_only && a.own_fused == 2) {
       if constexpr (sizeof(T) == 2 && D == 128) {
         const int64_t items = (int64_t)a.batch * a.h_kv * a.n_chunk;
-        if (items > INT32_MAX) return RAX_EINVAL;
-        hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a);
+        if (items > INT32_MAX || a.g > 16) return RAX_EINVAL;  // one 16-wide tile of query heads
+        static const OwnOrder none{};
+        hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a,
+                           ord && ord->n == a.batch ? *ord : none);
         rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
         if (rc != RAX_OK) return rc;
       } else {
@@ -2785,13 +2827,13 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
 
 template <bool kDecode>
 static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_t st,
-                           const AppendJob* ap = nullptr) {
+                           const AppendJob* ap = nullptr, const OwnOrder* ord = nullptr) {
   if (dt == RAX_BF16) {
-    if (d == 128) return launch_shape<__bf16, 128, kDecode>(a, s, st, ap);
-    if (d == 64) return launch_shape<__bf16, 64, kDecode>(a, s, st, ap);
+    if (d == 128) return launch_shape<__bf16, 128, kDecode>(a, s, st, ap, ord);
+    if (d == 64) return launch_shape<__bf16, 64, kDecode>(a, s, st, ap, ord);
   } else {
-    if (d == 128) return launch_shape<float, 128, kDecode>(a, s, st, ap);
-    if (d == 64) return launch_shape<float, 64, kDecode>(a, s, st, ap);
+    if (d == 128) return launch_shape<float, 128, kDecode>(a, s, st, ap, ord);
+    if (d == 64) return launch_shape<float, 64, kDecode>(a, s, st, ap, ord);
   }
   return RAX_EINVAL;
 }
@@ -2986,6 +3028,7 @@ DecodeHint raxk::decode_hint(const int32_t* len, const int32_t* shared_len, int3
   const int32_t per_block = 64 / (h_q / h_kv);  // requests per 64-row block
   const int64_t cap = 4 * (((int64_t)max_seq_len + BN - 1) / BN);  // as decode_layout's run_cap
   int64_t most = 0, own = 0;
+  std::vector<int64_t> own_r(static_cast<size_t>(batch), 0);
   for (int32_t b0 = 0; b0 < batch; b0 += per_block) {
     const int32_t b1 = std::min(batch, b0 + per_block);
     // the block rule: lengths after the append minus one (len here), hints to the predecessor
@@ -3012,13 +3055,23 @@ DecodeHint raxk::decode_hint(const int32_t* len, const int32_t* shared_len, int3
           start = L1;
         }
       }
-      for (int32_t r = i; r < j; ++r) own = std::max<int64_t>(own, (int64_t)len[r] + 1 - start);
+      for (int32_t r = i; r < j; ++r) {
+        own_r[r] = (int64_t)len[r] + 1 - start;
+        own = std::max<int64_t>(own, own_r[r]);
+      }
       i = j;
     }
     most = std::max(most, (L0 + BN - 1) / BN + extra);
   }
   hint.tiles = (int32_t)std::min<int64_t>(most, 1 << 24);
   hint.own = (int32_t)std::min<int64_t>(std::max<int64_t>(own, 0), 1 << 30);
+  if (batch <= kAppendMax) {
+    std::vector<int32_t> ord(static_cast<size_t>(batch));
+    std::iota(ord.begin(), ord.end(), 0);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return own_r[x] > own_r[y]; });
+    for (int32_t i = 0; i < batch; ++i) hint.order.req[i] = (uint16_t)ord[i];
+    hint.order.n = batch;
+  }
   return hint;
 }
 
@@ -3093,7 +3146,7 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
     }
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
-  return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap);
+  return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap, &hint.order);
 }
 
 // ---- decode attention that allocates nothing: for callers that cannot allocate device

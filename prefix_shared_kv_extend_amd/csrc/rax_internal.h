@@ -37,9 +37,17 @@ bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, ra
 // then read from the job, not from memory, by that kernel).
 // What the host knows of a decode batch from host copies of its lengths and hints
 // (decode_hint); zeros: nothing, the layout follows the longest sequence.
+// Dispatch order of the own-part workgroups (own_stream_kernel): requests by descending own
+// keys, each request's chunks together, so that the longest start first and the shortest
+// fill the end of the launch. n = 0 (or n != batch): batch order.
+struct OwnOrder {
+  int32_t n = 0;
+  uint16_t req[kAppendMax];
+};
 struct DecodeHint {
   int32_t tiles = 0;  // the most 64-key tiles the shared-prefix part of any row block computes
   int32_t own = 0;    // the most own keys of any request (past its block's or run's shared keys)
+  OwnOrder order;     // requests by descending own keys (batch <= kAppendMax)
 };
 
 // rax_decode_attention, with an optional append carried by its first kernel (seq_len is
