@@ -636,7 +636,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
             s[rt][r] = v;
             mx = fmaxf(mx, v);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+          mx = max_xor32(mx) * a.scale_log2;
           // Lazy rescale: the reference maximum of a row moves only when some row of the
           // wave sees a score more than 2^kLazy above its reference (also on the first
           // keys, reference -inf). In between, probabilities are up to 2^kLazy; l, acc
@@ -658,7 +658,7 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
             s[rt][r] = p;
             psum += p;
           }
-          psum += __shfl_xor(psum, 32);
+          psum = sum_xor32(psum);
           l_run[rt] += psum;
         }
 
@@ -1025,7 +1025,7 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    mx = max_xor32(mx) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -1042,7 +1042,7 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
       sc[r] = pv;
       psum += pv;
     }
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(psum);
     l_run += psum;
     bf16x8 pb[2];
 #pragma unroll
@@ -2153,7 +2153,7 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
         sc[r] = v;
         mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      mx = max_xor32(mx) * a.scale_log2;
       // lazy rescale, as in attn_kernel: the reference moves only when a row's maximum
       // exceeds it by more than 2^kLazy
       if (__any(mx > m_run + kLazy)) {
@@ -2172,7 +2172,7 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
         sc[r] = p;
         psum += p;
       }
-      psum += __shfl_xor(psum, 32);
+      psum = sum_xor32(psum);
       l_run += psum;
       bf16x8 pb[2];
 #pragma unroll
@@ -2617,8 +2617,7 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
         sc[kh][e] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    mx = max_xor16(max_xor32(mx)) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -2638,8 +2637,7 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
         psum += pv;
         pb[kh * 4 + e] = (__bf16)pv;
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor16(sum_xor32(psum));
     l_run += psum;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)

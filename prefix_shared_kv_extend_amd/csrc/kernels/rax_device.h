@@ -55,6 +55,41 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Cross-lane exchanges in the VALU (gfx950): v_permlane32_swap swaps lanes 32..63 of its
+// first register with lanes 0..31 of its second, v_permlane16_swap the odd 16-lane rows of
+// its first register with the even rows of its second. Written as asm: this toolchain's
+// builtins hand back the first register for both results. The s_nops pad the hazards
+// between a VALU write and the swap's read, and the swap's write and a later read.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// x combined (max or sum) with its value in lane l ^ 32, and in lane l ^ 16: after a swap
+// of two copies of x, lane l of the two registers holds x[l] and x[l ^ 32] (or ^ 16), in
+// some order.
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  return a + b;
+}
+
 // Wave-uniform copy (kept in an SGPR) of a value that is the same in every lane.
 __device__ __forceinline__ uint32_t uni32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
