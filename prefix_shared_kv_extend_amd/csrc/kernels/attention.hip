@@ -2307,62 +2307,18 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
   }
 }
 
-// End of an own-part workgroup with query-head groups (bf16, D = 128, 4 waves as four key
-// groups, the g query heads as rows of one 16-row tile; lane l holds row l % 16, dims
-// dt*16 + 4*(l/16) + {0..3} of acc[dt]): the groups' (m, l, acc) combine through LDS (xbuf:
-// at least kOwnXBytes, free when called), wave w finishing dims [32w, 32w + 32); then either
-// the request's only own chunk is merged in place with the shared part's split partials and
+// End of an own-part workgroup with query-head groups (bf16, D = 128): wave w holds dims
+// [32w, 32w + 32) of the chunk's output for query head l % 16 (lane l: dims 32w + 16j +
+// 4*(l/16) + {0..3} in o[j]) with the running (m, l), the same in every wave. Either the
+// request's only own chunk is merged in place with the shared part's split partials and
 // O written, or the chunk's partial goes to the workspace in own_kernel's layout.
-constexpr int kOwnXBytes = (8 * 4 * 4 + 4 * 2) * 64 * (int)sizeof(float);
 template <int D>
-__device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbuf, const f32x4 (&acc)[D / 16],
-                                                    float m_run, float l_run, int wkey, int lane, bool row_ok,
-                                                    int t, int h, int rh, int c, int n_act, int n_rh) {
-  constexpr int NKG = 4;
-  static_assert(D == 128, "four 32-dim quarters, one per key group");
+__device__ __forceinline__ void own_chunk_epilogue(const AttnArgs& a, const f32x4 (&o)[2], float m, float l,
+                                                   int wq, int lane, bool row_ok, int t, int h, int rh, int c,
+                                                   int n_act, int n_rh) {
+  static_assert(D == 128, "four 32-dim quarters, one per wave");
   const int G = a.g;
   const int r16 = lane & 15, g4 = lane >> 4;
-  float* xs = reinterpret_cast<float*>(xbuf);  // [dt][group][4][64]
-  float* xml = xs + (D / 16) * NKG * 4 * 64;   // [group][m, l][64]
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    if ((dt >> 1) == wkey) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) xs[((dt * NKG + wkey) * 4 + e) * 64 + lane] = acc[dt][e];
-  }
-  xml[(wkey * 2 + 0) * 64 + lane] = m_run;
-  xml[(wkey * 2 + 1) * 64 + lane] = l_run;
-  __syncthreads();
-  float mk[NKG], lk[NKG];
-  float m = kNegInf;
-#pragma unroll
-  for (int k = 0; k < NKG; ++k) {
-    mk[k] = xml[(k * 2 + 0) * 64 + lane];
-    lk[k] = xml[(k * 2 + 1) * 64 + lane];
-    m = fmaxf(m, mk[k]);
-  }
-  float l = 0.f;
-  f32x4 o[2] = {f32x4{}, f32x4{}};
-  if (m != kNegInf) {
-#pragma unroll
-    for (int k = 0; k < NKG; ++k) {
-      const float ak = mk[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mk[k] - m);
-      l += lk[k] * ak;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int dt = 2 * wkey + j;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // acc[dt] with dt chosen at run time would go through scratch: select instead
-          float mine = 0.f;
-#pragma unroll
-          for (int q = 0; q < D / 16; ++q)
-            if (q == dt) mine = acc[q][e];
-          o[j][e] += (k == wkey ? mine : xs[((dt * NKG + k) * 4 + e) * 64 + lane]) * ak;
-        }
-      }
-    }
-  }
   if (!row_ok) return;
   if (n_act == 1) {
     // the request's only own chunk: merge here with the shared part's split partials of
@@ -2396,7 +2352,7 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
       const float* pa = sh_acc + (int64_t)sp * a.bm * D;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wkey * 32 + 16 * j + 4 * g4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(pa + wq * 32 + 16 * j + 4 * g4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) fin[j][e] += w != 0.f ? w * x[e] : 0.f;
       }
@@ -2405,7 +2361,7 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
     const int64_t obase = ((int64_t)t * a.h_q + h * G + r16) * D;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int d0 = wkey * 32 + 16 * j + 4 * g4;
+      const int d0 = wq * 32 + 16 * j + 4 * g4;
       if (a.o_bf16)
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
             bf16x4{(__bf16)(fin[j][0] * inv), (__bf16)(fin[j][1] * inv), (__bf16)(fin[j][2] * inv),
@@ -2422,9 +2378,9 @@ __device__ __forceinline__ void own_groups_epilogue(const AttnArgs& a, char* xbu
     float* wacc = a.ws_own + (item * G + r16) * D;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4*>(wacc + wkey * 32 + 16 * j + 4 * g4));
+      __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4*>(wacc + wq * 32 + 16 * j + 4 * g4));
   }
-  if (wkey == 0 && g4 == 0) {
+  if (wq == 0 && g4 == 0) {
     float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + r16) * 2;
     __builtin_nontemporal_store(m, wml);
     __builtin_nontemporal_store(l, wml + 1);
@@ -2460,16 +2416,23 @@ __device__ __forceinline__ bf16x8 vt_frag16(const char* vt, int dt, int lane) {
 // first (one round of loads); then the chunk's keys stream through a ring of S stages of
 // 32 keys (8 KB of K and 8 KB of V each) filled straight from global memory: while stage i
 // is computed, the loads of the next S - 1 stages are in flight. One barrier per stage.
-// The four waves are four key groups: wave w computes stages i = w (mod 4) and the groups
-// combine at the end (own_groups_epilogue). A stage is S^T = K Q^T and O^T = V^T P^T on
-// 16x16x32 MFMA with the g <= 16 query heads as the columns of one 16-wide tile (columns
-// past g masked): the 16-row shape does half the matrix work of a 32-row one, so the one
-// wave that computes a stage holds the barrier half as long (per-workgroup timestamps of
-// the 32-row form: ~1 us per stage, about the stage's whole time). Keys past the chunk in
-// its last stage read the chunk's first slot (a key it attends, so finite) and are masked.
-constexpr int kStreamCap = 2048;  // most keys per own chunk of own_stream_kernel
+// A stage is S^T = K Q^T and O^T = V^T P^T on 16x16x32 MFMA, the g <= 16 query heads as
+// the columns of one 16-wide tile (columns past g masked). Every wave computes every
+// stage's scores and softmax (the same instructions on the same data, so the same values
+// in every wave) and O^T for its own quarter of the dims: the stage's critical path is
+// one wave's QK^T, softmax and a quarter of PV, with no end-of-chunk exchange between
+// waves. (Per-workgroup timestamps of the form where one wave computed a whole stage
+// while the others waited at the barrier: ~0.8 us per stage with the GPU nearly idle,
+// against ~0.37 us for the loads alone.) Keys past the chunk in its last stage read the
+// chunk's first slot (a key it attends, so finite) and are masked.
+constexpr int kStreamCap = 1024;  // most keys per own chunk of own_stream_kernel
 constexpr int kStreamTK = 32;     // keys per stage
-constexpr int kStreamStages = 4;
+// Two stages (one in flight while one is computed; 36 KB of LDS with the slot ids, four
+// workgroups per CU) measured faster than three (three per CU) or four (two per CU):
+// multi-turn decode 221.6, 223.0 and 224.3 us per call; six stages (one per CU) 262.7 us.
+// With more workgroups per CU, one's start (metadata, slot ids, first stage: ~5 us) runs
+// while the others stream.
+constexpr int kStreamStages = 2;
 
 template <int D, int S>
 __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder ord) {
@@ -2483,8 +2446,9 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
   constexpr int NI = TK / RPI;           // instructions per K (or V) stage
   constexpr int IPW = NI / NW;           // of them per wave
   constexpr int NKS = D / 32;
-  constexpr int KV_BYTES = S * 2 * TB > kOwnXBytes ? S * 2 * TB : kOwnXBytes;  // also the exchange area
+  constexpr int KV_BYTES = S * 2 * TB;
   static_assert(NI % NW == 0, "loads per wave");
+  static_assert(D == 32 * NW, "a 32-dim quarter per wave");
   __shared__ __align__(16) char kv[KV_BYTES];
   __shared__ int32_t slot[kStreamCap];
   const uint32_t kv_lds = lds_addr(kv);
@@ -2580,9 +2544,7 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
     }
   };
 
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
+  f32x4 acc[2] = {f32x4{}, f32x4{}};  // this wave's dims 32*wave + 16*j + 4*g4 + e
   float m_run = kNegInf, l_run = 0.f;
 
   for (int j = 0; j < S - 1 && j < n_tiles; ++j) issue(j);
@@ -2594,7 +2556,6 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
     else wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");
     if (i + S - 1 < n_tiles) issue(i + S - 1);
-    if ((i & (NW - 1)) != wave) continue;
     const char* kt = kv + (i % S) * 2 * TB;
     const char* vt = kt + TB;
     const int cnt = min(TK, n - i * TK);
@@ -2623,7 +2584,7 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+      for (int j = 0; j < 2; ++j) acc[j] *= alpha;
       m_run = m_new;
     }
     const float neg_m = m_run == kNegInf ? 0.f : -m_run;
@@ -2640,11 +2601,10 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
     psum = sum_xor16(sum_xor32(psum));
     l_run += psum;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag16(vt, dt, lane), pb, acc[dt], 0, 0, 0);
+    for (int j = 0; j < 2; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag16(vt, 2 * wave + j, lane), pb, acc[j], 0, 0, 0);
   }
-  __syncthreads();  // the exchange below overwrites the ring
-  own_groups_epilogue<D>(a, kv, acc, m_run, l_run, wave, lane, row_ok, t, h, rh, c, n_act, n_rh);
+  own_chunk_epilogue<D>(a, acc, m_run, l_run, wave, lane, row_ok, t, h, rh, c, n_act, n_rh);
 }
 
 // ------------------------------------------------------------------ host side
