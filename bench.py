@@ -345,7 +345,7 @@ def headline(args, dev):
 def roofline_of(cold, traffic_path):
     ext, dec = cold["extend"], cold["decode"]
     if ext["us_per_step"] >= dec["us_per_step"]:
-        roof = {"kernel": "extend attention (attn_kernel, bf16, D=128)", "bound": "mfma",
+        roof = {"kernel": "extend attention (extend_kernel, bf16, D=128)", "bound": "mfma",
                 "achieved": ext["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ext["frac_mfma_peak"], "launches_per_step": ext["calls"],
                 "avg_launch_us": ext["us_per_step"] / ext["calls"]}
@@ -780,6 +780,26 @@ def summarize_trace(csv_path):
     win = w1 - w0
     print(f"\nWindow of the hot path's kernels: {win / 1e6:.3f} ms; kernels busy {busy / 1e6:.3f} ms; "
           f"GPU idle {(win - busy) / 1e6:.3f} ms ({(win - busy) / win:.1%}).")
+    # per launch of each attention entry point (its first kernel and the own-part and merge
+    # kernels after it, in dispatch order): the span from the first kernel's start to the
+    # last one's end, comparable with the HIP-event time of a launch
+    spans, cur = {}, None
+    for s, e, k in rows:
+        entry = next((en for en, first in ENTRY_FIRST.items() if first in k), None)
+        if entry is not None:
+            cur = entry
+            spans.setdefault(cur, []).append([s, e, e - s])
+        elif cur is not None and any(r in k for r in ENTRY_REST):
+            sp = spans[cur][-1]
+            sp[1] = max(sp[1], e)
+            sp[2] += e - s
+        else:
+            cur = None
+    if spans:
+        print("\n| entry point | launches | mean launch span us | mean kernel time per launch us |\n|---|---|---|---|")
+        for entry, sp in spans.items():
+            n = len(sp)
+            print(f"| {entry} | {n} | {sum(b - a for a, b, _ in sp) / n / 1e3:.2f} | {sum(t for _, _, t in sp) / n / 1e3:.2f} |")
 
 
 # ------------------------------------------------------------------ main

@@ -1019,12 +1019,16 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
     }
   };
 
-  // the online softmax of one 32-key half (sub) of a tile's (masked) scores, then
-  // O^T += V^T P^T
-  auto half_step = [&](const uint32_t (&va)[D / 32], f32x16& sc, int sub) {
+  // the online softmax of a tile's (masked) scores, both 32-key halves against one running
+  // maximum (one wave-uniform branch per tile for the lazy rescale), then O^T += V^T P^T:
+  // the first half's PV MFMAs are issued before the second half's probabilities are
+  // computed, so that the VALU work of one overlaps the other's MFMAs in the same wave
+  auto tile_step = [&](const uint32_t (&va)[D / 32], f32x16 (&sc)[2]) {
     float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
     mx = max_xor32(mx) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
@@ -1037,24 +1041,24 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
     const float neg_m = m_run == kNegInf ? 0.f : -m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
-      sc[r] = pv;
-      psum += pv;
-    }
-    psum = sum_xor32(psum);
-    l_run += psum;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 pb[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_at(lds_ptr(va[dt]) + sub * 8192 + kh * 4096),
-                                                          pb[kh], acc[dt], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][kh * 8 + e], a.scale_log2, neg_m));
+          psum += pv;
+          pb[kh][e] = (__bf16)pv;
+        }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_at(lds_ptr(va[dt]) + sub * 8192 + kh * 4096),
+                                                            pb[kh], acc[dt], 0, 0, 0);
+    }
+    l_run += sum_xor32(psum);
   };
 
   for (int seg0 = tb; seg0 < te; seg0 += kExtSeg) {
@@ -1182,8 +1186,7 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
             }
         }
       }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) half_step(va, sall[sub], sub);
+      tile_step(va, sall);
     }
     __syncthreads();  // the next segment rewrites the table, the rows and the buffers
   }
