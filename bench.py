@@ -802,6 +802,35 @@ def summarize_trace(csv_path):
             print(f"| {entry} | {n} | {sum(b - a for a, b, _ in sp) / n / 1e3:.2f} | {sum(t for _, _, t in sp) / n / 1e3:.2f} |")
 
 
+def achievable_peaks(dev):
+    """Measured ceilings beside the published peaks: a plain device copy (4 GiB read and
+    4 GiB written, through torch) and a bf16 GEMM (8192^3, through torch and hipBLASLt).
+    Median of 10 timed runs after 3 untimed ones."""
+    import torch
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    src = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    t_gemm = timed(lambda: torch.mm(a, b))
+    return {"copy_gbs": 2 * (1 << 32) / t_copy / 1e9, "copy_frac_hbm_peak": 2 * (1 << 32) / t_copy / 1e9 / HBM_PEAK_GBS,
+            "gemm_bf16_tflops": 2 * n ** 3 / t_gemm / 1e12,
+            "gemm_frac_mfma_peak": 2 * n ** 3 / t_gemm / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -889,6 +918,7 @@ def main():
         out["scheduler"] = scheduler_ablation()
         out["host_tier"] = host_tier_measure(dev)
         out["qkv_projection"] = projection_measure(dev)
+        out["achievable_peaks"] = achievable_peaks(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(job, args.cpu_seconds)
     print(json.dumps(out), flush=True)
