@@ -780,6 +780,22 @@ def summarize_trace(csv_path):
     win = w1 - w0
     print(f"\nWindow of the hot path's kernels: {win / 1e6:.3f} ms; kernels busy {busy / 1e6:.3f} ms; "
           f"GPU idle {(win - busy) / 1e6:.3f} ms ({(win - busy) / win:.1%}).")
+    # idle gaps (no kernel running) by the kernel that ends them, and by tenth of the window
+    by_next, by_tenth, last_end = {}, [0] * 10, None
+    for s, e, k in rows:
+        if e <= w0 or s >= w1:
+            continue
+        if last_end is not None and s > last_end:
+            gap = s - last_end
+            name = k.split("(")[0].split("<")[0].replace("void ", "")[-40:]
+            by_next[name] = by_next.get(name, 0) + gap
+            by_tenth[min(9, int((last_end - w0) * 10 // win))] += gap
+        last_end = e if last_end is None else max(last_end, e)
+    if by_next:
+        print("\n| idle gap ended by | ms |\n|---|---|")
+        for name, g in sorted(by_next.items(), key=lambda kv: -kv[1])[:8]:
+            print(f"| `{name}` | {g / 1e6:.3f} |")
+        print("\nIdle ms by tenth of the window: " + ", ".join(f"{g / 1e6:.1f}" for g in by_tenth))
     # per launch of each attention entry point (its first kernel and the own-part and merge
     # kernels after it, in dispatch order): the span from the first kernel's start to the
     # last one's end, comparable with the HIP-event time of a launch
