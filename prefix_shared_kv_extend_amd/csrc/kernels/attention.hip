@@ -2469,13 +2469,29 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
   // index first, so that the rows whose live items are the long requests' chunks (a
   // prefix of each row) start first and the last row ends with the shortest requests.
   // Without it: chunk 0 first, in batch order.
-  const int row_i = blockIdx.x / n_rh;
-  const int in_row = blockIdx.x - row_i * n_rh;
   const bool ordered = ord.n == a.batch;
-  const int c = ordered ? a.n_chunk - 1 - row_i : row_i;
-  const int rank = in_row / a.h_kv;
-  const int h = in_row - rank * a.h_kv;
-  const int t = ordered ? (int)ord.req[rank] : rank;
+  int c, h, t, n_host = 0;
+  if (ordered) {
+    // the host's work list: item blockIdx / h_kv of the list, KV head blockIdx % h_kv;
+    // the item's request by binary search over the cumulative counts (wave-uniform)
+    const int item = (int)(blockIdx.x / (unsigned)a.h_kv);
+    h = (int)(blockIdx.x - (unsigned)item * a.h_kv);
+    int lo = 0, hi = ord.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)ord.cum[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    c = item - ord.cum[lo];
+    n_host = ord.cum[lo + 1] - ord.cum[lo];
+    t = ord.req[lo];
+  } else {
+    const int row_i = blockIdx.x / n_rh;
+    const int in_row = blockIdx.x - row_i * n_rh;
+    c = row_i;
+    t = in_row / a.h_kv;
+    h = in_row - t * a.h_kv;
+  }
   const int rh = t * a.h_kv + h;
 
   const int rb0 = t * G / a.bm;
@@ -2496,6 +2512,8 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
   const int end = __builtin_amdgcn_readlane(meta.len, rl);
   int first, per;
   const int n_act = own_chunks(a, row_t, end, L, first, per);
+  // the host's item count bounds the kernel's (else chunks past it would be missed)
+  if (ordered && c == n_host - 1 && n_act > n_host && tid == 0) flag_error(RAX_DEVERR_ROW);
   if (c >= n_act) return;  // the same for the whole workgroup
   const int start = first + c * per;
   int stop = min(start + per, end);
@@ -2770,11 +2788,13 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
     }
     if (a.shared_only && a.own_fused == 2) {
       if constexpr (sizeof(T) == 2 && D == 128) {
-        const int64_t items = (int64_t)a.batch * a.h_kv * a.n_chunk;
-        if (items > INT32_MAX || a.g > 16) return RAX_EINVAL;  // one 16-wide tile of query heads
         static const OwnOrder none{};
-        hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a,
-                           ord && ord->n == a.batch ? *ord : none);
+        const bool ordered = ord && ord->n == a.batch;
+        const int64_t items = ordered ? (int64_t)ord->cum[ord->n] * a.h_kv : (int64_t)a.batch * a.h_kv * a.n_chunk;
+        if (items > INT32_MAX || a.g > 16) return RAX_EINVAL;  // one 16-wide tile of query heads
+        if (items > 0)
+          hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a,
+                             ordered ? *ord : none);
         rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
         if (rc != RAX_OK) return rc;
       } else {
@@ -3030,7 +3050,10 @@ DecodeHint raxk::decode_hint(const int32_t* len, const int32_t* shared_len, int3
     std::vector<int32_t> ord(static_cast<size_t>(batch));
     std::iota(ord.begin(), ord.end(), 0);
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return own_r[x] > own_r[y]; });
-    for (int32_t i = 0; i < batch; ++i) hint.order.req[i] = (uint16_t)ord[i];
+    for (int32_t i = 0; i < batch; ++i) {
+      hint.order.req[i] = (uint16_t)ord[i];
+      hint.len_after[i] = len[i] + 1;
+    }
     hint.order.n = batch;
   }
   return hint;
@@ -3107,6 +3130,19 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
     }
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
+  if (hint.order.n == batch && l.own_mode == 2) {
+    // the own part's work list: per request, at most the chunks its length after the
+    // append allows (its own keys are at most that length)
+    int32_t acc_items = 0;
+    for (int32_t i = 0; i < batch; ++i) {
+      hint.order.cum[i] = (uint16_t)acc_items;
+      const int64_t up = std::max<int64_t>(hint.len_after[hint.order.req[i]], 0);
+      acc_items += (int32_t)std::min<int64_t>(l.n_chunk, std::max<int64_t>(1, (up + l.own_min - 1) / l.own_min));
+    }
+    hint.order.cum[batch] = (uint16_t)acc_items;  // <= 256 x 64
+  } else {
+    hint.order.n = 0;
+  }
   return dispatch<true>(a, dt, d, s, (hipStream_t)stream, ap, &hint.order);
 }
 
