@@ -796,6 +796,31 @@ def summarize_trace(csv_path):
         for name, g in sorted(by_next.items(), key=lambda kv: -kv[1])[:8]:
             print(f"| `{name}` | {g / 1e6:.3f} |")
         print("\nIdle ms by tenth of the window: " + ", ".join(f"{g / 1e6:.1f}" for g in by_tenth))
+    # idle inside runs of 5 consecutive decode launches (no extend between them), from the
+    # first one's start to the fifth one's end: the median and the worst over the job
+    starts = [i for i, (_, _, k) in enumerate(rows) if ENTRY_FIRST["decode"] in k]
+    runs = []
+    for j in range(len(starts) - 5):
+        a_i, b_i = starts[j], starts[j + 5]
+        if any(ENTRY_FIRST["extend"] in rows[x][2] for x in range(a_i, b_i)):
+            continue
+        seg = rows[a_i:b_i]
+        t0, t1 = seg[0][0], max(e for _, e, _ in seg)
+        busy5, cs, ce = 0, None, None
+        for s_, e_, _ in seg:
+            if ce is None or s_ > ce:
+                if ce is not None:
+                    busy5 += ce - cs
+                cs, ce = s_, e_
+            else:
+                ce = max(ce, e_)
+        busy5 += ce - cs
+        runs.append((t1 - t0 - busy5, t1 - t0))
+    if runs:
+        idle5 = sorted(r[0] for r in runs)
+        print(f"\nRuns of 5 consecutive decode launches with no extend between them: {len(runs)}; GPU idle "
+              f"inside a run: median {idle5[len(idle5) // 2] / 1e3:.1f} us, worst {idle5[-1] / 1e3:.1f} us "
+              f"(median run {sorted(r[1] for r in runs)[len(runs) // 2] / 1e3:.0f} us).")
     # per launch of each attention entry point (its first kernel and the own-part and merge
     # kernels after it, in dispatch order): the span from the first kernel's start to the
     # last one's end, comparable with the HIP-event time of a launch
