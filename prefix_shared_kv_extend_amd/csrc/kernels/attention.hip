@@ -3052,7 +3052,7 @@ DecodeHint raxk::decode_hint(const int32_t* len, const int32_t* shared_len, int3
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return own_r[x] > own_r[y]; });
     for (int32_t i = 0; i < batch; ++i) {
       hint.order.req[i] = (uint16_t)ord[i];
-      hint.len_after[i] = len[i] + 1;
+      hint.own_keys[i] = (int32_t)std::min<int64_t>(std::max<int64_t>(own_r[i], 0), 1 << 30);
     }
     hint.order.n = batch;
   }
@@ -3131,13 +3131,12 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   }
   if (ap && !(l.split_decode && dt == RAX_BF16 && d == 128)) return RAX_EINVAL;  // see decode_folds_append
   if (hint.order.n == batch && l.own_mode == 2) {
-    // the own part's work list: per request, at most the chunks its length after the
-    // append allows (its own keys are at most that length)
+    // the own part's work list: per request, the chunks of its own keys (own_chunks)
     int32_t acc_items = 0;
     for (int32_t i = 0; i < batch; ++i) {
       hint.order.cum[i] = (uint16_t)acc_items;
-      const int64_t up = std::max<int64_t>(hint.len_after[hint.order.req[i]], 0);
-      acc_items += (int32_t)std::min<int64_t>(l.n_chunk, std::max<int64_t>(1, (up + l.own_min - 1) / l.own_min));
+      const int64_t own = hint.own_keys[hint.order.req[i]];
+      acc_items += (int32_t)std::min<int64_t>(l.n_chunk, std::max<int64_t>(1, (own + l.own_min - 1) / l.own_min));
     }
     hint.order.cum[batch] = (uint16_t)acc_items;  // <= 256 x 64
   } else {

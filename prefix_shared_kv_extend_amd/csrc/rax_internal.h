@@ -38,11 +38,11 @@ bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, ra
 // What the host knows of a decode batch from host copies of its lengths and hints
 // (decode_hint); zeros: nothing, the layout follows the longest sequence.
 // Work list of the own-part workgroups (own_stream_kernel), from host copies of the
-// lengths: requests by descending own keys, each request's chunks (and in a chunk its KV
-// heads) together, so that the longest start first and the shortest fill the end of the
-// launch. Request req[i] gets cum[i + 1] - cum[i] chunk items, an upper bound of the
-// chunks the kernel finds (from its length after the step's append, which bounds its own
-// keys); items past the kernel's count exit at once. n = 0 (or n != batch): none, the
+// lengths and hints: requests by descending own keys, each request's chunks (and in a
+// chunk its KV heads) together, so that the longest start first and the shortest fill the
+// end of the launch. Request req[i] gets cum[i + 1] - cum[i] chunk items, counted from its
+// own keys by the kernels' rule (decode_hint); the kernel flags a request whose own keys
+// need more, and items past its count exit at once. n = 0 (or n != batch): none, the
 // kernel covers n_chunk items per request in batch order.
 struct OwnOrder {
   int32_t n = 0;
@@ -53,7 +53,7 @@ struct DecodeHint {
   int32_t tiles = 0;  // the most 64-key tiles the shared-prefix part of any row block computes
   int32_t own = 0;    // the most own keys of any request (past its block's or run's shared keys)
   OwnOrder order;     // requests by descending own keys (batch <= kAppendMax); cum set at launch
-  int32_t len_after[kAppendMax];  // per request: its length after the step's append
+  int32_t own_keys[kAppendMax];  // per request: its own keys after the step's append
 };
 
 // rax_decode_attention, with an optional append carried by its first kernel (seq_len is
