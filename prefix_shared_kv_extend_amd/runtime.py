@@ -35,11 +35,21 @@ pinned copy.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+from operator import itemgetter
 
 import numpy as np
 import torch
 
 from . import _lib as L
+
+
+def _take(d: dict, keys) -> list:
+    """[d[k] for k in keys], looked up in C (itemgetter): the per-request tables are read
+    for whole batches of up to 256 requests on every batch change."""
+    if not keys:
+        return []
+    got = itemgetter(*keys)(d)
+    return list(got) if len(keys) > 1 else [got]
 
 
 @dataclass
@@ -114,18 +124,14 @@ class RadixRuntime:
     def _upload(self, parts: dict) -> dict:
         """One pinned host buffer -> one device copy; returns named int32 device views."""
         names = list(parts)
-        arrs = [np.ascontiguousarray(parts[k], dtype=np.int32).ravel() for k in names]
-        total = sum(a.size for a in arrs)
+        arrs = [np.asarray(parts[k], dtype=np.int32).reshape(-1) for k in names]
+        sizes = [a.size for a in arrs]
+        total = sum(sizes)
         host = torch.empty(max(total, 1), dtype=torch.int32, pin_memory=True)
-        hv = host.numpy()
-        off = 0
-        spans = {}
-        for k, a in zip(names, arrs):
-            hv[off: off + a.size] = a
-            spans[k] = (off, a.size)
-            off += a.size
+        if total:
+            np.concatenate(arrs, out=host.numpy()[:total])
         dev = host.to(self.device, non_blocking=True)
-        return {k: dev[o: o + n] for k, (o, n) in spans.items()}
+        return dict(zip(names, torch.split(dev[:total], sizes)))
 
     def _workspace(self, nbytes: int):
         if nbytes == 0:
@@ -239,13 +245,14 @@ class RadixRuntime:
     def end_extend(self, eb: ExtendBatch, prompts=None) -> None:
         """Insert every prompt; requests switch to the tree's copy of any duplicate slots."""
         rids, ip = eb.rids, eb.tok_indptr
-        rows = [self.row_of[r] for r in rids]
-        slots = np.concatenate([self.rows[row, : self.n_prompt[r]] for r, row in zip(rids, rows)]) \
+        rows = _take(self.row_of, rids)
+        n_prompt = _take(self.n_prompt, rids)
+        slots = np.concatenate([self.rows[row, :n] for row, n in zip(rows, n_prompt)]) \
             if rids else np.zeros(0, np.int32)
         # each walk starts where the request's prefix matched (its locked node): the
         # matched slots are the tree's already
-        tslots, existing, nodes = self.tree.insert_batch_from([self.node_of[r] for r in rids],
-                                                              [self.trusted_of[r] for r in rids], eb.tokens, slots, ip)
+        old = _take(self.node_of, rids)
+        tslots, existing, nodes = self.tree.insert_batch_from(old, _take(self.trusted_of, rids), eb.tokens, slots, ip)
         if self.log is not None:
             for i, rid in enumerate(rids):
                 self._log("insert", rid, int(existing[i]), int(nodes[i]))
@@ -258,12 +265,10 @@ class RadixRuntime:
             k = len(diff)
             dv = self._upload(dict(rows=fix_rows, start=pos, indptr=np.arange(k + 1), src=tslots[diff]))
             L.req_to_token_write(self.rtt, dv["rows"], dv["start"], dv["indptr"], dv["src"], k)
-        old = [self.node_of[r] for r in rids]
         self.tree.lock_ref_batch(nodes, +1)
         self.tree.lock_ref_batch(old, -1)
-        for i, rid in enumerate(rids):
-            self.node_of[rid] = int(nodes[i])
-            self.trusted_of[rid] = self.n_prompt[rid]   # duplicates switched to the tree's above
+        self.node_of.update(zip(rids, nodes.tolist()))
+        self.trusted_of.update(zip(rids, n_prompt))   # duplicates switched to the tree's above
         self._sync_decode_lengths()
         self._dec_cache = None
 
@@ -271,8 +276,7 @@ class RadixRuntime:
     def _sync_decode_lengths(self):
         """Write the decode batch's cached lengths back to the per-request table."""
         if self._dec_cache is not None:
-            for r, n in zip(self._dec_cache.key, self._dec_cache.lens.tolist()):
-                self.len_of[r] = n
+            self.len_of.update(zip(self._dec_cache.key, self._dec_cache.lens.tolist()))
 
     def begin_decode(self, rids) -> DecodeBatch:
         """Describe the next decode step of `rids` (one new token each): db.seq_len holds the
@@ -282,16 +286,16 @@ class RadixRuntime:
         ds = self._dec_cache
         if ds is None or ds.key != key:
             self._sync_decode_lengths()
-            req_rows = np.array([self.row_of[r] for r in rids], dtype=np.int32)
-            nodes = [self.node_of[r] for r in rids]
+            req_rows = np.array(_take(self.row_of, rids), dtype=np.int32)
+            nodes = _take(self.node_of, rids)
             hints = self.tree.lca_depths(nodes)
             inv = self._upload(dict(req_pool_idx=req_rows, shared_len=hints, seq_len=np.zeros(len(rids))))
-            lens = np.array([self.len_of[r] for r in rids], dtype=np.int32)
+            lens = np.array(_take(self.len_of, rids), dtype=np.int32)
             prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
                                                  self.v_pool, self.h_q, shared_len=inv["shared_len"],
                                                  shared_len_host=hints)
             ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0,
-                                                {r: i for i, r in enumerate(key)}, hints)
+                                                dict(zip(key, range(len(key)))), hints)
         seq_len = ds.lens + 1
         max_seq = ds.max_len + 1 if len(seq_len) else 0
         if max_seq > self.max_ctx:
@@ -337,16 +341,16 @@ class RadixRuntime:
                 raise ValueError("finish: tokens and slot row differ in length")
         ip = np.zeros(len(rids) + 1, dtype=np.int64)
         ip[1:] = np.cumsum([len(t) for t in toks])
-        slots = np.concatenate([self.rows[self.row_of[r], : self.len_of[r]] for r in rids])
+        rows, lens, locked = _take(self.row_of, rids), _take(self.len_of, rids), _take(self.node_of, rids)
+        slots = np.concatenate([self.rows[row, :n] for row, n in zip(rows, lens)])
         # from each request's locked node (its prompt's; the row holds the tree's slots up
         # to its trusted length)
-        tslots, existing, nodes = self.tree.insert_batch_from([self.node_of[r] for r in rids],
-                                                              [self.trusted_of[r] for r in rids],
+        tslots, existing, nodes = self.tree.insert_batch_from(locked, _take(self.trusted_of, rids),
                                                               np.concatenate(toks), slots, ip)
         if self.log is not None:
             for i, rid in enumerate(rids):
                 self._log("insert", rid, int(existing[i]), int(nodes[i]))
-        self.tree.lock_ref_batch([self.node_of[r] for r in rids], -1)
+        self.tree.lock_ref_batch(locked, -1)
         out = []
         for i, rid in enumerate(rids):
             self.free_rows.append(self.row_of.pop(rid))
