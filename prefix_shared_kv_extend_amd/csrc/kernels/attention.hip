@@ -94,6 +94,10 @@ struct AttnArgs {
   int32_t sh_small;           // 1: shared part with 4-wave workgroups, 2 tiles per round
   int32_t run_cap;            // split decode: most extra shared-part tiles per row block taken
                               // for deeper runs (block_runs); 0: none
+  int32_t* own_cnt;           // own_fold: finished own chunks per (request, KV head), zeroed
+                              // by the shared part's kernel; nullptr otherwise
+  int32_t own_fold;           // own_fused == 2: own_stream_kernel also merges the requests
+                              // with several own chunks (else merge_kernel does)
 };
 
 template <typename T, int D, int NW, int RT, int KS>
@@ -1828,7 +1832,8 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
     const int rl = (int)(t - rb * a.bm / a.g);  // request t's lane in its block's metadata
     n_own = own_chunks(a, (int)t, row_shared_len(a, block_meta_load(a, rb, lane), lane, rl), first, per);
   }
-  if (a.own_fused == 2 && n_own == 1) return;  // own_stream_kernel merged this row and wrote O
+  // own_stream_kernel merged this row and wrote O
+  if (a.own_fused == 2 && (n_own == 1 || (n_own > 1 && a.own_fold))) return;
   if (lane >= nsplit + n_own) my_l = 0.f;  // own chunks past n_own were not written
   float M = my_l > 0.f ? my_m : kNegInf;
 #pragma unroll
@@ -1955,6 +1960,11 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + half * 8);
       qf[ks] = row_ok ? v : bf16x8{};
     }
+  }
+
+  if (a.own_cnt) {  // the own part's chunk counters start at zero (this launch precedes it)
+    const int n_cnt = batch * a.h_kv;
+    for (int i = (int)blockIdx.x * NW * 64 + tid; i < n_cnt; i += (int)gridDim.x * NW * 64) a.own_cnt[i] = 0;
   }
 
   // A decode step's append carried by this launch (rax_decode_step): token i's K/V row to
@@ -2375,16 +2385,33 @@ __device__ __forceinline__ void own_chunk_epilogue(const AttnArgs& a, const f32x
     }
     return;
   }
-  // partial of (request t, KV head h, chunk c), query head r16, in own_kernel's layout
+  // partial of (request t, KV head h, chunk c), query head r16, in own_kernel's layout.
+  // With own_fold another workgroup of the same launch (own_rows_merge), possibly on
+  // another XCD, reads it: stored coherent at device scope (through this XCD's L2), one
+  // dword at a time. Otherwise for the merge kernel: 16-byte non-temporal stores (dword
+  // device-scope stores here took multi-turn decode 218.5 -> 224 us per call).
   const int64_t item = (int64_t)rh * a.n_chunk + c;
+  float* wacc = a.ws_own + (item * G + r16) * D;
+  float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + r16) * 2;
+  if (a.own_fold) {
+    if (l > 0.f) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_dev(wacc + wq * 32 + 16 * j + 4 * g4 + e, o[j][e]);
+    }
+    if (wq == 0 && g4 == 0) {
+      store_dev(wml, m);
+      store_dev(wml + 1, l);
+    }
+    return;
+  }
   if (l > 0.f) {
-    float* wacc = a.ws_own + (item * G + r16) * D;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4*>(wacc + wq * 32 + 16 * j + 4 * g4));
   }
   if (wq == 0 && g4 == 0) {
-    float* wml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (item * G + r16) * 2;
     __builtin_nontemporal_store(m, wml);
     __builtin_nontemporal_store(l, wml + 1);
   }
@@ -2409,6 +2436,134 @@ __device__ __forceinline__ bf16x8 vt_frag16(const char* vt, int dt, int lane) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 16 * 256));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One 32-key stage of the own part on 16x16x32 MFMA (K at kt, V at vt, swizzled as
+// above): scores of this lane's query head r16 (row_ok: r16 < g) against the stage's first
+// cnt keys, the online softmax update of (m_run, l_run) shared by every wave, and this
+// wave's quarter of the output dims (acc[j]: dims 32*wave + 16*j + 4*(l/16) + e).
+__device__ __forceinline__ void own_stage16(const char* kt, const char* vt, const bf16x8 (&qf)[4], int cnt,
+                                            bool row_ok, int wave, int lane, float scale_log2, float& m_run,
+                                            float& l_run, f32x4 (&acc)[2]) {
+  const int g4 = lane >> 4;
+  f32x4 sc[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    sc[kh] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_frag16(kt, kh, ks, lane), qf[ks], sc[kh], 0, 0, 0);
+  }
+  // sc[kh][e] is the score of key 16*kh + 4*g4 + e of the stage for query head r16
+  float mx = kNegInf;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 16 * kh + 4 * g4 + e;
+      const float v = row_ok && key < cnt ? sc[kh][e] : kNegInf;
+      sc[kh][e] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max_xor16(max_xor32(mx)) * scale_log2;
+  if (__any(mx > m_run + kLazy)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] *= alpha;
+    m_run = m_new;
+  }
+  const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+  float psum = 0.f;
+  bf16x8 pb;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][e], scale_log2, neg_m));
+      psum += pv;
+      pb[kh * 4 + e] = (__bf16)pv;
+    }
+  psum = sum_xor16(sum_xor32(psum));
+  l_run += psum;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag16(vt, 2 * wave + j, lane), pb, acc[j], 0, 0, 0);
+}
+
+// Final merge of (request t, KV head h) when its own keys took several chunks: each row
+// (query head r16 < g of the group) combines the shared part's split partials of its row
+// block and the request's n_act own-chunk partials by log-sum-exp, and this wave writes
+// its quarter of the row's dims of O (own_chunk_epilogue's lane layout). Partials with
+// l = 0 saw no key and get weight 0 (their accumulators may be stale, hence the selects).
+template <int D>
+__device__ __forceinline__ void own_rows_merge(const AttnArgs& a, int wq, int lane, int t, int h, int rh, int n_act,
+                                               int n_rh) {
+  const int G = a.g;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  if (r16 >= G) return;
+  const int Grow = t * G + r16;
+  const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
+  const int nsplit = a.nsplit;
+  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * nsplit;
+  const int64_t item0 = ((int64_t)h * a.n_rb + rbr) * nsplit;
+  const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
+  const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D;
+  const int64_t own0 = (int64_t)rh * a.n_chunk;  // chunk c: item own0 + c
+  const float* ow_ml = a.ws_own + (int64_t)n_rh * a.n_chunk * G * D + (own0 * G + r16) * 2;
+  const float* ow_acc = a.ws_own + (own0 * G + r16) * (int64_t)D;
+  // Partial s < nsplit: split s of the shared part (the previous launch's), else own chunk
+  // s - nsplit (this launch's); all read with device-coherent loads, U partials per round
+  // trip (indices past the last repeat it and are dropped), combined by an online
+  // log-sum-exp (running maximum M, rescaled sums).
+  constexpr int U = 4;
+  const int n_all = nsplit + n_act;
+  float M = kNegInf, lsum = 0.f;
+  f32x4 fin[2] = {f32x4{}, f32x4{}};
+  for (int s0 = 0; s0 < n_all; s0 += U) {
+    float mv[U], lv[U];
+    f32x4 x[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, n_all - 1);
+      const bool sh = s < nsplit;
+      const float* pml = sh ? sh_ml + (int64_t)s * a.bm * 2 : ow_ml + (int64_t)(s - nsplit) * G * 2;
+      const float* pa = (sh ? sh_acc + (int64_t)s * a.bm * D : ow_acc + (int64_t)(s - nsplit) * G * D) + wq * 32 + 4 * g4;
+      mv[u] = load_dev(pml);
+      lv[u] = load_dev(pml + 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[u][j][e] = load_dev(pa + 16 * j + e);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= n_all || !(lv[u] > 0.f)) continue;  // no keys: weight 0 (stale accumulators)
+      const float m_new = fmaxf(M, mv[u]);
+      const float keep = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+      const float w = __builtin_amdgcn_exp2f(mv[u] - m_new);
+      lsum = lsum * keep + w * lv[u];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin[j][e] = fin[j][e] * keep + w * x[u][j][e];
+      M = m_new;
+    }
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int64_t obase = ((int64_t)t * a.h_q + h * G + r16) * D;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int d0 = wq * 32 + 16 * j + 4 * g4;
+    if (a.o_bf16)
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + obase + d0) =
+          bf16x4{(__bf16)(fin[j][0] * inv), (__bf16)(fin[j][1] * inv), (__bf16)(fin[j][2] * inv),
+                 (__bf16)(fin[j][3] * inv)};
+    else
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + d0) =
+          make_float4(fin[j][0] * inv, fin[j][1] * inv, fin[j][2] * inv, fin[j][3] * inv);
+  }
 }
 
 // Own part of split decode with query-head groups (bf16, D = 128), as one continuous
@@ -2437,45 +2592,58 @@ constexpr int kStreamTK = 32;     // keys per stage
 // while the others stream.
 constexpr int kStreamStages = 2;
 
-template <int D, int S>
-__global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder ord) {
+// Heads per workgroup: HP adjacent KV heads of the same (request, chunk), four waves each,
+// one slot-id list. A key's rows of adjacent heads are adjacent 256-byte pieces of its
+// slot's K (and V) row, and the waves of the heads load them in the same stage: a gather
+// probe (random slots, non-temporal 16-byte loads) read 512 contiguous bytes per slot at
+// 6.7 TB/s, against 6.3-6.4 TB/s for one 256-byte piece per slot; 1 KB or 2 KB pieces were
+// no faster than 512 bytes.
+constexpr int kStreamHeads = 2;
+// Most (chunk, KV head) items of requests with several own chunks for which the own part
+// merges such requests itself
+constexpr int64_t kOwnFoldMaxItems = 256;
+
+template <int D, int S, int HP>
+__global__ void __launch_bounds__(256 * HP) own_stream_kernel(AttnArgs a, OwnOrder ord) {
   static_assert(D == 128, "the swizzle assumes 16 chunks per row");
   static_assert(S >= 2 && 2 * (S - 2) < 64, "stages");
-  constexpr int NW = 4;
+  static_assert(HP >= 1 && HP <= 2, "heads per workgroup");
+  constexpr int NW = 4;                  // waves per head
   constexpr int TK = kStreamTK;
   constexpr int RB = D * 2;              // bytes per row
-  constexpr int TB = TK * RB;            // bytes of K (or V) per stage
+  constexpr int TB = TK * RB;            // bytes of K (or V) per stage and head
   constexpr int RPI = 1024 / RB;         // rows per 1 KB global-to-LDS instruction
-  constexpr int NI = TK / RPI;           // instructions per K (or V) stage
+  constexpr int NI = TK / RPI;           // instructions per K (or V) stage and head
   constexpr int IPW = NI / NW;           // of them per wave
   constexpr int NKS = D / 32;
-  constexpr int KV_BYTES = S * 2 * TB;
-  static_assert(NI % NW == 0, "loads per wave");
+  constexpr int KV_BYTES = S * HP * 2 * TB;
+  static_assert(NI % NW == 0 && (HP == 1 || IPW % HP == 0), "loads per wave");
   static_assert(D == 32 * NW, "a 32-dim quarter per wave");
-  __shared__ __align__(16) char kv[KV_BYTES];
+  __shared__ __align__(16) char kv[KV_BYTES];  // per stage: K then V of head 0, then of head 1, ...
   __shared__ int32_t slot[kStreamCap];
   const uint32_t kv_lds = lds_addr(kv);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = wave / NW, wq = wave - hh * NW;  // this wave's head of the group, dim quarter
   const int r16 = lane & 15, g4 = lane >> 4;
   const int G = a.g;
   const int n_rh = a.batch * a.h_kv;
+  const int n_hg = a.h_kv / HP;  // head groups per (request, chunk)
   // Workgroup order. The hardware hands out workgroups in id order, round-robin over the
   // XCDs and their shader engines, and waits for room on the next one's engine: work items
   // that exit at once must come in contiguous runs, not at a fixed stride (interleaving
   // one live item with three exiting ones put every live one on one engine in four and
-  // measured 2x slower). Rows of n_rh ids, one chunk index per row, heads of a request
-  // together. With the host's order (requests by descending own keys): the last chunk
-  // index first, so that the rows whose live items are the long requests' chunks (a
-  // prefix of each row) start first and the last row ends with the shortest requests.
-  // Without it: chunk 0 first, in batch order.
+  // measured 2x slower). With the host's work list (requests by descending own keys,
+  // each request's chunks and a chunk's head groups together): exactly the live items,
+  // the longest requests first. Without it: rows of batch x n_hg ids, one chunk index per
+  // row, chunk 0 first, in batch order; ids past a request's chunks exit at once.
   const bool ordered = ord.n == a.batch;
-  int c, h, t, n_host = 0;
+  int c, hg, t, n_host = 0;
   if (ordered) {
-    // the host's work list: item blockIdx / h_kv of the list, KV head blockIdx % h_kv;
-    // the item's request by binary search over the cumulative counts (wave-uniform)
-    const int item = (int)(blockIdx.x / (unsigned)a.h_kv);
-    h = (int)(blockIdx.x - (unsigned)item * a.h_kv);
+    // item blockIdx / n_hg of the list, head group blockIdx % n_hg; the item's request by
+    // binary search over the cumulative counts (wave-uniform)
+    const int item = (int)(blockIdx.x / (unsigned)n_hg);
+    hg = (int)(blockIdx.x - (unsigned)item * n_hg);
     int lo = 0, hi = ord.n - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -2486,18 +2654,20 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
     n_host = ord.cum[lo + 1] - ord.cum[lo];
     t = ord.req[lo];
   } else {
-    const int row_i = blockIdx.x / n_rh;
-    const int in_row = blockIdx.x - row_i * n_rh;
+    const int n_row = a.batch * n_hg;
+    const int row_i = blockIdx.x / n_row;
+    const int in_row = blockIdx.x - row_i * n_row;
     c = row_i;
-    t = in_row / a.h_kv;
-    h = in_row - t * a.h_kv;
+    t = in_row / n_hg;
+    hg = in_row - t * n_hg;
   }
+  const int h = hg * HP + hh;  // this wave's KV head
   const int rh = t * a.h_kv + h;
 
   const int rb0 = t * G / a.bm;
   const BlockMeta meta = block_meta_load(a, rb0, lane);
   const bool row_ok = r16 < G;
-  bf16x8 qf[NKS];  // B operand: query head r16, dims 32*ks + 8*g4 .. +8
+  bf16x8 qf[NKS];  // B operand: query head r16 of the group of KV head h, dims 32*ks + 8*g4 .. +8
   {
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + ((int64_t)t * a.h_q + h * G + (row_ok ? r16 : 0)) * D;
 #pragma unroll
@@ -2524,23 +2694,23 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
   const int n = stop - start;
   const int n_tiles = (n + TK - 1) / TK;
   const int64_t row_bytes = (int64_t)a.h_kv * RB;
-  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)h * RB;
-  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)h * RB;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + (int64_t)hg * HP * RB;  // the group's first head
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + (int64_t)hg * HP * RB;
   const int32_t* rtt_row = a.rtt + (int64_t)row_t * a.rtt_stride;  // row_t valid: n_act > 0
 
   // every slot id of the chunk into LDS in one round of loads (positions past the chunk
   // take the chunk's first slot)
   {
-    constexpr int PER_T = kStreamCap / (64 * NW);
+    constexpr int PER_T = kStreamCap / (64 * NW * HP);
     int raw[PER_T];
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const int i = tid + k * 64 * NW;
+      const int i = tid + k * 64 * NW * HP;
       raw[k] = rtt_row[start + (i < n ? i : 0)];
     }
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const int i = tid + k * 64 * NW;
+      const int i = tid + k * 64 * NW * HP;
       int sv = raw[k];
       if (sv < 0 || sv >= a.num_slots) {
         if (i < n) flag_error(RAX_DEVERR_SLOT);
@@ -2551,21 +2721,32 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
   }
   __syncthreads();
 
-  // the K and V rows of stage j's keys into ring slot j % S
+  // this wave's share of the K and V rows of stage j's keys into ring slot j % S: IPW of
+  // the stage's NI x HP 1 KB pieces (NI groups of RPI keys, one head each) per K and V;
+  // with a group of heads, one wave loads every head of its key group, one after another
+  // (adjacent pieces of the same slot rows)
   auto issue = [&](int j) {
-    const uint32_t kl = kv_lds + (j % S) * 2 * TB;
+    const uint32_t kl = kv_lds + (j % S) * HP * 2 * TB;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      const int q = wave + u * NW;
+      int q, hx;
+      if constexpr (HP == 1) {
+        q = wave + u * NW;
+        hx = 0;
+      } else {
+        const int x = wave * IPW + u;
+        q = x / HP;
+        hx = x % HP;
+      }
       const int r = q * RPI + (lane >> 4);
-      const int64_t off = (int64_t)slot[j * TK + r] * row_bytes;
+      const int64_t off = (int64_t)slot[j * TK + r] * row_bytes + hx * RB;
       // read once per call: non-temporal (multi-turn decode 300 -> 241 us per call)
-      lds_load16_nt(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + q * 1024));
-      lds_load16_nt(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + TB + q * 1024));
+      lds_load16_nt(kbase + off + (((lane & 15) ^ swz_k(r)) * 16), uni(kl + hx * 2 * TB + q * 1024));
+      lds_load16_nt(vbase + off + (((lane & 15) ^ swz_v(r)) * 16), uni(kl + hx * 2 * TB + TB + q * 1024));
     }
   };
 
-  f32x4 acc[2] = {f32x4{}, f32x4{}};  // this wave's dims 32*wave + 16*j + 4*g4 + e
+  f32x4 acc[2] = {f32x4{}, f32x4{}};  // this wave's dims 32*wq + 16*j + 4*g4 + e
   float m_run = kNegInf, l_run = 0.f;
 
   for (int j = 0; j < S - 1 && j < n_tiles; ++j) issue(j);
@@ -2577,55 +2758,25 @@ __global__ void __launch_bounds__(256) own_stream_kernel(AttnArgs a, OwnOrder or
     else wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");
     if (i + S - 1 < n_tiles) issue(i + S - 1);
-    const char* kt = kv + (i % S) * 2 * TB;
-    const char* vt = kt + TB;
-    const int cnt = min(TK, n - i * TK);
-    f32x4 sc[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      sc[kh] = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        sc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_frag16(kt, kh, ks, lane), qf[ks], sc[kh], 0, 0, 0);
-    }
-    // sc[kh][e] is the score of key 16*kh + 4*g4 + e of the stage for query head r16
-    float mx = kNegInf;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kh + 4 * g4 + e;
-        const float v = row_ok && key < cnt ? sc[kh][e] : kNegInf;
-        sc[kh][e] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = max_xor16(max_xor32(mx)) * a.scale_log2;
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-    float psum = 0.f;
-    bf16x8 pb;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][e], a.scale_log2, neg_m));
-        psum += pv;
-        pb[kh * 4 + e] = (__bf16)pv;
-      }
-    psum = sum_xor16(sum_xor32(psum));
-    l_run += psum;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag16(vt, 2 * wave + j, lane), pb, acc[j], 0, 0, 0);
+    const char* kt = kv + ((i % S) * HP + hh) * 2 * TB;
+    own_stage16(kt, kt + TB, qf, min(TK, n - i * TK), row_ok, wq, lane, a.scale_log2, m_run, l_run, acc);
   }
-  own_chunk_epilogue<D>(a, acc, m_run, l_run, wave, lane, row_ok, t, h, rh, c, n_act, n_rh);
+  own_chunk_epilogue<D>(a, acc, m_run, l_run, wq, lane, row_ok, t, h, rh, c, n_act, n_rh);
+  if (n_act > 1 && a.own_fold) {
+    // the workgroup that finishes the last of the request's chunks (per KV head) merges
+    // them. Its partial stores are device-coherent: once every wave has seen them
+    // complete (vmcnt 0), the count that follows is ordered after them, and the last
+    // workgroup's device-coherent loads see every chunk's partial. (Device-scope fences
+    // instead, which write back and invalidate a whole L2, made the multi-turn decode
+    // call 4x slower.)
+    __shared__ int32_t last[HP];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (wq == 0 && lane == 0)
+      last[hh] = __hip_atomic_fetch_add(a.own_cnt + rh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_act - 1;
+    __syncthreads();
+    if (last[hh]) own_rows_merge<D>(a, wq, lane, t, h, rh, n_act, n_rh);
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -2792,8 +2943,12 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
         const bool ordered = ord && ord->n == a.batch;
         const int64_t items = ordered ? (int64_t)ord->cum[ord->n] * a.h_kv : (int64_t)a.batch * a.h_kv * a.n_chunk;
         if (items > INT32_MAX || a.g > 16) return RAX_EINVAL;  // one 16-wide tile of query heads
-        if (items > 0)
-          hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages>), dim3((unsigned)items), dim3(256), 0, st, a,
+        // a group of kStreamHeads KV heads per workgroup where they divide h_kv
+        if (items > 0 && a.h_kv % kStreamHeads == 0)
+          hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages, kStreamHeads>), dim3((unsigned)(items / kStreamHeads)),
+                             dim3(256 * kStreamHeads), 0, st, a, ordered ? *ord : none);
+        else if (items > 0)
+          hipLaunchKernelGGL((own_stream_kernel<D, kStreamStages, 1>), dim3((unsigned)items), dim3(256), 0, st, a,
                              ordered ? *ord : none);
         rc = hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
         if (rc != RAX_OK) return rc;
@@ -2802,6 +2957,10 @@ static rax_status launch_shape(AttnArgs& a, Shape s, hipStream_t st, const Appen
       }
     }
   }
+  // split decode with the own part on own_stream_kernel merging in its own launch
+  // (own_fold): it writes every row with own keys, the merge kernel only rows without any
+  // (none when the host's list says so)
+  if (a.shared_only && a.own_fused == 2 && a.own_fold && ord && ord->n == a.batch && ord->all_own) return RAX_OK;
   if (a.nsplit > 1 || a.shared_only) return launch_merge<D>(a, st);
   return RAX_OK;
 }
@@ -2819,10 +2978,10 @@ static rax_status dispatch(AttnArgs& a, rax_dtype dt, int d, Shape s, hipStream_
   return RAX_EINVAL;
 }
 
-// Workspace of a decode call, in floats: shared-part partials (accumulators, then m/l),
-// the row blocks' shared lengths, own-part partials (accumulators, then m/l).
+// Workspace of a decode call, in 4-byte words: shared-part partials (accumulators, then
+// m/l), own-part partials (accumulators, then m/l), own-part chunk counters (own_mode 2).
 struct DecodeLayout {
-  int64_t sh_acc, sh_ml, own_acc, own_ml, total;
+  int64_t sh_acc, sh_ml, own_acc, own_ml, own_cnt, total;
   int32_t nsplit, n_rb, n_chunk, bm;
   bool split_decode;
   int32_t own_mode;  // 0: own_kernel + merge_kernel, 1: own_merge_kernel, 2: own_stream_kernel + merge_kernel
@@ -2905,7 +3064,8 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   l.sh_ml = sh_items * l.bm * 2;
   l.own_acc = own_rows * d;
   l.own_ml = own_rows * 2;
-  l.total = l.sh_acc + l.sh_ml + l.own_acc + l.own_ml;
+  l.own_cnt = l.own_mode == 2 ? batch * h_kv : 0;  // int32 chunk counters
+  l.total = l.sh_acc + l.sh_ml + l.own_acc + l.own_ml + l.own_cnt;
   return l;
 }
 
@@ -3133,12 +3293,28 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
   if (hint.order.n == batch && l.own_mode == 2) {
     // the own part's work list: per request, the chunks of its own keys (own_chunks)
     int32_t acc_items = 0;
+    hint.order.all_own = 1;
     for (int32_t i = 0; i < batch; ++i) {
       hint.order.cum[i] = (uint16_t)acc_items;
       const int64_t own = hint.own_keys[hint.order.req[i]];
+      if (own < 1) hint.order.all_own = 0;
       acc_items += (int32_t)std::min<int64_t>(l.n_chunk, std::max<int64_t>(1, (own + l.own_min - 1) / l.own_min));
     }
     hint.order.cum[batch] = (uint16_t)acc_items;  // <= 256 x 64
+    // Requests with several own chunks merge in the own part's launch when few: each of
+    // their workgroups then ends with a device-scope count (and the last one with the
+    // merge), a few microseconds in which it holds its CU slot. Measured: self-consistency
+    // decode (nearly every request one chunk) 195.8 -> 182.9 us per call without the merge
+    // launch; multi-turn (most requests 2-4 chunks, ~3000 such items) 218.5 -> 242.8 us.
+    int64_t multi = 0;
+    for (int32_t i = 0; i < batch; ++i) {
+      const int32_t n_i = hint.order.cum[i + 1] - hint.order.cum[i];
+      if (n_i > 1) multi += (int64_t)n_i * h_kv;
+    }
+    if (multi <= kOwnFoldMaxItems) {
+      a.own_fold = 1;
+      a.own_cnt = reinterpret_cast<int32_t*>(a.ws_own + l.own_acc + l.own_ml);
+    }
   } else {
     hint.order.n = 0;
   }
@@ -3149,7 +3325,8 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
 // memory (code under graph capture, tight serving loops). Its workspace is this file-scope
 // device array, which every GPU the library runs on holds until the process ends; calls
 // on one GPU share it, so calls that overlap on one GPU race. Nothing in it has to start
-// at zero (every kernel writes its partials before the merge reads them).
+// at zero (every kernel writes its partials before the merge reads them; the own part's
+// chunk counters, used only with host lengths, are zeroed by the call's first kernel).
 constexpr size_t kScratchBytes = 64ull << 20;  // covers 256 requests x 64 query heads
 static __device__ __align__(256) char scratch[kScratchBytes];
 

@@ -90,6 +90,16 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return a + b;
 }
 
+// Stores and loads coherent at device scope (relaxed atomics: on gfx950 they carry the sc1
+// bit and pass through the XCD's L2), for data that another workgroup of the same launch,
+// possibly on another XCD, reads after a device-scope atomic has ordered the two.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wave-uniform copy (kept in an SGPR) of a value that is the same in every lane.
 __device__ __forceinline__ uint32_t uni32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -46,6 +46,7 @@ bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, ra
 // kernel covers n_chunk items per request in batch order.
 struct OwnOrder {
   int32_t n = 0;
+  int32_t all_own = 0;  // every request has own keys (the own part then writes every row of O)
   uint16_t req[kAppendMax];
   uint16_t cum[kAppendMax + 1];
 };

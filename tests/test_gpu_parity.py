@@ -553,23 +553,30 @@ def test_decode_step_folded_append_equals_separate_calls():
 
 
 @pytest.mark.parametrize("h_q,h_kv,P,n_req", [(4, 2, 150, 12), (32, 4, 150, 12), (64, 4, 150, 12),
-                                             (16, 2, 2100, 256)])
+                                             (16, 2, 2100, 256), (32, 8, 150, -72)])
 def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
     """Decode attention with query-head groups (own keys on MFMA tiles) on hand-built rows:
     a P-key prefix shared by all requests (hinted), then own ranges of 0..2600 keys, so
     that chunks are empty, shorter than a tile, exactly one or two tiles, ragged, several
-    per (request, KV head), and longer than one round of tiles. The last case has 64 row
+    per (request, KV head), and longer than one round of tiles. The fourth case has 64 row
     blocks and a 2100-key prefix, so the shared part runs in 4-wave workgroups with two
-    tiles per round and several rounds per split. Outputs against fp64 attention over
-    each request's keys (oracle.attention.attend): every request, or 64 spread ones."""
+    tiles per round and several rounds per split. The last (n_req < 0: -n_req requests)
+    gives every request 1100..1400 own keys (two chunks each), so that with host lengths
+    so many items belong to requests with several chunks that these merge in the merge
+    kernel; in the other cases the own part's launch merges them itself. Outputs against
+    fp64 attention over each request's keys (oracle.attention.attend): every request, or
+    64 spread ones."""
     from oracle.attention import attend
     from prefix_shared_kv_extend_amd import _lib
     say(f"decode, query-head groups {h_q}/{h_kv}, {n_req} requests: own ranges 0..2600 keys past a {P}-key "
         f"shared prefix")
     d, S = 128, 1 << 17
     base = [0, 1, 63, 64, 65, 127, 128, 129, 300, 1100, 2600, 7]
-    own = (base * (n_req // len(base) + 1))[:n_req] if n_req <= len(base) else \
-        [base[i % len(base)] if i % 16 == 0 else int(i % 41) for i in range(n_req)]
+    if n_req < 0:
+        own = [1100 + (i * 97) % 301 for i in range(-n_req)]
+    else:
+        own = (base * (n_req // len(base) + 1))[:n_req] if n_req <= len(base) else \
+            [base[i % len(base)] if i % 16 == 0 else int(i % 41) for i in range(n_req)]
     B = len(own)
     W = P + max(own) + 2
     gen = torch.Generator().manual_seed(23 + h_q + P)
