@@ -2640,19 +2640,32 @@ __global__ void __launch_bounds__(256 * HP) own_stream_kernel(AttnArgs a, OwnOrd
   const bool ordered = ord.n == a.batch;
   int c, hg, t, n_host = 0;
   if (ordered) {
-    // item blockIdx / n_hg of the list, head group blockIdx % n_hg; the item's request by
-    // binary search over the cumulative counts (wave-uniform)
+    // item blockIdx / n_hg of the list, head group blockIdx % n_hg. The list's cumulative
+    // counts rise strictly, so the item's entry is the number of entries that start at or
+    // before it, minus one: lane l reads entries 4l .. 4l + 3 of the counts and of the
+    // requests in one round of loads and ballots count them. (A binary search made eight
+    // dependent loads from the argument memory at every workgroup's start.)
+    static_assert(kAppendMax == 256, "four list entries per lane");
     const int item = (int)(blockIdx.x / (unsigned)n_hg);
     hg = (int)(blockIdx.x - (unsigned)item * n_hg);
-    int lo = 0, hi = ord.n - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)ord.cum[mid] <= item) lo = mid;
-      else hi = mid - 1;
+    int cv[4], rv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cv[k] = ord.cum[4 * lane + k];
+      rv[k] = ord.req[4 * lane + k];
     }
-    c = item - ord.cum[lo];
-    n_host = ord.cum[lo + 1] - ord.cum[lo];
-    t = ord.req[lo];
+    const int cum_end = ord.cum[kAppendMax];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(4 * lane + k < ord.n && cv[k] <= item));
+    const int lo = cnt - 1;  // cum[0] = 0 <= item
+    auto pick = [](const int (&v)[4], int k) { return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3]; };
+    const int c_lo = __builtin_amdgcn_readlane(pick(cv, lo & 3), lo >> 2);
+    const int c_hi =
+        lo + 1 < kAppendMax ? __builtin_amdgcn_readlane(pick(cv, (lo + 1) & 3), (lo + 1) >> 2) : cum_end;
+    t = __builtin_amdgcn_readlane(pick(rv, lo & 3), lo >> 2);
+    c = item - c_lo;
+    n_host = c_hi - c_lo;
   } else {
     const int n_row = a.batch * n_hg;
     const int row_i = blockIdx.x / n_row;
