@@ -2325,10 +2325,40 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
 // 4*(l/16) + {0..3} in o[j]) with the running (m, l), the same in every wave. Either the
 // request's only own chunk is merged in place with the shared part's split partials and
 // O written, or the chunk's partial goes to the workspace in own_kernel's layout.
+// The shared part's split partials of one row of an own-chunk workgroup (this lane's dims
+// in own_chunk_epilogue's layout), when there are at most kShPre splits and the host's
+// list gives the request one chunk: loaded at the workgroup's start, next to the block
+// metadata, so that the in-place merge at its end waits for no load. (They are written
+// by the launch before.)
+constexpr int kShPre = 2;
+struct ShPre {
+  float2 ml[kShPre];
+  f32x4 acc[kShPre][2];
+};
+template <int D>
+__device__ __forceinline__ void sh_partials_load(const AttnArgs& a, int t, int h, int r16, int wq, int g4, ShPre& p) {
+  const int Grow = t * a.g + r16;
+  const int rbr = Grow / a.bm, Rr = Grow - rbr * a.bm;
+  const int64_t n_items = (int64_t)a.h_kv * a.n_rb * a.nsplit;
+  const int64_t item0 = ((int64_t)h * a.n_rb + rbr) * a.nsplit;
+  const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
+  const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D + wq * 32 + 4 * g4;
+#pragma unroll
+  for (int sp = 0; sp < kShPre; ++sp) {
+    if (sp < a.nsplit) {
+      p.ml[sp] = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) p.acc[sp][j] = *reinterpret_cast<const f32x4*>(sh_acc + (int64_t)sp * a.bm * D + 16 * j);
+    } else {
+      p.ml[sp] = make_float2(0.f, 0.f);  // l = 0: weight 0
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void own_chunk_epilogue(const AttnArgs& a, const f32x4 (&o)[2], float m, float l,
                                                    int wq, int lane, bool row_ok, int t, int h, int rh, int c,
-                                                   int n_act, int n_rh) {
+                                                   int n_act, int n_rh, bool pre_on, const ShPre& pre) {
   static_assert(D == 128, "four 32-dim quarters, one per wave");
   const int G = a.g;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -2346,14 +2376,37 @@ __device__ __forceinline__ void own_chunk_epilogue(const AttnArgs& a, const f32x
     const float* sh_ml = a.ws + n_items * a.bm * (int64_t)D + (item0 * a.bm + Rr) * 2;
     const float* sh_acc = a.ws + (item0 * a.bm + Rr) * (int64_t)D;
     float M = l > 0.f ? m : kNegInf;
+    f32x4 fin[2];
+    float lsum;
+    if (pre_on) {  // the splits' partials are in registers already
+#pragma unroll
+      for (int sp = 0; sp < kShPre; ++sp)
+        if (pre.ml[sp].y > 0.f) M = fmaxf(M, pre.ml[sp].x);
+      const float Mu = M == kNegInf ? 0.f : M;
+      const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
+      lsum = w_own * l;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin[j][e] = w_own != 0.f ? w_own * o[j][e] : 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kShPre; ++sp) {
+        const float2 ml = pre.ml[sp];
+        const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - Mu) : 0.f;
+        lsum += w * ml.y;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fin[j][e] += w != 0.f ? w * pre.acc[sp][j][e] : 0.f;
+      }
+    } else {
     for (int sp = 0; sp < nsplit; ++sp) {
       const float2 ml = *reinterpret_cast<const float2*>(sh_ml + (int64_t)sp * a.bm * 2);
       if (ml.y > 0.f) M = fmaxf(M, ml.x);
     }
     const float Mu = M == kNegInf ? 0.f : M;
     const float w_own = l > 0.f ? __builtin_amdgcn_exp2f(m - Mu) : 0.f;
-    float lsum = w_own * l;
-    f32x4 fin[2];
+    lsum = w_own * l;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -2369,6 +2422,7 @@ __device__ __forceinline__ void own_chunk_epilogue(const AttnArgs& a, const f32x
 #pragma unroll
         for (int e = 0; e < 4; ++e) fin[j][e] += w != 0.f ? w * x[e] : 0.f;
       }
+    }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const int64_t obase = ((int64_t)t * a.h_q + h * G + r16) * D;
@@ -2689,6 +2743,9 @@ __global__ void __launch_bounds__(256 * HP) own_stream_kernel(AttnArgs a, OwnOrd
       qf[ks] = row_ok ? v : bf16x8{};
     }
   }
+  ShPre pre;
+  const bool pre_on = a.nsplit <= kShPre && ordered && n_host == 1;  // merges in place (the host's count)
+  if (pre_on) sh_partials_load<D>(a, t, h, row_ok ? r16 : 0, wq, g4, pre);
   const int rl = t - rb0 * a.bm / G;
   const int L = row_shared_len(a, meta, lane, rl);
   const int row_t = __builtin_amdgcn_readlane(meta.row, rl);
@@ -2774,7 +2831,7 @@ __global__ void __launch_bounds__(256 * HP) own_stream_kernel(AttnArgs a, OwnOrd
     const char* kt = kv + ((i % S) * HP + hh) * 2 * TB;
     own_stage16(kt, kt + TB, qf, min(TK, n - i * TK), row_ok, wq, lane, a.scale_log2, m_run, l_run, acc);
   }
-  own_chunk_epilogue<D>(a, acc, m_run, l_run, wq, lane, row_ok, t, h, rh, c, n_act, n_rh);
+  own_chunk_epilogue<D>(a, acc, m_run, l_run, wq, lane, row_ok, t, h, rh, c, n_act, n_rh, pre_on, pre);
   if (n_act > 1 && a.own_fold) {
     // the workgroup that finishes the last of the request's chunks (per KV head) merges
     // them. Its partial stores are device-coherent: once every wave has seen them
