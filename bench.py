@@ -757,9 +757,18 @@ def summarize_trace(csv_path):
         p = per.setdefault(k, [0, 0])
         p[0] += 1
         p[1] += e - s
+    # the library's kernels one by one; the rest (the seeded input generator, scratch fills,
+    # copies) in one line
     print("| kernel | dispatches | mean us | total ms |\n|---|---|---|---|")
+    other_n, other_t = 0, 0
     for k, (n, tot) in sorted(per.items(), key=lambda kv: -kv[1][1]):
-        print(f"| `{k[:110]}` | {n} | {tot / n / 1e3:.2f} | {tot / 1e6:.3f} |")
+        if "raxk" in k:  # also the mangled names the demangler leaves (bf16 template arguments)
+            print(f"| `{k[:110]}` | {n} | {tot / n / 1e3:.2f} | {tot / 1e6:.3f} |")
+        else:
+            other_n, other_t = other_n + n, other_t + tot
+    if other_n:
+        print(f"| other kernels (input generator, scratch fills, copies) | {other_n} | {other_t / other_n / 1e3:.2f} | "
+              f"{other_t / 1e6:.3f} |")
     hot = [r for r in rows if any(h in r[2] for h in HOT)]
     if not hot:
         return
