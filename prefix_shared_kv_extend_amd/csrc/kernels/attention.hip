@@ -2624,9 +2624,10 @@ __device__ __forceinline__ void own_rows_merge(const AttnArgs& a, int wq, int la
 // stream per workgroup, on MFMA: the VALU own part (own_chunk) scores 32 / g keys per
 // batch through chains of cross-lane reductions, which for g > 1 bound it rather than
 // memory (0.56 ms per GQA 64/8 self-consistency call for 0.59 GB). A workgroup takes one
-// own chunk of (request t, KV head h), at most kStreamCap keys. Its slot ids go to LDS
+// own chunk of request t for HP adjacent KV heads (below), at most kStreamCap keys; four
+// waves per head. Its slot ids go to LDS
 // first (one round of loads); then the chunk's keys stream through a ring of S stages of
-// 32 keys (8 KB of K and 8 KB of V each) filled straight from global memory: while stage i
+// 32 keys (8 KB of K and 8 KB of V per head) filled straight from global memory: while stage i
 // is computed, the loads of the next S - 1 stages are in flight. One barrier per stage.
 // A stage is S^T = K Q^T and O^T = V^T P^T on 16x16x32 MFMA, the g <= 16 query heads as
 // the columns of one 16-wide tile (columns past g masked). Every wave computes every
@@ -2639,11 +2640,12 @@ __device__ __forceinline__ void own_rows_merge(const AttnArgs& a, int wq, int la
 // chunk's first slot (a key it attends, so finite) and are masked.
 constexpr int kStreamCap = 1024;  // most keys per own chunk of own_stream_kernel
 constexpr int kStreamTK = 32;     // keys per stage
-// Two stages (one in flight while one is computed; 36 KB of LDS with the slot ids, four
-// workgroups per CU) measured faster than three (three per CU) or four (two per CU):
-// multi-turn decode 221.6, 223.0 and 224.3 us per call; six stages (one per CU) 262.7 us.
-// With more workgroups per CU, one's start (metadata, slot ids, first stage: ~5 us) runs
-// while the others stream.
+// Two stages (one in flight while one is computed). Measured with one head per workgroup
+// (36 KB of LDS with the slot ids, four workgroups per CU), faster than three stages
+// (three per CU) or four (two per CU): multi-turn decode 221.6, 223.0 and 224.3 us per
+// call; six stages (one per CU) 262.7 us. With more workgroups per CU, one's start
+// (metadata, slot ids, first stage: ~5 us) runs while the others stream. With two heads
+// per workgroup: 68 KB, two workgroups (16 waves) per CU.
 constexpr int kStreamStages = 2;
 
 // Heads per workgroup: HP adjacent KV heads of the same (request, chunk), four waves each,
