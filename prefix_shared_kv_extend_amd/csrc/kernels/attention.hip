@@ -3399,7 +3399,10 @@ rax_status raxk::decode_attention_impl(const void* q, const void* k_pool, const 
 // on one GPU share it, so calls that overlap on one GPU race. Nothing in it has to start
 // at zero (every kernel writes its partials before the merge reads them; the own part's
 // chunk counters, used only with host lengths, are zeroed by the call's first kernel).
-constexpr size_t kScratchBytes = 64ull << 20;  // covers 256 requests x 64 query heads
+// 64 MiB covers 256 requests x 64 query heads x 128 dims for MHA at any length and for
+// query-head groups (2 to 16 per KV head) up to 5120 keys per request; larger layouts are
+// refused.
+constexpr size_t kScratchBytes = 64ull << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 // Device address of `scratch` on each device, taken once per device with that device
