@@ -244,8 +244,8 @@ class Tree:
             _need(shared_len.numel() == n, "shared_len: [batch]")
         h_kv, d = k_pool.shape[1], k_pool.shape[2]
         a = DecodeStepArgs()
-        keep = {"seq_len": seq_len, "out": np.empty(max(n, 1), dtype=np.int32),
-                "freed": np.empty(self.num_slots, dtype=np.int32)}
+        # evicted slots land in the tree's report buffer (num_slots entries, allocated once)
+        keep = {"seq_len": seq_len, "out": np.empty(max(n, 1), dtype=np.int32), "freed": self._freed}
         if shared_len_host is not None:
             _need(shared_len is not None and len(shared_len_host) == n, "shared_len_host: [batch], with shared_len")
             keep["sh_host"] = _i32arr(shared_len_host)
@@ -286,7 +286,7 @@ class Tree:
         if st == EINVAL and a.ws_needed > a.ws_bytes:
             return None, None, int(a.ws_needed)
         _check(st, "rax_decode_step")
-        return keep["out"][: a.batch], keep["freed"][: a.num_freed], int(a.ws_needed)
+        return keep["out"][: a.batch], keep["freed"][: a.num_freed].copy(), int(a.ws_needed)
 
     # ------------------------------------------------------------ host tier
     def set_host_tier(self, host_slots: int, k_host=None, v_host=None) -> None:

@@ -84,7 +84,7 @@ class _DecodeState:
     lens: np.ndarray              # host lengths (slots in each row), updated by every step
     prep: tuple                   # rax_decode_step argument block (Tree.decode_step_prepare)
     max_len: int = 0              # lens.max(), kept in step with lens
-    pos: dict = None              # request id -> its index in the batch
+    pos: dict = None              # request id -> its index in the batch (built on first use)
     hints: np.ndarray = None      # host copy of inv["shared_len"]
 
 
@@ -105,6 +105,7 @@ class RadixRuntime:
             self.v_host = torch.zeros((self.host_slots, h_kv, d), dtype=dtype, pin_memory=True)
             self.tree.set_host_tier(self.host_slots, self.k_host, self.v_host)
         self.rtt = torch.zeros((max_reqs, max_ctx), dtype=torch.int32, device=self.device)
+        self._seq_dev = torch.zeros(max_reqs, dtype=torch.int32, device=self.device)  # decode lengths on the device
         self.rows = np.zeros((max_reqs, max_ctx), dtype=np.int32)   # host mirror of rtt
         self.max_ctx = max_ctx
         self.free_rows = list(range(max_reqs - 1, -1, -1))
@@ -157,6 +158,8 @@ class RadixRuntime:
         """Current number of slots in the request's row."""
         ds = self._dec_cache
         if ds is not None:
+            if ds.pos is None:
+                ds.pos = dict(zip(ds.key, range(len(ds.key))))
             i = ds.pos.get(rid)
             if i is not None:
                 return int(ds.lens[i])
@@ -289,13 +292,14 @@ class RadixRuntime:
             req_rows = np.array(_take(self.row_of, rids), dtype=np.int32)
             nodes = _take(self.node_of, rids)
             hints = self.tree.lca_depths(nodes)
-            inv = self._upload(dict(req_pool_idx=req_rows, shared_len=hints, seq_len=np.zeros(len(rids))))
+            inv = self._upload(dict(req_pool_idx=req_rows, shared_len=hints))
+            inv["seq_len"] = self._seq_dev[: len(rids)]   # written by every step's append
             lens = np.array(_take(self.len_of, rids), dtype=np.int32)
             prep = self.tree.decode_step_prepare(lens, self.rtt, inv["req_pool_idx"], inv["seq_len"], self.k_pool,
                                                  self.v_pool, self.h_q, shared_len=inv["shared_len"],
                                                  shared_len_host=hints)
             ds = self._dec_cache = _DecodeState(key, req_rows, inv, lens, prep, int(lens.max()) if len(lens) else 0,
-                                                dict(zip(key, range(len(key)))), hints)
+                                                None, hints)
         seq_len = ds.lens + 1
         max_seq = ds.max_len + 1 if len(seq_len) else 0
         if max_seq > self.max_ctx:
