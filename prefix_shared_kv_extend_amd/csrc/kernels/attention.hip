@@ -1441,11 +1441,13 @@ __device__ __forceinline__ int row_shared_len(const AttnArgs& a, const BlockMeta
 // sets the first own position and the chunk size.
 constexpr int kOwnMin = 32;       // own_kernel / own_merge_kernel
 // own_stream_kernel: chunks of at least 1024 keys, at most 4 per (request, KV head) unless
-// more keep each within kStreamCap. Measured (with the tile-round form it replaced)
+// more keep each within 1024 keys (or one chunk per request, see decode_layout). Measured
+// (with the tile-round form it replaced)
 // on GQA decode (self-consistency 64/8, multi-turn 32/8) from 128/8 to 1024/4: fewer,
 // longer chunks win (275 -> 225 us, 204 -> 159 us); idle workgroups (chunks past a
 // request's keys) and partials to merge cost more than the parallelism they add.
 constexpr int kOwnTileMin = 1024;
+constexpr int64_t kOneChunkItems = 1024;  // (request, KV head) pairs for one chunk per request
 constexpr int kOwnTileChunks = 4;
 __device__ __forceinline__ int own_chunks(const AttnArgs& a, int row, int end, int L, int& first, int& per) {
   first = L;
@@ -2638,7 +2640,7 @@ __device__ __forceinline__ void own_rows_merge(const AttnArgs& a, int wq, int la
 // while the others waited at the barrier: ~0.8 us per stage with the GPU nearly idle,
 // against ~0.37 us for the loads alone.) Keys past the chunk in its last stage read the
 // chunk's first slot (a key it attends, so finite) and are masked.
-constexpr int kStreamCap = 1024;  // most keys per own chunk of own_stream_kernel
+constexpr int kStreamCap = 2048;  // most keys per own chunk of own_stream_kernel (slot ids in LDS)
 constexpr int kStreamTK = 32;     // keys per stage
 // Two stages (one in flight while one is computed). Measured with one head per workgroup
 // (36 KB of LDS with the slot ids, four workgroups per CU), faster than three stages
@@ -2778,7 +2780,7 @@ __global__ void __launch_bounds__(256 * HP) own_stream_kernel(AttnArgs a, OwnOrd
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int i = tid + k * 64 * NW * HP;
-      raw[k] = rtt_row[start + (i < n ? i : 0)];
+      raw[k] = k * 64 * NW * HP < n ? rtt_row[start + (i < n ? i : 0)] : 0;  // (uniform: rounds past n skipped)
     }
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
@@ -3105,14 +3107,25 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
   const int64_t pairs = std::max<int64_t>(1, batch * h_kv);
   // query-head groups: own keys on MFMA (own_stream_kernel), chunks of at least
   // kOwnTileMin keys, at most kOwnTileChunks per (request, KV head) unless more are needed
-  // to keep every chunk within kStreamCap keys (the slot ids a workgroup holds in LDS)
-  const int64_t cap_chunks = ((int64_t)max_seq_len + kStreamCap - 1) / kStreamCap;
+  // to keep every chunk within kOwnTileMin keys. Knowing that no request has more than
+  // kStreamCap own keys and that the batch fills the GPU (kOneChunkItems (request, KV head)
+  // pairs), every request takes one chunk instead: no request then needs a merge.
+  // Measured on self-consistency decode (256 requests, at most ~1100 own keys): 180.3 ->
+  // 173.1 us per call; on multi-turn, whose longest requests hold thousands of own keys,
+  // chunks of up to 1536 or 2048 keys made the longest workgroups the tail (216.7 -> 220.6
+  // and 227.0 us), so there the chunks stay at 1024 keys.
+  const int64_t cap_chunks = ((int64_t)max_seq_len + kOwnTileMin - 1) / kOwnTileMin;
   if (dt == RAX_BF16 && d == 128 && g >= 2 && cap_chunks <= 64 - l.nsplit) {
-    l.own_min = kOwnTileMin;
-    l.n_chunk = (int32_t)std::max<int64_t>(
-        {1, cap_chunks,
-         std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnTileMin - 1) / kOwnTileMin, kOwnTileChunks})});
     l.own_mode = 2;
+    if (hint.own > 0 && hint.own <= kStreamCap && batch * h_kv >= kOneChunkItems) {
+      l.own_min = kStreamCap;
+      l.n_chunk = 1;
+    } else {
+      l.own_min = kOwnTileMin;
+      l.n_chunk = (int32_t)std::max<int64_t>(
+          {1, cap_chunks,
+           std::min<int64_t>({64 - l.nsplit, (max_seq_len + kOwnTileMin - 1) / kOwnTileMin, kOwnTileChunks})});
+    }
   } else {
     l.own_min = kOwnMin;
     const int64_t by_len = (max_seq_len + kOwnMin - 1) / kOwnMin;
