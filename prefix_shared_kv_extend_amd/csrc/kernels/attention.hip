@@ -127,6 +127,7 @@ struct __align__(16) Smem {
   int32_t own[C::BM + 1];
   int32_t req_sh[C::BM];
   int32_t hdr[8];
+  int32_t cnt[32];
 };
 
 struct TileDesc {
@@ -198,15 +199,34 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-__device__ __forceinline__ int upper_req(const int32_t* qo, int batch, int64_t t) {
-  // last r in [0, batch) with qo[r] <= t
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (qo[mid] <= t) lo = mid;
-    else hi = mid - 1;
+// The requests whose extend rows [t0, t1] a block covers: ra = the last r in [0, batch)
+// with qo[r] <= t0, rb = the last with qo[r] <= t1. qo rises (never falls) from qo[0] = 0,
+// so the last such r is the number of r with qo[r] <= t, minus one: the block counts them
+// in one round of loads (a binary search in one thread made about 2 log2(batch) dependent
+// loads at every workgroup's start). cnt: 32 ints of LDS; every thread calls; ends with a
+// barrier.
+__device__ __forceinline__ void block_reqs(const int32_t* qo, int batch, int64_t t0, int64_t t1, int tid,
+                                           int nthreads, int* cnt, int& ra, int& rb) {
+  const int wave = tid >> 6, lane = tid & 63;
+  int c0 = 0, c1 = 0;
+  for (int i0 = 0; i0 < batch; i0 += nthreads) {  // the same trip count in every thread
+    const int i = i0 + tid;
+    const int64_t v = i < batch ? qo[i] : 0;
+    c0 += __popcll(__ballot(i < batch && v <= t0));
+    c1 += __popcll(__ballot(i < batch && v <= t1));
   }
-  return lo;
+  if (lane == 0) {
+    cnt[wave] = c0;
+    cnt[16 + wave] = c1;
+  }
+  __syncthreads();
+  int s0 = 0, s1 = 0;
+  for (int w = 0; w < nthreads / 64; ++w) {
+    s0 += cnt[w];
+    s1 += cnt[16 + w];
+  }
+  ra = max(s0 - 1, 0);
+  rb = max(s1 - 1, 0);
 }
 
 // Wave-uniform value (kept in an SGPR): block metadata read from LDS is the same in
@@ -354,19 +374,16 @@ __global__ void __launch_bounds__(64 * NW) attn_kernel(AttnArgs a) {
     r0 = (int)qa;
     nreq = (int)(qb - qa);
   } else {
-    if (tid == 0) {
-      const int ra = upper_req(a.qo_indptr, a.batch, qa);
-      int n = upper_req(a.qo_indptr, a.batch, qb - 1) - ra + 1;
-      if (n > BM) {  // only possible with empty requests in between
-        flag_error(RAX_DEVERR_ROW);
-        n = BM;
-      }
-      sm.hdr[0] = ra;
-      sm.hdr[1] = n;
+    static_assert(C::kThreads <= 16 * 64, "block_reqs counts per wave");
+    int ra, rb_last;
+    block_reqs(a.qo_indptr, a.batch, qa, qb - 1, tid, C::kThreads, sm.cnt, ra, rb_last);
+    int n = rb_last - ra + 1;
+    if (n > BM) {  // only possible with empty requests in between
+      if (tid == 0) flag_error(RAX_DEVERR_ROW);
+      n = BM;
     }
-    __syncthreads();
-    r0 = uni(sm.hdr[0]);
-    nreq = uni(sm.hdr[1]);
+    r0 = uni(ra);
+    nreq = uni(n);
   }
   for (int i = tid; i < nreq; i += C::kThreads) {
     const int r = r0 + i;
@@ -841,6 +858,7 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
     int32_t own[BM + 1];
     int32_t req_sh[BM];
     int32_t hdr[8];
+    int32_t cnt[32];
   };
   __shared__ Sm sm;
 
@@ -877,19 +895,15 @@ __global__ void __launch_bounds__(512) extend_kernel(AttnArgs a) {
   }
 
   // ---- block metadata (requests covered, shared length, tile list), as attn_kernel
-  if (tid == 0) {
-    const int ra = upper_req(a.qo_indptr, a.batch, qa);
-    int n = upper_req(a.qo_indptr, a.batch, qb - 1) - ra + 1;
-    if (n > BM) {  // only possible with empty requests in between
-      flag_error(RAX_DEVERR_ROW);
-      n = BM;
-    }
-    sm.hdr[0] = ra;
-    sm.hdr[1] = n;
+  int ra, rb_last;
+  block_reqs(a.qo_indptr, a.batch, qa, qb - 1, tid, 64 * NW, sm.cnt, ra, rb_last);
+  int n_req_blk = rb_last - ra + 1;
+  if (n_req_blk > BM) {  // only possible with empty requests in between
+    if (tid == 0) flag_error(RAX_DEVERR_ROW);
+    n_req_blk = BM;
   }
-  __syncthreads();
-  const int r0 = uni(sm.hdr[0]);
-  const int nreq = uni(sm.hdr[1]);
+  const int r0 = uni(ra);
+  const int nreq = uni(n_req_blk);
   for (int i = tid; i < nreq; i += 64 * NW) {
     const int r = r0 + i;
     int row = a.req_pool_idx[r];
