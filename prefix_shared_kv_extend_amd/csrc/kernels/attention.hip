@@ -2661,7 +2661,7 @@ constexpr int kStreamTK = 32;     // keys per stage
 // (three per CU) or four (two per CU): multi-turn decode 221.6, 223.0 and 224.3 us per
 // call; six stages (one per CU) 262.7 us. With more workgroups per CU, one's start
 // (metadata, slot ids, first stage: ~5 us) runs while the others stream. With two heads
-// per workgroup: 68 KB, two workgroups (16 waves) per CU.
+// per workgroup and a 2048-key slot-id list: 72 KB, two workgroups (16 waves) per CU.
 constexpr int kStreamStages = 2;
 
 // Heads per workgroup: HP adjacent KV heads of the same (request, chunk), four waves each,
