@@ -418,18 +418,34 @@ int64_t RadixTree::promote(const int32_t* tokens, int64_t n, std::vector<int32_t
   return done;
 }
 
-bool RadixTree::lca_depth(int64_t a, int64_t b, int64_t* out) const {
-  const Node* na = find(a);
-  const Node* nb = find(b);
-  if (!na || !nb) return false;
-  // bring both to the same depth, then climb together
+// Token depth of the deepest common ancestor of two nodes: bring both to the same depth,
+// then climb together.
+static int64_t lca_of(const Node* na, const Node* nb) {
   while (na->depth_end > nb->depth_end) na = na->parent;
   while (nb->depth_end > na->depth_end) nb = nb->parent;
   while (na != nb) {
     if (na->depth_end >= nb->depth_end) na = na->parent;
     else nb = nb->parent;
   }
-  *out = na->depth_end;
+  return na->depth_end;
+}
+
+bool RadixTree::lca_depth(int64_t a, int64_t b, int64_t* out) const {
+  const Node* na = find(a);
+  const Node* nb = find(b);
+  if (!na || !nb) return false;
+  *out = lca_of(na, nb);
+  return true;
+}
+
+bool RadixTree::lca_depths(const int64_t* ids, int32_t n, int32_t* out) const {
+  const Node* prev = nullptr;
+  for (int32_t i = 0; i < n; ++i) {  // each id looked up once
+    const Node* cur = find(ids[i]);
+    if (!cur) return false;
+    out[i] = i == 0 ? 0 : static_cast<int32_t>(lca_of(prev, cur));
+    prev = cur;
+  }
   return true;
 }
 

@@ -105,6 +105,8 @@ class RadixTree {
   int lock_ref(int64_t node, int32_t delta);
   int64_t evict(int64_t num_tokens, int32_t* out_freed, int64_t cap);
   bool lca_depth(int64_t a, int64_t b, int64_t* out) const;
+  // out[0] = 0, out[i] = lca_depth(ids[i - 1], ids[i]); false if an id is unknown
+  bool lca_depths(const int64_t* ids, int32_t n, int32_t* out) const;
   const Node* find(int64_t id) const;
   int64_t dump(int64_t* buf, int64_t cap) const;  // returns words needed
 

@@ -245,12 +245,7 @@ rax_status rax_lock_ref_batch(rax_tree* t, const rax_node* nodes, int32_t n, int
 rax_status rax_lca_depths(const rax_tree* t, const rax_node* nodes, int32_t n, int32_t* out) {
   if (!t || n < 0 || (n > 0 && (!nodes || !out))) return RAX_EINVAL;
   RAX_GUARD_BEGIN
-  if (n > 0) out[0] = 0;
-  for (int32_t i = 1; i < n; ++i) {
-    int64_t d = 0;
-    if (!t->t.lca_depth(nodes[i - 1], nodes[i], &d)) return RAX_ESTATE;
-    out[i] = static_cast<int32_t>(d);
-  }
+  if (!t->t.lca_depths(nodes, n, out)) return RAX_ESTATE;
   return RAX_OK;
   RAX_GUARD_END
 }

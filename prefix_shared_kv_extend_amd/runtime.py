@@ -113,6 +113,7 @@ class RadixRuntime:
         self.len_of: dict[int, int] = {}     # current sequence length (slots in the row)
         self.n_prompt: dict[int, int] = {}
         self.node_of: dict[int, int] = {}    # locked tree node
+        self.node_by_row = np.zeros(max_reqs, dtype=np.int64)  # the same, by req_to_token row
         self.trusted_of: dict[int, int] = {}  # row positions before it hold the tree's slots
         self.log = log
         self.step = 0                        # label of the current step in the event log (set by the caller)
@@ -213,6 +214,7 @@ class RadixRuntime:
             self.trusted_of[rid] = mi
             req_rows[i] = row
         req_rows = np.array(req_rows, dtype=np.int32)
+        self.node_by_row[req_rows] = nodes
         qo = np.zeros(len(rids) + 1, dtype=np.int32)
         qo[1:] = np.cumsum(q_len)
         eb = ExtendBatch(rids, m.astype(np.int32), q_len, qo, int(qo[-1]), toks, ip,
@@ -271,6 +273,7 @@ class RadixRuntime:
         self.tree.lock_ref_batch(nodes, +1)
         self.tree.lock_ref_batch(old, -1)
         self.node_of.update(zip(rids, nodes.tolist()))
+        self.node_by_row[np.asarray(rows, dtype=np.int64)] = nodes
         self.trusted_of.update(zip(rids, n_prompt))   # duplicates switched to the tree's above
         self._sync_decode_lengths()
         self._dec_cache = None
@@ -290,8 +293,7 @@ class RadixRuntime:
         if ds is None or ds.key != key:
             self._sync_decode_lengths()
             req_rows = np.array(_take(self.row_of, rids), dtype=np.int32)
-            nodes = _take(self.node_of, rids)
-            hints = self.tree.lca_depths(nodes)
+            hints = self.tree.lca_depths(self.node_by_row[req_rows])
             inv = self._upload(dict(req_pool_idx=req_rows, shared_len=hints))
             inv["seq_len"] = self._seq_dev[: len(rids)]   # written by every step's append
             lens = np.array(_take(self.len_of, rids), dtype=np.int32)
