@@ -553,14 +553,16 @@ def test_decode_step_folded_append_equals_separate_calls():
 
 
 @pytest.mark.parametrize("h_q,h_kv,P,n_req", [(4, 2, 150, 12), (32, 4, 150, 12), (64, 4, 150, 12),
+                                             (12, 3, 150, 12), (16, 1, 150, 12),
                                              (16, 2, 2100, 256), (32, 8, 150, -72), (32, 16, 150, -64)])
 def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
     """Decode attention with query-head groups (own keys on MFMA tiles) on hand-built rows:
     a P-key prefix shared by all requests (hinted), then own ranges of 0..2600 keys, so
     that chunks are empty, shorter than a tile, exactly one or two tiles, ragged, several
-    per (request, KV head), and longer than one round of tiles. The fourth case has 64 row
+    per (request, KV head), and longer than one round of tiles. The sixth case has 64 row
     blocks and a 2100-key prefix, so the shared part runs in 4-wave workgroups with two
-    tiles per round and several rounds per split. The last two (n_req < 0: -n_req
+    tiles per round and several rounds per split. An odd number of KV heads (3, and 1)
+    takes the own part's one-head workgroups. The last two (n_req < 0: -n_req
     requests) give every request 1100..1400 own keys: with 72 x 8 (request, KV head)
     pairs, two chunks each, so many items of requests with several chunks that these merge
     in the merge kernel (in the other cases the own part's launch merges them itself); with
