@@ -38,6 +38,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -548,8 +549,10 @@ def projection_measure(dev):
     """QKV projection fused with the KV write-back, on the cached few-shot extend batch:
     3150 new tokens, hidden 4096, 32 heads x 128 (MHA), so W is [12288, 4096]. Fused: one
     kernel writes Q, the contiguous K/V and the pool rows. Unfused: the same GEMM without
-    pool writes, then rax_kv_scatter from the contiguous K/V. HIP events around 20 calls of
-    each on the current stream."""
+    pool writes, then rax_kv_scatter from the contiguous K/V. Beside them, the projection
+    alone and the library GEMM (torch.matmul) of the same shape. HIP events around 10 calls
+    of each; the four are timed in turn, 7 rounds, and each reports its median (the clock
+    drifts as the GPU warms, so a fixed order would favour the first)."""
     import torch
     from prefix_shared_kv_extend_amd import _lib
     from workloads.gen import projection_inputs
@@ -564,22 +567,35 @@ def projection_measure(dev):
     def fused():
         _lib.qkv_project(x, w, h, h, out_loc=loc, k_pool=kp, v_pool=vp, q_out=q, k_ext=k, v_ext=v)
 
-    def unfused():
+    def projection():
         _lib.qkv_project(x, w, h, h, q_out=q, k_ext=k, v_ext=v)
+
+    def unfused():
+        projection()
         _lib.kv_scatter(k, v, loc, kp, vp)
+
+    def library():
+        torch.matmul(x, w.t())
 
     out = {"workload": "cached few-shot extend batch: 3150 tokens, hidden 4096, 32 heads x 128 (W 12288 x 4096)"}
     flops = 2.0 * t * hidden * 3 * h * d
-    for name, fn in (("fused", fused), ("gemm_then_scatter", unfused)):
-        for _ in range(3):
+    fns = (("fused", fused), ("gemm_then_scatter", unfused), ("projection_only", projection),
+           ("library_gemm_same_shape", library))
+    times = {name: [] for name, _ in fns}
+    for _ in range(3):
+        for _, fn in fns:
             fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(20):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / 20
+    for _ in range(7):
+        for name, fn in fns:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times[name].append(a.elapsed_time(b) * 1e3 / 10)
+    for name, _ in fns:
+        us = statistics.median(times[name])
         out[name] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
                      "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     out["saved_us"] = out["gemm_then_scatter"]["us"] - out["fused"]["us"]

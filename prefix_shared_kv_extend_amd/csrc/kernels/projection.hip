@@ -8,19 +8,30 @@
 // contiguous suffix buffers that extend attention reads and, optionally, in the same pass
 // to the pool slots out_loc[t], in place of the separate write-back (kv_scatter) and its
 // re-read of the suffix buffers. Measured on the few-shot batch (3150 tokens, hidden
-// 4096, 32 heads x 128), the fused write-back is slower: 430 us against 364 us for the
-// projection alone plus 17 us for kv_scatter. The output tiling splits every token's
-// pool row into one 256-byte piece per head, written by different workgroups at
-// different times, whereas kv_scatter writes each 8 KB row in one go.
+// 4096, 32 heads x 128): 335 us fused against 318 us for the projection alone plus the
+// separate write-back (340 us in all). With 256-feature tiles a token's pool row is
+// written in 512-byte pieces (two heads) by different workgroups at different times,
+// whereas kv_scatter writes each 8 KB row in one go, so fusing gains little.
 //
-// Tiling: a workgroup computes a 128-token x 128-feature output tile with 4 waves (each
-// 64 x 64 = 2 x 2 MFMA tiles of 32 x 32), k in steps of 64. Both operands are
-// k-contiguous rows (tokens of x, features of W), loaded straight into LDS with 16-byte
-// global-to-LDS loads, double-buffered; one load instruction fills 8 rows of 128 bytes,
-// whose 16-byte chunk positions are XOR-swizzled by (r % 8) ^ ((r / 8) % 2) so that the
-// fragment reads (32 rows x 2 chunks) are free of bank conflicts for 128 and 256 bytes
-// of banks. C = A B^T on v_mfma_f32_32x32x16_bf16 with A = token rows, B = feature rows.
-// Epilogue: the bf16 output tile goes through LDS (rows padded to 272 bytes), then every
+// Tiling: a workgroup computes a BM-token x BN-feature output tile with WM x WN waves, each
+// a (BM / WM) x (BN / WN) block of 32 x 32 MFMA tiles, k in steps of 64. Large batches
+// take 256 x 256 tiles (8 waves of 128 x 64, 132 KB of LDS, one workgroup per CU): per
+// k step a CU loads 64 KB for 8.4 MFLOP, half the operand traffic per flop of 128 x 128
+// tiles, and a wave reads 6 fragments from LDS per 8 MFMAs instead of 4 per 4. Measured
+// on the few-shot batch: 307-332 us against 412-448 us for 128 x 128 tiles in id order
+// (the library GEMM of the same shape, timed in turn with it: 239 us; its grid of 624
+// tiles is 2.44 rounds of 256 CUs). Batches below 1024 tokens keep 128 x 128 tiles (4
+// waves of 64 x 64), so that small grids still spread over the CUs.
+// Workgroup ids go round-robin over the 8 XCDs; each XCD takes a contiguous run of the
+// tile order, and that order walks groups of 8 token blocks feature block by feature
+// block, so the workgroups running at once on one XCD share their operand rows in its
+// L2 (128 x 128 tiles: 351 us grouped against 448 us with feature blocks fastest).
+// Both operands are k-contiguous rows (tokens of x, features of W), loaded straight into
+// LDS with 16-byte global-to-LDS loads, double-buffered; one load instruction fills 8
+// rows of 128 bytes, whose 16-byte chunk positions are XOR-swizzled by
+// (r % 8) ^ ((r / 8) % 2) so that the fragment reads (32 rows x 2 chunks) are free of bank
+// conflicts. C = A B^T on v_mfma_f32_32x32x16_bf16 with A = token rows, B = feature rows.
+// Epilogue: the bf16 output tile goes through LDS (rows padded by 16 bytes), then every
 // thread writes 16-byte chunks of token rows, looking up each row's slot once: Q chunks
 // to q_out, K and V chunks to the contiguous buffers and to the pool rows.
 #include "../../../include/rax.h"
@@ -28,53 +39,73 @@
 
 namespace raxk {
 
-constexpr int kPM = 128, kPN = 128, kPK = 64;
+constexpr int kPK = 64;             // k per step
+constexpr int kPBigMinTokens = 1024;  // batches from this size take 256 x 256 tiles
+constexpr int kPGroup = 8;            // token blocks per group of the tile order
 
 __device__ __forceinline__ int pswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__global__ void __launch_bounds__(256) qkv_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w,
-                                                  int64_t t_rows, int hidden, int n_q, int n_kv,
-                                                  const int32_t* __restrict__ out_loc, int64_t num_slots,
-                                                  __bf16* __restrict__ q_out, __bf16* __restrict__ k_ext,
-                                                  __bf16* __restrict__ v_ext, __bf16* __restrict__ k_pool,
-                                                  __bf16* __restrict__ v_pool) {
-  constexpr int kTile = kPM * kPK * 2;  // bytes of one operand tile
-  __shared__ __align__(16) char smem[4 * kTile];
-  char(*sa)[kTile] = reinterpret_cast<char(*)[kTile]>(smem);              // token rows, 128 B each
-  char(*sb)[kTile] = reinterpret_cast<char(*)[kTile]>(smem + 2 * kTile);  // feature rows
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * 64)
+    qkv_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w, int64_t t_rows, int hidden, int n_q,
+               int n_kv, const int32_t* __restrict__ out_loc, int64_t num_slots, __bf16* __restrict__ q_out,
+               __bf16* __restrict__ k_ext, __bf16* __restrict__ v_ext, __bf16* __restrict__ k_pool,
+               __bf16* __restrict__ v_pool, int tm, int tn, int per_xcd) {
+  constexpr int NW = WM * WN, NT = NW * 64;
+  constexpr int kA = BM * kPK * 2, kStage = kA + BN * kPK * 2;  // operand bytes of one k step
+  constexpr int kRow = BN * 2 + 16;                              // padded output row bytes
+  constexpr int kSmem = 2 * kStage > BM * kRow ? 2 * kStage : BM * kRow;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TI = WTM / 32, TJ = WTN / 32;
+  static_assert(TI * 32 == WTM && TJ * 32 == WTN && NT >= BM, "tile shape");
+  __shared__ __align__(16) char smem[kSmem];
+  __shared__ int32_t s_slot[BM];
+  // tile of this workgroup: the XCD's run of the tile order (8 * per_xcd ids cover the
+  // tm * tn tiles; the last few ids may have none), then the grouped order
+  const int g = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (g >= tm * tn) return;
+  const int grp = g / (kPGroup * tn);
+  const int m_first = grp * kPGroup;
+  const int gm = min(kPGroup, tm - m_first);
+  const int in = g - grp * kPGroup * tn;
+  const int64_t m0 = (int64_t)(m_first + in % gm) * BM;
+  const int n0 = in / gm * BN;
+  const int n_out = n_q + 2 * n_kv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;  // this wave's 64 x 64 quadrant
+  const int wm = wave % WM, wn = wave / WM;
   const int jrow = lane & 31, half = lane >> 5;
-  // feature blocks vary fastest: a token block's rows of x are read by workgroups that run
-  // at about the same time (measured 1.13x faster than token blocks fastest)
-  const int64_t m0 = (int64_t)blockIdx.y * kPM;
-  const int n0 = blockIdx.x * kPN;
-  __shared__ int32_t s_slot[kPM];
   // the tile's slot ids, fetched now and parked in LDS by the epilogue (one per thread)
-  const int32_t my_slot = out_loc && tid < kPM && m0 + tid < t_rows ? out_loc[m0 + tid] : -1;
+  const int32_t my_slot = out_loc && tid < BM && m0 + tid < t_rows ? out_loc[m0 + tid] : -1;
 
-  // k-step ks into buffer b: 16 instructions per operand tile, wave w issues w, w + 4, ...
-  // (token rows past t_rows read the last row; their results are not stored)
+  // k step ks into buffer b: one load instruction per 8 rows, wave w issues w, w + NW, ...
+  // (token rows past t_rows and feature rows past n_out read the last row; their results
+  // are not stored)
   auto issue = [&](int ks, int b) {
     const int k0 = ks * kPK;
+    const uint32_t sa = lds_addr(smem) + b * kStage, sb = sa + kA;
 #pragma unroll
-    for (int q = wave; q < 16; q += 4) {
+    for (int q = wave; q < BM / 8; q += NW) {
       const int r = q * 8 + (lane >> 3);
       const int cs = (lane & 7) ^ pswz(r);
       const int64_t mr = m0 + r < t_rows ? m0 + r : t_rows - 1;
-      lds_load16(x + mr * hidden + k0 + cs * 8, uni32(lds_addr(&sa[b][0]) + q * 1024));
-      lds_load16(w + (int64_t)(n0 + r) * hidden + k0 + cs * 8, uni32(lds_addr(&sb[b][0]) + q * 1024));
+      lds_load16(x + mr * hidden + k0 + cs * 8, uni32(sa + q * 1024));
+    }
+#pragma unroll
+    for (int q = wave; q < BN / 8; q += NW) {
+      const int r = q * 8 + (lane >> 3);
+      const int cs = (lane & 7) ^ pswz(r);
+      const int nr = n0 + r < n_out ? n0 + r : n_out - 1;
+      lds_load16(w + (int64_t)nr * hidden + k0 + cs * 8, uni32(sb + q * 1024));
     }
   };
   auto frag = [&](const char* base, int r, int kk) {
     return *reinterpret_cast<const bf16x8*>(base + r * 128 + (((2 * kk + half) ^ pswz(r)) * 16));
   };
 
-  f32x16 c[2][2];
+  f32x16 c[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) c[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) c[i][j] = f32x16{};
   const int nks = hidden / kPK;
   // the loads are asm (see lds_load16): __syncthreads does not wait for them, so each wave
   // waits for its own with s_waitcnt before every barrier
@@ -84,47 +115,49 @@ __global__ void __launch_bounds__(256) qkv_kernel(const __bf16* __restrict__ x, 
   for (int ks = 0; ks < nks; ++ks) {
     const int b = ks & 1;
     if (ks + 1 < nks) issue(ks + 1, b ^ 1);
+    const char* sa = smem + b * kStage;
+    const char* sb = sa + kA;
 #pragma unroll
     for (int kk = 0; kk < kPK / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = frag(&sa[b][0], wm * 64 + i * 32 + jrow, kk);
+      for (int i = 0; i < TI; ++i) af[i] = frag(sa, wm * WTM + i * 32 + jrow, kk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = frag(&sb[b][0], wn * 64 + j * 32 + jrow, kk);
+      for (int j = 0; j < TJ; ++j) bfr[j] = frag(sb, wn * WTN + j * 32 + jrow, kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], c[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], c[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // next buffer loaded by every wave; this one read by every wave
   }
 
-  // register r of tile (i, j): token wm*64 + i*32 + 8*(r/4) + 4*half + r%4, feature
-  // wn*64 + j*32 + l%32 of the workgroup's tile; into LDS as bf16 (the operand buffers
+  // register r of tile (i, j): token wm*WTM + i*32 + 8*(r/4) + 4*half + r%4, feature
+  // wn*WTN + j*32 + l%32 of the workgroup's tile; into LDS as bf16 (the operand buffers
   // are free after the loop's last barrier)
-  constexpr int kRow = kPN * 2 + 16;  // padded row bytes
-  static_assert(kPM * kRow <= (int)sizeof(smem), "output tile");
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int n = wn * 64 + j * 32 + jrow;
+        const int m = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int n = wn * WTN + j * 32 + jrow;
         *reinterpret_cast<__bf16*>(smem + m * kRow + n * 2) = (__bf16)c[i][j][r];
       }
-  if (tid < kPM) s_slot[tid] = my_slot;
+  if (tid < BM) s_slot[tid] = my_slot;
   __syncthreads();
-  // 128 rows x 16 chunks of 8 features; chunk boundaries never straddle Q / K / V (their
-  // sizes are multiples of d, and d of 8)
-  for (int e = tid; e < kPM * (kPN / 8); e += 256) {
-    const int rr = e >> 4, ch = e & 15;
+  // BM rows x BN / 8 chunks of 8 features; chunk boundaries never straddle Q / K / V (their
+  // sizes are multiples of d, and d of 8); with BN = 256 the last feature block may reach
+  // past n_out (a multiple of 128): those features were computed from the last W row and
+  // are not stored
+  for (int e = tid; e < BM * (BN / 8); e += NT) {
+    const int rr = e / (BN / 8), ch = e % (BN / 8);
     const int64_t m = m0 + rr;
-    if (m >= t_rows) continue;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(smem + rr * kRow + ch * 16);
     const int n = n0 + ch * 8;
+    if (m >= t_rows || n >= n_out) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(smem + rr * kRow + ch * 16);
     if (n < n_q) {
       *reinterpret_cast<u32x4*>(q_out + m * n_q + n) = val;
     } else {
@@ -148,18 +181,24 @@ extern "C" rax_status rax_qkv_project(const void* x, const void* w, int64_t n_to
                                       void* stream) {
   if (n_tok < 0 || hidden < 1 || h_q < 1 || h_kv < 1 || d < 8 || d % 8 || dt != RAX_BF16) return RAX_EINVAL;
   const int64_t n_out = (int64_t)(h_q + 2 * h_kv) * d;
-  if (hidden % raxk::kPK || n_out % raxk::kPN || n_out > INT32_MAX || (int64_t)h_q * d > INT32_MAX) return RAX_EINVAL;
+  if (hidden % raxk::kPK || n_out % 128 || n_out > INT32_MAX / 2) return RAX_EINVAL;
   if (n_tok == 0) return RAX_OK;
   if (!x || !w || !q_out || !k_ext || !v_ext) return RAX_EINVAL;
   if (out_loc && (!k_pool || !v_pool || num_slots < 1)) return RAX_EINVAL;
   if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)q_out | (uintptr_t)k_ext | (uintptr_t)v_ext |
        (uintptr_t)(out_loc ? k_pool : nullptr) | (uintptr_t)(out_loc ? v_pool : nullptr)) & 15)
     return RAX_EINVAL;
-  const int64_t m_blocks = (n_tok + raxk::kPM - 1) / raxk::kPM;
-  if (m_blocks > 65535) return RAX_EINVAL;
-  const dim3 grid((unsigned)(n_out / raxk::kPN), (unsigned)m_blocks);
-  hipLaunchKernelGGL(raxk::qkv_kernel, grid, dim3(256), 0, (hipStream_t)stream, (const __bf16*)x, (const __bf16*)w,
-                     n_tok, hidden, h_q * d, h_kv * d, out_loc, num_slots, (__bf16*)q_out, (__bf16*)k_ext,
-                     (__bf16*)v_ext, (__bf16*)k_pool, (__bf16*)v_pool);
+  const bool big = n_tok >= raxk::kPBigMinTokens;
+  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
+  const int64_t tm = (n_tok + bm - 1) / bm, tn = (n_out + bn - 1) / bn;
+  if (tm * tn > (1 << 28)) return RAX_EINVAL;
+  const int per = (int)((tm * tn + 7) / 8);  // tiles per XCD; 8 * per ids
+  auto go = [&](auto kernel, int threads) {
+    hipLaunchKernelGGL(kernel, dim3(8 * per), dim3(threads), 0, (hipStream_t)stream, (const __bf16*)x,
+                       (const __bf16*)w, n_tok, hidden, h_q * d, h_kv * d, out_loc, num_slots, (__bf16*)q_out,
+                       (__bf16*)k_ext, (__bf16*)v_ext, (__bf16*)k_pool, (__bf16*)v_pool, (int)tm, (int)tn, per);
+  };
+  if (big) go(raxk::qkv_kernel<256, 256, 2, 4>, 512);
+  else go(raxk::qkv_kernel<128, 128, 2, 2>, 256);
   return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
 }
