@@ -555,6 +555,60 @@ def test_decode_step_folded_append_equals_separate_calls():
     assert _lib.device_errors() == 0
 
 
+def test_decode_step_above_append_limit_every_output():
+    """A decode step of 300 requests, more than the 256 whose append one attention launch
+    can carry: rax_decode_step appends in a launch of its own, and the attention, laid out
+    from the host's lengths and hints, runs without a host work list (requests in batch
+    order). Runtime path (GQA 16/4, bf16, a 96-token prefix shared by all prompts), two
+    steps; after each, the new tokens' K/V rows in the pools equal the inputs bit for bit,
+    and every output is compared with fp64 attention over the request's keys read back
+    from the pools (oracle.attention.attend)."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    from prefix_shared_kv_extend_amd.runtime import RadixRuntime
+    h_q, h_kv, d, B = 16, 4, 128, 300
+    say(f"decode step above the folded-append limit: {B} requests, GQA {h_q}/{h_kv}")
+    rng = np.random.default_rng(31)
+    pre = rng.integers(0, 50, 96)
+    prompts = [np.concatenate([pre, rng.integers(0, 50, int(rng.integers(1, 40)))]).astype(np.int32)
+               for _ in range(B)]
+    gen = torch.Generator().manual_seed(17)
+
+    def rnd(*shape):
+        return torch.randn(shape, generator=gen).to(torch.bfloat16).cuda()
+
+    rt = RadixRuntime(32768, h_q, h_kv, d, torch.bfloat16, B, 256)
+    # the first prompt alone, so that the others find the prefix in the tree
+    for part in (list(enumerate(prompts))[:1], list(enumerate(prompts))[1:]):
+        eb = rt.begin_extend(part)
+        t = eb.total_q
+        rt.run_extend(eb, rnd(t, h_q, d), rnd(t, h_kv, d), rnd(t, h_kv, d),
+                      torch.empty((t, h_q, d), dtype=torch.bfloat16, device="cuda"))
+        rt.end_extend(eb)
+    assert int(np.min(eb.prefix_len)) >= len(pre)
+    rids = list(range(B))
+    worst = 0.0
+    for step in range(2):
+        qd, kd, vd = rnd(B, h_q, d), rnd(B, h_kv, d), rnd(B, h_kv, d)
+        o = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
+        db = rt.begin_decode(rids)
+        rt.run_decode(db, qd, kd, vd, o)
+        torch.cuda.synchronize()
+        assert _lib.device_errors() == 0
+        ds = rt._dec_cache
+        assert np.array_equal(ds.lens, db.seq_len)
+        kf, vf = rt.k_pool.cpu(), rt.v_pool.cpu()
+        newest = torch.as_tensor(rt.rows[ds.req_rows, ds.lens - 1].astype(np.int64))
+        assert torch.equal(kf[newest], kd.cpu()) and torch.equal(vf[newest], vd.cpu()), f"step {step}"
+        kf, vf, qf, got = kf.float().numpy(), vf.float().numpy(), qd.float().cpu().numpy(), o.float().cpu().numpy()
+        for i in range(B):
+            sl = rt.rows[ds.req_rows[i], : ds.lens[i]]
+            err = float(np.abs(got[i] - attend(qf[i], kf[sl], vf[sl])).max())
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], f"step {step}, request {i}: max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {B} requests x 2 steps")
+
+
 @pytest.mark.parametrize("h_q,h_kv,P,n_req", [(4, 2, 150, 12), (32, 4, 150, 12), (64, 4, 150, 12),
                                              (12, 3, 150, 12), (16, 1, 150, 12),
                                              (16, 2, 2100, 256), (32, 8, 150, -72), (32, 16, 150, -64)])
