@@ -18,10 +18,13 @@
 // take 256 x 256 tiles (8 waves of 128 x 64, 132 KB of LDS, one workgroup per CU): per
 // k step a CU loads 64 KB for 8.4 MFLOP, half the operand traffic per flop of 128 x 128
 // tiles, and a wave reads 6 fragments from LDS per 8 MFMAs instead of 4 per 4. Measured
-// on the few-shot batch: 307-332 us against 412-448 us for 128 x 128 tiles in id order
-// (the library GEMM of the same shape, timed in turn with it: 239 us; its grid of 624
-// tiles is 2.44 rounds of 256 CUs). Batches below 1024 tokens keep 128 x 128 tiles (4
-// waves of 64 x 64), so that small grids still spread over the CUs.
+// on the few-shot batch: 307-332 us against 412-448 us for 128 x 128 tiles in id order.
+// Batches below 1024 tokens keep 128 x 128 tiles (4 waves of 64 x 64), so that small
+// grids still spread over the CUs.
+// A grid whose last round of resident workgroups would be at most half full (the
+// few-shot batch: 624 tiles, 2.44 rounds of 256 CUs) runs that round's tiles as halves
+// of BM / 2 tokens, dispatched last, so it takes about half a round: 287 us against
+// 318 us (the library GEMM of the same shape, timed in turn with it: 227 and 239 us).
 // Workgroup ids go round-robin over the 8 XCDs; each XCD takes a contiguous run of the
 // tile order, and that order walks groups of 8 token blocks feature block by feature
 // block, so the workgroups running at once on one XCD share their operand rows in its
@@ -45,30 +48,37 @@ constexpr int kPGroup = 8;            // token blocks per group of the tile orde
 
 __device__ __forceinline__ int pswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(WM * WN * 64)
-    qkv_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w, int64_t t_rows, int hidden, int n_q,
-               int n_kv, const int32_t* __restrict__ out_loc, int64_t num_slots, __bf16* __restrict__ q_out,
-               __bf16* __restrict__ k_ext, __bf16* __restrict__ v_ext, __bf16* __restrict__ k_pool,
-               __bf16* __restrict__ v_pool, int tm, int tn, int per_xcd) {
-  constexpr int NW = WM * WN, NT = NW * 64;
-  constexpr int kA = BM * kPK * 2, kStage = kA + BN * kPK * 2;  // operand bytes of one k step
-  constexpr int kRow = BN * 2 + 16;                              // padded output row bytes
-  constexpr int kSmem = 2 * kStage > BM * kRow ? 2 * kStage : BM * kRow;
-  constexpr int WTM = BM / WM, WTN = BN / WN, TI = WTM / 32, TJ = WTN / 32;
-  static_assert(TI * 32 == WTM && TJ * 32 == WTN && NT >= BM, "tile shape");
-  __shared__ __align__(16) char smem[kSmem];
-  __shared__ int32_t s_slot[BM];
-  // tile of this workgroup: the XCD's run of the tile order (8 * per_xcd ids cover the
-  // tm * tn tiles; the last few ids may have none), then the grouped order
-  const int g = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (g >= tm * tn) return;
+// LDS bytes of a BM x BN tile: two k steps of both operands, reused for the output tile
+template <int BM, int BN>
+constexpr int qkv_smem() {
+  return 2 * (BM + BN) * kPK * 2 > BM * (BN * 2 + 16) ? 2 * (BM + BN) * kPK * 2 : BM * (BN * 2 + 16);
+}
+
+// First token and first feature of tile g of the grouped order: groups of kPGroup token
+// blocks, each walked feature block by feature block, token blocks fastest.
+__device__ __forceinline__ void tile_origin(int g, int tm, int tn, int bm, int bn, int64_t& m0, int& n0) {
   const int grp = g / (kPGroup * tn);
   const int m_first = grp * kPGroup;
   const int gm = min(kPGroup, tm - m_first);
   const int in = g - grp * kPGroup * tn;
-  const int64_t m0 = (int64_t)(m_first + in % gm) * BM;
-  const int n0 = in / gm * BN;
+  m0 = (int64_t)(m_first + in % gm) * bm;
+  n0 = in / gm * bn;
+}
+
+// One BM x BN output tile at (m0, n0) computed by the workgroup's WM x WN waves.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void qkv_tile(const __bf16* __restrict__ x, const __bf16* __restrict__ w,
+                                         int64_t t_rows, int hidden, int n_q, int n_kv,
+                                         const int32_t* __restrict__ out_loc, int64_t num_slots,
+                                         __bf16* __restrict__ q_out, __bf16* __restrict__ k_ext,
+                                         __bf16* __restrict__ v_ext, __bf16* __restrict__ k_pool,
+                                         __bf16* __restrict__ v_pool, int64_t m0, int n0, char* smem,
+                                         int32_t* s_slot) {
+  constexpr int NW = WM * WN, NT = NW * 64;
+  constexpr int kA = BM * kPK * 2, kStage = kA + BN * kPK * 2;  // operand bytes of one k step
+  constexpr int kRow = BN * 2 + 16;                              // padded output row bytes
+  constexpr int WTM = BM / WM, WTN = BN / WN, TI = WTM / 32, TJ = WTN / 32;
+  static_assert(TI * 32 == WTM && TJ * 32 == WTN && NT >= BM, "tile shape");
   const int n_out = n_q + 2 * n_kv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave % WM, wn = wave / WM;
@@ -173,6 +183,39 @@ __global__ void __launch_bounds__(WM * WN * 64)
   }
 }
 
+// Large tiles, and the last round's tiles in two halves: the ids below 8 * per_xcd take
+// whole BM x BN tiles (each XCD a contiguous run of the first n_whole tiles of the
+// order); the ids above take the remaining tiles as BM / 2-token halves, dispatched last.
+// When the whole tiles fill the CUs some rounds over and a partial round is left, half
+// tiles run that round in about half the time (the host sets n_whole and the grid).
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * 64)
+    qkv_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w, int64_t t_rows, int hidden, int n_q,
+               int n_kv, const int32_t* __restrict__ out_loc, int64_t num_slots, __bf16* __restrict__ q_out,
+               __bf16* __restrict__ k_ext, __bf16* __restrict__ v_ext, __bf16* __restrict__ k_pool,
+               __bf16* __restrict__ v_pool, int tm, int tn, int per_xcd, int n_whole) {
+  constexpr int kSmem = qkv_smem<BM, BN>() > qkv_smem<BM / 2, BN>() ? qkv_smem<BM, BN>() : qkv_smem<BM / 2, BN>();
+  __shared__ __align__(16) char smem[kSmem];
+  __shared__ int32_t s_slot[BM];
+  const int b = (int)blockIdx.x;
+  int64_t m0;
+  int n0;
+  if (b < 8 * per_xcd) {
+    const int g = (b & 7) * per_xcd + (b >> 3);
+    if (g >= n_whole) return;
+    tile_origin(g, tm, tn, BM, BN, m0, n0);
+    qkv_tile<BM, BN, WM, WN>(x, w, t_rows, hidden, n_q, n_kv, out_loc, num_slots, q_out, k_ext, v_ext, k_pool,
+                             v_pool, m0, n0, smem, s_slot);
+  } else {
+    const int h = b - 8 * per_xcd;
+    tile_origin(n_whole + h / 2, tm, tn, BM, BN, m0, n0);
+    m0 += (h & 1) * (BM / 2);
+    if (m0 >= t_rows) return;
+    qkv_tile<BM / 2, BN, WM, WN>(x, w, t_rows, hidden, n_q, n_kv, out_loc, num_slots, q_out, k_ext, v_ext, k_pool,
+                                 v_pool, m0, n0, smem, s_slot);
+  }
+}
+
 }  // namespace raxk
 
 extern "C" rax_status rax_qkv_project(const void* x, const void* w, int64_t n_tok, int32_t hidden, int32_t h_q,
@@ -192,11 +235,17 @@ extern "C" rax_status rax_qkv_project(const void* x, const void* w, int64_t n_to
   const int bm = big ? 256 : 128, bn = big ? 256 : 128;
   const int64_t tm = (n_tok + bm - 1) / bm, tn = (n_out + bn - 1) / bn;
   if (tm * tn > (1 << 28)) return RAX_EINVAL;
-  const int per = (int)((tm * tn + 7) / 8);  // tiles per XCD; 8 * per ids
+  // workgroups resident at once (256 CUs; one 256 x 256 workgroup per CU, two 128 x 128);
+  // a last round less than half full runs as half tiles
+  const int64_t tiles = tm * tn, slots = big ? 256 : 512, rem = tiles % slots;
+  const int64_t whole = tiles > slots && rem > 0 && 2 * rem <= slots ? tiles - rem : tiles;
+  const int per = (int)((whole + 7) / 8);  // whole tiles per XCD; 8 * per ids
+  const unsigned grid = (unsigned)(8 * (int64_t)per + 2 * (tiles - whole));
   auto go = [&](auto kernel, int threads) {
-    hipLaunchKernelGGL(kernel, dim3(8 * per), dim3(threads), 0, (hipStream_t)stream, (const __bf16*)x,
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream, (const __bf16*)x,
                        (const __bf16*)w, n_tok, hidden, h_q * d, h_kv * d, out_loc, num_slots, (__bf16*)q_out,
-                       (__bf16*)k_ext, (__bf16*)v_ext, (__bf16*)k_pool, (__bf16*)v_pool, (int)tm, (int)tn, per);
+                       (__bf16*)k_ext, (__bf16*)v_ext, (__bf16*)k_pool, (__bf16*)v_pool, (int)tm, (int)tn, per,
+                       (int)whole);
   };
   if (big) go(raxk::qkv_kernel<256, 256, 2, 4>, 512);
   else go(raxk::qkv_kernel<128, 128, 2, 2>, 256);

@@ -418,13 +418,17 @@ def test_full_multi_turn_fixed_requests_every_step():
 
 # ------------------------------------------------------------- QKV projection (fused write-back)
 @pytest.mark.parametrize("t,hidden,h_q,h_kv,d", [(300, 256, 4, 2, 128), (77, 512, 8, 2, 64), (1, 128, 1, 1, 128),
-                                                  (1100, 256, 1, 1, 128), (1300, 512, 8, 2, 64)])
+                                                  (1100, 256, 1, 1, 128), (1300, 512, 8, 2, 64),
+                                                  (800, 128, 32, 32, 128), (1500, 128, 32, 32, 128)])
 def test_qkv_project_small(t, hidden, h_q, h_kv, d):
     """Every output of the fused projection against the fp64 oracle (bf16 rounding of fp32
     sums: max-abs 2e-2 at values of order 1), and the pool rows bit for bit equal to the
     contiguous K/V outputs; untouched pool rows stay zero. From 1024 tokens the kernel takes
     256 x 256 tiles: 1100 tokens (a ragged last token block) with 384 output features (the
-    second feature block half past the end), and 1300 tokens with 768."""
+    second feature block half past the end), and 1300 tokens with 768. With 12288 output
+    features, 800 tokens make 672 tiles of 128 x 128 and 1500 tokens 288 of 256 x 256, so
+    the last partial round (160 and 32 tiles) runs as half tiles, the ragged last token
+    block among them."""
     from oracle.projection import qkv_project
     from prefix_shared_kv_extend_amd import _lib
     from workloads.gen import projection_inputs
