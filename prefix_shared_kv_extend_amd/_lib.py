@@ -111,7 +111,9 @@ def lib() -> ctypes.CDLL:
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
             f.restype = res
-            f.argtypes = args
+            # array pointers as void pointers: they take addresses as ints (_ptr) as well as
+            # ctypes pointer objects; the table keeps the element types for the reader
+            f.argtypes = [_vp if t in (_c_i32p, _c_i64p) else t for t in args]
         _lib = L
     return _lib
 
@@ -134,6 +136,13 @@ def _i32arr(x) -> np.ndarray:
 
 def _p32(a: np.ndarray):
     return a.ctypes.data_as(_c_i32p)
+
+
+def _ptr(a: np.ndarray) -> int:
+    """Address of a contiguous host array, for an entry point's pointer argument (the
+    argument types are void pointers, so the int goes straight through; several times
+    cheaper than building a ctypes pointer object)."""
+    return a.__array_interface__["data"][0]
 
 
 def status_str(st: int) -> str:
@@ -164,7 +173,7 @@ class Tree:
         t = _i32arr(tokens)
         out = np.empty(len(t), dtype=np.int32)
         m, node = _i64(), _i64()
-        _check(self._L.rax_match_prefix(self._h, _p32(t), len(t), _p32(out), ctypes.byref(m),
+        _check(self._L.rax_match_prefix(self._h, _ptr(t), len(t), _ptr(out), ctypes.byref(m),
                                         ctypes.byref(node)), "rax_match_prefix")
         return int(m.value), out[: m.value], int(node.value)
 
@@ -174,7 +183,7 @@ class Tree:
             raise ValueError("tokens and slots differ in length")
         out = np.empty(len(t), dtype=np.int32)
         ex, node = _i64(), _i64()
-        _check(self._L.rax_insert(self._h, _p32(t), _p32(s), len(t), _p32(out), ctypes.byref(ex),
+        _check(self._L.rax_insert(self._h, _ptr(t), _ptr(s), len(t), _ptr(out), ctypes.byref(ex),
                                   ctypes.byref(node)), "rax_insert")
         return int(ex.value), int(node.value), out
 
@@ -183,20 +192,20 @@ class Tree:
 
     def evict_lru(self, num_tokens: int) -> np.ndarray:
         n = _i64()
-        _check(self._L.rax_evict_lru(self._h, int(num_tokens), _p32(self._freed), self.num_slots,
+        _check(self._L.rax_evict_lru(self._h, int(num_tokens), _ptr(self._freed), self.num_slots,
                                      ctypes.byref(n)), "rax_evict_lru")
         return self._freed[: n.value].copy()
 
     def alloc_slots(self, n: int) -> np.ndarray:
         out = np.empty(int(n), dtype=np.int32)
-        _check(self._L.rax_alloc_slots(self._h, int(n), _p32(out)), "rax_alloc_slots")
+        _check(self._L.rax_alloc_slots(self._h, int(n), _ptr(out)), "rax_alloc_slots")
         return out
 
     def alloc_slots_evict(self, n: int):
         """(slots, freed) -- evicts LRU leaves first when the free set is short."""
         out = np.empty(int(n), dtype=np.int32)
         nf = _i64()
-        st = self._L.rax_alloc_slots_evict(self._h, int(n), _p32(out), _p32(self._freed), self.num_slots,
+        st = self._L.rax_alloc_slots_evict(self._h, int(n), _ptr(out), _ptr(self._freed), self.num_slots,
                                            ctypes.byref(nf))
         _check(st, "rax_alloc_slots_evict")
         return out, self._freed[: nf.value].copy()
@@ -218,7 +227,7 @@ class Tree:
         out = np.empty(n, dtype=np.int32)
         nf = _i64()
         st = self._L.rax_decode_append(
-            self._h, n, _p32(seq_len), _p32(out), _p32(self._freed), self.num_slots, ctypes.byref(nf),
+            self._h, n, _ptr(seq_len), _ptr(out), _ptr(self._freed), self.num_slots, ctypes.byref(nf),
             _dev(req_pool_idx), _dev(seq_len_dev), _dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
             _dev(k_new), _dev(v_new), _dev(k_pool), _dev(v_pool), k_pool.shape[1], k_pool.shape[2],
             _dtype_code(k_pool), _stream(stream, k_pool))
@@ -308,8 +317,8 @@ class Tree:
         cap = 2 * self.num_slots + len(t)
         freed = np.empty(cap, dtype=np.int32)
         nf = _i64()
-        _check(self._L.rax_promote_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), b,
-                                         out.ctypes.data_as(_c_i64p), _p32(freed), cap, ctypes.byref(nf)),
+        _check(self._L.rax_promote_batch(self._h, _ptr(t), _ptr(ip), b,
+                                         _ptr(out), _ptr(freed), cap, ctypes.byref(nf)),
                "rax_promote_batch")
         if nf.value > cap:
             raise RuntimeError("rax_promote_batch: eviction report truncated")
@@ -320,7 +329,7 @@ class Tree:
         n = _i64()
         _check(self._L.rax_take_moves(self._h, None, None, None, 0, ctypes.byref(n)), "rax_take_moves")
         k, s, d = (np.empty(max(n.value, 1), dtype=np.int32) for _ in range(3))
-        _check(self._L.rax_take_moves(self._h, _p32(k), _p32(s), _p32(d), len(k), ctypes.byref(n)),
+        _check(self._L.rax_take_moves(self._h, _ptr(k), _ptr(s), _ptr(d), len(k), ctypes.byref(n)),
                "rax_take_moves")
         return k[: n.value].copy(), s[: n.value].copy(), d[: n.value].copy()
 
@@ -338,7 +347,7 @@ class Tree:
 
     def free_slots(self, slots) -> None:
         s = _i32arr(slots)
-        _check(self._L.rax_free_slots(self._h, _p32(s), len(s)), "rax_free_slots")
+        _check(self._L.rax_free_slots(self._h, _ptr(s), len(s)), "rax_free_slots")
 
     def match_prefix_batch(self, tokens_flat, indptr, cut_full=True, lock=True):
         """Batched match (and lock) of requests tokens_flat[indptr[r]:indptr[r+1]].
@@ -349,9 +358,9 @@ class Tree:
         out = np.empty(max(len(t), 1), dtype=np.int32)
         m = np.empty(b, dtype=np.int64)
         nodes = np.empty(b, dtype=np.int64)
-        _check(self._L.rax_match_prefix_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), b, int(cut_full),
-                                              int(lock), _p32(out), m.ctypes.data_as(_c_i64p),
-                                              nodes.ctypes.data_as(_c_i64p)), "rax_match_prefix_batch")
+        _check(self._L.rax_match_prefix_batch(self._h, _ptr(t), _ptr(ip), b, int(cut_full),
+                                              int(lock), _ptr(out), _ptr(m),
+                                              _ptr(nodes)), "rax_match_prefix_batch")
         return out[: len(t)], m, nodes
 
     def prefix_len_batch(self, tokens_flat, indptr) -> np.ndarray:
@@ -359,8 +368,8 @@ class Tree:
         t = _i32arr(tokens_flat)
         ip = np.ascontiguousarray(indptr, dtype=np.int64)
         out = np.empty(len(ip) - 1, dtype=np.int64)
-        _check(self._L.rax_prefix_len_batch(self._h, _p32(t), ip.ctypes.data_as(_c_i64p), len(ip) - 1,
-                                            out.ctypes.data_as(_c_i64p)), "rax_prefix_len_batch")
+        _check(self._L.rax_prefix_len_batch(self._h, _ptr(t), _ptr(ip), len(ip) - 1,
+                                            _ptr(out)), "rax_prefix_len_batch")
         return out
 
     def schedule_order(self, policy: int, tokens_flat, indptr, seed: int = 0):
@@ -371,8 +380,8 @@ class Tree:
         b = len(ip) - 1
         order = np.empty(b, dtype=np.int32)
         m = np.empty(b, dtype=np.int64)
-        _check(self._L.rax_schedule_order(self._h, int(policy), _p32(t), ip.ctypes.data_as(_c_i64p), b,
-                                          int(seed) & (2 ** 64 - 1), _p32(order), m.ctypes.data_as(_c_i64p)),
+        _check(self._L.rax_schedule_order(self._h, int(policy), _ptr(t), _ptr(ip), b,
+                                          int(seed) & (2 ** 64 - 1), _ptr(order), _ptr(m)),
                "rax_schedule_order")
         return order, m
 
@@ -385,8 +394,8 @@ class Tree:
         ex = np.empty(b, dtype=np.int64)
         nodes = np.empty(b, dtype=np.int64)
         done = ctypes.c_int32()
-        _check(self._L.rax_insert_batch(self._h, _p32(t), _p32(sl), ip.ctypes.data_as(_c_i64p), b, _p32(out),
-                                        ex.ctypes.data_as(_c_i64p), nodes.ctypes.data_as(_c_i64p),
+        _check(self._L.rax_insert_batch(self._h, _ptr(t), _ptr(sl), _ptr(ip), b, _ptr(out),
+                                        _ptr(ex), _ptr(nodes),
                                         ctypes.byref(done)), "rax_insert_batch")
         return out[: len(t)], ex, nodes
 
@@ -404,22 +413,22 @@ class Tree:
         ex = np.empty(b, dtype=np.int64)
         nodes = np.empty(b, dtype=np.int64)
         done = ctypes.c_int32()
-        _check(self._L.rax_insert_batch_from(self._h, st.ctypes.data_as(_c_i64p), tr.ctypes.data_as(_c_i64p),
-                                             _p32(t), _p32(sl),
-                                             ip.ctypes.data_as(_c_i64p), b, _p32(out), ex.ctypes.data_as(_c_i64p),
-                                             nodes.ctypes.data_as(_c_i64p), ctypes.byref(done)),
+        _check(self._L.rax_insert_batch_from(self._h, _ptr(st), _ptr(tr),
+                                             _ptr(t), _ptr(sl),
+                                             _ptr(ip), b, _ptr(out), _ptr(ex),
+                                             _ptr(nodes), ctypes.byref(done)),
                "rax_insert_batch_from")
         return out[: len(t)], ex, nodes
 
     def lock_ref_batch(self, nodes, delta: int) -> None:
         nd = np.ascontiguousarray(nodes, dtype=np.int64)
-        _check(self._L.rax_lock_ref_batch(self._h, nd.ctypes.data_as(_c_i64p), len(nd), int(delta)),
+        _check(self._L.rax_lock_ref_batch(self._h, _ptr(nd), len(nd), int(delta)),
                "rax_lock_ref_batch")
 
     def lca_depths(self, nodes) -> np.ndarray:
         nd = np.ascontiguousarray(nodes, dtype=np.int64)
         out = np.zeros(len(nd), dtype=np.int32)
-        _check(self._L.rax_lca_depths(self._h, nd.ctypes.data_as(_c_i64p), len(nd), _p32(out)), "rax_lca_depths")
+        _check(self._L.rax_lca_depths(self._h, _ptr(nd), len(nd), _ptr(out)), "rax_lca_depths")
         return out
 
     def lca_depth(self, a: int, b: int) -> int:
@@ -437,7 +446,7 @@ class Tree:
         n = _i64()
         _check(self._L.rax_tree_dump(self._h, None, 0, ctypes.byref(n)), "rax_tree_dump")
         buf = np.empty(max(1, n.value), dtype=np.int64)
-        _check(self._L.rax_tree_dump(self._h, buf.ctypes.data_as(_c_i64p), len(buf), ctypes.byref(n)),
+        _check(self._L.rax_tree_dump(self._h, _ptr(buf), len(buf), ctypes.byref(n)),
                "rax_tree_dump")
         out, i, words = [], 0, buf[: n.value].tolist()
         while i < len(words):
@@ -598,7 +607,7 @@ def decode_attention_hinted(q, k_pool, v_pool, req_to_token, req_pool_idx, seq_l
         _dev(q), _dev(k_pool), _dev(v_pool), k_pool.shape[0], _dev(req_to_token), req_to_token.shape[1],
         req_to_token.shape[0], _dev(req_pool_idx), _dev(seq_len), _dev(shared_len), b, int(max_seq_len),
         q.shape[1], k_pool.shape[1], d, scale, _dtype_code(q), _dev(o), _dtype_code(o), _dev(workspace), ws,
-        _stream(stream, q), _p32(sl), _p32(sh), ctypes.byref(need))
+        _stream(stream, q), _ptr(sl), _ptr(sh), ctypes.byref(need))
     if st == EINVAL and need.value > ws:
         return int(need.value)
     _check(st, "rax_decode_attention_hinted")
