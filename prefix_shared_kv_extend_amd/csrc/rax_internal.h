@@ -33,10 +33,6 @@ struct AppendJob {
 // AppendJob (bf16, D = 128, split decode, batch <= kAppendMax).
 bool decode_folds_append(int32_t batch, int32_t h_q, int32_t h_kv, int32_t d, rax_dtype dt);
 
-// rax_decode_attention, with an optional append carried by its first kernel (seq_len is
-// then read from the job, not from memory, by that kernel).
-// What the host knows of a decode batch from host copies of its lengths and hints
-// (decode_hint); zeros: nothing, the layout follows the longest sequence.
 // Work list of the own-part workgroups (own_stream_kernel), from host copies of the
 // lengths and hints: requests by descending own keys, each request's chunks (and in a
 // chunk its KV heads) together, so that the longest start first and the shortest fill the
@@ -50,6 +46,8 @@ struct OwnOrder {
   uint16_t req[kAppendMax];
   uint16_t cum[kAppendMax + 1];
 };
+// What the host knows of a decode batch from host copies of its lengths and hints
+// (decode_hint); zeros: nothing, the layout follows the longest sequence.
 struct DecodeHint {
   int32_t tiles = 0;  // the most 64-key tiles the shared-prefix part of any row block computes
   int32_t own = 0;    // the most own keys of any request (past its block's or run's shared keys)
