@@ -690,6 +690,62 @@ def test_decode_query_head_groups_direct(h_q, h_kv, P, n_req):
     say(f"  worst max-abs {worst:.3g} over {len(check)} requests, plain and hinted layouts")
 
 
+@pytest.mark.parametrize("h_q,h_kv,d,dt", [(32, 8, 128, "bf16"), (16, 16, 128, "bf16"), (8, 8, 64, "f32")])
+def test_decode_long_request_many_own_chunks(h_q, h_kv, d, dt):
+    """Decode where one request holds 20,000 own keys past a 100-key shared prefix, beside
+    requests of 3000, 64, 1 and 0 own keys: the long request's own part is cut into many
+    chunks (more than the four of shorter requests, more than the eight the MHA own part
+    merges by itself), whose partials the merge combines with the shared part's splits.
+    GQA 32/8 and MHA in bf16 (D = 128), MHA in fp32 (D = 64); plain and hinted layouts;
+    every output against fp64 attention over the request's keys (oracle.attention.attend)."""
+    from oracle.attention import attend
+    from prefix_shared_kv_extend_amd import _lib
+    say(f"decode, one request of 20000 own keys: {h_q}/{h_kv} heads, d={d}, {dt}")
+    P, own = 100, [20000, 1, 0, 3000, 64]
+    B = len(own)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    lens = np.array([P + n + 1 for n in own], dtype=np.int32)
+    S = int(lens.sum()) + 64
+    W = int(lens.max()) + 3
+    gen = torch.Generator().manual_seed(41 + h_q + d)
+    k_pool = torch.randn((S, h_kv, d), generator=gen).to(tdt)
+    v_pool = torch.randn((S, h_kv, d), generator=gen).to(tdt)
+    q = torch.randn((B, h_q, d), generator=gen).to(tdt)
+    perm = torch.randperm(S, generator=gen).numpy().astype(np.int32)
+    rtt = np.full((B + 2, W), -1, dtype=np.int32)
+    rows = np.array([3, 0, 5, 1, 2], dtype=np.int32)
+    used = P
+    for i in range(B):
+        rtt[rows[i], :P] = perm[:P]
+        rtt[rows[i], P:lens[i]] = perm[used: used + lens[i] - P]
+        used += lens[i] - P
+    assert used <= S
+    hints = np.full(B, P, dtype=np.int32)
+    dev = lambda x: torch.as_tensor(x).cuda()
+    ws = torch.empty(_lib.attention_workspace_bytes(True, B, h_q, h_kv, d, int(lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    ob = torch.empty((B, h_q, d), dtype=torch.float32, device="cuda")
+    _lib.decode_attention(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows), dev(lens), int(lens.max()), ob,
+                          workspace=ws, shared_len=dev(hints))
+    oh = torch.empty_like(ob)
+    hinted = lambda w: _lib.decode_attention_hinted(dev(q), dev(k_pool), dev(v_pool), dev(rtt), dev(rows),
+                                                    dev(lens), int(lens.max()), oh, lens, hints, workspace=w,
+                                                    shared_len=dev(hints))
+    hinted(torch.empty(hinted(None), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert _lib.device_errors() == 0
+    kf, vf, qf = k_pool.double().numpy(), v_pool.double().numpy(), q.double().numpy()
+    worst = 0.0
+    for i in range(B):
+        sl = rtt[rows[i], : lens[i]]
+        ref = attend(qf[i], kf[sl], vf[sl])
+        for got in (ob.cpu().numpy(), oh.cpu().numpy()):
+            err = float(np.abs(got[i] - ref).max())
+            worst = max(worst, err)
+            assert err <= TOL[dt], f"request {i} (own {own[i]}): max abs err {err:.3g}"
+    say(f"  worst max-abs {worst:.3g} over {B} requests, plain and hinted layouts")
+
+
 @pytest.mark.parametrize("d,B", [(64, 150), (128, 131)])
 def test_decode_fp32_mha_many_requests_direct(d, B):
     """fp32 MHA decode with more than 128 requests, so row blocks are full and there are
