@@ -2094,10 +2094,151 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
+  // One 32-key half (sub) of a tile in LDS (kt, vt) for this wave's rows: S^T on MFMA,
+  // online softmax, O^T += V^T P^T.
+  auto half_step = [&](const char* kt, const char* vt, const TileRef& tt, int sub) {
+    const int cnt = min(BN, tt.k1 - tt.k0);
+    const bool rows_in = rq >= tt.ra && rq < tt.rb;  // run tiles: the run's rows only
+    // S^T over this wave's 32 keys: row kr of the tile, dims ks*16 + half*8
+    f32x16 sc = f32x16{};
+    const int kr = sub * 32 + jrow;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
+    }
+    // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
+    const bool unmasked = cnt == BN && all_rows_ok && tt.ra == 0 && tt.rb == 64;
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = sc[r];
+      if (!unmasked) {
+        const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        v = row_ok && rows_in && key < cnt ? v : kNegInf;
+      }
+      sc[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = max_xor32(mx) * a.scale_log2;
+    // lazy rescale, as in attn_kernel: the reference moves only when a row's maximum
+    // exceeds it by more than 2^kLazy
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == kNegInf ? 0.f : -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
+      sc[r] = p;
+      psum += p;
+    }
+    psum = sum_xor32(psum);
+    l_run += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
+    // O^T += V^T P^T (V^T fragments by transposing LDS reads)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+  };
+
   // The tile loop in two forms: blocks with taken runs, and blocks without (every tile
   // from the block's row for all rows, whose code stays that of the plain loop).
   auto tile_loop = [&](auto with_runs) {
   constexpr bool kRuns = decltype(with_runs)::value;
+  if constexpr (ST == 2) {
+    // Two-tile form: a ring of two tile slots, one tile at a time. While tile v is
+    // computed, tile v + 1's K/V rows and tile v + 2's slot ids (into registers) are in
+    // flight, so a tile's ids never wait in front of its loads and each tile takes one
+    // barrier. The slot-id list holds the ids of the ring's two tiles.
+    auto tref = [&](int v) {
+      if constexpr (kRuns) {
+        return tile_ref(v);
+      } else {
+        TileRef r;
+        r.k0 = v * BN;
+        r.k1 = L;
+        r.row = row0;
+        r.ra = 0;
+        r.rb = 64;
+        return r;
+      }
+    };
+    int id_raw = 0;
+    bool id_in = false;
+    auto load_ids = [&](int v) {  // threads < BN: the id of key tid of tile v, into a register
+      const TileRef r = tref(v);
+      const int pos = r.k0 + tid;
+      id_in = tid < BN && pos < r.k1;
+      id_raw = id_in ? a.rtt[(int64_t)r.row * a.rtt_stride + pos] : 0;
+    };
+    auto put_ids = [&](int v) {  // ... into tile v's half of the list (out of range: -1)
+      if (tid < BN) {
+        int sv = id_raw;
+        if (id_in && (sv < 0 || sv >= a.num_slots)) {
+          flag_error(RAX_DEVERR_SLOT);
+          sv = -1;
+        }
+        slot[((v - t_begin) & 1) * BN + tid] = id_in ? sv : -1;
+      }
+    };
+    auto issue_kv = [&](int v) {  // every K and V row of tile v into its ring slot
+      const int t = (v - t_begin) & 1;
+#pragma unroll
+      for (int q = wave; q < NI; q += NW) {
+        const int r = q * RPI + lane / CH;
+        const int sv = slot[t * BN + r];
+        const int64_t off = (int64_t)(sv < 0 ? 0 : sv) * row_bytes;
+        lds_load16(kbase + off + (((lane % CH) ^ swz_k(r)) * 16), uni(kv_lds + t * TB + q * 1024));
+        lds_load16(vbase + off + (((lane % CH) ^ swz_v(r)) * 16), uni(kv_lds + (ST + t) * TB + q * 1024));
+      }
+    };
+    if (t_begin < t_end) {
+      load_ids(t_begin);
+      put_ids(t_begin);
+      if (t_begin + 1 < t_end) load_ids(t_begin + 1);
+      __syncthreads();
+      issue_kv(t_begin);
+    }
+    for (int v = t_begin; v < t_end; ++v) {
+      const int t = (v - t_begin) & 1;
+      // tile v's rows and tile v + 1's ids (issued during tile v - 1) have arrived
+      __builtin_amdgcn_s_waitcnt(0);
+      if (v + 1 < t_end) put_ids(v + 1);
+      // every wave's rows of tile v in LDS, tile v + 1's ids written, and every wave done
+      // with tile v - 1, whose ring slot tile v + 1 takes (a plain barrier after the LDS
+      // writes: __syncthreads' release fence would also wait for loads in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (v + 1 < t_end) issue_kv(v + 1);
+      if (v + 2 < t_end) load_ids(v + 2);
+      const TileRef tv = tref(v);
+      const int cnt = tv.k1 - tv.k0;
+      if (cnt < BN) {
+        // rows past the tile's last key read slot 0: zero them (their scores are masked;
+        // zeros keep P.V finite)
+        for (int i = tid; i < (BN - cnt) * CH; i += 64 * NW) {
+          const int off = t * TB + (cnt + i / CH) * RB + (i % CH) * 16;
+          *reinterpret_cast<u32x4*>(kv + off) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(kv + ST * TB + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      for (int sub = wkey; sub < 2; sub += NKG) half_step(kv + t * TB, kv + (ST + t) * TB, tv, sub);
+    }
+    __syncthreads();  // the epilogue reuses the tile area
+    return;
+  }
   for (int tb = t_begin; tb < t_end; tb += ST) {
     const int nt = min(ST, t_end - tb);
     if constexpr (kRuns) {
@@ -2156,64 +2297,8 @@ shared_kernel(const int32_t* p_rpi, const int32_t* p_len, const int32_t* p_sh,
       if (zeroed) __syncthreads();
       // 32-key halves 2 t0 .. 2 t1 - 1 of the round, round-robin over the key groups
       for (int j = 2 * t0 + wkey; j < 2 * t1; j += NKG) {
-      const int t = j >> 1, sub = j & 1;
-      const TileRef tt = tile(t);
-      const int cnt = min(BN, tt.k1 - tt.k0);
-      const bool rows_in = rq >= tt.ra && rq < tt.rb;  // run tiles: the run's rows only
-      const char* kt = kv + t * TB;
-      const char* vt = kv + (ST + t) * TB;
-      // S^T over this wave's 32 keys: row kr of the tile, dims ks*16 + half*8
-      f32x16 sc = f32x16{};
-      const int kr = sub * 32 + jrow;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, kr, ks, half), qf[ks], sc, 0, 0, 0);
-      }
-      // register r holds key sub*32 + 8*(r/4) + 4*half + r%4 of this lane's row
-      const bool unmasked = cnt == BN && all_rows_ok && tt.ra == 0 && tt.rb == 64;
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sc[r];
-        if (!unmasked) {
-          const int key = sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          v = row_ok && rows_in && key < cnt ? v : kNegInf;
-        }
-        sc[r] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = max_xor32(mx) * a.scale_log2;
-      // lazy rescale, as in attn_kernel: the reference moves only when a row's maximum
-      // exceeds it by more than 2^kLazy
-      if (__any(mx > m_run + kLazy)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == kNegInf ? 0.f : -m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, neg_m));
-        sc[r] = p;
-        psum += p;
-      }
-      psum = sum_xor32(psum);
-      l_run += psum;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kh][e] = (__bf16)sc[kh * 8 + e];
-      // O^T += V^T P^T (V^T fragments by transposing LDS reads)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag(vt, sub, dt, kh, lane), pb[kh], acc[dt], 0, 0, 0);
+        const int t = j >> 1;
+        half_step(kv + t * TB, kv + (ST + t) * TB, tile(t), j & 1);
       }
     }
     __syncthreads();  // the next round overwrites the tiles
