@@ -1906,7 +1906,8 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnArgs a) {
 // the 32-key halves of a round's tiles go round-robin to the key groups, whose softmax
 // states combine in LDS at the end. Two forms: NKG = 4, ST = kShTiles (8 waves, 128 KB of
 // LDS, one workgroup per CU), and, when a split holds many tiles, NKG = 2, ST = 2 (4
-// waves, 64 KB, two workgroups per CU whose rounds overlap). (Running the requests' own
+// waves, 64 KB, two workgroups per CU), which runs its tiles through a ring of two slots
+// (tile_loop). (Running the requests' own
 // keys in the same workgroups, while the tiles arrive, measured slower: with eight waves
 // per CU each own-key stream is a chain of round trips that the separate own-part
 // kernel's 16 waves per CU hide.) LDS layout and fragment reads: see "tiles loaded
