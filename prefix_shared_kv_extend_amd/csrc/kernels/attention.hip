@@ -3184,6 +3184,13 @@ static DecodeLayout decode_layout(int64_t batch, int32_t h_q, int32_t h_kv, int3
     if (l.split_decode && dt == RAX_BF16 && d == 128 && tiles > 8 * (int64_t)l.nsplit) {
       l.sh_small = 1;
       l.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(512 + blocks - 1) / blocks, tiles, 32}));
+    } else if (hint.tiles > 0 && l.split_decode && dt == RAX_BF16 && d == 128) {
+      // the 8-wave form takes a round of kShTiles tiles at once: with the hints' tile
+      // count known, no split takes less than a round (a short shared prefix, such as a
+      // system prompt under many blocks, then runs in one workgroup per block, with one
+      // partial per row to write and merge)
+      l.nsplit = (int32_t)std::max<int64_t>(
+          1, std::min<int64_t>(l.nsplit, (hint.tiles + kShTiles - 1) / kShTiles));
     }
   }
   // Deeper runs (block_runs) where the shared part runs in shared_kernel: up to four
