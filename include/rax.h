@@ -291,6 +291,18 @@ rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_stride, int
                                   const int32_t* src_indptr, const int32_t* src_slots, int32_t batch,
                                   int64_t total, void* stream);
 
+/* An extend call's two write-backs in one launch: rax_req_to_token_write(req_to_token, ...,
+ * total) and rax_kv_scatter(k_new, ..., dt), with the same arguments, checks and flagged
+ * errors; either half may be empty (batch or total 0: no rows; n_tok 0: no K/V). The two
+ * write different arrays, so nothing orders them within the launch. For a runtime that
+ * fills a batch's rows and writes its suffix K/V in the same step (one launch fewer per
+ * extend call). */
+rax_status rax_extend_write(int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                            const int32_t* req_pool_idx, const int32_t* start, const int32_t* src_indptr,
+                            const int32_t* src_slots, int32_t batch, int64_t total, const void* k_new,
+                            const void* v_new, const int32_t* out_loc, int64_t n_tok, void* k_pool, void* v_pool,
+                            int64_t num_slots, int32_t h_kv, int32_t d, rax_dtype dt, void* stream);
+
 /* One decode step's bookkeeping and write-back for a batch of running requests, in one
  * call: the work a scheduler does between two decode attention calls ([notes] App. A.2:
  * take memory for the batch, evicting LRU leaves when short; [bowen] "insert": keep the

@@ -83,6 +83,8 @@ _SIGS = {
     "rax_decode_append": (_i32, [_vp, _i32, _c_i32p, _c_i32p, _c_i32p, _i64, _c_i64p, _vp, _vp, _vp, _i64, _i64,
                                  _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "rax_req_to_token_write": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _vp]),
+    "rax_extend_write": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
+                                _i64, _i32, _i32, _i32, _vp]),
     "rax_extend_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
                                     _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "rax_decode_attention": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32,
@@ -514,6 +516,25 @@ def req_to_token_write(req_to_token, req_pool_idx, start, src_indptr, src_slots,
     _check(lib().rax_req_to_token_write(_dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
                                         _dev(req_pool_idx), _dev(start), _dev(src_indptr), _dev(src_slots),
                                         b, int(total), _stream(stream, req_to_token)), "rax_req_to_token_write")
+
+
+def extend_write(req_to_token, req_pool_idx, start, src_indptr, src_slots, total: int, k_new, v_new, out_loc,
+                 k_pool, v_pool, stream=None) -> None:
+    """rax_extend_write: req_to_token_write and kv_scatter (the same arguments) in one launch."""
+    _cuda_i32(req_to_token, req_pool_idx, start, src_indptr, src_slots, out_loc)
+    _need(req_to_token.dim() == 2, "req_to_token: [rows, stride]")
+    b = req_pool_idx.numel()
+    _need(start.numel() == b and src_indptr.numel() == b + 1 and src_slots.numel() >= total, "shapes")
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new: [n_tok, h_kv, d]")
+    _need(k_pool.shape == v_pool.shape and k_pool.shape[1:] == k_new.shape[1:], "pool: [num_slots, h_kv, d]")
+    _need(k_new.dtype == k_pool.dtype == v_new.dtype == v_pool.dtype, "dtypes must agree")
+    _need(all(t.is_contiguous() and t.is_cuda for t in (k_new, v_new, k_pool, v_pool)), "contiguous cuda tensors")
+    _need(out_loc.numel() == k_new.shape[0], "out_loc: [n_tok]")
+    _check(lib().rax_extend_write(_dev(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
+                                  _dev(req_pool_idx), _dev(start), _dev(src_indptr), _dev(src_slots), b, int(total),
+                                  _dev(k_new), _dev(v_new), _dev(out_loc), k_new.shape[0], _dev(k_pool), _dev(v_pool),
+                                  k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], _dtype_code(k_pool),
+                                  _stream(stream, k_pool)), "rax_extend_write")
 
 
 def attention_workspace_bytes(is_decode: bool, rows: int, h_q: int, h_kv: int, d: int, max_kv_len: int) -> int:

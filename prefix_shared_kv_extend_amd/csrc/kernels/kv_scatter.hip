@@ -19,15 +19,14 @@ namespace raxk {
 
 __device__ int32_t g_rax_err = 0;
 
-// One thread moves one 16-byte chunk of one token row, for K and for V.
-__global__ void __launch_bounds__(256) kv_scatter_kernel(const uint4* __restrict__ k_new,
-                                                         const uint4* __restrict__ v_new,
-                                                         const int32_t* __restrict__ out_loc, int64_t n_tok,
-                                                         uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
-                                                         int64_t num_slots, int64_t chunks_per_row) {
+// One thread moves one 16-byte chunk of one token row, for K and for V; blocks b of nb
+// of a grid-stride loop.
+__device__ __forceinline__ void kv_scatter_part(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                                const int32_t* __restrict__ out_loc, int64_t n_tok,
+                                                uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                int64_t num_slots, int64_t chunks_per_row, int64_t b, int64_t nb) {
   const int64_t total = n_tok * chunks_per_row;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = b * 256 + threadIdx.x; i < total; i += nb * 256) {
     const int64_t tok = i / chunks_per_row;
     const int64_t c = i - tok * chunks_per_row;
     const int32_t slot = out_loc[tok];
@@ -41,14 +40,14 @@ __global__ void __launch_bounds__(256) kv_scatter_kernel(const uint4* __restrict
   }
 }
 
-__global__ void __launch_bounds__(256) rtt_write_kernel(int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
-                                                        const int32_t* __restrict__ req_pool_idx,
-                                                        const int32_t* __restrict__ start,
-                                                        const int32_t* __restrict__ indptr,
-                                                        const int32_t* __restrict__ src, int32_t batch,
-                                                        int64_t total) {
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
+// One thread writes one req_to_token entry: entry e of the concatenated sources goes to
+// row req_pool_idx[r], column start[r] + e - indptr[r] of its request r; blocks b of nb.
+__device__ __forceinline__ void rtt_write_part(int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
+                                               const int32_t* __restrict__ req_pool_idx,
+                                               const int32_t* __restrict__ start,
+                                               const int32_t* __restrict__ indptr, const int32_t* __restrict__ src,
+                                               int32_t batch, int64_t total, int64_t b, int64_t nb) {
+  for (int64_t e = b * 256 + threadIdx.x; e < total; e += nb * 256) {
     // request owning entry e: last r with indptr[r] <= e
     int lo = 0, hi = batch - 1;
     while (lo < hi) {
@@ -64,6 +63,44 @@ __global__ void __launch_bounds__(256) rtt_write_kernel(int32_t* __restrict__ rt
     }
     rtt[row * stride + col] = src[e];
   }
+}
+
+__global__ void __launch_bounds__(256) kv_scatter_kernel(const uint4* __restrict__ k_new,
+                                                         const uint4* __restrict__ v_new,
+                                                         const int32_t* __restrict__ out_loc, int64_t n_tok,
+                                                         uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                         int64_t num_slots, int64_t chunks_per_row) {
+  kv_scatter_part(k_new, v_new, out_loc, n_tok, k_pool, v_pool, num_slots, chunks_per_row, blockIdx.x, gridDim.x);
+}
+
+__global__ void __launch_bounds__(256) rtt_write_kernel(int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
+                                                        const int32_t* __restrict__ req_pool_idx,
+                                                        const int32_t* __restrict__ start,
+                                                        const int32_t* __restrict__ indptr,
+                                                        const int32_t* __restrict__ src, int32_t batch,
+                                                        int64_t total) {
+  rtt_write_part(rtt, stride, rows, req_pool_idx, start, indptr, src, batch, total, blockIdx.x, gridDim.x);
+}
+
+// An extend call's two write-backs in one launch: the first g_rtt blocks fill the
+// requests' req_to_token rows, the others write the new tokens' K/V rows into the pools.
+// The two touch different arrays, so their blocks need no order.
+__global__ void __launch_bounds__(256) extend_write_kernel(int32_t* __restrict__ rtt, int64_t stride, int64_t rows,
+                                                           const int32_t* __restrict__ req_pool_idx,
+                                                           const int32_t* __restrict__ start,
+                                                           const int32_t* __restrict__ indptr,
+                                                           const int32_t* __restrict__ src, int32_t batch,
+                                                           int64_t total, int32_t g_rtt,
+                                                           const uint4* __restrict__ k_new,
+                                                           const uint4* __restrict__ v_new,
+                                                           const int32_t* __restrict__ out_loc, int64_t n_tok,
+                                                           uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                           int64_t num_slots, int64_t chunks_per_row) {
+  if ((int)blockIdx.x < g_rtt)
+    rtt_write_part(rtt, stride, rows, req_pool_idx, start, indptr, src, batch, total, blockIdx.x, g_rtt);
+  else
+    kv_scatter_part(k_new, v_new, out_loc, n_tok, k_pool, v_pool, num_slots, chunks_per_row, blockIdx.x - g_rtt,
+                    gridDim.x - g_rtt);
 }
 
 // Decode step write-back: for request i of the batch, its new slot b.slot[i] goes to
@@ -218,6 +255,33 @@ extern "C" rax_status rax_req_to_token_write(int32_t* req_to_token, int64_t rtt_
   hipLaunchKernelGGL(raxk::rtt_write_kernel, dim3(raxk::grid_for(total, 256)), dim3(256), 0,
                      (hipStream_t)stream, req_to_token, rtt_stride, rtt_rows, req_pool_idx, start, src_indptr,
                      src_slots, batch, total);
+  return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
+}
+
+extern "C" rax_status rax_extend_write(int32_t* req_to_token, int64_t rtt_stride, int64_t rtt_rows,
+                                      const int32_t* req_pool_idx, const int32_t* start, const int32_t* src_indptr,
+                                      const int32_t* src_slots, int32_t batch, int64_t total, const void* k_new,
+                                      const void* v_new, const int32_t* out_loc, int64_t n_tok, void* k_pool,
+                                      void* v_pool, int64_t num_slots, int32_t h_kv, int32_t d, rax_dtype dt,
+                                      void* stream) {
+  // each half checked as its own entry point checks it
+  if (batch < 0 || total < 0 || rtt_stride < 1 || rtt_rows < 1) return RAX_EINVAL;
+  if (n_tok < 0 || num_slots < 1 || h_kv < 1 || d < 1 || (dt != RAX_F32 && dt != RAX_BF16)) return RAX_EINVAL;
+  const bool do_rtt = batch > 0 && total > 0, do_kv = n_tok > 0;
+  if (do_rtt && (!req_to_token || !req_pool_idx || !start || !src_indptr || !src_slots)) return RAX_EINVAL;
+  const int64_t row_bytes = (int64_t)h_kv * d * (dt == RAX_F32 ? 4 : 2);
+  if (do_kv) {
+    if (!k_new || !v_new || !out_loc || !k_pool || !v_pool || row_bytes % 16) return RAX_EINVAL;
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15) return RAX_EINVAL;
+  }
+  if (!do_rtt && !do_kv) return RAX_OK;
+  const int64_t cpr = row_bytes / 16;
+  const int g_rtt = do_rtt ? raxk::grid_for(total, 256) : 0;
+  const int g_kv = do_kv ? raxk::grid_for(n_tok * cpr, 256) : 0;
+  hipLaunchKernelGGL(raxk::extend_write_kernel, dim3(g_rtt + g_kv), dim3(256), 0, (hipStream_t)stream, req_to_token,
+                     rtt_stride, rtt_rows, req_pool_idx, start, src_indptr, src_slots, batch, total, g_rtt,
+                     (const uint4*)k_new, (const uint4*)v_new, out_loc, do_kv ? n_tok : 0, (uint4*)k_pool,
+                     (uint4*)v_pool, num_slots, cpr);
   return hipGetLastError() == hipSuccess ? RAX_OK : RAX_EDEVICE;
 }
 

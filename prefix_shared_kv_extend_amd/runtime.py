@@ -63,6 +63,7 @@ class ExtendBatch:
     tok_indptr: np.ndarray = None
     max_kv_len: int = 0           # the most keys a query row sees (the longest prompt)
     dev: dict = field(default_factory=dict)
+    rtt_total: int = 0            # req_to_token entries of the batch's rows (run_extend writes them)
 
 
 @dataclass
@@ -223,8 +224,8 @@ class RadixRuntime:
             req_pool_idx=req_rows, prefix_len=eb.prefix_len, qo_indptr=qo,
             shared_len=self.tree.lca_depths(nodes), out_loc=new, rtt_start=np.zeros(len(rids)),
             rtt_indptr=ip, rtt_src=src))
-        L.req_to_token_write(self.rtt, eb.dev["req_pool_idx"], eb.dev["rtt_start"], eb.dev["rtt_indptr"],
-                             eb.dev["rtt_src"], int(ip[-1]))
+        # the rows are filled by run_extend's launch, together with the K/V write-back
+        eb.rtt_total = int(ip[-1])
         if self.host_slots:
             self.tree.run_moves(self.k_pool, self.v_pool)   # before the scatter writes the freed slots
         self._sync_decode_lengths()
@@ -234,8 +235,12 @@ class RadixRuntime:
     def run_extend(self, eb: ExtendBatch, q, k_ext, v_ext, o) -> None:
         """Write the suffix K/V into the pool and run extend attention (q/k/v/o on the device)."""
         if eb.total_q == 0:
+            L.req_to_token_write(self.rtt, eb.dev["req_pool_idx"], eb.dev["rtt_start"], eb.dev["rtt_indptr"],
+                                 eb.dev["rtt_src"], eb.rtt_total)
             return
-        L.kv_scatter(k_ext, v_ext, eb.dev["out_loc"], self.k_pool, self.v_pool)
+        # the requests' req_to_token rows and the suffix K/V rows in one launch
+        L.extend_write(self.rtt, eb.dev["req_pool_idx"], eb.dev["rtt_start"], eb.dev["rtt_indptr"], eb.dev["rtt_src"],
+                       eb.rtt_total, k_ext, v_ext, eb.dev["out_loc"], self.k_pool, self.v_pool)
         if self.pre_attention is not None:
             self.pre_attention()
         ws = self._workspace(L.attention_workspace_bytes(False, eb.total_q, self.h_q, self.h_kv, self.d,

@@ -105,6 +105,54 @@ def test_kv_scatter_bit_exact():
     assert _lib.device_errors() == 0
 
 
+def test_extend_write_equals_separate_calls():
+    """rax_extend_write (the rows and the K/V write-back in one launch) against
+    rax_req_to_token_write followed by rax_kv_scatter with the same arguments, bit for bit:
+    bf16 [1500, 8, 128] rows into shuffled slots with 9 ragged requests' rows; then each half
+    alone (no K/V rows; no req_to_token entries); then an out-of-range slot and row, skipped
+    and flagged as by the separate calls."""
+    from prefix_shared_kv_extend_amd import _lib
+    say("extend_write: rows + K/V write-back in one launch vs the two calls")
+    g = torch.Generator().manual_seed(7)
+    n, h, d, S, B, W = 1500, 8, 128, 6000, 9, 700
+    lens = torch.randint(1, 300, (B,), generator=g)
+    ip = torch.zeros(B + 1, dtype=torch.int32)
+    ip[1:] = torch.cumsum(lens, 0)
+    total = int(ip[-1])
+    rows = torch.randperm(B + 4, generator=g)[:B].to(torch.int32)
+    start = torch.randint(0, W - 300, (B,), generator=g).to(torch.int32)
+    src = torch.randint(0, S, (total,), generator=g).to(torch.int32)
+    k = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    loc = torch.randperm(S, generator=g)[:n].to(torch.int32).cuda()
+    dev = [t.cuda() for t in (rows, start, ip, src)]
+
+    def run(fused, kk, vv, ll, tot):
+        rtt = torch.full((B + 4, W), -1, dtype=torch.int32, device="cuda")
+        kp = torch.zeros((S, h, d), dtype=torch.bfloat16, device="cuda")
+        vp = torch.zeros_like(kp)
+        if fused:
+            _lib.extend_write(rtt, *dev, tot, kk, vv, ll, kp, vp)
+        else:
+            _lib.req_to_token_write(rtt, *dev, tot)
+            _lib.kv_scatter(kk, vv, ll, kp, vp)
+        torch.cuda.synchronize()
+        return rtt.cpu(), kp.cpu(), vp.cpu(), _lib.device_errors()
+
+    empty = (k[:0], v[:0], loc[:0])
+    for args in ((k, v, loc, total), (*empty, total), (k, v, loc, 0)):
+        a, b = run(True, *args), run(False, *args)
+        assert all(torch.equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3] == 0
+    # out of range: one slot past the pool, one row start past the row width
+    bad_loc = loc.clone()
+    bad_loc[5] = S
+    start[3] = W
+    dev[1] = start.cuda()
+    a, b = run(True, k, v, bad_loc, total), run(False, k, v, bad_loc, total)
+    assert all(torch.equal(x, y) for x, y in zip(a[:3], b[:3]))
+    assert a[3] == b[3] == (_lib.DEVERR_SLOT | _lib.DEVERR_ROW)
+
+
 def test_kv_scatter_out_of_range_slot_is_skipped_and_flagged():
     from prefix_shared_kv_extend_amd import _lib
     say("kv_scatter: slot ids -1 and S are skipped by the kernel's own bounds check")
